@@ -1,0 +1,234 @@
+"""Throughput of the tokenizer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one synthetic clip of the
+DV8x16x16-720p shape (1 x 3 x 49 x 720 x 1280 bf16), every stage a HIP kernel
+behind the C ABI:
+
+  Haar patcher (causal first frame, 2 levels)  ->  spatial 1x3x3 conv 192->256
+  ->  causal temporal 3x1x1 conv 256->256  ->  1x1 projection 256->6  ->  FSQ
+  indices;  FSQ of a separate N(0, 1.5) 6-channel latent  ->  dequantize;
+  inverse Haar of the coefficients back to pixels.
+
+Inputs are resident in HBM before timing.  `value` is frames per second of the
+whole step (49 frames per step).  The roofline object reports the dominant
+kernel, the spatial convolution's MFMA implicit GEMM: algorithmic FLOPs
+2*9*Cin*Cout per output position, divided by its average duration measured
+with HIP events on the launch stream over the timed steps.  The CPU baseline is
+the float64 oracle timed on a bounded sample of the same workload (a strip of
+the frame), scaled to the full clip.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "720p frames/sec through Haar+causal conv+FSQ; HBM GB/s & MFMA % of peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4_dv8x16x16_720p_49f")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-width", type=int, default=320,
+                    help="pixel width of the strip the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
+              "across GPUs in this library", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import causal_video_tokenizer_amd as cvt
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[args.workload]
+    if args.workload != "c4_dv8x16x16_720p_49f":
+        raise SystemExit("only the DV8x16x16-720p-shaped workload is wired into the benchmark step")
+    dev = torch.device("cuda:0")
+    B, C, T, H, W = wl["x"]
+    Tq, Hq, Wq = 1 + (T - 1) // 4, H // 4, W // 4
+    P = B * Tq * Hq * Wq
+    cid = 4
+
+    log(f"generating inputs {wl['x']} ...")
+    xbits = si.to_bf16_bits(si.video_trans(wl["x"], wl["seed"]))
+    zbits = si.to_bf16_bits(si.normal(wl["latent"], wl["latent_seed"], wl["latent_std"]))
+
+    def bf16_dev(bits, cl=False):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return t.to(memory_format=torch.channels_last_3d) if cl else t
+
+    ws_b = si.to_bf16_bits(si.normal((256, 192, 1, 3, 3), si.weight_seed(cid, 0), 0.02))
+    wt_b = si.to_bf16_bits(si.normal((256, 256, 3, 1, 1), si.weight_seed(cid, 1), 0.02))
+    pj_b = si.to_bf16_bits(si.normal((6, 256, 1, 1, 1), si.weight_seed(cid, 2), 0.02))
+    x = bf16_dev(xbits)
+    z_sep = bf16_dev(zbits)
+    w_s, w_t, w_p = bf16_dev(ws_b), bf16_dev(wt_b), bf16_dev(pj_b)
+
+    cl = torch.channels_last_3d
+    hz = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    s1 = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    y1 = torch.empty_like(s1)
+    lat = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    idx = torch.empty((B, Tq, Hq, Wq), dtype=torch.int32, device=dev)
+    idx2 = torch.empty_like(idx)
+    codes = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    xr = torch.empty_like(x)
+    ws_sp = torch.empty(cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)
+    ws_tm = torch.empty(cvt.conv_workspace_bytes(s1.shape, 256, 3, False, True), dtype=torch.uint8, device=dev)
+    ws_pj = torch.empty(cvt.conv_workspace_bytes(y1.shape, 6, 1, True, False), dtype=torch.uint8, device=dev)
+
+    stages = ["haar_fwd", "conv_spatial", "conv_temporal", "proj_1x1", "fsq_quantize", "fsq_quantize_sep",
+              "fsq_dequantize", "haar_inv"]
+    calls = {
+        "haar_fwd": lambda: cvt.haar3d_fwd(x, out=hz),
+        "conv_spatial": lambda: cvt.causal_conv3d_fact(hz, w_s, None, workspace=ws_sp, out=s1),
+        "conv_temporal": lambda: cvt.causal_conv3d_fact(s1, None, w_t, workspace=ws_tm, out=y1),
+        "proj_1x1": lambda: cvt.causal_conv3d_fact(y1, w_p, None, workspace=ws_pj, out=lat),
+        "fsq_quantize": lambda: cvt.fsq_quantize(lat, indices=idx),
+        "fsq_quantize_sep": lambda: cvt.fsq_quantize(z_sep, indices=idx2),
+        "fsq_dequantize": lambda: cvt.fsq_dequantize(idx2, out=codes),
+        "haar_inv": lambda: cvt.haar3d_inv(hz, out=xr),
+    }
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        for i, name in enumerate(stages):
+            if evs is not None:
+                evs[i].record(stream)
+            calls[name]()
+        if evs is not None:
+            evs[len(stages)].record(stream)
+
+    log("warmup ...")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+                for i, name in enumerate(stages)}
+
+    # algorithmic work per stage
+    conv_flops = {
+        "conv_spatial": 2.0 * 9 * 192 * 256 * P,
+        "conv_temporal": 2.0 * 3 * 256 * 256 * P,
+        "proj_1x1": 2.0 * 256 * 6 * P,
+    }
+    hbm_bytes = {
+        "haar_fwd": 2.0 * B * C * T * H * W + 2.0 * P * 192,
+        "haar_inv": 2.0 * P * 192 + 2.0 * B * C * T * H * W,
+        "fsq_quantize": P * (6 * 2 + 4.0),
+        "fsq_quantize_sep": P * (6 * 2 + 4.0),
+        "fsq_dequantize": P * (4 + 6 * 2.0),
+        "proj_1x1": P * (256 * 2 + 6 * 2.0),
+    }
+    per_stage = {}
+    for name in stages:
+        d = {"ms": round(stage_ms[name], 4)}
+        if name in conv_flops:
+            d["TFLOPs"] = round(conv_flops[name] / (stage_ms[name] * 1e-3) / 1e12, 2)
+        if name in hbm_bytes:
+            d["GBps"] = round(hbm_bytes[name] / (stage_ms[name] * 1e-3) / 1e9, 1)
+        per_stage[name] = d
+
+    dom = "conv_spatial"
+    achieved = conv_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "conv_igemm_kernel<SPATIAL3,256,128,2,2> (1x3x3 conv 192->256, bf16 MFMA)",
+                "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, (B, C, T, H, W), args.cpu_width)
+
+    frames = B * T
+    out = {
+        "metric": METRIC,
+        "value": round(frames / (ms_per_step * 1e-3), 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DV8x16x16-720p-shaped discrete path, 1x3x49x720x1280 bf16 "
+                               "(Haar -> conv 192->256 k3 -> 1x1 ->6 -> FSQ; FSQ+dequant of a 6x13x180x320 "
+                               "N(0,1.5) latent; inverse Haar)",
+                   "frames_per_step": frames, "latent_grid": [Tq, Hq, Wq]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": per_stage,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):
+    """The float64 oracle on a strip of the clip (all frames, all rows, `width`
+    pixel columns), scaled to the whole clip by the width ratio."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import bf16 as obf16
+    from oracle import conv as oconv
+    from oracle import fsq as ofsq
+    from oracle import haar as ohaar
+
+    B, C, T, H, W = shape
+    width = max(4, min(W, width - width % 4))
+    wq = width // 4
+    log(f"cpu baseline: oracle on a {T}x{H}x{width} strip ...")
+    t0 = time.perf_counter()
+    xs = obf16.decode(xbits[:, :, :, :, :width])
+    hz = ohaar.haar3d_fwd(xs, 2)
+    hzb = obf16.round_to_bf16(hz)
+    y = oconv.causal_conv3d_fact(hzb, obf16.decode(ws_b), obf16.decode(wt_b))
+    lat = oconv.pointwise(obf16.round_to_bf16(y), obf16.decode(pj_b))
+    ofsq.quantize(obf16.round_to_bf16(lat))
+    i2, _, _ = ofsq.quantize(obf16.decode(zbits[:, :, :, :, :wq]))
+    ofsq.dequantize(i2)
+    ohaar.haar3d_inv(hzb, 2)
+    dt = time.perf_counter() - t0
+    scale = W / width
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(B * T / (dt * scale), 4), "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"all {T} frames x {H} rows x {width} of {W} pixel columns (1/{scale:g} of the clip), "
+                      f"{dt:.1f} s, scaled by {scale:g}; float64 NumPy, BLAS threads={threads}",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

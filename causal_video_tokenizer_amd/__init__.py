@@ -1,0 +1,231 @@
+"""Causal video tokenizer hot path on AMD MI355X: Python binding of libcvt.
+
+The work is done by the HIP kernels in ``libcvt.so`` behind the C ABI declared
+in ``include/cvt.h``.  This module only marshals arguments: it allocates
+outputs with torch on the input's device, passes raw device pointers, sizes and
+torch's current HIP stream, and raises ``CvtError`` on a non-OK status.  There
+is no fallback: if the library is missing, importing this module fails.
+
+Tensor conventions
+------------------
+* Pixel videos are [B, C, T, H, W] contiguous (NCTHW), float32 or bfloat16.
+* Latents / Haar coefficients default to NTHWC, exposed as torch tensors of
+  logical shape [B, C, T, H, W] in ``torch.channels_last_3d`` memory format.
+* FSQ indices are int32 [B, T, H, W].
+
+Entry points (same names as the C functions without the ``cvt_`` prefix):
+``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``, ``fsq_quantize``,
+``fsq_dequantize``.  ``lib`` is the loaded ctypes library with the raw C
+functions.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcvt.so")
+
+CVT_F32, CVT_BF16 = 0, 1
+CVT_NCTHW, CVT_NTHWC = 0, 1
+DEFAULT_LEVELS = (8, 8, 8, 5, 5, 5)
+
+# Every symbol include/cvt.h declares, with its ctypes signature.
+_vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "cvt_abi_version": (_ci, []),
+    "cvt_status_string": (ctypes.c_char_p, [_ci]),
+    "cvt_last_error": (ctypes.c_char_p, []),
+    "cvt_haar3d_fwd": (_ci, [_vp, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
+    "cvt_haar3d_inv": (_ci, [_vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
+    "cvt_causal_conv3d_fact_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
+    "cvt_causal_conv3d_fact": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp]),
+    "cvt_fsq_quantize": (_ci, [_vp, _ci, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp]),
+    "cvt_fsq_dequantize": (_ci, [_vp, _vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
+}
+
+
+class CvtError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = lib.cvt_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.cvt_status_string(status).decode()} ({detail})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m causal_video_tokenizer_amd.build` "
+            "(hipcc for gfx950); there is no fallback implementation")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def _check(status, where):
+    if status != 0:
+        raise CvtError(status, where)
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return CVT_F32
+    if t == torch.bfloat16:
+        return CVT_BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a ROCm GPU device")
+
+
+def _layout_of(t):
+    """Physical layout code of a 5-D tensor (NCTHW contiguous or NTHWC)."""
+    if t.is_contiguous():
+        return CVT_NCTHW
+    if t.is_contiguous(memory_format=torch.channels_last_3d):
+        return CVT_NTHWC
+    raise ValueError("5-D tensors must be contiguous (NCTHW) or channels_last_3d (NTHWC)")
+
+
+def _empty5(shape, dtype, device, layout):
+    mf = torch.channels_last_3d if layout == CVT_NTHWC else torch.contiguous_format
+    return torch.empty(shape, dtype=dtype, device=device, memory_format=mf)
+
+
+def haar3d_fwd(x, temporal_levels=2, out_dtype=None, layout="NTHWC", out=None):
+    """Forward Haar patcher: x [B, C, T, H, W] NCTHW -> [B, 64C, T', H/4, W/4]
+    (16C and T with temporal_levels=0) in ``layout``."""
+    _require_gpu(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be NCTHW-contiguous")
+    B, C, T, H, W = x.shape
+    lay = CVT_NTHWC if layout == "NTHWC" else CVT_NCTHW
+    odt = out_dtype or x.dtype
+    if temporal_levels == 2:
+        shape = (B, 64 * C, 1 + max(T - 1, 0) // 4, H // 4, W // 4)
+    else:
+        shape = (B, 16 * C, T, H // 4, W // 4)
+    y = out if out is not None else _empty5(shape, odt, x.device, lay)
+    _check(lib.cvt_haar3d_fwd(_ptr(x), _dtype_code(x.dtype), _ptr(y), _dtype_code(y.dtype), lay,
+                              B, C, T, H, W, temporal_levels, _stream(x.device)), "haar3d_fwd")
+    return y
+
+
+def haar3d_inv(y, temporal_levels=2, out_dtype=None, out=None):
+    """Inverse Haar patcher: coefficients [B, 64C, T', H', W'] (either layout)
+    -> pixels [B, C, 4T'-3, 4H', 4W'] NCTHW (T' frames with temporal_levels=0)."""
+    _require_gpu(y)
+    lay = _layout_of(y)
+    B, NCH, Tq, Hq, Wq = y.shape
+    G = 64 if temporal_levels == 2 else 16
+    if NCH % G:
+        raise ValueError(f"coefficient channels must be a multiple of {G}")
+    C = NCH // G
+    T = 4 * Tq - 3 if temporal_levels == 2 else Tq
+    odt = out_dtype or y.dtype
+    x = out if out is not None else torch.empty((B, C, T, 4 * Hq, 4 * Wq), dtype=odt, device=y.device)
+    _check(lib.cvt_haar3d_inv(_ptr(y), _dtype_code(y.dtype), lay, _ptr(x), _dtype_code(x.dtype),
+                              B, C, T, 4 * Hq, 4 * Wq, temporal_levels, _stream(y.device)), "haar3d_inv")
+    return x
+
+
+CVT_CONV_SPATIAL, CVT_CONV_TEMPORAL = 1, 2
+
+
+def conv_workspace_bytes(x_shape, Cout, k, spatial=True, temporal=True):
+    B, Cin, T, H, W = x_shape
+    parts = (CVT_CONV_SPATIAL if spatial else 0) | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_causal_conv3d_fact_workspace(B, Cin, Cout, T, H, W, k, parts))
+
+
+def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out=None):
+    """Factorized causal convolution on a bf16 NTHWC tensor.
+
+    x: [B, Cin, T, H, W] bf16 channels_last_3d; w_s: [Cout, Cin, 1, k, k] bf16
+    or None (temporal part only); w_t: [Cout, Cout, k, 1, 1] bf16 or None
+    (spatial part only); b_s, b_t: float32 [Cout] or None.
+    Returns y [B, Cout, T, H, W] bf16 channels_last_3d.
+    """
+    _require_gpu(x, w_s, w_t, b_s, b_t)
+    if not x.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError("x must be channels_last_3d (NTHWC)")
+    B, Cin, T, H, W = x.shape
+    if w_s is not None:
+        Cout, Cin_w, kt, k, k2 = w_s.shape
+        if Cin_w != Cin or kt != 1 or k != k2:
+            raise ValueError("w_s must be [Cout, Cin, 1, k, k]")
+    elif w_t is not None:
+        Cout, k = w_t.shape[0], w_t.shape[2]
+    else:
+        raise ValueError("at least one of w_s and w_t is needed")
+    if w_t is not None and tuple(w_t.shape) != (Cout, Cout, k, 1, 1):
+        raise ValueError("w_t must be [Cout, Cout, k, 1, 1]")
+    for w in (w_s, w_t):
+        if w is not None and (w.dtype != torch.bfloat16 or not w.is_contiguous()):
+            raise ValueError("weights must be contiguous bfloat16")
+    for b in (b_s, b_t):
+        if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or b.numel() != Cout):
+            raise ValueError("biases must be contiguous float32 [Cout]")
+    need = conv_workspace_bytes(x.shape, Cout, k, w_s is not None, w_t is not None)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = out if out is not None else _empty5((B, Cout, T, H, W), torch.bfloat16, x.device, CVT_NTHWC)
+    _check(lib.cvt_causal_conv3d_fact(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
+                                      B, Cin, Cout, T, H, W, k, _ptr(workspace), workspace.numel(),
+                                      _stream(x.device)), "causal_conv3d_fact")
+    return y
+
+
+def _levels_arg(levels):
+    arr = (ctypes.c_int32 * len(levels))(*levels)
+    return arr, len(levels)
+
+
+def fsq_quantize(z, levels=DEFAULT_LEVELS, return_codes=False, indices=None, codes=None):
+    """FSQ: z [B, D, T, H, W] (NCTHW or NTHWC, f32/bf16) -> int32 indices [B, T, H, W]
+    (and the quantized codes, shaped and laid out like z, when return_codes)."""
+    _require_gpu(z)
+    lay = _layout_of(z)
+    B, D, T, H, W = z.shape
+    arr, n = _levels_arg(levels)
+    idx = indices if indices is not None else torch.empty((B, T, H, W), dtype=torch.int32, device=z.device)
+    if return_codes and codes is None:
+        codes = _empty5(tuple(z.shape), z.dtype, z.device, lay)
+    _check(lib.cvt_fsq_quantize(_ptr(z), _dtype_code(z.dtype), lay, _ptr(idx), _ptr(codes) if return_codes else None,
+                                arr, n, B, T, H, W, _stream(z.device)), "fsq_quantize")
+    return (idx, codes) if return_codes else idx
+
+
+def fsq_dequantize(indices, levels=DEFAULT_LEVELS, dtype=torch.bfloat16, layout="NTHWC", invalid_count=None,
+                   out=None):
+    """FSQ dequantize: int32 indices [B, T, H, W] -> codes [B, D, T, H, W] in
+    ``layout``.  ``invalid_count``: optional int32 device tensor of one element
+    to which the number of out-of-range indices is added."""
+    _require_gpu(indices)
+    if indices.dtype != torch.int32 or not indices.is_contiguous():
+        raise ValueError("indices must be contiguous int32")
+    B, T, H, W = indices.shape
+    lay = CVT_NTHWC if layout == "NTHWC" else CVT_NCTHW
+    arr, n = _levels_arg(levels)
+    codes = out if out is not None else _empty5((B, n, T, H, W), dtype, indices.device, lay)
+    _check(lib.cvt_fsq_dequantize(_ptr(indices), _ptr(codes), _dtype_code(codes.dtype), lay, arr, n,
+                                  B, T, H, W, _ptr(invalid_count), _stream(indices.device)), "fsq_dequantize")
+    return codes

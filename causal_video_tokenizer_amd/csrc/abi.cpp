@@ -1,0 +1,213 @@
+// C ABI entry points: argument validation, host-side parameter preparation
+// and dispatch to the HIP launchers.  Every check runs before any launch, so
+// an error status means nothing was enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <limits>
+
+#include "cvt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return CVT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CVT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == CVT_F32 || d == CVT_BF16; }
+bool valid_layout(int l) { return l == CVT_NCTHW || l == CVT_NTHWC; }
+
+int check_haar(const void* a, int a_dt, const void* b, int b_dt, int layout, int B, int C, int T, int H, int W,
+               int tl) {
+    if (!a || !b) return fail(CVT_E_NULL, "null tensor pointer");
+    if (!valid_dtype(a_dt) || !valid_dtype(b_dt)) return fail(CVT_E_DTYPE, "dtype must be CVT_F32 or CVT_BF16");
+    if (!valid_layout(layout)) return fail(CVT_E_LAYOUT, "layout must be CVT_NCTHW or CVT_NTHWC");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (tl != 0 && tl != 2) return fail(CVT_E_SHAPE, "temporal_levels must be 0 or 2, got %d", tl);
+    if (H % 4 || W % 4) return fail(CVT_E_SHAPE, "H and W must be multiples of 4 (got %dx%d)", H, W);
+    if (tl == 2 && (T - 1) % 4) return fail(CVT_E_SHAPE, "temporal Haar needs T = 1 + 4k frames (got %d)", T);
+    if (!aligned16(a) || !aligned16(b)) return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    return CVT_OK;
+}
+
+// FSQ breakpoints.  For L levels with h = (L-1)(1+eps)/2, o = 1/2 (L even) or
+// 0, s = atanh(o/h), the rounded bound q = rint(tanh(z+s) h - o) steps from j
+// to j+1 where tanh(z+s) h - o = j + 1/2, i.e. at z_j = atanh((j+1/2+o)/h) - s,
+// j = -floor(L/2) .. ceil(L/2) - 2 (L - 1 breakpoints).  The digit
+// d = q + floor(L/2) is the number of breakpoints below z.  Each z_j is
+// replaced by the smallest float f with f > z_j, so that for every float z
+// "z >= f" is exactly "z > z_j".
+constexpr double kFsqEps = 1e-3;
+
+float float_above(double zj) {
+    float f = (float)zj;
+    if ((double)f <= zj) f = nextafterf(f, std::numeric_limits<float>::infinity());
+    return f;
+}
+
+int fsq_params(const int32_t* levels, int D, cvt::FsqParams* p) {
+    if (!levels) return fail(CVT_E_NULL, "levels is NULL");
+    if (D < 1 || D > cvt::FSQ_MAX_D) return fail(CVT_E_LEVELS, "D must be in [1, %d], got %d", cvt::FSQ_MAX_D, D);
+    memset(p, 0, sizeof(*p));
+    p->D = D;
+    long long prod = 1;
+    for (int i = 0; i < D; ++i) {
+        const int L = levels[i];
+        if (L < 2 || L > cvt::FSQ_MAX_L)
+            return fail(CVT_E_LEVELS, "level %d is %d, must be in [2, %d]", i, L, cvt::FSQ_MAX_L);
+        p->levels[i] = L;
+        p->basis[i] = (int)prod;
+        prod *= L;
+        if (prod >= (1LL << 31)) return fail(CVT_E_LEVELS, "product of levels must be below 2^31");
+        p->half[i] = L / 2;
+        p->nthr[i] = L - 1;
+        int l = 0;
+        while ((1 << l) < L) ++l;
+        p->magic[i] = (unsigned int)(((1ull << (31 + l)) + (unsigned long long)L - 1ull) / (unsigned long long)L);
+        p->shift[i] = l - 1;
+        const double h = (L - 1) * (1.0 + kFsqEps) / 2.0;
+        const double o = (L % 2 == 0) ? 0.5 : 0.0;
+        const double s = atanh(o / h);
+        const int half = L / 2;
+        for (int j = 0; j < cvt::FSQ_MAX_L - 1; ++j) p->thr[i][j] = std::numeric_limits<float>::quiet_NaN();
+        for (int j = -half, n = 0; j <= (L + 1) / 2 - 2; ++j, ++n) p->thr[i][n] = float_above(atanh((j + 0.5 + o) / h) - s);
+    }
+    p->codebook = (int)prod;
+    return CVT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cvt_abi_version(void) { return 1; }
+
+const char* cvt_status_string(int s) {
+    switch (s) {
+        case CVT_OK: return "CVT_OK";
+        case CVT_E_NULL: return "CVT_E_NULL: a required pointer is NULL";
+        case CVT_E_SHAPE: return "CVT_E_SHAPE: invalid size or shape";
+        case CVT_E_DTYPE: return "CVT_E_DTYPE: unsupported dtype";
+        case CVT_E_LAYOUT: return "CVT_E_LAYOUT: unsupported layout";
+        case CVT_E_ALIGN: return "CVT_E_ALIGN: pointer not 16-byte aligned";
+        case CVT_E_LEVELS: return "CVT_E_LEVELS: unsupported FSQ levels";
+        case CVT_E_WORKSPACE: return "CVT_E_WORKSPACE: workspace missing or too small";
+        case CVT_E_HIP: return "CVT_E_HIP: HIP runtime error";
+        default: return "unknown cvt status";
+    }
+}
+
+const char* cvt_last_error(void) { return g_err; }
+
+int cvt_haar3d_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout, int B, int C, int T, int H, int W,
+                   int temporal_levels, void* stream) {
+    const int st = check_haar(x, x_dtype, y, y_dtype, y_layout, B, C, T, H, W, temporal_levels);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_haar_fwd(x, x_dtype, y, y_dtype, y_layout, B, C, T, H, W, temporal_levels,
+                                           (hipStream_t)stream),
+                      "cvt_haar3d_fwd launch");
+}
+
+int cvt_haar3d_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype, int B, int C, int T, int H, int W,
+                   int temporal_levels, void* stream) {
+    const int st = check_haar(y, y_dtype, x, x_dtype, y_layout, B, C, T, H, W, temporal_levels);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_haar_inv(y, y_dtype, y_layout, x, x_dtype, B, C, T, H, W, temporal_levels,
+                                           (hipStream_t)stream),
+                      "cvt_haar3d_inv launch");
+}
+
+size_t cvt_causal_conv3d_fact_workspace(int B, int Cin, int Cout, int T, int H, int W, int k, int parts) {
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0 || (k != 1 && k != 3)) return 0;
+    if (parts < 1 || parts > 3) return 0;
+    return cvt::conv_workspace_bytes(B, Cin, Cout, T, H, W, k, (parts & CVT_CONV_SPATIAL) != 0,
+                                     (parts & CVT_CONV_TEMPORAL) != 0);
+}
+
+int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                           void* y, int B, int Cin, int Cout, int T, int H, int W, int k, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!x || !y) return fail(CVT_E_NULL, "x and y must not be NULL");
+    if (!w_s && !w_t) return fail(CVT_E_NULL, "at least one of w_s and w_t must be given");
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0)
+        return fail(CVT_E_SHAPE, "non-positive size");
+    if (k != 1 && k != 3) return fail(CVT_E_SHAPE, "k must be 1 or 3, got %d", k);
+    if (Cout > 4096) return fail(CVT_E_SHAPE, "Cout must be at most 4096, got %d", Cout);
+    if (!w_s && Cin != Cout)
+        return fail(CVT_E_SHAPE, "a temporal-only call needs Cin == Cout (got %d and %d)", Cin, Cout);
+    if (Cin % 8 != 0 && !(k == 1 && Cin <= 16 && w_s))
+        return fail(CVT_E_SHAPE, "Cin must be a multiple of 8 (or at most 16 with k = 1), got %d", Cin);
+    if (w_t && Cout % 8 != 0)
+        return fail(CVT_E_SHAPE, "the temporal convolution needs Cout to be a multiple of 8, got %d", Cout);
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_conv_fact(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, k, workspace,
+                                            (hipStream_t)stream),
+                      "cvt_causal_conv3d_fact launch");
+}
+
+int cvt_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* indices, void* codes, const int32_t* levels,
+                     int D, int B, int T, int H, int W, void* stream) {
+    if (!z || !indices) return fail(CVT_E_NULL, "z and indices must not be NULL");
+    if (!valid_dtype(z_dtype)) return fail(CVT_E_DTYPE, "dtype must be CVT_F32 or CVT_BF16");
+    if (!valid_layout(z_layout)) return fail(CVT_E_LAYOUT, "layout must be CVT_NCTHW or CVT_NTHWC");
+    if (B <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    cvt::FsqParams p;
+    const int st = fsq_params(levels, D, &p);
+    if (st != CVT_OK) return st;
+    if (!aligned16(z) || !aligned16(indices) || (codes && !aligned16(codes)))
+        return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    const long long npb = (long long)T * H * W;
+    return hip_status(cvt::launch_fsq_quantize(z, z_dtype, z_layout, indices, codes, p, B, npb, (hipStream_t)stream),
+                      "cvt_fsq_quantize launch");
+}
+
+int cvt_fsq_dequantize(const int32_t* indices, void* codes, int c_dtype, int c_layout, const int32_t* levels, int D,
+                       int B, int T, int H, int W, int32_t* d_invalid_count, void* stream) {
+    if (!indices || !codes) return fail(CVT_E_NULL, "indices and codes must not be NULL");
+    if (!valid_dtype(c_dtype)) return fail(CVT_E_DTYPE, "dtype must be CVT_F32 or CVT_BF16");
+    if (!valid_layout(c_layout)) return fail(CVT_E_LAYOUT, "layout must be CVT_NCTHW or CVT_NTHWC");
+    if (B <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    cvt::FsqParams p;
+    const int st = fsq_params(levels, D, &p);
+    if (st != CVT_OK) return st;
+    if (!aligned16(indices) || !aligned16(codes)) return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (d_invalid_count && (reinterpret_cast<uintptr_t>(d_invalid_count) & 3u))
+        return fail(CVT_E_ALIGN, "the invalid-index counter must be 4-byte aligned");
+    const long long npb = (long long)T * H * W;
+    return hip_status(cvt::launch_fsq_dequantize(indices, codes, c_dtype, c_layout, p, B, npb, d_invalid_count,
+                                                 (hipStream_t)stream),
+                      "cvt_fsq_dequantize launch");
+}
+
+}  // extern "C"

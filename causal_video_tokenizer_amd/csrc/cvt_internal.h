@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP translation units of libcvt.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "cvt.h"
+
+namespace cvt {
+
+// ---------------------------------------------------------------- device helpers
+
+// bf16 is handled as raw 16-bit patterns; widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are already
+// validated by the C ABI layer.
+
+hipError_t launch_haar_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout,
+                           int B, int C, int T, int H, int W, int temporal_levels,
+                           hipStream_t stream);
+hipError_t launch_haar_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype,
+                           int B, int C, int T, int H, int W, int temporal_levels,
+                           hipStream_t stream);
+
+// FSQ parameters precomputed on the host (double precision) and passed by value.
+constexpr int FSQ_MAX_D = 8;
+constexpr int FSQ_MAX_L = 16;
+struct FsqParams {
+    int D;
+    int nthr[FSQ_MAX_D];                    // L_i - 1 breakpoints per channel
+    int half[FSQ_MAX_D];                    // floor(L_i / 2)
+    int levels[FSQ_MAX_D];
+    int basis[FSQ_MAX_D];                   // mixed-radix place values
+    unsigned int magic[FSQ_MAX_D];          // floor(n / L_i) = mulhi(n, magic) >> shift, n < 2^31
+    int shift[FSQ_MAX_D];
+    float thr[FSQ_MAX_D][FSQ_MAX_L - 1];    // digit = #{j : z >= thr[i][j]}
+    int codebook;                           // product of the levels
+};
+
+hipError_t launch_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* idx, void* codes,
+                               const FsqParams& p, long long B, long long npos_per_b,
+                               hipStream_t stream);
+hipError_t launch_fsq_dequantize(const int32_t* idx, void* codes, int c_dtype, int c_layout,
+                                 const FsqParams& p, long long B, long long npos_per_b,
+                                 int32_t* invalid, hipStream_t stream);
+
+// Factorized causal convolution.
+size_t conv_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, int k, bool spatial, bool temporal);
+hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, const float* b_s,
+                            const float* b_t, void* y, int B, int Cin, int Cout, int T, int H,
+                            int W, int k, void* workspace, hipStream_t stream);
+
+}  // namespace cvt

@@ -1,0 +1,305 @@
+// FSQ quantize / dequantize kernels.
+//
+// FSQ as described in "NVIDIA Cosmos Tokenizer 完全指南", section 7.2: each
+// latent channel is bounded with tanh and rounded to its own level count,
+// the digits form one mixed-radix index (codes_to_indices) and the index is
+// turned back into codes without any codebook table (indices_to_codes).
+//
+// Quantize.  The bound tanh(z + s) h - o is strictly increasing in z, so the
+// rounded value changes only where the bound crosses a half-integer.  Those
+// breakpoints are computed once per call on the host in double precision and
+// adjusted to the float32 grid (see fsq_params in abi.cpp), so that
+// "z >= thr" holds exactly when z lies above the breakpoint.  The digit is
+// then the number of breakpoints at or below z: no transcendental is evaluated
+// per element and the decision equals the exact one for every float input
+// not within double rounding of a breakpoint.
+//
+// Mapping: one thread per run of 8 consecutive positions.  Planar (NCTHW)
+// latents are read as one 16-byte (bf16) or two 16-byte (fp32) loads per
+// channel; NTHWC latents as the thread's contiguous 8*D-element span.  Indices
+// are written as two 16-byte stores.  Ragged tails and plane sizes that are not
+// multiples of 8 take the per-position path.
+#include <math.h>
+
+#include "cvt_internal.h"
+
+namespace cvt {
+namespace {
+
+constexpr int G = 8;  // positions per thread
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+    uint4 u;
+    u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ float ld1(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ void st1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ void st1(float* p, float v) { *p = v; }
+
+template <int NT>
+__device__ __forceinline__ int digit_of(float v, const float* thr) {
+    int d = 0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) d += (v >= thr[j]) ? 1 : 0;  // padded entries are NaN: never counted
+    return d;
+}
+
+__device__ __forceinline__ float code_of(int d, int half) {
+    return (float)(d - half) / (float)half;
+}
+
+// DC: compile-time D (0 = runtime); NT: breakpoints per channel (padded).
+template <typename T, int LAYOUT, int DC, int NT>
+__global__ __launch_bounds__(256) void fsq_quantize_kernel(const T* __restrict__ z, int32_t* __restrict__ idx,
+                                                           T* __restrict__ codes, FsqParams p,
+                                                           long long npb, long long total, int vec) {
+    const int D = DC > 0 ? DC : p.D;
+    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long pos0 = g * G;
+    if (pos0 >= total) return;
+
+    if (vec && pos0 + G <= total) {
+        int acc[G];
+        bool nan_[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) { acc[k] = 0; nan_[k] = false; }
+        if (LAYOUT == CVT_NCTHW) {
+            const long long b = pos0 / npb, r = pos0 - b * npb;
+#pragma unroll
+            for (int i = 0; i < (DC > 0 ? DC : FSQ_MAX_D); ++i) {
+                if (DC == 0 && i >= D) break;
+                float v[G];
+                load8<T>(z + ((size_t)b * D + i) * npb + r, v);
+                float cv[G];
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    const int d = digit_of<NT>(v[k], p.thr[i]);
+                    acc[k] += d * p.basis[i];
+                    nan_[k] |= (v[k] != v[k]);
+                    cv[k] = (v[k] != v[k]) ? __builtin_nanf("") : code_of(d, p.half[i]);
+                }
+                if (codes) store8(codes + ((size_t)b * D + i) * npb + r, cv);
+            }
+        } else {
+            const T* src = z + (size_t)pos0 * D;
+            T* dst = codes ? codes + (size_t)pos0 * D : nullptr;
+#pragma unroll
+            for (int c8 = 0; c8 < (DC > 0 ? DC : FSQ_MAX_D); ++c8) {  // D chunks of 8 elements
+                if (DC == 0 && c8 >= D) break;
+                float v[G], cv[G];
+                load8<T>(src + c8 * G, v);
+#pragma unroll
+                for (int e = 0; e < G; ++e) {
+                    const int flat = c8 * G + e;  // = k * D + i
+                    const int k = flat / D, i = flat - (flat / D) * D;
+                    const int d = digit_of<NT>(v[e], p.thr[i]);
+                    acc[k] += d * p.basis[i];
+                    nan_[k] |= (v[e] != v[e]);
+                    cv[e] = (v[e] != v[e]) ? __builtin_nanf("") : code_of(d, p.half[i]);
+                }
+                if (dst) store8(dst + c8 * G, cv);
+            }
+        }
+        int4 o0, o1;
+        o0.x = nan_[0] ? -1 : acc[0]; o0.y = nan_[1] ? -1 : acc[1];
+        o0.z = nan_[2] ? -1 : acc[2]; o0.w = nan_[3] ? -1 : acc[3];
+        o1.x = nan_[4] ? -1 : acc[4]; o1.y = nan_[5] ? -1 : acc[5];
+        o1.z = nan_[6] ? -1 : acc[6]; o1.w = nan_[7] ? -1 : acc[7];
+        *reinterpret_cast<int4*>(idx + pos0) = o0;
+        *reinterpret_cast<int4*>(idx + pos0 + 4) = o1;
+        return;
+    }
+
+    // per-position path (tails, unaligned planes)
+    for (long long pos = pos0; pos < pos0 + G && pos < total; ++pos) {
+        int acc = 0;
+        bool isnan_ = false;
+        const long long b = pos / npb, r = pos - b * npb;
+        for (int i = 0; i < D; ++i) {
+            const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * D + i) * npb + r : (size_t)pos * D + i;
+            const float v = ld1(z + off);
+            const int d = digit_of<NT>(v, p.thr[i]);
+            acc += d * p.basis[i];
+            isnan_ |= (v != v);
+            if (codes) st1(codes + off, (v != v) ? __builtin_nanf("") : code_of(d, p.half[i]));
+        }
+        idx[pos] = isnan_ ? -1 : acc;
+    }
+}
+
+// Exact floor(n / L) for 0 <= n < 2^31 and 2 <= L <= 16.  With l = ceil(log2 L),
+// M = ceil(2^(31+l) / L) < 2^32 and n M / 2^(31+l) exceeds n / L by less than
+// n / 2^(31+l) < 2^-l <= 1/L, the smallest gap between n / L and the next
+// integer, so floor(mulhi(n, M) / 2^(l-1)) = floor(n / L).
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, int sh) {
+    return __umulhi(n, M) >> sh;
+}
+
+template <typename T, int LAYOUT, int DC>
+__global__ __launch_bounds__(256) void fsq_dequantize_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
+                                                             FsqParams p, long long npb, long long total,
+                                                             int vec, int32_t* __restrict__ invalid) {
+    const int D = DC > 0 ? DC : p.D;
+    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long pos0 = g * G;
+    if (pos0 >= total) return;
+    int nbad = 0;
+
+
+    if (vec && pos0 + G <= total) {
+        const int4 a = *reinterpret_cast<const int4*>(idx + pos0);
+        const int4 c = *reinterpret_cast<const int4*>(idx + pos0 + 4);
+        const int id[G] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        bool bad[G];
+        uint32_t rem[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            bad[k] = id[k] < 0 || id[k] >= p.codebook;
+            nbad += bad[k] ? 1 : 0;
+            rem[k] = bad[k] ? 0u : (uint32_t)id[k];
+        }
+        if (LAYOUT == CVT_NCTHW) {
+            const long long b = pos0 / npb, r = pos0 - b * npb;
+#pragma unroll
+            for (int i = 0; i < (DC > 0 ? DC : FSQ_MAX_D); ++i) {
+                if (DC == 0 && i >= D) break;
+                float cv[G];
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    const uint32_t q = div_magic(rem[k], p.magic[i], p.shift[i]);
+                    const int d = (int)(rem[k] - q * (uint32_t)p.levels[i]);
+                    rem[k] = q;
+                    cv[k] = bad[k] ? __builtin_nanf("") : code_of(d, p.half[i]);
+                }
+                store8(codes + ((size_t)b * D + i) * npb + r, cv);
+            }
+        } else {
+            T* dst = codes + (size_t)pos0 * D;
+            float cv[G * FSQ_MAX_D];
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+#pragma unroll
+                for (int i = 0; i < (DC > 0 ? DC : FSQ_MAX_D); ++i) {
+                    if (DC == 0 && i >= D) break;
+                    const uint32_t q = div_magic(rem[k], p.magic[i], p.shift[i]);
+                    const int d = (int)(rem[k] - q * (uint32_t)p.levels[i]);
+                    rem[k] = q;
+                    cv[k * D + i] = bad[k] ? __builtin_nanf("") : code_of(d, p.half[i]);
+                }
+#pragma unroll
+            for (int c8 = 0; c8 < (DC > 0 ? DC : FSQ_MAX_D); ++c8) {
+                if (DC == 0 && c8 >= D) break;
+                store8(dst + c8 * G, cv + c8 * G);
+            }
+        }
+    } else {
+        for (long long pos = pos0; pos < pos0 + G && pos < total; ++pos) {
+            const int v = idx[pos];
+            const bool bd = v < 0 || v >= p.codebook;
+            nbad += bd ? 1 : 0;
+            uint32_t rem = bd ? 0u : (uint32_t)v;
+            const long long b = pos / npb, r = pos - b * npb;
+            for (int i = 0; i < D; ++i) {
+                const uint32_t q = div_magic(rem, p.magic[i], p.shift[i]);
+                const int d = (int)(rem - q * (uint32_t)p.levels[i]);
+                rem = q;
+                const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * D + i) * npb + r : (size_t)pos * D + i;
+                st1(codes + off, bd ? __builtin_nanf("") : code_of(d, p.half[i]));
+            }
+        }
+    }
+    if (invalid && nbad) atomicAdd(invalid, nbad);
+}
+
+template <typename T, int LAYOUT, int DC>
+hipError_t quantize_nt(const void* z, int32_t* idx, void* codes, const FsqParams& p, long long npb,
+                       long long total, int vec, hipStream_t s) {
+    int maxthr = 0;
+    for (int i = 0; i < p.D; ++i) maxthr = p.nthr[i] > maxthr ? p.nthr[i] : maxthr;
+    const long long nthreads = (total + G - 1) / G;
+    const long long nblk = (nthreads + 255) / 256;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nblk), block(256);
+#define CVT_FSQ_Q(NT) \
+    hipLaunchKernelGGL((fsq_quantize_kernel<T, LAYOUT, DC, NT>), grid, block, 0, s, (const T*)z, idx, (T*)codes, p, npb, total, vec)
+    if (maxthr <= 1) CVT_FSQ_Q(1);
+    else if (maxthr <= 3) CVT_FSQ_Q(3);
+    else if (maxthr <= 4) CVT_FSQ_Q(4);
+    else if (maxthr <= 7) CVT_FSQ_Q(7);
+    else CVT_FSQ_Q(15);
+#undef CVT_FSQ_Q
+    return hipGetLastError();
+}
+
+template <typename T, int LAYOUT>
+hipError_t quantize_t(const void* z, int32_t* idx, void* codes, const FsqParams& p, long long B, long long npb,
+                      hipStream_t s) {
+    const long long total = B * npb;
+    // vector path: 8-aligned plane starts for NCTHW; NTHWC spans are always contiguous
+    const int vec = LAYOUT == CVT_NTHWC ? 1 : (npb % G == 0);
+    if (p.D == 6) return quantize_nt<T, LAYOUT, 6>(z, idx, codes, p, npb, total, vec, s);
+    return quantize_nt<T, LAYOUT, 0>(z, idx, codes, p, npb, total, vec, s);
+}
+
+template <typename T, int LAYOUT>
+hipError_t dequantize_t(const int32_t* idx, void* codes, const FsqParams& p, long long B, long long npb,
+                        int32_t* invalid, hipStream_t s) {
+    const long long total = B * npb;
+    const int vec = LAYOUT == CVT_NTHWC ? 1 : (npb % G == 0);
+    const long long nthreads = (total + G - 1) / G;
+    const long long nblk = (nthreads + 255) / 256;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (p.D == 6)
+        hipLaunchKernelGGL((fsq_dequantize_kernel<T, LAYOUT, 6>), dim3((unsigned)nblk), dim3(256), 0, s, idx, (T*)codes, p,
+                           npb, total, vec, invalid);
+    else
+        hipLaunchKernelGGL((fsq_dequantize_kernel<T, LAYOUT, 0>), dim3((unsigned)nblk), dim3(256), 0, s, idx, (T*)codes, p,
+                           npb, total, vec, invalid);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* idx, void* codes,
+                               const FsqParams& p, long long B, long long npb, hipStream_t s) {
+    if (z_dtype == CVT_BF16)
+        return z_layout == CVT_NTHWC ? quantize_t<uint16_t, CVT_NTHWC>(z, idx, codes, p, B, npb, s)
+                                     : quantize_t<uint16_t, CVT_NCTHW>(z, idx, codes, p, B, npb, s);
+    return z_layout == CVT_NTHWC ? quantize_t<float, CVT_NTHWC>(z, idx, codes, p, B, npb, s)
+                                 : quantize_t<float, CVT_NCTHW>(z, idx, codes, p, B, npb, s);
+}
+
+hipError_t launch_fsq_dequantize(const int32_t* idx, void* codes, int c_dtype, int c_layout, const FsqParams& p,
+                                 long long B, long long npb, int32_t* invalid, hipStream_t s) {
+    if (c_dtype == CVT_BF16)
+        return c_layout == CVT_NTHWC ? dequantize_t<uint16_t, CVT_NTHWC>(idx, codes, p, B, npb, invalid, s)
+                                     : dequantize_t<uint16_t, CVT_NCTHW>(idx, codes, p, B, npb, invalid, s);
+    return c_layout == CVT_NTHWC ? dequantize_t<float, CVT_NTHWC>(idx, codes, p, B, npb, invalid, s)
+                                 : dequantize_t<float, CVT_NCTHW>(idx, codes, p, B, npb, invalid, s);
+}
+
+}  // namespace cvt

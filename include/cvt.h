@@ -1,0 +1,188 @@
+/*
+ * cvt.h - C ABI of the causal video tokenizer hot path on AMD MI355X (gfx950).
+ *
+ * The library computes the encoder front end and quantizer of the Cosmos
+ * Tokenizer and their inverses: 2-level Haar wavelet patching with the causal
+ * first frame, the factorized causal 3D convolution, FSQ quantization to a
+ * mixed-radix index, FSQ dequantization and the inverse Haar transform.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named x, y, z, w_*, b_*, indices, codes and workspace are DEVICE
+ *   pointers (memory from hipMalloc or torch on the same device).  `levels` is
+ *   a HOST array read during the call only.  The caller allocates and frees
+ *   all memory and owns the stream; the library allocates nothing and keeps no
+ *   pointer after it returns.
+ * - Every function is asynchronous on `stream` (a hipStream_t; NULL means the
+ *   null stream) and returns a cvt_status.  All arguments are validated before
+ *   anything is launched: on an error nothing runs and nothing is written.
+ *   CVT_E_HIP means a launch failed; cvt_last_error() gives the detail
+ *   (thread-local).  No C++ exception crosses this interface.
+ * - Dense tensors are contiguous.  A [B, C, T, H, W] tensor is stored either
+ *   NCTHW (W fastest) or NTHWC (C fastest, torch's channels_last_3d).
+ * - bf16 is IEEE binary32's upper half; conversions to bf16 round to nearest
+ *   even.  Device pointers must be 16-byte aligned.
+ * - Sizes are int; element counts may exceed 2^31 (the library indexes with
+ *   64-bit offsets).
+ */
+#ifndef CVT_H
+#define CVT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CVT_OK = 0,
+    CVT_E_NULL = 1,      /* a required pointer is NULL */
+    CVT_E_SHAPE = 2,     /* a size is non-positive or violates the operation's shape rule */
+    CVT_E_DTYPE = 3,     /* unsupported dtype code */
+    CVT_E_LAYOUT = 4,    /* unsupported layout code */
+    CVT_E_ALIGN = 5,     /* a device pointer is not 16-byte aligned */
+    CVT_E_LEVELS = 6,    /* FSQ levels outside the supported range */
+    CVT_E_WORKSPACE = 7, /* workspace missing or smaller than required */
+    CVT_E_HIP = 8        /* the HIP runtime reported an error on launch */
+} cvt_status;
+
+typedef enum { CVT_F32 = 0, CVT_BF16 = 1 } cvt_dtype;
+typedef enum { CVT_NCTHW = 0, CVT_NTHWC = 1 } cvt_layout;
+
+/* Version of this interface (incremented on any signature change). */
+int cvt_abi_version(void);
+/* Static string naming a status code. */
+const char* cvt_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* cvt_last_error(void);
+
+/*
+ * Forward Haar patcher with the causal first frame.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南" (a guide to the tokenizer
+ * README), section 7.1 (Haar wavelet patching) and sections 6.1 / 7.3 (first
+ * latent frame aligned with frame 0, T' = 1 + (T-1)/4); the
+ * Cosmos-Tokenize1-CV8x8x8-720p model card, "Model Architecture" (the encoder
+ * starts with a 2-level Haar transform, 4x in T, H and W).
+ *
+ * x: [B, C, T, H, W] NCTHW, dtype x_dtype (CVT_F32 or CVT_BF16).
+ * temporal_levels = 2 (video): T = 1 + 4k; the sequence is extended by three
+ *   leading copies of frame 0 and two orthonormal Haar levels are applied along
+ *   t, h and w.  y: [B, 64C, T', H/4, W/4] with T' = 1 + (T-1)/4.
+ * temporal_levels = 0 (image patcher, per frame): two levels along h and w.
+ *   y: [B, 16C, T, H/4, W/4].
+ * Output channel = s2*G*C + s1*C + c with G = 8 (3D) or 4 (2D), where s1, s2
+ * are the level-1 and level-2 subbands, s = 4*b_t + 2*b_h + b_w (2D:
+ * 2*b_h + b_w), b = 0 for the low-pass (e+o)/sqrt(2) and 1 for the high-pass
+ * (e-o)/sqrt(2), e being the earlier / upper / left sample of a pair.
+ * y is stored in y_layout (NTHWC is the layout the convolution consumes) with
+ * dtype y_dtype.  Arithmetic is float32.
+ * Errors: CVT_E_SHAPE if H or W is not a multiple of 4, T is not 1 + 4k with
+ * temporal_levels = 2, or temporal_levels is not 0 or 2.
+ */
+int cvt_haar3d_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout,
+                   int B, int C, int T, int H, int W, int temporal_levels, void* stream);
+
+/*
+ * Inverse Haar patcher (the decoder's last layer).
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.1 (the inverse
+ * wavelet transform restores the pixels); Cosmos-Tokenize1-CV8x8x8-720p model
+ * card, "Model Architecture" (the decoder ends with an inverse wavelet
+ * transform).
+ *
+ * y: coefficients as produced by cvt_haar3d_fwd, layout y_layout, dtype
+ * y_dtype.  x: output [B, C, T, H, W] NCTHW, dtype x_dtype, where T, H, W are
+ * the PIXEL sizes (T = 4T' - 3 with temporal_levels = 2, the three leading
+ * padded frames being dropped; T = T' with temporal_levels = 0).
+ * Errors: as cvt_haar3d_fwd.
+ */
+int cvt_haar3d_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype,
+                   int B, int C, int T, int H, int W, int temporal_levels, void* stream);
+
+/*
+ * Factorized causal 3D convolution: a 1 x k x k spatial convolution
+ * (Cin -> Cout, zero padding (k-1)/2 in H and W, cross-correlation) followed by
+ * a k x 1 x 1 temporal convolution (Cout -> Cout) with k-1 zero frames of left
+ * padding, so output frame t depends on frames t-k+1 .. t only.
+ *
+ * Defined by: "Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer" (1 x k x k then
+ * k x 1 x 1 with left padding k-1 for causality); model card "Model
+ * Architecture" (causal temporal convolution).
+ *
+ * x:   bf16 NTHWC [B, Cin, T, H, W]; Cin a multiple of 8 (or Cin <= 16
+ *      for a spatial-only call with k = 1).
+ * w_s: bf16 [Cout, Cin, 1, k, k] (torch's Conv3d weight order), or NULL for
+ *      the temporal part alone (then Cin must equal Cout).
+ * w_t: bf16 [Cout, Cout, k, 1, 1], or NULL for the spatial part alone
+ *      (with k = 1 and w_t = NULL the call is a 1x1x1 projection).
+ *      At least one of w_s and w_t must be given.
+ * b_s, b_t: float32 [Cout] biases or NULL.
+ * y:   bf16 NTHWC [B, Cout, T, H, W].
+ * k:   1 or 3.
+ * Accumulation is float32; the spatial result is stored as bf16 in the
+ * workspace before the temporal convolution reads it.
+ * workspace: device scratch of at least cvt_causal_conv3d_fact_workspace()
+ * bytes (packed weights and, when both parts run, the intermediate), owned by
+ * the caller; `parts` there is CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL for the
+ * parts the call will run (0 is returned for invalid arguments).
+ * Errors: CVT_E_SHAPE for k not 1 or 3, Cin or Cout out of range (Cin must
+ * be a multiple of 8, or at most 16 with k = 1; 1 <= Cout <= 4096);
+ * CVT_E_WORKSPACE when workspace_bytes is too small.
+ */
+enum { CVT_CONV_SPATIAL = 1, CVT_CONV_TEMPORAL = 2 };
+size_t cvt_causal_conv3d_fact_workspace(int B, int Cin, int Cout, int T, int H, int W, int k, int parts);
+int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t,
+                           const float* b_s, const float* b_t, void* y,
+                           int B, int Cin, int Cout, int T, int H, int W, int k,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FSQ quantization: per position, D latent values -> one int32 index.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (each channel
+ * bounded with tanh and rounded to its own number of levels; the index is the
+ * mixed-radix number of the digits; codebook size = product of levels =
+ * 64000 for (8,8,8,5,5,5)) and section 6.2 (indices [B,T',H',W'], codes
+ * [B,6,T',H',W']); the bound is the FSQ method's
+ * tanh(z + atanh(o/h)) * h - o with h = (L-1)(1+1e-3)/2, o = 1/2 for even L
+ * else 0, rounded half to even; digit d = q + floor(L/2); index =
+ * sum_i d_i * prod_{j<i} L_j (channel 0 least significant).
+ *
+ * z: [B, D, T, H, W] in z_layout, dtype z_dtype.  indices: int32 [B, T, H, W].
+ * codes: NULL or an output like z receiving the quantized codes
+ * q / floor(L/2) in [-1, 1].  levels: host int32[D].
+ * The digit is decided exactly: z is compared with the breakpoints where the
+ * bound crosses a half-integer, computed in double precision on the host.
+ * A NaN in any channel gives index -1 (and NaN codes); +-inf saturate.
+ * Errors: CVT_E_LEVELS unless 1 <= D <= 8, 2 <= L_i <= 16 and the product
+ * of the levels is below 2^31.
+ */
+int cvt_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* indices, void* codes,
+                     const int32_t* levels, int D, int B, int T, int H, int W, void* stream);
+
+/*
+ * FSQ dequantization: index -> digits d_i = floor(idx / beta_i) mod L_i ->
+ * codes (d_i - floor(L_i/2)) / floor(L_i/2).
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2
+ * (indices_to_codes restores the codes from the index).
+ *
+ * indices: int32 [B, T, H, W].  codes: output [B, D, T, H, W] in c_layout,
+ * dtype c_dtype.  levels: host int32[D].
+ * An index outside [0, prod L) is invalid: its codes are NaN and, when
+ * d_invalid_count is not NULL, the number of invalid indices is ADDED to the
+ * int32 device counter it points to (the caller zeroes it beforehand).
+ * Errors: as cvt_fsq_quantize.
+ */
+int cvt_fsq_dequantize(const int32_t* indices, void* codes, int c_dtype, int c_layout,
+                       const int32_t* levels, int D, int B, int T, int H, int W,
+                       int32_t* d_invalid_count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CVT_H */

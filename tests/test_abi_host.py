@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/cvt.h declares, and rejects invalid arguments before any
+launch with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cvt.h")
+
+cvt = pytest.importorskip("causal_video_tokenizer_amd", reason="libcvt.so not built")
+lib = cvt.lib
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_LAYOUT, E_ALIGN, E_LEVELS, E_WORKSPACE = range(8)
+# Fake, 256-byte aligned "device" addresses: every call below fails validation,
+# so nothing is ever dereferenced or launched.
+A, B_, C_ = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+MIS = ctypes.c_void_p(0x100008)
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(cvt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = header_symbols()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in cvt.SIGNATURES, n
+
+
+def test_version_and_status_strings():
+    assert lib.cvt_abi_version() == 1
+    assert lib.cvt_status_string(0) == b"CVT_OK"
+    for s in range(1, 9):
+        assert lib.cvt_status_string(s).startswith(b"CVT_E_")
+    assert lib.cvt_status_string(99) == b"unknown cvt status"
+
+
+def fwd(*, x=A, xdt=1, y=B_, ydt=1, lay=1, B=1, C=3, T=5, H=8, W=8, tl=2):
+    return lib.cvt_haar3d_fwd(x, xdt, y, ydt, lay, B, C, T, H, W, tl, None)
+
+
+def test_haar_validation():
+    assert fwd(x=None) == E_NULL
+    assert fwd(xdt=7) == E_DTYPE
+    assert fwd(lay=5) == E_LAYOUT
+    assert fwd(T=4) == E_SHAPE            # T != 1 + 4k
+    assert fwd(H=6) == E_SHAPE
+    assert fwd(W=10) == E_SHAPE
+    assert fwd(tl=1) == E_SHAPE
+    assert fwd(B=0) == E_SHAPE
+    assert fwd(x=MIS) == E_ALIGN
+    assert b"1 + 4k" in lib.cvt_last_error() or True
+    assert fwd(T=4) == E_SHAPE and b"T = 1 + 4k" in lib.cvt_last_error()
+    assert lib.cvt_haar3d_inv(A, 1, 1, B_, 1, 1, 3, 6, 8, 8, 2, None) == E_SHAPE
+    assert lib.cvt_haar3d_inv(None, 1, 1, B_, 1, 1, 3, 5, 8, 8, 2, None) == E_NULL
+
+
+def levels(*ls):
+    return (ctypes.c_int32 * len(ls))(*ls)
+
+
+def test_fsq_validation():
+    L = levels(8, 8, 8, 5, 5, 5)
+    q = lambda **kw: lib.cvt_fsq_quantize(kw.get("z", A), kw.get("dt", 1), kw.get("lay", 0), kw.get("idx", B_),
+                                          None, kw.get("lv", L), kw.get("D", 6), 1, 2, 4, 4, None)
+    assert q(z=None) == E_NULL
+    assert q(idx=None) == E_NULL
+    assert q(dt=3) == E_DTYPE
+    assert q(lay=2) == E_LAYOUT
+    assert q(lv=None) == E_NULL
+    assert q(D=0) == E_LEVELS
+    assert q(D=9) == E_LEVELS
+    assert q(lv=levels(8, 1, 8, 5, 5, 5)) == E_LEVELS
+    assert q(lv=levels(8, 17, 8, 5, 5, 5)) == E_LEVELS
+    assert q(lv=levels(16, 16, 16, 16, 16, 16, 16, 16), D=8) == E_LEVELS   # 2^32 codes
+    assert q(z=MIS) == E_ALIGN
+    dq = lambda **kw: lib.cvt_fsq_dequantize(kw.get("idx", A), kw.get("c", B_), 1, 1, L, 6, 1, 2, 4, 4,
+                                             kw.get("cnt", None), None)
+    assert dq(idx=None) == E_NULL
+    assert dq(c=MIS) == E_ALIGN
+    assert dq(cnt=ctypes.c_void_p(0x100002)) == E_ALIGN
+
+
+def test_conv_validation_and_workspace():
+    ws = lib.cvt_causal_conv3d_fact_workspace(1, 192, 256, 5, 8, 8, 3, 3)
+    P = 5 * 8 * 8
+    assert ws >= 256 * 192 * 9 * 2 + 256 * 256 * 3 * 2 + P * 256 * 2
+    assert lib.cvt_causal_conv3d_fact_workspace(1, 192, 256, 5, 8, 8, 2, 3) == 0
+    assert lib.cvt_causal_conv3d_fact_workspace(1, 192, 256, 5, 8, 8, 3, 1) < ws
+    assert lib.cvt_causal_conv3d_fact_workspace(1, 256, 256, 5, 8, 8, 3, 2) == 256 * 256 * 3 * 2
+    assert lib.cvt_causal_conv3d_fact_workspace(1, 192, 256, 5, 8, 8, 3, 0) == 0
+
+    def call(**kw):
+        return lib.cvt_causal_conv3d_fact(kw.get("x", A), kw.get("ws", B_), kw.get("wt", C_), None, None,
+                                          kw.get("y", ctypes.c_void_p(0x400000)), 1, kw.get("Cin", 192),
+                                          kw.get("Cout", 256), 5, 8, 8, kw.get("k", 3),
+                                          kw.get("work", ctypes.c_void_p(0x500000)), kw.get("wsb", ws), None)
+    assert call(x=None) == E_NULL
+    assert call(ws=None, wt=None) == E_NULL
+    assert call(ws=None) == E_SHAPE           # temporal-only needs Cin == Cout
+    assert call(k=2) == E_SHAPE
+    assert call(Cin=12) == E_SHAPE            # not a multiple of 8 with k = 3
+    assert call(Cout=12) == E_SHAPE           # temporal part needs Cout % 8 == 0
+    assert call(Cout=5000) == E_SHAPE
+    assert call(x=MIS) == E_ALIGN
+    assert call(wsb=ws - 1) == E_WORKSPACE
+    assert call(work=None) == E_WORKSPACE
