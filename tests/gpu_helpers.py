@@ -3,7 +3,8 @@ device, reading results back, and the comparison criteria.
 
 Criteria (applied element by element):
 * float32 stages: |g - o| <= tol * (|o| + rms(o)), tol = 1e-5 for Haar;
-* bf16 outputs of exact stages (Haar): |g - bf16(o)| <= 1 bf16 ulp of bf16(o);
+* bf16 outputs of exact stages (Haar): |g - bf16(o)| <= 1 bf16 ulp of bf16(o)
+  (or |g - o| <= 1e-12 rms(o), the oracle's own rounding level);
 * bf16 convolution outputs: |g - o| <= 2e-2 * (|o| + rms(o));
 * integer outputs (FSQ indices, digits): bit-exact.
 The reference o is always the float64 oracle evaluated on the same bits.
@@ -75,13 +76,17 @@ def assert_rel(g, o, tol, what):
 
 def assert_bf16_ulp(g_bits, o, what, max_ulp=1):
     """g_bits: GPU bf16 bits; o: float64 oracle values.  Each GPU value must be
-    within max_ulp bf16 ulps of the oracle rounded to bf16."""
+    within max_ulp bf16 ulps of the oracle rounded to bf16, or within
+    1e-12 * rms(o) of it: the oracle's own float64 rounding (it multiplies by
+    1/sqrt(2) per level) leaves ~1e-16 where the exact coefficient is 0, which
+    the float32 butterflies return exactly."""
     ob = obf16.encode(o)
     gv = obf16.decode(g_bits)
     ov = obf16.decode(ob)
     diff = np.abs(gv - ov)
     u = obf16.ulp(ob)
-    nbad = int(np.sum(diff > max_ulp * u))
+    floor = 1e-12 * float(np.sqrt(np.mean(np.square(o)))) if np.size(o) else 0.0
+    nbad = int(np.sum((diff > max_ulp * u) & (np.abs(gv - o) > floor)))
     nne = int(np.sum(g_bits != ob))
     log(f"  {what}: n={o.size} not-identical={nne} ({nne / max(o.size, 1):.2e}) beyond {max_ulp} ulp={nbad}")
     assert nbad == 0, f"{what}: {nbad} elements beyond {max_ulp} bf16 ulp"

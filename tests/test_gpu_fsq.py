@@ -118,9 +118,15 @@ def test_dequantize_all_indices_and_invalid(layout, dtype):
     same = (gc == oc) | (np.isnan(gc) & np.isnan(oc))
     assert same.all()
     assert int(cnt.item()) == bad == 5
-    # quantize(dequantize(i)) = i for every valid index
+    # every valid index survives quantize(lattice centre of its codes): the latent
+    # whose bound is exactly the integer q = code * floor(L/2), via the inverse of tanh
     valid = idx[..., :64000]
-    z = torch.from_numpy(oc[..., :64000].astype(np.float32)).cuda()
+    zc = np.empty_like(oc[..., :64000])
+    for i, L in enumerate(LEVELS):
+        h, o, s = ofsq.constants(L)
+        q = oc[:, i, ..., :64000] * (L // 2)
+        zc[:, i] = np.arctanh((q + o) / h) - s
+    z = torch.from_numpy(zc.astype(np.float32)).cuda()
     assert np.array_equal(cvt.fsq_quantize(z).cpu().numpy(), valid)
 
 
