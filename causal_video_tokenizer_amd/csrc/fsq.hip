@@ -60,6 +60,42 @@ __device__ __forceinline__ float ld1(const float* p) { return *p; }
 __device__ __forceinline__ void st1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
 
+// Level-set descriptors.  Runtime<D>: everything read from FsqParams.  Default:
+// the levels (8,8,8,5,5,5) of the pages, with compile-time breakpoint counts,
+// place values and power-of-two code scales (thresholds stay runtime values).
+struct RuntimeLevels {
+    static constexpr bool fixed = false;
+};
+struct DefaultLevels {
+    static constexpr bool fixed = true;
+    static constexpr int D = 6;
+    __device__ static constexpr int L(int i) { return i < 3 ? 8 : 5; }
+    __device__ static constexpr int nthr(int i) { return L(i) - 1; }
+    __device__ static constexpr int half(int i) { return L(i) / 2; }
+    __device__ static constexpr float inv_half(int i) { return i < 3 ? 0.25f : 0.5f; }
+    __device__ static constexpr int basis(int i) {
+        return i == 0 ? 1 : i == 1 ? 8 : i == 2 ? 64 : i == 3 ? 512 : i == 4 ? 2560 : 12800;
+    }
+    static constexpr int codebook = 64000;
+};
+
+template <int NT>
+__device__ __forceinline__ int digit_exact(float v, const float* thr) {
+    int d = 0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) d += (v >= thr[j]) ? 1 : 0;
+    return d;
+}
+
+// NaN for a NaN input, else +0: added to a code it marks NaN latents without a branch
+// (+-inf inputs keep their saturated codes).
+__device__ __forceinline__ float nan_or_zero(float x) { return (x != x) ? __builtin_nanf("") : 0.0f; }
+
+// Digit of channel i under the default levels (i is a constant after unrolling).
+__device__ __forceinline__ int digit_default(int i, float x, const FsqParams& p) {
+    return i < 3 ? digit_exact<7>(x, p.thr[i]) : digit_exact<4>(x, p.thr[i]);
+}
+
 template <int NT>
 __device__ __forceinline__ int digit_of(float v, const float* thr) {
     int d = 0;
@@ -70,6 +106,84 @@ __device__ __forceinline__ int digit_of(float v, const float* thr) {
 
 __device__ __forceinline__ float code_of(int d, int half) {
     return (float)(d - half) / (float)half;
+}
+
+// Quantize with the default levels: 8 positions per thread, compile-time
+// breakpoint counts (7 for L = 8, 4 for L = 5); codes only when CODES.
+template <typename T, int LAYOUT, bool CODES>
+__global__ __launch_bounds__(256) void fsq_quantize_default_kernel(const T* __restrict__ z, int32_t* __restrict__ idx,
+                                                                   T* __restrict__ codes, FsqParams p, long long npb,
+                                                                   long long total) {
+    using LV = DefaultLevels;
+    constexpr int D = LV::D;
+    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long pos0 = g * G;
+    if (pos0 >= total) return;
+    int acc[G];
+    bool nan_[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) { acc[k] = 0; nan_[k] = false; }
+    if (pos0 + G <= total) {
+        if (LAYOUT == CVT_NCTHW) {
+            const long long b = pos0 / npb, r = pos0 - b * npb;
+            float v[D][G];
+#pragma unroll
+            for (int i = 0; i < D; ++i) load8<T>(z + ((size_t)b * D + i) * npb + r, v[i]);
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                float cv[G];
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    const int d = digit_default(i, v[i][k], p);
+                    acc[k] += d * LV::basis(i);
+                    nan_[k] |= (v[i][k] != v[i][k]);
+                    if (CODES) cv[k] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_or_zero(v[i][k]);
+                }
+                if (CODES) store8(codes + ((size_t)b * D + i) * npb + r, cv);
+            }
+        } else {
+            float v[D][G];  // D chunks of 8 consecutive elements = 8 positions x 6 channels
+#pragma unroll
+            for (int c8 = 0; c8 < D; ++c8) load8<T>(z + (size_t)pos0 * D + c8 * G, v[c8]);
+#pragma unroll
+            for (int c8 = 0; c8 < D; ++c8) {
+                float cv[G];
+#pragma unroll
+                for (int e = 0; e < G; ++e) {
+                    const int flat = c8 * G + e, k = flat / D, i = flat % D;
+                    const float x = v[c8][e];
+                    const int d = digit_default(i, x, p);
+                    acc[k] += d * LV::basis(i);
+                    nan_[k] |= (x != x);
+                    if (CODES) cv[e] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_or_zero(x);
+                }
+                if (CODES) store8(codes + (size_t)pos0 * D + c8 * G, cv);
+            }
+        }
+        int4 o0, o1;
+        o0.x = nan_[0] ? -1 : acc[0]; o0.y = nan_[1] ? -1 : acc[1];
+        o0.z = nan_[2] ? -1 : acc[2]; o0.w = nan_[3] ? -1 : acc[3];
+        o1.x = nan_[4] ? -1 : acc[4]; o1.y = nan_[5] ? -1 : acc[5];
+        o1.z = nan_[6] ? -1 : acc[6]; o1.w = nan_[7] ? -1 : acc[7];
+        *reinterpret_cast<int4*>(idx + pos0) = o0;
+        *reinterpret_cast<int4*>(idx + pos0 + 4) = o1;
+        return;
+    }
+    for (long long pos = pos0; pos < total; ++pos) {  // ragged tail (< 8 positions)
+        int a = 0;
+        bool isnan_ = false;
+        const long long b = pos / npb, r = pos - b * npb;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * D + i) * npb + r : (size_t)pos * D + i;
+            const float x = ld1(z + off);
+            const int d = digit_exact<7>(x, p.thr[i]);  // unused breakpoints are NaN
+            a += d * LV::basis(i);
+            isnan_ |= (x != x);
+            if (CODES) st1(codes + off, (x != x) ? __builtin_nanf("") : (float)(d - LV::half(i)) * LV::inv_half(i));
+        }
+        idx[pos] = isnan_ ? -1 : a;
+    }
 }
 
 // DC: compile-time D (0 = runtime); NT: breakpoints per channel (padded).
@@ -159,6 +273,71 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, int sh) {
     return __umulhi(n, M) >> sh;
 }
 
+// Dequantize with the default levels: compile-time radices (the compiler
+// divides by 8 and 5 with shifts / multiply-high) and power-of-two code scales.
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(256) void fsq_dequantize_default_kernel(const int32_t* __restrict__ idx,
+                                                                     T* __restrict__ codes, long long npb,
+                                                                     long long total, int32_t* __restrict__ invalid) {
+    using LV = DefaultLevels;
+    constexpr int D = LV::D;
+    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long pos0 = g * G;
+    if (pos0 >= total) return;
+    int nbad = 0;
+    if (pos0 + G <= total) {
+        const int4 a = *reinterpret_cast<const int4*>(idx + pos0);
+        const int4 c = *reinterpret_cast<const int4*>(idx + pos0 + 4);
+        const int id[G] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        float cv[D][G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const bool bad = (unsigned)id[k] >= (unsigned)LV::codebook;
+            nbad += bad ? 1 : 0;
+            // branchless invalid handling: the digits of 0 plus a NaN addend
+            const float nan_add = bad ? __builtin_nanf("") : 0.0f;
+            uint32_t rem = bad ? 0u : (uint32_t)id[k];
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                const uint32_t q = rem / (uint32_t)LV::L(i);
+                const int d = (int)(rem - q * (uint32_t)LV::L(i));
+                rem = q;
+                cv[i][k] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_add;
+            }
+        }
+        if (LAYOUT == CVT_NCTHW) {
+            const long long b = pos0 / npb, r = pos0 - b * npb;
+#pragma unroll
+            for (int i = 0; i < D; ++i) store8(codes + ((size_t)b * D + i) * npb + r, cv[i]);
+        } else {
+            float flat[G * D];
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+#pragma unroll
+                for (int i = 0; i < D; ++i) flat[k * D + i] = cv[i][k];
+#pragma unroll
+            for (int c8 = 0; c8 < D; ++c8) store8(codes + (size_t)pos0 * D + c8 * G, flat + c8 * G);
+        }
+    } else {
+        for (long long pos = pos0; pos < total; ++pos) {
+            const int v = idx[pos];
+            const bool bad = (unsigned)v >= (unsigned)LV::codebook;
+            nbad += bad ? 1 : 0;
+            uint32_t rem = bad ? 0u : (uint32_t)v;
+            const long long b = pos / npb, r = pos - b * npb;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                const uint32_t q = rem / (uint32_t)LV::L(i);
+                const int d = (int)(rem - q * (uint32_t)LV::L(i));
+                rem = q;
+                const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * D + i) * npb + r : (size_t)pos * D + i;
+                st1(codes + off, bad ? __builtin_nanf("") : (float)(d - LV::half(i)) * LV::inv_half(i));
+            }
+        }
+    }
+    if (invalid && nbad) atomicAdd(invalid, nbad);
+}
+
 template <typename T, int LAYOUT, int DC>
 __global__ __launch_bounds__(256) void fsq_dequantize_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
                                                              FsqParams p, long long npb, long long total,
@@ -235,6 +414,14 @@ __global__ __launch_bounds__(256) void fsq_dequantize_kernel(const int32_t* __re
     if (invalid && nbad) atomicAdd(invalid, nbad);
 }
 
+bool is_default(const FsqParams& p) {
+    static const int def[6] = {8, 8, 8, 5, 5, 5};
+    if (p.D != 6) return false;
+    for (int i = 0; i < 6; ++i)
+        if (p.levels[i] != def[i]) return false;
+    return true;
+}
+
 template <typename T, int LAYOUT, int DC>
 hipError_t quantize_nt(const void* z, int32_t* idx, void* codes, const FsqParams& p, long long npb,
                        long long total, int vec, hipStream_t s) {
@@ -261,6 +448,17 @@ hipError_t quantize_t(const void* z, int32_t* idx, void* codes, const FsqParams&
     const long long total = B * npb;
     // vector path: 8-aligned plane starts for NCTHW; NTHWC spans are always contiguous
     const int vec = LAYOUT == CVT_NTHWC ? 1 : (npb % G == 0);
+    if (is_default(p) && vec) {
+        const long long nblk = ((total + G - 1) / G + 255) / 256;
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        if (codes)
+            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, true>), dim3((unsigned)nblk), dim3(256), 0, s,
+                               (const T*)z, idx, (T*)codes, p, npb, total);
+        else
+            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, false>), dim3((unsigned)nblk), dim3(256), 0, s,
+                               (const T*)z, idx, (T*)nullptr, p, npb, total);
+        return hipGetLastError();
+    }
     if (p.D == 6) return quantize_nt<T, LAYOUT, 6>(z, idx, codes, p, npb, total, vec, s);
     return quantize_nt<T, LAYOUT, 0>(z, idx, codes, p, npb, total, vec, s);
 }
@@ -273,7 +471,10 @@ hipError_t dequantize_t(const int32_t* idx, void* codes, const FsqParams& p, lon
     const long long nthreads = (total + G - 1) / G;
     const long long nblk = (nthreads + 255) / 256;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (p.D == 6)
+    if (is_default(p) && vec)
+        hipLaunchKernelGGL((fsq_dequantize_default_kernel<T, LAYOUT>), dim3((unsigned)nblk), dim3(256), 0, s, idx,
+                           (T*)codes, npb, total, invalid);
+    else if (p.D == 6)
         hipLaunchKernelGGL((fsq_dequantize_kernel<T, LAYOUT, 6>), dim3((unsigned)nblk), dim3(256), 0, s, idx, (T*)codes, p,
                            npb, total, vec, invalid);
     else

@@ -101,172 +101,292 @@ __device__ __forceinline__ WaveTile decode_tile(int Tq, int Hq, int Wq, int nchu
     return w;
 }
 
-// NF = 4: 3D (two levels along t, h, w); NF = 1: 2D per frame.
-// CT > 0: compile-time channel count; CT = 0: runtime C.
-template <typename Tin, typename Tout, int NF, int LAYOUT, int CT>
-__global__ __launch_bounds__(64) void haar_fwd_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
-                                                      int C_rt, int T, int H, int W, int Tq, int Hq,
-                                                      int Wq, int nchunk, int stage) {
-    extern __shared__ uint32_t lds[];
-    const int C = CT > 0 ? CT : C_rt;
+// Element traits: bytes per element and 16-byte packing.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+    static constexpr int per16 = 8;  // elements per 16 bytes
+};
+template <>
+struct Elem<float> {
+    static constexpr int per16 = 4;
+};
+
+// Pack 4 (bf16: 8) consecutive floats of `v` into one 16-byte word.
+__device__ __forceinline__ uint4 pack16(const float* v, uint16_t*) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+__device__ __forceinline__ uint4 pack16(const float* v, float*) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+// Unpack one 16-byte word into 8 (bf16) or 4 (fp32) floats.
+__device__ __forceinline__ void unpack16(const uint4 u, float* v, const uint16_t*) {
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 u, float* v, const float*) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y); v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+}
+
+// Raw 4-element row segment as loaded from memory.
+template <typename T>
+struct Row4;
+template <>
+struct Row4<uint16_t> {
+    uint2 u;
+    __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ void get(float* v) const {
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    }
+};
+template <>
+struct Row4<float> {
+    float4 u;
+    __device__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+    __device__ void get(float* v) const { v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; }
+};
+
+// Forward/inverse transform of one channel's 4 x 4 x 4 (NF = 4) or 4 x 4 (NF = 1) block in place.
+template <int NF>
+__device__ __forceinline__ void block_transform(float (&v)[NF][4][4]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) packet4(v[f][r][0], v[f][r][1], v[f][r][2], v[f][r][3]);
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packet4(v[f][0][k], v[f][1][k], v[f][2][k], v[f][3][k]);
+    if constexpr (NF == 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) packet4(v[0][r][k], v[1][r][k], v[2][r][k], v[3][r][k]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fast forward kernel: compile-time channel count CT, NTHWC output staged through LDS.
+// Each lane keeps all 64*CT coefficients of its position in registers, packs them
+// into 16-byte words in channel order and writes its LDS row with 128-bit stores;
+// the wave then copies its 64 contiguous rows out with 16-byte coalesced stores.
+// LDS row stride = row bytes + 16, so the 128-bit row accesses of 16 lanes fall
+// on distinct banks.
+template <typename Tin, typename Tout, int NF, int CT>
+__global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
+                                                             int T, int H, int W, int Tq, int Hq, int Wq,
+                                                             int nchunk) {
+    constexpr int C = CT;
+    constexpr int G = NF == 4 ? 64 : 16;
+    constexpr int NCH = G * C;
+    constexpr int P16 = Elem<Tout>::per16;
+    constexpr int ROW16 = NCH / P16;          // 16-byte words per row
+    constexpr int STRIDE = (ROW16 + 1) * 16;  // bytes
+    static_assert(NCH % P16 == 0, "row must be a whole number of 16-byte words");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[64 * STRIDE];
+    const float scale = NF == 4 ? 0.125f : 0.25f;
+
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     const int lane = threadIdx.x;
-    const int wq_ld = tile.valid ? tile.wq : (Wq - 1);  // keep loads in bounds
-    const int NCH = (NF == 4 ? 64 : 16) * C;
-    const float scale = NF == 4 ? 0.125f : 0.25f;
-    const int rowwords = NCH * (int)sizeof(Tout) / 4;
-    const int stride = rowwords + 1;
-    uint8_t* lds_row = reinterpret_cast<uint8_t*>(lds) + (size_t)lane * stride * 4;
+    const int wq_ld = tile.valid ? tile.wq : (Wq - 1);
 
-    constexpr int kUnrollC = CT > 0 ? CT : 1;
-#pragma unroll kUnrollC
-    for (int cr = 0; cr < C; ++cr) {
-        {
-            float v[NF][4][4];
+    // 1. all loads of the block, every channel
+    Row4<Tin> raw[C][NF][4];
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int src = NF == 4 ? max(4 * tile.tq + f - 3, 0) : tile.tq;
-                const Tin* base = x + (((size_t)(tile.b * C + cr) * T + src) * H + 4 * tile.hq) * W + 4 * wq_ld;
+    for (int c = 0; c < C; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) load4(base + (size_t)r * W, v[f][r]);
-            }
+        for (int f = 0; f < NF; ++f) {
+            const int src = NF == 4 ? max(4 * tile.tq + f - 3, 0) : tile.tq;
+            const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * wq_ld;
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) packet4(v[f][r][0], v[f][r][1], v[f][r][2], v[f][r][3]);
-#pragma unroll
-            for (int f = 0; f < NF; ++f)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) packet4(v[f][0][k], v[f][1][k], v[f][2][k], v[f][3][k]);
-            if constexpr (NF == 4) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) packet4(v[0][r][k], v[1][r][k], v[2][r][k], v[3][r][k]);
-            }
-#pragma unroll
-            for (int rt = 0; rt < NF; ++rt)
-#pragma unroll
-                for (int rh = 0; rh < 4; ++rh)
-#pragma unroll
-                    for (int rw = 0; rw < 4; ++rw) {
-                        const int ch = coef_channel<NF>(rt, rh, rw, cr, C);
-                        const float val = v[rt][rh][rw] * scale;
-                        if (LAYOUT == CVT_NCTHW) {
-                            if (tile.valid)
-                                store1(y + ((((size_t)tile.b * NCH + ch) * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq, val);
-                        } else if (stage) {
-                            store1(reinterpret_cast<Tout*>(lds_row) + ch, val);
-                        } else if (tile.valid) {
-                            store1(y + ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq) * NCH + ch, val);
-                        }
-                    }
+            for (int r = 0; r < 4; ++r) raw[c][f][r].load(base + (size_t)r * W);
         }
+
+    // 2. transform, in output channel order
+    float out[NCH];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        float v[NF][4][4];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) raw[c][f][r].get(v[f][r]);
+        block_transform<NF>(v);
+#pragma unroll
+        for (int rt = 0; rt < NF; ++rt)
+#pragma unroll
+            for (int rh = 0; rh < 4; ++rh)
+#pragma unroll
+                for (int rw = 0; rw < 4; ++rw) out[coef_channel<NF>(rt, rh, rw, c, C)] = v[rt][rh][rw] * scale;
     }
 
-    if (LAYOUT == CVT_NTHWC && stage) {
-        __syncthreads();
-        const int nvalid = min(64, Wq - tile.chunk * 64);
-        const int total = nvalid * rowwords;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(
-            y + ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + (size_t)tile.chunk * 64) * NCH);
-        int row = lane / rowwords, col = lane - (lane / rowwords) * rowwords;
-        for (int w = lane; w < total; w += 64) {
-            dst[w] = lds[row * stride + col];
-            col += 64;
-            while (col >= rowwords) {
-                col -= rowwords;
-                ++row;
-            }
+    // 3. row -> LDS (128-bit stores), then coalesced 16-byte copy-out of the wave's rows
+    uint8_t* row = lds + lane * STRIDE;
+#pragma unroll
+    for (int j = 0; j < ROW16; ++j)
+        *reinterpret_cast<uint4*>(row + 16 * j) = pack16(out + j * P16, (Tout*)nullptr);
+    __syncthreads();
+    const int nvalid = min(64, Wq - tile.chunk * 64);
+    const int total = nvalid * ROW16;
+    uint4* dst = reinterpret_cast<uint4*>(
+        y + ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + (size_t)tile.chunk * 64) * NCH);
+#pragma unroll
+    for (int i = 0; i < ROW16; ++i) {
+        const int q = lane + 64 * i;
+        if (q < total) {
+            const int r = q / ROW16, c16 = q - (q / ROW16) * ROW16;
+            dst[q] = *reinterpret_cast<const uint4*>(lds + r * STRIDE + 16 * c16);
         }
     }
 }
 
-template <typename Tin, typename Tout, int NF, int LAYOUT, int CT>
-__global__ __launch_bounds__(64) void haar_inv_kernel(const Tin* __restrict__ y, Tout* __restrict__ x,
-                                                      int C_rt, int T, int H, int W, int Tq, int Hq,
-                                                      int Wq, int nchunk, int stage) {
-    extern __shared__ uint32_t lds[];
-    const int C = CT > 0 ? CT : C_rt;
+// Fast inverse kernel: compile-time CT, NTHWC input staged through LDS with
+// coalesced 16-byte loads; each lane reads its row back with 128-bit LDS reads.
+template <typename Tin, typename Tout, int NF, int CT>
+__global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restrict__ y, Tout* __restrict__ x,
+                                                             int T, int H, int W, int Tq, int Hq, int Wq,
+                                                             int nchunk) {
+    constexpr int C = CT;
+    constexpr int G = NF == 4 ? 64 : 16;
+    constexpr int NCH = G * C;
+    constexpr int P16 = Elem<Tin>::per16;
+    constexpr int ROW16 = NCH / P16;
+    constexpr int STRIDE = (ROW16 + 1) * 16;
+    static_assert(NCH % P16 == 0, "row must be a whole number of 16-byte words");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[64 * STRIDE];
+    const float scale = NF == 4 ? 0.125f : 0.25f;
+
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     const int lane = threadIdx.x;
-    const int NCH = (NF == 4 ? 64 : 16) * C;
-    const float scale = NF == 4 ? 0.125f : 0.25f;
-    const int rowwords = NCH * (int)sizeof(Tin) / 4;
-    const int stride = rowwords + 1;
-    const size_t pos = (((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq;
+    const int nvalid = min(64, Wq - tile.chunk * 64);
+    const int total = nvalid * ROW16;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        y + ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + (size_t)tile.chunk * 64) * NCH);
 
-    if (LAYOUT == CVT_NTHWC && stage) {
-        const int nvalid = min(64, Wq - tile.chunk * 64);
-        const int total = nvalid * rowwords;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(y + (pos + (size_t)tile.chunk * 64) * NCH);
-        int row = lane / rowwords, col = lane - (lane / rowwords) * rowwords;
-        for (int w = lane; w < total; w += 64) {
-            lds[row * stride + col] = src[w];
-            col += 64;
-            while (col >= rowwords) {
-                col -= rowwords;
-                ++row;
-            }
-        }
-        __syncthreads();
+    // 1. coalesced 16-byte loads of the wave's rows, all in flight, then LDS.  On a
+    // partial run the index is clamped: the duplicate words land in LDS rows that
+    // belong to positions past the end, which no valid lane reads.
+    uint4 stage[ROW16];
+#pragma unroll
+    for (int i = 0; i < ROW16; ++i) stage[i] = src[min(lane + 64 * i, total - 1)];
+#pragma unroll
+    for (int i = 0; i < ROW16; ++i) {
+        const int q = lane + 64 * i;
+        const int r = q / ROW16, c16 = q - (q / ROW16) * ROW16;
+        *reinterpret_cast<uint4*>(lds + r * STRIDE + 16 * c16) = stage[i];
     }
+    __syncthreads();
     if (!tile.valid) return;
-    const Tin* lds_row = reinterpret_cast<const Tin*>(reinterpret_cast<const uint8_t*>(lds) + (size_t)lane * stride * 4);
 
-    constexpr int kUnrollC = CT > 0 ? CT : 1;
-#pragma unroll kUnrollC
-    for (int cr = 0; cr < C; ++cr) {
-        {
-            float v[NF][4][4];
+    // 2. this lane's row
+    float coef[NCH];
+    const uint8_t* row = lds + lane * STRIDE;
 #pragma unroll
-            for (int rt = 0; rt < NF; ++rt)
+    for (int j = 0; j < ROW16; ++j) unpack16(*reinterpret_cast<const uint4*>(row + 16 * j), coef + j * P16, (const Tin*)nullptr);
+
+    // 3. per channel: inverse transform and 8/16-byte pixel-row stores
 #pragma unroll
-                for (int rh = 0; rh < 4; ++rh)
+    for (int c = 0; c < C; ++c) {
+        float v[NF][4][4];
 #pragma unroll
-                    for (int rw = 0; rw < 4; ++rw) {
-                        const int ch = coef_channel<NF>(rt, rh, rw, cr, C);
-                        float val;
-                        if (LAYOUT == CVT_NCTHW)
-                            val = load1(y + ((((size_t)tile.b * NCH + ch) * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq);
-                        else if (stage)
-                            val = load1(lds_row + ch);
-                        else
-                            val = load1(y + (pos + tile.wq) * NCH + ch);
-                        v[rt][rh][rw] = val;
-                    }
+        for (int rt = 0; rt < NF; ++rt)
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+            for (int rh = 0; rh < 4; ++rh)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) packet4(v[f][r][0], v[f][r][1], v[f][r][2], v[f][r][3]);
+                for (int rw = 0; rw < 4; ++rw) v[rt][rh][rw] = coef[coef_channel<NF>(rt, rh, rw, c, C)];
+        block_transform<NF>(v);
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
+        for (int f = 0; f < NF; ++f) {
+            const int t = NF == 4 ? 4 * tile.tq + f - 3 : tile.tq;  // drop the 3 leading padded frames
+            if (t < 0) continue;
+            Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) packet4(v[f][0][k], v[f][1][k], v[f][2][k], v[f][3][k]);
-            if constexpr (NF == 4) {
+            for (int r = 0; r < 4; ++r) {
+                float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) packet4(v[0][r][k], v[1][r][k], v[2][r][k], v[3][r][k]);
-            }
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int t = NF == 4 ? 4 * tile.tq + f - 3 : tile.tq;  // drop the 3 leading padded frames
-                if (t < 0) continue;
-                Tout* base = x + (((size_t)(tile.b * C + cr) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float o[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
-                    store4(base + (size_t)r * W, o);
-                }
+                for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                store4(base + (size_t)r * W, o);
             }
         }
     }
 }
 
-constexpr int kLdsLimit = 64 * 1024;
+// ---------------------------------------------------------------------------------------------
+// Generic kernels (runtime channel count, either layout, no staging): correct for
+// every shape the ABI accepts; used when the fast kernels do not apply.
+template <typename Tin, typename Tout, int NF, int LAYOUT>
+__global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restrict__ x, Tout* __restrict__ y, int C,
+                                                              int T, int H, int W, int Tq, int Hq, int Wq,
+                                                              int nchunk) {
+    const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
+    if (!tile.valid) return;
+    const int NCH = (NF == 4 ? 64 : 16) * C;
+    const float scale = NF == 4 ? 0.125f : 0.25f;
+    for (int c = 0; c < C; ++c) {
+        float v[NF][4][4];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int src = NF == 4 ? max(4 * tile.tq + f - 3, 0) : tile.tq;
+            const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * tile.wq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) load4(base + (size_t)r * W, v[f][r]);
+        }
+        block_transform<NF>(v);
+#pragma unroll
+        for (int rt = 0; rt < NF; ++rt)
+#pragma unroll
+            for (int rh = 0; rh < 4; ++rh)
+#pragma unroll
+                for (int rw = 0; rw < 4; ++rw) {
+                    const int ch = coef_channel<NF>(rt, rh, rw, c, C);
+                    const size_t off = LAYOUT == CVT_NCTHW
+                        ? ((((size_t)tile.b * NCH + ch) * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq
+                        : ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq) * NCH + ch;
+                    store1(y + off, v[rt][rh][rw] * scale);
+                }
+    }
+}
+
+template <typename Tin, typename Tout, int NF, int LAYOUT>
+__global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restrict__ y, Tout* __restrict__ x, int C,
+                                                              int T, int H, int W, int Tq, int Hq, int Wq,
+                                                              int nchunk) {
+    const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
+    if (!tile.valid) return;
+    const int NCH = (NF == 4 ? 64 : 16) * C;
+    const float scale = NF == 4 ? 0.125f : 0.25f;
+    for (int c = 0; c < C; ++c) {
+        float v[NF][4][4];
+#pragma unroll
+        for (int rt = 0; rt < NF; ++rt)
+#pragma unroll
+            for (int rh = 0; rh < 4; ++rh)
+#pragma unroll
+                for (int rw = 0; rw < 4; ++rw) {
+                    const int ch = coef_channel<NF>(rt, rh, rw, c, C);
+                    const size_t off = LAYOUT == CVT_NCTHW
+                        ? ((((size_t)tile.b * NCH + ch) * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq
+                        : ((((size_t)tile.b * Tq + tile.tq) * Hq + tile.hq) * Wq + tile.wq) * NCH + ch;
+                    v[rt][rh][rw] = load1(y + off);
+                }
+        block_transform<NF>(v);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int t = NF == 4 ? 4 * tile.tq + f - 3 : tile.tq;
+            if (t < 0) continue;
+            Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                store4(base + (size_t)r * W, o);
+            }
+        }
+    }
+}
 
 template <typename Tin, typename Tout, int NF, int LAYOUT>
 hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int W, hipStream_t s) {
@@ -274,16 +394,12 @@ hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int 
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int NCH = (NF == 4 ? 64 : 16) * C;
-    const size_t lds_bytes = (size_t)64 * (NCH * sizeof(Tout) / 4 + 1) * 4;
-    const int stage = (LAYOUT == CVT_NTHWC) && lds_bytes <= (size_t)kLdsLimit;
-    const size_t shmem = stage ? lds_bytes : 0;
-    if (C == 3)
-        hipLaunchKernelGGL((haar_fwd_kernel<Tin, Tout, NF, LAYOUT, 3>), dim3((unsigned)nblk), dim3(64), shmem, s,
-                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk, stage);
+    if (LAYOUT == CVT_NTHWC && C == 3)
+        hipLaunchKernelGGL((haar_fwd_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)x, (Tout*)y, T, H, W, Tq, Hq, Wq, nchunk);
     else
-        hipLaunchKernelGGL((haar_fwd_kernel<Tin, Tout, NF, LAYOUT, 0>), dim3((unsigned)nblk), dim3(64), shmem, s,
-                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk, stage);
+        hipLaunchKernelGGL((haar_fwd_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk);
     return hipGetLastError();
 }
 
@@ -293,16 +409,12 @@ hipError_t launch_inv_t(const void* y, void* x, int B, int C, int T, int H, int 
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int NCH = (NF == 4 ? 64 : 16) * C;
-    const size_t lds_bytes = (size_t)64 * (NCH * sizeof(Tin) / 4 + 1) * 4;
-    const int stage = (LAYOUT == CVT_NTHWC) && lds_bytes <= (size_t)kLdsLimit;
-    const size_t shmem = stage ? lds_bytes : 0;
-    if (C == 3)
-        hipLaunchKernelGGL((haar_inv_kernel<Tin, Tout, NF, LAYOUT, 3>), dim3((unsigned)nblk), dim3(64), shmem, s,
-                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk, stage);
+    if (LAYOUT == CVT_NTHWC && C == 3)
+        hipLaunchKernelGGL((haar_inv_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)y, (Tout*)x, T, H, W, Tq, Hq, Wq, nchunk);
     else
-        hipLaunchKernelGGL((haar_inv_kernel<Tin, Tout, NF, LAYOUT, 0>), dim3((unsigned)nblk), dim3(64), shmem, s,
-                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk, stage);
+        hipLaunchKernelGGL((haar_inv_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk);
     return hipGetLastError();
 }
 
