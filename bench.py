@@ -17,7 +17,9 @@ kernel, the spatial convolution's MFMA implicit GEMM: algorithmic FLOPs
 2*9*Cin*Cout per output position, divided by its average duration measured
 with HIP events on the launch stream over the timed steps.  The CPU baseline is
 the float64 oracle timed on a bounded sample of the same workload (a strip of
-the frame), scaled to the full clip.
+the frame), scaled to the full clip.  A second object reports the 121-frame
+CV8x8x8-720p-shaped chain (two factorized conv layers and the 1x1), where the
+convolution's MFMA fraction is quoted.
 """
 
 import argparse
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "720p frames/sec through Haar+causal conv+FSQ; HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+COPY_CAL_BYTES = 256 * 1024 * 1024
 
 
 def parse():
@@ -44,6 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_dv8x16x16_720p_49f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-c3", action="store_true", help="skip the 121-frame chain measurement")
     ap.add_argument("--cpu-width", type=int, default=320,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -168,6 +172,16 @@ def main():
                 "kernel": "conv_tap_gemm_kernel<SPATIAL3,256,8,64,8> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
+    c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
+
+    # Copy calibration for the HBM-traffic counters: one device copy of a known
+    # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
+    # scale the dominant kernel's).
+    cal = torch.empty(COPY_CAL_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, (B, C, T, H, W), args.cpu_width)
@@ -193,8 +207,84 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": per_stage,
+        "cv8x8x8_720p_121f": c3,
+        "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
+
+
+def cv8x8x8_chain(cvt, si, torch, dev, args):
+    """The 121-frame 720p chain (Haar -> conv 192->256 k3 -> conv 256->256 k3 -> 1x1 -> 16),
+    timed per stage with HIP events; reports frames/s of the chain and the MFMA
+    fraction of each convolution (the conv target is quoted on this clip)."""
+    wl = si.WORKLOADS["c3_cv8x8x8_720p_121f"]
+    B, C, T, H, W = wl["x"]
+    Tq, Hq, Wq = 1 + (T - 1) // 4, H // 4, W // 4
+    P = B * Tq * Hq * Wq
+    log(f"121-frame chain: generating {wl['x']} ...")
+    xbits = si.to_bf16_bits(si.video_trans(wl["x"], wl["seed"]))
+
+    def dev_bits(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = dev_bits(xbits)
+    del xbits
+    w = [dev_bits(si.to_bf16_bits(si.normal(shape, si.weight_seed(3, i), 0.02)))
+         for i, shape in enumerate([(256, 192, 1, 3, 3), (256, 256, 3, 1, 1), (256, 256, 1, 3, 3),
+                                    (256, 256, 3, 1, 1), (16, 256, 1, 1, 1)])]
+    cl = torch.channels_last_3d
+    hz = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    a = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    b = torch.empty_like(a)
+    lat = torch.empty((B, 16, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    ws = {k: torch.empty(n, dtype=torch.uint8, device=dev) for k, n in [
+        ("s1", cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False)),
+        ("t", cvt.conv_workspace_bytes(a.shape, 256, 3, False, True)),
+        ("s2", cvt.conv_workspace_bytes(a.shape, 256, 3, True, False)),
+        ("p", cvt.conv_workspace_bytes(a.shape, 16, 1, True, False))]}
+    stages = [
+        ("haar_fwd", lambda: cvt.haar3d_fwd(x, out=hz), None),
+        ("l1_spatial", lambda: cvt.causal_conv3d_fact(hz, w[0], None, workspace=ws["s1"], out=a), 2.0 * 9 * 192 * 256 * P),
+        ("l1_temporal", lambda: cvt.causal_conv3d_fact(a, None, w[1], workspace=ws["t"], out=b), 2.0 * 3 * 256 * 256 * P),
+        ("l2_spatial", lambda: cvt.causal_conv3d_fact(b, w[2], None, workspace=ws["s2"], out=a), 2.0 * 9 * 256 * 256 * P),
+        ("l2_temporal", lambda: cvt.causal_conv3d_fact(a, None, w[3], workspace=ws["t"], out=b), 2.0 * 3 * 256 * 256 * P),
+        ("proj_1x1", lambda: cvt.causal_conv3d_fact(b, w[4], None, workspace=ws["p"], out=lat), 2.0 * 256 * 16 * P),
+    ]
+    stream = torch.cuda.current_stream(dev)
+    steps = max(2, args.steps // 2)
+    for _ in range(max(1, args.warmup)):
+        for _, fn, _ in stages:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for k in range(steps):
+        for i, (_, fn, _) in enumerate(stages):
+            evs[k][i].record(stream)
+            fn()
+        evs[k][len(stages)].record(stream)
+    torch.cuda.synchronize()
+    out = {"steps": steps, "stages": {}}
+    total = 0.0
+    conv_flops = conv_ms = 0.0
+    for i, (name, _, flops) in enumerate(stages):
+        ms = float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+        total += ms
+        d = {"ms": round(ms, 4)}
+        if flops:
+            d["TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            d["mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            if name != "proj_1x1":
+                conv_flops += flops
+                conv_ms += ms
+        else:
+            d["GBps"] = round((2.0 * B * C * T * H * W + 2.0 * P * 192) / (ms * 1e-3) / 1e9, 1)
+        out["stages"][name] = d
+    out["frames_per_s"] = round(B * T / (total * 1e-3), 1)
+    out["conv_TFLOPs"] = round(conv_flops / (conv_ms * 1e-3) / 1e12, 1)
+    out["conv_mfma_frac"] = round(conv_flops / (conv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del x, hz, a, b, lat, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):

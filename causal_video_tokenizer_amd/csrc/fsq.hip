@@ -15,7 +15,7 @@
 // not within double rounding of a breakpoint.
 //
 // Mapping: one thread per run of 8 consecutive positions.  Planar (NCTHW)
-// latents are read as one 16-byte (bf16) or two 16-byte (fp32) loads per
+// latents are read as one 16-byte (bf16) or two 16-byte (fp32) streaming loads per
 // channel; NTHWC latents as the thread's contiguous 8*D-element span.  Indices
 // are written as two 16-byte stores.  Ragged tails and plane sizes that are not
 // multiples of 8 take the per-position path.
@@ -32,16 +32,16 @@ template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* v);
 template <>
 __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint4 u = ld_stream16(p);
     v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
     v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
 }
 template <>
 __device__ __forceinline__ void load8<float>(const float* p, float* v) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const uint4 a = ld_stream16(p);
+    const uint4 b = ld_stream16(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
@@ -286,8 +286,9 @@ __global__ __launch_bounds__(256) void fsq_dequantize_default_kernel(const int32
     if (pos0 >= total) return;
     int nbad = 0;
     if (pos0 + G <= total) {
-        const int4 a = *reinterpret_cast<const int4*>(idx + pos0);
-        const int4 c = *reinterpret_cast<const int4*>(idx + pos0 + 4);
+        const uint4 ua = ld_stream16(idx + pos0), uc = ld_stream16(idx + pos0 + 4);
+        const int4 a = make_int4((int)ua.x, (int)ua.y, (int)ua.z, (int)ua.w);
+        const int4 c = make_int4((int)uc.x, (int)uc.y, (int)uc.z, (int)uc.w);
         const int id[G] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
         float cv[D][G];
 #pragma unroll
@@ -338,6 +339,143 @@ __global__ __launch_bounds__(256) void fsq_dequantize_default_kernel(const int32
     if (invalid && nbad) atomicAdd(invalid, nbad);
 }
 
+// Dequantize with the default levels through two LDS tables.  With radices
+// (8,8,8,5,5,5) the index splits into lo = idx mod 512 (the three base-8 digits) and
+// hi = idx / 512 < 125 (the three base-5 digits); each table row holds the three
+// codes of its digits, packed as the output type (bf16 pairs or floats), and row
+// 512 / 125 holds NaNs for invalid indices.  Per position this is two LDS reads and
+// a few byte permutes instead of six divisions and conversions.  Each workgroup
+// fills its tables once and then walks several 8-position groups.
+template <typename T>
+struct CodeRow;
+template <>
+struct CodeRow<uint16_t> {
+    using type = uint2;  // x = c0 | c1 << 16, y = c2
+    __device__ static type make(float c0, float c1, float c2) {
+        return make_uint2(pack_bf16x2(c0, c1), pack_bf16x2(c2, 0.0f));
+    }
+};
+template <>
+struct CodeRow<float> {
+    using type = float4;
+    __device__ static type make(float c0, float c1, float c2) { return make_float4(c0, c1, c2, 0.0f); }
+};
+
+constexpr int DQ_GROUPS = 4;  // 8-position groups per thread
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(256) void fsq_dequantize_lut_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
+                                                                 long long npb, long long total,
+                                                                 int32_t* __restrict__ invalid) {
+    using Row = typename CodeRow<T>::type;
+    __shared__ Row lutA[513];
+    __shared__ Row lutB[126];
+    const float qnan = __builtin_nanf("");
+    for (int e = threadIdx.x; e < 513 + 126; e += blockDim.x) {
+        if (e < 512) {
+            lutA[e] = CodeRow<T>::make(((e & 7) - 4) * 0.25f, (((e >> 3) & 7) - 4) * 0.25f, ((e >> 6) - 4) * 0.25f);
+        } else if (e == 512) {
+            lutA[e] = CodeRow<T>::make(qnan, qnan, qnan);
+        } else {
+            const int h = e - 513;
+            lutB[h] = h < 125 ? CodeRow<T>::make((h % 5 - 2) * 0.5f, ((h / 5) % 5 - 2) * 0.5f, (h / 25 - 2) * 0.5f)
+                              : CodeRow<T>::make(qnan, qnan, qnan);
+        }
+    }
+    __syncthreads();
+
+    int nbad = 0;
+    for (int r = 0; r < DQ_GROUPS; ++r) {
+        const long long pos0 = ((long long)(blockIdx.x * DQ_GROUPS + r) * blockDim.x + threadIdx.x) * G;
+        if (pos0 >= total) break;
+        if (pos0 + G <= total) {
+            const uint4 ua = ld_stream16(idx + pos0), uc = ld_stream16(idx + pos0 + 4);
+            const uint32_t id[G] = {ua.x, ua.y, ua.z, ua.w, uc.x, uc.y, uc.z, uc.w};
+            Row A[G], Bv[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const bool bad = id[k] >= 64000u;
+                nbad += bad ? 1 : 0;
+                A[k] = lutA[bad ? 512 : (id[k] & 511u)];
+                Bv[k] = lutB[bad ? 125 : (id[k] >> 9)];
+            }
+            if constexpr (sizeof(T) == 2) {
+                // bf16: combine 16-bit fields with byte permutes
+                auto lo2 = [](uint32_t p, uint32_t q) { return __builtin_amdgcn_perm(q, p, 0x05040100u); };
+                auto hi2 = [](uint32_t p, uint32_t q) { return __builtin_amdgcn_perm(q, p, 0x07060302u); };
+                if (LAYOUT == CVT_NCTHW) {
+                    const long long b = pos0 / npb, rr = pos0 - b * npb;
+                    uint4 o[6];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int p = 2 * j, q = 2 * j + 1;
+                        (&o[0].x)[j] = lo2(A[p].x, A[q].x);
+                        (&o[1].x)[j] = hi2(A[p].x, A[q].x);
+                        (&o[2].x)[j] = lo2(A[p].y, A[q].y);
+                        (&o[3].x)[j] = lo2(Bv[p].x, Bv[q].x);
+                        (&o[4].x)[j] = hi2(Bv[p].x, Bv[q].x);
+                        (&o[5].x)[j] = lo2(Bv[p].y, Bv[q].y);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 6; ++i)
+                        *reinterpret_cast<uint4*>(codes + ((size_t)b * 6 + i) * npb + rr) = o[i];
+                } else {
+                    // per position: (c0 c1) (c2 c3) (c4 c5)
+                    uint32_t w[3 * G];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        w[3 * k] = A[k].x;
+                        w[3 * k + 1] = lo2(A[k].y, Bv[k].x);
+                        w[3 * k + 2] = __builtin_amdgcn_perm(Bv[k].y, Bv[k].x, 0x05040302u);
+                    }
+                    uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos0 * 6);
+#pragma unroll
+                    for (int c = 0; c < 6; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+                }
+            } else {
+                float cv[6][G];
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    cv[0][k] = A[k].x; cv[1][k] = A[k].y; cv[2][k] = A[k].z;
+                    cv[3][k] = Bv[k].x; cv[4][k] = Bv[k].y; cv[5][k] = Bv[k].z;
+                }
+                if (LAYOUT == CVT_NCTHW) {
+                    const long long b = pos0 / npb, rr = pos0 - b * npb;
+#pragma unroll
+                    for (int i = 0; i < 6; ++i) store8(codes + ((size_t)b * 6 + i) * npb + rr, cv[i]);
+                } else {
+                    float flat[6 * G];
+#pragma unroll
+                    for (int k = 0; k < G; ++k)
+#pragma unroll
+                        for (int i = 0; i < 6; ++i) flat[k * 6 + i] = cv[i][k];
+#pragma unroll
+                    for (int c8 = 0; c8 < 6; ++c8) store8(codes + (size_t)pos0 * 6 + c8 * G, flat + c8 * G);
+                }
+            }
+        } else {
+            for (long long pos = pos0; pos < total; ++pos) {  // ragged tail (< 8 positions)
+                const uint32_t v = (uint32_t)idx[pos];
+                const bool bad = v >= 64000u;
+                nbad += bad ? 1 : 0;
+                uint32_t rem = bad ? 0u : v;
+                const long long b = pos / npb, rr = pos - b * npb;
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const uint32_t L = i < 3 ? 8u : 5u;
+                    const uint32_t q = rem / L;
+                    const int d = (int)(rem - q * L);
+                    rem = q;
+                    const float c = bad ? qnan : (float)(d - (int)(L / 2)) * (i < 3 ? 0.25f : 0.5f);
+                    const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * 6 + i) * npb + rr : (size_t)pos * 6 + i;
+                    st1(codes + off, c);
+                }
+            }
+        }
+    }
+    if (invalid && nbad) atomicAdd(invalid, nbad);
+}
+
 template <typename T, int LAYOUT, int DC>
 __global__ __launch_bounds__(256) void fsq_dequantize_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
                                                              FsqParams p, long long npb, long long total,
@@ -350,8 +488,9 @@ __global__ __launch_bounds__(256) void fsq_dequantize_kernel(const int32_t* __re
 
 
     if (vec && pos0 + G <= total) {
-        const int4 a = *reinterpret_cast<const int4*>(idx + pos0);
-        const int4 c = *reinterpret_cast<const int4*>(idx + pos0 + 4);
+        const uint4 ua = ld_stream16(idx + pos0), uc = ld_stream16(idx + pos0 + 4);
+        const int4 a = make_int4((int)ua.x, (int)ua.y, (int)ua.z, (int)ua.w);
+        const int4 c = make_int4((int)uc.x, (int)uc.y, (int)uc.z, (int)uc.w);
         const int id[G] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
         bool bad[G];
         uint32_t rem[G];
@@ -472,8 +611,8 @@ hipError_t dequantize_t(const int32_t* idx, void* codes, const FsqParams& p, lon
     const long long nblk = (nthreads + 255) / 256;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (is_default(p) && vec)
-        hipLaunchKernelGGL((fsq_dequantize_default_kernel<T, LAYOUT>), dim3((unsigned)nblk), dim3(256), 0, s, idx,
-                           (T*)codes, npb, total, invalid);
+        hipLaunchKernelGGL((fsq_dequantize_lut_kernel<T, LAYOUT>), dim3((unsigned)((nblk + DQ_GROUPS - 1) / DQ_GROUPS)),
+                           dim3(256), 0, s, idx, (T*)codes, npb, total, invalid);
     else if (p.D == 6)
         hipLaunchKernelGGL((fsq_dequantize_kernel<T, LAYOUT, 6>), dim3((unsigned)nblk), dim3(256), 0, s, idx, (T*)codes, p,
                            npb, total, vec, invalid);

@@ -21,8 +21,8 @@
 //
 // Mapping: one wavefront per (b, t', h', run of 64 w' positions); lane = w'.
 // Each lane loads the 4 x 4 x 4 block of every input channel with 8-byte
-// (bf16) or 16-byte (fp32) row loads, so each load instruction covers 512 or
-// 1024 contiguous bytes of a pixel row.  For the NTHWC coefficient layout the
+// (bf16) or 16-byte (fp32) streaming row loads, so each load instruction covers
+// 512 or 1024 contiguous bytes of a pixel row.  For the NTHWC coefficient layout the
 // 64 x (64C) output tile is transposed through LDS (rows padded by one dword so
 // the per-lane scattered writes hit distinct banks) and written as contiguous
 // dwords; the inverse stages its NTHWC input the same way.
@@ -136,7 +136,7 @@ struct Row4;
 template <>
 struct Row4<uint16_t> {
     uint2 u;
-    __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ void load(const uint16_t* p) { u = ld_stream8(p); }
     __device__ void get(float* v) const {
         v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
     }
@@ -144,7 +144,10 @@ struct Row4<uint16_t> {
 template <>
 struct Row4<float> {
     float4 u;
-    __device__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+    __device__ void load(const float* p) {
+        const uint4 w = ld_stream16(p);
+        u = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+    }
     __device__ void get(float* v) const { v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; }
 };
 
@@ -243,7 +246,8 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
 }
 
 // Fast inverse kernel: compile-time CT, NTHWC input staged through LDS with
-// coalesced 16-byte loads; each lane reads its row back with 128-bit LDS reads.
+// coalesced 16-byte streaming loads; each lane reads its row back with 128-bit
+// LDS reads.
 template <typename Tin, typename Tout, int NF, int CT>
 __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restrict__ y, Tout* __restrict__ x,
                                                              int T, int H, int W, int Tq, int Hq, int Wq,
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restri
     // belong to positions past the end, which no valid lane reads.
     uint4 stage[ROW16];
 #pragma unroll
-    for (int i = 0; i < ROW16; ++i) stage[i] = src[min(lane + 64 * i, total - 1)];
+    for (int i = 0; i < ROW16; ++i) stage[i] = ld_stream16(src + min(lane + 64 * i, total - 1));
 #pragma unroll
     for (int i = 0; i < ROW16; ++i) {
         const int q = lane + 64 * i;
