@@ -30,6 +30,8 @@
 //     issues v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //   * The epilogue adds the optional fp32 bias, rounds to bf16 (RNE) and
 //     stores 4 consecutive output channels (8 bytes) per lane and block row.
+#include <algorithm>
+
 #include "cvt_internal.h"
 
 namespace cvt {
@@ -554,6 +556,249 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CVT_TAP
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Temporal 3-tap convolution over several output frames per workgroup.
+//
+// One workgroup (4 waves) computes 128 output channels x 64 positions x F consecutive
+// output frames t0 .. t0+F-1.  Output frame t reads input frames t-2, t-1, t through taps
+// 0, 1, 2, so the tile needs the F+2 input frames t0-2 .. t0+F-1 (the REGION); region
+// frame r meets tap j in output frame t0 + r - j.  Each wave owns 64 channels (two
+// 32-row MFMA blocks) x 32 positions x all F frames: per 16-channel k-step it takes the
+// six weight fragments (3 taps x 2 blocks) once and walks the region frames, each
+// activation fragment feeding up to three taps, i.e. three output frames.
+//
+// Only the region is staged in LDS (two 30 KB buffers, so two workgroups share a CU and
+// one's barrier and epilogue overlap the other's MFMAs).  The weights are packed once per
+// call in MFMA fragment order (see pack_frag_kernel): each fragment is 1 KB of which lane
+// l reads bytes [16 l, 16 l + 16), one fully coalesced load straight into the operand
+// registers, prefetched one k-step ahead.  Region chunk loads of step c + 1 are issued
+// after the weight loads of the current step, so waiting for weights never waits for
+// the region.
+//
+// Region frames before frame 0 (causal padding) read zeros; output frames past the end
+// are neither computed (the count of valid frames is a compile-time branch per tile) nor
+// stored.  Blocks are mapped to tiles XCD by XCD: block L runs tile
+// (L mod 8) * per_xcd + L / 8, so consecutive tiles - the channel and frame tiles of one
+// position block, which share region frames - land on the same L2.
+struct TempGeom {
+    int B, T, HW, Cin, Cout;
+    int x_bytes, wf_bytes;  // buffer-resource extents (the launcher keeps both below 2^31)
+    int NA, KC16;           // 32-row weight blocks, 16-channel k-steps
+    int nct, nft, npt;      // channel tiles, frame tiles, position tiles
+    int ntiles, per_xcd;
+};
+
+constexpr int TEMP_PT = 64;       // positions per tile
+constexpr int TEMP_XS = 64 + 16;  // LDS bytes per region row: 32 channels + 16 bytes of padding
+
+template <int F, int NV>
+__device__ __forceinline__ void temporal_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
+                                              const float* __restrict__ bias, uint16_t* __restrict__ Y,
+                                              const TempGeom& g, uint8_t (*sX)[(F + 2) * TEMP_PT * TEMP_XS], int b,
+                                              int ct, int t0, int hw0) {
+    constexpr int NTH = 256, PT = TEMP_PT, NR = F + 2, BK = 32, CPR = BK / 8, XS = TEMP_XS;
+    constexpr int XROWS = NR * PT;
+    constexpr int XL = XROWS * CPR / NTH;
+    constexpr int OOB = 0x7fffffff;
+    constexpr int NRU = NV + 2;  // region frames that feed a valid output frame
+    static_assert(XROWS * CPR % NTH == 0 && XROWS % 8 == 0, "region split");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wch = wave & 1, wpos = wave >> 1;
+
+    // Region chunk q of a thread is (row, c16) with 8 consecutive lanes on 8 consecutive rows
+    // at one chunk: LDS stores go 8 lanes (128 bytes) at a time, and 8 rows of 80 bytes at
+    // one offset cover 32 distinct banks, where 4 chunks of 2 rows would collide.
+    auto xmap = [](int q, int& row, int& c16) {
+        row = (q / (8 * CPR)) * 8 + (q & 7);
+        c16 = (q >> 3) % CPR;
+    };
+    int xbase[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        int row, c16;
+        xmap(tid + NTH * i, row, c16);
+        const int r = row / PT, hw = hw0 + row % PT, fr = t0 - 2 + r;
+        const bool ok = r < NRU && fr >= 0 && fr < g.T && hw < g.HW;
+        xbase[i] = ok ? (((b * g.T + fr) * g.HW + hw) * g.Cin + c16 * 8) * 2 : -1;
+    }
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, g.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)Wf, (short)0, g.wf_bytes, 0x00020000);
+
+    uint4 xr[XL];
+    auto load_region = [&](int kc) {  // kc past the last chunk reads zeros
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            int row, c16;
+            xmap(tid + NTH * i, row, c16);
+            const bool ok = xbase[i] >= 0 && kc * BK + c16 * 8 < g.Cin;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, ok ? xbase[i] + kc * BK * 2 : OOB, 0, 0);
+            xr[i] = *reinterpret_cast<const uint4*>(&v);
+        }
+    };
+    auto store_region = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            int row, c16;
+            xmap(tid + NTH * i, row, c16);
+            *reinterpret_cast<uint4*>(&sX[buf][row * XS + c16 * 16]) = xr[i];
+        }
+    };
+
+    // weight fragments of k-step kc16: blocks ab0, ab0 + 1 of taps 0..2 (zeros past the end)
+    const int ab0 = ct * 4 + wch * 2;
+    bf16x8_t fa[2][3][2];
+    auto load_frags = [&](int kc16, int set) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int ab = ab0 + a;
+                const int off = (kc16 < g.KC16 && ab < g.NA) ? (((kc16 * 3 + j) * g.NA + ab) * 64 + lane) * 16 : OOB;
+                fa[set][j][a] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0));
+            }
+    };
+
+    f32x16_t acc[NV][2];
+#pragma unroll
+    for (int f = 0; f < NV; ++f)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][a][e] = 0.0f;
+
+    const int khalf = lane >> 5, px = lane & 31;
+    auto compute = [&](const uint8_t* xb, int ks, int set) {
+        const int ch = ks * 2 + khalf;
+        bf16x8_t fb[NRU];
+#pragma unroll
+        for (int r = 0; r < NRU; ++r) fb[r] = *reinterpret_cast<const bf16x8_t*>(xb + r * PT * XS + ch * 16);
+#pragma unroll
+        for (int r = 0; r < NRU; ++r)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int tl = r - j;
+                if (tl < 0 || tl >= NV) continue;
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    acc[tl][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][j][a], fb[r], acc[tl][a], 0, 0, 0);
+            }
+    };
+
+    const int nchunks = (g.Cin + BK - 1) / BK;
+    load_frags(0, 0);
+    load_region(0);
+    store_region(0);
+    __syncthreads();
+    for (int kc = 0; kc < nchunks; ++kc) {
+        const uint8_t* xb = sX[kc & 1] + (wpos * 32 + px) * XS;
+        load_frags(2 * kc + 1, 1);
+        load_region(kc + 1);
+        compute(xb, 0, 0);
+        load_frags(2 * kc + 2, 0);
+        compute(xb, 1, 1);
+        store_region((kc + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: bias, bf16 RNE, staged per frame through a wave-private LDS tile of
+    // 32 positions x 64 channels (rows of 128 bytes + 16 bytes of padding, so the 8-byte
+    // writes of 8 consecutive positions hit distinct banks), then written back with each
+    // 8 consecutive lanes storing one position's 128 contiguous bytes.  The region buffers
+    // are free after the last barrier of the K loop; a wave reads back only what it wrote
+    // and its LDS accesses execute in order, so no barrier is needed.
+    constexpr int OS = 144;
+    uint8_t* stage = &sX[0][0] + wave * (32 * OS);
+    const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
+    float bv[2][4][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf + e;
+                bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
+            }
+#pragma unroll
+    for (int tl = 0; tl < NV; ++tl) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint2 u;
+                u.x = pack_bf16x2(acc[tl][a][4 * q] + bv[a][q][0], acc[tl][a][4 * q + 1] + bv[a][q][1]);
+                u.y = pack_bf16x2(acc[tl][a][4 * q + 2] + bv[a][q][2], acc[tl][a][4 * q + 3] + bv[a][q][3]);
+                *reinterpret_cast<uint2*>(stage + px * OS + (a * 32 + 8 * q + 4 * khalf) * 2) = u;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int c16 = lane & 7;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int row = it * 8 + (lane >> 3);
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * OS + c16 * 16);
+            const int hw = hw0 + wpos * 32 + row;
+            const int n = (ab0 * 32) + c16 * 8;
+            if (hw < g.HW && n < g.Cout) {  // Cout is a multiple of 8 (checked at the boundary)
+                uint8_t* yrow = reinterpret_cast<uint8_t*>(Y + ((size_t)(b * g.T + t0 + tl) * g.HW + hw) * g.Cout);
+                *reinterpret_cast<uint4*>(yrow + nb + c16 * 16) = v;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+template <int F>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_temporal_frames_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
+    uint16_t* __restrict__ Y, TempGeom g) {
+    static_assert(F >= 1 && F <= 4, "frames per tile");
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][(F + 2) * TEMP_PT * TEMP_XS];
+
+    int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
+    if (tile >= g.ntiles) return;
+    const int ct = tile % g.nct;
+    tile /= g.nct;
+    const int ft = tile % g.nft;
+    tile /= g.nft;
+    const int pt = tile % g.npt;
+    const int b = tile / g.npt;
+    const int t0 = ft * F, hw0 = pt * TEMP_PT;
+    const int nv = min(F, g.T - t0);  // output frames of this tile inside the clip (block-uniform)
+    if (nv >= F)
+        temporal_tile<F, F>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+    else if (nv == 3)
+        temporal_tile<F, (F > 3 ? 3 : F)>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+    else if (nv == 2)
+        temporal_tile<F, (F > 2 ? 2 : F)>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+    else
+        temporal_tile<F, 1>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+}
+
+// Weights in MFMA fragment order for the temporal kernel: fragment f = (kc16 * taps + j) * NA
+// + ab holds, for lane l, the 8 values w[ab * 32 + l % 32][kc16 * 16 + (l / 32) * 8 + e][j],
+// e = 0..7, at element offset (f * 64 + l) * 8 + e; rows past Cout and channels past Cin
+// are zero.  Input layout is torch's [Cout][Cin][taps].
+__global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wf,
+                                                        int Cout, int Cin, int ntaps, int NA, int KC16) {
+    const long long total = (long long)KC16 * ntaps * NA * 512;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const int e = (int)(i & 7), l = (int)((i >> 3) & 63);
+        const long long f = i >> 9;
+        const int ab = (int)(f % NA);
+        const long long f2 = f / NA;
+        const int j = (int)(f2 % ntaps), kc16 = (int)(f2 / ntaps);
+        const int row = ab * 32 + (l & 31), k = kc16 * 16 + (l >> 5) * 8 + e;
+        wf[i] = (row < Cout && k < Cin) ? w[((size_t)row * Cin + k) * ntaps + j] : (uint16_t)0;
+    }
+}
+
+size_t temporal_frag_bytes(int Cout, int Cin) {
+    return (size_t)((Cin + 15) / 16) * 3 * ((Cout + 31) / 32) * 512 * 2;
+}
+
 // Wp[n][tap][c] = w[n][c][tap]  (torch order [Cout][Cin][kernel...] -> K contiguous)
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp,
                                                            int Cout, int Cin, int ntaps) {
@@ -655,6 +900,31 @@ hipError_t launch_tap_t(const uint16_t* X, const uint16_t* Wp, const float* bias
     return hipGetLastError();
 }
 
+#ifndef CVT_TEMP_F
+#define CVT_TEMP_F 4  // output frames per temporal tile
+#endif
+
+hipError_t launch_temporal(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
+                           int B, hipStream_t s) {
+    constexpr int F = CVT_TEMP_F;
+    TempGeom g{};
+    g.B = B; g.T = cg.T; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
+    g.x_bytes = (int)(cg.P * cg.Cin * 2);
+    g.wf_bytes = (int)temporal_frag_bytes(cg.Cout, cg.Cin);
+    g.NA = (cg.Cout + 31) / 32;
+    g.KC16 = (cg.Cin + 15) / 16;
+    g.nct = (cg.Cout + 127) / 128;
+    g.nft = (cg.T + F - 1) / F;
+    g.npt = (g.HW + TEMP_PT - 1) / TEMP_PT;
+    const long long ntiles = (long long)g.nct * g.nft * g.npt * B;
+    if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
+    g.ntiles = (int)ntiles;
+    g.per_xcd = (int)((ntiles + 7) / 8);
+    hipLaunchKernelGGL((conv_temporal_frames_kernel<F>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X, Wf,
+                       bias, Y, g);
+    return hipGetLastError();
+}
+
 template <int KIND>
 hipError_t launch_tap(const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y, const ConvGeom& g,
                       int B, hipStream_t s) {
@@ -672,8 +942,8 @@ hipError_t launch_igemm(int kind, const uint16_t* X, const uint16_t* Wp, const f
     // 32-bit buffer offsets need the input below 2 GiB)
     if (g.Cout >= 64 && kind != POINT && g.P * g.Cin * 2 < 0x7fffffffLL) {
         const int B = (int)(g.P / ((long long)g.T * g.H * g.W));
-        return kind == SPATIAL3 ? launch_tap<SPATIAL3>(X, Wp, bias, Y, g, B, s)
-                                : launch_tap<TEMPORAL3>(X, Wp, bias, Y, g, B, s);
+        if (kind == SPATIAL3) return launch_tap<SPATIAL3>(X, Wp, bias, Y, g, B, s);
+        return launch_tap<TEMPORAL3>(X, Wp, bias, Y, g, B, s);
     }
     if (kind == SPATIAL3) return launch_igemm_k<SPATIAL3>(X, Wp, bias, Y, g, s);
     if (kind == TEMPORAL3) return launch_igemm_k<TEMPORAL3>(X, Wp, bias, Y, g, s);
@@ -691,11 +961,17 @@ hipError_t pack(const void* w, uint16_t* wp, int Cout, int Cin, int ntaps, hipSt
 
 }  // namespace
 
+// packed temporal weights: fragment order for the multi-frame kernel, [Cout][tap][Cin] otherwise
+size_t temporal_pack_bytes(int Cout, int k) {
+    const size_t plain = (size_t)Cout * Cout * k * 2;
+    return align256(k == 3 ? std::max(plain, temporal_frag_bytes(Cout, Cout)) : plain);
+}
+
 size_t conv_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, int k, bool spatial, bool temporal) {
     const size_t P = (size_t)B * T * H * W;
     size_t b = 0;
     if (spatial) b += align256((size_t)Cout * Cin * k * k * 2);
-    if (temporal) b += align256((size_t)Cout * Cout * k * 2);
+    if (temporal) b += temporal_pack_bytes(Cout, k);
     if (spatial && temporal) b += align256(P * Cout * 2);
     return b;
 }
@@ -715,7 +991,7 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     }
     if (w_t) {
         wpt = reinterpret_cast<uint16_t*>(ws + off);
-        off += align256((size_t)Cout * Cout * k * 2);
+        off += temporal_pack_bytes(Cout, k);
     }
     if (w_s && w_t) S = reinterpret_cast<uint16_t*>(ws + off);
     hipError_t e;
@@ -745,10 +1021,20 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     if (!w_t) return hipSuccess;
 
     // temporal part: Cout -> Cout (its input is x itself when there is no spatial part)
-    if ((e = pack(w_t, wpt, Cout, Cout, k, s)) != hipSuccess) return e;
     ConvGeom g{};
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
     g.kchunks = (Cout + BK - 1) / BK;
+    if (k == 3 && Cout >= 64 && P * Cout * 2 < 0x7fffffffLL) {
+        // multi-frame kernel (its 32-bit buffer offsets need the input below 2 GiB)
+        const int NA = (Cout + 31) / 32, KC16 = (Cout + 15) / 16;
+        const long long total = (long long)KC16 * 3 * NA * 512;
+        const long long nblk = std::min((total + 255) / 256, 65535LL);
+        hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)nblk), dim3(256), 0, s, (const uint16_t*)w_t, wpt, Cout,
+                           Cout, 3, NA, KC16);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return launch_temporal(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
+    }
+    if ((e = pack(w_t, wpt, Cout, Cout, k, s)) != hipSuccess) return e;
     return launch_igemm(k == 3 ? TEMPORAL3 : POINT, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
 }
 

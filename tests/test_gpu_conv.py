@@ -49,6 +49,9 @@ CASES = [
     (1, 64, 6, 1, 16, 16, 1, False, False),
     (1, 6, 192, 3, 8, 8, 1, False, True),        # 6 -> 192 lift after dequantization (small-Cin path)
     (1, 16, 24, 2, 4, 4, 1, True, False),        # k = 1 with a temporal 1x1x1 part
+    (2, 128, 128, 7, 6, 11, 3, True, True),      # frame tiles of 4 and 3 output frames, 2 clips
+    (1, 64, 96, 6, 9, 9, 3, True, False),        # frame tiles of 4 and 2, Cout tail in a 128 tile
+    (1, 96, 256, 2, 5, 70, 3, True, True),       # 2 frames only: every region frame but the last two is padding
 ]
 
 
