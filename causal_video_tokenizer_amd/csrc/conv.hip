@@ -557,52 +557,75 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CVT_TAP
 }
 
 // ---------------------------------------------------------------------------------------------
-// Temporal 3-tap convolution over several output frames per workgroup.
+// 3-tap-set convolutions over R output rows per workgroup (the hot kernels).
 //
-// One workgroup (4 waves) computes 128 output channels x 64 positions x F consecutive
-// output frames t0 .. t0+F-1.  Output frame t reads input frames t-2, t-1, t through taps
-// 0, 1, 2, so the tile needs the F+2 input frames t0-2 .. t0+F-1 (the REGION); region
-// frame r meets tap j in output frame t0 + r - j.  Each wave owns 64 channels (two
-// 32-row MFMA blocks) x 32 positions x all F frames: per 16-channel k-step it takes the
-// six weight fragments (3 taps x 2 blocks) once and walks the region frames, each
-// activation fragment feeding up to three taps, i.e. three output frames.
+// Both convolutions are a 3-tap filter along one "row" axis, repeated over KX column
+// shifts:
+//   TEMPORAL3: rows are frames, columns are 64 flattened (h, w) positions; output frame t
+//              reads input frames t-2, t-1, t through taps 0, 1, 2 (KX = 1);
+//   SPATIAL3:  rows are image rows of one frame, columns are 64 pixels of a row plus a
+//              1-pixel halo (66); output row y, pixel x reads input row y-1+ky, pixel
+//              x-1+kx through tap (ky, kx) (KX = 3).
+// One workgroup (4 waves) computes 128 output channels x 64 columns x R consecutive output
+// rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2 temporal,
+// 1 spatial): the REGION, staged once per 32-channel K chunk.  Region row rr meets tap
+// row ky in output row r0 + rr - ky.  Each wave owns 64 channels (two 32-row MFMA blocks)
+// x 32 columns x all R rows: per (16-channel k-step, column shift kx) it takes the six
+// weight fragments (3 tap rows x 2 blocks) once and walks the region rows, each
+// activation fragment feeding up to three tap rows, i.e. three output rows.
 //
-// Only the region is staged in LDS (two 30 KB buffers, so two workgroups share a CU and
-// one's barrier and epilogue overlap the other's MFMAs).  The weights are packed once per
-// call in MFMA fragment order (see pack_frag_kernel): each fragment is 1 KB of which lane
-// l reads bytes [16 l, 16 l + 16), one fully coalesced load straight into the operand
-// registers, prefetched one k-step ahead.  Region chunk loads of step c + 1 are issued
-// after the weight loads of the current step, so waiting for weights never waits for
-// the region.
+// Only the region is staged in LDS (two buffers of about 30 KB, so two workgroups share a
+// CU and one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
+// once per call in MFMA fragment order (see pack_frag_kernel): each fragment is 1 KB of
+// which lane l reads bytes [16 l, 16 l + 16), one coalesced load straight into the operand
+// registers, prefetched one step ahead.  The region loads of chunk c + 1 are issued in two
+// batches during chunk c, each after that step's weight prefetch and stored a few steps
+// later, so a weight wait never waits for a region load issued less than two steps before.
 //
-// Region frames before frame 0 (causal padding) read zeros; output frames past the end
-// are neither computed (the count of valid frames is a compile-time branch per tile) nor
-// stored.  Blocks are mapped to tiles XCD by XCD: block L runs tile
-// (L mod 8) * per_xcd + L / 8, so consecutive tiles - the channel and frame tiles of one
-// position block, which share region frames - land on the same L2.
-struct TempGeom {
-    int B, T, HW, Cin, Cout;
+// Rows and columns outside the tensor read zeros (padding, including the causal frames
+// before 0): every global load is a raw buffer load whose resource is sized to the tensor
+// and padding rows get an offset past its end.  Output rows past the end are neither
+// computed (the count of valid rows is a compile-time branch per tile) nor stored.
+// Blocks are mapped to tiles XCD by XCD: block L runs tile (L mod 8) * per_xcd + L / 8,
+// so consecutive tiles - the channel tiles of one region, then the row tiles above and
+// below it, which re-read two of its rows - share an L2.
+struct RowsGeom {
+    int B, T, H, W, HW, Cin, Cout;
     int x_bytes, wf_bytes;  // buffer-resource extents (the launcher keeps both below 2^31)
     int NA, KC16;           // 32-row weight blocks, 16-channel k-steps
-    int nct, nft, npt;      // channel tiles, frame tiles, position tiles
+    int nct, ncol, nrow;    // channel tiles, column tiles, row tiles
     int ntiles, per_xcd;
 };
 
-constexpr int TEMP_PT = 64;       // positions per tile
-constexpr int TEMP_XS = 64 + 16;  // LDS bytes per region row: 32 channels + 16 bytes of padding
+constexpr int ROWS_XS = 64 + 16;  // LDS bytes per region row: 32 channels + 16 bytes of padding
+constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (tensors stay below it)
 
-template <int F, int NV>
-__device__ __forceinline__ void temporal_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
-                                              const float* __restrict__ bias, uint16_t* __restrict__ Y,
-                                              const TempGeom& g, uint8_t (*sX)[(F + 2) * TEMP_PT * TEMP_XS], int b,
-                                              int ct, int t0, int hw0) {
-    constexpr int NTH = 256, PT = TEMP_PT, NR = F + 2, BK = 32, CPR = BK / 8, XS = TEMP_XS;
-    constexpr int XROWS = NR * PT;
-    constexpr int XL = XROWS * CPR / NTH;
+template <int KIND>
+struct RowsShape {
+    static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;    // column shifts
+    static constexpr int RC = KIND == SPATIAL3 ? 66 : 64;  // region columns
+    static constexpr int OFF = KIND == SPATIAL3 ? 1 : 2;   // rows of look-back (halo or causal pad)
+};
+
+template <int KIND, int R>
+constexpr int rows_region_rows() {
+    return ((R + 2) * RowsShape<KIND>::RC + 7) / 8 * 8;
+}
+
+template <int KIND, int R, int NV, bool TAIL>
+__device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
+                                          const float* __restrict__ bias, uint16_t* __restrict__ Y, const RowsGeom& g,
+                                          uint8_t (*sX)[rows_region_rows<KIND, R>() * ROWS_XS], int b, int t, int ct,
+                                          int r0, int c0) {
+    using S = RowsShape<KIND>;
+    constexpr int NTH = 256, RC = S::RC, KX = S::KX, BK = 32, CPR = BK / 8, XS = ROWS_XS;
+    constexpr int XROWS = rows_region_rows<KIND, R>();
+    constexpr int XQ = XROWS * CPR;
+    constexpr int XL = (XQ + NTH - 1) / NTH;
     constexpr int OOB = 0x7fffffff;
-    constexpr int NRU = NV + 2;  // region frames that feed a valid output frame
-    static_assert(XROWS * CPR % NTH == 0 && XROWS % 8 == 0, "region split");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NRU = NV + 2;  // region rows that feed a valid output row
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in a scalar register
     const int wch = wave & 1, wpos = wave >> 1;
 
     // Region chunk q of a thread is (row, c16) with 8 consecutive lanes on 8 consecutive rows
@@ -615,46 +638,83 @@ __device__ __forceinline__ void temporal_tile(const uint16_t* __restrict__ Wf, c
     int xbase[XL];
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
+        const int q = tid + NTH * i;
         int row, c16;
-        xmap(tid + NTH * i, row, c16);
-        const int r = row / PT, hw = hw0 + row % PT, fr = t0 - 2 + r;
-        const bool ok = r < NRU && fr >= 0 && fr < g.T && hw < g.HW;
-        xbase[i] = ok ? (((b * g.T + fr) * g.HW + hw) * g.Cin + c16 * 8) * 2 : -1;
+        xmap(q, row, c16);
+        const int rr = row / RC, cc = row % RC;
+        bool ok = q < XQ && rr < NRU;
+        int pos = 0;
+        if (KIND == SPATIAL3) {
+            const int y = r0 - 1 + rr, x = c0 - 1 + cc;
+            ok = ok && y >= 0 && y < g.H && x >= 0 && x < g.W;
+            pos = ((b * g.T + t) * g.H + y) * g.W + x;
+        } else {
+            const int fr = r0 - 2 + rr, hw = c0 + cc;
+            ok = ok && fr >= 0 && fr < g.T && hw < g.HW;
+            pos = (b * g.T + fr) * g.HW + hw;
+        }
+        // rows outside the tensor get a base past its end for every chunk (the launcher keeps
+        // the tensor below ROWS_OOB_BASE bytes and chunk offsets below 64 KiB)
+        xbase[i] = ok ? (pos * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
     }
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, g.x_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)Wf, (short)0, g.wf_bytes, 0x00020000);
 
-    uint4 xr[XL];
-    auto load_region = [&](int kc) {  // kc past the last chunk reads zeros
+    // The region of chunk c + 1 goes to the buffer last read in chunk c - 1, free since that
+    // chunk's closing barrier, so it is loaded and stored in two batches inside chunk c
+    // (batch 0: loads i < XH, batch 1: the rest), which halves the staging registers.  With
+    // fewer than 4 steps per chunk there is one batch of all XL loads.
+    constexpr int NS = 2 * KX;                        // steps per chunk: (k-step, column shift)
+    constexpr int XH = NS >= 4 ? (XL + 1) / 2 : XL;  // loads of batch 0 (short chunks: one batch)
+    uint4 xr[XH];
+    auto load_region = [&](int kc, int half) {  // kc past the last chunk reads zeros
 #pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            int row, c16;
-            xmap(tid + NTH * i, row, c16);
-            const bool ok = xbase[i] >= 0 && kc * BK + c16 * 8 < g.Cin;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, ok ? xbase[i] + kc * BK * 2 : OOB, 0, 0);
-            xr[i] = *reinterpret_cast<const uint4*>(&v);
+        for (int i = half * XH; i < (half ? XL : XH); ++i) {
+            int off = xbase[i] + kc * BK * 2;
+            if (TAIL) {  // Cin not a multiple of BK: chunks past Cin read zeros
+                int row, c16;
+                xmap(tid + NTH * i, row, c16);
+                off = kc * BK + c16 * 8 < g.Cin ? off : OOB;
+            }
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0);
+            xr[i - half * XH] = *reinterpret_cast<const uint4*>(&v);
         }
     };
-    auto store_region = [&](int buf) {
+    auto store_region = [&](int buf, int half) {
 #pragma unroll
-        for (int i = 0; i < XL; ++i) {
+        for (int i = half * XH; i < (half ? XL : XH); ++i) {
+            const int q = tid + NTH * i;
             int row, c16;
-            xmap(tid + NTH * i, row, c16);
-            *reinterpret_cast<uint4*>(&sX[buf][row * XS + c16 * 16]) = xr[i];
+            xmap(q, row, c16);
+            if (XQ % NTH == 0 || q < XQ) *reinterpret_cast<uint4*>(&sX[buf][row * XS + c16 * 16]) = xr[i - half * XH];
         }
     };
 
-    // weight fragments of k-step kc16: blocks ab0, ab0 + 1 of taps 0..2 (zeros past the end)
+    // weight fragments of (k-step kc16, column shift kx): tap rows 0..2 of blocks ab0, ab0 + 1
+    // (zeros past the end)
     const int ab0 = ct * 4 + wch * 2;
     bf16x8_t fa[2][3][2];
-    auto load_frags = [&](int kc16, int set) {
+    const int lane16 = lane * 16;
+    auto load_frags = [&](int kc16, int kx, int set) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                const int ab = ab0 + a;
-                const int off = (kc16 < g.KC16 && ab < g.NA) ? (((kc16 * 3 + j) * g.NA + ab) * 64 + lane) * 16 : OOB;
-                fa[set][j][a] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0));
+                const int ab = ab0 + a, tap = ky * KX + kx;
+                // wave-uniform fragment base (scalar) plus the lane's 16 bytes.  Blocks past Cout
+                // only feed outputs that are not stored, and k-steps past the last one are only
+                // the never-used prefetch after the final step, so both are clamped to a valid
+                // fragment (no select: a select here becomes a branch with a full memory wait).
+                // With a channel tail (TAIL) the padded k-step must multiply zeros, so it reads
+                // zeros past the buffer instead.
+                const int abc = min(ab, g.NA - 1);
+                int fbase;
+                if (TAIL)
+                    fbase = kc16 < g.KC16 ? ((kc16 * 3 * KX + tap) * g.NA + abc) * 1024 : OOB - 1024;
+                else
+                    fbase = ((min(kc16, g.KC16 - 1) * 3 * KX + tap) * g.NA + abc) * 1024;
+                const int off = fbase + lane16;
+                fa[set][ky][a] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0));
             }
     };
 
@@ -667,46 +727,74 @@ __device__ __forceinline__ void temporal_tile(const uint16_t* __restrict__ Wf, c
             for (int e = 0; e < 16; ++e) acc[f][a][e] = 0.0f;
 
     const int khalf = lane >> 5, px = lane & 31;
-    auto compute = [&](const uint8_t* xb, int ks, int set) {
+    auto compute = [&](const uint8_t* xb, int ks, int kx, int set) {
         const int ch = ks * 2 + khalf;
         bf16x8_t fb[NRU];
 #pragma unroll
-        for (int r = 0; r < NRU; ++r) fb[r] = *reinterpret_cast<const bf16x8_t*>(xb + r * PT * XS + ch * 16);
+        for (int rr = 0; rr < NRU; ++rr)
+            fb[rr] = *reinterpret_cast<const bf16x8_t*>(xb + (rr * RC + kx) * XS + ch * 16);
 #pragma unroll
-        for (int r = 0; r < NRU; ++r)
+        for (int rr = 0; rr < NRU; ++rr)
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int tl = r - j;
-                if (tl < 0 || tl >= NV) continue;
+            for (int ky = 0; ky < 3; ++ky) {
+                const int ry = rr - ky;
+                if (ry < 0 || ry >= NV) continue;
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
-                    acc[tl][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][j][a], fb[r], acc[tl][a], 0, 0, 0);
+                    acc[ry][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ky][a], fb[rr], acc[ry][a], 0, 0, 0);
             }
     };
 
+    // Steps of a chunk: the weight prefetch of step s + 1 comes first, then the region
+    // batches: batch 0 is loaded at step 0 and stored at step L1, batch 1 loaded at step L1
+    // and stored at the chunk's end (with fewer than 4 steps both are loaded at step 0 and
+    // stored at the end).  The memory counter completes in order, so a weight
+    // wait at step s also waits for every region batch issued before step s - 1.
+    constexpr int L1 = NS >= 4 ? NS / 2 : 0;
+    static_assert(L1 > 0 || XH == XL, "a single batch when both would be in flight together");
     const int nchunks = (g.Cin + BK - 1) / BK;
-    load_frags(0, 0);
-    load_region(0);
-    store_region(0);
+    load_frags(0, 0, 0);
+    load_region(0, 0);
+    store_region(0, 0);
+    if (L1 > 0) {
+        load_region(0, 1);
+        store_region(0, 1);
+    }
     __syncthreads();
     for (int kc = 0; kc < nchunks; ++kc) {
         const uint8_t* xb = sX[kc & 1] + (wpos * 32 + px) * XS;
-        load_frags(2 * kc + 1, 1);
-        load_region(kc + 1);
-        compute(xb, 0, 0);
-        load_frags(2 * kc + 2, 0);
-        compute(xb, 1, 1);
-        store_region((kc + 1) & 1);
+        const int nbuf = (kc + 1) & 1;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int s1 = st + 1;
+            if (s1 < NS)
+                load_frags(2 * kc + s1 / KX, s1 % KX, s1 & 1);
+            else
+                load_frags(2 * kc + 2, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // weight prefetch before any region load
+            if (L1 > 0 && st == L1) store_region(nbuf, 0);
+            if (st == 0) load_region(kc + 1, 0);
+            if (L1 > 0 && st == L1) load_region(kc + 1, 1);
+            // keep the prefetches issued here: left alone the scheduler sinks them towards
+            // their use to save registers, which exposes the memory latency
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xb, st / KX, st % KX, st & 1);
+        }
+        if (L1 == 0)
+            store_region(nbuf, 0);
+        else
+            store_region(nbuf, 1);
         __syncthreads();
     }
 
-    // ---- epilogue: bias, bf16 RNE, staged per frame through a wave-private LDS tile of
-    // 32 positions x 64 channels (rows of 128 bytes + 16 bytes of padding, so the 8-byte
-    // writes of 8 consecutive positions hit distinct banks), then written back with each
-    // 8 consecutive lanes storing one position's 128 contiguous bytes.  The region buffers
+    // ---- epilogue: bias, bf16 RNE, staged per output row through a wave-private LDS tile
+    // of 32 columns x 64 channels (rows of 128 bytes + 16 bytes of padding, so the 8-byte
+    // writes of 8 consecutive columns hit distinct banks), then written back with each 8
+    // consecutive lanes storing one position's 128 contiguous bytes.  The region buffers
     // are free after the last barrier of the K loop; a wave reads back only what it wrote
     // and its LDS accesses execute in order, so no barrier is needed.
     constexpr int OS = 144;
+    static_assert(4 * 32 * OS <= XROWS * XS, "epilogue staging fits in one region buffer");
     uint8_t* stage = &sX[0][0] + wave * (32 * OS);
     const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
     float bv[2][4][4];
@@ -720,63 +808,79 @@ __device__ __forceinline__ void temporal_tile(const uint16_t* __restrict__ Wf, c
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
 #pragma unroll
-    for (int tl = 0; tl < NV; ++tl) {
+    for (int ry = 0; ry < NV; ++ry) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint2 u;
-                u.x = pack_bf16x2(acc[tl][a][4 * q] + bv[a][q][0], acc[tl][a][4 * q + 1] + bv[a][q][1]);
-                u.y = pack_bf16x2(acc[tl][a][4 * q + 2] + bv[a][q][2], acc[tl][a][4 * q + 3] + bv[a][q][3]);
+                u.x = pack_bf16x2(acc[ry][a][4 * q] + bv[a][q][0], acc[ry][a][4 * q + 1] + bv[a][q][1]);
+                u.y = pack_bf16x2(acc[ry][a][4 * q + 2] + bv[a][q][2], acc[ry][a][4 * q + 3] + bv[a][q][3]);
                 *reinterpret_cast<uint2*>(stage + px * OS + (a * 32 + 8 * q + 4 * khalf) * 2) = u;
             }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int c16 = lane & 7;
+        const int n = ab0 * 32 + c16 * 8;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int row = it * 8 + (lane >> 3);
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + row * OS + c16 * 16);
-            const int hw = hw0 + wpos * 32 + row;
-            const int n = (ab0 * 32) + c16 * 8;
-            if (hw < g.HW && n < g.Cout) {  // Cout is a multiple of 8 (checked at the boundary)
-                uint8_t* yrow = reinterpret_cast<uint8_t*>(Y + ((size_t)(b * g.T + t0 + tl) * g.HW + hw) * g.Cout);
-                *reinterpret_cast<uint4*>(yrow + nb + c16 * 16) = v;
+            const int col = it * 8 + (lane >> 3);
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + col * OS + c16 * 16);
+            long long pos;
+            bool ok;
+            if (KIND == SPATIAL3) {
+                const int y = r0 + ry, x = c0 + wpos * 32 + col;
+                ok = x < g.W;
+                pos = (((long long)b * g.T + t) * g.H + y) * g.W + x;
+            } else {
+                const int hw = c0 + wpos * 32 + col;
+                ok = hw < g.HW;
+                pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
             }
+            if (ok && n < g.Cout)  // Cout is a multiple of 8 on this path (checked by the launcher)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(Y + pos * g.Cout) + nb + c16 * 16) = v;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
-template <int F>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_temporal_frames_kernel(
+template <int KIND, int R, bool TAIL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
-    uint16_t* __restrict__ Y, TempGeom g) {
-    static_assert(F >= 1 && F <= 4, "frames per tile");
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][(F + 2) * TEMP_PT * TEMP_XS];
+    uint16_t* __restrict__ Y, RowsGeom g) {
+    static_assert(R >= 1 && R <= 4, "output rows per tile");
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][rows_region_rows<KIND, R>() * ROWS_XS];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
+    // tile order (fastest first): channel tile, row tile, column tile, frame, clip; the
+    // channel tiles of a region and the row tiles that share its look-back rows run back to
+    // back on one XCD
     const int ct = tile % g.nct;
     tile /= g.nct;
-    const int ft = tile % g.nft;
-    tile /= g.nft;
-    const int pt = tile % g.npt;
-    const int b = tile / g.npt;
-    const int t0 = ft * F, hw0 = pt * TEMP_PT;
-    const int nv = min(F, g.T - t0);  // output frames of this tile inside the clip (block-uniform)
-    if (nv >= F)
-        temporal_tile<F, F>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+    const int rt = tile % g.nrow;
+    tile /= g.nrow;
+    const int cl = tile % g.ncol;
+    tile /= g.ncol;
+    int t = 0, b = tile;
+    if (KIND == SPATIAL3) {
+        t = tile % g.T;
+        b = tile / g.T;
+    }
+    const int r0 = rt * R, c0 = cl * 64;
+    const int nv = min(R, (KIND == SPATIAL3 ? g.H : g.T) - r0);  // valid output rows (block-uniform)
+    if (nv >= R)
+        rows_tile<KIND, R, R, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else if (nv == 3)
-        temporal_tile<F, (F > 3 ? 3 : F)>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+        rows_tile<KIND, R, (R > 3 ? 3 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else if (nv == 2)
-        temporal_tile<F, (F > 2 ? 2 : F)>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+        rows_tile<KIND, R, (R > 2 ? 2 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else
-        temporal_tile<F, 1>(Wf, X, bias, Y, g, sX, b, ct, t0, hw0);
+        rows_tile<KIND, R, 1, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
 }
 
-// Weights in MFMA fragment order for the temporal kernel: fragment f = (kc16 * taps + j) * NA
+// Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
 // + ab holds, for lane l, the 8 values w[ab * 32 + l % 32][kc16 * 16 + (l / 32) * 8 + e][j],
 // e = 0..7, at element offset (f * 64 + l) * 8 + e; rows past Cout and channels past Cin
 // are zero.  Input layout is torch's [Cout][Cin][taps].
@@ -795,8 +899,8 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restri
     }
 }
 
-size_t temporal_frag_bytes(int Cout, int Cin) {
-    return (size_t)((Cin + 15) / 16) * 3 * ((Cout + 31) / 32) * 512 * 2;
+size_t frag_bytes(int Cout, int Cin, int ntaps) {
+    return (size_t)((Cin + 15) / 16) * ntaps * ((Cout + 31) / 32) * 512 * 2;
 }
 
 // Wp[n][tap][c] = w[n][c][tap]  (torch order [Cout][Cin][kernel...] -> K contiguous)
@@ -900,28 +1004,41 @@ hipError_t launch_tap_t(const uint16_t* X, const uint16_t* Wp, const float* bias
     return hipGetLastError();
 }
 
-#ifndef CVT_TEMP_F
-#define CVT_TEMP_F 4  // output frames per temporal tile
+#ifndef CVT_ROWS_R
+#define CVT_ROWS_R 4  // output rows (frames or image rows) per tile
 #endif
 
-hipError_t launch_temporal(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
-                           int B, hipStream_t s) {
-    constexpr int F = CVT_TEMP_F;
-    TempGeom g{};
-    g.B = B; g.T = cg.T; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
+// conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes
+template <int KIND>
+hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
+                       int B, hipStream_t s) {
+    constexpr int R = CVT_ROWS_R;
+    RowsGeom g{};
+    g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
     g.x_bytes = (int)(cg.P * cg.Cin * 2);
-    g.wf_bytes = (int)temporal_frag_bytes(cg.Cout, cg.Cin);
+    g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
     g.NA = (cg.Cout + 31) / 32;
     g.KC16 = (cg.Cin + 15) / 16;
     g.nct = (cg.Cout + 127) / 128;
-    g.nft = (cg.T + F - 1) / F;
-    g.npt = (g.HW + TEMP_PT - 1) / TEMP_PT;
-    const long long ntiles = (long long)g.nct * g.nft * g.npt * B;
+    long long ntiles;
+    if (KIND == SPATIAL3) {
+        g.ncol = (cg.W + 63) / 64;
+        g.nrow = (cg.H + R - 1) / R;
+        ntiles = (long long)g.nct * g.ncol * g.nrow * cg.T * B;
+    } else {
+        g.ncol = (g.HW + 63) / 64;
+        g.nrow = (cg.T + R - 1) / R;
+        ntiles = (long long)g.nct * g.ncol * g.nrow * B;
+    }
     if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
-    hipLaunchKernelGGL((conv_temporal_frames_kernel<F>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X, Wf,
-                       bias, Y, g);
+    if (cg.Cin % 32 == 0)
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, false>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
+                           Wf, bias, Y, g);
+    else
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, true>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
+                           Wf, bias, Y, g);
     return hipGetLastError();
 }
 
@@ -961,17 +1078,30 @@ hipError_t pack(const void* w, uint16_t* wp, int Cout, int Cin, int ntaps, hipSt
 
 }  // namespace
 
-// packed temporal weights: fragment order for the multi-frame kernel, [Cout][tap][Cin] otherwise
-size_t temporal_pack_bytes(int Cout, int k) {
-    const size_t plain = (size_t)Cout * Cout * k * 2;
-    return align256(k == 3 ? std::max(plain, temporal_frag_bytes(Cout, Cout)) : plain);
+// packed weights of one convolution: the larger of the fragment order used by
+// conv_rows_kernel and the [Cout][tap][Cin] order used by the other kernels
+size_t pack_bytes(int Cout, int Cin, int ntaps) {
+    return align256(std::max((size_t)Cout * Cin * ntaps * 2, frag_bytes(Cout, Cin, ntaps)));
+}
+
+bool use_rows_kernel(int k, int Cout, long long P, int Cin) {
+    return k == 3 && Cout >= 64 && Cout % 8 == 0 && P * Cin * 2 < ROWS_OOB_BASE;
+}
+
+hipError_t pack_frag(const void* w, uint16_t* wf, int Cout, int Cin, int ntaps, hipStream_t s) {
+    const int NA = (Cout + 31) / 32, KC16 = (Cin + 15) / 16;
+    const long long total = (long long)KC16 * ntaps * NA * 512;
+    const long long nblk = std::min((total + 255) / 256, 65535LL);
+    hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)nblk), dim3(256), 0, s, (const uint16_t*)w, wf, Cout, Cin,
+                       ntaps, NA, KC16);
+    return hipGetLastError();
 }
 
 size_t conv_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, int k, bool spatial, bool temporal) {
     const size_t P = (size_t)B * T * H * W;
     size_t b = 0;
-    if (spatial) b += align256((size_t)Cout * Cin * k * k * 2);
-    if (temporal) b += temporal_pack_bytes(Cout, k);
+    if (spatial) b += pack_bytes(Cout, Cin, k * k);
+    if (temporal) b += pack_bytes(Cout, Cout, k);
     if (spatial && temporal) b += align256(P * Cout * 2);
     return b;
 }
@@ -987,11 +1117,11 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     uint16_t* S = nullptr;
     if (w_s) {
         wps = reinterpret_cast<uint16_t*>(ws + off);
-        off += align256((size_t)Cout * Cin * k * k * 2);
+        off += pack_bytes(Cout, Cin, k * k);
     }
     if (w_t) {
         wpt = reinterpret_cast<uint16_t*>(ws + off);
-        off += temporal_pack_bytes(Cout, k);
+        off += pack_bytes(Cout, Cout, k);
     }
     if (w_s && w_t) S = reinterpret_cast<uint16_t*>(ws + off);
     hipError_t e;
@@ -1009,12 +1139,18 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
                                (const uint16_t*)w_s, b_s, sout, P, Cin, Cout);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else {
-            if ((e = pack(w_s, wps, Cout, Cin, k * k, s)) != hipSuccess) return e;
             ConvGeom g{};
             g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cin; g.Cout = Cout;
             g.kchunks = (Cin + BK - 1) / BK;
-            if ((e = launch_igemm(k == 3 ? SPATIAL3 : POINT, (const uint16_t*)x, wps, b_s, sout, g, s)) != hipSuccess)
-                return e;
+            if (use_rows_kernel(k, Cout, P, Cin)) {
+                if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+                if ((e = launch_rows<SPATIAL3>((const uint16_t*)x, wps, b_s, sout, g, B, s)) != hipSuccess) return e;
+            } else {
+                if ((e = pack(w_s, wps, Cout, Cin, k * k, s)) != hipSuccess) return e;
+                if ((e = launch_igemm(k == 3 ? SPATIAL3 : POINT, (const uint16_t*)x, wps, b_s, sout, g, s)) !=
+                    hipSuccess)
+                    return e;
+            }
         }
         tin = S;
     }
@@ -1024,15 +1160,9 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     ConvGeom g{};
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
     g.kchunks = (Cout + BK - 1) / BK;
-    if (k == 3 && Cout >= 64 && P * Cout * 2 < 0x7fffffffLL) {
-        // multi-frame kernel (its 32-bit buffer offsets need the input below 2 GiB)
-        const int NA = (Cout + 31) / 32, KC16 = (Cout + 15) / 16;
-        const long long total = (long long)KC16 * 3 * NA * 512;
-        const long long nblk = std::min((total + 255) / 256, 65535LL);
-        hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)nblk), dim3(256), 0, s, (const uint16_t*)w_t, wpt, Cout,
-                           Cout, 3, NA, KC16);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        return launch_temporal(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
+    if (use_rows_kernel(k, Cout, P, Cout)) {
+        if ((e = pack_frag(w_t, wpt, Cout, Cout, 3, s)) != hipSuccess) return e;
+        return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
     }
     if ((e = pack(w_t, wpt, Cout, Cout, k, s)) != hipSuccess) return e;
     return launch_igemm(k == 3 ? TEMPORAL3 : POINT, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
