@@ -169,7 +169,7 @@ def main():
     achieved = conv_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "conv_tap_gemm_kernel<SPATIAL3,256,8,64,8> (1x3x3 conv 192->256, bf16 MFMA)",
+                "kernel": "conv_rows_kernel<SPATIAL3,4,false> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)

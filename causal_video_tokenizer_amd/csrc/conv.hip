@@ -15,21 +15,16 @@
 // taps are (j - (k-1), 0, 0), so frames before 0 read zeros (causal left
 // padding) and no frame after t is ever read.
 //
-// Weights are repacked once per call into [Cout][tap][Cin] (K contiguous per
-// output channel) so both operands stream 16-byte chunks of 8 channels.
-//
-// Kernel structure (one workgroup = 4 wavefronts, a TC x TP output tile):
-//   * K is walked in steps of (one tap, 64 input channels).  Each step stages a
-//     TC x 64 weight tile and a TP x 64 activation tile in LDS, rows of 128
-//     bytes whose 16-byte chunks are XOR-swizzled by (row / 2) mod 8 so that
-//     the MFMA operand reads of 16 consecutive lanes touch 16 distinct chunk
-//     positions.
-//   * The global loads of step s + 1 are issued into registers before the
-//     MFMAs of step s, so memory latency overlaps the matrix work.
-//   * Each wave owns a (TC / WC) x (TP / WP) sub-tile as 32 x 32 blocks and
-//     issues v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
-//   * The epilogue adds the optional fp32 bias, rounds to bf16 (RNE) and
-//     stores 4 consecutive output channels (8 bytes) per lane and block row.
+// Kernels:
+//   * conv_rows_kernel - the hot path, k = 3 with Cout >= 64 and Cout % 8 == 0:
+//     both parts as a 3-tap filter along a row axis (image rows or frames), R
+//     output rows per workgroup sharing one staged input region, weights read
+//     from L2 in MFMA fragment order (layout and schedule at the kernel);
+//   * conv_igemm_kernel - every other shape (k = 1 projections, narrow outputs):
+//     one tap x 64 input channels per K step, weight and activation tiles staged
+//     in LDS with XOR-swizzled 128-byte rows, 4 waves of 32 x 32 MFMA blocks;
+//   * pointwise_small_kernel - 1 x 1 x 1 with at most 16 input channels (fp32 FMA).
+// All of them add the optional fp32 bias and round to bf16 (RNE) once.
 #include <algorithm>
 
 #include "cvt_internal.h"
@@ -39,30 +34,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// Tile shape of the 3-tap kernels: patch rows (32 positions each) per tile and
-// input channels per K step, for the spatial (_S) and temporal (_T) kernels.
-#ifndef CVT_TAP_PR_S
-#define CVT_TAP_PR_S 8
-#endif
-#ifndef CVT_TAP_BK_S
-#define CVT_TAP_BK_S 64
-#endif
-#ifndef CVT_TAP_PR_T
-#define CVT_TAP_PR_T 8
-#endif
-#ifndef CVT_TAP_BK_T
-#define CVT_TAP_BK_T 32
-#endif
-#ifndef CVT_TAP_NW_S
-#define CVT_TAP_NW_S 8  // waves per workgroup
-#endif
-#ifndef CVT_TAP_WPE
-#define CVT_TAP_WPE 1   // minimum waves per SIMD the register allocation must allow
-#endif
-#ifndef CVT_TAP_NW_T
-#define CVT_TAP_NW_T 8
-#endif
 
 constexpr int BK = 64;          // input channels per K step
 constexpr int ROWB = BK * 2;    // bytes per LDS row
@@ -244,303 +215,6 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
                     v[e] = acc[a][b][4 * q + e];
                     if (bias && n + e < g.Cout) v[e] += bias[n + e];
                 }
-                if (vec_store && n + 3 < g.Cout) {
-                    uint2 u;
-                    u.x = pack_bf16x2(v[0], v[1]);
-                    u.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(yrow + n) = u;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < g.Cout) yrow[n + e] = f32_to_bf16(v[e]);
-                }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// 3-tap-set convolutions with a shared input region (the hot kernels).
-//
-// One workgroup computes a TC x TP output tile (TC output channels, TP = 32 * PR
-// positions) with 4 waves as 2 (channels) x 2 (positions), each wave TC/2 x TP/2 in
-// fp32 accumulators (v_mfma_f32_32x32x16_bf16).  K is walked as 32-channel chunks;
-// inside a chunk the taps are unrolled at compile time.  For each chunk the
-// workgroup stages in LDS the REGION of input rows that all taps of the tile read:
-//   SPATIAL3:  a PR x 32 patch plus a 1-pixel halo, (PR+2) x 34 rows; tap (ky, kx)
-//              reads the window starting at region row ky * 34 + kx, so the 9 taps
-//              share one load of the halo instead of nine;
-//   TEMPORAL3: the TP positions at frames t-2, t-1, t (3 * TP rows); tap j reads
-//              block j.
-// Rows outside the image or before frame 0 read zeros (the padding): every global
-// load is a raw buffer load whose resource is sized to the tensor, and padding rows
-// get an offset past its end.  Each region row holds 32 bf16 channels (64 bytes)
-// whose 16-byte chunks are XOR-swizzled with (row / 4) mod 4, so the MFMA operand
-// reads of 16 consecutive rows hit distinct banks.
-//
-// Pipelining with one barrier per tap step: the weight tile of step s + 1 is loaded
-// into registers at the start of step s and stored to the other LDS weight buffer at
-// its end; the region of chunk c + 1 is loaded at the start of tap 0 (after that
-// step's weight loads, so waiting for the weights never waits for it) and stored to
-// the other region buffer at the end of tap 1.  Inside a step the operand fragments
-// of k-substep ks + 1 are read before the MFMAs of substep ks.  Every step issues the
-// same loads (out-of-range ones read zeros), so all wait counts are static.
-struct TapGeom {
-    int B, T, H, W;
-    int Cin, Cout;
-    int x_bytes, w_bytes;  // buffer-resource extents (the launcher keeps both below 2^31)
-    int nct;               // output-channel tiles
-    int ntx, nty;          // spatial patches along W and H (SPATIAL3)
-    int nthw;              // TP-position blocks per frame (TEMPORAL3)
-};
-
-template <int KIND, int PR>
-struct RegionShape;
-template <int PR>
-struct RegionShape<SPATIAL3, PR> {
-    static constexpr int PW = 32, RW = PW + 2, rows = (PR + 2) * RW, taps = 9;
-    // region row of tap j for patch row py, column px
-    __device__ static constexpr int row(int j, int py, int px) { return (py + j / 3) * RW + px + j % 3; }
-};
-template <int PR>
-struct RegionShape<TEMPORAL3, PR> {
-    static constexpr int TP = 32 * PR, rows = 3 * TP, taps = 3;
-    __device__ static constexpr int row(int j, int py, int px) { return j * TP + py * 32 + px; }
-};
-
-// XOR swizzle of the 16-byte chunks of an LDS row: 64-byte rows (4 chunks) use
-// (row / 4) mod 4, 128-byte rows (8 chunks) use (row / 2) mod 8; either way 16
-// consecutive rows read at one logical chunk land on 16 distinct bank groups.
-template <int ROWB>
-__device__ __forceinline__ int swz(int row, int chunk) {
-    if constexpr (ROWB == 64)
-        return chunk ^ ((row >> 2) & 3);
-    else
-        return chunk ^ ((row >> 1) & 7);
-}
-
-template <int KIND, int TC, int PR, int BK, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CVT_TAP_WPE))) void conv_tap_gemm_kernel(const uint16_t* __restrict__ X,
-                                                            const uint16_t* __restrict__ Wp,
-                                                            const float* __restrict__ bias,
-                                                            uint16_t* __restrict__ Y, TapGeom g) {
-    using RS = RegionShape<KIND, PR>;
-    constexpr int ROWB = BK * 2, TP = 32 * PR;
-    constexpr int CPR = BK / 8;                                // 16-byte chunks per row
-    constexpr int NT = RS::taps;
-    constexpr int NREG = RS::rows;
-    constexpr int NTH = NW * 64;                               // threads
-    constexpr int WPN = NW / 2;                                // waves along positions
-    constexpr int FA = TC / 64, FB = PR / WPN;                 // 32-blocks per wave
-    constexpr int KS = BK / 16;                                // 16-wide k-substeps per step
-    constexpr int XL = (NREG * CPR + NTH - 1) / NTH;           // region chunk-loads per thread
-    constexpr int WL = (TC * CPR + NTH - 1) / NTH;             // weight chunk-loads per thread
-    constexpr int OOB = 0x7fffffff;
-    static_assert(TC % 64 == 0 && PR % WPN == 0 && FB >= 1, "tile shape");
-
-    // Region rows are padded by 16 bytes instead of swizzled: a stride of 5 or 9
-    // 16-byte units maps 16 consecutive rows to distinct bank groups, and every tap's
-    // window is a constant offset from one per-lane base address.
-    constexpr int XS = ROWB + 16;
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][TC * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][NREG * XS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wc = wave & 1, wp = wave >> 1;  // 2 waves along channels, WPN along positions
-
-    // ---- tile coordinates
-    long long tile = blockIdx.x;
-    const int ct = (int)(tile % g.nct);
-    tile /= g.nct;
-    int b, t, y0 = 0, x0 = 0, hw0 = 0;
-    if (KIND == SPATIAL3) {
-        const int tx = (int)(tile % g.ntx);
-        tile /= g.ntx;
-        const int ty = (int)(tile % g.nty);
-        tile /= g.nty;
-        t = (int)(tile % g.T);
-        b = (int)(tile / g.T);
-        y0 = ty * PR;
-        x0 = tx * 32;
-    } else {
-        const int th = (int)(tile % g.nthw);
-        tile /= g.nthw;
-        t = (int)(tile % g.T);
-        b = (int)(tile / g.T);
-        hw0 = th * TP;
-    }
-    const int n0 = ct * TC;
-    const int HW = g.H * g.W;
-
-    // ---- per-thread region load descriptors: byte offset of channel 0, or OOB
-    int xbase[XL];
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-        const int row = (tid + NTH * i) / CPR;
-        int pos = -1;
-        if (row < NREG) {
-            if (KIND == SPATIAL3) {
-                constexpr int RW = RegionShape<SPATIAL3, PR>::RW;
-                const int y = y0 - 1 + row / RW, x = x0 - 1 + row % RW;
-                if (y >= 0 && y < g.H && x >= 0 && x < g.W) pos = ((b * g.T + t) * g.H + y) * g.W + x;
-            } else {
-                const int fr = t + row / TP - 2;
-                const int hw = hw0 + row % TP;
-                if (fr >= 0 && hw < HW) pos = (b * g.T + fr) * HW + hw;
-            }
-        }
-        xbase[i] = pos >= 0 ? (pos * g.Cin + ((tid + NTH * i) % CPR) * 8) * 2 : -1;
-    }
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, g.x_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)Wp, (short)0, g.w_bytes, 0x00020000);
-    // weight rows of this thread: byte offset of (n, tap 0, channel chunk), or -1
-    int wbase[WL];
-#pragma unroll
-    for (int i = 0; i < WL; ++i) {
-        const int q = tid + NTH * i;
-        const int n = n0 + q / CPR;
-        wbase[i] = (q < TC * CPR && n < g.Cout) ? (n * NT * g.Cin + (q % CPR) * 8) * 2 : -1;
-    }
-
-    uint4 xr[XL], wr[WL];
-    auto load_region = [&](int kc) {  // kc >= nchunks reads zeros
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int cb = kc * BK * 2;
-            const bool ok = xbase[i] >= 0 && kc * BK + ((tid + NTH * i) % CPR) * 8 < g.Cin;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, ok ? xbase[i] + cb : OOB, 0, 0);
-            xr[i] = *reinterpret_cast<const uint4*>(&v);
-        }
-    };
-    auto store_region = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int q = tid + NTH * i;
-            const int row = q / CPR, c16 = q % CPR;
-            if (row < NREG) *reinterpret_cast<uint4*>(&sX[buf][row * XS + c16 * 16]) = xr[i];
-        }
-    };
-    auto load_weights = [&](int tap, int kc) {  // kc >= nchunks reads zeros
-#pragma unroll
-        for (int i = 0; i < WL; ++i) {
-            const int c = kc * BK + ((tid + NTH * i) % CPR) * 8;
-            const bool ok = wbase[i] >= 0 && c < g.Cin;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                wres, ok ? wbase[i] + (tap * g.Cin + kc * BK) * 2 : OOB, 0, 0);
-            wr[i] = *reinterpret_cast<const uint4*>(&v);
-        }
-    };
-    auto store_weights = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < WL; ++i) {
-            const int q = tid + NTH * i;
-            const int row = q / CPR, c16 = q % CPR;
-            if (row < TC) *reinterpret_cast<uint4*>(&sW[buf][row * ROWB + swz<ROWB>(row, c16) * 16]) = wr[i];
-        }
-    };
-
-    f32x16_t acc[FA][FB];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int bb = 0; bb < FB; ++bb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][bb][e] = 0.0f;
-
-    const int nchunks = (g.Cin + BK - 1) / BK;
-    const int arow0 = wc * (TC / 2) + (lane & 31);   // A-fragment row of block 0
-    const int khalf = lane >> 5;                      // which 8-channel half of a 16-k step
-    const int px = lane & 31;
-
-    // operand fragments: two sets (current k-substep and the next one)
-    bf16x8_t fa[2][FA], fb[2][FB];
-    auto read_frags = [&](const uint8_t* wbuf, const uint8_t* xlane, int tap, int ks, int set) {
-        const int ch = ks * 2 + khalf;
-#pragma unroll
-        for (int a = 0; a < FA; ++a) {
-            const int row = arow0 + a * 32;
-            fa[set][a] = *reinterpret_cast<const bf16x8_t*>(wbuf + row * ROWB + swz<ROWB>(row, ch) * 16);
-        }
-#pragma unroll
-        for (int bb = 0; bb < FB; ++bb)
-            fb[set][bb] =
-                *reinterpret_cast<const bf16x8_t*>(xlane + (RS::row(tap, wp * FB + bb, 0) * XS + ch * 16));
-    };
-
-    // prologue: region of chunk 0 and weights of (chunk 0, tap 0)
-    load_weights(0, 0);
-    load_region(0);
-    store_weights(0);
-    store_region(0);
-    __syncthreads();
-
-    int wbuf_i = 0;
-    for (int kc = 0; kc < nchunks; ++kc) {
-        const uint8_t* xlane = sX[kc & 1] + px * XS;  // this lane's column of the region
-#pragma unroll
-        for (int tap = 0; tap < NT; ++tap) {
-            // next step's weights (zeros past the last step), then at tap 0 the next region
-            if (tap + 1 < NT)
-                load_weights(tap + 1, kc);
-            else
-                load_weights(0, kc + 1);
-            if (tap == 0) load_region(kc + 1);
-
-            const uint8_t* wbuf = sW[wbuf_i];
-            read_frags(wbuf, xlane, tap, 0, 0);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 1 < KS) read_frags(wbuf, xlane, tap, ks + 1, (ks + 1) & 1);
-#pragma unroll
-                for (int a = 0; a < FA; ++a)
-#pragma unroll
-                    for (int bb = 0; bb < FB; ++bb)
-                        acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][bb], acc[a][bb],
-                                                                              0, 0, 0);
-            }
-
-            store_weights(wbuf_i ^ 1);
-            if (tap == 1) store_region((kc + 1) & 1);
-            __syncthreads();
-            wbuf_i ^= 1;
-        }
-    }
-
-    // ---- epilogue: bias, bf16 RNE, 4 consecutive channels (8 bytes) per store
-    const bool vec_store = (g.Cout & 3) == 0;
-    float bv[FA][4][4];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = n0 + wc * (TC / 2) + a * 32 + 8 * q + 4 * khalf + e;
-                bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
-            }
-#pragma unroll
-    for (int bb = 0; bb < FB; ++bb) {
-        long long pos;
-        bool pvalid;
-        if (KIND == SPATIAL3) {
-            const int y = y0 + wp * FB + bb, x = x0 + px;
-            pvalid = y < g.H && x < g.W;
-            pos = (((long long)b * g.T + t) * g.H + y) * g.W + x;
-        } else {
-            const int hw = hw0 + (wp * FB + bb) * 32 + px;
-            pvalid = hw < HW;
-            pos = ((long long)b * g.T + t) * HW + hw;
-        }
-        if (!pvalid) continue;
-        uint16_t* yrow = Y + (size_t)pos * g.Cout;
-#pragma unroll
-        for (int a = 0; a < FA; ++a) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wc * (TC / 2) + a * 32 + 8 * q + 4 * khalf;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[a][bb][4 * q + e] + bv[a][q][e];
                 if (vec_store && n + 3 < g.Cout) {
                     uint2 u;
                     u.x = pack_bf16x2(v[0], v[1]);
@@ -981,29 +655,6 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
     return launch_igemm_t<KIND, 256, 128, 2, 2>(X, Wp, bias, Y, g, s);
 }
 
-template <int KIND, int TC, int PR, int BK, int NW>
-hipError_t launch_tap_t(const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y, const ConvGeom& cg,
-                        int B, hipStream_t s) {
-    TapGeom g{};
-    g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
-    g.x_bytes = (int)(cg.P * cg.Cin * 2);
-    g.w_bytes = (int)((long long)cg.Cout * (KIND == SPATIAL3 ? 9 : 3) * cg.Cin * 2);
-    g.nct = (cg.Cout + TC - 1) / TC;
-    long long nblk;
-    if (KIND == SPATIAL3) {
-        g.ntx = (cg.W + 31) / 32;
-        g.nty = (cg.H + PR - 1) / PR;
-        nblk = (long long)g.nct * g.ntx * g.nty * cg.T * B;
-    } else {
-        g.nthw = (int)(((long long)cg.H * cg.W + 32 * PR - 1) / (32 * PR));
-        nblk = (long long)g.nct * g.nthw * cg.T * B;
-    }
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((conv_tap_gemm_kernel<KIND, TC, PR, BK, NW>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, X, Wp,
-                       bias, Y, g);
-    return hipGetLastError();
-}
-
 #ifndef CVT_ROWS_R
 #define CVT_ROWS_R 4  // output rows (frames or image rows) per tile
 #endif
@@ -1042,26 +693,8 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     return hipGetLastError();
 }
 
-template <int KIND>
-hipError_t launch_tap(const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y, const ConvGeom& g,
-                      int B, hipStream_t s) {
-    constexpr int PR = KIND == SPATIAL3 ? CVT_TAP_PR_S : CVT_TAP_PR_T;
-    constexpr int BKT = KIND == SPATIAL3 ? CVT_TAP_BK_S : CVT_TAP_BK_T;
-    constexpr int NW = KIND == SPATIAL3 ? CVT_TAP_NW_S : CVT_TAP_NW_T;
-    if (g.Cout <= 128) return launch_tap_t<KIND, 128, PR, BKT, NW>(X, Wp, bias, Y, g, B, s);
-    if (g.Cout <= 192) return launch_tap_t<KIND, 192, PR, BKT, NW>(X, Wp, bias, Y, g, B, s);
-    return launch_tap_t<KIND, 256, PR, BKT, NW>(X, Wp, bias, Y, g, B, s);
-}
-
 hipError_t launch_igemm(int kind, const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y,
                         const ConvGeom& g, hipStream_t s) {
-    // 3-tap sets with wide enough output go to the shared-region kernels (their
-    // 32-bit buffer offsets need the input below 2 GiB)
-    if (g.Cout >= 64 && kind != POINT && g.P * g.Cin * 2 < 0x7fffffffLL) {
-        const int B = (int)(g.P / ((long long)g.T * g.H * g.W));
-        if (kind == SPATIAL3) return launch_tap<SPATIAL3>(X, Wp, bias, Y, g, B, s);
-        return launch_tap<TEMPORAL3>(X, Wp, bias, Y, g, B, s);
-    }
     if (kind == SPATIAL3) return launch_igemm_k<SPATIAL3>(X, Wp, bias, Y, g, s);
     if (kind == TEMPORAL3) return launch_igemm_k<TEMPORAL3>(X, Wp, bias, Y, g, s);
     return launch_igemm_k<POINT>(X, Wp, bias, Y, g, s);

@@ -63,11 +63,8 @@ __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
 // Level-set descriptors.  Runtime<D>: everything read from FsqParams.  Default:
 // the levels (8,8,8,5,5,5) of the pages, with compile-time breakpoint counts,
 // place values and power-of-two code scales (thresholds stay runtime values).
-struct RuntimeLevels {
-    static constexpr bool fixed = false;
-};
+struct RuntimeLevels {};
 struct DefaultLevels {
-    static constexpr bool fixed = true;
     static constexpr int D = 6;
     __device__ static constexpr int L(int i) { return i < 3 ? 8 : 5; }
     __device__ static constexpr int nthr(int i) { return L(i) - 1; }
