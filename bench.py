@@ -39,6 +39,15 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COPY_CAL_BYTES = 256 * 1024 * 1024
 
+# HBM traffic of one launch of the dominant kernel (conv_rows_kernel<SPATIAL3, 4, false>,
+# 1x3x3 192->256 on the 13 x 180 x 320 latent grid), from two rocprofv3 --pmc passes over
+# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
+# what it reads for the 256 MiB device copy this script issues after timing: FETCH_SIZE
+# reads 131106.4 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
+# for the kernel version the counters were taken on: set to None when it changes.
+SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 237772.3, 374400.0
+COPY_FETCH_KIB, COPY_WRITE_KIB = 131106.4, 262144.0
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -168,7 +177,9 @@ def main():
     dom = "conv_spatial"
     achieved = conv_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": 2.0 * P * (192 + 256) + 2.0 * 256 * 192 * 9,
                 "kernel": "conv_rows_kernel<SPATIAL3,4,false> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
@@ -211,6 +222,13 @@ def main():
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
+
+
+def traffic_bytes():
+    if SPATIAL_FETCH_KIB is None:
+        return None
+    cal = COPY_CAL_BYTES / 1024.0
+    return round(1024.0 * (SPATIAL_FETCH_KIB * cal / COPY_FETCH_KIB + SPATIAL_WRITE_KIB * cal / COPY_WRITE_KIB))
 
 
 def cv8x8x8_chain(cvt, si, torch, dev, args):
