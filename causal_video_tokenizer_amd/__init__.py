@@ -105,6 +105,21 @@ def _layout_of(t):
     raise ValueError("5-D tensors must be contiguous (NCTHW) or channels_last_3d (NTHWC)")
 
 
+def _check_out(t, shape, dtype, device, layout=None, what="out"):
+    """A caller-provided output must match what the kernel writes: logical shape, dtype,
+    device and memory layout (NTHWC = channels_last_3d, else C-contiguous)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    fmt = torch.channels_last_3d if layout == CVT_NTHWC else torch.contiguous_format
+    if not t.is_contiguous(memory_format=fmt):
+        raise ValueError(f"{what} must be {'channels_last_3d (NTHWC)' if layout == CVT_NTHWC else 'contiguous'}")
+    return t
+
+
 def _empty5(shape, dtype, device, layout):
     mf = torch.channels_last_3d if layout == CVT_NTHWC else torch.contiguous_format
     return torch.empty(shape, dtype=dtype, device=device, memory_format=mf)
@@ -118,12 +133,12 @@ def haar3d_fwd(x, temporal_levels=2, out_dtype=None, layout="NTHWC", out=None):
         raise ValueError("x must be NCTHW-contiguous")
     B, C, T, H, W = x.shape
     lay = CVT_NTHWC if layout == "NTHWC" else CVT_NCTHW
-    odt = out_dtype or x.dtype
+    odt = out_dtype or (out.dtype if out is not None else x.dtype)
     if temporal_levels == 2:
         shape = (B, 64 * C, 1 + max(T - 1, 0) // 4, H // 4, W // 4)
     else:
         shape = (B, 16 * C, T, H // 4, W // 4)
-    y = out if out is not None else _empty5(shape, odt, x.device, lay)
+    y = _check_out(out, shape, odt, x.device, lay) if out is not None else _empty5(shape, odt, x.device, lay)
     _check(lib.cvt_haar3d_fwd(_ptr(x), _dtype_code(x.dtype), _ptr(y), _dtype_code(y.dtype), lay,
                               B, C, T, H, W, temporal_levels, _stream(x.device)), "haar3d_fwd")
     return y
@@ -140,8 +155,9 @@ def haar3d_inv(y, temporal_levels=2, out_dtype=None, out=None):
         raise ValueError(f"coefficient channels must be a multiple of {G}")
     C = NCH // G
     T = 4 * Tq - 3 if temporal_levels == 2 else Tq
-    odt = out_dtype or y.dtype
-    x = out if out is not None else torch.empty((B, C, T, 4 * Hq, 4 * Wq), dtype=odt, device=y.device)
+    odt = out_dtype or (out.dtype if out is not None else y.dtype)
+    shape = (B, C, T, 4 * Hq, 4 * Wq)
+    x = _check_out(out, shape, odt, y.device) if out is not None else torch.empty(shape, dtype=odt, device=y.device)
     _check(lib.cvt_haar3d_inv(_ptr(y), _dtype_code(y.dtype), lay, _ptr(x), _dtype_code(x.dtype),
                               B, C, T, 4 * Hq, 4 * Wq, temporal_levels, _stream(y.device)), "haar3d_inv")
     return x
@@ -187,7 +203,9 @@ def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out
     need = conv_workspace_bytes(x.shape, Cout, k, w_s is not None, w_t is not None)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    y = out if out is not None else _empty5((B, Cout, T, H, W), torch.bfloat16, x.device, CVT_NTHWC)
+    shape = (B, Cout, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
     _check(lib.cvt_causal_conv3d_fact(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
                                       B, Cin, Cout, T, H, W, k, _ptr(workspace), workspace.numel(),
                                       _stream(x.device)), "causal_conv3d_fact")
@@ -206,9 +224,13 @@ def fsq_quantize(z, levels=DEFAULT_LEVELS, return_codes=False, indices=None, cod
     lay = _layout_of(z)
     B, D, T, H, W = z.shape
     arr, n = _levels_arg(levels)
-    idx = indices if indices is not None else torch.empty((B, T, H, W), dtype=torch.int32, device=z.device)
-    if return_codes and codes is None:
-        codes = _empty5(tuple(z.shape), z.dtype, z.device, lay)
+    if indices is not None:
+        idx = _check_out(indices, (B, T, H, W), torch.int32, z.device, what="indices")
+    else:
+        idx = torch.empty((B, T, H, W), dtype=torch.int32, device=z.device)
+    if return_codes:
+        codes = (_check_out(codes, tuple(z.shape), z.dtype, z.device, lay, what="codes") if codes is not None
+                 else _empty5(tuple(z.shape), z.dtype, z.device, lay))
     _check(lib.cvt_fsq_quantize(_ptr(z), _dtype_code(z.dtype), lay, _ptr(idx), _ptr(codes) if return_codes else None,
                                 arr, n, B, T, H, W, _stream(z.device)), "fsq_quantize")
     return (idx, codes) if return_codes else idx
@@ -225,7 +247,9 @@ def fsq_dequantize(indices, levels=DEFAULT_LEVELS, dtype=torch.bfloat16, layout=
     B, T, H, W = indices.shape
     lay = CVT_NTHWC if layout == "NTHWC" else CVT_NCTHW
     arr, n = _levels_arg(levels)
-    codes = out if out is not None else _empty5((B, n, T, H, W), dtype, indices.device, lay)
+    shape = (B, n, T, H, W)
+    codes = (_check_out(out, shape, dtype, indices.device, lay) if out is not None
+             else _empty5(shape, dtype, indices.device, lay))
     _check(lib.cvt_fsq_dequantize(_ptr(indices), _ptr(codes), _dtype_code(codes.dtype), lay, arr, n,
                                   B, T, H, W, _ptr(invalid_count), _stream(indices.device)), "fsq_dequantize")
     return codes

@@ -39,6 +39,15 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Streaming (non-temporal) stores for outputs that no later access of the same kernel reads.
+__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
+    const u32x2_t t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are already

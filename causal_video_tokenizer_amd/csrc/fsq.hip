@@ -16,10 +16,13 @@
 //
 // Mapping: one thread per run of 8 consecutive positions.  Planar (NCTHW)
 // latents are read as one 16-byte (bf16) or two 16-byte (fp32) streaming loads per
-// channel; NTHWC latents as the thread's contiguous 8*D-element span.  Indices
-// are written as two 16-byte stores.  Ragged tails and plane sizes that are not
-// multiples of 8 take the per-position path.
+// channel; NTHWC latents as the thread's contiguous 8*D-element span.  For the
+// default levels each wave takes 512 positions and moves NTHWC spans and index runs
+// through LDS, so every wave-wide access is one contiguous 1 KB (see "Wave tiles").
+// Ragged tails and plane sizes that are not multiples of 8 take the per-position path.
 #include <math.h>
+
+#include <algorithm>
 
 #include "cvt_internal.h"
 
@@ -105,68 +108,151 @@ __device__ __forceinline__ float code_of(int d, int half) {
     return (float)(d - half) / (float)half;
 }
 
-// Quantize with the default levels: 8 positions per thread, compile-time
-// breakpoint counts (7 for L = 8, 4 for L = 5); codes only when CODES.
+// Wave tiles.  The default-level kernels give each wave 512 consecutive positions (8 per
+// lane).  Data that is contiguous per lane but interleaved across lanes - an NTHWC span
+// of 8 positions x D channels, or 8 indices - is moved through a wave-private LDS tile,
+// so that every global load or store instruction of the wave covers one contiguous
+// 1 KB (lane l at bytes 16 l) instead of 64 strided pieces.  A wave reads back only what
+// it wrote and its LDS accesses execute in order, so no barrier is needed.
+constexpr int WAVE_POS = 64 * G;
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16-byte chunk <-> 8 bf16 or 4 float values
+__device__ __forceinline__ void unpack16(const uint4 u, float* v, uint16_t) {
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 u, float* v, float) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y); v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ uint4 pack16(const float* v, uint16_t) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+__device__ __forceinline__ uint4 pack16(const float* v, float) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+
+// Quantize with the default levels: compile-time breakpoint counts (7 for L = 8, 4 for
+// L = 5); codes only when CODES.  Full wave tiles take the staged path; the positions
+// after the last full tile (fewer than 512) are done by one more wave, 8 per lane, with
+// direct accesses and a per-position path for the last partial group.
 template <typename T, int LAYOUT, bool CODES>
 __global__ __launch_bounds__(256) void fsq_quantize_default_kernel(const T* __restrict__ z, int32_t* __restrict__ idx,
                                                                    T* __restrict__ codes, FsqParams p, long long npb,
                                                                    long long total) {
     using LV = DefaultLevels;
     constexpr int D = LV::D;
-    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long pos0 = g * G;
-    if (pos0 >= total) return;
-    int acc[G];
-    bool nan_[G];
-#pragma unroll
-    for (int k = 0; k < G; ++k) { acc[k] = 0; nan_[k] = false; }
-    if (pos0 + G <= total) {
+    constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    constexpr int NCH = G * D / EPC;          // chunks of one lane's NTHWC span (6 bf16, 12 fp32)
+    constexpr int SCH = LAYOUT == CVT_NTHWC ? NCH : 2;  // staged chunks per lane (NCTHW: indices only)
+    __shared__ uint4 stage[4][64 * SCH];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint4* st = stage[w];
+    const long long wave_id = (long long)blockIdx.x * 4 + w;
+    const long long nfull = total / WAVE_POS;
+    if (wave_id > nfull) return;
+    const bool full = wave_id < nfull;
+    const long long pos0 = wave_id * WAVE_POS + lane * G;
+    if (!full && pos0 >= total) return;
+
+    if (full || pos0 + G <= total) {
+        float v[D][G];  // v[i][k]: channel i of position pos0 + k
+        long long b = 0, r = 0;
         if (LAYOUT == CVT_NCTHW) {
-            const long long b = pos0 / npb, r = pos0 - b * npb;
-            float v[D][G];
+            b = pos0 / npb;
+            r = pos0 - b * npb;
 #pragma unroll
             for (int i = 0; i < D; ++i) load8<T>(z + ((size_t)b * D + i) * npb + r, v[i]);
-#pragma unroll
-            for (int i = 0; i < D; ++i) {
-                float cv[G];
-#pragma unroll
-                for (int k = 0; k < G; ++k) {
-                    const int d = digit_default(i, v[i][k], p);
-                    acc[k] += d * LV::basis(i);
-                    nan_[k] |= (v[i][k] != v[i][k]);
-                    if (CODES) cv[k] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_or_zero(v[i][k]);
-                }
-                if (CODES) store8(codes + ((size_t)b * D + i) * npb + r, cv);
-            }
         } else {
-            float v[D][G];  // D chunks of 8 consecutive elements = 8 positions x 6 channels
+            float flat[G * D];
+            if (full) {
+                const uint4* src = reinterpret_cast<const uint4*>(z + (size_t)(wave_id * WAVE_POS) * D);
+                uint4 t[NCH];
 #pragma unroll
-            for (int c8 = 0; c8 < D; ++c8) load8<T>(z + (size_t)pos0 * D + c8 * G, v[c8]);
+                for (int c = 0; c < NCH; ++c) t[c] = ld_stream16(src + c * 64 + lane);
 #pragma unroll
-            for (int c8 = 0; c8 < D; ++c8) {
-                float cv[G];
+                for (int c = 0; c < NCH; ++c) st[c * 64 + lane] = t[c];
+                wave_lds_sync();
 #pragma unroll
-                for (int e = 0; e < G; ++e) {
-                    const int flat = c8 * G + e, k = flat / D, i = flat % D;
-                    const float x = v[c8][e];
-                    const int d = digit_default(i, x, p);
-                    acc[k] += d * LV::basis(i);
-                    nan_[k] |= (x != x);
-                    if (CODES) cv[e] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_or_zero(x);
+                for (int c = 0; c < NCH; ++c) unpack16(st[lane * NCH + c], flat + c * EPC, T());
+                wave_lds_sync();
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(z + (size_t)pos0 * D);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) unpack16(ld_stream16(src + c), flat + c * EPC, T());
+            }
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+#pragma unroll
+                for (int i = 0; i < D; ++i) v[i][k] = flat[k * D + i];
+        }
+
+        int acc[G];
+        bool nan_[G];
+        float cv[D][G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) { acc[k] = 0; nan_[k] = false; }
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const float x = v[i][k];
+                const int d = digit_default(i, x, p);
+                acc[k] += d * LV::basis(i);
+                nan_[k] |= (x != x);
+                if (CODES) cv[i][k] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_or_zero(x);
+            }
+
+        if (CODES) {
+            if (LAYOUT == CVT_NCTHW) {
+#pragma unroll
+                for (int i = 0; i < D; ++i) store8(codes + ((size_t)b * D + i) * npb + r, cv[i]);
+            } else {
+                float flat[G * D];
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+#pragma unroll
+                    for (int i = 0; i < D; ++i) flat[k * D + i] = cv[i][k];
+                if (full) {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) st[lane * NCH + c] = pack16(flat + c * EPC, T());
+                    wave_lds_sync();
+                    uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)(wave_id * WAVE_POS) * D);
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) st_stream16(dst + c * 64 + lane, st[c * 64 + lane]);
+                    wave_lds_sync();
+                } else {
+                    uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos0 * D);
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) dst[c] = pack16(flat + c * EPC, T());
                 }
-                if (CODES) store8(codes + (size_t)pos0 * D + c8 * G, cv);
             }
         }
+
         int4 o0, o1;
         o0.x = nan_[0] ? -1 : acc[0]; o0.y = nan_[1] ? -1 : acc[1];
         o0.z = nan_[2] ? -1 : acc[2]; o0.w = nan_[3] ? -1 : acc[3];
         o1.x = nan_[4] ? -1 : acc[4]; o1.y = nan_[5] ? -1 : acc[5];
         o1.z = nan_[6] ? -1 : acc[6]; o1.w = nan_[7] ? -1 : acc[7];
-        *reinterpret_cast<int4*>(idx + pos0) = o0;
-        *reinterpret_cast<int4*>(idx + pos0 + 4) = o1;
+        if (full) {
+            st[2 * lane] = *reinterpret_cast<uint4*>(&o0);
+            st[2 * lane + 1] = *reinterpret_cast<uint4*>(&o1);
+            wave_lds_sync();
+            uint4* dst = reinterpret_cast<uint4*>(idx + wave_id * WAVE_POS);
+            st_stream16(dst + lane, st[lane]);
+            st_stream16(dst + 64 + lane, st[64 + lane]);
+        } else {
+            *reinterpret_cast<int4*>(idx + pos0) = o0;
+            *reinterpret_cast<int4*>(idx + pos0 + 4) = o1;
+        }
         return;
     }
-    for (long long pos = pos0; pos < total; ++pos) {  // ragged tail (< 8 positions)
+    for (long long pos = pos0; pos < total; ++pos) {  // last partial group (< 8 positions)
         int a = 0;
         bool isnan_ = false;
         const long long b = pos / npb, r = pos - b * npb;
@@ -270,84 +356,17 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, int sh) {
     return __umulhi(n, M) >> sh;
 }
 
-// Dequantize with the default levels: compile-time radices (the compiler
-// divides by 8 and 5 with shifts / multiply-high) and power-of-two code scales.
-template <typename T, int LAYOUT>
-__global__ __launch_bounds__(256) void fsq_dequantize_default_kernel(const int32_t* __restrict__ idx,
-                                                                     T* __restrict__ codes, long long npb,
-                                                                     long long total, int32_t* __restrict__ invalid) {
-    using LV = DefaultLevels;
-    constexpr int D = LV::D;
-    const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long pos0 = g * G;
-    if (pos0 >= total) return;
-    int nbad = 0;
-    if (pos0 + G <= total) {
-        const uint4 ua = ld_stream16(idx + pos0), uc = ld_stream16(idx + pos0 + 4);
-        const int4 a = make_int4((int)ua.x, (int)ua.y, (int)ua.z, (int)ua.w);
-        const int4 c = make_int4((int)uc.x, (int)uc.y, (int)uc.z, (int)uc.w);
-        const int id[G] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        float cv[D][G];
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const bool bad = (unsigned)id[k] >= (unsigned)LV::codebook;
-            nbad += bad ? 1 : 0;
-            // branchless invalid handling: the digits of 0 plus a NaN addend
-            const float nan_add = bad ? __builtin_nanf("") : 0.0f;
-            uint32_t rem = bad ? 0u : (uint32_t)id[k];
-#pragma unroll
-            for (int i = 0; i < D; ++i) {
-                const uint32_t q = rem / (uint32_t)LV::L(i);
-                const int d = (int)(rem - q * (uint32_t)LV::L(i));
-                rem = q;
-                cv[i][k] = (float)(d - LV::half(i)) * LV::inv_half(i) + nan_add;
-            }
-        }
-        if (LAYOUT == CVT_NCTHW) {
-            const long long b = pos0 / npb, r = pos0 - b * npb;
-#pragma unroll
-            for (int i = 0; i < D; ++i) store8(codes + ((size_t)b * D + i) * npb + r, cv[i]);
-        } else {
-            float flat[G * D];
-#pragma unroll
-            for (int k = 0; k < G; ++k)
-#pragma unroll
-                for (int i = 0; i < D; ++i) flat[k * D + i] = cv[i][k];
-#pragma unroll
-            for (int c8 = 0; c8 < D; ++c8) store8(codes + (size_t)pos0 * D + c8 * G, flat + c8 * G);
-        }
-    } else {
-        for (long long pos = pos0; pos < total; ++pos) {
-            const int v = idx[pos];
-            const bool bad = (unsigned)v >= (unsigned)LV::codebook;
-            nbad += bad ? 1 : 0;
-            uint32_t rem = bad ? 0u : (uint32_t)v;
-            const long long b = pos / npb, r = pos - b * npb;
-#pragma unroll
-            for (int i = 0; i < D; ++i) {
-                const uint32_t q = rem / (uint32_t)LV::L(i);
-                const int d = (int)(rem - q * (uint32_t)LV::L(i));
-                rem = q;
-                const size_t off = LAYOUT == CVT_NCTHW ? ((size_t)b * D + i) * npb + r : (size_t)pos * D + i;
-                st1(codes + off, bad ? __builtin_nanf("") : (float)(d - LV::half(i)) * LV::inv_half(i));
-            }
-        }
-    }
-    if (invalid && nbad) atomicAdd(invalid, nbad);
-}
-
-// Dequantize with the default levels through two LDS tables.  With radices
-// (8,8,8,5,5,5) the index splits into lo = idx mod 512 (the three base-8 digits) and
-// hi = idx / 512 < 125 (the three base-5 digits); each table row holds the three
-// codes of its digits, packed as the output type (bf16 pairs or floats), and row
-// 512 / 125 holds NaNs for invalid indices.  Per position this is two LDS reads and
-// a few byte permutes instead of six divisions and conversions.  Each workgroup
-// fills its tables once and then walks several 8-position groups.
+// Dequantize with the default levels.  With radices (8,8,8,5,5,5) the index splits into
+// lo = idx mod 512, whose three octal digits are bit fields, and hi = idx / 512 < 125,
+// whose base-5 digits come from two exact multiply-shift divisions (hi / 5 =
+// (hi * 52429) >> 18 and hi / 25 = (hi * 5243) >> 17 for hi < 125).  Codes are
+// (d - L/2) * (2/L) with power-of-two scales, exact in bf16 and fp32; invalid indices
+// add a NaN.  Each wave takes one 512-position tile (see "Wave tiles").
 template <typename T>
 struct CodeRow;
 template <>
 struct CodeRow<uint16_t> {
-    using type = uint2;  // x = c0 | c1 << 16, y = c2
+    using type = uint2;  // three codes: x = c0 | c1 << 16, y = c2
     __device__ static type make(float c0, float c1, float c2) {
         return make_uint2(pack_bf16x2(c0, c1), pack_bf16x2(c2, 0.0f));
     }
@@ -358,79 +377,103 @@ struct CodeRow<float> {
     __device__ static type make(float c0, float c1, float c2) { return make_float4(c0, c1, c2, 0.0f); }
 };
 
-constexpr int DQ_GROUPS = 4;  // 8-position groups per thread
-
 template <typename T, int LAYOUT>
-__global__ __launch_bounds__(256) void fsq_dequantize_lut_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
+__global__ __launch_bounds__(256) void fsq_dequantize_default_kernel(const int32_t* __restrict__ idx, T* __restrict__ codes,
                                                                  long long npb, long long total,
                                                                  int32_t* __restrict__ invalid) {
     using Row = typename CodeRow<T>::type;
-    __shared__ Row lutA[513];
-    __shared__ Row lutB[126];
+    constexpr int D = 6;
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int NCH = G * D / EPC;  // chunks of one lane's NTHWC span (6 bf16, 12 fp32)
+    constexpr int SCH = LAYOUT == CVT_NTHWC ? NCH : 2;  // staged chunks per lane (NCTHW: indices only)
+    __shared__ uint4 stage[4][64 * SCH];
     const float qnan = __builtin_nanf("");
-    for (int e = threadIdx.x; e < 513 + 126; e += blockDim.x) {
-        if (e < 512) {
-            lutA[e] = CodeRow<T>::make(((e & 7) - 4) * 0.25f, (((e >> 3) & 7) - 4) * 0.25f, ((e >> 6) - 4) * 0.25f);
-        } else if (e == 512) {
-            lutA[e] = CodeRow<T>::make(qnan, qnan, qnan);
-        } else {
-            const int h = e - 513;
-            lutB[h] = h < 125 ? CodeRow<T>::make((h % 5 - 2) * 0.5f, ((h / 5) % 5 - 2) * 0.5f, (h / 25 - 2) * 0.5f)
-                              : CodeRow<T>::make(qnan, qnan, qnan);
-        }
-    }
-    __syncthreads();
 
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint4* st = stage[w];
+    const long long nfull = total / WAVE_POS;
     int nbad = 0;
-    for (int r = 0; r < DQ_GROUPS; ++r) {
-        const long long pos0 = ((long long)(blockIdx.x * DQ_GROUPS + r) * blockDim.x + threadIdx.x) * G;
-        if (pos0 >= total) break;
-        if (pos0 + G <= total) {
-            const uint4 ua = ld_stream16(idx + pos0), uc = ld_stream16(idx + pos0 + 4);
+    // grid-stride over the wave tiles (the launch covers all of them, one per wave)
+    for (long long wave_id = (long long)blockIdx.x * 4 + w; wave_id <= nfull; wave_id += (long long)gridDim.x * 4) {
+        const bool full = wave_id < nfull;
+        const long long pos0 = wave_id * WAVE_POS + lane * G;
+        if (!full && pos0 >= total) break;
+        if (full || pos0 + G <= total) {
+            uint4 ua, uc;
+            if (full) {  // the wave's 512 indices as two contiguous 1 KB loads
+                const uint4* src = reinterpret_cast<const uint4*>(idx + wave_id * WAVE_POS);
+                const uint4 t0 = ld_stream16(src + lane), t1 = ld_stream16(src + 64 + lane);
+                st[lane] = t0;
+                st[64 + lane] = t1;
+                wave_lds_sync();
+                ua = st[2 * lane];
+                uc = st[2 * lane + 1];
+                wave_lds_sync();
+            } else {
+                ua = ld_stream16(idx + pos0);
+                uc = ld_stream16(idx + pos0 + 4);
+            }
             const uint32_t id[G] = {ua.x, ua.y, ua.z, ua.w, uc.x, uc.y, uc.z, uc.w};
             Row A[G], Bv[G];
 #pragma unroll
             for (int k = 0; k < G; ++k) {
-                const bool bad = id[k] >= 64000u;
+                const bool bad = id[k] >= (uint32_t)DefaultLevels::codebook;
                 nbad += bad ? 1 : 0;
-                A[k] = lutA[bad ? 512 : (id[k] & 511u)];
-                Bv[k] = lutB[bad ? 125 : (id[k] >> 9)];
+                const uint32_t lo = id[k] & 511u, hi = bad ? 0u : (id[k] >> 9);
+                const uint32_t h5 = (hi * 52429u) >> 18, h25 = (hi * 5243u) >> 17;
+                const float na = bad ? qnan : 0.0f;
+                A[k] = CodeRow<T>::make(((int)(lo & 7) - 4) * 0.25f + na, ((int)((lo >> 3) & 7) - 4) * 0.25f + na,
+                                        ((int)(lo >> 6) - 4) * 0.25f + na);
+                Bv[k] = CodeRow<T>::make(((int)(hi - 5 * h5) - 2) * 0.5f + na, ((int)(h5 - 5 * h25) - 2) * 0.5f + na,
+                                         ((int)h25 - 2) * 0.5f + na);
             }
+            // the lane's codes as NCH 16-byte chunks in NTHWC order, or 6 planes of 8 (NCTHW)
             if constexpr (sizeof(T) == 2) {
                 // bf16: combine 16-bit fields with byte permutes
-                auto lo2 = [](uint32_t p, uint32_t q) { return __builtin_amdgcn_perm(q, p, 0x05040100u); };
-                auto hi2 = [](uint32_t p, uint32_t q) { return __builtin_amdgcn_perm(q, p, 0x07060302u); };
+                auto lo2 = [](uint32_t a, uint32_t c) { return __builtin_amdgcn_perm(c, a, 0x05040100u); };
+                auto hi2 = [](uint32_t a, uint32_t c) { return __builtin_amdgcn_perm(c, a, 0x07060302u); };
                 if (LAYOUT == CVT_NCTHW) {
                     const long long b = pos0 / npb, rr = pos0 - b * npb;
                     uint4 o[6];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int p = 2 * j, q = 2 * j + 1;
-                        (&o[0].x)[j] = lo2(A[p].x, A[q].x);
-                        (&o[1].x)[j] = hi2(A[p].x, A[q].x);
-                        (&o[2].x)[j] = lo2(A[p].y, A[q].y);
-                        (&o[3].x)[j] = lo2(Bv[p].x, Bv[q].x);
-                        (&o[4].x)[j] = hi2(Bv[p].x, Bv[q].x);
-                        (&o[5].x)[j] = lo2(Bv[p].y, Bv[q].y);
+                        const int q0 = 2 * j, q1 = 2 * j + 1;
+                        (&o[0].x)[j] = lo2(A[q0].x, A[q1].x);
+                        (&o[1].x)[j] = hi2(A[q0].x, A[q1].x);
+                        (&o[2].x)[j] = lo2(A[q0].y, A[q1].y);
+                        (&o[3].x)[j] = lo2(Bv[q0].x, Bv[q1].x);
+                        (&o[4].x)[j] = hi2(Bv[q0].x, Bv[q1].x);
+                        (&o[5].x)[j] = lo2(Bv[q0].y, Bv[q1].y);
                     }
 #pragma unroll
                     for (int i = 0; i < 6; ++i)
-                        *reinterpret_cast<uint4*>(codes + ((size_t)b * 6 + i) * npb + rr) = o[i];
+                        st_stream16(codes + ((size_t)b * 6 + i) * npb + rr, o[i]);
                 } else {
                     // per position: (c0 c1) (c2 c3) (c4 c5)
-                    uint32_t w[3 * G];
+                    uint32_t wd[3 * G];
 #pragma unroll
                     for (int k = 0; k < G; ++k) {
-                        w[3 * k] = A[k].x;
-                        w[3 * k + 1] = lo2(A[k].y, Bv[k].x);
-                        w[3 * k + 2] = __builtin_amdgcn_perm(Bv[k].y, Bv[k].x, 0x05040302u);
+                        wd[3 * k] = A[k].x;
+                        wd[3 * k + 1] = lo2(A[k].y, Bv[k].x);
+                        wd[3 * k + 2] = __builtin_amdgcn_perm(Bv[k].y, Bv[k].x, 0x05040302u);
                     }
-                    uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos0 * 6);
+                    if (full) {
 #pragma unroll
-                    for (int c = 0; c < 6; ++c) dst[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+                        for (int c = 0; c < NCH; ++c)
+                            st[lane * NCH + c] = make_uint4(wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]);
+                        wave_lds_sync();
+                        uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)(wave_id * WAVE_POS) * D);
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) st_stream16(dst + c * 64 + lane, st[c * 64 + lane]);
+                    } else {
+                        uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos0 * D);
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c)
+                            dst[c] = make_uint4(wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]);
+                    }
                 }
             } else {
-                float cv[6][G];
+                float cv[D][G];
 #pragma unroll
                 for (int k = 0; k < G; ++k) {
                     cv[0][k] = A[k].x; cv[1][k] = A[k].y; cv[2][k] = A[k].z;
@@ -439,21 +482,31 @@ __global__ __launch_bounds__(256) void fsq_dequantize_lut_kernel(const int32_t* 
                 if (LAYOUT == CVT_NCTHW) {
                     const long long b = pos0 / npb, rr = pos0 - b * npb;
 #pragma unroll
-                    for (int i = 0; i < 6; ++i) store8(codes + ((size_t)b * 6 + i) * npb + rr, cv[i]);
+                    for (int i = 0; i < D; ++i) store8(codes + ((size_t)b * D + i) * npb + rr, cv[i]);
                 } else {
-                    float flat[6 * G];
+                    float flat[D * G];
 #pragma unroll
                     for (int k = 0; k < G; ++k)
 #pragma unroll
-                        for (int i = 0; i < 6; ++i) flat[k * 6 + i] = cv[i][k];
+                        for (int i = 0; i < D; ++i) flat[k * D + i] = cv[i][k];
+                    if (full) {
 #pragma unroll
-                    for (int c8 = 0; c8 < 6; ++c8) store8(codes + (size_t)pos0 * 6 + c8 * G, flat + c8 * G);
+                        for (int c = 0; c < NCH; ++c) st[lane * NCH + c] = pack16(flat + c * EPC, T());
+                        wave_lds_sync();
+                        uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)(wave_id * WAVE_POS) * D);
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) st_stream16(dst + c * 64 + lane, st[c * 64 + lane]);
+                    } else {
+                        uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)pos0 * D);
+#pragma unroll
+                        for (int c = 0; c < NCH; ++c) dst[c] = pack16(flat + c * EPC, T());
+                    }
                 }
             }
         } else {
-            for (long long pos = pos0; pos < total; ++pos) {  // ragged tail (< 8 positions)
+            for (long long pos = pos0; pos < total; ++pos) {  // last partial group (< 8 positions)
                 const uint32_t v = (uint32_t)idx[pos];
-                const bool bad = v >= 64000u;
+                const bool bad = v >= (uint32_t)DefaultLevels::codebook;
                 nbad += bad ? 1 : 0;
                 uint32_t rem = bad ? 0u : v;
                 const long long b = pos / npb, rr = pos - b * npb;
@@ -469,6 +522,7 @@ __global__ __launch_bounds__(256) void fsq_dequantize_lut_kernel(const int32_t* 
                 }
             }
         }
+        wave_lds_sync();  // this tile's staged reads before the next tile's writes
     }
     if (invalid && nbad) atomicAdd(invalid, nbad);
 }
@@ -585,7 +639,7 @@ hipError_t quantize_t(const void* z, int32_t* idx, void* codes, const FsqParams&
     // vector path: 8-aligned plane starts for NCTHW; NTHWC spans are always contiguous
     const int vec = LAYOUT == CVT_NTHWC ? 1 : (npb % G == 0);
     if (is_default(p) && vec) {
-        const long long nblk = ((total + G - 1) / G + 255) / 256;
+        const long long nblk = (total + 4 * WAVE_POS - 1) / (4 * WAVE_POS);  // one 512-position tile per wave
         if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         if (codes)
             hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, true>), dim3((unsigned)nblk), dim3(256), 0, s,
@@ -608,7 +662,8 @@ hipError_t dequantize_t(const int32_t* idx, void* codes, const FsqParams& p, lon
     const long long nblk = (nthreads + 255) / 256;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (is_default(p) && vec)
-        hipLaunchKernelGGL((fsq_dequantize_lut_kernel<T, LAYOUT>), dim3((unsigned)((nblk + DQ_GROUPS - 1) / DQ_GROUPS)),
+        hipLaunchKernelGGL((fsq_dequantize_default_kernel<T, LAYOUT>),
+                           dim3((unsigned)((total + 4 * WAVE_POS - 1) / (4 * WAVE_POS))),
                            dim3(256), 0, s, idx, (T*)codes, npb, total, invalid);
     else if (p.D == 6)
         hipLaunchKernelGGL((fsq_dequantize_kernel<T, LAYOUT, 6>), dim3((unsigned)nblk), dim3(256), 0, s, idx, (T*)codes, p,

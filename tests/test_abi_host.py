@@ -112,3 +112,23 @@ def test_conv_validation_and_workspace():
     assert call(x=MIS) == E_ALIGN
     assert call(wsb=ws - 1) == E_WORKSPACE
     assert call(work=None) == E_WORKSPACE
+
+
+def test_binding_rejects_mismatched_outputs():
+    """A caller-provided output must have the shape, dtype and memory layout the kernel
+    writes (an NCTHW buffer for an NTHWC result would be filled in the wrong order)."""
+    import torch
+    import causal_video_tokenizer_amd as cvt
+    shape = (1, 6, 3, 4, 8)
+    good = torch.empty(shape, dtype=torch.bfloat16, memory_format=torch.channels_last_3d)
+    assert cvt._check_out(good, shape, torch.bfloat16, good.device, cvt.CVT_NTHWC) is good
+    planar = torch.empty(shape, dtype=torch.bfloat16)
+    assert cvt._check_out(planar, shape, torch.bfloat16, planar.device, cvt.CVT_NCTHW) is planar
+    with pytest.raises(ValueError, match="channels_last_3d"):
+        cvt._check_out(planar, shape, torch.bfloat16, planar.device, cvt.CVT_NTHWC)
+    with pytest.raises(ValueError, match="contiguous"):
+        cvt._check_out(good, shape, torch.bfloat16, good.device, cvt.CVT_NCTHW)
+    with pytest.raises(ValueError, match="dtype"):
+        cvt._check_out(good, shape, torch.float32, good.device, cvt.CVT_NTHWC)
+    with pytest.raises(ValueError, match="shape"):
+        cvt._check_out(good, (1, 6, 3, 4, 4), torch.bfloat16, good.device, cvt.CVT_NTHWC)
