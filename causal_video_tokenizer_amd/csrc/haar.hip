@@ -22,10 +22,11 @@
 // Mapping: one wavefront per (b, t', h', run of 64 w' positions); lane = w'.
 // Each lane loads the 4 x 4 x 4 block of every input channel with 8-byte
 // (bf16) or 16-byte (fp32) streaming row loads, so each load instruction covers
-// 512 or 1024 contiguous bytes of a pixel row.  For the NTHWC coefficient layout the
-// 64 x (64C) output tile is transposed through LDS (rows padded by one dword so
-// the per-lane scattered writes hit distinct banks) and written as contiguous
-// dwords; the inverse stages its NTHWC input the same way.
+// 512 or 1024 contiguous bytes of a pixel row.  For the NTHWC coefficient layout
+// with C = 3 the 64 x (64C) output tile goes through LDS (rows padded by 16 bytes so
+// the 128-bit row accesses of 16 lanes hit distinct banks) and leaves as contiguous
+// 16-byte stores; the inverse stages its NTHWC input the same way.  Other channel
+// counts and layouts use the generic kernels at the end of the file.
 #include "cvt_internal.h"
 
 namespace cvt {
