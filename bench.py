@@ -180,7 +180,7 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": 2.0 * P * (192 + 256) + 2.0 * 256 * 192 * 9,
-                "kernel": "conv_rows_kernel<SPATIAL3,4,false> (1x3x3 conv 192->256, bf16 MFMA)",
+                "kernel": "conv_rows_kernel<SPATIAL3,4,2,32,false> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)

@@ -240,16 +240,18 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 //   SPATIAL3:  rows are image rows of one frame, columns are 64 pixels of a row plus a
 //              1-pixel halo (66); output row y, pixel x reads input row y-1+ky, pixel
 //              x-1+kx through tap (ky, kx) (KX = 3).
-// One workgroup (4 waves) computes 128 output channels x 64 columns x R consecutive output
-// rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2 temporal,
-// 1 spatial): the REGION, staged once per 32-channel K chunk.  Region row rr meets tap
-// row ky in output row r0 + rr - ky.  Each wave owns 64 channels (two 32-row MFMA blocks)
-// x 32 columns x all R rows: per (16-channel k-step, column shift kx) it takes the six
-// weight fragments (3 tap rows x 2 blocks) once and walks the region rows, each
-// activation fragment feeding up to three tap rows, i.e. three output rows.
+// One workgroup (4 waves) computes 256 / WP output channels x 32 WP columns x R consecutive
+// output rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2
+// temporal, 1 spatial): the REGION, staged once per BK-channel K chunk.  Region row rr
+// meets tap row ky in output row r0 + rr - ky.  Each wave owns 64 channels (two 32-row
+// MFMA blocks) x 32 columns x all R rows: per (16-channel k-step, column shift kx) it
+// takes the six weight fragments (3 tap rows x 2 blocks) once and walks the region rows,
+// each activation fragment feeding up to three tap rows, i.e. three output rows.  The
+// spatial conv uses WP = 2 (128 channels x 64 pixels), the temporal conv WP = 1 (all 256
+// channels x 32 positions, so each region is staged once for every output channel).
 //
-// Only the region is staged in LDS (two buffers of about 30 KB, so two workgroups share a
-// CU and one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
+// Only the region is staged in LDS (two buffers of 15-32 KB, so two workgroups share a CU
+// and one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
 // once per call in MFMA fragment order (see pack_frag_kernel): each fragment is 1 KB of
 // which lane l reads bytes [16 l, 16 l + 16), one coalesced load straight into the operand
 // registers, prefetched one step ahead.  The region loads of chunk c + 1 are issued in two
@@ -271,36 +273,45 @@ struct RowsGeom {
     int ntiles, per_xcd;
 };
 
-constexpr int ROWS_XS = 64 + 16;  // LDS bytes per region row: 32 channels + 16 bytes of padding
+// LDS bytes per region row: BK channels + 16 bytes of padding
+template <int BK>
+constexpr int rows_xs() {
+    return BK * 2 + 16;
+}
 constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (tensors stay below it)
 
-template <int KIND>
+// WP: waves along columns (1 or 2); the other 4 / WP waves split the output channels,
+// 64 each, so a workgroup covers 256 / WP channels x 32 WP columns.
+template <int KIND, int WP>
 struct RowsShape {
-    static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;    // column shifts
-    static constexpr int RC = KIND == SPATIAL3 ? 66 : 64;  // region columns
-    static constexpr int OFF = KIND == SPATIAL3 ? 1 : 2;   // rows of look-back (halo or causal pad)
+    static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;  // column shifts
+    static constexpr int WCH = 4 / WP;                   // waves along output channels
+    static constexpr int TCH = 64 * WCH;                 // output channels per workgroup
+    static constexpr int NC = 32 * WP;                   // output columns per workgroup
+    static constexpr int RC = NC + (KIND == SPATIAL3 ? 2 : 0);  // region columns (with the x halo)
 };
 
-template <int KIND, int R>
+template <int KIND, int R, int WP>
 constexpr int rows_region_rows() {
-    return ((R + 2) * RowsShape<KIND>::RC + 7) / 8 * 8;
+    return ((R + 2) * RowsShape<KIND, WP>::RC + 7) / 8 * 8;
 }
 
-template <int KIND, int R, int NV, bool TAIL>
+template <int KIND, int R, int WP, int BK, int NV, bool TAIL>
 __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
                                           const float* __restrict__ bias, uint16_t* __restrict__ Y, const RowsGeom& g,
-                                          uint8_t (*sX)[rows_region_rows<KIND, R>() * ROWS_XS], int b, int t, int ct,
-                                          int r0, int c0) {
-    using S = RowsShape<KIND>;
-    constexpr int NTH = 256, RC = S::RC, KX = S::KX, BK = 32, CPR = BK / 8, XS = ROWS_XS;
-    constexpr int XROWS = rows_region_rows<KIND, R>();
+                                          uint8_t (*sX)[rows_region_rows<KIND, R, WP>() * rows_xs<BK>()], int b,
+                                          int t, int ct, int r0, int c0) {
+    using S = RowsShape<KIND, WP>;
+    constexpr int NTH = 256, RC = S::RC, KX = S::KX, CPR = BK / 8, XS = rows_xs<BK>(), KS = BK / 16;
+    constexpr int WCH = S::WCH;
+    constexpr int XROWS = rows_region_rows<KIND, R, WP>();
     constexpr int XQ = XROWS * CPR;
     constexpr int XL = (XQ + NTH - 1) / NTH;
     constexpr int OOB = 0x7fffffff;
     constexpr int NRU = NV + 2;  // region rows that feed a valid output row
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in a scalar register
-    const int wch = wave & 1, wpos = wave >> 1;
+    const int wch = wave % WCH, wpos = wave / WCH;
 
     // Region chunk q of a thread is (row, c16) with 8 consecutive lanes on 8 consecutive rows
     // at one chunk: LDS stores go 8 lanes (128 bytes) at a time, and 8 rows of 80 bytes at
@@ -338,7 +349,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // chunk's closing barrier, so it is loaded and stored in two batches inside chunk c
     // (batch 0: loads i < XH, batch 1: the rest), which halves the staging registers.  With
     // fewer than 4 steps per chunk there is one batch of all XL loads.
-    constexpr int NS = 2 * KX;                        // steps per chunk: (k-step, column shift)
+    constexpr int NS = KS * KX;                       // steps per chunk: (k-step, column shift)
     constexpr int XH = NS >= 4 ? (XL + 1) / 2 : XL;  // loads of batch 0 (short chunks: one batch)
     uint4 xr[XH];
     auto load_region = [&](int kc, int half) {  // kc past the last chunk reads zeros
@@ -366,7 +377,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 
     // weight fragments of (k-step kc16, column shift kx): tap rows 0..2 of blocks ab0, ab0 + 1
     // (zeros past the end)
-    const int ab0 = ct * 4 + wch * 2;
+    const int ab0 = ct * (2 * WCH) + wch * 2;
     bf16x8_t fa[2][3][2];
     const int lane16 = lane * 16;
     auto load_frags = [&](int kc16, int kx, int set) {
@@ -442,9 +453,9 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         for (int st = 0; st < NS; ++st) {
             const int s1 = st + 1;
             if (s1 < NS)
-                load_frags(2 * kc + s1 / KX, s1 % KX, s1 & 1);
+                load_frags(KS * kc + s1 / KX, s1 % KX, s1 & 1);
             else
-                load_frags(2 * kc + 2, 0, 0);
+                load_frags(KS * kc + KS, 0, 0);
             __builtin_amdgcn_sched_barrier(0);  // weight prefetch before any region load
             if (L1 > 0 && st == L1) store_region(nbuf, 0);
             if (st == 0) load_region(kc + 1, 0);
@@ -468,7 +479,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // are free after the last barrier of the K loop; a wave reads back only what it wrote
     // and its LDS accesses execute in order, so no barrier is needed.
     constexpr int OS = 144;
-    static_assert(4 * 32 * OS <= XROWS * XS, "epilogue staging fits in one region buffer");
+    static_assert(4 * 32 * OS <= 2 * XROWS * XS, "epilogue staging fits in the region buffers");
     uint8_t* stage = &sX[0][0] + wave * (32 * OS);
     const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
     float bv[2][4][4];
@@ -519,12 +530,12 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     }
 }
 
-template <int KIND, int R, bool TAIL>
+template <int KIND, int R, int WP, int BK, bool TAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
     uint16_t* __restrict__ Y, RowsGeom g) {
-    static_assert(R >= 1 && R <= 4, "output rows per tile");
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][rows_region_rows<KIND, R>() * ROWS_XS];
+    static_assert(R >= 1 && R <= 4 && (WP == 1 || WP == 2) && (BK == 32 || BK == 64), "tile shape");
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][rows_region_rows<KIND, R, WP>() * rows_xs<BK>()];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -542,16 +553,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         t = tile % g.T;
         b = tile / g.T;
     }
-    const int r0 = rt * R, c0 = cl * 64;
+    const int r0 = rt * R, c0 = cl * RowsShape<KIND, WP>::NC;
     const int nv = min(R, (KIND == SPATIAL3 ? g.H : g.T) - r0);  // valid output rows (block-uniform)
     if (nv >= R)
-        rows_tile<KIND, R, R, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, R, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else if (nv == 3)
-        rows_tile<KIND, R, (R > 3 ? 3 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, (R > 3 ? 3 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else if (nv == 2)
-        rows_tile<KIND, R, (R > 2 ? 2 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, (R > 2 ? 2 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
     else
-        rows_tile<KIND, R, 1, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, 1, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
 }
 
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
@@ -658,37 +669,52 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 #ifndef CVT_ROWS_R
 #define CVT_ROWS_R 4  // output rows (frames or image rows) per tile
 #endif
+#ifndef CVT_ROWS_WP_S
+#define CVT_ROWS_WP_S 2  // waves along columns, spatial
+#endif
+#ifndef CVT_ROWS_WP_T
+#define CVT_ROWS_WP_T 1  // waves along columns, temporal
+#endif
+#ifndef CVT_ROWS_BK_S
+#define CVT_ROWS_BK_S 32  // input channels per K chunk, spatial
+#endif
+#ifndef CVT_ROWS_BK_T
+#define CVT_ROWS_BK_T 32  // input channels per K chunk, temporal
+#endif
 
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes
 template <int KIND>
 hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
                        int B, hipStream_t s) {
     constexpr int R = CVT_ROWS_R;
+    constexpr int WP = KIND == SPATIAL3 ? CVT_ROWS_WP_S : CVT_ROWS_WP_T;
+    constexpr int BK = KIND == SPATIAL3 ? CVT_ROWS_BK_S : CVT_ROWS_BK_T;
+    using S = RowsShape<KIND, WP>;
     RowsGeom g{};
     g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
     g.x_bytes = (int)(cg.P * cg.Cin * 2);
     g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
     g.NA = (cg.Cout + 31) / 32;
     g.KC16 = (cg.Cin + 15) / 16;
-    g.nct = (cg.Cout + 127) / 128;
+    g.nct = (cg.Cout + S::TCH - 1) / S::TCH;
     long long ntiles;
     if (KIND == SPATIAL3) {
-        g.ncol = (cg.W + 63) / 64;
+        g.ncol = (cg.W + S::NC - 1) / S::NC;
         g.nrow = (cg.H + R - 1) / R;
         ntiles = (long long)g.nct * g.ncol * g.nrow * cg.T * B;
     } else {
-        g.ncol = (g.HW + 63) / 64;
+        g.ncol = (g.HW + S::NC - 1) / S::NC;
         g.nrow = (cg.T + R - 1) / R;
         ntiles = (long long)g.nct * g.ncol * g.nrow * B;
     }
     if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
-    if (cg.Cin % 32 == 0)
-        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, false>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
+    if (cg.Cin % BK == 0)
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, false>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
                            Wf, bias, Y, g);
     else
-        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, true>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, true>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
                            Wf, bias, Y, g);
     return hipGetLastError();
 }
