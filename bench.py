@@ -7,9 +7,9 @@ DV8x16x16-720p shape (1 x 3 x 49 x 720 x 1280 bf16), every stage a HIP kernel
 behind the C ABI:
 
   Haar patcher (causal first frame, 2 levels)  ->  spatial 1x3x3 conv 192->256
-  ->  causal temporal 3x1x1 conv 256->256  ->  1x1 projection 256->6  ->  FSQ
-  indices;  FSQ of a separate N(0, 1.5) 6-channel latent  ->  dequantize;
-  inverse Haar of the coefficients back to pixels.
+  ->  causal temporal 3x1x1 conv 256->256 with the 1x1 projection 256->6 in its
+  epilogue  ->  FSQ indices;  FSQ of a separate N(0, 1.5) 6-channel latent  ->
+  dequantize;  inverse Haar of the coefficients back to pixels.
 
 Inputs are resident in HBM before timing.  `value` is frames per second of the
 whole step (49 frames per step).  The roofline object reports the dominant
@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--workload", default="c4_dv8x16x16_720p_49f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-c3", action="store_true", help="skip the 121-frame chain measurement")
-    ap.add_argument("--cpu-width", type=int, default=320,
+    ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
 
@@ -104,23 +104,21 @@ def main():
     cl = torch.channels_last_3d
     hz = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
     s1 = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
-    y1 = torch.empty_like(s1)
     lat = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
     idx = torch.empty((B, Tq, Hq, Wq), dtype=torch.int32, device=dev)
     idx2 = torch.empty_like(idx)
     codes = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
     xr = torch.empty_like(x)
     ws_sp = torch.empty(cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)
-    ws_tm = torch.empty(cvt.conv_workspace_bytes(s1.shape, 256, 3, False, True), dtype=torch.uint8, device=dev)
-    ws_pj = torch.empty(cvt.conv_workspace_bytes(y1.shape, 6, 1, True, False), dtype=torch.uint8, device=dev)
+    ws_tp = torch.empty(cvt.conv_proj_workspace_bytes(s1.shape, 256, 6, 3, False, True), dtype=torch.uint8,
+                        device=dev)
 
-    stages = ["haar_fwd", "conv_spatial", "conv_temporal", "proj_1x1", "fsq_quantize", "fsq_quantize_sep",
+    stages = ["haar_fwd", "conv_spatial", "conv_temporal_proj", "fsq_quantize", "fsq_quantize_sep",
               "fsq_dequantize", "haar_inv"]
     calls = {
         "haar_fwd": lambda: cvt.haar3d_fwd(x, out=hz),
         "conv_spatial": lambda: cvt.causal_conv3d_fact(hz, w_s, None, workspace=ws_sp, out=s1),
-        "conv_temporal": lambda: cvt.causal_conv3d_fact(s1, None, w_t, workspace=ws_tm, out=y1),
-        "proj_1x1": lambda: cvt.causal_conv3d_fact(y1, w_p, None, workspace=ws_pj, out=lat),
+        "conv_temporal_proj": lambda: cvt.causal_conv3d_fact_proj(s1, None, w_t, w_p, workspace=ws_tp, out=lat),
         "fsq_quantize": lambda: cvt.fsq_quantize(lat, indices=idx),
         "fsq_quantize_sep": lambda: cvt.fsq_quantize(z_sep, indices=idx2),
         "fsq_dequantize": lambda: cvt.fsq_dequantize(idx2, out=codes),
@@ -154,8 +152,7 @@ def main():
     # algorithmic work per stage
     conv_flops = {
         "conv_spatial": 2.0 * 9 * 192 * 256 * P,
-        "conv_temporal": 2.0 * 3 * 256 * 256 * P,
-        "proj_1x1": 2.0 * 256 * 6 * P,
+        "conv_temporal_proj": 2.0 * 3 * 256 * 256 * P + 2.0 * 256 * 6 * P,
     }
     hbm_bytes = {
         "haar_fwd": 2.0 * B * C * T * H * W + 2.0 * P * 192,
@@ -163,7 +160,6 @@ def main():
         "fsq_quantize": P * (6 * 2 + 4.0),
         "fsq_quantize_sep": P * (6 * 2 + 4.0),
         "fsq_dequantize": P * (4 + 6 * 2.0),
-        "proj_1x1": P * (256 * 2 + 6 * 2.0),
     }
     per_stage = {}
     for name in stages:
@@ -212,7 +208,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "DV8x16x16-720p-shaped discrete path, 1x3x49x720x1280 bf16 "
-                               "(Haar -> conv 192->256 k3 -> 1x1 ->6 -> FSQ; FSQ+dequant of a 6x13x180x320 "
+                               "(Haar -> conv 192->256 k3 with the 1x1 ->6 fused -> FSQ; FSQ+dequant of a 6x13x180x320 "
                                "N(0,1.5) latent; inverse Haar)",
                    "frames_per_step": frames, "latent_grid": [Tq, Hq, Wq]},
         "roofline": roofline,
@@ -232,7 +228,8 @@ def traffic_bytes():
 
 
 def cv8x8x8_chain(cvt, si, torch, dev, args):
-    """The 121-frame 720p chain (Haar -> conv 192->256 k3 -> conv 256->256 k3 -> 1x1 -> 16),
+    """The 121-frame 720p chain (Haar -> conv 192->256 k3 -> conv 256->256 k3 with the 1x1 -> 16
+    in its temporal epilogue),
     timed per stage with HIP events; reports frames/s of the chain and the MFMA
     fraction of each convolution (the conv target is quoted on this clip)."""
     wl = si.WORKLOADS["c3_cv8x8x8_720p_121f"]
@@ -259,14 +256,14 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
         ("s1", cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False)),
         ("t", cvt.conv_workspace_bytes(a.shape, 256, 3, False, True)),
         ("s2", cvt.conv_workspace_bytes(a.shape, 256, 3, True, False)),
-        ("p", cvt.conv_workspace_bytes(a.shape, 16, 1, True, False))]}
+        ("tp", cvt.conv_proj_workspace_bytes(a.shape, 256, 16, 3, False, True))]}
     stages = [
         ("haar_fwd", lambda: cvt.haar3d_fwd(x, out=hz), None),
         ("l1_spatial", lambda: cvt.causal_conv3d_fact(hz, w[0], None, workspace=ws["s1"], out=a), 2.0 * 9 * 192 * 256 * P),
         ("l1_temporal", lambda: cvt.causal_conv3d_fact(a, None, w[1], workspace=ws["t"], out=b), 2.0 * 3 * 256 * 256 * P),
         ("l2_spatial", lambda: cvt.causal_conv3d_fact(b, w[2], None, workspace=ws["s2"], out=a), 2.0 * 9 * 256 * 256 * P),
-        ("l2_temporal", lambda: cvt.causal_conv3d_fact(a, None, w[3], workspace=ws["t"], out=b), 2.0 * 3 * 256 * 256 * P),
-        ("proj_1x1", lambda: cvt.causal_conv3d_fact(b, w[4], None, workspace=ws["p"], out=lat), 2.0 * 256 * 16 * P),
+        ("l2_temporal_proj", lambda: cvt.causal_conv3d_fact_proj(a, None, w[3], w[4], workspace=ws["tp"], out=lat),
+         2.0 * 3 * 256 * 256 * P + 2.0 * 256 * 16 * P),
     ]
     stream = torch.cuda.current_stream(dev)
     steps = max(2, args.steps // 2)
@@ -291,9 +288,8 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
         if flops:
             d["TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
             d["mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
-            if name != "proj_1x1":
-                conv_flops += flops
-                conv_ms += ms
+            conv_flops += flops
+            conv_ms += ms
         else:
             d["GBps"] = round((2.0 * B * C * T * H * W + 2.0 * P * 192) / (ms * 1e-3) / 1e9, 1)
         out["stages"][name] = d

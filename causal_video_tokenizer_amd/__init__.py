@@ -41,6 +41,9 @@ SIGNATURES = {
     "cvt_haar3d_inv": (_ci, [_vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_causal_conv3d_fact_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp]),
+    "cvt_causal_conv3d_fact_proj_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
+    "cvt_causal_conv3d_fact_proj": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                                          _ci, _vp, _sz, _vp]),
     "cvt_fsq_quantize": (_ci, [_vp, _ci, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_dequantize": (_ci, [_vp, _vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
 }
@@ -209,6 +212,54 @@ def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out
     _check(lib.cvt_causal_conv3d_fact(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
                                       B, Cin, Cout, T, H, W, k, _ptr(workspace), workspace.numel(),
                                       _stream(x.device)), "causal_conv3d_fact")
+    return y
+
+
+def conv_proj_workspace_bytes(x_shape, Cout, Cp, k, spatial=True, temporal=True):
+    B, Cin, T, H, W = x_shape
+    parts = (CVT_CONV_SPATIAL if spatial else 0) | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_causal_conv3d_fact_proj_workspace(B, Cin, Cout, Cp, T, H, W, k, parts))
+
+
+def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, workspace=None, out=None):
+    """Factorized causal convolution followed by a 1x1x1 projection, without
+    materialising the Cout-channel result.
+
+    x, w_s, w_t, b_s, b_t: as causal_conv3d_fact; w_p: [Cp, Cout, 1, 1, 1] bf16;
+    b_p: float32 [Cp] or None.  Returns [B, Cp, T, H, W] bf16 channels_last_3d.
+    """
+    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p)
+    if not x.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError("x must be channels_last_3d (NTHWC)")
+    B, Cin, T, H, W = x.shape
+    if w_s is not None:
+        Cout, k = w_s.shape[0], w_s.shape[3]
+        if tuple(w_s.shape) != (Cout, Cin, 1, k, k):
+            raise ValueError("w_s must be [Cout, Cin, 1, k, k]")
+    elif w_t is not None:
+        Cout, k = w_t.shape[0], w_t.shape[2]
+    else:
+        raise ValueError("at least one of w_s and w_t is needed")
+    if w_t is not None and tuple(w_t.shape) != (Cout, Cout, k, 1, 1):
+        raise ValueError("w_t must be [Cout, Cout, k, 1, 1]")
+    Cp = w_p.shape[0]
+    if tuple(w_p.shape) != (Cp, Cout, 1, 1, 1):
+        raise ValueError("w_p must be [Cp, Cout, 1, 1, 1]")
+    for w in (w_s, w_t, w_p):
+        if w is not None and (w.dtype != torch.bfloat16 or not w.is_contiguous()):
+            raise ValueError("weights must be contiguous bfloat16")
+    for bias, n in ((b_s, Cout), (b_t, Cout), (b_p, Cp)):
+        if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != n):
+            raise ValueError("biases must be contiguous float32 of their output width")
+    need = conv_proj_workspace_bytes(x.shape, Cout, Cp, k, w_s is not None, w_t is not None)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    shape = (B, Cp, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_causal_conv3d_fact_proj(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(w_p), _ptr(b_p),
+                                           _ptr(y), B, Cin, Cout, Cp, T, H, W, k, _ptr(workspace), workspace.numel(),
+                                           _stream(x.device)), "causal_conv3d_fact_proj")
     return y
 
 

@@ -271,6 +271,7 @@ struct RowsGeom {
     int NA, KC16;           // 32-row weight blocks, 16-channel k-steps
     int nct, ncol, nrow;    // channel tiles, column tiles, row tiles
     int ntiles, per_xcd;
+    int Cp, wp_bytes;       // fused 1x1 projection: output channels, packed weight bytes (0 = none)
 };
 
 // LDS bytes per region row: BK channels + 16 bytes of padding
@@ -296,9 +297,11 @@ constexpr int rows_region_rows() {
     return ((R + 2) * RowsShape<KIND, WP>::RC + 7) / 8 * 8;
 }
 
-template <int KIND, int R, int WP, int BK, int NV, bool TAIL>
+template <int KIND, int R, int WP, int BK, int NV, bool TAIL, bool PROJ>
 __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
-                                          const float* __restrict__ bias, uint16_t* __restrict__ Y, const RowsGeom& g,
+                                          const float* __restrict__ bias, uint16_t* __restrict__ Y,
+                                          const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
+                                          const RowsGeom& g,
                                           uint8_t (*sX)[rows_region_rows<KIND, R, WP>() * rows_xs<BK>()], int b,
                                           int t, int ct, int r0, int c0) {
     using S = RowsShape<KIND, WP>;
@@ -492,6 +495,25 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf + e;
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
+    // Fused 1x1 projection (PROJ, temporal kernel with all output channels in the workgroup):
+    // per output row, each wave multiplies its staged bf16 64-channel slice by the matching
+    // four k-steps of the projection weights (fragment order, rows o >= Cp zero) with MFMAs,
+    // the four partial sums meet in LDS after the staging tiles, and one pass adds the bias
+    // and rounds to bf16 once.  The rounding points are those of the separate 1x1 conv on
+    // the bf16 output; only the fp32 summation order differs.
+    constexpr int PMAX = 16;  // projection outputs handled in the epilogue
+    float* part = reinterpret_cast<float*>(&sX[0][0] + 4 * 32 * OS);  // [4 waves][PMAX][32]
+    static_assert(!PROJ || (4 * 32 * OS + 4 * PMAX * 32 * 4 <= 2 * XROWS * XS && WCH == 4),
+                  "projection partials fit after the staging tiles; all channels in one workgroup");
+    bf16x8_t fp[4];
+    if constexpr (PROJ) {
+        const __amdgpu_buffer_rsrc_t pres =
+            __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)  // k-step wch * 4 + ks, the only 32-row block (Cp <= 32)
+            fp[ks] = __builtin_bit_cast(bf16x8_t,
+                                        __builtin_amdgcn_raw_buffer_load_b128(pres, ((wch * 4 + ks) * 64 + lane) * 16, 0, 0));
+    }
 #pragma unroll
     for (int ry = 0; ry < NV; ++ry) {
 #pragma unroll
@@ -505,6 +527,35 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (PROJ) {
+            f32x16_t pacc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pacc[e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8_t fb = *reinterpret_cast<const bf16x8_t*>(stage + px * OS + (ks * 16 + khalf * 8) * 2);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[ks], fb, pacc, 0, 0, 0);
+            }
+            // element r of the block is output 8 (r / 4) + 4 khalf + r % 4 at column px
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int o = 8 * (r / 4) + 4 * khalf + (r % 4);
+                part[(wave * PMAX + o) * 32 + px] = pacc[r];
+            }
+            __syncthreads();
+            for (int j = threadIdx.x; j < g.Cp * 32; j += 256) {
+                const int o = j % g.Cp, col = j / g.Cp;
+                const int hw = c0 + col;
+                if (hw < g.HW) {
+                    const float sum = part[(0 * PMAX + o) * 32 + col] + part[(1 * PMAX + o) * 32 + col] +
+                                      part[(2 * PMAX + o) * 32 + col] + part[(3 * PMAX + o) * 32 + col];
+                    const long long pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
+                    Y[pos * g.Cp + o] = f32_to_bf16(sum + (bias_p ? bias_p[o] : 0.0f));
+                }
+            }
+            __syncthreads();
+            continue;
+        }
         const int c16 = lane & 7;
         const int n = ab0 * 32 + c16 * 8;
 #pragma unroll
@@ -530,10 +581,10 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     }
 }
 
-template <int KIND, int R, int WP, int BK, bool TAIL>
+template <int KIND, int R, int WP, int BK, bool TAIL, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
-    uint16_t* __restrict__ Y, RowsGeom g) {
+    uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p, RowsGeom g) {
     static_assert(R >= 1 && R <= 4 && (WP == 1 || WP == 2) && (BK == 32 || BK == 64), "tile shape");
     __shared__ __attribute__((aligned(16))) uint8_t sX[2][rows_region_rows<KIND, R, WP>() * rows_xs<BK>()];
 
@@ -556,13 +607,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const int r0 = rt * R, c0 = cl * RowsShape<KIND, WP>::NC;
     const int nv = min(R, (KIND == SPATIAL3 ? g.H : g.T) - r0);  // valid output rows (block-uniform)
     if (nv >= R)
-        rows_tile<KIND, R, WP, BK, R, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, R, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
     else if (nv == 3)
-        rows_tile<KIND, R, WP, BK, (R > 3 ? 3 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, (R > 3 ? 3 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
     else if (nv == 2)
-        rows_tile<KIND, R, WP, BK, (R > 2 ? 2 : R), TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, (R > 2 ? 2 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
     else
-        rows_tile<KIND, R, WP, BK, 1, TAIL>(Wf, X, bias, Y, g, sX, b, t, ct, r0, c0);
+        rows_tile<KIND, R, WP, BK, 1, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
 }
 
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
@@ -682,10 +733,13 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 #define CVT_ROWS_BK_T 32  // input channels per K chunk, temporal
 #endif
 
-// conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes
+// conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
+// With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
+// to Cp channels and Y is the [positions][Cp] projected output.
 template <int KIND>
 hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
-                       int B, hipStream_t s) {
+                       int B, hipStream_t s, const uint16_t* Wpf = nullptr, const float* bias_p = nullptr,
+                       int Cp = 0) {
     constexpr int R = CVT_ROWS_R;
     constexpr int WP = KIND == SPATIAL3 ? CVT_ROWS_WP_S : CVT_ROWS_WP_T;
     constexpr int BK = KIND == SPATIAL3 ? CVT_ROWS_BK_S : CVT_ROWS_BK_T;
@@ -697,6 +751,8 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     g.NA = (cg.Cout + 31) / 32;
     g.KC16 = (cg.Cin + 15) / 16;
     g.nct = (cg.Cout + S::TCH - 1) / S::TCH;
+    g.Cp = Cp;
+    g.wp_bytes = Wpf ? (int)frag_bytes(Cp, cg.Cout, 1) : 0;
     long long ntiles;
     if (KIND == SPATIAL3) {
         g.ncol = (cg.W + S::NC - 1) / S::NC;
@@ -710,12 +766,26 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
-    if (cg.Cin % BK == 0)
-        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, false>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
-                           Wf, bias, Y, g);
+    const dim3 grid((unsigned)(8LL * g.per_xcd)), block(256);
+    const bool tail = cg.Cin % BK != 0;
+    if constexpr (KIND == TEMPORAL3) {
+        if (Wpf) {
+            if (g.nct != 1 || Cp < 1 || Cp > 16) return hipErrorInvalidValue;
+            if (tail)
+                hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, true, true>), grid, block, 0, s, X, Wf, bias, Y,
+                                   Wpf, bias_p, g);
+            else
+                hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, false, true>), grid, block, 0, s, X, Wf, bias, Y,
+                                   Wpf, bias_p, g);
+            return hipGetLastError();
+        }
+    }
+    if (tail)
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, true, false>), grid, block, 0, s, X, Wf, bias, Y,
+                           (const uint16_t*)nullptr, (const float*)nullptr, g);
     else
-        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, true>), dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, X,
-                           Wf, bias, Y, g);
+        hipLaunchKernelGGL((conv_rows_kernel<KIND, R, WP, BK, false, false>), grid, block, 0, s, X, Wf, bias, Y,
+                           (const uint16_t*)nullptr, (const float*)nullptr, g);
     return hipGetLastError();
 }
 
@@ -825,6 +895,63 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     }
     if ((e = pack(w_t, wpt, Cout, Cout, k, s)) != hipSuccess) return e;
     return launch_igemm(k == 3 ? TEMPORAL3 : POINT, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
+}
+
+namespace {
+// the fused projection applies when the temporal part runs on conv_rows_kernel with every
+// output channel in one workgroup
+bool proj_fused(int k, int Cout, int Cp, long long P, bool temporal) {
+    return temporal && use_rows_kernel(k, Cout, P, Cout) && Cout <= 256 && Cp <= 16;
+}
+}  // namespace
+
+size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
+                                 bool temporal) {
+    const long long P = (long long)B * T * H * W;
+    if (proj_fused(k, Cout, Cp, P, temporal)) {
+        size_t b = pack_bytes(Cout, Cout, k) + align256(frag_bytes(Cp, Cout, 1));
+        if (spatial) b += pack_bytes(Cout, Cin, k * k) + align256((size_t)P * Cout * 2);
+        return b;
+    }
+    return conv_workspace_bytes(B, Cin, Cout, T, H, W, k, spatial, temporal) + align256((size_t)P * Cout * 2) +
+           conv_workspace_bytes(B, Cout, Cp, T, H, W, 1, true, false);
+}
+
+hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                                 const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp, int T,
+                                 int H, int W, int k, void* workspace, hipStream_t s) {
+    const long long P = (long long)B * T * H * W;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    hipError_t e;
+    if (!proj_fused(k, Cout, Cp, P, w_t != nullptr)) {
+        // conv into the workspace, then the 1x1 projection
+        size_t off = conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
+        uint16_t* ymid = reinterpret_cast<uint16_t*>(ws + off);
+        off += align256((size_t)P * Cout * 2);
+        if ((e = launch_conv_fact(x, w_s, w_t, b_s, b_t, ymid, B, Cin, Cout, T, H, W, k, ws, s)) != hipSuccess)
+            return e;
+        return launch_conv_fact(ymid, w_p, nullptr, b_p, nullptr, y, B, Cout, Cp, T, H, W, 1, ws + off, s);
+    }
+    size_t off = 0;
+    const uint16_t* tin = static_cast<const uint16_t*>(x);
+    if (w_s) {  // spatial part on its own into the workspace
+        uint8_t* sws = ws + off;
+        off += pack_bytes(Cout, Cin, k * k);
+        uint16_t* S = reinterpret_cast<uint16_t*>(ws + off);
+        off += align256((size_t)P * Cout * 2);
+        if ((e = launch_conv_fact(x, w_s, nullptr, b_s, nullptr, S, B, Cin, Cout, T, H, W, k, sws, s)) != hipSuccess)
+            return e;
+        tin = S;
+    }
+    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + off);
+    off += pack_bytes(Cout, Cout, k);
+    uint16_t* wpp = reinterpret_cast<uint16_t*>(ws + off);
+    if ((e = pack_frag(w_t, wpt, Cout, Cout, 3, s)) != hipSuccess) return e;
+    if ((e = pack_frag(w_p, wpp, Cp, Cout, 1, s)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
+    g.kchunks = (Cout + BK - 1) / BK;
+    return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp, b_p, Cp);
 }
 
 }  // namespace cvt

@@ -140,6 +140,40 @@ int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Factorized causal convolution (as cvt_causal_conv3d_fact) followed by a
+ * 1x1x1 projection to Cp channels, without writing the Cout-channel result:
+ *   y = bf16( w_p . bf16(conv(x)) + b_p ),
+ * i.e. the same two roundings as calling cvt_causal_conv3d_fact and then the
+ * k = 1 projection on its bf16 output; only the float32 summation order of the
+ * projection differs.
+ *
+ * Defined by: "Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer" (the factorized
+ * causal convolution) and the model card's "Input/Output Specifications"
+ * (latent width: 16 continuous channels, 6 FSQ channels) for the projection
+ * to the latent.
+ *
+ * x, w_s, w_t, b_s, b_t, B, Cin, Cout, T, H, W, k: as cvt_causal_conv3d_fact,
+ *      with Cin and Cout multiples of 8.
+ * w_p: bf16 [Cp, Cout, 1, 1, 1] (torch's Conv3d weight order); b_p: float32
+ *      [Cp] or NULL.
+ * y:   bf16 NTHWC [B, Cp, T, H, W].
+ * The projection runs inside the temporal convolution's epilogue when the
+ * temporal part is given, k = 3, Cout <= 256 and Cp <= 16; otherwise the
+ * convolution output is materialised in the workspace and projected by a
+ * second pass (same result).
+ * workspace: device scratch of at least cvt_causal_conv3d_fact_proj_workspace()
+ * bytes, owned by the caller (`parts` as for cvt_causal_conv3d_fact_workspace;
+ * 0 is returned for invalid arguments).
+ * Errors: as cvt_causal_conv3d_fact; CVT_E_NULL also when w_p is NULL;
+ * CVT_E_SHAPE also for Cp outside 1..4096 or Cin or Cout not a multiple of 8.
+ */
+size_t cvt_causal_conv3d_fact_proj_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, int parts);
+int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                                const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp,
+                                int T, int H, int W, int k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FSQ quantization: per position, D latent values -> one int32 index.
  *
  * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (each channel

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -112,6 +112,38 @@ def test_conv_validation_and_workspace():
     assert call(x=MIS) == E_ALIGN
     assert call(wsb=ws - 1) == E_WORKSPACE
     assert call(work=None) == E_WORKSPACE
+
+
+def test_conv_proj_validation_and_workspace():
+    """The fused conv + 1x1 entry point: workspace query (fused path: no Cout-channel
+    intermediate for a temporal-only call; fallback path: it is included) and argument
+    checks before any launch."""
+    P = 5 * 8 * 8
+    fused = lib.cvt_causal_conv3d_fact_proj_workspace(1, 256, 256, 6, 5, 8, 8, 3, 2)
+    assert 256 * 256 * 3 * 2 <= fused < 256 * 256 * 3 * 2 + P * 256 * 2
+    both = lib.cvt_causal_conv3d_fact_proj_workspace(1, 192, 256, 6, 5, 8, 8, 3, 3)
+    assert both >= 256 * 192 * 9 * 2 + 256 * 256 * 3 * 2 + P * 256 * 2
+    wide = lib.cvt_causal_conv3d_fact_proj_workspace(1, 256, 256, 24, 5, 8, 8, 3, 2)  # Cp > 16: two passes
+    assert wide >= 256 * 256 * 3 * 2 + P * 256 * 2
+    assert lib.cvt_causal_conv3d_fact_proj_workspace(1, 256, 256, 0, 5, 8, 8, 3, 2) == 0
+    assert lib.cvt_causal_conv3d_fact_proj_workspace(1, 256, 256, 6, 5, 8, 8, 2, 2) == 0
+
+    def call(**kw):
+        return lib.cvt_causal_conv3d_fact_proj(kw.get("x", A), kw.get("ws", B_), kw.get("wt", C_), None, None,
+                                               kw.get("wp", ctypes.c_void_p(0x600000)), None,
+                                               kw.get("y", ctypes.c_void_p(0x400000)), 1, kw.get("Cin", 192),
+                                               kw.get("Cout", 256), kw.get("Cp", 6), 5, 8, 8, kw.get("k", 3),
+                                               kw.get("work", ctypes.c_void_p(0x500000)), kw.get("wsb", both), None)
+    assert call(wp=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(ws=None, wt=None) == E_NULL
+    assert call(Cp=0) == E_SHAPE
+    assert call(Cp=5000) == E_SHAPE
+    assert call(Cin=12) == E_SHAPE
+    assert call(Cout=12) == E_SHAPE
+    assert call(ws=None) == E_SHAPE           # temporal-only needs Cin == Cout
+    assert call(wp=ctypes.c_void_p(0x600001)) == E_ALIGN
+    assert call(wsb=both - 1) == E_WORKSPACE
 
 
 def test_binding_rejects_mismatched_outputs():

@@ -204,3 +204,45 @@ def test_dv8x16x16_720p_chain_sampled():
             f"mismatches on safe {int(np.sum((gi != oi) & safe))}, elsewhere {int(np.sum((gi != oi) & ~safe))}")
         assert np.all(gi[safe] == oi[safe])
         assert safe.sum() > 0.5 * safe.size
+
+
+PROJ_CASES = [
+    # B, Cin, Cout, Cp, T, H, W, spatial, bias
+    (1, 192, 256, 6, 5, 12, 20, True, True),    # the 49-frame chain's shape family: conv -> 1x1 to the FSQ latent
+    (1, 256, 256, 16, 7, 9, 13, False, True),   # temporal-only, 16-dim continuous latent, frame tiles of 4 and 3
+    (2, 96, 192, 6, 6, 5, 70, True, False),     # Cout 192 in a 256-channel workgroup, ragged columns, 2 clips
+    (1, 64, 64, 3, 2, 8, 8, True, True),        # narrow channels, 2 frames
+    (1, 64, 128, 24, 3, 6, 6, True, True),      # Cp > 16: conv then a separate 1x1 pass
+]
+
+
+@pytest.mark.parametrize("case", PROJ_CASES)
+def test_conv_proj_parity(case):
+    """Fused conv + 1x1 against the oracle: conv in float64, rounded to bf16 (the stored
+    intermediate of the unfused chain), then the 1x1 projection; |g - o| <= 2e-2 (|o| + rms)."""
+    B, Cin, Cout, Cp, T, H, W, spatial, bias = case
+    log(f"conv+proj case {case}")
+    seed = 300 + Cin + Cout + Cp
+    dev, ref = make_case(B, Cin, Cout, T, H, W, 3, True, bias, seed)
+    if not spatial:
+        xb, x64 = bf16_input((B, Cout, T, H, W), seed + 9, 1.0)
+        dev["x"], ref["x"] = bits_to_torch(xb, channels_last=True), x64
+        dev["w_s"], dev["b_s"], ref["ws"], ref["bs"] = None, None, None, None
+    wpb, wp64 = bf16_input((Cp, Cout, 1, 1, 1), seed + 5, 0.05)
+    bp = si.normal((Cp,), seed + 6, 0.1) if bias else None
+    y = cvt.causal_conv3d_fact_proj(dev["x"], dev["w_s"], dev["w_t"], bits_to_torch(wpb), b_s=dev["b_s"],
+                                    b_t=dev["b_t"], b_p=f32_to_torch(bp) if bias else None)
+    torch.cuda.synchronize()
+    assert y.shape == (B, Cp, T, H, W) and y.is_contiguous(memory_format=torch.channels_last_3d)
+    if spatial:
+        o1 = oconv.causal_conv3d_fact(ref["x"], ref["ws"], ref["wt"], ref["bs"], ref["bt"])
+    else:
+        o1 = oconv.temporal_conv(ref["x"], ref["wt"], ref["bt"])
+    o = oconv.pointwise(obf16.round_to_bf16(o1), wp64, bp)
+    assert_rel(to_f64(y), o, TOL, "conv+proj")
+    # the unfused GPU chain on the same inputs agrees to a bf16 ulp or so
+    y1 = cvt.causal_conv3d_fact(dev["x"], dev["w_s"], dev["w_t"], dev["b_s"], dev["b_t"]) if spatial else \
+        cvt.causal_conv3d_fact(dev["x"], None, dev["w_t"], None, dev["b_t"])
+    y2 = cvt.causal_conv3d_fact(y1, bits_to_torch(wpb), None, f32_to_torch(bp) if bias else None)
+    torch.cuda.synchronize()
+    assert_rel(to_f64(y), to_f64(y2), 1e-2, "fused vs unfused")
