@@ -246,3 +246,44 @@ def test_conv_proj_parity(case):
     y2 = cvt.causal_conv3d_fact(y1, bits_to_torch(wpb), None, f32_to_torch(bp) if bias else None)
     torch.cuda.synchronize()
     assert_rel(to_f64(y), to_f64(y2), 1e-2, "fused vs unfused")
+
+
+def test_dv4x8x8_360p_decode_chain_sampled():
+    """8 clips, int32 indices 8 x 13 x 90 x 160 -> dequantize -> 1x1 6->192 -> conv
+    192->192 (k = 3) -> inverse Haar to 8 x 3 x 49 x 360 x 640, sampled.  The oracle runs
+    the chain on a latent window with 3 frames of causal context and a 1-pixel halo, and
+    inverts the window's coefficients; the conv output and the pixels of the window are
+    compared (the pixels inherit the conv tolerance)."""
+    cid = 5
+    wl = si.WORKLOADS["c5_dv4x8x8_360p_decode"]
+    idx = si.uniform_indices(wl["indices"], wl["seed"])
+    lift, lift64 = bf16_input((192, 6, 1, 1, 1), si.weight_seed(cid, 0), 0.02)
+    wsb, ws64 = bf16_input((192, 192, 1, 3, 3), si.weight_seed(cid, 1), 0.02)
+    wtb, wt64 = bf16_input((192, 192, 3, 1, 1), si.weight_seed(cid, 2), 0.02)
+    codes = cvt.fsq_dequantize(torch.from_numpy(idx).cuda(), dtype=torch.bfloat16, layout="NTHWC")
+    z = cvt.causal_conv3d_fact(codes, bits_to_torch(lift))
+    y = cvt.causal_conv3d_fact(z, bits_to_torch(wsb), bits_to_torch(wtb))
+    del codes, z
+    x = cvt.haar3d_inv(y)
+    torch.cuda.synchronize()
+    assert tuple(x.shape) == wl["out_x"]
+    _, Tq, Hq, Wq = idx.shape
+    for b, tq1, rows, cols in [(0, 0, (0, 3), (0, 4)), (3, 5, (40, 43), (100, 104)), (7, 12, (87, 90), (156, 160)),
+                               (5, 1, (10, 12), (0, 3))]:
+        log(f"  clip {b} window t'={tq1} rows={rows} cols={cols}")
+        tq0 = max(0, tq1 - 3)
+        r0, r1 = max(0, rows[0] - 1), min(Hq, rows[1] + 1)
+        c0, c1 = max(0, cols[0] - 1), min(Wq, cols[1] + 1)
+        oc, _ = ofsq.dequantize(idx[b:b + 1, tq0:tq1 + 1, r0:r1, c0:c1], ofsq.DEFAULT_LEVELS)
+        oz = obf16.round_to_bf16(oconv.pointwise(oc, lift64))
+        oy = oconv.causal_conv3d_fact(oz, ws64, wt64)
+        f0 = max(0, tq1 - 1)  # the inverse of latent frames f0..tq1 ends with latent frame tq1's pixels
+        sl = (slice(None), slice(None), slice(f0 - tq0, tq1 - tq0 + 1),
+              slice(rows[0] - r0, rows[1] - r0), slice(cols[0] - c0, cols[1] - c0))
+        assert_rel(to_f64(y[b:b + 1, :, f0:tq1 + 1, rows[0]:rows[1], cols[0]:cols[1]]), oy[sl], TOL, "conv 192->192")
+        ox = ohaar.haar3d_inv(obf16.round_to_bf16(oy[sl]), 2)
+        npx = 1 if tq1 == 0 else 4  # pixel frames of latent frame tq1
+        gx = to_f64(x[b:b + 1, :, max(0, 4 * tq1 - 3):4 * tq1 + 1, 4 * rows[0]:4 * rows[1], 4 * cols[0]:4 * cols[1]])
+        assert_rel(gx, ox[:, :, -npx:], TOL, "pixels")
+    del y, x
+    torch.cuda.empty_cache()
