@@ -751,7 +751,10 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 #define CVT_ROWS_SP_FA 1
 #endif
 using SpatialCfg = RowsCfg<SPATIAL3, 4, CVT_ROWS_SP_WCH, CVT_ROWS_SP_FA, 32>;
-using TemporalCfg = RowsCfg<TEMPORAL3, 4, 4, 2, 32>;
+#ifndef CVT_ROWS_TM_BK
+#define CVT_ROWS_TM_BK 32
+#endif
+using TemporalCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK>;
 
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
