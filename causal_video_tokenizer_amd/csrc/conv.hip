@@ -241,18 +241,19 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 //   SPATIAL3:  rows are image rows of one frame, columns are 64 pixels of a row plus a
 //              1-pixel halo (66); output row y, pixel x reads input row y-1+ky, pixel
 //              x-1+kx through tap (ky, kx) (KX = 3).
-// One workgroup (4 waves) computes TCH output channels x NC columns x R consecutive output
-// rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2 temporal,
-// 1 spatial): the REGION, staged once per BK-channel K chunk.  Region row rr meets tap row
-// ky in output row r0 + rr - ky.  Each wave owns FA 32-channel x FB 32-column MFMA blocks
-// (FA * FB = 2) over all R rows: per (16-channel k-step, column shift kx) it takes its
-// 3 FA weight fragments (3 tap rows) once and walks the region rows, each activation
-// fragment feeding up to three tap rows, i.e. three output rows.  The temporal conv puts
-// all 256 channels in one workgroup (4 channel waves x 32 positions), so each region is
-// staged once for every output channel.
+// One workgroup (4 or 8 waves) computes TCH output channels x NC columns x R consecutive
+// output rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2
+// temporal, 1 spatial): the REGION, staged once per BK-channel K chunk.  Region row rr
+// meets tap row ky in output row r0 + rr - ky.  Each wave owns FA 32-channel x FB 32-column
+// MFMA blocks (FA * FB = 2) over all R rows: per (16-channel k-step, column shift kx) it
+// takes its 3 FA weight fragments (3 tap rows) once and walks the region rows, each
+// activation fragment feeding up to three tap rows, i.e. three output rows.  Both
+// convolutions use FA = 1, FB = 2 (32 channels x 64 columns per wave), which needs half the
+// weight bytes per MFMA of 64 x 32.  The temporal conv puts up to 256 channels in one
+// workgroup of 8 waves, so each region is staged once for every output channel.
 //
-// Only the region is staged in LDS (two buffers of 15-32 KB, so two workgroups share a CU
-// and one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
+// Only the region is staged in LDS (two buffers of 30-36 KB; two 4-wave workgroups share a
+// CU, so one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
 // once per call in MFMA fragment order (see pack_frag_kernel): each fragment is 1 KB of
 // which lane l reads bytes [16 l, 16 l + 16), one coalesced load straight into the operand
 // registers, prefetched one step ahead.  The region loads of chunk c + 1 are issued in two
@@ -282,13 +283,14 @@ constexpr int rows_xs() {
 }
 constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (tensors stay below it)
 
-// Tile configuration.  A workgroup has 4 waves: WCH along output channels and 4 / WCH
-// along columns.  Each wave owns FA 32-channel MFMA blocks x FB 32-column blocks
+// Tile configuration.  A workgroup has NW waves (4 or 8): WCH along output channels and
+// NW / WCH along columns.  Each wave owns FA 32-channel MFMA blocks x FB 32-column blocks
 // (FA * FB = 2, so 128 fp32 accumulators for R = 4 rows) over all R output rows.
-template <int KIND_, int R_, int WCH_, int FA_, int BK_>
+template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4>
 struct RowsCfg {
-    static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_;
-    static constexpr int WPOS = 4 / WCH;                        // waves along columns
+    static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_, NW = NW_;
+    static constexpr int NTH = 64 * NW;                         // threads per workgroup
+    static constexpr int WPOS = NW / WCH;                       // waves along columns
     static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;         // column shifts
     static constexpr int TCH = 32 * FA * WCH;                   // output channels per workgroup
     static constexpr int NC = 32 * FB * WPOS;                   // output columns per workgroup
@@ -298,19 +300,24 @@ struct RowsCfg {
     // over the 256 threads: every thread issues the same unguarded loads (padding rows read
     // zeros and are never used), which keeps the compiler from sinking a guarded load into a
     // branch followed by a full memory wait
-    static constexpr int PASS = 256 / (BK / 8);
+    static constexpr int PASS = NTH / (BK / 8);
     static constexpr int XROWS = ((R + 2) * RC + PASS - 1) / PASS * PASS;
-    static_assert(WCH * WPOS == 4 && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 && R <= 4, "tile shape");
+    static constexpr int REGION_BYTES = 2 * XROWS * rows_xs<BK>();       // the two region buffers
+    static constexpr int PRS = TCH * 2 + 16;                              // fused projection: bytes per staged column
+    static constexpr int PROJ_BYTES = R * NC * PRS;                       // R frames of staged columns
+    static_assert((NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
+                      R <= 4,
+                  "tile shape");
 };
 
 template <typename C, int NV, bool TAIL, bool PROJ>
 __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
                                           const float* __restrict__ bias, uint16_t* __restrict__ Y,
                                           const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
-                                          const RowsGeom& g, uint8_t (*sX)[C::XROWS * C::XS], int b, int t, int ct,
+                                          const RowsGeom& g, uint8_t* smem, int b, int t, int ct,
                                           int r0, int c0) {
     constexpr int KIND = C::KIND, BK = C::BK, FA = C::FA, FB = C::FB;
-    constexpr int NTH = 256, RC = C::RC, KX = C::KX, CPR = BK / 8, XS = C::XS, KS = BK / 16;
+    constexpr int NTH = C::NTH, RC = C::RC, KX = C::KX, CPR = BK / 8, XS = C::XS, KS = BK / 16;
     constexpr int WCH = C::WCH;
     constexpr int XROWS = C::XROWS;
     constexpr int XQ = XROWS * CPR;
@@ -320,6 +327,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in a scalar register
     const int wch = wave % WCH, wpos = wave / WCH;
+    auto sX = [&](int buf) { return smem + buf * (XROWS * XS); };  // the two region buffers
 
     // Region chunk q of a thread is (row, c16) with 8 consecutive lanes on 8 consecutive rows
     // at one chunk: LDS stores go 8 lanes (128 bytes) at a time, and 8 rows of 80 bytes at
@@ -379,7 +387,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             const int q = tid + NTH * i;
             int row, c16;
             xmap(q, row, c16);
-            if (XQ % NTH == 0 || q < XQ) *reinterpret_cast<uint4*>(&sX[buf][row * XS + c16 * 16]) = xr[i - half * XH];
+            if (XQ % NTH == 0 || q < XQ) *reinterpret_cast<uint4*>(sX(buf) + row * XS + c16 * 16) = xr[i - half * XH];
         }
     };
 
@@ -465,7 +473,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     }
     __syncthreads();
     for (int kc = 0; kc < nchunks; ++kc) {
-        const uint8_t* xb = sX[kc & 1] + (wpos * 32 * FB + px) * XS;
+        const uint8_t* xb = sX(kc & 1) + (wpos * 32 * FB + px) * XS;
         const int nbuf = (kc + 1) & 1;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -490,17 +498,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         __syncthreads();
     }
 
-    // ---- epilogue: bias, bf16 RNE, staged per output row through a wave-private LDS tile
-    // of 32 FB columns x 32 FA channels (rows of 64 FA bytes + 16 bytes of padding, so the
-    // 8-byte writes of 8 consecutive columns hit distinct banks), then written back with
-    // each 4 FA consecutive lanes storing one position's 64 FA contiguous bytes.  The region
-    // buffers are free after the last barrier of the K loop; a wave reads back only what it
-    // wrote and its LDS accesses execute in order, so no barrier is needed.
-    constexpr int OS = 64 * FA + 16;
-    constexpr int STAGE = 32 * FB * OS;  // bytes per wave
-    static_assert(4 * STAGE <= 2 * XROWS * XS, "epilogue staging fits in the region buffers");
-    uint8_t* stage = &sX[0][0] + wave * STAGE;
-    const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
+    // ---- epilogue.  Bias of the accumulator elements: element 4 q + e of block a is output
+    // channel (ab0 + a) * 32 + 8 q + 4 khalf + e.
     float bv[FA][4][4];
 #pragma unroll
     for (int a = 0; a < FA; ++a)
@@ -511,25 +510,96 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf + e;
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
-    // Fused 1x1 projection (PROJ, temporal kernel with all output channels in the workgroup):
-    // per output row, each wave multiplies its staged bf16 64-channel slice by the matching
-    // four k-steps of the projection weights (fragment order, rows o >= Cp zero) with MFMAs,
-    // the four partial sums meet in LDS after the staging tiles, and one pass adds the bias
-    // and rounds to bf16 once.  The rounding points are those of the separate 1x1 conv on
-    // the bf16 output; only the fp32 summation order differs.
-    constexpr int PMAX = 16;  // projection outputs handled in the epilogue
-    float* part = reinterpret_cast<float*>(&sX[0][0] + 4 * STAGE);  // [4 waves][PMAX][32]
-    static_assert(!PROJ || (4 * STAGE + 4 * PMAX * 32 * 4 <= 2 * XROWS * XS && WCH == 4 && FA == 2),
-                  "projection partials fit after the staging tiles; all channels in one workgroup");
-    bf16x8_t fp[4];
+
     if constexpr (PROJ) {
-        const __amdgpu_buffer_rsrc_t pres =
-            __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
+        // Fused 1x1 projection (temporal kernel with every output channel in the workgroup).
+        // The tile's conv outputs, bias added and rounded to bf16 once (what a separate 1x1
+        // conv would read), are staged in LDS as [frame][column][channel] rows; then each wave
+        // takes (frame, 32-column block) pairs and multiplies the projection weights (A
+        // operand, rows o < Cp, standard fragment order) by the staged columns over all TCH
+        // channels (B operand), so every projected value is one MFMA accumulation chain and no
+        // partial sums cross waves.  Channels past Cout are staged as zeros.
+        constexpr int TCH = C::TCH, NC = C::NC, PRS = C::PRS, KST = TCH / 16;
+        const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
+        // the projection weights (the only 32-row block, Cp <= 32; k-steps past Cout read
+        // zeros) are requested first and arrive while the tile is staged
+        bf16x8_t fp[KST];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)  // k-step wch * 4 + ks, the only 32-row block (Cp <= 32)
-            fp[ks] = __builtin_bit_cast(bf16x8_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(pres, ((wch * 4 + ks) * 64 + lane) * 16, 0, 0));
+        for (int ks = 0; ks < KST; ++ks)
+            fp[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(pres, (ks * 64 + lane) * 16, 0, 0));
+#pragma unroll
+        for (int ry = 0; ry < NV; ++ry)
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int cb = 0; cb < FB; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x16_t& c = acc[ry][a][cb];
+                        const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf;  // first of 4 channels (Cout % 8 == 0)
+                        uint2 u;
+                        u.x = pack_bf16x2(c[4 * q] + bv[a][q][0], c[4 * q + 1] + bv[a][q][1]);
+                        u.y = pack_bf16x2(c[4 * q + 2] + bv[a][q][2], c[4 * q + 3] + bv[a][q][3]);
+                        if (n >= g.Cout) u = make_uint2(0u, 0u);
+                        *reinterpret_cast<uint2*>(smem + (ry * NC + wpos * 32 * FB + cb * 32 + px) * PRS + n * 2) = u;
+                    }
+        __syncthreads();
+        const int Cp = g.Cp;
+        float bp[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int o = 8 * (r / 4) + 4 * khalf + (r % 4);
+            bp[r] = bias_p && o < Cp ? bias_p[o] : 0.0f;
+        }
+        constexpr int NBLK = NC / 32;  // 32-column blocks per frame
+        for (int pr = wave; pr < NV * NBLK; pr += C::NW) {  // wave-uniform
+            const int fr = pr / NBLK, cblk = pr % NBLK;
+            const uint8_t* brow = smem + (fr * NC + cblk * 32 + px) * PRS + khalf * 16;
+            f32x16_t pacc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pacc[e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks)
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[ks], *reinterpret_cast<const bf16x8_t*>(brow + ks * 32),
+                                                               pacc, 0, 0, 0);
+            // element r < 8 is projection output 8 (r / 4) + 4 khalf + r % 4 at column px
+            const int hw = c0 + cblk * 32 + px;
+            if (hw < g.HW) {
+                uint16_t* yp = Y + (((long long)b * g.T + r0 + fr) * g.HW + hw) * Cp;
+                if ((Cp & 3) == 0) {  // 4 consecutive outputs per 8-byte store
+#pragma unroll
+                    for (int hq = 0; hq < 2; ++hq) {
+                        const int o = 8 * hq + 4 * khalf;
+                        if (o < Cp) {
+                            uint2 u;
+                            u.x = pack_bf16x2(pacc[4 * hq] + bp[4 * hq], pacc[4 * hq + 1] + bp[4 * hq + 1]);
+                            u.y = pack_bf16x2(pacc[4 * hq + 2] + bp[4 * hq + 2], pacc[4 * hq + 3] + bp[4 * hq + 3]);
+                            *reinterpret_cast<uint2*>(yp + o) = u;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int o = 8 * (r / 4) + 4 * khalf + (r % 4);
+                        if (o < Cp) yp[o] = f32_to_bf16(pacc[r] + bp[r]);
+                    }
+                }
+            }
+        }
+        return;
     }
+
+    // Bias, bf16 RNE, staged per output row through a wave-private LDS tile of 32 FB columns
+    // x 32 FA channels (rows of 64 FA bytes + 16 bytes of padding, so the 8-byte writes of 8
+    // consecutive columns hit distinct banks), then written back with each 4 FA consecutive
+    // lanes storing one position's 64 FA contiguous bytes.  The region buffers are free after
+    // the last barrier of the K loop; a wave reads back only what it wrote and its LDS
+    // accesses execute in order, so no barrier is needed.
+    constexpr int OS = 64 * FA + 16;
+    constexpr int STAGE = 32 * FB * OS;  // bytes per wave
+    static_assert(C::NW * STAGE <= C::REGION_BYTES, "epilogue staging fits in the region buffers");
+    uint8_t* stage = smem + wave * STAGE;
+    const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
 #pragma unroll
     for (int ry = 0; ry < NV; ++ry) {
 #pragma unroll
@@ -546,35 +616,6 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if constexpr (PROJ) {
-            f32x16_t pacc;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) pacc[e] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8_t fb = *reinterpret_cast<const bf16x8_t*>(stage + px * OS + (ks * 16 + khalf * 8) * 2);
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[ks], fb, pacc, 0, 0, 0);
-            }
-            // element r of the block is output 8 (r / 4) + 4 khalf + r % 4 at column px
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int o = 8 * (r / 4) + 4 * khalf + (r % 4);
-                part[(wave * PMAX + o) * 32 + px] = pacc[r];
-            }
-            __syncthreads();
-            for (int j = threadIdx.x; j < g.Cp * 32; j += 256) {
-                const int o = j % g.Cp, col = j / g.Cp;
-                const int hw = c0 + col;
-                if (hw < g.HW) {
-                    const float sum = part[(0 * PMAX + o) * 32 + col] + part[(1 * PMAX + o) * 32 + col] +
-                                      part[(2 * PMAX + o) * 32 + col] + part[(3 * PMAX + o) * 32 + col];
-                    const long long pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
-                    Y[pos * g.Cp + o] = f32_to_bf16(sum + (bias_p ? bias_p[o] : 0.0f));
-                }
-            }
-            __syncthreads();
-            continue;
-        }
         constexpr int CPP = 4 * FA;   // 16-byte chunks per position slice
         constexpr int PPI = 64 / CPP;  // positions per store instruction
         const int c16 = lane % CPP;
@@ -603,11 +644,12 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 }
 
 template <typename C, bool TAIL, bool PROJ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
+__global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
     uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p, RowsGeom g) {
     constexpr int KIND = C::KIND, R = C::R;
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][C::XROWS * C::XS];
+    // the region buffers; the fused projection's partial sums reuse them after the K loop
+    __shared__ __attribute__((aligned(16))) uint8_t smem[PROJ ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -625,16 +667,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         t = tile % g.T;
         b = tile / g.T;
     }
-    const int r0 = rt * R, c0 = cl * C::NC;
-    const int nv = min(R, (KIND == SPATIAL3 ? g.H : g.T) - r0);  // valid output rows (block-uniform)
+    // the rows are split evenly over the nrow = ceil(rows / R) row tiles (13 frames as
+    // 4 + 3 + 3 + 3, not 4 + 4 + 4 + 1): a tile's weight traffic does not shrink with its
+    // row count, so one short tile costs nearly as much as a full one
+    const int rows = KIND == SPATIAL3 ? g.H : g.T;
+    const int rbase = rows / g.nrow, rextra = rows - rbase * g.nrow;
+    const int nv = rbase + (rt < rextra ? 1 : 0);  // valid output rows (block-uniform, <= R)
+    const int r0 = rt * rbase + min(rt, rextra), c0 = cl * C::NC;
     if (nv >= R)
-        rows_tile<C, R, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
+        rows_tile<C, R, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
     else if (nv == 3)
-        rows_tile<C, (R > 3 ? 3 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
+        rows_tile<C, (R > 3 ? 3 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
     else if (nv == 2)
-        rows_tile<C, (R > 2 ? 2 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
+        rows_tile<C, (R > 2 ? 2 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
     else
-        rows_tile<C, 1, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, sX, b, t, ct, r0, c0);
+        rows_tile<C, 1, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
 }
 
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
@@ -651,7 +698,8 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restri
         const int ab = (int)(f % NA);
         const long long f2 = f / NA;
         const int j = (int)(f2 % ntaps), kc16 = (int)(f2 / ntaps);
-        const int row = ab * 32 + (l & 31), k = kc16 * 16 + (l >> 5) * 8 + e;
+        const int row = ab * 32 + (l & 31);
+        const int k = kc16 * 16 + (l >> 5) * 8 + e;
         wf[i] = (row < Cout && k < Cin) ? w[((size_t)row * Cin + k) * ntaps + j] : (uint16_t)0;
     }
 }
@@ -741,30 +789,35 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 // Tile configurations of conv_rows_kernel (see RowsCfg).  Spatial: 4 channel waves of 32
 // channels x 64 pixels each (128 x 64 per workgroup): three weight fragments per step per
 // wave instead of six, which relieves the per-CU vector-memory path that carries them
-// (measured 2-3% faster than 2 x 2 waves of 64 x 32).  Temporal: 4 channel waves of 64
-// channels x 32 positions (all 256 output channels in one workgroup, which the fused
-// projection needs).
+// (measured 2-3% faster than 2 x 2 waves of 64 x 32).  Temporal: waves of 32 channels x 64
+// positions as well, 8 of them for up to 256 output channels (all in one workgroup, which
+// the fused projection needs), 4 for up to 128.
 #ifndef CVT_ROWS_SP_WCH
 #define CVT_ROWS_SP_WCH 4
 #endif
 #ifndef CVT_ROWS_SP_FA
 #define CVT_ROWS_SP_FA 1
 #endif
-using SpatialCfg = RowsCfg<SPATIAL3, 4, CVT_ROWS_SP_WCH, CVT_ROWS_SP_FA, 32>;
+#ifndef CVT_ROWS_SP_NW
+#define CVT_ROWS_SP_NW 4
+#endif
+#ifndef CVT_ROWS_SP_BK
+#define CVT_ROWS_SP_BK 32
+#endif
+using SpatialCfg = RowsCfg<SPATIAL3, 4, CVT_ROWS_SP_WCH, CVT_ROWS_SP_FA, CVT_ROWS_SP_BK, CVT_ROWS_SP_NW>;
 #ifndef CVT_ROWS_TM_BK
 #define CVT_ROWS_TM_BK 32
 #endif
-using TemporalCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK>;
+using TemporalCfg = RowsCfg<TEMPORAL3, 4, 8, 1, CVT_ROWS_TM_BK, 8>;
+using TemporalNarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, CVT_ROWS_TM_BK, 4>;
 
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
 // to Cp channels and Y is the [positions][Cp] projected output.
-template <int KIND>
-hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
-                       int B, hipStream_t s, const uint16_t* Wpf = nullptr, const float* bias_p = nullptr,
-                       int Cp = 0) {
-    using C = std::conditional_t<KIND == SPATIAL3, SpatialCfg, TemporalCfg>;
-    constexpr int R = C::R, BK = C::BK;
+template <typename C>
+hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
+                           int B, hipStream_t s, const uint16_t* Wpf, const float* bias_p, int Cp) {
+    constexpr int KIND = C::KIND, R = C::R, BK = C::BK;
     RowsGeom g{};
     g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
     g.x_bytes = (int)(cg.P * cg.Cin * 2);
@@ -787,7 +840,7 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
-    const dim3 grid((unsigned)(8LL * g.per_xcd)), block(256);
+    const dim3 grid((unsigned)(8LL * g.per_xcd)), block(C::NTH);
     const bool tail = cg.Cin % BK != 0;
     if constexpr (KIND == TEMPORAL3) {
         if (Wpf) {
@@ -808,6 +861,21 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
         hipLaunchKernelGGL((conv_rows_kernel<C, false, false>), grid, block, 0, s, X, Wf, bias, Y,
                            (const uint16_t*)nullptr, (const float*)nullptr, g);
     return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
+                       int B, hipStream_t s, const uint16_t* Wpf = nullptr, const float* bias_p = nullptr,
+                       int Cp = 0) {
+    if constexpr (KIND == SPATIAL3)
+        return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
+#ifdef CVT_TM_NARROW_ALL
+    if (cg.Cout <= TemporalNarrowCfg::TCH || !Wpf)
+#else
+    if (cg.Cout <= TemporalNarrowCfg::TCH)
+#endif
+        return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
+    return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
 }
 
 hipError_t launch_igemm(int kind, const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y,
