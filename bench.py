@@ -19,7 +19,11 @@ with HIP events on the launch stream over the timed steps.  The CPU baseline is
 the float64 oracle timed on a bounded sample of the same workload (a strip of
 the frame), scaled to the full clip.  A second object reports the 121-frame
 CV8x8x8-720p-shaped chain (two factorized conv layers and the 1x1), where the
-convolution's MFMA fraction is quoted.
+convolution's MFMA fraction is quoted; a third, FSQ quantize and dequantize at a
+bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak.
+
+The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
+stage measures about 10% slower.
 """
 
 import argparse
@@ -52,11 +56,13 @@ COPY_FETCH_KIB, COPY_WRITE_KIB = 131091.9, 262144.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=25,
+                    help="untimed steps first; below about 20 the GPU clocks have not settled (~10%% slower)")
     ap.add_argument("--workload", default="c4_dv8x16x16_720p_49f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-c3", action="store_true", help="skip the 121-frame chain measurement")
+    ap.add_argument("--no-fsq-bw", action="store_true", help="skip the FSQ bandwidth-size measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -180,6 +186,7 @@ def main():
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
+    fsq_bw = None if args.no_fsq_bw else fsq_bandwidth(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -215,6 +222,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": per_stage,
         "cv8x8x8_720p_121f": c3,
+        "fsq_bandwidth_size": fsq_bw,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -267,7 +275,7 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
     ]
     stream = torch.cuda.current_stream(dev)
     steps = max(2, args.steps // 2)
-    for _ in range(max(1, args.warmup)):
+    for _ in range(max(1, min(args.warmup, 10))):  # the clocks drop while the host generates the clip
         for _, fn, _ in stages:
             fn()
     torch.cuda.synchronize()
@@ -297,6 +305,54 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
     out["conv_TFLOPs"] = round(conv_flops / (conv_ms * 1e-3) / 1e12, 1)
     out["conv_mfma_frac"] = round(conv_flops / (conv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     del x, hz, a, b, lat, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def fsq_bandwidth(cvt, si, torch, dev, args):
+    """FSQ quantize and dequantize at a size where HBM bandwidth, not launch latency,
+    bounds them: 64 latents of the 49-frame grid, 64 x 6 x 13 x 180 x 320 bf16 N(0, 1.5)
+    (575 MB of latents, 192 MB of indices), planar (NCTHW) and channels-last (NTHWC).
+    Each call moves 6 x 2 + 4 bytes per position; timed over back-to-back calls with HIP
+    events and reported against the 8 TB/s HBM peak."""
+    wl = si.WORKLOADS["fsq_bw"]
+    shape = wl["latent"]
+    B, D, T, H, W = shape
+    P = B * T * H * W
+    log(f"FSQ bandwidth size: generating {shape} ...")
+    zb = si.to_bf16_bits(si.normal(shape, wl["latent_seed"], wl["latent_std"]))
+    z = torch.from_numpy(np.ascontiguousarray(zb).view(np.int16)).view(torch.bfloat16).to(dev)
+    del zb
+    zc = z.to(memory_format=torch.channels_last_3d)
+    idx = torch.empty((B, T, H, W), dtype=torch.int32, device=dev)
+    codes = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    codes_c = torch.empty_like(zc)
+    cases = [
+        ("quantize_ncthw", lambda: cvt.fsq_quantize(z, indices=idx)),
+        ("dequantize_ncthw", lambda: cvt.fsq_dequantize(idx, layout="NCTHW", out=codes)),
+        ("quantize_nthwc", lambda: cvt.fsq_quantize(zc, indices=idx)),
+        ("dequantize_nthwc", lambda: cvt.fsq_dequantize(idx, out=codes_c)),
+    ]
+    reps = max(10, args.steps)
+    nbytes = P * (D * 2 + 4.0)
+    out = {"shape": list(shape), "bytes_per_call": nbytes, "reps": reps}
+    # the GPU idled while the host generated the latents: bring its clocks back up first
+    for _ in range(max(10, args.warmup)):
+        for _, fn in cases:
+            fn()
+    torch.cuda.synchronize()
+    for name, fn in cases:
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del z, zc, idx, codes, codes_c
     torch.cuda.empty_cache()
     return out
 

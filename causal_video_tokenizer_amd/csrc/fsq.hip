@@ -153,19 +153,24 @@ __global__ __launch_bounds__(256) void fsq_quantize_default_kernel(const T* __re
     __shared__ uint4 stage[4][64 * SCH];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint4* st = stage[w];
-    const long long wave_id = (long long)blockIdx.x * 4 + w;
-    const long long nfull = total / WAVE_POS;
+    // Planar latents: grid row blockIdx.y is one clip (its npb positions, a multiple of 8
+    // on this path), so the plane offsets need no division; NTHWC: one row over all.
+    const long long base = LAYOUT == CVT_NCTHW ? (long long)blockIdx.y * npb : 0;
+    const long long span = LAYOUT == CVT_NCTHW ? npb : total;
+    const long long wave_id = (long long)blockIdx.x * 4 + w;  // wave tile within the row
+    const long long nfull = span / WAVE_POS;
     if (wave_id > nfull) return;
     const bool full = wave_id < nfull;
-    const long long pos0 = wave_id * WAVE_POS + lane * G;
-    if (!full && pos0 >= total) return;
+    const long long lpos0 = wave_id * WAVE_POS + lane * G;
+    if (!full && lpos0 >= span) return;
+    const long long pos0 = base + lpos0;
 
-    if (full || pos0 + G <= total) {
+    if (full || lpos0 + G <= span) {
         float v[D][G];  // v[i][k]: channel i of position pos0 + k
         long long b = 0, r = 0;
         if (LAYOUT == CVT_NCTHW) {
-            b = pos0 / npb;
-            r = pos0 - b * npb;
+            b = blockIdx.y;
+            r = lpos0;
 #pragma unroll
             for (int i = 0; i < D; ++i) load8<T>(z + ((size_t)b * D + i) * npb + r, v[i]);
         } else {
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void fsq_quantize_default_kernel(const T* __re
             st[2 * lane] = *reinterpret_cast<uint4*>(&o0);
             st[2 * lane + 1] = *reinterpret_cast<uint4*>(&o1);
             wave_lds_sync();
-            uint4* dst = reinterpret_cast<uint4*>(idx + wave_id * WAVE_POS);
+            uint4* dst = reinterpret_cast<uint4*>(idx + base + wave_id * WAVE_POS);
             st_stream16(dst + lane, st[lane]);
             st_stream16(dst + 64 + lane, st[64 + lane]);
         } else {
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(256) void fsq_quantize_default_kernel(const T* __re
         }
         return;
     }
-    for (long long pos = pos0; pos < total; ++pos) {  // last partial group (< 8 positions)
+    for (long long pos = pos0; pos < base + span; ++pos) {  // last partial group (< 8 positions, NTHWC only)
         int a = 0;
         bool isnan_ = false;
         const long long b = pos / npb, r = pos - b * npb;
@@ -638,15 +643,18 @@ hipError_t quantize_t(const void* z, int32_t* idx, void* codes, const FsqParams&
     const long long total = B * npb;
     // vector path: 8-aligned plane starts for NCTHW; NTHWC spans are always contiguous
     const int vec = LAYOUT == CVT_NTHWC ? 1 : (npb % G == 0);
-    if (is_default(p) && vec) {
-        const long long nblk = (total + 4 * WAVE_POS - 1) / (4 * WAVE_POS);  // one 512-position tile per wave
+    if (is_default(p) && vec && (LAYOUT == CVT_NTHWC || B <= 65535)) {
+        // one 512-position tile per wave; planar latents get one grid row per clip
+        const long long span = LAYOUT == CVT_NCTHW ? npb : total;
+        const long long nblk = (span + 4 * WAVE_POS - 1) / (4 * WAVE_POS);
         if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)nblk, LAYOUT == CVT_NCTHW ? (unsigned)B : 1u);
         if (codes)
-            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, true>), dim3((unsigned)nblk), dim3(256), 0, s,
-                               (const T*)z, idx, (T*)codes, p, npb, total);
+            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, true>), grid, dim3(256), 0, s, (const T*)z, idx,
+                               (T*)codes, p, npb, total);
         else
-            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, false>), dim3((unsigned)nblk), dim3(256), 0, s,
-                               (const T*)z, idx, (T*)nullptr, p, npb, total);
+            hipLaunchKernelGGL((fsq_quantize_default_kernel<T, LAYOUT, false>), grid, dim3(256), 0, s, (const T*)z, idx,
+                               (T*)nullptr, p, npb, total);
         return hipGetLastError();
     }
     if (p.D == 6) return quantize_nt<T, LAYOUT, 6>(z, idx, codes, p, npb, total, vec, s);

@@ -128,4 +128,6 @@ WORKLOADS = {
     "c5_dv4x8x8_360p_decode": dict(
         indices=(8, 13, 90, 160), seed=1005,
         convs=[(6, 192, 1), (192, 192, 3)], out_x=(8, 3, 49, 360, 640)),
+    # FSQ at a bandwidth-meaningful size: 64 latents of the 49-frame 720p grid
+    "fsq_bw": dict(latent=(64, 6, 13, 180, 320), latent_seed=1015, latent_std=1.5),
 }
