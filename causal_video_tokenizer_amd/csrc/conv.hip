@@ -248,9 +248,11 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 // MFMA blocks (FA * FB = 2) over all R rows: per (16-channel k-step, column shift kx) it
 // takes its 3 FA weight fragments (3 tap rows) once and walks the region rows, each
 // activation fragment feeding up to three tap rows, i.e. three output rows.  Both
-// convolutions use FA = 1, FB = 2 (32 channels x 64 columns per wave), which needs half the
-// weight bytes per MFMA of 64 x 32.  The temporal conv puts up to 256 channels in one
-// workgroup of 8 waves, so each region is staged once for every output channel.
+// convolutions mostly use FA = 1, FB = 2 (32 channels x 64 columns per wave), which needs
+// half the weight bytes per MFMA of 64 x 32.  The temporal conv puts up to 256 channels in
+// one workgroup (8 waves, or 4 waves of 64 x 32 with the fused projection), so each region
+// is staged once for every output channel.  A step's activation reads are issued during the
+// previous step's MFMAs (see compute), so only a chunk's first step waits for LDS.
 //
 // Only the region is staged in LDS (two buffers of 30-36 KB; two 4-wave workgroups share a
 // CU, so one's barrier and epilogue overlap the other's MFMAs).  The weights are packed
@@ -286,6 +288,9 @@ constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows
 // Tile configuration.  A workgroup has NW waves (4 or 8): WCH along output channels and
 // NW / WCH along columns.  Each wave owns FA 32-channel MFMA blocks x FB 32-column blocks
 // (FA * FB = 2, so 128 fp32 accumulators for R = 4 rows) over all R output rows.
+#ifndef CVT_ROWS_SP_PD
+#define CVT_ROWS_SP_PD 1
+#endif
 template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4>
 struct RowsCfg {
     static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_, NW = NW_;
@@ -300,6 +305,7 @@ struct RowsCfg {
     // over the 256 threads: every thread issues the same unguarded loads (padding rows read
     // zeros and are never used), which keeps the compiler from sinking a guarded load into a
     // branch followed by a full memory wait
+    static constexpr int PD = KIND == SPATIAL3 ? CVT_ROWS_SP_PD : 1;  // weight prefetch distance in steps
     static constexpr int PASS = NTH / (BK / 8);
     static constexpr int XROWS = ((R + 2) * RC + PASS - 1) / PASS * PASS;
     static constexpr int REGION_BYTES = 2 * XROWS * rows_xs<BK>();       // the two region buffers
@@ -394,7 +400,11 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // weight fragments of (k-step kc16, column shift kx): tap rows 0..2 of blocks ab0 ..
     // ab0 + FA - 1
     const int ab0 = ct * (FA * WCH) + wch * FA;
-    bf16x8_t fa[2][3][FA];
+    // weight fragments are prefetched PD steps ahead into NSET = PD + 1 register sets; a
+    // chunk's step count is a multiple of NSET, so step st of every chunk uses set st % NSET
+    constexpr int PD = C::PD, NSET = PD + 1;
+    static_assert(C::KX * KS % NSET == 0, "whole fragment-set cycles per chunk");
+    bf16x8_t fa[NSET][3][FA];
     const int lane16 = lane * 16;
     auto load_frags = [&](int kc16, int kx, int set) {
 #pragma unroll
@@ -430,41 +440,58 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 for (int e = 0; e < 16; ++e) acc[f][a][cb][e] = 0.0f;
 
     const int khalf = lane >> 5, px = lane & 31;
-    auto compute = [&](const uint8_t* xb, int ks, int kx, int set) {
-        const int ch = ks * 2 + khalf;
-        bf16x8_t fb[NRU][FB];
+    // Activation fragments of step s, region row rr: FB 32-column blocks at column shift
+    // s % KX, channels of k-step s / KX.
+    auto read_row = [&](bf16x8_t (&f)[NRU][FB], const uint8_t* xb, int s, int rr) {
+        const int ch = (s / KX) * 2 + khalf, kx = s % KX;
 #pragma unroll
-        for (int rr = 0; rr < NRU; ++rr)
+        for (int cb = 0; cb < FB; ++cb)
+            f[rr][cb] = *reinterpret_cast<const bf16x8_t*>(xb + (rr * RC + cb * 32 + kx) * XS + ch * 16);
+    };
+    // The MFMAs of region row rr: it meets tap row ky in output row rr - ky.
+    auto mfma_row = [&](const bf16x8_t (&f)[NRU][FB], int set, int rr) {
 #pragma unroll
-            for (int cb = 0; cb < FB; ++cb)
-                fb[rr][cb] = *reinterpret_cast<const bf16x8_t*>(xb + (rr * RC + cb * 32 + kx) * XS + ch * 16);
-        // all activation reads of the step go out before its MFMAs (left alone the compiler
-        // reuses one register and waits for each read right before its first MFMA)
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ky = 0; ky < 3; ++ky) {
+            const int ry = rr - ky;
+            if (ry < 0 || ry >= NV) continue;
 #pragma unroll
-        for (int rr = 0; rr < NRU; ++rr)
+            for (int a = 0; a < FA; ++a)
 #pragma unroll
-            for (int ky = 0; ky < 3; ++ky) {
-                const int ry = rr - ky;
-                if (ry < 0 || ry >= NV) continue;
+                for (int cb = 0; cb < FB; ++cb)
+                    acc[ry][a][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ky][a], f[rr][cb], acc[ry][a][cb],
+                                                                             0, 0, 0);
+        }
+    };
+    // One step's MFMAs with the next step's activation reads software-pipelined into them:
+    // row rr of step s + 1 is read right after the MFMAs of row rr of step s, the last use
+    // of that row's registers, so every read has the rest of the step to arrive (the
+    // scheduling barriers keep that order; left alone the compiler would move the reads).
+    auto compute = [&](const bf16x8_t (&cur)[NRU][FB], bf16x8_t (&nxt)[NRU][FB], const uint8_t* xb, int s, int set,
+                       bool read_next) {
 #pragma unroll
-                for (int a = 0; a < FA; ++a)
-#pragma unroll
-                    for (int cb = 0; cb < FB; ++cb)
-                        acc[ry][a][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ky][a], fb[rr][cb],
-                                                                                 acc[ry][a][cb], 0, 0, 0);
-            }
+        for (int rr = 0; rr < NRU; ++rr) {
+            mfma_row(cur, set, rr);
+            if (read_next) read_row(nxt, xb, s + 1, rr);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
-    // Steps of a chunk: the weight prefetch of step s + 1 comes first, then the region
+    // Steps of a chunk: the weight prefetch of step s + PD comes first, then the region
     // batches: batch 0 is loaded at step 0 and stored at step L1, batch 1 loaded at step L1
     // and stored at the chunk's end (with fewer than 4 steps both are loaded at step 0 and
-    // stored at the end).  The memory counter completes in order, so a weight
-    // wait at step s also waits for every region batch issued before step s - 1.
+    // stored at the end).  The memory counter completes in order, so a weight wait at step s
+    // also waits for every region batch issued before step s - PD: with PD = 2 a region
+    // load has at least three steps to arrive from HBM before any weight wait covers it.
     constexpr int L1 = NS >= 4 ? NS / 2 : 0;
     static_assert(L1 > 0 || XH == XL, "a single batch when both would be in flight together");
     const int nchunks = (g.Cin + BK - 1) / BK;
-    load_frags(0, 0, 0);
+    // step s of chunk kc: k-step KS kc + s / KX, column shift s % KX (s >= NS: next chunk)
+    auto prefetch = [&](int kc, int s) {
+        const int kcs = s < NS ? kc : kc + 1, ss = s < NS ? s : s - NS;
+        load_frags(KS * kcs + ss / KX, ss % KX, s % NSET);
+    };
+#pragma unroll
+    for (int s = 0; s < PD; ++s) prefetch(0, s);
     load_region(0, 0);
     store_region(0, 0);
     if (L1 > 0) {
@@ -472,16 +499,17 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         store_region(0, 1);
     }
     __syncthreads();
+    bf16x8_t fb[2][NRU][FB];  // activation fragments of the current and the next step
     for (int kc = 0; kc < nchunks; ++kc) {
         const uint8_t* xb = sX(kc & 1) + (wpos * 32 * FB + px) * XS;
         const int nbuf = (kc + 1) & 1;
+        // a chunk's first step reads its rows after the barrier (the other steps' rows are
+        // read during the step before)
+#pragma unroll
+        for (int rr = 0; rr < NRU; ++rr) read_row(fb[0], xb, 0, rr);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const int s1 = st + 1;
-            if (s1 < NS)
-                load_frags(KS * kc + s1 / KX, s1 % KX, s1 & 1);
-            else
-                load_frags(KS * kc + KS, 0, 0);
+            prefetch(kc, st + PD);
             __builtin_amdgcn_sched_barrier(0);  // weight prefetch before any region load
             if (L1 > 0 && st == L1) store_region(nbuf, 0);
             if (st == 0) load_region(kc + 1, 0);
@@ -489,7 +517,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             // keep the prefetches issued here: left alone the scheduler sinks them towards
             // their use to save registers, which exposes the memory latency
             __builtin_amdgcn_sched_barrier(0);
-            compute(xb, st / KX, st % KX, st & 1);
+            compute(fb[st & 1], fb[(st + 1) & 1], xb, st, st % NSET, st + 1 < NS);
         }
         if (L1 == 0)
             store_region(nbuf, 0);
@@ -790,8 +818,11 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 // channels x 64 pixels each (128 x 64 per workgroup): three weight fragments per step per
 // wave instead of six, which relieves the per-CU vector-memory path that carries them
 // (measured 2-3% faster than 2 x 2 waves of 64 x 32).  Temporal: waves of 32 channels x 64
-// positions as well, 8 of them for up to 256 output channels (all in one workgroup, which
-// the fused projection needs), 4 for up to 128.
+// positions as well, 8 of them for up to 256 output channels (one workgroup per CU), 4 for
+// up to 128.  Temporal with the fused projection (all output channels in one workgroup):
+// 4 waves of 64 channels x 32 positions, so that two workgroups share a CU and their waves
+// are not all tied by one barrier; that measured 3-8% faster than the 8-wave tile there,
+// which in turn is 3% faster without the projection.
 #ifndef CVT_ROWS_SP_WCH
 #define CVT_ROWS_SP_WCH 4
 #endif
@@ -810,6 +841,7 @@ using SpatialCfg = RowsCfg<SPATIAL3, 4, CVT_ROWS_SP_WCH, CVT_ROWS_SP_FA, CVT_ROW
 #endif
 using TemporalCfg = RowsCfg<TEMPORAL3, 4, 8, 1, CVT_ROWS_TM_BK, 8>;
 using TemporalNarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, CVT_ROWS_TM_BK, 4>;
+using TemporalProjCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK, 4>;
 
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
@@ -869,12 +901,9 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
                        int Cp = 0) {
     if constexpr (KIND == SPATIAL3)
         return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
-#ifdef CVT_TM_NARROW_ALL
-    if (cg.Cout <= TemporalNarrowCfg::TCH || !Wpf)
-#else
     if (cg.Cout <= TemporalNarrowCfg::TCH)
-#endif
         return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
+    if (Wpf) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
     return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
 }
 
