@@ -18,7 +18,8 @@ Sources (the web pages describing the Cosmos Tokenizer):
 * "nvidia/Cosmos-Tokenize1-CV8x8x8-720p" (model card), section
   "Model Architecture".
 * "Cosmos World Foundation Model Platform for Physical AI (Cosmos-Predict1)"
-  (paper summary), section "1) Cosmos Tokenizer".
+  (paper summary), section "1) Cosmos Tokenizer" (factorized convolution and
+  factorized causal self-attention).
 * FSQ's bound function follows the published method: Mentzer et al. 2023,
   "Finite Scalar Quantization: VQ-VAE Made Simple" (arXiv:2309.15505).
 
@@ -28,4 +29,4 @@ closed forms, invariants, brute force or library routines.  No function is
 high-pass sign, FSQ epsilon) are documented where they are fixed.
 """
 
-from . import bf16, haar, conv, fsq  # noqa: F401
+from . import bf16, haar, conv, fsq, attention  # noqa: F401
