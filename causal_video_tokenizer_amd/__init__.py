@@ -44,6 +44,7 @@ SIGNATURES = {
     "cvt_causal_conv3d_fact_proj_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact_proj": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                           _ci, _vp, _sz, _vp]),
+    "cvt_attention3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_quantize": (_ci, [_vp, _ci, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_dequantize": (_ci, [_vp, _vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
 }
@@ -59,7 +60,7 @@ class CvtError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m causal_video_tokenizer_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python causal_video_tokenizer_amd/build.py` "
             "(hipcc for gfx950); there is no fallback implementation")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
@@ -261,6 +262,31 @@ def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, work
                                            _ptr(y), B, Cin, Cout, Cp, T, H, W, k, _ptr(workspace), workspace.numel(),
                                            _stream(x.device)), "causal_conv3d_fact_proj")
     return y
+
+
+CVT_ATTN_SPATIAL, CVT_ATTN_TEMPORAL_CAUSAL = 0, 1
+
+
+def attention3d(q, k, v, heads, axis="spatial", out=None):
+    """Factorized self-attention core on bf16 NTHWC tensors [B, C, T, H, W]:
+    softmax(q k^T / sqrt(d)) v per head of d = C / heads consecutive channels,
+    over the H*W positions of each frame (axis="spatial") or, causally, over the
+    T frames of each position (axis="temporal").  Returns out (channels_last_3d)."""
+    _require_gpu(q, k, v)
+    codes = {"spatial": CVT_ATTN_SPATIAL, "temporal": CVT_ATTN_TEMPORAL_CAUSAL}
+    if axis not in codes:
+        raise ValueError('axis must be "spatial" or "temporal"')
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous(memory_format=torch.channels_last_3d):
+            raise ValueError("q, k and v must be bfloat16 channels_last_3d (NTHWC)")
+        if tuple(t.shape) != tuple(q.shape) or t.device != q.device:
+            raise ValueError("q, k and v must have one shape and device")
+    B, C, T, H, W = q.shape
+    o = (_check_out(out, q.shape, torch.bfloat16, q.device, CVT_NTHWC) if out is not None
+         else _empty5(q.shape, torch.bfloat16, q.device, CVT_NTHWC))
+    _check(lib.cvt_attention3d(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, C, T, H, W, heads, codes[axis],
+                               _stream(q.device)), "attention3d")
+    return o
 
 
 def _levels_arg(levels):

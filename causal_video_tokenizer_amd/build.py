@@ -1,6 +1,6 @@
 """Build libcvt.so (the HIP library behind the C ABI) in-tree for gfx950.
 
-    python -m causal_video_tokenizer_amd.build [--jobs N]
+    python causal_video_tokenizer_amd/build.py [--jobs N]
 
 Each source is compiled by hipcc for gfx950 only, then linked into
 ``causal_video_tokenizer_amd/libcvt.so``.  Packed-FP32 instruction selection is
@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcvt.so")
-SOURCES = ["abi.cpp", "haar.hip", "fsq.hip", "conv.hip"]
+SOURCES = ["abi.cpp", "haar.hip", "fsq.hip", "conv.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

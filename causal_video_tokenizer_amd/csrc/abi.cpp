@@ -214,6 +214,29 @@ int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t,
                       "cvt_causal_conv3d_fact_proj launch");
 }
 
+int cvt_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H, int W,
+                    int heads, int axis, void* stream) {
+    if (!q || !k || !v || !out) return fail(CVT_E_NULL, "q, k, v and out must not be NULL");
+    if (axis != CVT_ATTN_SPATIAL && axis != CVT_ATTN_TEMPORAL_CAUSAL)
+        return fail(CVT_E_LAYOUT, "axis must be CVT_ATTN_SPATIAL or CVT_ATTN_TEMPORAL_CAUSAL, got %d", axis);
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0 || heads <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (C % 8 != 0 || C > 4096) return fail(CVT_E_SHAPE, "C must be a multiple of 8 and at most 4096, got %d", C);
+    if (C % heads != 0) return fail(CVT_E_SHAPE, "heads (%d) must divide C (%d)", heads, C);
+    const int d = C / heads;
+    if (axis == CVT_ATTN_SPATIAL && d != 64) return fail(CVT_E_SHAPE, "spatial attention needs head dim 64, got %d", d);
+    if (axis == CVT_ATTN_TEMPORAL_CAUSAL) {
+        if (d != 32 && d != 64) return fail(CVT_E_SHAPE, "temporal attention needs head dim 32 or 64, got %d", d);
+        if ((long long)T * C > cvt::attention_max_tc())
+            return fail(CVT_E_SHAPE, "temporal attention needs T * C <= %d, got %lld", cvt::attention_max_tc(),
+                        (long long)T * C);
+    }
+    if ((long long)H * W * C >= (1LL << 30)) return fail(CVT_E_SHAPE, "a frame of H * W * C must stay below 2^30");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    return hip_status(cvt::launch_attention3d(q, k, v, out, B, C, T, H, W, heads, axis, (hipStream_t)stream),
+                      "cvt_attention3d launch");
+}
+
 int cvt_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* indices, void* codes, const int32_t* levels,
                      int D, int B, int T, int H, int W, void* stream) {
     if (!z || !indices) return fail(CVT_E_NULL, "z and indices must not be NULL");

@@ -1,0 +1,401 @@
+// Factorized causal self-attention over an NTHWC bf16 feature map.
+//
+// The operation is the space-time factorized causal self-attention that
+// "Cosmos World Foundation Model Platform for Physical AI (Cosmos-Predict1)",
+// section "1) Cosmos Tokenizer", pairs with the factorized convolution, and the
+// model card's "Model Architecture" calls causal temporal attention: per head
+// (d = C / heads consecutive channels), softmax(Q K^T / sqrt(d)) V
+//   * SPATIAL: over the H*W positions of one frame, every position attending to
+//     every position of the frame;
+//   * TEMPORAL: over the T frames of one position, causal (frame t sees s <= t).
+// Q, K, V and the output are [B, C, T, H, W] bf16 in NTHWC order; scores,
+// softmax and accumulation are fp32, the probabilities enter the P V product
+// as bf16, the output is rounded to bf16 once.
+//
+// Kernels:
+//   * attn_spatial_kernel - flash attention (d = 64) on bf16 MFMA 32x32x16, in
+//     transposed form: S^T = K Q^T and O^T = V^T P^T, so a lane owns one query
+//     column of every accumulator and the running max / sum of the online
+//     softmax stay in its registers (the two lane halves of a column exchange
+//     once per block).  A lane's 16 S^T values of a 32-key block are keys
+//     8 (r / 4) + 4 (lane / 32) + r % 4; bf16-rounded, the values r = 8h .. 8h+7
+//     are directly the B operand of a 16-key k-step whose key order is that
+//     permutation, and V^T is staged in LDS with its keys in the same order, so
+//     P never leaves the registers.
+//   * attn_temporal_kernel - causal attention (d = 32 or 64, T * C <= 16384): K and
+//     V of a few consecutive positions staged in LDS (one contiguous run per frame),
+//     one thread per (position, head, query frame) in fp32.  The work is a few
+//     FLOPs per byte: it is bound by HBM, not by the matrix cores.
+#include "cvt_internal.h"
+
+namespace cvt {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------------------
+// Spatial attention.  Workgroup = 4 waves x 64 queries (two 32-query MFMA column blocks
+// per wave) of one (clip, frame, head) sequence; the keys go by in blocks of 64, staged
+// in LDS (K rows [key][64 channels], V^T rows [channel][64 keys], 16-byte padded rows,
+// two buffers), loaded during the previous block.  Per block and wave: 16 MFMAs for
+// S^T (2 key blocks x 2 query blocks x 4 channel k-steps) and 16 for O^T (2 channel
+// blocks x 2 query blocks x 4 key k-steps).
+constexpr int AD = 64;               // head dim of the spatial kernel
+constexpr int AQW = 64;              // queries per wave
+constexpr int AQT = 4 * AQW;         // queries per workgroup
+constexpr int AKB = 64;              // keys per block
+constexpr int AKRS = AD * 2 + 16;    // bytes per K row in LDS
+constexpr int AVRS = AKB * 2 + 16;   // bytes per V^T row in LDS
+constexpr int AKBUF = AKB * AKRS;
+constexpr int AVBUF = AD * AVRS;
+
+struct AttnGeom {
+    int N;          // tokens per sequence (H * W)
+    int C;          // channels per token
+    int G;          // heads
+    int nqt;        // query tiles per sequence
+    int ntiles, per_xcd;
+    int ext;        // bytes from a sequence's first element to its last (buffer extent)
+    float scale2;   // log2(e) / sqrt(d)
+};
+
+// Position of key k within its 16-key group in a V^T row: lane half h's keys of a k-step,
+// {4h .. 4h+3, 8+4h .. 8+4h+3}, become the contiguous 8 at 8h (bits 2 and 3 swapped).
+__device__ __forceinline__ int vperm(int k) {
+    return (k & ~15) | (k & 3) | (((k >> 3) & 1) << 2) | (((k >> 2) & 1) << 3);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_spatial_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, AttnGeom g) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (AKBUF + AVBUF)];
+    // XCD-aware order: consecutive tiles (the query tiles of one sequence, which read the
+    // same keys) run on one XCD's L2
+    const int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
+    if (tile >= g.ntiles) return;
+    const int qt = tile % g.nqt, seq = tile / g.nqt;
+    const int head = seq % g.G;
+    const long long base = (long long)(seq / g.G) * g.N * g.C + head * AD;  // element offset of token 0
+    const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int px = lane & 31, hh = lane >> 5;
+    const int rowb = g.C * 2;  // bytes between consecutive tokens
+
+    // Q^T B operand: lane (query px of block qb, half hh) holds channels 16 ks + 8 hh .. +7.
+    // Queries past N read zeros (past the buffer) and are never stored.
+    bf16x8_t qf[2][AD / 16];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qt * AQT + wave * AQW + qb * 32 + px;
+        const int off = qi < g.N ? qi * rowb : 0x7fffff00;
+#pragma unroll
+        for (int ks = 0; ks < AD / 16; ++ks)
+            qf[qb][ks] = __builtin_bit_cast(bf16x8_t,
+                                            __builtin_amdgcn_raw_buffer_load_b128(qres, off + (ks * 16 + hh * 8) * 2, 0, 0));
+    }
+
+    // Staging of a key block: thread -> key j = tid / 8 (+ 32), 16-byte chunk c8 = tid % 8
+    // for K; pair of keys 2 p, 2 p + 1 (p = tid / 8) at chunk c8 for V.  Keys past N are
+    // staged as zeros (and masked from the scores).
+    const int c8 = tid & 7, jr = tid >> 3;
+    uint4 kst[2], vst[2];
+    auto load_block = [&](int blk) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int j = blk * AKB + jr + 32 * r;
+            const auto kv = __builtin_amdgcn_raw_buffer_load_b128(kres, j < g.N ? j * rowb + c8 * 16 : 0x7fffff00, 0, 0);
+            kst[r] = *reinterpret_cast<const uint4*>(&kv);
+            const int jv = blk * AKB + 2 * jr + r;
+            const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, jv < g.N ? jv * rowb + c8 * 16 : 0x7fffff00, 0, 0);
+            vst[r] = *reinterpret_cast<const uint4*>(&vv);
+        }
+    };
+    auto store_block = [&](int buf) {
+        uint8_t* sk = smem + buf * (AKBUF + AVBUF);
+        uint8_t* sv = sk + AKBUF;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(sk + (jr + 32 * r) * AKRS + c8 * 16) = kst[r];
+        // V^T: channel c8 * 8 + e gets the pair (key 2 jr, key 2 jr + 1) at its permuted column
+        const uint32_t a[4] = {vst[0].x, vst[0].y, vst[0].z, vst[0].w};
+        const uint32_t b[4] = {vst[1].x, vst[1].y, vst[1].z, vst[1].w};
+        const int col = vperm(2 * jr) * 2;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            // channels 2 e2 and 2 e2 + 1 of the chunk: low halves, then high halves
+            *reinterpret_cast<uint32_t*>(sv + (c8 * 8 + 2 * e2) * AVRS + col) = (a[e2] & 0xffffu) | (b[e2] << 16);
+            *reinterpret_cast<uint32_t*>(sv + (c8 * 8 + 2 * e2 + 1) * AVRS + col) = (a[e2] >> 16) | (b[e2] & 0xffff0000u);
+        }
+    };
+
+    f32x16_t o[2][2];  // O^T: [channel block][query block]
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[cb][qb][e] = 0.0f;
+    float m[2] = {-INFINITY, -INFINITY};  // running max (log2 domain) of the lane's query
+    float lp[2] = {0.0f, 0.0f};           // running sum over the lane's own keys
+
+    const int nblk = (g.N + AKB - 1) / AKB;
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const uint8_t* sk = smem + (blk & 1) * (AKBUF + AVBUF);
+        const uint8_t* sv = sk + AKBUF;
+        if (blk + 1 < nblk) load_block(blk + 1);
+
+        // S^T = K Q^T: rows = 64 keys (2 blocks), columns = the wave's 64 queries
+        f32x16_t s[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < AD / 16; ++ks) {
+                const bf16x8_t kf =
+                    *reinterpret_cast<const bf16x8_t*>(sk + (kb * 32 + px) * AKRS + (ks * 16 + hh * 8) * 2);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+            }
+        }
+        // keys past N (last block only): -inf
+        if ((blk + 1) * AKB > g.N) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = blk * AKB + kb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+                    if (j >= g.N) {
+                        s[kb][0][r] = -INFINITY;
+                        s[kb][1][r] = -INFINITY;
+                    }
+                }
+        }
+
+        // online softmax per query column; P (bf16) straight into the P V MFMAs
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = s[0][qb][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m[qb], mx * g.scale2);
+            const float alpha = exp2f(m[qb] - mnew);
+            m[qb] = mnew;
+            float sum = 0.0f;
+            bf16x8_t pf[2][2];  // [key block][half of the block]
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = exp2f(fmaf(s[kb][qb][8 * h2 + e], g.scale2, -mnew));
+                        sum += p[e];
+                    }
+                    uint4 u;
+                    u.x = pack_bf16x2(p[0], p[1]);
+                    u.y = pack_bf16x2(p[2], p[3]);
+                    u.z = pack_bf16x2(p[4], p[5]);
+                    u.w = pack_bf16x2(p[6], p[7]);
+                    pf[kb][h2] = __builtin_bit_cast(bf16x8_t, u);
+                }
+            lp[qb] = lp[qb] * alpha + sum;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[cb][qb][e] *= alpha;
+            // O^T += V^T P^T: A = V^T rows (32 channels) x the k-step's 16 keys in lane order
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
+                            sv + (cb * 32 + px) * AVRS + (kb * 32 + h2 * 16 + hh * 8) * 2);
+                        o[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][h2], o[cb][qb], 0, 0, 0);
+                    }
+        }
+        if (blk + 1 < nblk) store_block((blk + 1) & 1);
+        __syncthreads();
+    }
+
+    // normalise and store: element r of O^T block (cb, qb) is channel 32 cb + 8 (r / 4) +
+    // 4 hh + r % 4 of the lane's query; four consecutive channels per 8-byte store
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float l = lp[qb] + __shfl_xor(lp[qb], 32);
+        const float inv = 1.0f / l;
+        const int qi = qt * AQT + wave * AQW + qb * 32 + px;
+        if (qi < g.N) {
+            uint16_t* orow = O + base + (long long)qi * g.C;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    uint2 u;
+                    u.x = pack_bf16x2(o[cb][qb][4 * q4] * inv, o[cb][qb][4 * q4 + 1] * inv);
+                    u.y = pack_bf16x2(o[cb][qb][4 * q4 + 2] * inv, o[cb][qb][4 * q4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(orow + cb * 32 + q4 * 8 + hh * 4) = u;
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Temporal causal attention.  Workgroup = NP consecutive positions of one clip, all heads,
+// all T frames: K and V are staged in LDS as [frame][position][channel] (for each frame the
+// NP positions are one contiguous run of NP * C * 2 bytes), then thread -> (position, head,
+// query frame t), t fastest, so the threads of one (position, head) read the same key row
+// together.  Each computes its query's online softmax over frames 0..t in fp32 and writes
+// its d output channels.
+constexpr int TLDS = 65536;  // bytes of LDS for K and V
+
+struct TAttnGeom {
+    int B, T, HW, C, G;
+    int np;        // positions per workgroup
+    int ntp;       // position tiles per clip
+    float scale2;  // log2(e) / sqrt(d)
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __restrict__ Q,
+                                                            const uint16_t* __restrict__ K,
+                                                            const uint16_t* __restrict__ V,
+                                                            uint16_t* __restrict__ O, TAttnGeom g) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[TLDS];
+    const int b = blockIdx.x / g.ntp, p0 = (blockIdx.x % g.ntp) * g.np;
+    const int np = min(g.np, g.HW - p0);  // positions in this tile
+    const int run = np * g.C;             // elements per frame run
+    uint16_t* sk = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* sv = sk + g.T * g.np * g.C;
+    const size_t fstride = (size_t)g.HW * g.C;  // elements between frames
+    const size_t tbase = ((size_t)b * g.T * g.HW + p0) * g.C;
+    // stage K and V: 16-byte chunks, frame-major
+    const int cpr = run / 8;  // chunks per frame run
+    for (int q = threadIdx.x; q < g.T * cpr; q += 256) {
+        const int t = q / cpr, c = q - t * cpr;
+        const size_t src = tbase + t * fstride + (size_t)c * 8;
+        *reinterpret_cast<uint4*>(sk + t * run + c * 8) = ld_stream16(K + src);
+        *reinterpret_cast<uint4*>(sv + t * run + c * 8) = ld_stream16(V + src);
+    }
+    __syncthreads();
+
+    const int items = np * g.G * g.T;
+    for (int it = threadIdx.x; it < items; it += 256) {
+        const int t = it % g.T, rest = it / g.T;
+        const int hd = rest % g.G, pl = rest / g.G;
+        const size_t tok = tbase + t * fstride + (size_t)pl * g.C + hd * D;
+        float q[D];
+#pragma unroll
+        for (int c = 0; c < D; c += 8) {
+            const uint4 u = ld_stream16(Q + tok + c);
+            q[c] = bf16_lo(u.x); q[c + 1] = bf16_hi(u.x); q[c + 2] = bf16_lo(u.y); q[c + 3] = bf16_hi(u.y);
+            q[c + 4] = bf16_lo(u.z); q[c + 5] = bf16_hi(u.z); q[c + 6] = bf16_lo(u.w); q[c + 7] = bf16_hi(u.w);
+        }
+        float o[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] = 0.0f;
+        float m = -INFINITY, l = 0.0f;
+        const int koff = pl * g.C + hd * D;
+        for (int j = 0; j <= t; ++j) {
+            const uint16_t* kr = sk + j * run + koff;
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D; c += 8) {
+                const uint4 u = *reinterpret_cast<const uint4*>(kr + c);
+                s = fmaf(q[c], bf16_lo(u.x), s); s = fmaf(q[c + 1], bf16_hi(u.x), s);
+                s = fmaf(q[c + 2], bf16_lo(u.y), s); s = fmaf(q[c + 3], bf16_hi(u.y), s);
+                s = fmaf(q[c + 4], bf16_lo(u.z), s); s = fmaf(q[c + 5], bf16_hi(u.z), s);
+                s = fmaf(q[c + 6], bf16_lo(u.w), s); s = fmaf(q[c + 7], bf16_hi(u.w), s);
+            }
+            s *= g.scale2;
+            const float mn = fmaxf(m, s);
+            const float alpha = exp2f(m - mn), p = exp2f(s - mn);
+            m = mn;
+            l = fmaf(l, alpha, p);
+            const uint16_t* vr = sv + j * run + koff;
+#pragma unroll
+            for (int c = 0; c < D; c += 8) {
+                const uint4 u = *reinterpret_cast<const uint4*>(vr + c);
+                o[c] = fmaf(o[c], alpha, p * bf16_lo(u.x)); o[c + 1] = fmaf(o[c + 1], alpha, p * bf16_hi(u.x));
+                o[c + 2] = fmaf(o[c + 2], alpha, p * bf16_lo(u.y)); o[c + 3] = fmaf(o[c + 3], alpha, p * bf16_hi(u.y));
+                o[c + 4] = fmaf(o[c + 4], alpha, p * bf16_lo(u.z)); o[c + 5] = fmaf(o[c + 5], alpha, p * bf16_hi(u.z));
+                o[c + 6] = fmaf(o[c + 6], alpha, p * bf16_lo(u.w)); o[c + 7] = fmaf(o[c + 7], alpha, p * bf16_hi(u.w));
+            }
+        }
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int c = 0; c < D; c += 8) {
+            uint4 u;
+            u.x = pack_bf16x2(o[c] * inv, o[c + 1] * inv);
+            u.y = pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv);
+            u.z = pack_bf16x2(o[c + 4] * inv, o[c + 5] * inv);
+            u.w = pack_bf16x2(o[c + 6] * inv, o[c + 7] * inv);
+            st_stream16(O + tok + c, u);
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_temporal(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int B, int C, int T,
+                           int HW, int G, hipStream_t s) {
+    TAttnGeom g{};
+    g.B = B; g.T = T; g.HW = HW; g.C = C; g.G = G;
+    g.np = TLDS / (2 * T * C * 2);  // the launcher guarantees T * C * 4 <= TLDS
+    if (g.np > HW) g.np = HW;
+    g.ntp = (HW + g.np - 1) / g.np;
+    g.scale2 = 1.4426950408889634f / sqrtf((float)D);
+    const long long nblk = (long long)B * g.ntp;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_temporal_kernel<D>), dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, o, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int attention_max_tc() { return TLDS / 4; }
+
+hipError_t launch_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H,
+                              int W, int heads, int axis, hipStream_t s) {
+    const uint16_t* Q = static_cast<const uint16_t*>(q);
+    const uint16_t* K = static_cast<const uint16_t*>(k);
+    const uint16_t* V = static_cast<const uint16_t*>(v);
+    uint16_t* O = static_cast<uint16_t*>(out);
+    const int d = C / heads, HW = H * W;
+    if (axis == CVT_ATTN_SPATIAL) {
+        if (d != AD) return hipErrorInvalidValue;
+        AttnGeom g{};
+        g.N = HW; g.C = C; g.G = heads;
+        g.nqt = (HW + AQT - 1) / AQT;
+        const long long ntiles = (long long)B * T * heads * g.nqt;
+        if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
+        g.ntiles = (int)ntiles;
+        g.per_xcd = (int)((ntiles + 7) / 8);
+        g.ext = ((HW - 1) * C + AD) * 2;
+        g.scale2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+        hipLaunchKernelGGL(attn_spatial_kernel, dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, Q, K, V, O, g);
+        return hipGetLastError();
+    }
+    if (T * C > attention_max_tc()) return hipErrorInvalidValue;
+    switch (d) {
+        case 32: return launch_temporal<32>(Q, K, V, O, B, C, T, HW, heads, s);
+        case 64: return launch_temporal<64>(Q, K, V, O, B, C, T, HW, heads, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace cvt

@@ -94,4 +94,10 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
                                  const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp, int T,
                                  int H, int W, int k, void* workspace, hipStream_t s);
 
+// Factorized self-attention (attention.hip).  Spatial: head dim 64; temporal causal:
+// head dim 32 or 64 and T * C <= attention_max_tc().
+int attention_max_tc();
+hipError_t launch_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H,
+                              int W, int heads, int axis, hipStream_t stream);
+
 }  // namespace cvt

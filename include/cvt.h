@@ -174,6 +174,38 @@ int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t,
                                 int T, int H, int W, int k, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Factorized causal self-attention core, one axis per call:
+ *   out = softmax(q k^T / sqrt(d) [+ causal mask]) v   per head,
+ * with the C channels split into `heads` heads of d = C / heads consecutive
+ * channels (head g = channels g*d .. g*d + d - 1).
+ *   axis = CVT_ATTN_SPATIAL: the tokens are the H*W positions of one frame of
+ *          one clip, every position attending to every position of the frame.
+ *   axis = CVT_ATTN_TEMPORAL_CAUSAL: the tokens are the T frames of one position
+ *          of one clip; frame t attends to frames s <= t only.
+ *
+ * Defined by: "Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer" (space-time
+ * factorized causal self-attention next to the factorized convolution) and the
+ * model card's "Model Architecture" (causal temporal attention keeps the frame
+ * order).  The pages give no formula, head count or width: scaled dot-product
+ * attention with consecutive-channel heads is the reading taken.
+ *
+ * q, k, v: bf16 NTHWC (torch channels_last_3d) [B, C, T, H, W], produced by the
+ *      caller (e.g. 1x1x1 convolutions of a feature map).
+ * out: bf16 NTHWC [B, C, T, H, W]; must not overlap q, k or v.
+ * Scores, softmax and accumulation are float32; the probabilities are rounded
+ * to bf16 for the P v product; out is rounded to bf16 once.
+ * Errors: CVT_E_NULL for a NULL tensor; CVT_E_ALIGN unless all four are
+ * 16-byte aligned; CVT_E_LAYOUT for an unknown axis; CVT_E_SHAPE for a
+ * non-positive size, heads not dividing C, C not a multiple of 8 or above
+ * 4096, a head dim other than 64 (spatial) or 32 / 64 (temporal), or, for the
+ * temporal axis, T * C above 16384 (K and V of one position must fit in LDS).
+ */
+enum { CVT_ATTN_SPATIAL = 0, CVT_ATTN_TEMPORAL_CAUSAL = 1 };
+int cvt_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H, int W,
+                    int heads, int axis, void* stream);
+
+/*
  * FSQ quantization: per position, D latent values -> one int32 index.
  *
  * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (each channel

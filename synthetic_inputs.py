@@ -130,4 +130,7 @@ WORKLOADS = {
         convs=[(6, 192, 1), (192, 192, 3)], out_x=(8, 3, 49, 360, 640)),
     # FSQ at a bandwidth-meaningful size: 64 latents of the 49-frame 720p grid
     "fsq_bw": dict(latent=(64, 6, 13, 180, 320), latent_seed=1015, latent_std=1.5),
+    # factorized attention on the CV8x8x8-720p token grid of a 121-frame clip (16 x 90 x 160),
+    # 256 channels in 4 heads of 64; q, k, v ~ N(0, 1), seeds seed, seed + 1, seed + 2
+    "attn_cv8x8x8_720p_tokens": dict(x=(1, 256, 16, 90, 160), heads=4, seed=1006, std=1.0),
 }

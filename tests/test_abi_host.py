@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -164,3 +164,24 @@ def test_binding_rejects_mismatched_outputs():
         cvt._check_out(good, shape, torch.float32, good.device, cvt.CVT_NTHWC)
     with pytest.raises(ValueError, match="shape"):
         cvt._check_out(good, (1, 6, 3, 4, 4), torch.bfloat16, good.device, cvt.CVT_NTHWC)
+
+
+def test_attention_validation():
+    """cvt_attention3d rejects bad arguments before any launch."""
+    def call(**kw):
+        return lib.cvt_attention3d(kw.get("q", A), kw.get("k", B_), kw.get("v", C_), kw.get("o", ctypes.c_void_p(0x400000)),
+                                   kw.get("B", 1), kw.get("C", 256), kw.get("T", 16), kw.get("H", 9), kw.get("W", 10),
+                                   kw.get("heads", 4), kw.get("axis", 0), None)
+    assert call(q=None) == E_NULL
+    assert call(o=None) == E_NULL
+    assert call(axis=2) == E_LAYOUT
+    assert call(heads=3) == E_SHAPE           # does not divide 256
+    assert call(heads=2) == E_SHAPE           # spatial head dim 128
+    assert call(heads=2, axis=1) == E_SHAPE   # temporal head dim 128
+    assert call(C=260, heads=4) == E_SHAPE    # C not a multiple of 8
+    assert call(T=65, axis=1) == E_SHAPE      # T * C above 16384
+    assert call(H=0) == E_SHAPE
+    assert call(q=MIS) == E_ALIGN
+    assert call(o=ctypes.c_void_p(0x400008)) == E_ALIGN
+    assert b"head dim" in (call(heads=2) and lib.cvt_last_error())
+
