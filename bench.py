@@ -20,7 +20,9 @@ the float64 oracle timed on a bounded sample of the same workload (a strip of
 the frame), scaled to the full clip.  A second object reports the 121-frame
 CV8x8x8-720p-shaped chain (two factorized conv layers and the 1x1), where the
 convolution's MFMA fraction is quoted; a third, FSQ quantize and dequantize at a
-bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak.
+bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak; a fourth,
+the factorized self-attention (spatial and causal temporal) on the 16 x 90 x 160 token
+grid of the CV8x8x8-720p model, 256 channels in 4 heads.
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -63,6 +65,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-c3", action="store_true", help="skip the 121-frame chain measurement")
     ap.add_argument("--no-fsq-bw", action="store_true", help="skip the FSQ bandwidth-size measurement")
+    ap.add_argument("--no-attention", action="store_true", help="skip the factorized-attention measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -187,6 +190,7 @@ def main():
 
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
     fsq_bw = None if args.no_fsq_bw else fsq_bandwidth(cvt, si, torch, dev, args)
+    attn = None if args.no_attention else attention_tokens(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -223,6 +227,7 @@ def main():
         "stages": per_stage,
         "cv8x8x8_720p_121f": c3,
         "fsq_bandwidth_size": fsq_bw,
+        "attention_cv8x8x8_720p_tokens": attn,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -353,6 +358,57 @@ def fsq_bandwidth(cvt, si, torch, dev, args):
         gbps = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     del z, zc, idx, codes, codes_c
+    torch.cuda.empty_cache()
+    return out
+
+
+def attention_tokens(cvt, si, torch, dev, args):
+    """Factorized self-attention on the CV8x8x8-720p token grid of a 121-frame clip
+    (1 x 256 x 16 x 90 x 160, 4 heads of 64): spatial attention over each frame's 14,400
+    positions (4 N^2 d FLOP per frame and head, MFMA) and causal temporal attention over
+    each position's 16 frames (q, k, v read and the output written once: HBM).  Timed
+    over back-to-back calls with HIP events."""
+    wl = si.WORKLOADS["attn_cv8x8x8_720p_tokens"]
+    shape, heads = wl["x"], wl["heads"]
+    B, C, T, H, W = shape
+    N, d = H * W, C // heads
+    log(f"attention: generating q, k, v {shape} ...")
+
+    def dev_bits(seed):
+        bits = si.to_bf16_bits(si.normal(shape, seed, wl["std"]))
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return t.to(memory_format=torch.channels_last_3d)
+
+    q, k, v = (dev_bits(wl["seed"] + i) for i in range(3))
+    o = torch.empty_like(q)
+    calls = {"spatial": lambda: cvt.attention3d(q, k, v, heads, "spatial", out=o),
+             "temporal_causal": lambda: cvt.attention3d(q, k, v, heads, "temporal", out=o)}
+    for _ in range(max(3, min(args.warmup, 10))):
+        for fn in calls.values():
+            fn()
+    torch.cuda.synchronize()
+    out = {"shape": list(shape), "heads": heads}
+    for name, fn in calls.items():
+        reps = max(5, args.steps // 2) if name == "spatial" else max(10, args.steps)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        if name == "spatial":
+            flops = 4.0 * N * N * d * heads * B * T
+            tf = flops / (ms * 1e-3) / 1e12
+            out[name] = {"ms": round(ms, 4), "flops": flops, "TFLOPs": round(tf, 1),
+                         "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        else:
+            nbytes = 4.0 * q.numel() * 2
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            out[name] = {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(gbps, 1),
+                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del q, k, v, o
     torch.cuda.empty_cache()
     return out
 

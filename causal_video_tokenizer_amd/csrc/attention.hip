@@ -26,6 +26,8 @@
 //     V of a few consecutive positions staged in LDS (one contiguous run per frame),
 //     one thread per (position, head, query frame) in fp32.  The work is a few
 //     FLOPs per byte: it is bound by HBM, not by the matrix cores.
+#include <type_traits>
+
 #include "cvt_internal.h"
 
 namespace cvt {
@@ -59,6 +61,11 @@ struct AttnGeom {
     int ext;        // bytes from a sequence's first element to its last (buffer extent)
     float scale2;   // log2(e) / sqrt(d)
 };
+
+// 2^x by the hardware's v_exp_f32 alone.  exp2f adds a denormal-range rescaling (compares,
+// selects and an ldexp around every exponential) that a softmax does not need: a weight
+// below 2^-126 next to the row maximum's weight of 1 is zero either way.  2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Position of key k within its 16-key group in a V^T row: lane half h's keys of a k-step,
 // {4h .. 4h+3, 8+4h .. 8+4h+3}, become the contiguous 8 at 8h (bits 2 and 3 swapped).
@@ -142,12 +149,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     float lp[2] = {0.0f, 0.0f};           // running sum over the lane's own keys
 
     const int nblk = (g.N + AKB - 1) / AKB;
-    load_block(0);
-    store_block(0);
-    __syncthreads();
-    for (int blk = 0; blk < nblk; ++blk) {
-        const uint8_t* sk = smem + (blk & 1) * (AKBUF + AVBUF);
-        const uint8_t* sv = sk + AKBUF;
+    // per-lane byte offsets of the K and V^T fragments within a buffer; every fragment is
+    // this plus a compile-time offset
+    const int klane = px * AKRS + hh * 16, vlane = AKBUF + px * AVRS + hh * 16;
+
+    // One key block.  MASKED (the last block when N is not a multiple of 64): keys past N
+    // get a score of -inf.  A compile-time flag, so that the full blocks carry no mask code.
+    auto block = [&](int blk, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const uint8_t* kbase = smem + (blk & 1) * (AKBUF + AVBUF) + klane;
+        const uint8_t* vbase = smem + (blk & 1) * (AKBUF + AVBUF) + vlane;
         if (blk + 1 < nblk) load_block(blk + 1);
 
         // S^T = K Q^T: rows = 64 keys (2 blocks), columns = the wave's 64 queries
@@ -160,15 +171,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < AD / 16; ++ks) {
-                const bf16x8_t kf =
-                    *reinterpret_cast<const bf16x8_t*>(sk + (kb * 32 + px) * AKRS + (ks * 16 + hh * 8) * 2);
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kbase + kb * 32 * AKRS + ks * 32);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
                     s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
             }
         }
-        // keys past N (last block only): -inf
-        if ((blk + 1) * AKB > g.N) {
+        if constexpr (MASKED) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -191,32 +200,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mnew = fmaxf(m[qb], mx * g.scale2);
-            const float alpha = exp2f(m[qb] - mnew);
+            const float alpha = fast_exp2(m[qb] - mnew);
             m[qb] = mnew;
+            // the row sum adds the bf16-rounded weights that enter the P V product (two per
+            // v_dot2_f32_bf16), so numerator and denominator use the same weights
             float sum = 0.0f;
             bf16x8_t pf[2][2];  // [key block][half of the block]
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     float p[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        p[e] = exp2f(fmaf(s[kb][qb][8 * h2 + e], g.scale2, -mnew));
-                        sum += p[e];
+                    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[kb][qb][8 * h2 + e], g.scale2, -mnew));
+                    uint32_t u[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        u[e2] = pack_bf16x2(p[2 * e2], p[2 * e2 + 1]);
+                        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e2]), ones, sum, false);
                     }
-                    uint4 u;
-                    u.x = pack_bf16x2(p[0], p[1]);
-                    u.y = pack_bf16x2(p[2], p[3]);
-                    u.z = pack_bf16x2(p[4], p[5]);
-                    u.w = pack_bf16x2(p[6], p[7]);
-                    pf[kb][h2] = __builtin_bit_cast(bf16x8_t, u);
+                    pf[kb][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
                 }
             lp[qb] = lp[qb] * alpha + sum;
+            // rescale the accumulators only when some lane's running maximum moved (alpha < 1);
+            // once the maximum has settled, most blocks skip it
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
+                for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) o[cb][qb][e] *= alpha;
+                    for (int e = 0; e < 16; ++e) o[cb][qb][e] *= alpha;
+            }
             // O^T += V^T P^T: A = V^T rows (32 channels) x the k-step's 16 keys in lane order
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -224,14 +238,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                     for (int cb = 0; cb < 2; ++cb) {
-                        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-                            sv + (cb * 32 + px) * AVRS + (kb * 32 + h2 * 16 + hh * 8) * 2);
+                        const bf16x8_t vf =
+                            *reinterpret_cast<const bf16x8_t*>(vbase + cb * 32 * AVRS + (kb * 32 + h2 * 16) * 2);
                         o[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][h2], o[cb][qb], 0, 0, 0);
                     }
         }
         if (blk + 1 < nblk) store_block((blk + 1) & 1);
         __syncthreads();
-    }
+    };
+
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+    const int nfull = g.N / AKB;  // blocks without keys past N
+    for (int blk = 0; blk < nfull; ++blk) block(blk, std::false_type{});
+    if (nfull < nblk) block(nfull, std::true_type{});
 
     // normalise and store: element r of O^T block (cb, qb) is channel 32 cb + 8 (r / 4) +
     // 4 hh + r % 4 of the lane's query; four consecutive channels per 8-byte store
@@ -284,13 +305,29 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
     uint16_t* sv = sk + g.T * g.np * g.C;
     const size_t fstride = (size_t)g.HW * g.C;  // elements between frames
     const size_t tbase = ((size_t)b * g.T * g.HW + p0) * g.C;
-    // stage K and V: 16-byte chunks, frame-major
+    // stage K and V: 16-byte chunks, frame-major, eight chunks of each per thread in
+    // flight before any is stored
     const int cpr = run / 8;  // chunks per frame run
-    for (int q = threadIdx.x; q < g.T * cpr; q += 256) {
-        const int t = q / cpr, c = q - t * cpr;
-        const size_t src = tbase + t * fstride + (size_t)c * 8;
-        *reinterpret_cast<uint4*>(sk + t * run + c * 8) = ld_stream16(K + src);
-        *reinterpret_cast<uint4*>(sv + t * run + c * 8) = ld_stream16(V + src);
+    const int nch = g.T * cpr;
+    for (int q0 = 0; q0 < nch; q0 += 8 * 256) {
+        uint4 kr[8], vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = min(q0 + i * 256 + (int)threadIdx.x, nch - 1);  // clamped: re-reads a valid chunk
+            const int t = q / cpr, c = q - t * cpr;
+            const size_t src = tbase + t * fstride + (size_t)c * 8;
+            kr[i] = ld_stream16(K + src);
+            vr[i] = ld_stream16(V + src);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = q0 + i * 256 + (int)threadIdx.x;
+            if (q < nch) {
+                const int t = q / cpr, c = q - t * cpr;
+                *reinterpret_cast<uint4*>(sk + t * run + c * 8) = kr[i];
+                *reinterpret_cast<uint4*>(sv + t * run + c * 8) = vr[i];
+            }
+        }
     }
     __syncthreads();
 
@@ -324,7 +361,7 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
             }
             s *= g.scale2;
             const float mn = fmaxf(m, s);
-            const float alpha = exp2f(m - mn), p = exp2f(s - mn);
+            const float alpha = fast_exp2(m - mn), p = fast_exp2(s - mn);
             m = mn;
             l = fmaf(l, alpha, p);
             const uint16_t* vr = sv + j * run + koff;
