@@ -22,10 +22,12 @@
 //     are directly the B operand of a 16-key k-step whose key order is that
 //     permutation, and V^T is staged in LDS with its keys in the same order, so
 //     P never leaves the registers.
-//   * attn_temporal_kernel - causal attention (d = 32 or 64, T * C <= 16384): K and
-//     V of a few consecutive positions staged in LDS (one contiguous run per frame),
-//     one thread per (position, head, query frame) in fp32.  The work is a few
-//     FLOPs per byte: it is bound by HBM, not by the matrix cores.
+//   * attn_temporal_mfma_kernel - causal attention with d = 64 and T <= 32: one wave
+//     per (position, head) sequence, the T x T scores in one MFMA block; a few FLOPs
+//     per byte, so it is bound by HBM, not by the matrix cores;
+//   * attn_temporal_kernel - the other temporal cases (d = 32, or 32 < T, T * C <=
+//     16384): K and V of a few consecutive positions staged in LDS (one contiguous run
+//     per frame), one thread per (position, head, query frame) in fp32.
 #include <type_traits>
 
 #include "cvt_internal.h"
@@ -278,12 +280,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ---------------------------------------------------------------------------------------
 // Temporal causal attention.  Workgroup = NP consecutive positions of one clip, all heads,
-// all T frames: K and V are staged in LDS as [frame][position][channel] (for each frame the
-// NP positions are one contiguous run of NP * C * 2 bytes), then thread -> (position, head,
-// query frame t), t fastest, so the threads of one (position, head) read the same key row
-// together.  Each computes its query's online softmax over frames 0..t in fp32 and writes
-// its d output channels.
-constexpr int TLDS = 65536;  // bytes of LDS for K and V
+// all T frames: K and V are read as one contiguous run of NP * C * 2 bytes per frame and
+// staged in LDS (layout below), then thread -> (position, head, query frame t).  Each
+// computes its query's softmax over frames 0..t in two passes (the
+// maximum, then the weights and the weighted sum; the scores are bf16 dot products on the
+// packed inputs, v_dot2_f32_bf16 with fp32 accumulation; weights and sums in fp32) and
+// writes its d output channels.
+// K and V rows in LDS: [frame][position][head][D + 8] (a head row padded by 16 bytes, so
+// the rows of 16 consecutive (position, head) pairs start on 16 distinct 4-bank groups and
+// a wave's reads of one key frame are conflict-free).  80 KB: two workgroups per CU.
+constexpr int TLDS = 81920;
 
 struct TAttnGeom {
     int B, T, HW, C, G;
@@ -300,14 +306,17 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
     __shared__ __attribute__((aligned(16))) uint8_t smem[TLDS];
     const int b = blockIdx.x / g.ntp, p0 = (blockIdx.x % g.ntp) * g.np;
     const int np = min(g.np, g.HW - p0);  // positions in this tile
-    const int run = np * g.C;             // elements per frame run
+    constexpr int DP = D + 8;             // padded head row (elements)
+    const int prow = g.G * DP;            // elements per (frame, position) in LDS
+    const int frow = np * prow;           // elements per frame in LDS
     uint16_t* sk = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* sv = sk + g.T * g.np * g.C;
-    const size_t fstride = (size_t)g.HW * g.C;  // elements between frames
+    uint16_t* sv = sk + g.T * g.np * prow;
+    const size_t fstride = (size_t)g.HW * g.C;  // elements between frames in memory
     const size_t tbase = ((size_t)b * g.T * g.HW + p0) * g.C;
-    // stage K and V: 16-byte chunks, frame-major, eight chunks of each per thread in
-    // flight before any is stored
-    const int cpr = run / 8;  // chunks per frame run
+    // stage K and V: 16-byte chunks of each frame's contiguous run of np * C elements,
+    // eight chunks of each tensor per thread in flight before any is stored
+    const int cpp = g.C / 8;   // chunks per position
+    const int cpr = np * cpp;  // chunks per frame run
     const int nch = g.T * cpr;
     for (int q0 = 0; q0 < nch; q0 += 8 * 256) {
         uint4 kr[8], vr[8];
@@ -324,54 +333,64 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
             const int q = q0 + i * 256 + (int)threadIdx.x;
             if (q < nch) {
                 const int t = q / cpr, c = q - t * cpr;
-                *reinterpret_cast<uint4*>(sk + t * run + c * 8) = kr[i];
-                *reinterpret_cast<uint4*>(sv + t * run + c * 8) = vr[i];
+                const int pl = c / cpp, ch = (c - pl * cpp) * 8;  // position, first channel
+                const int dst = t * frow + pl * prow + (ch / D) * DP + ch % D;
+                *reinterpret_cast<uint4*>(sk + dst) = kr[i];
+                *reinterpret_cast<uint4*>(sv + dst) = vr[i];
             }
         }
     }
     __syncthreads();
 
-    const int items = np * g.G * g.T;
+    // thread -> (query frame t, head, position), t slowest: the lanes of a wave share t or
+    // neighbouring t, so their causal loops (frames 0..t) have nearly equal lengths
+    const int items = np * g.G * g.T, npg = np * g.G;
     for (int it = threadIdx.x; it < items; it += 256) {
-        const int t = it % g.T, rest = it / g.T;
+        const int t = it / npg, rest = it - t * npg;
         const int hd = rest % g.G, pl = rest / g.G;
         const size_t tok = tbase + t * fstride + (size_t)pl * g.C + hd * D;
-        float q[D];
+        bf16x2_t q2[D / 2];  // the query as bf16 pairs, the operands of v_dot2_f32_bf16
 #pragma unroll
         for (int c = 0; c < D; c += 8) {
             const uint4 u = ld_stream16(Q + tok + c);
-            q[c] = bf16_lo(u.x); q[c + 1] = bf16_hi(u.x); q[c + 2] = bf16_lo(u.y); q[c + 3] = bf16_hi(u.y);
-            q[c + 4] = bf16_lo(u.z); q[c + 5] = bf16_hi(u.z); q[c + 6] = bf16_lo(u.w); q[c + 7] = bf16_hi(u.w);
+            q2[c / 2] = __builtin_bit_cast(bf16x2_t, u.x); q2[c / 2 + 1] = __builtin_bit_cast(bf16x2_t, u.y);
+            q2[c / 2 + 2] = __builtin_bit_cast(bf16x2_t, u.z); q2[c / 2 + 3] = __builtin_bit_cast(bf16x2_t, u.w);
         }
-        float o[D];
-#pragma unroll
-        for (int c = 0; c < D; ++c) o[c] = 0.0f;
-        float m = -INFINITY, l = 0.0f;
-        const int koff = pl * g.C + hd * D;
-        for (int j = 0; j <= t; ++j) {
-            const uint16_t* kr = sk + j * run + koff;
-            float s = 0.0f;
+        const int koff = pl * prow + hd * DP;
+        auto score = [&](int j) {  // q . k_j in fp32, two products per instruction
+            const uint16_t* kr = sk + j * frow + koff;
+            float a = 0.0f;
 #pragma unroll
             for (int c = 0; c < D; c += 8) {
                 const uint4 u = *reinterpret_cast<const uint4*>(kr + c);
-                s = fmaf(q[c], bf16_lo(u.x), s); s = fmaf(q[c + 1], bf16_hi(u.x), s);
-                s = fmaf(q[c + 2], bf16_lo(u.y), s); s = fmaf(q[c + 3], bf16_hi(u.y), s);
-                s = fmaf(q[c + 4], bf16_lo(u.z), s); s = fmaf(q[c + 5], bf16_hi(u.z), s);
-                s = fmaf(q[c + 6], bf16_lo(u.w), s); s = fmaf(q[c + 7], bf16_hi(u.w), s);
+                a = __builtin_amdgcn_fdot2_f32_bf16(q2[c / 2], __builtin_bit_cast(bf16x2_t, u.x), a, false);
+                a = __builtin_amdgcn_fdot2_f32_bf16(q2[c / 2 + 1], __builtin_bit_cast(bf16x2_t, u.y), a, false);
+                a = __builtin_amdgcn_fdot2_f32_bf16(q2[c / 2 + 2], __builtin_bit_cast(bf16x2_t, u.z), a, false);
+                a = __builtin_amdgcn_fdot2_f32_bf16(q2[c / 2 + 3], __builtin_bit_cast(bf16x2_t, u.w), a, false);
             }
-            s *= g.scale2;
-            const float mn = fmaxf(m, s);
-            const float alpha = fast_exp2(m - mn), p = fast_exp2(s - mn);
-            m = mn;
-            l = fmaf(l, alpha, p);
-            const uint16_t* vr = sv + j * run + koff;
+            return a;
+        };
+        // pass 1: the maximum score over frames 0..t, so pass 2 needs no rescaling
+        float mx = -INFINITY;
+        for (int j = 0; j <= t; ++j) mx = fmaxf(mx, score(j));
+        const float m2 = mx * g.scale2;
+        // pass 2: weights p_j = 2^(s_j c - m c) in fp32 and o += p_j v_j (each channel on its
+        // own, so a non-finite value stays in its channel)
+        float o[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] = 0.0f;
+        float l = 0.0f;
+        for (int j = 0; j <= t; ++j) {
+            const float p = fast_exp2(fmaf(score(j), g.scale2, -m2));
+            l += p;
+            const uint16_t* vr = sv + j * frow + koff;
 #pragma unroll
             for (int c = 0; c < D; c += 8) {
                 const uint4 u = *reinterpret_cast<const uint4*>(vr + c);
-                o[c] = fmaf(o[c], alpha, p * bf16_lo(u.x)); o[c + 1] = fmaf(o[c + 1], alpha, p * bf16_hi(u.x));
-                o[c + 2] = fmaf(o[c + 2], alpha, p * bf16_lo(u.y)); o[c + 3] = fmaf(o[c + 3], alpha, p * bf16_hi(u.y));
-                o[c + 4] = fmaf(o[c + 4], alpha, p * bf16_lo(u.z)); o[c + 5] = fmaf(o[c + 5], alpha, p * bf16_hi(u.z));
-                o[c + 6] = fmaf(o[c + 6], alpha, p * bf16_lo(u.w)); o[c + 7] = fmaf(o[c + 7], alpha, p * bf16_hi(u.w));
+                o[c] = fmaf(p, bf16_lo(u.x), o[c]); o[c + 1] = fmaf(p, bf16_hi(u.x), o[c + 1]);
+                o[c + 2] = fmaf(p, bf16_lo(u.y), o[c + 2]); o[c + 3] = fmaf(p, bf16_hi(u.y), o[c + 3]);
+                o[c + 4] = fmaf(p, bf16_lo(u.z), o[c + 4]); o[c + 5] = fmaf(p, bf16_hi(u.z), o[c + 5]);
+                o[c + 6] = fmaf(p, bf16_lo(u.w), o[c + 6]); o[c + 7] = fmaf(p, bf16_hi(u.w), o[c + 7]);
             }
         }
         const float inv = 1.0f / l;
@@ -387,12 +406,136 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Temporal causal attention on the matrix cores (head dim 64, T <= 32): one wave per
+// (clip, position, head) sequence, a workgroup = 4 consecutive sequences (with 4 heads, the
+// 4 heads of one position, whose frame rows are one contiguous 512-byte run per frame).
+// S^T = K Q^T is one 32 x 32 block (4 MFMAs over the channels; frames past T read zeros),
+// keys after the query's frame are masked, the softmax runs over the lane's query column
+// as in the spatial kernel, and O^T = V^T P^T takes 2 channel blocks x 2 key k-steps.  V^T
+// goes through a wave-private LDS tile (64 channel rows of 32 keys in the k-step key order,
+// 16-byte padded rows) - the only LDS use, so many waves fit on a CU to hide HBM latency.
+constexpr int TM_VRS = 32 * 2 + 16;  // bytes per V^T row (32 keys)
+constexpr int TM_WAVE_LDS = 64 * TM_VRS;
+
+struct TAttnMGeom {
+    int T, HW, C, G;
+    int nseq;       // sequences = B * HW * G
+    int ext;        // bytes from a sequence's first element to its last (buffer extent)
+    int fsb;        // bytes between frames
+    float scale2;   // log2(e) / 8
+};
+
+__global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t* __restrict__ Q,
+                                                                 const uint16_t* __restrict__ K,
+                                                                 const uint16_t* __restrict__ V,
+                                                                 uint16_t* __restrict__ O, TAttnMGeom g) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TM_WAVE_LDS];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sq = blockIdx.x * 4 + wave;
+    if (sq >= g.nseq) return;  // wave-uniform; the kernel has no workgroup barrier
+    const int px = lane & 31, hh = lane >> 5;
+    const int per_b = g.HW * g.G;
+    const int b = sq / per_b, rem = sq - b * per_b;
+    const int pos = rem / g.G, head = rem - pos * g.G;
+    const long long base = ((long long)b * g.T * g.HW + pos) * g.C + head * 64;  // frame 0 token
+    const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
+    // lane (px, hh): frame px (a key for K and V, a query for Q), channels 16 ks + 8 hh ..
+    // +7; frames past T read zeros (offset past the buffer)
+    const int roff = px < g.T ? px * g.fsb + hh * 16 : 0x7fffff00;
+    bf16x8_t kf[4], qf[4];
+    uint4 vr[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, roff + ks * 32, 0, 0));
+        qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qres, roff + ks * 32, 0, 0));
+        const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, roff + ks * 32, 0, 0);
+        vr[ks] = *reinterpret_cast<const uint4*>(&vv);
+    }
+    // V^T into the wave's LDS tile: channel 16 ks + 8 hh + e, key px at its k-step column
+    uint8_t* vt = smem + wave * TM_WAVE_LDS;
+    const int col = vperm(px) * 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t w[4] = {vr[ks].x, vr[ks].y, vr[ks].z, vr[ks].w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int row = ks * 16 + hh * 8 + 2 * e2;
+            *reinterpret_cast<uint16_t*>(vt + row * TM_VRS + col) = (uint16_t)(w[e2] & 0xffffu);
+            *reinterpret_cast<uint16_t*>(vt + (row + 1) * TM_VRS + col) = (uint16_t)(w[e2] >> 16);
+        }
+    }
+    // S^T = K Q^T (rows = keys, columns = queries)
+    f32x16_t st;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+    // causal mask: key j after query px (this also masks keys past T for queries < T)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = 8 * (r / 4) + 4 * hh + (r % 4);
+        if (j > px) st[r] = -INFINITY;
+        mx = fmaxf(mx, st[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = mx * g.scale2;
+    float sum = 0.0f;
+    bf16x8_t pf[2];
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = fast_exp2(fmaf(st[8 * h2 + 2 * e2], g.scale2, -m2));
+            const float p1 = fast_exp2(fmaf(st[8 * h2 + 2 * e2 + 1], g.scale2, -m2));
+            u[e2] = pack_bf16x2(p0, p1);
+            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e2]), ones, sum, false);
+        }
+        pf[h2] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
+    }
+    const float l = sum + __shfl_xor(sum, 32);
+    // the LDS tile is wave-private and its accesses execute in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x16_t ot[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ot[cb][e] = 0.0f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const bf16x8_t vf =
+                *reinterpret_cast<const bf16x8_t*>(vt + (cb * 32 + px) * TM_VRS + (h2 * 16 + hh * 8) * 2);
+            ot[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h2], ot[cb], 0, 0, 0);
+        }
+    }
+    if (px < g.T) {
+        const float inv = 1.0f / l;
+        uint16_t* orow = O + base + (long long)px * (g.fsb / 2);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint2 u;
+                u.x = pack_bf16x2(ot[cb][4 * q4] * inv, ot[cb][4 * q4 + 1] * inv);
+                u.y = pack_bf16x2(ot[cb][4 * q4 + 2] * inv, ot[cb][4 * q4 + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + cb * 32 + q4 * 8 + hh * 4) = u;
+            }
+    }
+}
+
 template <int D>
 hipError_t launch_temporal(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int B, int C, int T,
                            int HW, int G, hipStream_t s) {
     TAttnGeom g{};
     g.B = B; g.T = T; g.HW = HW; g.C = C; g.G = G;
-    g.np = TLDS / (2 * T * C * 2);  // the launcher guarantees T * C * 4 <= TLDS
+    g.np = TLDS / (2 * T * (C + 8 * G) * 2);  // at least 1: T * C <= 16384 and C + 8 G <= 1.25 C
     if (g.np > HW) g.np = HW;
     g.ntp = (HW + g.np - 1) / g.np;
     g.scale2 = 1.4426950408889634f / sqrtf((float)D);
@@ -404,7 +547,7 @@ hipError_t launch_temporal(const uint16_t* q, const uint16_t* k, const uint16_t*
 
 }  // namespace
 
-int attention_max_tc() { return TLDS / 4; }
+int attention_max_tc() { return 16384; }
 
 hipError_t launch_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H,
                               int W, int heads, int axis, hipStream_t s) {
@@ -428,6 +571,19 @@ hipError_t launch_attention3d(const void* q, const void* k, const void* v, void*
         return hipGetLastError();
     }
     if (T * C > attention_max_tc()) return hipErrorInvalidValue;
+    const long long fsb = (long long)HW * C * 2;         // bytes between frames
+    const long long ext = (long long)(T - 1) * fsb + 64 * 2;  // a sequence's buffer extent
+    const long long nseq = (long long)B * HW * heads;
+    if (d == 64 && T <= 32 && ext < 0x7fff0000LL && nseq <= 0x7ffffff0LL) {
+        TAttnMGeom g{};
+        g.T = T; g.HW = HW; g.C = C; g.G = heads;
+        g.nseq = (int)nseq;
+        g.fsb = (int)fsb;
+        g.ext = (int)ext;
+        g.scale2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+        hipLaunchKernelGGL(attn_temporal_mfma_kernel, dim3((unsigned)((nseq + 3) / 4)), dim3(256), 0, s, Q, K, V, O, g);
+        return hipGetLastError();
+    }
     switch (d) {
         case 32: return launch_temporal<32>(Q, K, V, O, B, C, T, HW, heads, s);
         case 64: return launch_temporal<64>(Q, K, V, O, B, C, T, HW, heads, s);
