@@ -44,6 +44,9 @@ SIGNATURES = {
     "cvt_causal_conv3d_fact_proj_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact_proj": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                           _ci, _vp, _sz, _vp]),
+    "cvt_causal_conv3d_temporal_stream_workspace": (_sz, [_ci, _ci]),
+    "cvt_causal_conv3d_temporal_stream": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci,
+                                                _vp, _sz, _vp]),
     "cvt_attention3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_quantize": (_ci, [_vp, _ci, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_dequantize": (_ci, [_vp, _vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
@@ -131,7 +134,8 @@ def _empty5(shape, dtype, device, layout):
 
 def haar3d_fwd(x, temporal_levels=2, out_dtype=None, layout="NTHWC", out=None):
     """Forward Haar patcher: x [B, C, T, H, W] NCTHW -> [B, 64C, T', H/4, W/4]
-    (16C and T with temporal_levels=0) in ``layout``."""
+    (16C and T with temporal_levels=0; T' = T/4 for a continuation chunk,
+    temporal_levels=3) in ``layout``."""
     _require_gpu(x)
     if not x.is_contiguous():
         raise ValueError("x must be NCTHW-contiguous")
@@ -140,6 +144,8 @@ def haar3d_fwd(x, temporal_levels=2, out_dtype=None, layout="NTHWC", out=None):
     odt = out_dtype or (out.dtype if out is not None else x.dtype)
     if temporal_levels == 2:
         shape = (B, 64 * C, 1 + max(T - 1, 0) // 4, H // 4, W // 4)
+    elif temporal_levels == 3:  # continuation chunk of 4k frames
+        shape = (B, 64 * C, T // 4, H // 4, W // 4)
     else:
         shape = (B, 16 * C, T, H // 4, W // 4)
     y = _check_out(out, shape, odt, x.device, lay) if out is not None else _empty5(shape, odt, x.device, lay)
@@ -154,11 +160,11 @@ def haar3d_inv(y, temporal_levels=2, out_dtype=None, out=None):
     _require_gpu(y)
     lay = _layout_of(y)
     B, NCH, Tq, Hq, Wq = y.shape
-    G = 64 if temporal_levels == 2 else 16
+    G = 64 if temporal_levels in (2, 3) else 16
     if NCH % G:
         raise ValueError(f"coefficient channels must be a multiple of {G}")
     C = NCH // G
-    T = 4 * Tq - 3 if temporal_levels == 2 else Tq
+    T = {2: 4 * Tq - 3, 3: 4 * Tq}.get(temporal_levels, Tq)
     odt = out_dtype or (out.dtype if out is not None else y.dtype)
     shape = (B, C, T, 4 * Hq, 4 * Wq)
     x = _check_out(out, shape, odt, y.device) if out is not None else torch.empty(shape, dtype=odt, device=y.device)
@@ -261,6 +267,46 @@ def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, work
     _check(lib.cvt_causal_conv3d_fact_proj(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(w_p), _ptr(b_p),
                                            _ptr(y), B, Cin, Cout, Cp, T, H, W, k, _ptr(workspace), workspace.numel(),
                                            _stream(x.device)), "causal_conv3d_fact_proj")
+    return y
+
+
+def temporal_stream_workspace_bytes(C, Cp=0):
+    return int(lib.cvt_causal_conv3d_temporal_stream_workspace(C, Cp))
+
+
+def causal_conv3d_temporal_stream(x, w_t, hist=None, w_p=None, b_t=None, b_p=None, workspace=None, out=None):
+    """Causal temporal convolution (k = 3) of one chunk of a stream, optionally with the
+    fused 1x1 projection w_p [Cp, C, 1, 1, 1].  x: [B, C, T, H, W] bf16 channels_last_3d;
+    hist: None (start of a stream: zero padding) or the two frames before x,
+    [B, C, 2, H, W] bf16 channels_last_3d (for B = 1 a view of the previous chunk's last
+    two frames).  Chunk by chunk this equals one call over the whole clip, bit for bit."""
+    _require_gpu(x, w_t, hist, w_p, b_t, b_p)
+    if x.dtype != torch.bfloat16 or not x.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError("x must be bfloat16 channels_last_3d (NTHWC)")
+    B, C, T, H, W = x.shape
+    if hist is not None:
+        if (tuple(hist.shape) != (B, C, 2, H, W) or hist.dtype != torch.bfloat16
+                or not hist.is_contiguous(memory_format=torch.channels_last_3d)):
+            raise ValueError("hist must be bfloat16 channels_last_3d [B, C, 2, H, W]")
+    if tuple(w_t.shape) != (C, C, 3, 1, 1) or w_t.dtype != torch.bfloat16 or not w_t.is_contiguous():
+        raise ValueError("w_t must be contiguous bfloat16 [C, C, 3, 1, 1]")
+    Cp = 0
+    if w_p is not None:
+        Cp = w_p.shape[0]
+        if tuple(w_p.shape) != (Cp, C, 1, 1, 1) or w_p.dtype != torch.bfloat16 or not w_p.is_contiguous():
+            raise ValueError("w_p must be contiguous bfloat16 [Cp, C, 1, 1, 1]")
+    for bias, n in ((b_t, C), (b_p, Cp)):
+        if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != n):
+            raise ValueError("biases must be contiguous float32 of their output width")
+    need = temporal_stream_workspace_bytes(C, Cp)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    shape = (B, Cp if w_p is not None else C, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_causal_conv3d_temporal_stream(_ptr(x), _ptr(hist), _ptr(w_t), _ptr(b_t), _ptr(w_p), _ptr(b_p),
+                                                 _ptr(y), B, C, Cp, T, H, W, _ptr(workspace), workspace.numel(),
+                                                 _stream(x.device)), "causal_conv3d_temporal_stream")
     return y
 
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <limits>
 
@@ -45,9 +46,10 @@ int check_haar(const void* a, int a_dt, const void* b, int b_dt, int layout, int
     if (!valid_dtype(a_dt) || !valid_dtype(b_dt)) return fail(CVT_E_DTYPE, "dtype must be CVT_F32 or CVT_BF16");
     if (!valid_layout(layout)) return fail(CVT_E_LAYOUT, "layout must be CVT_NCTHW or CVT_NTHWC");
     if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
-    if (tl != 0 && tl != 2) return fail(CVT_E_SHAPE, "temporal_levels must be 0 or 2, got %d", tl);
+    if (tl != 0 && tl != 2 && tl != 3) return fail(CVT_E_SHAPE, "temporal_levels must be 0, 2 or 3, got %d", tl);
     if (H % 4 || W % 4) return fail(CVT_E_SHAPE, "H and W must be multiples of 4 (got %dx%d)", H, W);
     if (tl == 2 && (T - 1) % 4) return fail(CVT_E_SHAPE, "temporal Haar needs T = 1 + 4k frames (got %d)", T);
+    if (tl == 3 && T % 4) return fail(CVT_E_SHAPE, "a continuation chunk needs T = 4k frames (got %d)", T);
     if (!aligned16(a) || !aligned16(b)) return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
     return CVT_OK;
 }
@@ -212,6 +214,40 @@ int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t,
     return hip_status(cvt::launch_conv_fact_proj(x, w_s, w_t, b_s, b_t, w_p, b_p, y, B, Cin, Cout, Cp, T, H, W, k,
                                                  workspace, (hipStream_t)stream),
                       "cvt_causal_conv3d_fact_proj launch");
+}
+
+size_t cvt_causal_conv3d_temporal_stream_workspace(int C, int Cp) {
+    if (C <= 0 || Cp < 0) return 0;
+    return cvt::conv_temporal_stream_workspace_bytes(C, Cp);
+}
+
+int cvt_causal_conv3d_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
+                                      const void* w_p, const float* b_p, void* y, int B, int C, int Cp, int T, int H,
+                                      int W, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !w_t || !y) return fail(CVT_E_NULL, "x, w_t and y must not be NULL");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    const int cp = w_p ? Cp : 0;
+    if (w_p && (Cp < 1 || Cp > 16 || C > 256))
+        return fail(CVT_E_SHAPE, "the fused projection needs C <= 256 and 1 <= Cp <= 16 (got C=%d, Cp=%d)", C, Cp);
+    // the kernel addresses x and the two history frames with 31-bit byte offsets
+    const long long P = std::max((long long)B * T * H * W, hist ? 2LL * B * H * W : 0LL);
+    if (C < 64 || C % 8 != 0 || !cvt::conv_temporal_stream_supported(C, cp, P))
+        return fail(CVT_E_SHAPE, "the stream convolution needs C >= 64, C %% 8 == 0 and an input below 2 GiB (C=%d)",
+                    C);
+    if (!aligned16(x) || !aligned16(y) || (hist && !aligned16(hist)))
+        return fail(CVT_E_ALIGN, "x, hist and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_t) & 1u) || (reinterpret_cast<uintptr_t>(w_p) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)) || (b_p && (reinterpret_cast<uintptr_t>(b_p) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::conv_temporal_stream_workspace_bytes(C, cp);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_conv_temporal_stream(x, hist, w_t, b_t, w_p, b_p, y, B, C, cp, T, H, W, workspace,
+                                                       (hipStream_t)stream),
+                      "cvt_causal_conv3d_temporal_stream launch");
 }
 
 int cvt_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H, int W,

@@ -276,6 +276,7 @@ struct RowsGeom {
     int nct, ncol, nrow;    // channel tiles, column tiles, row tiles
     int ntiles, per_xcd;
     int Cp, wp_bytes;       // fused 1x1 projection: output channels, packed weight bytes (0 = none)
+    int h_bytes;            // temporal stream: extent of the two history frames [B][2][HW][Cin] (0 = none)
 };
 
 // LDS bytes per region row: BK channels + 16 bytes of padding
@@ -316,12 +317,12 @@ struct RowsCfg {
                   "tile shape");
 };
 
-template <typename C, int NV, bool TAIL, bool PROJ>
+template <typename C, int NV, bool TAIL, bool PROJ, bool HIST>
 __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
                                           const float* __restrict__ bias, uint16_t* __restrict__ Y,
                                           const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
-                                          const RowsGeom& g, uint8_t* smem, int b, int t, int ct,
-                                          int r0, int c0) {
+                                          const uint16_t* __restrict__ Hx, const RowsGeom& g, uint8_t* smem, int b,
+                                          int t, int ct, int r0, int c0) {
     constexpr int KIND = C::KIND, BK = C::BK, FA = C::FA, FB = C::FB;
     constexpr int NTH = C::NTH, RC = C::RC, KX = C::KX, CPR = BK / 8, XS = C::XS, KS = BK / 16;
     constexpr int WCH = C::WCH;
@@ -343,6 +344,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         c16 = (q >> 3) % CPR;
     };
     int xbase[XL];
+    int hbase[HIST ? XL : 1];  // HIST (temporal stream, first row tile): offsets into the history frames
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
         const int q = tid + NTH * i;
@@ -357,6 +359,10 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             pos = ((b * g.T + t) * g.H + y) * g.W + x;
         } else {
             const int fr = r0 - 2 + rr, hw = c0 + cc;
+            if constexpr (HIST) {  // frames -2 and -1 are the history frames 0 and 1
+                const bool hok = ok && fr < 0 && hw < g.HW;
+                hbase[i] = hok ? (((b * 2 + fr + 2) * g.HW + hw) * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
+            }
             ok = ok && fr >= 0 && fr < g.T && hw < g.HW;
             pos = (b * g.T + fr) * g.HW + hw;
         }
@@ -365,6 +371,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         xbase[i] = ok ? (pos * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
     }
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, g.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t hres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(HIST ? Hx : X), (short)0, HIST ? g.h_bytes : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)Wf, (short)0, g.wf_bytes, 0x00020000);
 
     // The region of chunk c + 1 goes to the buffer last read in chunk c - 1, free since that
@@ -378,13 +386,22 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 #pragma unroll
         for (int i = half * XH; i < (half ? XL : XH); ++i) {
             int off = xbase[i] + kc * BK * 2;
-            if (TAIL) {  // Cin not a multiple of BK: chunks past Cin read zeros
+            bool inc = true;  // chunk channels below Cin
+            if (TAIL) {       // Cin not a multiple of BK: chunks past Cin read zeros
                 int row, c16;
                 xmap(tid + NTH * i, row, c16);
-                off = kc * BK + c16 * 8 < g.Cin ? off : OOB;
+                inc = kc * BK + c16 * 8 < g.Cin;
+                off = inc ? off : OOB;
             }
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0);
-            xr[i - half * XH] = *reinterpret_cast<const uint4*>(&v);
+            uint4 u = *reinterpret_cast<const uint4*>(&v);
+            if constexpr (HIST) {  // each row is in exactly one of the two buffers: the other reads zeros
+                const int hoff = inc ? hbase[i] + kc * BK * 2 : OOB;
+                const auto vh = __builtin_amdgcn_raw_buffer_load_b128(hres, hoff, 0, 0);
+                const uint4 w = *reinterpret_cast<const uint4*>(&vh);
+                u.x |= w.x; u.y |= w.y; u.z |= w.z; u.w |= w.w;
+            }
+            xr[i - half * XH] = u;
         }
     };
     auto store_region = [&](int buf, int half) {
@@ -671,11 +688,28 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     }
 }
 
-template <typename C, bool TAIL, bool PROJ>
+// rows_tile with a compile-time count of valid output rows
+template <typename C, bool TAIL, bool PROJ, bool HIST>
+__device__ __forceinline__ void rows_nv(int nv, const uint16_t* Wf, const uint16_t* X, const float* bias, uint16_t* Y,
+                                        const uint16_t* Wpf, const float* bias_p, const uint16_t* Hx,
+                                        const RowsGeom& g, uint8_t* smem, int b, int t, int ct, int r0, int c0) {
+    constexpr int R = C::R;
+    if (nv >= R)
+        rows_tile<C, R, TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+    else if (nv == 3)
+        rows_tile<C, (R > 3 ? 3 : R), TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+    else if (nv == 2)
+        rows_tile<C, (R > 2 ? 2 : R), TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+    else
+        rows_tile<C, 1, TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+}
+
+template <typename C, bool TAIL, bool PROJ, bool HISTK = false>
 __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
-    uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p, RowsGeom g) {
-    constexpr int KIND = C::KIND, R = C::R;
+    uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
+    const uint16_t* __restrict__ Hx, RowsGeom g) {
+    constexpr int KIND = C::KIND;
     // the region buffers; the fused projection's partial sums reuse them after the K loop
     __shared__ __attribute__((aligned(16))) uint8_t smem[PROJ ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
 
@@ -702,14 +736,12 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int rbase = rows / g.nrow, rextra = rows - rbase * g.nrow;
     const int nv = rbase + (rt < rextra ? 1 : 0);  // valid output rows (block-uniform, <= R)
     const int r0 = rt * rbase + min(rt, rextra), c0 = cl * C::NC;
-    if (nv >= R)
-        rows_tile<C, R, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
-    else if (nv == 3)
-        rows_tile<C, (R > 3 ? 3 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
-    else if (nv == 2)
-        rows_tile<C, (R > 2 ? 2 : R), TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
+    // temporal stream (HISTK): only the tiles whose look-back frames reach before frame 0
+    // read the history frames
+    if (HISTK && r0 < 2)
+        rows_nv<C, TAIL, PROJ, HISTK>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
     else
-        rows_tile<C, 1, TAIL, PROJ>(Wf, X, bias, Y, Wpf, bias_p, g, smem, b, t, ct, r0, c0);
+        rows_nv<C, TAIL, PROJ, false>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
 }
 
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
@@ -846,9 +878,27 @@ using TemporalProjCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK, 4>;
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
 // to Cp channels and Y is the [positions][Cp] projected output.
+template <typename C, bool TAIL, bool PROJ>
+hipError_t launch_rows_k(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const uint16_t* Wpf,
+                         const float* bias_p, const uint16_t* Hx, const RowsGeom& g, hipStream_t s) {
+    const dim3 grid((unsigned)(8LL * g.per_xcd)), block(C::NTH);
+    if constexpr (C::KIND == TEMPORAL3) {
+        if (Hx) {
+            hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, PROJ, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
+                               Hx, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, PROJ, false>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p, Hx, g);
+    return hipGetLastError();
+}
+
+// Hx (temporal only): the two frames before X, [B][2][HW][Cin] NTHWC, read in place of the
+// causal zero padding (a chunk of a stream); nullptr = zero padding.
 template <typename C>
 hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
-                           int B, hipStream_t s, const uint16_t* Wpf, const float* bias_p, int Cp) {
+                           int B, hipStream_t s, const uint16_t* Wpf, const float* bias_p, int Cp,
+                           const uint16_t* Hx) {
     constexpr int KIND = C::KIND, R = C::R, BK = C::BK;
     RowsGeom g{};
     g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
@@ -859,6 +909,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.nct = (cg.Cout + C::TCH - 1) / C::TCH;
     g.Cp = Cp;
     g.wp_bytes = Wpf ? (int)frag_bytes(Cp, cg.Cout, 1) : 0;
+    g.h_bytes = Hx ? (int)((long long)B * 2 * g.HW * cg.Cin * 2) : 0;
     long long ntiles;
     if (KIND == SPATIAL3) {
         g.ncol = (cg.W + C::NC - 1) / C::NC;
@@ -872,39 +923,28 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
-    const dim3 grid((unsigned)(8LL * g.per_xcd)), block(C::NTH);
     const bool tail = cg.Cin % BK != 0;
     if constexpr (KIND == TEMPORAL3) {
         if (Wpf) {
             if (g.nct != 1 || Cp < 1 || Cp > 16) return hipErrorInvalidValue;
-            if (tail)
-                hipLaunchKernelGGL((conv_rows_kernel<C, true, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
-                                   g);
-            else
-                hipLaunchKernelGGL((conv_rows_kernel<C, false, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
-                                   g);
-            return hipGetLastError();
+            return tail ? launch_rows_k<C, true, true>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, s)
+                        : launch_rows_k<C, false, true>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, s);
         }
     }
-    if (tail)
-        hipLaunchKernelGGL((conv_rows_kernel<C, true, false>), grid, block, 0, s, X, Wf, bias, Y,
-                           (const uint16_t*)nullptr, (const float*)nullptr, g);
-    else
-        hipLaunchKernelGGL((conv_rows_kernel<C, false, false>), grid, block, 0, s, X, Wf, bias, Y,
-                           (const uint16_t*)nullptr, (const float*)nullptr, g);
-    return hipGetLastError();
+    return tail ? launch_rows_k<C, true, false>(X, Wf, bias, Y, nullptr, nullptr, Hx, g, s)
+                : launch_rows_k<C, false, false>(X, Wf, bias, Y, nullptr, nullptr, Hx, g, s);
 }
 
 template <int KIND>
 hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
                        int B, hipStream_t s, const uint16_t* Wpf = nullptr, const float* bias_p = nullptr,
-                       int Cp = 0) {
+                       int Cp = 0, const uint16_t* Hx = nullptr) {
     if constexpr (KIND == SPATIAL3)
-        return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
+        return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr);
     if (cg.Cout <= TemporalNarrowCfg::TCH)
-        return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
-    if (Wpf) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
-    return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp);
+        return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
+    if (Wpf) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
+    return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
 }
 
 hipError_t launch_igemm(int kind, const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y,
@@ -1070,6 +1110,33 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
     g.kchunks = (Cout + BK - 1) / BK;
     return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp, b_p, Cp);
+}
+
+// Causal temporal convolution of one chunk of a stream (optionally with the fused 1x1
+// projection): the frames before the chunk come from hist instead of the zero padding.
+size_t conv_temporal_stream_workspace_bytes(int C, int Cp) {
+    return pack_bytes(C, C, 3) + (Cp > 0 ? align256(frag_bytes(Cp, C, 1)) : 0);
+}
+
+bool conv_temporal_stream_supported(int C, int Cp, long long P) {
+    return use_rows_kernel(3, C, P, C) && (Cp == 0 || (C <= 256 && Cp <= 16));
+}
+
+hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
+                                       const void* w_p, const float* b_p, void* y, int B, int C, int Cp, int T,
+                                       int H, int W, void* workspace, hipStream_t s) {
+    const long long P = (long long)B * T * H * W;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* wpp = w_p ? reinterpret_cast<uint16_t*>(ws + pack_bytes(C, C, 3)) : nullptr;
+    hipError_t e;
+    if ((e = pack_frag(w_t, wpt, C, C, 3, s)) != hipSuccess) return e;
+    if (w_p && (e = pack_frag(w_p, wpp, Cp, C, 1, s)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = C; g.Cout = C;
+    g.kchunks = (C + BK - 1) / BK;
+    return launch_rows<TEMPORAL3>(static_cast<const uint16_t*>(x), wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp,
+                                  b_p, w_p ? Cp : 0, static_cast<const uint16_t*>(hist));
 }
 
 }  // namespace cvt

@@ -94,6 +94,14 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
                                  const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp, int T,
                                  int H, int W, int k, void* workspace, hipStream_t s);
 
+// Causal temporal convolution of one chunk of a stream (conv.hip): history frames in place
+// of the zero padding, optional fused 1x1 projection (C <= 256, Cp <= 16).
+size_t conv_temporal_stream_workspace_bytes(int C, int Cp);
+bool conv_temporal_stream_supported(int C, int Cp, long long P);
+hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
+                                       const void* w_p, const float* b_p, void* y, int B, int C, int Cp, int T,
+                                       int H, int W, void* workspace, hipStream_t s);
+
 // Factorized self-attention (attention.hip).  Spatial: head dim 64; temporal causal:
 // head dim 32 or 64 and T * C <= attention_max_tc().
 int attention_max_tc();

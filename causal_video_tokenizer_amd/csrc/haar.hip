@@ -17,7 +17,9 @@
 // same butterflies.
 //
 // The causal extension is index arithmetic: padded frame p reads input frame
-// max(p - 3, 0), so the extended sequence is never materialised.
+// max(p - pad, 0) with pad = 3, so the extended sequence is never materialised.
+// A continuation chunk of a stream (pad = 0) has no leading copies: its latent
+// frame j is frames 4j .. 4j+3, exactly the latent frame the whole clip gives there.
 //
 // Mapping: one wavefront per (b, t', h', run of 64 w' positions); lane = w'.
 // Each lane loads the 4 x 4 x 4 block of every input channel with 8-byte
@@ -181,7 +183,7 @@ __device__ __forceinline__ void block_transform(float (&v)[NF][4][4]) {
 template <typename Tin, typename Tout, int NF, int CT>
 __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
                                                              int T, int H, int W, int Tq, int Hq, int Wq,
-                                                             int nchunk) {
+                                                             int nchunk, int pad) {
     constexpr int C = CT;
     constexpr int G = NF == 4 ? 64 : 16;
     constexpr int NCH = G * C;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
     for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const int src = NF == 4 ? max(4 * tile.tq + f - 3, 0) : tile.tq;
+            const int src = NF == 4 ? max(4 * tile.tq + f - pad, 0) : tile.tq;
             const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * wq_ld;
 #pragma unroll
             for (int r = 0; r < 4; ++r) raw[c][f][r].load(base + (size_t)r * W);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
 template <typename Tin, typename Tout, int NF, int CT>
 __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restrict__ y, Tout* __restrict__ x,
                                                              int T, int H, int W, int Tq, int Hq, int Wq,
-                                                             int nchunk) {
+                                                             int nchunk, int pad) {
     constexpr int C = CT;
     constexpr int G = NF == 4 ? 64 : 16;
     constexpr int NCH = G * C;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restri
         block_transform<NF>(v);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const int t = NF == 4 ? 4 * tile.tq + f - 3 : tile.tq;  // drop the 3 leading padded frames
+            const int t = NF == 4 ? 4 * tile.tq + f - pad : tile.tq;  // drop the leading padded frames
             if (t < 0) continue;
             Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restri
 template <typename Tin, typename Tout, int NF, int LAYOUT>
 __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restrict__ x, Tout* __restrict__ y, int C,
                                                               int T, int H, int W, int Tq, int Hq, int Wq,
-                                                              int nchunk) {
+                                                              int nchunk, int pad) {
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     if (!tile.valid) return;
     const int NCH = (NF == 4 ? 64 : 16) * C;
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restr
         float v[NF][4][4];
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const int src = NF == 4 ? max(4 * tile.tq + f - 3, 0) : tile.tq;
+            const int src = NF == 4 ? max(4 * tile.tq + f - pad, 0) : tile.tq;
             const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
             for (int r = 0; r < 4; ++r) load4(base + (size_t)r * W, v[f][r]);
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restr
 template <typename Tin, typename Tout, int NF, int LAYOUT>
 __global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restrict__ y, Tout* __restrict__ x, int C,
                                                               int T, int H, int W, int Tq, int Hq, int Wq,
-                                                              int nchunk) {
+                                                              int nchunk, int pad) {
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     if (!tile.valid) return;
     const int NCH = (NF == 4 ? 64 : 16) * C;
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restr
         block_transform<NF>(v);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const int t = NF == 4 ? 4 * tile.tq + f - 3 : tile.tq;
+            const int t = NF == 4 ? 4 * tile.tq + f - pad : tile.tq;
             if (t < 0) continue;
             Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
@@ -393,52 +395,60 @@ __global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restr
     }
 }
 
+// pad: leading copies of frame 0 (3 for a clip or a stream's first chunk, 0 for a
+// continuation chunk of 4k frames)
 template <typename Tin, typename Tout, int NF, int LAYOUT>
-hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int W, hipStream_t s) {
-    const int Tq = NF == 4 ? 1 + (T - 1) / 4 : T, Hq = H / 4, Wq = W / 4;
+hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int W, int pad, hipStream_t s) {
+    const int Tq = NF == 4 ? (T + pad) / 4 : T, Hq = H / 4, Wq = W / 4;
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (LAYOUT == CVT_NTHWC && C == 3)
         hipLaunchKernelGGL((haar_fwd_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)x, (Tout*)y, T, H, W, Tq, Hq, Wq, nchunk);
+                           (const Tin*)x, (Tout*)y, T, H, W, Tq, Hq, Wq, nchunk, pad);
     else
         hipLaunchKernelGGL((haar_fwd_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk);
+                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk, pad);
     return hipGetLastError();
 }
 
 template <typename Tin, typename Tout, int NF, int LAYOUT>
-hipError_t launch_inv_t(const void* y, void* x, int B, int C, int T, int H, int W, hipStream_t s) {
-    const int Tq = NF == 4 ? (T + 3) / 4 : T, Hq = H / 4, Wq = W / 4;
+hipError_t launch_inv_t(const void* y, void* x, int B, int C, int T, int H, int W, int pad, hipStream_t s) {
+    const int Tq = NF == 4 ? (T + pad) / 4 : T, Hq = H / 4, Wq = W / 4;
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (LAYOUT == CVT_NTHWC && C == 3)
         hipLaunchKernelGGL((haar_inv_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)y, (Tout*)x, T, H, W, Tq, Hq, Wq, nchunk);
+                           (const Tin*)y, (Tout*)x, T, H, W, Tq, Hq, Wq, nchunk, pad);
     else
         hipLaunchKernelGGL((haar_inv_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk);
+                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk, pad);
     return hipGetLastError();
 }
 
+// tl: 0 = per-frame 2D patcher; 2 = 3D with the causal first frame; 3 = 3D continuation
+// chunk (frames 4j .. 4j+3 form latent frame j, no leading copies)
 template <typename Tin, typename Tout>
 hipError_t fwd_by_shape(const void* x, void* y, int layout, int B, int C, int T, int H, int W, int tl, hipStream_t s) {
-    if (tl == 2)
-        return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 4, CVT_NTHWC>(x, y, B, C, T, H, W, s)
-                                   : launch_fwd_t<Tin, Tout, 4, CVT_NCTHW>(x, y, B, C, T, H, W, s);
-    return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 1, CVT_NTHWC>(x, y, B, C, T, H, W, s)
-                               : launch_fwd_t<Tin, Tout, 1, CVT_NCTHW>(x, y, B, C, T, H, W, s);
+    if (tl == 2 || tl == 3) {
+        const int pad = tl == 2 ? 3 : 0;
+        return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 4, CVT_NTHWC>(x, y, B, C, T, H, W, pad, s)
+                                   : launch_fwd_t<Tin, Tout, 4, CVT_NCTHW>(x, y, B, C, T, H, W, pad, s);
+    }
+    return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 1, CVT_NTHWC>(x, y, B, C, T, H, W, 0, s)
+                               : launch_fwd_t<Tin, Tout, 1, CVT_NCTHW>(x, y, B, C, T, H, W, 0, s);
 }
 
 template <typename Tin, typename Tout>
 hipError_t inv_by_shape(const void* y, void* x, int layout, int B, int C, int T, int H, int W, int tl, hipStream_t s) {
-    if (tl == 2)
-        return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 4, CVT_NTHWC>(y, x, B, C, T, H, W, s)
-                                   : launch_inv_t<Tin, Tout, 4, CVT_NCTHW>(y, x, B, C, T, H, W, s);
-    return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 1, CVT_NTHWC>(y, x, B, C, T, H, W, s)
-                               : launch_inv_t<Tin, Tout, 1, CVT_NCTHW>(y, x, B, C, T, H, W, s);
+    if (tl == 2 || tl == 3) {
+        const int pad = tl == 2 ? 3 : 0;
+        return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 4, CVT_NTHWC>(y, x, B, C, T, H, W, pad, s)
+                                   : launch_inv_t<Tin, Tout, 4, CVT_NCTHW>(y, x, B, C, T, H, W, pad, s);
+    }
+    return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 1, CVT_NTHWC>(y, x, B, C, T, H, W, 0, s)
+                               : launch_inv_t<Tin, Tout, 1, CVT_NCTHW>(y, x, B, C, T, H, W, 0, s);
 }
 
 }  // namespace

@@ -72,6 +72,12 @@ const char* cvt_last_error(void);
  *   t, h and w.  y: [B, 64C, T', H/4, W/4] with T' = 1 + (T-1)/4.
  * temporal_levels = 0 (image patcher, per frame): two levels along h and w.
  *   y: [B, 16C, T, H/4, W/4].
+ * temporal_levels = 3 (continuation chunk of a stream): T = 4k frames, no
+ *   leading copies; latent frame j is made of frames 4j .. 4j+3, so encoding a
+ *   clip's frames 0 .. 4a as one temporal_levels = 2 call and the following 4k
+ *   frames as a temporal_levels = 3 call gives exactly the latent frames of one
+ *   call over the whole clip (the causal design: a frame depends only on itself
+ *   and earlier frames).  y: [B, 64C, T/4, H/4, W/4].
  * Output channel = s2*G*C + s1*C + c with G = 8 (3D) or 4 (2D), where s1, s2
  * are the level-1 and level-2 subbands, s = 4*b_t + 2*b_h + b_w (2D:
  * 2*b_h + b_w), b = 0 for the low-pass (e+o)/sqrt(2) and 1 for the high-pass
@@ -79,7 +85,8 @@ const char* cvt_last_error(void);
  * y is stored in y_layout (NTHWC is the layout the convolution consumes) with
  * dtype y_dtype.  Arithmetic is float32.
  * Errors: CVT_E_SHAPE if H or W is not a multiple of 4, T is not 1 + 4k with
- * temporal_levels = 2, or temporal_levels is not 0 or 2.
+ * temporal_levels = 2 or 4k with temporal_levels = 3, or temporal_levels is not
+ * 0, 2 or 3.
  */
 int cvt_haar3d_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout,
                    int B, int C, int T, int H, int W, int temporal_levels, void* stream);
@@ -95,7 +102,8 @@ int cvt_haar3d_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layou
  * y: coefficients as produced by cvt_haar3d_fwd, layout y_layout, dtype
  * y_dtype.  x: output [B, C, T, H, W] NCTHW, dtype x_dtype, where T, H, W are
  * the PIXEL sizes (T = 4T' - 3 with temporal_levels = 2, the three leading
- * padded frames being dropped; T = T' with temporal_levels = 0).
+ * padded frames being dropped; T = 4T' for a continuation chunk,
+ * temporal_levels = 3; T = T' with temporal_levels = 0).
  * Errors: as cvt_haar3d_fwd.
  */
 int cvt_haar3d_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype,
@@ -172,6 +180,40 @@ size_t cvt_causal_conv3d_fact_proj_workspace(int B, int Cin, int Cout, int Cp, i
 int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
                                 const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp,
                                 int T, int H, int W, int k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal temporal convolution (k = 3) of one chunk of a stream, optionally followed
+ * by the fused 1x1x1 projection:
+ *   y[t] = sum_j w_t[:, :, j] . x[t + j - 2] (+ b_t),   t = 0 .. T-1,
+ * where x[-2] and x[-1] are the two frames of `hist` (the last two frames of the
+ * previous chunk's input), or zeros when hist is NULL (the start of a stream: the
+ * causal left padding of cvt_causal_conv3d_fact).  Running a clip chunk by chunk
+ * this way gives bit for bit the result of one call over the whole clip, so clips
+ * of any length can be encoded with memory bounded by the chunk size.
+ *
+ * Defined by: "Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer" (the temporal
+ * convolution is causal with k - 1 frames of left padding) and the guide's
+ * section 6.3 (videos of any length).
+ *
+ * x: bf16 NTHWC [B, C, T, H, W]; hist: NULL or bf16 NTHWC [B, C, 2, H, W] (with
+ *    B = 1 it may point into the previous chunk's buffer at its frame T_prev - 2);
+ * w_t: bf16 [C, C, 3, 1, 1]; b_t: float32 [C] or NULL;
+ * w_p: NULL (y = the convolution, bf16 NTHWC [B, C, T, H, W]) or bf16
+ *    [Cp, C, 1, 1, 1] with C <= 256 and 1 <= Cp <= 16 (y = the projection,
+ *    bf16 NTHWC [B, Cp, T, H, W], rounded as cvt_causal_conv3d_fact_proj);
+ *    b_p: float32 [Cp] or NULL.
+ * workspace: at least cvt_causal_conv3d_temporal_stream_workspace(C, Cp) bytes
+ *    (Cp = 0 without projection); owned by the caller.
+ * Errors: CVT_E_NULL for a NULL x, w_t or y; CVT_E_SHAPE for a non-positive
+ * size, C < 64, C not a multiple of 8, a projection outside the limits above or
+ * an input of 2 GiB or more; CVT_E_ALIGN unless x, hist and y are 16-byte
+ * aligned; CVT_E_WORKSPACE when the workspace is too small.
+ */
+size_t cvt_causal_conv3d_temporal_stream_workspace(int C, int Cp);
+int cvt_causal_conv3d_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
+                                      const void* w_p, const float* b_p, void* y, int B, int C, int Cp, int T,
+                                      int H, int W, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Factorized causal self-attention core, one axis per call:

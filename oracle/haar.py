@@ -118,6 +118,8 @@ def haar3d_fwd(x, temporal_levels=2):
     """Forward patcher on x [B, C, T, H, W] (float64).
 
     temporal_levels=2: 3D, output [B, 64C, 1+(T-1)/4, H/4, W/4].
+    temporal_levels=3: 3D continuation chunk of a stream (T = 4k, no leading
+    copies of frame 0), output [B, 64C, T/4, H/4, W/4].
     temporal_levels=0: 2D per frame, output [B, 16C, T, H/4, W/4].
     """
     x = np.asarray(x, dtype=np.float64)
@@ -127,11 +129,16 @@ def haar3d_fwd(x, temporal_levels=2):
         latent_frames(T)
         X = causal_pad(x)
         axes = (2, 3, 4)
+    elif temporal_levels == 3:  # continuation chunk: frames 4j .. 4j+3 form latent frame j
+        if T % 4 != 0:
+            raise ValueError(f"a continuation chunk needs T = 4k frames, got T={T}")
+        X = x
+        axes = (2, 3, 4)
     elif temporal_levels == 0:
         X = x
         axes = (3, 4)
     else:
-        raise ValueError("temporal_levels must be 0 or 2")
+        raise ValueError("temporal_levels must be 0, 2 or 3")
     X = haar_level(X, axes)
     X = haar_level(X, axes)
     return X
@@ -139,9 +146,10 @@ def haar3d_fwd(x, temporal_levels=2):
 
 def haar3d_inv(y, temporal_levels=2):
     """Inverse patcher: y [B, 64C, T', H', W'] -> x [B, C, 4T'-3, 4H', 4W']
-    (temporal_levels=2), or [B, 16C, T, H', W'] -> [B, C, T, 4H', 4W'] (0)."""
+    (temporal_levels=2), [B, C, 4T', 4H', 4W'] for a continuation chunk (3), or
+    [B, 16C, T, H', W'] -> [B, C, T, 4H', 4W'] (0)."""
     y = np.asarray(y, dtype=np.float64)
-    if temporal_levels == 2:
+    if temporal_levels in (2, 3):
         axes = (2, 3, 4)
         if y.shape[1] % 64:
             raise ValueError("3D inverse needs 64*C channels")
@@ -150,7 +158,7 @@ def haar3d_inv(y, temporal_levels=2):
         if y.shape[1] % 16:
             raise ValueError("2D inverse needs 16*C channels")
     else:
-        raise ValueError("temporal_levels must be 0 or 2")
+        raise ValueError("temporal_levels must be 0, 2 or 3")
     X = haar_level_inv(y, axes)
     X = haar_level_inv(X, axes)
     if temporal_levels == 2:

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -184,4 +184,25 @@ def test_attention_validation():
     assert call(q=MIS) == E_ALIGN
     assert call(o=ctypes.c_void_p(0x400008)) == E_ALIGN
     assert b"head dim" in (call(heads=2) and lib.cvt_last_error())
+
+
+def test_temporal_stream_validation():
+    ws = lib.cvt_causal_conv3d_temporal_stream_workspace(256, 6)
+    assert ws >= 256 * 256 * 3 * 2 and lib.cvt_causal_conv3d_temporal_stream_workspace(256, 0) < ws
+    assert lib.cvt_causal_conv3d_temporal_stream_workspace(0, 0) == 0
+
+    def call(**kw):
+        return lib.cvt_causal_conv3d_temporal_stream(kw.get("x", A), kw.get("hist", None), kw.get("wt", B_), None,
+                                                     kw.get("wp", None), None, kw.get("y", C_), 1, kw.get("C", 256),
+                                                     kw.get("Cp", 0), 5, 8, 8, kw.get("work", ctypes.c_void_p(0x500000)),
+                                                     kw.get("wsb", ws), None)
+    assert call(x=None) == E_NULL
+    assert call(wt=None) == E_NULL
+    assert call(C=48) == E_SHAPE                                     # below 64 channels
+    assert call(C=260) == E_SHAPE                                    # not a multiple of 8
+    assert call(wp=ctypes.c_void_p(0x600000), Cp=17) == E_SHAPE     # projection wider than 16
+    assert call(wp=ctypes.c_void_p(0x600000), Cp=6, C=512) == E_SHAPE
+    assert call(hist=MIS) == E_ALIGN
+    assert call(wsb=10) == E_WORKSPACE
+    assert call(work=None) == E_WORKSPACE
 

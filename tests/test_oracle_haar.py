@@ -223,3 +223,21 @@ def test_inverse_is_transpose_on_detail_blocks():
         r = rows[0] * 16 + rows[1] * 4 + rows[2]
         np.testing.assert_allclose(x[0, 0, 1:5].ravel(), M3[r], atol=1e-15)
         assert np.all(x[0, 0, 0] == 0)
+
+
+def test_continuation_chunks_equal_the_whole_clip():
+    """A clip encoded as a first chunk (frames 0 .. 4a, causal first frame) followed by
+    continuation chunks of 4k frames gives exactly the whole clip's latent frames, and
+    the inverse of each chunk gives back its frames: the causal design makes a latent
+    frame depend only on its own and earlier frames."""
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=(2, 3, 1 + 4 * 5, 8, 12))
+    whole = haar.haar3d_fwd(x, 2)
+    parts = [haar.haar3d_fwd(x[:, :, :1 + 4 * 2], 2), haar.haar3d_fwd(x[:, :, 9:13], 3),
+             haar.haar3d_fwd(x[:, :, 13:], 3)]
+    assert [p.shape[2] for p in parts] == [3, 1, 2]
+    assert np.array_equal(np.concatenate(parts, axis=2), whole)
+    back = [haar.haar3d_inv(parts[0], 2), haar.haar3d_inv(parts[1], 3), haar.haar3d_inv(parts[2], 3)]
+    assert np.max(np.abs(np.concatenate(back, axis=2) - x)) < 1e-12
+    with pytest.raises(ValueError):
+        haar.haar3d_fwd(x[:, :, :6], 3)
