@@ -14,8 +14,10 @@ Tensor conventions
 * FSQ indices are int32 [B, T, H, W].
 
 Entry points (same names as the C functions without the ``cvt_`` prefix):
-``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``, ``fsq_quantize``,
-``fsq_dequantize``.  ``lib`` is the loaded ctypes library with the raw C
+``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``,
+``causal_conv3d_fact_proj``, ``causal_conv3d_temporal_stream``, ``attention3d``,
+``fsq_quantize``, ``fsq_dequantize``, ``video_window``, ``video_pad``,
+``video_unpad``.  ``lib`` is the loaded ctypes library with the raw C
 functions.
 """
 
@@ -33,6 +35,7 @@ DEFAULT_LEVELS = (8, 8, 8, 5, 5, 5)
 
 # Every symbol include/cvt.h declares, with its ctypes signature.
 _vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_pi = ctypes.POINTER(_ci)
 SIGNATURES = {
     "cvt_abi_version": (_ci, []),
     "cvt_status_string": (ctypes.c_char_p, [_ci]),
@@ -50,6 +53,9 @@ SIGNATURES = {
     "cvt_attention3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_quantize": (_ci, [_vp, _ci, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_fsq_dequantize": (_ci, [_vp, _vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "cvt_video_window": (_ci, [_ci] * 7 + [_pi] * 6),
+    "cvt_video_pad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
+    "cvt_video_unpad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
 }
 
 
@@ -376,3 +382,53 @@ def fsq_dequantize(indices, levels=DEFAULT_LEVELS, dtype=torch.bfloat16, layout=
     _check(lib.cvt_fsq_dequantize(_ptr(indices), _ptr(codes), _dtype_code(codes.dtype), lay, arr, n,
                                   B, T, H, W, _ptr(invalid_count), _stream(indices.device)), "fsq_dequantize")
     return codes
+
+
+def video_window(T, H, W, window=17, t_align=4, s_align=4, index=0):
+    """Window ``index`` of a T-frame H x W clip cut into windows of ``window`` frames:
+    (n_windows, t0, nt, Tp, Hp, Wp), the padded sizes being the smallest
+    1 + k*t_align >= nt and multiples of s_align >= H, W (host arithmetic in the library)."""
+    out = [ctypes.c_int(0) for _ in range(6)]
+    _check(lib.cvt_video_window(T, H, W, window, t_align, s_align, index, *[ctypes.byref(o) for o in out]),
+           "video_window")
+    return tuple(o.value for o in out)
+
+
+def video_windows(T, H, W, window=17, t_align=4, s_align=4):
+    """[(t0, nt, Tp, Hp, Wp), ...] for every window of the clip."""
+    n = video_window(T, H, W, window, t_align, s_align, 0)[0]
+    return [video_window(T, H, W, window, t_align, s_align, i)[1:] for i in range(n)]
+
+
+def video_pad(x, t0, nt, Tp, Hp, Wp, out=None):
+    """Frames t0 .. t0+nt-1 of the clip x [B, C, T, H, W] (contiguous, f32/bf16) padded to
+    [B, C, Tp, Hp, Wp]: frames mirrored about the window's last frame, zero rows and
+    columns after the content."""
+    _require_gpu(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (NCTHW)")
+    B, C, T, H, W = x.shape
+    shape = (B, C, Tp, Hp, Wp)
+    y = (_check_out(out, shape, x.dtype, x.device) if out is not None
+         else torch.empty(shape, dtype=x.dtype, device=x.device))
+    _check(lib.cvt_video_pad(_ptr(x), _ptr(y), _dtype_code(x.dtype), B, C, T, H, W, t0, nt, Tp, Hp, Wp,
+                             _stream(x.device)), "video_pad")
+    return y
+
+
+def video_unpad(y, clip, t0, nt):
+    """Crop the padded window y [B, C, Tp, Hp, Wp] to nt frames and the clip's H x W and
+    write it at frames t0 .. t0+nt-1 of ``clip`` [B, C, T, H, W] (contiguous, same
+    dtype), in place.  Returns clip."""
+    _require_gpu(y, clip)
+    if not y.is_contiguous() or not clip.is_contiguous():
+        raise ValueError("y and clip must be contiguous (NCTHW)")
+    if y.dtype != clip.dtype or y.device != clip.device:
+        raise ValueError("y and clip must share dtype and device")
+    B, C, T, H, W = clip.shape
+    By, Cy, Tp, Hp, Wp = y.shape
+    if (By, Cy) != (B, C):
+        raise ValueError("y and clip must have the same batch and channels")
+    _check(lib.cvt_video_unpad(_ptr(y), _ptr(clip), _dtype_code(clip.dtype), B, C, T, H, W, t0, nt, Tp, Hp, Wp,
+                               _stream(clip.device)), "video_unpad")
+    return clip

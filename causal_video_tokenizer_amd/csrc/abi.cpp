@@ -40,6 +40,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_dtype(int d) { return d == CVT_F32 || d == CVT_BF16; }
 bool valid_layout(int l) { return l == CVT_NCTHW || l == CVT_NTHWC; }
 
+int check_window(const void* a, const void* b, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp,
+                 int Hp, int Wp, long long frames) {
+    if (!a || !b) return fail(CVT_E_NULL, "null tensor pointer");
+    if (!valid_dtype(dtype)) return fail(CVT_E_DTYPE, "dtype must be CVT_F32 or CVT_BF16");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0 || nt <= 0 || Tp <= 0 || Hp <= 0 || Wp <= 0)
+        return fail(CVT_E_SHAPE, "non-positive size");
+    if (t0 < 0 || (long long)t0 + nt > T)
+        return fail(CVT_E_SHAPE, "window %d + %d outside the clip of %d frames", t0, nt, T);
+    if (Tp < nt || Hp < H || Wp < W)
+        return fail(CVT_E_SHAPE, "padded size %dx%dx%d below the window's %dx%dx%d", Tp, Hp, Wp, nt, H, W);
+    if ((long long)Hp * Wp >= (1LL << 30)) return fail(CVT_E_SHAPE, "a padded frame of Hp*Wp must stay below 2^30");
+    if ((long long)B * C * frames >= (1LL << 31)) return fail(CVT_E_SHAPE, "B*C*Tp must stay below 2^31");
+    if (!aligned16(a) || !aligned16(b)) return fail(CVT_E_ALIGN, "tensor pointers must be 16-byte aligned");
+    return CVT_OK;
+}
+
 int check_haar(const void* a, int a_dt, const void* b, int b_dt, int layout, int B, int C, int T, int H, int W,
                int tl) {
     if (!a || !b) return fail(CVT_E_NULL, "null tensor pointer");
@@ -305,6 +321,45 @@ int cvt_fsq_dequantize(const int32_t* indices, void* codes, int c_dtype, int c_l
     return hip_status(cvt::launch_fsq_dequantize(indices, codes, c_dtype, c_layout, p, B, npb, d_invalid_count,
                                                  (hipStream_t)stream),
                       "cvt_fsq_dequantize launch");
+}
+
+int cvt_video_window(int T, int H, int W, int window, int t_align, int s_align, int index, int* n_windows, int* t0,
+                     int* nt, int* Tp, int* Hp, int* Wp) {
+    if (T <= 0 || H <= 0 || W <= 0 || window <= 0 || t_align <= 0 || s_align <= 0)
+        return fail(CVT_E_SHAPE, "sizes, window and alignments must be positive");
+    const long long n = ((long long)T + window - 1) / window;
+    if (index < 0 || index >= n) return fail(CVT_E_SHAPE, "window index %d outside [0, %lld)", index, n);
+    const long long a = (long long)index * window;
+    const long long len = std::min((long long)window, (long long)T - a);
+    const long long tp = 1 + ((len - 1 + t_align - 1) / t_align) * t_align;
+    const long long hp = ((long long)H + s_align - 1) / s_align * s_align;
+    const long long wp = ((long long)W + s_align - 1) / s_align * s_align;
+    const long long imax = std::numeric_limits<int>::max();
+    if (tp > imax || hp > imax || wp > imax) return fail(CVT_E_SHAPE, "padded size above INT_MAX");
+    if (n_windows) *n_windows = (int)n;
+    if (t0) *t0 = (int)a;
+    if (nt) *nt = (int)len;
+    if (Tp) *Tp = (int)tp;
+    if (Hp) *Hp = (int)hp;
+    if (Wp) *Wp = (int)wp;
+    return ok();
+}
+
+
+int cvt_video_pad(const void* x, void* y, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp, int Hp,
+                  int Wp, void* stream) {
+    const int st = check_window(x, y, dtype, B, C, T, H, W, t0, nt, Tp, Hp, Wp, Tp);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_video_pad(x, y, dtype, B, C, T, H, W, t0, nt, Tp, Hp, Wp, (hipStream_t)stream),
+                      "cvt_video_pad launch");
+}
+
+int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp,
+                    int Hp, int Wp, void* stream) {
+    const int st = check_window(y, x, dtype, B, C, T, H, W, t0, nt, Tp, Hp, Wp, Tp);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_video_unpad(y, x, dtype, B, C, T, H, W, t0, nt, Tp, Hp, Wp, (hipStream_t)stream),
+                      "cvt_video_unpad launch");
 }
 
 }  // extern "C"

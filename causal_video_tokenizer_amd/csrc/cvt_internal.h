@@ -108,4 +108,11 @@ int attention_max_tc();
 hipError_t launch_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H,
                               int W, int heads, int axis, hipStream_t stream);
 
+// Sliding-window padding and cropping (window.hip).  Arguments validated by the ABI layer:
+// planes of Hp*Wp and H*W elements below 2^30, B*C*Tp below 2^31.
+hipError_t launch_video_pad(const void* x, void* y, int dtype, int B, int C, int T, int H, int W, int t0, int nt,
+                            int Tp, int Hp, int Wp, hipStream_t s);
+hipError_t launch_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int H, int W, int t0, int nt,
+                              int Tp, int Hp, int Wp, hipStream_t s);
+
 }  // namespace cvt

@@ -289,6 +289,55 @@ int cvt_fsq_dequantize(const int32_t* indices, void* codes, int c_dtype, int c_l
                        const int32_t* levels, int D, int B, int T, int H, int W,
                        int32_t* d_invalid_count, void* stream);
 
+/*
+ * Sliding windows over a video of any length and size.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 6.3 (videos of any
+ * length are worked through in windows of temporal_window frames, 17 in the
+ * guide; each window is padded to the sizes the network accepts, with zeros in
+ * space and by reflection at the edge in time, and cropped back after
+ * reconstruction) and sections 6.1 / 7.3 (a causal clip holds 1 + k*f frames
+ * for a temporal compression f).
+ *
+ * cvt_video_window: host arithmetic, no device work.  The windows are
+ * consecutive: window i holds frames t0 = i*window .. t0 + nt - 1 with
+ * nt = min(window, T - t0); there are n_windows = ceil(T / window).  Its padded
+ * size is Tp = the smallest 1 + k*t_align >= nt, Hp and Wp = the smallest
+ * multiples of s_align >= H and >= W.  Each output pointer may be NULL.
+ * Errors: CVT_E_SHAPE for a non-positive argument, index outside
+ * [0, n_windows) or a padded size above INT_MAX.
+ */
+int cvt_video_window(int T, int H, int W, int window, int t_align, int s_align, int index, int* n_windows,
+                     int* t0, int* nt, int* Tp, int* Hp, int* Wp);
+
+/*
+ * Pad window (t0, nt) of a clip: x [B, C, T, H, W] NCTHW -> y [B, C, Tp, Hp, Wp]
+ * NCTHW, both of dtype (CVT_F32 or CVT_BF16), a bit-exact copy:
+ *   y[b,c,t,h,w] = x[b,c,t0 + r(t),h,w] for h < H and w < W, else 0,
+ * with r(t) = t for t < nt, continued past the last frame by the mirror about
+ * it that does not repeat it (nt-2, nt-3, ...), bouncing between the window's
+ * two ends when the pad is longer than the window; r = 0 when nt = 1.
+ * Padding goes after the content, so the crop keeps indices.
+ * Any Tp >= nt, Hp >= H, Wp >= W are accepted (cvt_video_window gives the
+ * aligned ones).  y must not overlap x.
+ * Errors: CVT_E_NULL, CVT_E_DTYPE; CVT_E_SHAPE for a non-positive size, a
+ * window outside the clip, a padded size below the window's, a plane of
+ * Hp*Wp elements at or above 2^30 or B*C*Tp at or above 2^31; CVT_E_ALIGN
+ * unless x and y are 16-byte aligned.
+ */
+int cvt_video_pad(const void* x, void* y, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp,
+                  int Hp, int Wp, void* stream);
+
+/*
+ * Crop a processed padded window y [B, C, Tp, Hp, Wp] NCTHW back to its nt
+ * frames and H x W pixels and write it at frames t0 .. t0 + nt - 1 of the clip
+ * x [B, C, T, H, W] NCTHW (other frames of x are left untouched), dtype as
+ * cvt_video_pad:  x[b,c,t0+t,h,w] = y[b,c,t,h,w].
+ * Errors: as cvt_video_pad.
+ */
+int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp,
+                    int Hp, int Wp, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

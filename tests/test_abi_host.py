@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -206,3 +206,37 @@ def test_temporal_stream_validation():
     assert call(wsb=10) == E_WORKSPACE
     assert call(work=None) == E_WORKSPACE
 
+
+
+def test_video_window_geometry_matches_the_oracle():
+    from oracle import window as ow
+    for T, H, W, win, ta, sa in [(40, 720, 1280, 17, 4, 16), (121, 1080, 1919, 17, 8, 16), (5, 3, 5, 2, 4, 4),
+                                 (1, 7, 9, 17, 4, 8), (33, 36, 64, 16, 4, 4)]:
+        bounds = ow.window_bounds(T, win)
+        got = cvt.video_windows(T, H, W, win, ta, sa)
+        assert got == [(t0, nt) + ow.aligned_size(nt, H, W, ta, sa) for t0, nt in bounds]
+        assert cvt.video_window(T, H, W, win, ta, sa)[0] == len(bounds)
+    n = ctypes.c_int(0)
+    assert lib.cvt_video_window(40, 8, 8, 17, 4, 4, 3, ctypes.byref(n), None, None, None, None, None) == E_SHAPE
+    assert lib.cvt_video_window(40, 8, 8, 0, 4, 4, 0, None, None, None, None, None, None) == E_SHAPE
+    assert lib.cvt_video_window(40, 8, 8, 17, 4, 4, 2, ctypes.byref(n), None, None, None, None, None) == OK
+    assert n.value == 3
+
+
+def test_video_pad_validation():
+    def pad(**kw):
+        a = dict(x=A, y=B_, dt=1, B=1, C=3, T=40, H=30, W=50, t0=34, nt=6, Tp=9, Hp=32, Wp=56)
+        a.update(kw)
+        return lib.cvt_video_pad(a["x"], a["y"], a["dt"], a["B"], a["C"], a["T"], a["H"], a["W"], a["t0"], a["nt"],
+                                 a["Tp"], a["Hp"], a["Wp"], None)
+    assert pad(x=None) == E_NULL
+    assert pad(dt=5) == E_DTYPE
+    assert pad(nt=7) == E_SHAPE            # past the clip's end
+    assert pad(t0=-1) == E_SHAPE
+    assert pad(Tp=5) == E_SHAPE            # shorter than the window
+    assert pad(Hp=29) == E_SHAPE
+    assert pad(Wp=49) == E_SHAPE
+    assert pad(Hp=32768, Wp=32768) == E_SHAPE
+    assert pad(y=MIS) == E_ALIGN
+    assert lib.cvt_video_unpad(A, B_, 1, 1, 3, 40, 30, 50, 34, 7, 9, 32, 56, None) == E_SHAPE
+    assert lib.cvt_video_unpad(MIS, B_, 1, 1, 3, 40, 30, 50, 34, 6, 9, 32, 56, None) == E_ALIGN
