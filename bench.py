@@ -22,7 +22,8 @@ CV8x8x8-720p-shaped chain (two factorized conv layers and the 1x1), where the
 convolution's MFMA fraction is quoted; a third, FSQ quantize and dequantize at a
 bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak; a fourth,
 the factorized self-attention (spatial and causal temporal) on the 16 x 90 x 160 token
-grid of the CV8x8x8-720p model, 256 channels in 4 heads.
+grid of the CV8x8x8-720p model, 256 channels in 4 heads; a fifth, sliding windows of 17
+frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop).
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -66,6 +67,7 @@ def parse():
     ap.add_argument("--no-c3", action="store_true", help="skip the 121-frame chain measurement")
     ap.add_argument("--no-fsq-bw", action="store_true", help="skip the FSQ bandwidth-size measurement")
     ap.add_argument("--no-attention", action="store_true", help="skip the factorized-attention measurement")
+    ap.add_argument("--no-window", action="store_true", help="skip the sliding-window measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -191,6 +193,7 @@ def main():
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
     fsq_bw = None if args.no_fsq_bw else fsq_bandwidth(cvt, si, torch, dev, args)
     attn = None if args.no_attention else attention_tokens(cvt, si, torch, dev, args)
+    win = None if args.no_window else windowed_1080p(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -228,6 +231,7 @@ def main():
         "cv8x8x8_720p_121f": c3,
         "fsq_bandwidth_size": fsq_bw,
         "attention_cv8x8x8_720p_tokens": attn,
+        "window_1080p_50f": win,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -411,6 +415,72 @@ def attention_tokens(cvt, si, torch, dev, args):
     del q, k, v, o
     torch.cuda.empty_cache()
     return out
+
+
+def windowed_1080p(cvt, si, torch, dev, args):
+    """Sliding windows over a clip the tokenizer does not accept as it is (1 x 3 x 50 x
+    1080 x 1920 bf16): per window of 17 frames, pad (mirror in time to 1 + 4k frames, zeros
+    to 1088 rows), 2-level Haar, inverse Haar, crop back into the output clip.  Reports the
+    whole windowed round trip in frames/s and the pad and crop kernels against the HBM
+    peak (bytes read + written by each call, summed over the windows)."""
+    wl = si.WORKLOADS["window_1080p_50f"]
+    shape = wl["x"]
+    B, C, T, H, W = shape
+    log(f"sliding windows: generating {shape} ...")
+    xb = si.to_bf16_bits(si.normal(shape, wl["seed"], wl["std"]))
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
+    del xb
+    out = torch.empty_like(x)
+    wins = cvt.video_windows(T, H, W, wl["window"], wl["t_align"], wl["s_align"])
+    bufs = [torch.empty((B, C, Tp, Hp, Wp), dtype=torch.bfloat16, device=dev) for _, _, Tp, Hp, Wp in wins]
+    coef = [torch.empty((B, 64 * C, 1 + (Tp - 1) // 4, Hp // 4, Wp // 4), dtype=torch.bfloat16, device=dev)
+            .to(memory_format=torch.channels_last_3d) for _, _, Tp, Hp, Wp in wins]
+    rec = [torch.empty_like(b) for b in bufs]
+
+    def pads():
+        for (t0, nt, Tp, Hp, Wp), b in zip(wins, bufs):
+            cvt.video_pad(x, t0, nt, Tp, Hp, Wp, out=b)
+
+    def crops():
+        for (t0, nt, _, _, _), r in zip(wins, rec):
+            cvt.video_unpad(r, out, t0, nt)
+
+    def round_trip():
+        for (t0, nt, Tp, Hp, Wp), b, c, r in zip(wins, bufs, coef, rec):
+            cvt.video_pad(x, t0, nt, Tp, Hp, Wp, out=b)
+            cvt.haar3d_fwd(b, 2, out=c)
+            cvt.haar3d_inv(c, 2, out=r)
+            cvt.video_unpad(r, out, t0, nt)
+
+    for _ in range(max(3, min(args.warmup, 10))):
+        round_trip()
+    torch.cuda.synchronize()
+    reps = max(5, args.steps // 2)
+    res = {"shape": list(shape), "windows": [list(w) for w in wins]}
+    pad_bytes = sum(2.0 * B * C * (nt * H * W + Tp * Hp * Wp) for _, nt, Tp, Hp, Wp in wins)
+    crop_bytes = sum(2.0 * B * C * 2 * nt * H * W for _, nt, _, _, _ in wins)
+    for name, fn, nbytes in (("pad", pads, pad_bytes), ("crop", crops, crop_bytes), ("round_trip", round_trip, None)):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        if nbytes is None:
+            res[name] = {"ms": round(ms, 4), "frames_per_s": round(B * T / (ms * 1e-3), 1)}
+        else:
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            res[name] = {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(gbps, 1),
+                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    # the round trip must give back the clip (Haar is orthonormal; bf16 storage of the
+    # coefficients and pixels rounds)
+    err = (out.float() - x.float()).abs().max().item()
+    res["round_trip_max_abs_err"] = err
+    del x, out, bufs, coef, rec
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):
