@@ -17,7 +17,7 @@ Entry points (same names as the C functions without the ``cvt_`` prefix):
 ``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``,
 ``causal_conv3d_fact_proj``, ``causal_conv3d_temporal_stream``, ``attention3d``,
 ``fsq_quantize``, ``fsq_dequantize``, ``video_window``, ``video_pad``,
-``video_unpad``.  ``lib`` is the loaded ctypes library with the raw C
+``video_unpad``, ``layernorm3d``, ``resblock3d``, ``downsample3d``, ``upsample3d``.  ``lib`` is the loaded ctypes library with the raw C
 functions.
 """
 
@@ -56,7 +56,20 @@ SIGNATURES = {
     "cvt_video_window": (_ci, [_ci] * 7 + [_pi] * 6),
     "cvt_video_pad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
     "cvt_video_unpad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
+    "cvt_layernorm3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _ci, _vp]),
+    "cvt_resblock3d_workspace": (_sz, [_ci] * 5),
+    "cvt_resblock3d": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _vp, _sz, _vp]),
+    "cvt_downsample3d_workspace": (_sz, [_ci] * 7),
+    "cvt_downsample3d": (_ci, [_vp] * 6 + [_ci] * 6 + [_vp, _sz, _vp]),
+    "cvt_upsample3d_workspace": (_sz, [_ci] * 8),
+    "cvt_upsample3d": (_ci, [_vp] * 6 + [_ci] * 8 + [_vp, _sz, _vp]),
 }
+
+
+class ResblockWeights(ctypes.Structure):
+    """cvt_resblock_weights: device pointers of one residual block's parameters."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ln1_g", "ln1_b", "c1_s", "c1_t", "c1_bs", "c1_bt",
+                                               "ln2_g", "ln2_b", "c2_s", "c2_t", "c2_bs", "c2_bt")]
 
 
 class CvtError(RuntimeError):
@@ -432,3 +445,119 @@ def video_unpad(y, clip, t0, nt):
     _check(lib.cvt_video_unpad(_ptr(y), _ptr(clip), _dtype_code(clip.dtype), B, C, T, H, W, t0, nt, Tp, Hp, Wp,
                                _stream(clip.device)), "video_unpad")
     return clip
+
+
+LN_EPS = 1e-6
+
+
+def _nthwc_bf16(t, what):
+    if t.dtype != torch.bfloat16 or not t.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError(f"{what} must be bfloat16 channels_last_3d (NTHWC)")
+
+
+def _f32_vec(t, n, what):
+    if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n):
+        raise ValueError(f"{what} must be contiguous float32 of {n} elements")
+
+
+def _bf16_w(t, shape, what):
+    if t is None or tuple(t.shape) != tuple(shape) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous bfloat16 {list(shape)}")
+
+
+def layernorm3d(x, gamma, beta, eps=LN_EPS, swish=False, out=None):
+    """LayerNorm over the channels of each position of a bf16 NTHWC tensor [B, C, T, H, W],
+    per-channel float32 scale and shift, then Swish if ``swish``.  ``out`` may be x."""
+    _require_gpu(x, gamma, beta)
+    _nthwc_bf16(x, "x")
+    B, C, T, H, W = x.shape
+    _f32_vec(gamma, C, "gamma")
+    _f32_vec(beta, C, "beta")
+    y = _check_out(out, x.shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None else torch.empty_like(x)
+    _check(lib.cvt_layernorm3d(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), B, C, T, H, W, eps, int(bool(swish)),
+                               _stream(x.device)), "layernorm3d")
+    return y
+
+
+RESBLOCK_KEYS = ("ln1_g", "ln1_b", "c1_s", "c1_t", "c1_bs", "c1_bt", "ln2_g", "ln2_b", "c2_s", "c2_t", "c2_bs",
+                 "c2_bt")
+
+
+def resblock3d(x, p, eps=LN_EPS, workspace=None, out=None):
+    """Residual block y = x + conv2(swish(LN2(conv1(swish(LN1(x)))))) on a bf16 NTHWC tensor.
+    p: dict with ln1_g, ln1_b, ln2_g, ln2_b (float32 [C]), c1_s, c2_s (bf16 [C, C, 1, 3, 3]),
+    c1_t, c2_t (bf16 [C, C, 3, 1, 1]) and optional biases c1_bs, c1_bt, c2_bs, c2_bt."""
+    _require_gpu(x, *[p.get(k) for k in RESBLOCK_KEYS])
+    _nthwc_bf16(x, "x")
+    B, C, T, H, W = x.shape
+    for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
+        if p.get(k) is None:
+            raise ValueError(f"{k} is required")
+        _f32_vec(p[k], C, k)
+    for k in ("c1_bs", "c1_bt", "c2_bs", "c2_bt"):
+        _f32_vec(p.get(k), C, k)
+    for c in ("c1", "c2"):
+        _bf16_w(p.get(c + "_s"), (C, C, 1, 3, 3), c + "_s")
+        _bf16_w(p.get(c + "_t"), (C, C, 3, 1, 1), c + "_t")
+    w = ResblockWeights(*[p[k].data_ptr() if p.get(k) is not None else None for k in RESBLOCK_KEYS])
+    need = int(lib.cvt_resblock3d_workspace(B, C, T, H, W))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = _check_out(out, x.shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None else torch.empty_like(x)
+    _check(lib.cvt_resblock3d(_ptr(x), ctypes.byref(w), _ptr(y), B, C, T, H, W, eps, _ptr(workspace),
+                              workspace.numel(), _stream(x.device)), "resblock3d")
+    return y
+
+
+def downsample3d(x, w_s=None, w_t=None, b_s=None, b_t=None, workspace=None, out=None):
+    """Downsampling block on a bf16 NTHWC tensor: 1x3x3 conv at stride 2 in H and W (w_s
+    [Cout, Cin, 1, 3, 3]) and/or causal 3x1x1 conv at stride 2 in time (w_t [Cout, C, 3, 1, 1],
+    T = 1 + 2k -> 1 + k)."""
+    _require_gpu(x, w_s, w_t, b_s, b_t)
+    _nthwc_bf16(x, "x")
+    B, Cin, T, H, W = x.shape
+    if w_s is None and w_t is None:
+        raise ValueError("at least one of w_s and w_t is needed")
+    Cout = (w_s if w_s is not None else w_t).shape[0]
+    if w_s is not None:
+        _bf16_w(w_s, (Cout, Cin, 1, 3, 3), "w_s")
+    if w_t is not None:
+        _bf16_w(w_t, (Cout, Cout if w_s is not None else Cin, 3, 1, 1), "w_t")
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    parts = (CVT_CONV_SPATIAL if w_s is not None else 0) | (CVT_CONV_TEMPORAL if w_t is not None else 0)
+    need = int(lib.cvt_downsample3d_workspace(B, Cin, Cout, T, H, W, parts))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    shape = (B, Cout, 1 + (T - 1) // 2 if w_t is not None else T, H // 2 if w_s is not None else H,
+             W // 2 if w_s is not None else W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_downsample3d(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout, T, H, W,
+                                _ptr(workspace), workspace.numel(), _stream(x.device)), "downsample3d")
+    return y
+
+
+def upsample3d(x, w_s, w_t, b_s=None, b_t=None, space=True, time=True, workspace=None, out=None):
+    """Upsampling block on a bf16 NTHWC tensor: nearest-neighbour repetition x2 in H and W
+    (space) and/or causal x2 in time (time: T -> 2T - 1), then the factorized conv
+    (w_s [Cout, Cin, 1, 3, 3], w_t [Cout, Cout, 3, 1, 1])."""
+    _require_gpu(x, w_s, w_t, b_s, b_t)
+    _nthwc_bf16(x, "x")
+    B, Cin, T, H, W = x.shape
+    Cout = w_s.shape[0]
+    _bf16_w(w_s, (Cout, Cin, 1, 3, 3), "w_s")
+    _bf16_w(w_t, (Cout, Cout, 3, 1, 1), "w_t")
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    need = int(lib.cvt_upsample3d_workspace(B, Cin, Cout, T, H, W, int(space), int(time)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    f = 2 if space else 1
+    shape = (B, Cout, 2 * T - 1 if time else T, f * H, f * W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_upsample3d(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout, T, H, W,
+                              int(space), int(time), _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "upsample3d")
+    return y

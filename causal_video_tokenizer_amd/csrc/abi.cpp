@@ -362,4 +362,110 @@ int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int 
                       "cvt_video_unpad launch");
 }
 
+int cvt_layernorm3d(const void* x, const float* gamma, const float* beta, void* y, int B, int C, int T, int H, int W,
+                    float eps, int swish, void* stream) {
+    if (!x || !gamma || !beta || !y) return fail(CVT_E_NULL, "x, gamma, beta and y must not be NULL");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (C % 8 != 0 || C > 4096) return fail(CVT_E_SHAPE, "C must be a multiple of 8 and at most 4096, got %d", C);
+    if (!(eps >= 0.0f)) return fail(CVT_E_SHAPE, "eps must be >= 0");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta))
+        return fail(CVT_E_ALIGN, "x, y, gamma and beta must be 16-byte aligned");
+    return hip_status(cvt::launch_layernorm(x, gamma, beta, y, (long long)B * T * H * W, C, eps, swish,
+                                            (hipStream_t)stream),
+                      "cvt_layernorm3d launch");
+}
+
+size_t cvt_resblock3d_workspace(int B, int C, int T, int H, int W) {
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    return cvt::resblock_workspace_bytes(B, C, T, H, W);
+}
+
+int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W, float eps,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !w || !y) return fail(CVT_E_NULL, "x, w and y must not be NULL");
+    if (!w->ln1_g || !w->ln1_b || !w->ln2_g || !w->ln2_b || !w->c1_s || !w->c1_t || !w->c2_s || !w->c2_t)
+        return fail(CVT_E_NULL, "scales, shifts and conv weights must not be NULL");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    const long long P = (long long)B * T * H * W;
+    if (C < 64 || C % 8 != 0 || !cvt::resblock_supported(C, P))
+        return fail(CVT_E_SHAPE, "the residual block needs C >= 64, C %% 8 == 0 and tensors below 2 GiB (C=%d)", C);
+    if (!(eps >= 0.0f)) return fail(CVT_E_SHAPE, "eps must be >= 0");
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    for (const float* v : {w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b})
+        if (!aligned16(v)) return fail(CVT_E_ALIGN, "LayerNorm scales and shifts must be 16-byte aligned");
+    for (const void* v : {w->c1_s, w->c1_t, w->c2_s, w->c2_t})
+        if (reinterpret_cast<uintptr_t>(v) & 1u) return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    for (const float* v : {w->c1_bs, w->c1_bt, w->c2_bs, w->c2_bt})
+        if (v && (reinterpret_cast<uintptr_t>(v) & 3u)) return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::resblock_workspace_bytes(B, C, T, H, W);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_resblock(x, *w, y, B, C, T, H, W, eps, workspace, (hipStream_t)stream),
+                      "cvt_resblock3d launch");
+}
+
+size_t cvt_downsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0 || parts < 1 || parts > 3) return 0;
+    return cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, parts & CVT_CONV_SPATIAL, parts & CVT_CONV_TEMPORAL);
+}
+
+int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                     int B, int Cin, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (!x || !y || (!w_s && !w_t)) return fail(CVT_E_NULL, "x, y and at least one weight must not be NULL");
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (Cin % 8 != 0 || Cout % 8 != 0)
+        return fail(CVT_E_SHAPE, "Cin and Cout must be multiples of 8 (got %d, %d)", Cin, Cout);
+    if (w_s && (H % 2 || W % 2)) return fail(CVT_E_SHAPE, "spatial downsampling needs even H and W (got %dx%d)", H, W);
+    if (w_t && (T - 1) % 2) return fail(CVT_E_SHAPE, "temporal downsampling needs T = 1 + 2k frames (got %d)", T);
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, w_s != nullptr, w_t != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_downsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace,
+                                             (hipStream_t)stream),
+                      "cvt_downsample3d launch");
+}
+
+size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time) {
+    (void)up_time;
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    return cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0);
+}
+
+int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
+                   int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (!x || !y || !w_s || !w_t) return fail(CVT_E_NULL, "x, y, w_s and w_t must not be NULL");
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    const int f = up_space ? 2 : 1;
+    const long long Pin = (long long)B * T * H * W, Pmid = Pin * f * f;
+    const long long Pout = (long long)B * (up_time ? 2 * T - 1 : T) * f * H * f * W;
+    if (Cin % 8 != 0 || Cout % 8 != 0 || Cout < 64 || !cvt::upsample_supported(Cin, Cout, Pin, Pmid) ||
+        (long long)f * H * f * W * Cout >= (1LL << 30) || Pout * Cout * 2 >= (1LL << 40))
+        return fail(CVT_E_SHAPE, "upsampling needs Cin, Cout multiples of 8, Cout >= 64 and tensors below 2 GiB "
+                                 "(Cin=%d, Cout=%d)", Cin, Cout);
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_upsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, up_space != 0,
+                                           up_time != 0, workspace, (hipStream_t)stream),
+                      "cvt_upsample3d launch");
+}
+
 }  // extern "C"

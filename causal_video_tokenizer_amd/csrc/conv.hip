@@ -67,10 +67,17 @@ struct Taps<POINT> {
 };
 
 struct ConvGeom {
-    long long P;                // positions = B*T*H*W
-    int T, H, W;
+    long long P;                // output positions = B*T*H*W
+    int T, H, W;                // output grid
     int Cin, Cout;
     int kchunks;                // ceil(Cin / BK)
+    // input grid and strides of conv_igemm_kernel (stride 2 = the downsampling convolution:
+    // output (t, y, x) reads input (st t + dt, ss y + dy, ss x + dx)); st = 0 means the input
+    // grid is the output grid at stride 1
+    int Ti, Hi, Wi, st, ss;
+    // conv_rows_kernel reading a nearest-neighbour upsampled input (x2 in H and W for the
+    // spatial part, causal x2 in time for the temporal part): Ti, Hi, Wi are then the input's
+    int ups;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -103,20 +110,23 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
     const int chunk = tid & 7;
     const int rbase = tid >> 3;  // 0..31
 
-    // decode the activation rows this thread loads
+    // decode the activation rows this thread loads: output (b, t, y, x) -> input base row
+    // (b, st t, ss y, ss x)
     int bt_[LB], by_[LB], bx_[LB];
     long long bpos[LB];
     bool bin[LB];
     const long long HW = (long long)g.H * g.W;
+    const long long HWi = (long long)g.Hi * g.Wi;
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
         const long long pos = p0 + rbase + 32 * i;
         bin[i] = pos < g.P;
         const long long pc = bin[i] ? pos : 0;
-        bpos[i] = pc;
-        bx_[i] = (int)(pc % g.W);
-        by_[i] = (int)((pc / g.W) % g.H);
-        bt_[i] = (int)((pc / HW) % g.T);
+        bx_[i] = (int)(pc % g.W) * g.ss;
+        by_[i] = (int)((pc / g.W) % g.H) * g.ss;
+        bt_[i] = (int)((pc / HW) % g.T) * g.st;
+        const long long b = pc / (HW * g.T);
+        bpos[i] = (b * g.Ti + bt_[i]) * HWi + (long long)by_[i] * g.Wi + bx_[i];
     }
 
     f32x16_t acc[FA][FB];
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
         const int c0 = kc * BK + chunk * 8;
         const bool cval = c0 < g.Cin;
         const int dt = TP_::dt(tap), dy = TP_::dy(tap), dx = TP_::dx(tap);
-        const long long doff = (long long)dt * HW + (long long)dy * g.W + dx;
+        const long long doff = (long long)dt * HWi + (long long)dy * g.Wi + dx;
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
             const int n = n0 + rbase + 32 * i;
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
             const int t = bt_[i] + dt, y = by_[i] + dy, x = bx_[i] + dx;
-            const bool v = cval && bin[i] && t >= 0 && t < g.T && y >= 0 && y < g.H && x >= 0 && x < g.W;
+            const bool v = cval && bin[i] && t >= 0 && t < g.Ti && y >= 0 && y < g.Hi && x >= 0 && x < g.Wi;
             if (v)
                 rb[i] = *reinterpret_cast<const uint4*>(X + (size_t)(bpos[i] + doff) * g.Cin + c0);
             else
@@ -277,6 +287,21 @@ struct RowsGeom {
     int ntiles, per_xcd;
     int Cp, wp_bytes;       // fused 1x1 projection: output channels, packed weight bytes (0 = none)
     int h_bytes;            // temporal stream: extent of the two history frames [B][2][HW][Cin] (0 = none)
+    int ups;                // input nearest-neighbour upsampled (spatial: x2 in H, W; temporal: causal x2)
+    int Ti, Hi, Wi;         // with ups: the input grid
+};
+
+// Epilogues of conv_rows_kernel.  PLAIN: bias, bf16.  PROJ: the fused 1x1 projection.
+// NORM: LayerNorm over the Cout channels of each position (scale, shift) and optionally
+// Swish.  RES: a residual tensor shaped like the output added before the rounding.  PROJ
+// and NORM need every output channel in the workgroup (one channel tile).
+constexpr int EPI_PLAIN = 0, EPI_PROJ = 1, EPI_NORM = 2, EPI_RES = 3;
+struct RowsAux {
+    const uint16_t* res;   // RES: [positions][Cout] bf16, the output's layout
+    const float* ln_g;     // NORM: per-channel scale and shift, float32 [Cout]
+    const float* ln_b;
+    float eps;             // NORM: added to the variance
+    int swish;             // NORM: apply Swish after the affine step
 };
 
 // LDS bytes per region row: BK channels + 16 bytes of padding
@@ -317,12 +342,12 @@ struct RowsCfg {
                   "tile shape");
 };
 
-template <typename C, int NV, bool TAIL, bool PROJ, bool HIST>
+template <typename C, int NV, bool TAIL, int EPI, bool HIST>
 __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const uint16_t* __restrict__ X,
                                           const float* __restrict__ bias, uint16_t* __restrict__ Y,
                                           const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
-                                          const uint16_t* __restrict__ Hx, const RowsGeom& g, uint8_t* smem, int b,
-                                          int t, int ct, int r0, int c0) {
+                                          const uint16_t* __restrict__ Hx, const RowsGeom& g, const RowsAux& aux,
+                                          uint8_t* smem, int b, int t, int ct, int r0, int c0) {
     constexpr int KIND = C::KIND, BK = C::BK, FA = C::FA, FB = C::FB;
     constexpr int NTH = C::NTH, RC = C::RC, KX = C::KX, CPR = BK / 8, XS = C::XS, KS = BK / 16;
     constexpr int WCH = C::WCH;
@@ -356,7 +381,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         if (KIND == SPATIAL3) {
             const int y = r0 - 1 + rr, x = c0 - 1 + cc;
             ok = ok && y >= 0 && y < g.H && x >= 0 && x < g.W;
-            pos = ((b * g.T + t) * g.H + y) * g.W + x;
+            pos = g.ups ? ((b * g.T + t) * g.Hi + (y >> 1)) * g.Wi + (x >> 1) : ((b * g.T + t) * g.H + y) * g.W + x;
         } else {
             const int fr = r0 - 2 + rr, hw = c0 + cc;
             if constexpr (HIST) {  // frames -2 and -1 are the history frames 0 and 1
@@ -364,7 +389,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 hbase[i] = hok ? (((b * 2 + fr + 2) * g.HW + hw) * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
             }
             ok = ok && fr >= 0 && fr < g.T && hw < g.HW;
-            pos = (b * g.T + fr) * g.HW + hw;
+            // upsampled in time: output frame fr of the causal repetition is input frame (fr + 1) / 2
+            pos = g.ups ? (b * g.Ti + ((fr + 1) >> 1)) * g.HW + hw : (b * g.T + fr) * g.HW + hw;
         }
         // rows outside the tensor get a base past its end for every chunk (the launcher keeps
         // the tensor below ROWS_OOB_BASE bytes and chunk offsets below 64 KiB)
@@ -556,22 +582,27 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
 
-    if constexpr (PROJ) {
-        // Fused 1x1 projection (temporal kernel with every output channel in the workgroup).
-        // The tile's conv outputs, bias added and rounded to bf16 once (what a separate 1x1
-        // conv would read), are staged in LDS as [frame][column][channel] rows; then each wave
-        // takes (frame, 32-column block) pairs and multiplies the projection weights (A
-        // operand, rows o < Cp, standard fragment order) by the staged columns over all TCH
-        // channels (B operand), so every projected value is one MFMA accumulation chain and no
-        // partial sums cross waves.  Channels past Cout are staged as zeros.
+    if constexpr (EPI == EPI_PROJ || EPI == EPI_NORM) {
+        // Epilogues over whole position rows (temporal kernel with every output channel in the
+        // workgroup).  The tile's conv outputs, bias added and rounded to bf16 once (what a
+        // separate pass would read), are staged in LDS as [frame][column][channel] rows, and
+        // each wave then takes (frame, 32-column block) pairs.  Channels past Cout are staged
+        // as zeros.
+        // PROJ: the projection weights (A operand, rows o < Cp, standard fragment order) times
+        // the staged columns over all TCH channels (B operand), so every projected value is one
+        // MFMA accumulation chain and no partial sums cross waves.
         constexpr int TCH = C::TCH, NC = C::NC, PRS = C::PRS, KST = TCH / 16;
-        const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
         // the projection weights (the only 32-row block, Cp <= 32; k-steps past Cout read
         // zeros) are requested first and arrive while the tile is staged
-        bf16x8_t fp[KST];
+        bf16x8_t fp[EPI == EPI_PROJ ? KST : 1];
+        if constexpr (EPI == EPI_PROJ) {
+            const __amdgpu_buffer_rsrc_t pres =
+                __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
 #pragma unroll
-        for (int ks = 0; ks < KST; ++ks)
-            fp[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(pres, (ks * 64 + lane) * 16, 0, 0));
+            for (int ks = 0; ks < KST; ++ks)
+                fp[ks] = __builtin_bit_cast(bf16x8_t,
+                                            __builtin_amdgcn_raw_buffer_load_b128(pres, (ks * 64 + lane) * 16, 0, 0));
+        }
 #pragma unroll
         for (int ry = 0; ry < NV; ++ry)
 #pragma unroll
@@ -589,6 +620,77 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                         *reinterpret_cast<uint2*>(smem + (ry * NC + wpos * 32 * FB + cb * 32 + px) * PRS + n * 2) = u;
                     }
         __syncthreads();
+        if constexpr (EPI == EPI_NORM) {
+            // LayerNorm over the Cout channels of each staged column, then the per-channel scale
+            // and shift and (optionally) Swish.  Lane (px, khalf) sums half of the channels of
+            // column px and the halves meet through one cross-lane exchange: the mean first,
+            // then the centred squares (a second pass over LDS).  The results are written as
+            // whole position rows, 16-byte chunks of consecutive lanes.
+            constexpr int HALF = TCH / 2;
+            constexpr int NBLK = NC / 32;
+            const int Cout = g.Cout, cpr = Cout >> 3;  // 16-byte chunks per position row
+            const float inv_n = 1.0f / (float)Cout;
+            const int nit = (32 * cpr + 63) >> 6;
+            for (int pr = wave; pr < NV * NBLK; pr += C::NW) {  // wave-uniform
+                const int fr = pr / NBLK, cblk = pr % NBLK;
+                const uint8_t* col = smem + (fr * NC + cblk * 32) * PRS;
+                const uint8_t* mine = col + px * PRS + khalf * HALF * 2;
+                float sum = 0.0f;
+#pragma unroll
+                for (int c8 = 0; c8 < HALF / 8; ++c8) {  // channels past Cout are staged zeros
+                    const uint4 v = *reinterpret_cast<const uint4*>(mine + c8 * 16);
+                    sum += (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
+                           (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
+                }
+                sum += __shfl_xor(sum, 32);
+                const float mean = sum * inv_n;
+                float sq = 0.0f;
+#pragma unroll
+                for (int c8 = 0; c8 < HALF / 8; ++c8) {
+                    if (khalf * HALF + c8 * 8 < Cout) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(mine + c8 * 16);
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float d0 = bf16_lo(w[k]) - mean, d1 = bf16_hi(w[k]) - mean;
+                            sq += d0 * d0 + d1 * d1;
+                        }
+                    }
+                }
+                sq += __shfl_xor(sq, 32);
+                const float rstd = rsqrtf(sq * inv_n + aux.eps);
+                const int hw0 = c0 + cblk * 32;
+                const long long pbase = ((long long)b * g.T + r0 + fr) * g.HW + hw0;
+                for (int it = 0; it < nit; ++it) {  // wave-uniform trip count
+                    const int f = it * 64 + lane;
+                    const int pc = f / cpr, ch = f - pc * cpr;
+                    const float m = __shfl(mean, pc & 31), r = __shfl(rstd, pc & 31);
+                    if (pc < 32 && hw0 + pc < g.HW) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(col + pc * PRS + ch * 16);
+                        const float4 g0 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8);
+                        const float4 g1 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8 + 4);
+                        const float4 b0 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8);
+                        const float4 b1 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8 + 4);
+                        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                        uint32_t o[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            float y0 = (bf16_lo(w[k]) - m) * r * gg[2 * k] + bb[2 * k];
+                            float y1 = (bf16_hi(w[k]) - m) * r * gg[2 * k + 1] + bb[2 * k + 1];
+                            if (aux.swish) {
+                                y0 = y0 / (1.0f + __expf(-y0));
+                                y1 = y1 / (1.0f + __expf(-y1));
+                            }
+                            o[k] = pack_bf16x2(y0, y1);
+                        }
+                        *reinterpret_cast<uint4*>(Y + (pbase + pc) * Cout + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                }
+            }
+            return;
+        }
         const int Cp = g.Cp;
         float bp[8];
 #pragma unroll
@@ -654,9 +756,35 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x16_t& c = acc[ry][a][cb];
+                    float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (EPI == EPI_RES) {  // 4 consecutive channels of the residual
+                        const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf;
+                        long long pos;
+                        bool ok;
+                        if (KIND == SPATIAL3) {
+                            const int x = c0 + wpos * 32 * FB + cb * 32 + px;
+                            ok = x < g.W;
+                            pos = (((long long)b * g.T + t) * g.H + r0 + ry) * g.W + x;
+                        } else {
+                            const int hw = c0 + wpos * 32 * FB + cb * 32 + px;
+                            ok = hw < g.HW;
+                            pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
+                        }
+                        if (ok && n < g.Cout) {
+                            const uint2 rr = *reinterpret_cast<const uint2*>(aux.res + pos * g.Cout + n);
+                            rv[0] = bf16_lo(rr.x); rv[1] = bf16_hi(rr.x);
+                            rv[2] = bf16_lo(rr.y); rv[3] = bf16_hi(rr.y);
+                        }
+                    }
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[e] = c[4 * q + e] + bv[a][q][e];
+                        if constexpr (EPI == EPI_RES) o[e] += rv[e];
+                    }
                     uint2 u;
-                    u.x = pack_bf16x2(c[4 * q] + bv[a][q][0], c[4 * q + 1] + bv[a][q][1]);
-                    u.y = pack_bf16x2(c[4 * q + 2] + bv[a][q][2], c[4 * q + 3] + bv[a][q][3]);
+                    u.x = pack_bf16x2(o[0], o[1]);
+                    u.y = pack_bf16x2(o[2], o[3]);
                     *reinterpret_cast<uint2*>(stage + (cb * 32 + px) * OS + (a * 32 + 8 * q + 4 * khalf) * 2) = u;
                 }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -689,29 +817,30 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 }
 
 // rows_tile with a compile-time count of valid output rows
-template <typename C, bool TAIL, bool PROJ, bool HIST>
+template <typename C, bool TAIL, int EPI, bool HIST>
 __device__ __forceinline__ void rows_nv(int nv, const uint16_t* Wf, const uint16_t* X, const float* bias, uint16_t* Y,
                                         const uint16_t* Wpf, const float* bias_p, const uint16_t* Hx,
-                                        const RowsGeom& g, uint8_t* smem, int b, int t, int ct, int r0, int c0) {
+                                        const RowsGeom& g, const RowsAux& aux, uint8_t* smem, int b, int t, int ct,
+                                        int r0, int c0) {
     constexpr int R = C::R;
     if (nv >= R)
-        rows_tile<C, R, TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_tile<C, R, TAIL, EPI, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
     else if (nv == 3)
-        rows_tile<C, (R > 3 ? 3 : R), TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_tile<C, (R > 3 ? 3 : R), TAIL, EPI, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
     else if (nv == 2)
-        rows_tile<C, (R > 2 ? 2 : R), TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_tile<C, (R > 2 ? 2 : R), TAIL, EPI, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
     else
-        rows_tile<C, 1, TAIL, PROJ, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_tile<C, 1, TAIL, EPI, HIST>(Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
 }
 
-template <typename C, bool TAIL, bool PROJ, bool HISTK = false>
+template <typename C, bool TAIL, int EPI, bool HISTK = false>
 __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) void conv_rows_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wf, const float* __restrict__ bias,
     uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wpf, const float* __restrict__ bias_p,
-    const uint16_t* __restrict__ Hx, RowsGeom g) {
+    const uint16_t* __restrict__ Hx, RowsGeom g, RowsAux aux) {
     constexpr int KIND = C::KIND;
     // the region buffers; the fused projection's partial sums reuse them after the K loop
-    __shared__ __attribute__((aligned(16))) uint8_t smem[PROJ ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[(EPI == EPI_PROJ || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -739,9 +868,9 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     // temporal stream (HISTK): only the tiles whose look-back frames reach before frame 0
     // read the history frames
     if (HISTK && r0 < 2)
-        rows_nv<C, TAIL, PROJ, HISTK>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_nv<C, TAIL, EPI, HISTK>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
     else
-        rows_nv<C, TAIL, PROJ, false>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, smem, b, t, ct, r0, c0);
+        rows_nv<C, TAIL, EPI, false>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
 }
 
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
@@ -878,31 +1007,48 @@ using TemporalProjCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK, 4>;
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
 // to Cp channels and Y is the [positions][Cp] projected output.
-template <typename C, bool TAIL, bool PROJ>
+template <typename C, bool TAIL, int EPI>
 hipError_t launch_rows_k(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const uint16_t* Wpf,
-                         const float* bias_p, const uint16_t* Hx, const RowsGeom& g, hipStream_t s) {
+                         const float* bias_p, const uint16_t* Hx, const RowsGeom& g, const RowsAux& aux,
+                         hipStream_t s) {
     const dim3 grid((unsigned)(8LL * g.per_xcd)), block(C::NTH);
-    if constexpr (C::KIND == TEMPORAL3) {
+    if constexpr (C::KIND == TEMPORAL3 && (EPI == EPI_PLAIN || EPI == EPI_PROJ)) {
         if (Hx) {
-            hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, PROJ, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
-                               Hx, g);
+            hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, EPI, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
+                               Hx, g, aux);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, PROJ, false>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p, Hx, g);
+    if (Hx) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, EPI, false>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p, Hx, g,
+                       aux);
     return hipGetLastError();
 }
 
+template <typename C, int EPI>
+hipError_t launch_rows_tail(bool tail, const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y,
+                            const uint16_t* Wpf, const float* bias_p, const uint16_t* Hx, const RowsGeom& g,
+                            const RowsAux& aux, hipStream_t s) {
+    return tail ? launch_rows_k<C, true, EPI>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, aux, s)
+                : launch_rows_k<C, false, EPI>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, aux, s);
+}
+
 // Hx (temporal only): the two frames before X, [B][2][HW][Cin] NTHWC, read in place of the
-// causal zero padding (a chunk of a stream); nullptr = zero padding.
+// causal zero padding (a chunk of a stream); nullptr = zero padding.  aux selects the NORM
+// (aux.ln_g set) or RES (aux.res set) epilogue.
 template <typename C>
 hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
                            int B, hipStream_t s, const uint16_t* Wpf, const float* bias_p, int Cp,
-                           const uint16_t* Hx) {
+                           const uint16_t* Hx, const RowsAux& aux) {
     constexpr int KIND = C::KIND, R = C::R, BK = C::BK;
     RowsGeom g{};
     g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
-    g.x_bytes = (int)(cg.P * cg.Cin * 2);
+    g.ups = cg.ups;
+    g.Ti = cg.ups ? cg.Ti : cg.T;
+    g.Hi = cg.ups ? cg.Hi : cg.H;
+    g.Wi = cg.ups ? cg.Wi : cg.W;
+    g.x_bytes = (int)((long long)B * g.Ti * g.Hi * g.Wi * cg.Cin * 2);
+    if (cg.ups && Hx) return hipErrorInvalidValue;
     g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
     g.NA = (cg.Cout + 31) / 32;
     g.KC16 = (cg.Cin + 15) / 16;
@@ -924,31 +1070,46 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
     const bool tail = cg.Cin % BK != 0;
-    if constexpr (KIND == TEMPORAL3) {
+    if constexpr (KIND == TEMPORAL3 && C::NW == 4) {  // the 4-wave temporal tiles: fused projection, norm
         if (Wpf) {
-            if (g.nct != 1 || Cp < 1 || Cp > 16) return hipErrorInvalidValue;
-            return tail ? launch_rows_k<C, true, true>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, s)
-                        : launch_rows_k<C, false, true>(X, Wf, bias, Y, Wpf, bias_p, Hx, g, s);
+            if (g.nct != 1 || Cp < 1 || Cp > 16 || aux.ln_g || aux.res) return hipErrorInvalidValue;
+            return launch_rows_tail<C, EPI_PROJ>(tail, X, Wf, bias, Y, Wpf, bias_p, Hx, g, aux, s);
+        }
+        if (aux.ln_g) {
+            if (g.nct != 1 || aux.res) return hipErrorInvalidValue;
+            return launch_rows_tail<C, EPI_NORM>(tail, X, Wf, bias, Y, nullptr, nullptr, Hx, g, aux, s);
         }
     }
-    return tail ? launch_rows_k<C, true, false>(X, Wf, bias, Y, nullptr, nullptr, Hx, g, s)
-                : launch_rows_k<C, false, false>(X, Wf, bias, Y, nullptr, nullptr, Hx, g, s);
+    if (Wpf || aux.ln_g) return hipErrorInvalidValue;
+    if constexpr (KIND == TEMPORAL3 && C::FA == 1) {  // residual epilogue on the plain temporal tiles
+        if (aux.res) return launch_rows_tail<C, EPI_RES>(tail, X, Wf, bias, Y, nullptr, nullptr, Hx, g, aux, s);
+    }
+    if (aux.res) return hipErrorInvalidValue;
+    return launch_rows_tail<C, EPI_PLAIN>(tail, X, Wf, bias, Y, nullptr, nullptr, Hx, g, aux, s);
 }
 
 template <int KIND>
 hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
                        int B, hipStream_t s, const uint16_t* Wpf = nullptr, const float* bias_p = nullptr,
-                       int Cp = 0, const uint16_t* Hx = nullptr) {
+                       int Cp = 0, const uint16_t* Hx = nullptr, const RowsAux& aux = RowsAux{}) {
     if constexpr (KIND == SPATIAL3)
-        return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr);
+        return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr, aux);
     if (cg.Cout <= TemporalNarrowCfg::TCH)
-        return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
-    if (Wpf) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
-    return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx);
+        return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
+    if (Wpf || aux.ln_g) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
+    return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
 }
 
+// Largest Cout whose temporal conv can take the NORM epilogue (all channels in one workgroup).
+constexpr int ROWS_NORM_MAX_C = TemporalProjCfg::TCH;
+
 hipError_t launch_igemm(int kind, const uint16_t* X, const uint16_t* Wp, const float* bias, uint16_t* Y,
-                        const ConvGeom& g, hipStream_t s) {
+                        const ConvGeom& g0, hipStream_t s) {
+    ConvGeom g = g0;
+    if (g.st == 0) {  // stride 1 on the output grid
+        g.Ti = g.T; g.Hi = g.H; g.Wi = g.W; g.st = 1; g.ss = 1;
+    }
+    if (g.ups) return hipErrorInvalidValue;
     if (kind == SPATIAL3) return launch_igemm_k<SPATIAL3>(X, Wp, bias, Y, g, s);
     if (kind == TEMPORAL3) return launch_igemm_k<TEMPORAL3>(X, Wp, bias, Y, g, s);
     return launch_igemm_k<POINT>(X, Wp, bias, Y, g, s);
@@ -1137,6 +1298,148 @@ hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const vo
     g.kchunks = (C + BK - 1) / BK;
     return launch_rows<TEMPORAL3>(static_cast<const uint16_t*>(x), wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp,
                                   b_p, w_p ? Cp : 0, static_cast<const uint16_t*>(hist));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Encoder and decoder blocks.
+
+// Residual block y = x + conv2(swish(LN2(conv1(swish(LN1(x)))))), conv = factorized causal
+// conv C -> C, k = 3.  Workspace: the four packed weights and two bf16 [P][C] buffers A, S.
+//   A = swish(LN1(x))                      (layernorm kernel)
+//   S = spatial1(A)
+//   A = swish(LN2(temporal1(S)))           (NORM epilogue; C > 256: plain conv + layernorm in place)
+//   S = spatial2(A)
+//   y = temporal2(S) + x                   (RES epilogue, one rounding)
+bool resblock_supported(int C, long long P) { return use_rows_kernel(3, C, P, C); }
+
+size_t resblock_workspace_bytes(int B, int C, int T, int H, int W) {
+    const size_t P = (size_t)B * T * H * W;
+    return 2 * pack_bytes(C, C, 9) + 2 * pack_bytes(C, C, 3) + 2 * align256(P * C * 2);
+}
+
+hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
+                           float eps, void* workspace, hipStream_t s) {
+    const long long P = (long long)B * T * H * W;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        uint8_t* q = ws + off;
+        off += n;
+        return reinterpret_cast<uint16_t*>(q);
+    };
+    uint16_t* w1s = take(pack_bytes(C, C, 9));
+    uint16_t* w1t = take(pack_bytes(C, C, 3));
+    uint16_t* w2s = take(pack_bytes(C, C, 9));
+    uint16_t* w2t = take(pack_bytes(C, C, 3));
+    uint16_t* A = take(align256((size_t)P * C * 2));
+    uint16_t* S = take(align256((size_t)P * C * 2));
+    hipError_t e;
+    if ((e = pack_frag(w.c1_s, w1s, C, C, 9, s)) != hipSuccess) return e;
+    if ((e = pack_frag(w.c1_t, w1t, C, C, 3, s)) != hipSuccess) return e;
+    if ((e = pack_frag(w.c2_s, w2s, C, C, 9, s)) != hipSuccess) return e;
+    if ((e = pack_frag(w.c2_t, w2t, C, C, 3, s)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = C; g.Cout = C;
+    g.kchunks = (C + BK - 1) / BK;
+    if ((e = launch_layernorm(x, w.ln1_g, w.ln1_b, A, P, C, eps, 1, s)) != hipSuccess) return e;
+    if ((e = launch_rows<SPATIAL3>(A, w1s, w.c1_bs, S, g, B, s)) != hipSuccess) return e;
+    if (C <= ROWS_NORM_MAX_C) {
+        RowsAux aux{};
+        aux.ln_g = w.ln2_g; aux.ln_b = w.ln2_b; aux.eps = eps; aux.swish = 1;
+        if ((e = launch_rows<TEMPORAL3>(S, w1t, w.c1_bt, A, g, B, s, nullptr, nullptr, 0, nullptr, aux)) != hipSuccess)
+            return e;
+    } else {
+        if ((e = launch_rows<TEMPORAL3>(S, w1t, w.c1_bt, A, g, B, s)) != hipSuccess) return e;
+        if ((e = launch_layernorm(A, w.ln2_g, w.ln2_b, A, P, C, eps, 1, s)) != hipSuccess) return e;
+    }
+    if ((e = launch_rows<SPATIAL3>(A, w2s, w.c2_bs, S, g, B, s)) != hipSuccess) return e;
+    RowsAux res{};
+    res.res = static_cast<const uint16_t*>(x);
+    return launch_rows<TEMPORAL3>(S, w2t, w.c2_bt, static_cast<uint16_t*>(y), g, B, s, nullptr, nullptr, 0, nullptr,
+                                  res);
+}
+
+// Downsampling block: the spatial 1x3x3 conv at stride 2 in H and W (zero padding 1), then
+// the causal temporal 3x1x1 conv at stride 2 (T = 1 + 2k -> 1 + k), either part optional,
+// on conv_igemm_kernel with the strided input mapping.
+size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time) {
+    size_t b = 0;
+    if (space) b += pack_bytes(Cout, Cin, 9);
+    if (time) b += pack_bytes(Cout, space ? Cout : Cin, 3);
+    if (space && time) b += align256((size_t)B * T * (H / 2) * (W / 2) * Cout * 2);
+    return b;
+}
+
+hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    size_t off = 0;
+    hipError_t e;
+    const uint16_t* tin = static_cast<const uint16_t*>(x);
+    int C1 = Cin, H1 = H, W1 = W;
+    if (w_s) {
+        uint16_t* wps = reinterpret_cast<uint16_t*>(ws + off);
+        off += pack_bytes(Cout, Cin, 9);
+        uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(ws + off + (w_t ? pack_bytes(Cout, Cout, 3) : 0))
+                          : static_cast<uint16_t*>(y);
+        if ((e = pack(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+        H1 = H / 2;
+        W1 = W / 2;
+        ConvGeom g{};
+        g.P = (long long)B * T * H1 * W1; g.T = T; g.H = H1; g.W = W1; g.Cin = Cin; g.Cout = Cout;
+        g.kchunks = (Cin + BK - 1) / BK;
+        g.Ti = T; g.Hi = H; g.Wi = W; g.st = 1; g.ss = 2;
+        if ((e = launch_igemm(SPATIAL3, tin, wps, b_s, S, g, s)) != hipSuccess) return e;
+        tin = S;
+        C1 = Cout;
+    }
+    if (!w_t) return hipSuccess;
+    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + off);
+    if ((e = pack(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
+    const int T1 = 1 + (T - 1) / 2;
+    ConvGeom g{};
+    g.P = (long long)B * T1 * H1 * W1; g.T = T1; g.H = H1; g.W = W1; g.Cin = C1; g.Cout = Cout;
+    g.kchunks = (C1 + BK - 1) / BK;
+    g.Ti = T; g.Hi = H1; g.Wi = W1; g.st = 2; g.ss = 1;
+    return launch_igemm(TEMPORAL3, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
+}
+
+// Decoder upsampling block: nearest-neighbour repetition (x2 in H and W and/or causal x2 in
+// time, T -> 2T - 1) followed by the factorized conv, with the repetition done by the conv's
+// region loads (conv_rows_kernel reads the low-resolution input through the upsampled
+// index), so the repeated tensor is never written.  The spatial conv runs on the T input
+// frames (it is frame-local, so repeating frames before or after it is the same), the
+// temporal conv reads those frames through the causal repetition.
+bool upsample_supported(int Cin, int Cout, long long P_in, long long P_mid) {
+    return use_rows_kernel(3, Cout, P_in, Cin) && use_rows_kernel(3, Cout, P_mid, Cout);
+}
+
+size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space) {
+    const int f = up_space ? 2 : 1;
+    return pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3) + align256((size_t)B * T * (f * H) * (f * W) * Cout * 2);
+}
+
+hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                           int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool up_time, void* workspace,
+                           hipStream_t s) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint16_t* wps = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + pack_bytes(Cout, Cin, 9));
+    uint16_t* S = reinterpret_cast<uint16_t*>(ws + pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3));
+    const int Ho = up_space ? 2 * H : H, Wo = up_space ? 2 * W : W, To = up_time ? 2 * T - 1 : T;
+    hipError_t e;
+    if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+    if ((e = pack_frag(w_t, wpt, Cout, Cout, 3, s)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = (long long)B * T * Ho * Wo; g.T = T; g.H = Ho; g.W = Wo; g.Cin = Cin; g.Cout = Cout;
+    g.kchunks = (Cin + BK - 1) / BK;
+    g.ups = up_space ? 1 : 0; g.Ti = T; g.Hi = H; g.Wi = W;
+    if ((e = launch_rows<SPATIAL3>(static_cast<const uint16_t*>(x), wps, b_s, S, g, B, s)) != hipSuccess) return e;
+    ConvGeom g2{};
+    g2.P = (long long)B * To * Ho * Wo; g2.T = To; g2.H = Ho; g2.W = Wo; g2.Cin = Cout; g2.Cout = Cout;
+    g2.kchunks = (Cout + BK - 1) / BK;
+    g2.ups = up_time ? 1 : 0; g2.Ti = T; g2.Hi = Ho; g2.Wi = Wo;
+    return launch_rows<TEMPORAL3>(S, wpt, b_t, static_cast<uint16_t*>(y), g2, B, s);
 }
 
 }  // namespace cvt

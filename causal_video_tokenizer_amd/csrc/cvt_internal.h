@@ -115,4 +115,22 @@ hipError_t launch_video_pad(const void* x, void* y, int dtype, int B, int C, int
 hipError_t launch_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int H, int W, int t0, int nt,
                               int Tp, int Hp, int Wp, hipStream_t s);
 
+// LayerNorm (+ Swish) over the channels of an NTHWC bf16 tensor (norm.hip); x == y allowed.
+hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, void* y, long long P, int C,
+                            float eps, int swish, hipStream_t s);
+
+// Encoder / decoder blocks (conv.hip).
+bool resblock_supported(int C, long long P);
+size_t resblock_workspace_bytes(int B, int C, int T, int H, int W);
+hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
+                           float eps, void* workspace, hipStream_t s);
+size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time);
+hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
+bool upsample_supported(int Cin, int Cout, long long P_in, long long P_mid);
+size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space);
+hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                           int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool up_time, void* workspace,
+                           hipStream_t s);
+
 }  // namespace cvt

@@ -1,0 +1,117 @@
+// LayerNorm over the channels of each position of an NTHWC bf16 tensor, with a
+// per-channel scale and shift and optional Swish - the normalization and activation of
+// the encoder's blocks ("Cosmos World Foundation Model Platform for Physical AI
+// (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer": Swish activations,
+// LayerNorm rather than GroupNorm).
+//
+// HBM-bound: a position's C channels are one contiguous row of 2C bytes.  G lanes (the
+// smallest power of two >= C/8, at most 64) share a row, each holding NCH 16-byte chunks in
+// registers, so the row is read once: the mean and then the centred squares are reduced
+// across the G lanes with butterfly exchanges, and the normalized row is written back with
+// the same 16-byte accesses.  A wave covers 64/G rows per step; all statistics are float32.
+// x and y may be the same buffer: every chunk is read before any store of its row.
+#include "cvt_internal.h"
+
+namespace cvt {
+
+namespace {
+
+template <int NCH>
+__global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* x, const float* __restrict__ gam,
+                                                        const float* __restrict__ bet, uint16_t* y,
+                                                        long long P, int C, int G, float eps, int swish) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / G, gl = lane - sub * G;
+    const int ppw = 64 / G;  // rows per wave step
+    const int cpr = C >> 3;   // 16-byte chunks per row
+    const float inv_n = 1.0f / (float)C;
+    float gg[NCH][8], bb[NCH][8];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int ch = gl + k * G;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            gg[k][e] = ch < cpr ? gam[ch * 8 + e] : 0.0f;
+            bb[k][e] = ch < cpr ? bet[ch * 8 + e] : 0.0f;
+        }
+    }
+    const long long nw = (long long)gridDim.x * 4;
+    for (long long p0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * ppw; p0 < P; p0 += nw * ppw) {
+        const long long p = p0 + sub;
+        const bool prow = p < P;
+        float v[NCH][8];
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int ch = gl + k * G;
+            uint4 u = make_uint4(0u, 0u, 0u, 0u);
+            if (prow && ch < cpr) u = ld_stream16(x + p * C + ch * 8);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[k][2 * e] = bf16_lo(w[e]);
+                v[k][2 * e + 1] = bf16_hi(w[e]);
+                sum += v[k][2 * e] + v[k][2 * e + 1];
+            }
+        }
+        for (int m = 1; m < G; m <<= 1) sum += __shfl_xor(sum, m);
+        const float mean = sum * inv_n;
+        float sq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            if (gl + k * G < cpr) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = v[k][e] - mean;
+                    sq += d * d;
+                }
+            }
+        }
+        for (int m = 1; m < G; m <<= 1) sq += __shfl_xor(sq, m);
+        const float rstd = rsqrtf(sq * inv_n + eps);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int ch = gl + k * G;
+            if (prow && ch < cpr) {
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float y0 = (v[k][2 * e] - mean) * rstd * gg[k][2 * e] + bb[k][2 * e];
+                    float y1 = (v[k][2 * e + 1] - mean) * rstd * gg[k][2 * e + 1] + bb[k][2 * e + 1];
+                    if (swish) {
+                        y0 = y0 / (1.0f + __expf(-y0));
+                        y1 = y1 / (1.0f + __expf(-y1));
+                    }
+                    o[e] = pack_bf16x2(y0, y1);
+                }
+                *reinterpret_cast<uint4*>(y + p * C + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, void* y, long long P, int C,
+                            float eps, int swish, hipStream_t s) {
+    const int cpr = C / 8;
+    int G = 1;
+    while (G < cpr && G < 64) G <<= 1;
+    const int nch = (cpr + 63) / 64;
+    const long long rows_per_block = 4LL * (64 / G);
+    const long long nblk = std::min((P + rows_per_block - 1) / rows_per_block, 16384LL);
+    const dim3 grid((unsigned)nblk), block(256);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint16_t* ys = static_cast<uint16_t*>(y);
+    if (nch == 1)
+        hipLaunchKernelGGL(layernorm_kernel<1>, grid, block, 0, s, xs, gamma, beta, ys, P, C, G, eps, swish);
+    else if (nch == 2)
+        hipLaunchKernelGGL(layernorm_kernel<2>, grid, block, 0, s, xs, gamma, beta, ys, P, C, G, eps, swish);
+    else if (nch <= 4)
+        hipLaunchKernelGGL(layernorm_kernel<4>, grid, block, 0, s, xs, gamma, beta, ys, P, C, G, eps, swish);
+    else
+        hipLaunchKernelGGL(layernorm_kernel<8>, grid, block, 0, s, xs, gamma, beta, ys, P, C, G, eps, swish);
+    return hipGetLastError();
+}
+
+}  // namespace cvt

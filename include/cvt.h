@@ -338,6 +338,101 @@ int cvt_video_pad(const void* x, void* y, int dtype, int B, int C, int T, int H,
 int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int H, int W, int t0, int nt, int Tp,
                     int Hp, int Wp, void* stream);
 
+/*
+ * Encoder and decoder blocks.
+ *
+ * Defined by: "Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)" summary, section "1) Cosmos Tokenizer" (after the Haar
+ * transform the encoder is residual blocks and downsampling blocks built from
+ * the factorized causal convolution, with Swish activations and LayerNorm
+ * rather than GroupNorm; the video compression factors are 4x8x8, 8x8x8 and
+ * 8x16x16) and the CV8x8x8-720p model card, "Model Architecture" (the decoder
+ * mirrors the encoder).  The pages give no block diagram; the readings taken:
+ * LayerNorm normalizes the C channels of each position (biased variance, eps
+ * inside the square root) and applies a per-channel scale and shift;
+ * Swish(x) = x * sigmoid(x); the residual block is the pre-activation form;
+ * downsampling is the factorized conv at stride 2; upsampling is
+ * nearest-neighbour repetition followed by the factorized conv.
+ *
+ * All tensors are bf16 NTHWC [B, C, T, H, W] (torch channels_last_3d), 16-byte
+ * aligned; scales, shifts and biases float32 (scales and shifts 16-byte
+ * aligned); conv weights bf16 in torch's [Cout, Cin, kT, kH, kW] order.
+ * Outputs must not overlap inputs.  Arithmetic is float32 with bf16
+ * intermediates between the steps listed.
+ */
+
+/*
+ * y = LN(x) * gamma + beta over the C channels of each position, then Swish if
+ * swish != 0.  y may equal x.  Errors: CVT_E_NULL; CVT_E_SHAPE for a
+ * non-positive size, C not a multiple of 8 or above 4096; CVT_E_ALIGN.
+ */
+int cvt_layernorm3d(const void* x, const float* gamma, const float* beta, void* y, int B, int C, int T, int H,
+                    int W, float eps, int swish, void* stream);
+
+/* Weights of one residual block over C channels. */
+typedef struct cvt_resblock_weights {
+    const float* ln1_g; /* [C] scale and shift of the first LayerNorm */
+    const float* ln1_b;
+    const void* c1_s;   /* bf16 [C, C, 1, 3, 3]: first factorized conv, spatial part */
+    const void* c1_t;   /* bf16 [C, C, 3, 1, 1]: its causal temporal part */
+    const float* c1_bs; /* [C] or NULL */
+    const float* c1_bt; /* [C] or NULL */
+    const float* ln2_g; /* second LayerNorm */
+    const float* ln2_b;
+    const void* c2_s;   /* second factorized conv */
+    const void* c2_t;
+    const float* c2_bs;
+    const float* c2_bt;
+} cvt_resblock_weights;
+
+/*
+ * Residual block: y = x + conv2(swish(LN2(conv1(swish(LN1(x)))))), conv = the
+ * factorized causal conv C -> C with k = 3 (1x3x3 zero padding 1, then 3x1x1
+ * with two zero frames in front).  The second LayerNorm and Swish run in the
+ * first conv's epilogue for C <= 256, the residual add in the second conv's
+ * epilogue (one rounding).
+ * workspace: cvt_resblock3d_workspace(B, C, T, H, W) bytes, caller-owned.
+ * Errors: CVT_E_NULL for a NULL tensor, weight or scale/shift; CVT_E_SHAPE for
+ * a non-positive size, C < 64, C not a multiple of 8 or a tensor of 2 GiB or
+ * more; CVT_E_ALIGN; CVT_E_WORKSPACE.
+ */
+size_t cvt_resblock3d_workspace(int B, int C, int T, int H, int W);
+int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W,
+                   float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Downsampling block: the 1x3x3 conv Cin -> Cout at stride 2 in H and W (zero
+ * padding 1: H, W -> H/2, W/2), then the causal 3x1x1 conv at stride 2 in time
+ * (two zero frames in front: T = 1 + 2k -> 1 + k, output frame 0 from frame 0
+ * alone, output frame j from frames 2j-2 .. 2j).  Either weight may be NULL to
+ * skip that part (w_t is then [Cout, Cin, 3, 1, 1] when w_s is NULL).
+ * x: [B, Cin, T, H, W]; y: [B, Cout, T', H', W'].
+ * parts for the workspace query: CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL.
+ * Errors: CVT_E_NULL (both weights NULL); CVT_E_SHAPE for a non-positive
+ * size, Cin not a multiple of 8, odd H or W with w_s, T not 1 + 2k with w_t;
+ * CVT_E_ALIGN; CVT_E_WORKSPACE.
+ */
+size_t cvt_downsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int parts);
+int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                     int B, int Cin, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Upsampling block (the decoder's mirror of downsampling): nearest-neighbour
+ * repetition x2 in H and W (up_space) and/or causal repetition in time
+ * (up_time: frame 0 once, every later frame twice, T -> 2T - 1), then the
+ * factorized conv Cin -> Cout (w_s [Cout, Cin, 1, 3, 3], w_t [Cout, Cout, 3,
+ * 1, 1], both required).  The repetition happens inside the conv's loads.
+ * x: [B, Cin, T, H, W]; y: [B, Cout, T', 2H or H, 2W or W].
+ * Errors: CVT_E_NULL; CVT_E_SHAPE for a non-positive size, Cin or Cout not a
+ * multiple of 8, Cout < 64 or a tensor of 2 GiB or more; CVT_E_ALIGN;
+ * CVT_E_WORKSPACE.
+ */
+size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time);
+int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                   int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

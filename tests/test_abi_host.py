@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 17
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -240,3 +240,48 @@ def test_video_pad_validation():
     assert pad(y=MIS) == E_ALIGN
     assert lib.cvt_video_unpad(A, B_, 1, 1, 3, 40, 30, 50, 34, 7, 9, 32, 56, None) == E_SHAPE
     assert lib.cvt_video_unpad(MIS, B_, 1, 1, 3, 40, 30, 50, 34, 6, 9, 32, 56, None) == E_ALIGN
+
+
+def test_block_validation():
+    F = ctypes.c_void_p(0x700000)
+    assert lib.cvt_layernorm3d(None, F, F, B_, 1, 256, 2, 4, 4, 1e-6, 1, None) == E_NULL
+    assert lib.cvt_layernorm3d(A, F, F, B_, 1, 252, 2, 4, 4, 1e-6, 1, None) == E_SHAPE
+    assert lib.cvt_layernorm3d(A, ctypes.c_void_p(0x700004), F, B_, 1, 256, 2, 4, 4, 1e-6, 1, None) == E_ALIGN
+
+    w = cvt.ResblockWeights(*([0x700000] * 12))
+    need = lib.cvt_resblock3d_workspace(1, 256, 5, 8, 8)
+    assert need >= 2 * 256 * 256 * 12 * 2
+    wk = ctypes.c_void_p(0x800000)
+
+    def rb(**kw):
+        return lib.cvt_resblock3d(kw.get("x", A), ctypes.byref(kw.get("w", w)), B_, 1, kw.get("C", 256), 5, 8, 8,
+                                  1e-6, kw.get("work", wk), kw.get("wsb", need), None)
+    bad = cvt.ResblockWeights(*([0x700000] * 12))
+    bad.c2_t = None
+    assert rb(w=bad) == E_NULL
+    assert rb(C=48) == E_SHAPE
+    assert rb(C=260) == E_SHAPE
+    assert rb(wsb=need - 1) == E_WORKSPACE
+    assert rb(x=MIS) == E_ALIGN
+    odd = cvt.ResblockWeights(*([0x700000] * 12))
+    odd.ln2_b = 0x700004
+    assert rb(w=odd) == E_ALIGN
+
+    def ds(**kw):
+        return lib.cvt_downsample3d(A, kw.get("ws", C_), kw.get("wt", C_), None, None, B_, 1, kw.get("Cin", 64), 64,
+                                    kw.get("T", 5), kw.get("H", 8), 8, wk, kw.get("wsb", 1 << 30), None)
+    assert ds(ws=None, wt=None) == E_NULL
+    assert ds(T=4) == E_SHAPE                # not 1 + 2k
+    assert ds(H=7) == E_SHAPE                # odd height with the spatial part
+    assert ds(Cin=60) == E_SHAPE
+    assert ds(wsb=10) == E_WORKSPACE
+    assert lib.cvt_downsample3d_workspace(1, 64, 64, 5, 8, 8, 0) == 0
+
+    def us(**kw):
+        return lib.cvt_upsample3d(A, kw.get("ws", C_), C_, None, None, B_, 1, 64, kw.get("Cout", 64), 3, 4, 4, 1, 1,
+                                  wk, kw.get("wsb", 1 << 30), None)
+    assert us(ws=None) == E_NULL
+    assert us(Cout=32) == E_SHAPE
+    assert us(wsb=10) == E_WORKSPACE
+    assert lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4, 4, 1, 1) > lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4,
+                                                                                                   4, 0, 1)
