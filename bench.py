@@ -23,7 +23,8 @@ convolution's MFMA fraction is quoted; a third, FSQ quantize and dequantize at a
 bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak; a fourth,
 the factorized self-attention (spatial and causal temporal) on the 16 x 90 x 160 token
 grid of the CV8x8x8-720p model, 256 channels in 4 heads; a fifth, sliding windows of 17
-frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop).
+frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop); a sixth, the encoder's
+residual and downsampling blocks and the decoder's upsampling block on the CV8x8x8-720p grids.
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -68,6 +69,7 @@ def parse():
     ap.add_argument("--no-fsq-bw", action="store_true", help="skip the FSQ bandwidth-size measurement")
     ap.add_argument("--no-attention", action="store_true", help="skip the factorized-attention measurement")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window measurement")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the encoder/decoder block measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -194,6 +196,7 @@ def main():
     fsq_bw = None if args.no_fsq_bw else fsq_bandwidth(cvt, si, torch, dev, args)
     attn = None if args.no_attention else attention_tokens(cvt, si, torch, dev, args)
     win = None if args.no_window else windowed_1080p(cvt, si, torch, dev, args)
+    blk = None if args.no_blocks else blocks_cv8x8x8(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -232,6 +235,7 @@ def main():
         "fsq_bandwidth_size": fsq_bw,
         "attention_cv8x8x8_720p_tokens": attn,
         "window_1080p_50f": win,
+        "blocks_cv8x8x8_720p": blk,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -481,6 +485,71 @@ def windowed_1080p(cvt, si, torch, dev, args):
     del x, out, bufs, coef, rec
     torch.cuda.empty_cache()
     return res
+
+
+def blocks_cv8x8x8(cvt, si, torch, dev, args):
+    """Encoder and decoder blocks on the CV8x8x8-720p grids of a 121-frame clip, 256 channels:
+    the residual block at the post-Haar grid 31 x 180 x 320 (LayerNorm + Swish, two
+    factorized convs, LayerNorm + Swish and the residual add fused into the temporal convs),
+    the stride-2 downsampling block to 16 x 90 x 160, and the decoder's upsampling block back
+    (repetition inside the conv loads).  FLOP = 2 * taps * Cin * Cout per output position of
+    each conv; timed over back-to-back calls with HIP events."""
+    wl = si.WORKLOADS["blocks_cv8x8x8_720p"]
+    B, C, T, H, W = wl["x"]
+    _, _, Tl, Hl, Wl = wl["low"]
+    seed, std = wl["seed"], wl["w_std"]
+    log(f"blocks: generating {wl['x']} ...")
+
+    def bf(shape, sd, s_):
+        bits = si.to_bf16_bits(si.normal(shape, sd, s_))
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf((B, C, T, H, W), seed, 1.0).to(memory_format=torch.channels_last_3d)
+    xl = bf((B, C, Tl, Hl, Wl), seed + 1, 1.0).to(memory_format=torch.channels_last_3d)
+    ones = torch.ones(C, dtype=torch.float32, device=dev)
+    zeros = torch.zeros(C, dtype=torch.float32, device=dev)
+    p = {"ln1_g": ones, "ln1_b": zeros, "ln2_g": ones, "ln2_b": zeros,
+         "c1_s": bf((C, C, 1, 3, 3), seed + 2, std), "c1_t": bf((C, C, 3, 1, 1), seed + 3, std),
+         "c2_s": bf((C, C, 1, 3, 3), seed + 4, std), "c2_t": bf((C, C, 3, 1, 1), seed + 5, std)}
+    ds_s, ds_t = bf((C, C, 1, 3, 3), seed + 6, std), bf((C, C, 3, 1, 1), seed + 7, std)
+    us_s, us_t = bf((C, C, 1, 3, 3), seed + 8, std), bf((C, C, 3, 1, 1), seed + 9, std)
+    y = torch.empty_like(x)
+    yd = torch.empty_like(xl)
+    yu = torch.empty_like(x)
+    ws_r = torch.empty(int(cvt.lib.cvt_resblock3d_workspace(B, C, T, H, W)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(int(cvt.lib.cvt_downsample3d_workspace(B, C, C, T, H, W, 3)), dtype=torch.uint8, device=dev)
+    ws_u = torch.empty(int(cvt.lib.cvt_upsample3d_workspace(B, C, C, Tl, Hl, Wl, 1, 1)), dtype=torch.uint8,
+                       device=dev)
+    P = B * T * H * W
+    conv = 2.0 * C * C * (9 + 3)
+    calls = {
+        "resblock_31x180x320": (lambda: cvt.resblock3d(x, p, workspace=ws_r, out=y), 2 * conv * P),
+        "downsample_to_16x90x160": (lambda: cvt.downsample3d(x, ds_s, ds_t, workspace=ws_d, out=yd),
+                                    2.0 * C * C * 9 * B * T * Hl * Wl + 2.0 * C * C * 3 * B * Tl * Hl * Wl),
+        "upsample_to_31x180x320": (lambda: cvt.upsample3d(xl, us_s, us_t, workspace=ws_u, out=yu),
+                                   2.0 * C * C * 9 * B * Tl * H * W + 2.0 * C * C * 3 * P),
+    }
+    for _ in range(max(3, min(args.warmup, 10))):
+        for fn, _ in calls.values():
+            fn()
+    torch.cuda.synchronize()
+    reps = max(5, args.steps // 2)
+    out = {"grid": [T, H, W], "low_grid": [Tl, Hl, Wl], "channels": C}
+    for name, (fn, flops) in calls.items():
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "flops": flops, "TFLOPs": round(tf, 1),
+                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del x, xl, y, yd, yu, ws_r, ws_d, ws_u, p
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):
