@@ -56,6 +56,9 @@ SIGNATURES = {
     "cvt_video_window": (_ci, [_ci] * 7 + [_pi] * 6),
     "cvt_video_pad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
     "cvt_video_unpad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
+    "cvt_causal_conv3d_fact_proj_fsq_workspace": (_sz, [_ci] * 9),
+    "cvt_causal_conv3d_fact_proj_fsq": (_ci, [_vp] * 7 + [_vp, _ci, _vp, _vp] + [_ci] * 7 + [_vp, _sz, _vp]),
+    "cvt_fsq_dequantize_proj": (_ci, [_vp, _vp, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "cvt_layernorm3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _ci, _vp]),
     "cvt_resblock3d_workspace": (_sz, [_ci] * 5),
     "cvt_resblock3d": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _vp, _sz, _vp]),
@@ -560,4 +563,65 @@ def upsample3d(x, w_s, w_t, b_s=None, b_t=None, space=True, time=True, workspace
     _check(lib.cvt_upsample3d(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout, T, H, W,
                               int(space), int(time), _ptr(workspace), workspace.numel(), _stream(x.device)),
            "upsample3d")
+    return y
+
+
+def causal_conv3d_fact_proj_fsq(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, levels=DEFAULT_LEVELS,
+                                return_latent=False, workspace=None, indices=None, latent=None):
+    """causal_conv3d_fact_proj to the D = len(levels) latent, then FSQ, in one pass where
+    the projection is fused: returns int32 indices [B, T, H, W] (and the bf16 NTHWC latent
+    when return_latent).  Bit-identical to fsq_quantize(causal_conv3d_fact_proj(...))."""
+    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p)
+    if not x.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError("x must be channels_last_3d (NTHWC)")
+    B, Cin, T, H, W = x.shape
+    if w_s is not None:
+        Cout, k = w_s.shape[0], w_s.shape[3]
+    elif w_t is not None:
+        Cout, k = w_t.shape[0], w_t.shape[2]
+    else:
+        raise ValueError("at least one of w_s and w_t is needed")
+    D = len(levels)
+    if tuple(w_p.shape) != (D, Cout, 1, 1, 1):
+        raise ValueError("w_p must be [len(levels), Cout, 1, 1, 1]")
+    for w in (w_s, w_t, w_p):
+        if w is not None and (w.dtype != torch.bfloat16 or not w.is_contiguous()):
+            raise ValueError("weights must be contiguous bfloat16")
+    for bias, n in ((b_s, Cout), (b_t, Cout), (b_p, D)):
+        _f32_vec(bias, n, "bias")
+    parts = (CVT_CONV_SPATIAL if w_s is not None else 0) | (CVT_CONV_TEMPORAL if w_t is not None else 0)
+    need = int(lib.cvt_causal_conv3d_fact_proj_fsq_workspace(B, Cin, Cout, D, T, H, W, k, parts))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    idx = (_check_out(indices, (B, T, H, W), torch.int32, x.device, what="indices") if indices is not None
+           else torch.empty((B, T, H, W), dtype=torch.int32, device=x.device))
+    lat = None
+    if return_latent or latent is not None:
+        lat = (_check_out(latent, (B, D, T, H, W), torch.bfloat16, x.device, CVT_NTHWC, what="latent")
+               if latent is not None else _empty5((B, D, T, H, W), torch.bfloat16, x.device, CVT_NTHWC))
+    arr, n = _levels_arg(levels)
+    _check(lib.cvt_causal_conv3d_fact_proj_fsq(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(w_p),
+                                               _ptr(b_p), arr, n, _ptr(lat), _ptr(idx), B, Cin, Cout, T, H, W, k,
+                                               _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "causal_conv3d_fact_proj_fsq")
+    return (idx, lat) if return_latent else idx
+
+
+def fsq_dequantize_proj(indices, w_p, b_p=None, levels=DEFAULT_LEVELS, invalid_count=None, out=None):
+    """FSQ dequantize + the 1x1 projection D -> Cout in one kernel: int32 indices
+    [B, T, H, W] -> bf16 NTHWC [B, Cout, T, H, W] (w_p bf16 [Cout, D, 1, 1, 1])."""
+    _require_gpu(indices, w_p, b_p, invalid_count)
+    if indices.dtype != torch.int32 or not indices.is_contiguous():
+        raise ValueError("indices must be contiguous int32 [B, T, H, W]")
+    B, T, H, W = indices.shape
+    D = len(levels)
+    Cout = w_p.shape[0]
+    _bf16_w(w_p, (Cout, D, 1, 1, 1), "w_p")
+    _f32_vec(b_p, Cout, "b_p")
+    shape = (B, Cout, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, indices.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, indices.device, CVT_NTHWC))
+    arr, n = _levels_arg(levels)
+    _check(lib.cvt_fsq_dequantize_proj(_ptr(indices), arr, n, _ptr(w_p), _ptr(b_p), _ptr(y), B, Cout, T, H, W,
+                                       _ptr(invalid_count), _stream(indices.device)), "fsq_dequantize_proj")
     return y

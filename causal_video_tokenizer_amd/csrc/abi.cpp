@@ -468,4 +468,66 @@ int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float*
                       "cvt_upsample3d launch");
 }
 
+size_t cvt_causal_conv3d_fact_proj_fsq_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k,
+                                                 int parts) {
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || Cp <= 0 || T <= 0 || H <= 0 || W <= 0 || (k != 1 && k != 3)) return 0;
+    if (parts < 1 || parts > 3) return 0;
+    return cvt::conv_proj_fsq_workspace_bytes(B, Cin, Cout, Cp, T, H, W, k, (parts & CVT_CONV_SPATIAL) != 0,
+                                              (parts & CVT_CONV_TEMPORAL) != 0);
+}
+
+int cvt_causal_conv3d_fact_proj_fsq(const void* x, const void* w_s, const void* w_t, const float* b_s,
+                                    const float* b_t, const void* w_p, const float* b_p, const int32_t* levels, int D,
+                                    void* y, int32_t* indices, int B, int Cin, int Cout, int T, int H, int W, int k,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !w_p || !indices) return fail(CVT_E_NULL, "x, w_p and indices must not be NULL");
+    if (!w_s && !w_t) return fail(CVT_E_NULL, "at least one of w_s and w_t must be given");
+    cvt::FsqParams p;
+    const int st = fsq_params(levels, D, &p);
+    if (st != CVT_OK) return st;
+    const int Cp = D;
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (k != 1 && k != 3) return fail(CVT_E_SHAPE, "k must be 1 or 3, got %d", k);
+    if (Cout > 4096) return fail(CVT_E_SHAPE, "Cout must be at most 4096, got %d", Cout);
+    if (!w_s && Cin != Cout)
+        return fail(CVT_E_SHAPE, "a temporal-only call needs Cin == Cout (got %d and %d)", Cin, Cout);
+    if (Cin % 8 != 0) return fail(CVT_E_SHAPE, "Cin must be a multiple of 8, got %d", Cin);
+    if (Cout % 8 != 0) return fail(CVT_E_SHAPE, "Cout must be a multiple of 8, got %d", Cout);
+    if (!aligned16(x) || (y && !aligned16(y)) || !aligned16(indices))
+        return fail(CVT_E_ALIGN, "x, y and indices must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u) ||
+        (reinterpret_cast<uintptr_t>(w_p) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)) ||
+        (b_p && (reinterpret_cast<uintptr_t>(b_p) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need =
+        cvt::conv_proj_fsq_workspace_bytes(B, Cin, Cout, Cp, T, H, W, k, w_s != nullptr, w_t != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_conv_fact_proj(x, w_s, w_t, b_s, b_t, w_p, b_p, y, B, Cin, Cout, Cp, T, H, W, k,
+                                                 workspace, (hipStream_t)stream, indices, &p),
+                      "cvt_causal_conv3d_fact_proj_fsq launch");
+}
+
+int cvt_fsq_dequantize_proj(const int32_t* indices, const int32_t* levels, int D, const void* w_p, const float* b_p,
+                            void* y, int B, int Cout, int T, int H, int W, int32_t* d_invalid_count, void* stream) {
+    if (!indices || !w_p || !y) return fail(CVT_E_NULL, "indices, w_p and y must not be NULL");
+    cvt::FsqParams p;
+    const int st = fsq_params(levels, D, &p);
+    if (st != CVT_OK) return st;
+    if (B <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (Cout > 4096) return fail(CVT_E_SHAPE, "Cout must be at most 4096, got %d", Cout);
+    if (!aligned16(indices) || !aligned16(y)) return fail(CVT_E_ALIGN, "indices and y must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(w_p) & 1u) return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if (b_p && (reinterpret_cast<uintptr_t>(b_p) & 3u)) return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    if (d_invalid_count && (reinterpret_cast<uintptr_t>(d_invalid_count) & 3u))
+        return fail(CVT_E_ALIGN, "the invalid counter must be 4-byte aligned");
+    return hip_status(cvt::launch_fsq_dequant_proj(indices, p, w_p, b_p, y, (long long)B * T * H * W, Cout,
+                                                   d_invalid_count, (hipStream_t)stream),
+                      "cvt_fsq_dequantize_proj launch");
+}
+
 }  // extern "C"

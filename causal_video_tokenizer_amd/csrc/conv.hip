@@ -302,6 +302,8 @@ struct RowsAux {
     const float* ln_b;
     float eps;             // NORM: added to the variance
     int swish;             // NORM: apply Swish after the affine step
+    int32_t* fsq_idx;      // PROJ: FSQ indices of the projected latent (nullptr = none)
+    FsqParams fsq;         // PROJ with fsq_idx: the level set (D = Cp <= 8)
 };
 
 // LDS bytes per region row: BK channels + 16 bytes of padding
@@ -711,7 +713,31 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                                                                pacc, 0, 0, 0);
             // element r < 8 is projection output 8 (r / 4) + 4 khalf + r % 4 at column px
             const int hw = c0 + cblk * 32 + px;
-            if (hw < g.HW) {
+            if (aux.fsq_idx) {  // FSQ of the bf16 latent: lane khalf = 0 gathers outputs 4..7 from lane + 32
+                float lat[4], up[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lat[r] = bf16_to_f32(f32_to_bf16(pacc[r] + bp[r]));
+                    up[r] = __shfl_xor(lat[r], 32);
+                }
+                if (khalf == 0 && hw < g.HW) {
+                    const float z[8] = {lat[0], lat[1], lat[2], lat[3], up[0], up[1], up[2], up[3]};
+                    int acc = 0;
+                    bool nan = false;
+#pragma unroll
+                    for (int i = 0; i < FSQ_MAX_D; ++i) {
+                        if (i < aux.fsq.D) {
+                            int d = 0;
+#pragma unroll
+                            for (int j = 0; j < FSQ_MAX_L - 1; ++j) d += (z[i] >= aux.fsq.thr[i][j]) ? 1 : 0;  // NaN pads
+                            acc += d * aux.fsq.basis[i];
+                            nan |= z[i] != z[i];
+                        }
+                    }
+                    aux.fsq_idx[((long long)b * g.T + r0 + fr) * g.HW + hw] = nan ? -1 : acc;
+                }
+            }
+            if (Y && hw < g.HW) {
                 uint16_t* yp = Y + (((long long)b * g.T + r0 + fr) * g.HW + hw) * Cp;
                 if ((Cp & 3) == 0) {  // 4 consecutive outputs per 8-byte store
 #pragma unroll
@@ -933,6 +959,71 @@ __global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __
 #pragma unroll
             for (int c = 0; c < 16; ++c)
                 if (c < Cin) a = fmaf(bf16_to_f32(w[(size_t)n * Cin + c]), xv[c], a);
+        }
+        o[e] = a;
+    }
+    uint16_t* yrow = Y + (size_t)pos * Cout;
+    if ((Cout & 7) == 0) {
+        uint4 u;
+        u.x = pack_bf16x2(o[0], o[1]);
+        u.y = pack_bf16x2(o[2], o[3]);
+        u.z = pack_bf16x2(o[4], o[5]);
+        u.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4*>(yrow + n0) = u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (n0 + e < Cout) yrow[n0 + e] = f32_to_bf16(o[e]);
+    }
+}
+
+// FSQ dequantize fused with the 1x1 projection D -> Cout that follows it in the decoder:
+// thread = (position, 8 output channels).  The index is split into digits by exact
+// multiply-shift divisions, each code (d - L/2) / (L/2) is rounded to bf16 (what the
+// dequantize kernel stores) and the projection accumulates exactly as
+// pointwise_small_kernel does, so the result is bit-identical to the two kernels in a row
+// while the D-channel codes never reach HBM.  An index outside [0, codebook) gives NaN
+// outputs and is counted once per position in *invalid (one atomic per wave).
+__global__ __launch_bounds__(256) void fsq_dequant_proj_kernel(const int32_t* __restrict__ idx, FsqParams p,
+                                                               const uint16_t* __restrict__ w,
+                                                               const float* __restrict__ bias,
+                                                               uint16_t* __restrict__ Y, long long P, int Cout,
+                                                               int32_t* __restrict__ invalid) {
+    const int ng = (Cout + 7) / 8;
+    const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = item < P * ng;
+    const long long pos = live ? item / ng : 0;
+    const int n0 = (int)(item - pos * ng) * 8;
+    const int id = live ? idx[pos] : 0;
+    const bool bad = id < 0 || id >= p.codebook;
+    if (invalid) {
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(live && bad && n0 == 0);
+        if (m && (threadIdx.x & 63) == (int)__builtin_ctzll(m)) atomicAdd(invalid, (int)__builtin_popcountll(m));
+    }
+    if (!live) return;
+    uint32_t rem = bad ? 0u : (uint32_t)id;
+    float xv[FSQ_MAX_D];
+#pragma unroll
+    for (int i = 0; i < FSQ_MAX_D; ++i) {
+        xv[i] = 0.0f;
+        if (i < p.D) {
+            const uint32_t q = div_magic(rem, p.magic[i], p.shift[i]);
+            const int d = (int)(rem - q * (uint32_t)p.levels[i]);
+            rem = q;
+            const float code = (float)(d - p.half[i]) / (float)p.half[i];
+            xv[i] = bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code));
+        }
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int n = n0 + e;
+        float a = 0.0f;
+        if (n < Cout) {
+            a = bias ? bias[n] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < FSQ_MAX_D; ++c)
+                if (c < p.D) a = fmaf(bf16_to_f32(w[(size_t)n * p.D + c]), xv[c], a);
         }
         o[e] = a;
     }
@@ -1236,12 +1327,28 @@ size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H,
            conv_workspace_bytes(B, Cout, Cp, T, H, W, 1, true, false);
 }
 
+size_t conv_proj_fsq_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
+                                     bool temporal) {
+    return conv_proj_workspace_bytes(B, Cin, Cout, Cp, T, H, W, k, spatial, temporal) +
+           align256((size_t)B * T * H * W * Cp * 2);
+}
+
 hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
                                  const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp, int T,
-                                 int H, int W, int k, void* workspace, hipStream_t s) {
+                                 int H, int W, int k, void* workspace, hipStream_t s, int32_t* idx,
+                                 const FsqParams* fsq) {
     const long long P = (long long)B * T * H * W;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     hipError_t e;
+    if (idx && (!proj_fused(k, Cout, Cp, P, w_t != nullptr) || Cp > 8)) {
+        // the unfused route: the latent (into y, or the workspace's last buffer), then FSQ
+        const size_t base = conv_proj_workspace_bytes(B, Cin, Cout, Cp, T, H, W, k, w_s != nullptr, w_t != nullptr);
+        void* lat = y ? y : static_cast<void*>(ws + base);
+        if ((e = launch_conv_fact_proj(x, w_s, w_t, b_s, b_t, w_p, b_p, lat, B, Cin, Cout, Cp, T, H, W, k, ws, s)) !=
+            hipSuccess)
+            return e;
+        return launch_fsq_quantize(lat, CVT_BF16, CVT_NTHWC, idx, nullptr, *fsq, B, (long long)T * H * W, s);
+    }
     if (!proj_fused(k, Cout, Cp, P, w_t != nullptr)) {
         // conv into the workspace, then the 1x1 projection
         size_t off = conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
@@ -1270,7 +1377,12 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
     ConvGeom g{};
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
     g.kchunks = (Cout + BK - 1) / BK;
-    return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp, b_p, Cp);
+    RowsAux aux{};
+    if (idx) {
+        aux.fsq_idx = idx;
+        aux.fsq = *fsq;
+    }
+    return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp, b_p, Cp, nullptr, aux);
 }
 
 // Causal temporal convolution of one chunk of a stream (optionally with the fused 1x1
@@ -1440,6 +1552,16 @@ hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, cons
     g2.kchunks = (Cout + BK - 1) / BK;
     g2.ups = up_time ? 1 : 0; g2.Ti = T; g2.Hi = Ho; g2.Wi = Wo;
     return launch_rows<TEMPORAL3>(S, wpt, b_t, static_cast<uint16_t*>(y), g2, B, s);
+}
+
+hipError_t launch_fsq_dequant_proj(const int32_t* idx, const FsqParams& p, const void* w_p, const float* b_p, void* y,
+                                   long long P, int Cout, int32_t* invalid, hipStream_t s) {
+    const long long items = P * ((Cout + 7) / 8);
+    const long long nblk = (items + 255) / 256;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fsq_dequant_proj_kernel, dim3((unsigned)nblk), dim3(256), 0, s, idx, p,
+                       static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
+    return hipGetLastError();
 }
 
 }  // namespace cvt

@@ -75,6 +75,14 @@ struct FsqParams {
     int codebook;                           // product of the levels
 };
 
+// Exact floor(n / L) for 0 <= n < 2^31 and 2 <= L <= 16.  With l = ceil(log2 L),
+// M = ceil(2^(31+l) / L) < 2^32 and n M / 2^(31+l) exceeds n / L by less than
+// n / 2^(31+l) < 2^-l <= 1/L, the smallest gap between n / L and the next
+// integer, so floor(mulhi(n, M) / 2^(l-1)) = floor(n / L).
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, int sh) {
+    return __umulhi(n, M) >> sh;
+}
+
 hipError_t launch_fsq_quantize(const void* z, int z_dtype, int z_layout, int32_t* idx, void* codes,
                                const FsqParams& p, long long B, long long npos_per_b,
                                hipStream_t stream);
@@ -90,9 +98,19 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
 // Factorized causal convolution followed by a 1x1x1 projection to Cp channels.
 size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
                                  bool temporal);
+// With idx (and fsq), FSQ of the projected latent too: the indices are computed in the
+// projection's epilogue where it is fused (y may then be nullptr), else by the FSQ kernel
+// on the latent; the workspace is then conv_proj_fsq_workspace_bytes.
 hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
                                  const void* w_p, const float* b_p, void* y, int B, int Cin, int Cout, int Cp, int T,
-                                 int H, int W, int k, void* workspace, hipStream_t s);
+                                 int H, int W, int k, void* workspace, hipStream_t s, int32_t* idx = nullptr,
+                                 const FsqParams* fsq = nullptr);
+size_t conv_proj_fsq_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
+                                     bool temporal);
+// FSQ dequantize followed by the 1x1 projection D -> Cout (the decoder's first layer), one
+// kernel: y [positions][Cout] bf16 = w_p . bf16(codes) + b_p.
+hipError_t launch_fsq_dequant_proj(const int32_t* idx, const FsqParams& p, const void* w_p, const float* b_p, void* y,
+                                   long long P, int Cout, int32_t* invalid, hipStream_t s);
 
 // Causal temporal convolution of one chunk of a stream (conv.hip): history frames in place
 // of the zero padding, optional fused 1x1 projection (C <= 256, Cp <= 16).

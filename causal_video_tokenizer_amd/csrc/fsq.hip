@@ -353,13 +353,6 @@ __global__ __launch_bounds__(256) void fsq_quantize_kernel(const T* __restrict__
     }
 }
 
-// Exact floor(n / L) for 0 <= n < 2^31 and 2 <= L <= 16.  With l = ceil(log2 L),
-// M = ceil(2^(31+l) / L) < 2^32 and n M / 2^(31+l) exceeds n / L by less than
-// n / 2^(31+l) < 2^-l <= 1/L, the smallest gap between n / L and the next
-// integer, so floor(mulhi(n, M) / 2^(l-1)) = floor(n / L).
-__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, int sh) {
-    return __umulhi(n, M) >> sh;
-}
 
 // Dequantize with the default levels.  With radices (8,8,8,5,5,5) the index splits into
 // lo = idx mod 512, whose three octal digits are bit fields, and hi = idx / 512 < 125,

@@ -182,6 +182,32 @@ int cvt_causal_conv3d_fact_proj(const void* x, const void* w_s, const void* w_t,
                                 int T, int H, int W, int k, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The factorized conv with the 1x1 projection to the D-dim latent AND its FSQ
+ * quantization (cvt_fsq_quantize of the bf16 latent) in one pass: where the
+ * projection runs in the temporal conv's epilogue (temporal part present,
+ * k = 3, Cout <= 256, D <= 8) the indices are computed there and the latent
+ * need not be written; otherwise the latent goes through the FSQ kernel.
+ * Either way indices equal cvt_fsq_quantize of cvt_causal_conv3d_fact_proj's
+ * output bit for bit.
+ *
+ * Defined by: the Cosmos-Predict1 summary, section "1) Cosmos Tokenizer" (the
+ * discrete tokenizer quantizes a 6-dim latent with FSQ levels (8,8,8,5,5,5))
+ * and "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (FSQ).
+ *
+ * Arguments as cvt_causal_conv3d_fact_proj with Cp = D, plus levels (host
+ * int32[D]) and indices (int32 [B, T, H, W], 16-byte aligned); y (the bf16
+ * NTHWC latent [B, D, T, H, W]) may be NULL.  workspace:
+ * cvt_causal_conv3d_fact_proj_fsq_workspace(..., Cp = D, ...) bytes.
+ * Errors: as cvt_causal_conv3d_fact_proj and cvt_fsq_quantize.
+ */
+size_t cvt_causal_conv3d_fact_proj_fsq_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k,
+                                                 int parts);
+int cvt_causal_conv3d_fact_proj_fsq(const void* x, const void* w_s, const void* w_t, const float* b_s,
+                                    const float* b_t, const void* w_p, const float* b_p, const int32_t* levels, int D,
+                                    void* y, int32_t* indices, int B, int Cin, int Cout, int T, int H, int W, int k,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal temporal convolution (k = 3) of one chunk of a stream, optionally followed
  * by the fused 1x1x1 projection:
  *   y[t] = sum_j w_t[:, :, j] . x[t + j - 2] (+ b_t),   t = 0 .. T-1,
@@ -432,6 +458,27 @@ size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, i
 int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                    int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * FSQ dequantize fused with the decoder's first layer, the 1x1 projection
+ * D -> Cout: y = w_p . codes + b_p per position, the codes being those of
+ * cvt_fsq_dequantize rounded to bf16, accumulated in float32 in channel order,
+ * so y equals cvt_fsq_dequantize (bf16 NTHWC) followed by
+ * cvt_causal_conv3d_fact with k = 1 bit for bit, without writing the codes.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (indices_to_codes
+ * restores the codes from the index) and the model card's "Model Architecture"
+ * (the decoder mirrors the encoder, whose last layer is the 1x1 projection).
+ *
+ * indices: int32 [B, T, H, W]; levels: host int32[D]; w_p: bf16 [Cout, D, 1, 1,
+ * 1]; b_p: float32 [Cout] or NULL; y: bf16 NTHWC [B, Cout, T, H, W].  An index
+ * outside [0, prod L) gives NaN outputs and, when d_invalid_count is not NULL,
+ * is ADDED to that int32 device counter.
+ * Errors: CVT_E_NULL, CVT_E_LEVELS (as cvt_fsq_quantize), CVT_E_SHAPE for a
+ * non-positive size or Cout above 4096, CVT_E_ALIGN.
+ */
+int cvt_fsq_dequantize_proj(const int32_t* indices, const int32_t* levels, int D, const void* w_p, const float* b_p,
+                            void* y, int B, int Cout, int T, int H, int W, int32_t* d_invalid_count, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 24
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -285,3 +285,31 @@ def test_block_validation():
     assert us(wsb=10) == E_WORKSPACE
     assert lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4, 4, 1, 1) > lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4,
                                                                                                    4, 0, 1)
+
+
+def test_fused_fsq_validation():
+    lv = (ctypes.c_int32 * 6)(8, 8, 8, 5, 5, 5)
+    bad_lv = (ctypes.c_int32 * 6)(8, 8, 8, 5, 5, 1)
+    need = lib.cvt_causal_conv3d_fact_proj_fsq_workspace(1, 192, 256, 6, 5, 8, 8, 3, 3)
+    assert need > lib.cvt_causal_conv3d_fact_proj_workspace(1, 192, 256, 6, 5, 8, 8, 3, 3)
+    wk = ctypes.c_void_p(0x800000)
+
+    def call(**kw):
+        return lib.cvt_causal_conv3d_fact_proj_fsq(A, B_, C_, None, None, kw.get("wp", ctypes.c_void_p(0x600000)),
+                                                   None, kw.get("lv", lv), 6, None, kw.get("idx", C_), 1,
+                                                   kw.get("Cin", 192), 256, 5, 8, 8, 3, wk, kw.get("wsb", need), None)
+    assert call(wp=None) == E_NULL
+    assert call(idx=None) == E_NULL
+    assert call(lv=bad_lv) == E_LEVELS
+    assert call(Cin=190) == E_SHAPE
+    assert call(idx=MIS) == E_ALIGN
+    assert call(wsb=need - 1) == E_WORKSPACE
+
+    def dq(**kw):
+        return lib.cvt_fsq_dequantize_proj(kw.get("idx", A), kw.get("lv", lv), 6, kw.get("wp", B_), None,
+                                           kw.get("y", C_), 1, kw.get("Cout", 192), 5, 8, 8, None, None)
+    assert dq(idx=None) == E_NULL
+    assert dq(wp=None) == E_NULL
+    assert dq(lv=bad_lv) == E_LEVELS
+    assert dq(Cout=0) == E_SHAPE
+    assert dq(y=MIS) == E_ALIGN
