@@ -295,7 +295,12 @@ struct RowsGeom {
 // NORM: LayerNorm over the Cout channels of each position (scale, shift) and optionally
 // Swish.  RES: a residual tensor shaped like the output added before the rounding.  PROJ
 // and NORM need every output channel in the workgroup (one channel tile).
-constexpr int EPI_PLAIN = 0, EPI_PROJ = 1, EPI_NORM = 2, EPI_RES = 3;
+// PFSQ: PROJ followed by FSQ of the bf16 latent (indices out, the latent optional).
+constexpr int EPI_PLAIN = 0, EPI_PROJ = 1, EPI_NORM = 2, EPI_RES = 3, EPI_PFSQ = 4;
+template <int EPI>
+constexpr bool epi_proj() {
+    return EPI == EPI_PROJ || EPI == EPI_PFSQ;
+}
 struct RowsAux {
     const uint16_t* res;   // RES: [positions][Cout] bf16, the output's layout
     const float* ln_g;     // NORM: per-channel scale and shift, float32 [Cout]
@@ -584,7 +589,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
 
-    if constexpr (EPI == EPI_PROJ || EPI == EPI_NORM) {
+    if constexpr (epi_proj<EPI>() || EPI == EPI_NORM) {
         // Epilogues over whole position rows (temporal kernel with every output channel in the
         // workgroup).  The tile's conv outputs, bias added and rounded to bf16 once (what a
         // separate pass would read), are staged in LDS as [frame][column][channel] rows, and
@@ -596,8 +601,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         constexpr int TCH = C::TCH, NC = C::NC, PRS = C::PRS, KST = TCH / 16;
         // the projection weights (the only 32-row block, Cp <= 32; k-steps past Cout read
         // zeros) are requested first and arrive while the tile is staged
-        bf16x8_t fp[EPI == EPI_PROJ ? KST : 1];
-        if constexpr (EPI == EPI_PROJ) {
+        bf16x8_t fp[epi_proj<EPI>() ? KST : 1];
+        if constexpr (epi_proj<EPI>()) {
             const __amdgpu_buffer_rsrc_t pres =
                 __builtin_amdgcn_make_buffer_rsrc((void*)Wpf, (short)0, g.wp_bytes, 0x00020000);
 #pragma unroll
@@ -713,7 +718,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                                                                pacc, 0, 0, 0);
             // element r < 8 is projection output 8 (r / 4) + 4 khalf + r % 4 at column px
             const int hw = c0 + cblk * 32 + px;
-            if (aux.fsq_idx) {  // FSQ of the bf16 latent: lane khalf = 0 gathers outputs 4..7 from lane + 32
+            if constexpr (EPI == EPI_PFSQ) {  // FSQ of the bf16 latent: lane khalf = 0 gathers outputs 4..7 from lane + 32
                 float lat[4], up[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -729,7 +734,10 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                         if (i < aux.fsq.D) {
                             int d = 0;
 #pragma unroll
-                            for (int j = 0; j < FSQ_MAX_L - 1; ++j) d += (z[i] >= aux.fsq.thr[i][j]) ? 1 : 0;  // NaN pads
+                            for (int j = 0; j < FSQ_MAX_L - 1; ++j) {
+                                if (j >= aux.fsq.nthr[i]) break;  // uniform: the channel's breakpoint count
+                                d += (z[i] >= aux.fsq.thr[i][j]) ? 1 : 0;
+                            }
                             acc += d * aux.fsq.basis[i];
                             nan |= z[i] != z[i];
                         }
@@ -737,7 +745,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                     aux.fsq_idx[((long long)b * g.T + r0 + fr) * g.HW + hw] = nan ? -1 : acc;
                 }
             }
-            if (Y && hw < g.HW) {
+            if ((EPI != EPI_PFSQ || Y) && hw < g.HW) {
                 uint16_t* yp = Y + (((long long)b * g.T + r0 + fr) * g.HW + hw) * Cp;
                 if ((Cp & 3) == 0) {  // 4 consecutive outputs per 8-byte store
 #pragma unroll
@@ -866,7 +874,7 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint16_t* __restrict__ Hx, RowsGeom g, RowsAux aux) {
     constexpr int KIND = C::KIND;
     // the region buffers; the fused projection's partial sums reuse them after the K loop
-    __shared__ __attribute__((aligned(16))) uint8_t smem[(EPI == EPI_PROJ || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[(epi_proj<EPI>() || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -1164,6 +1172,10 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     if constexpr (KIND == TEMPORAL3 && C::NW == 4) {  // the 4-wave temporal tiles: fused projection, norm
         if (Wpf) {
             if (g.nct != 1 || Cp < 1 || Cp > 16 || aux.ln_g || aux.res) return hipErrorInvalidValue;
+            if (aux.fsq_idx) {
+                if (Cp != aux.fsq.D || Cp > 8 || Hx) return hipErrorInvalidValue;
+                return launch_rows_tail<C, EPI_PFSQ>(tail, X, Wf, bias, Y, Wpf, bias_p, Hx, g, aux, s);
+            }
             return launch_rows_tail<C, EPI_PROJ>(tail, X, Wf, bias, Y, Wpf, bias_p, Hx, g, aux, s);
         }
         if (aux.ln_g) {
