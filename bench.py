@@ -51,10 +51,10 @@ COPY_CAL_BYTES = 256 * 1024 * 1024
 # 1x3x3 192->256 on the 13 x 180 x 320 latent grid), from two rocprofv3 --pmc passes over
 # this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
 # what it reads for the 256 MiB device copy this script issues after timing: FETCH_SIZE
-# reads 131091.2 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
+# reads 131091.1 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
 # for the kernel version the counters were taken on: set to None when it changes.
-SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 229891.7, 374454.0
-COPY_FETCH_KIB, COPY_WRITE_KIB = 131091.2, 262144.0
+SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 233116.0, 374445.2
+COPY_FETCH_KIB, COPY_WRITE_KIB = 131091.1, 262144.0
 
 
 def parse():
