@@ -344,6 +344,7 @@ struct RowsCfg {
     static constexpr int REGION_BYTES = 2 * XROWS * rows_xs<BK>();       // the two region buffers
     static constexpr int PRS = TCH * 2 + 16;                              // fused projection: bytes per staged column
     static constexpr int PROJ_BYTES = R * NC * PRS;                       // R frames of staged columns
+    static constexpr int RES_BYTES = NW * 32 * FB * (128 * FA + 16);       // residual epilogue: float32 row stages
     static_assert((NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
                       R <= 4,
                   "tile shape");
@@ -638,6 +639,21 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             const int Cout = g.Cout, cpr = Cout >> 3;  // 16-byte chunks per position row
             const float inv_n = 1.0f / (float)Cout;
             const int nit = (32 * cpr + 63) >> 6;
+            // a lane's channel chunk is lane % cpr in every store step when cpr divides 64 (C =
+            // 64, 128, 256): its scale and shift are then loaded once
+            const bool fixed_ch = (64 % cpr) == 0;
+            float gg[8], bb[8];
+            auto load_affine = [&](int ch) {
+                const float4 g0 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8);
+                const float4 g1 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8 + 4);
+                const float4 b0 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8);
+                const float4 b1 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8 + 4);
+                gg[0] = g0.x; gg[1] = g0.y; gg[2] = g0.z; gg[3] = g0.w;
+                gg[4] = g1.x; gg[5] = g1.y; gg[6] = g1.z; gg[7] = g1.w;
+                bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+                bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+            };
+            if (fixed_ch) load_affine(lane % cpr);
             for (int pr = wave; pr < NV * NBLK; pr += C::NW) {  // wave-uniform
                 const int fr = pr / NBLK, cblk = pr % NBLK;
                 const uint8_t* col = smem + (fr * NC + cblk * 32) * PRS;
@@ -674,12 +690,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                     const float m = __shfl(mean, pc & 31), r = __shfl(rstd, pc & 31);
                     if (pc < 32 && hw0 + pc < g.HW) {
                         const uint4 v = *reinterpret_cast<const uint4*>(col + pc * PRS + ch * 16);
-                        const float4 g0 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8);
-                        const float4 g1 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8 + 4);
-                        const float4 b0 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8);
-                        const float4 b1 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8 + 4);
-                        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                        if (!fixed_ch) load_affine(ch);
                         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
                         uint32_t o[4];
 #pragma unroll
@@ -687,8 +698,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                             float y0 = (bf16_lo(w[k]) - m) * r * gg[2 * k] + bb[2 * k];
                             float y1 = (bf16_hi(w[k]) - m) * r * gg[2 * k + 1] + bb[2 * k + 1];
                             if (aux.swish) {
-                                y0 = y0 / (1.0f + __expf(-y0));
-                                y1 = y1 / (1.0f + __expf(-y1));
+                                y0 = swish_f(y0);
+                                y1 = swish_f(y1);
                             }
                             o[k] = pack_bf16x2(y0, y1);
                         }
@@ -776,9 +787,14 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // lanes storing one position's 64 FA contiguous bytes.  The region buffers are free after
     // the last barrier of the K loop; a wave reads back only what it wrote and its LDS
     // accesses execute in order, so no barrier is needed.
-    constexpr int OS = 64 * FA + 16;
+    // RES stages the float32 sums instead (rows of 128 FA + 16 bytes) and adds the residual in
+    // the store step, where each lane's 16 residual bytes sit at its store's offset (one
+    // coalesced load per store) before the single bf16 rounding.
+    constexpr int ES = EPI == EPI_RES ? 4 : 2;  // staged element bytes
+    constexpr int OS = 32 * FA * ES + 16;
     constexpr int STAGE = 32 * FB * OS;  // bytes per wave
-    static_assert(C::NW * STAGE <= C::REGION_BYTES, "epilogue staging fits in the region buffers");
+    static_assert(C::NW * STAGE <= (EPI == EPI_RES ? C::RES_BYTES : C::REGION_BYTES),
+                  "epilogue staging fits in the LDS buffer");
     uint8_t* stage = smem + wave * STAGE;
     const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
 #pragma unroll
@@ -790,47 +806,27 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x16_t& c = acc[ry][a][cb];
-                    float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (EPI == EPI_RES) {  // 4 consecutive channels of the residual
-                        const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf;
-                        long long pos;
-                        bool ok;
-                        if (KIND == SPATIAL3) {
-                            const int x = c0 + wpos * 32 * FB + cb * 32 + px;
-                            ok = x < g.W;
-                            pos = (((long long)b * g.T + t) * g.H + r0 + ry) * g.W + x;
-                        } else {
-                            const int hw = c0 + wpos * 32 * FB + cb * 32 + px;
-                            ok = hw < g.HW;
-                            pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
-                        }
-                        if (ok && n < g.Cout) {
-                            const uint2 rr = *reinterpret_cast<const uint2*>(aux.res + pos * g.Cout + n);
-                            rv[0] = bf16_lo(rr.x); rv[1] = bf16_hi(rr.x);
-                            rv[2] = bf16_lo(rr.y); rv[3] = bf16_hi(rr.y);
-                        }
+                    uint8_t* dst = stage + (cb * 32 + px) * OS + (a * 32 + 8 * q + 4 * khalf) * ES;
+                    if constexpr (EPI == EPI_RES) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q] + bv[a][q][0], c[4 * q + 1] + bv[a][q][1],
+                                                                      c[4 * q + 2] + bv[a][q][2],
+                                                                      c[4 * q + 3] + bv[a][q][3]);
+                    } else {
+                        uint2 u;
+                        u.x = pack_bf16x2(c[4 * q] + bv[a][q][0], c[4 * q + 1] + bv[a][q][1]);
+                        u.y = pack_bf16x2(c[4 * q + 2] + bv[a][q][2], c[4 * q + 3] + bv[a][q][3]);
+                        *reinterpret_cast<uint2*>(dst) = u;
                     }
-                    float o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        o[e] = c[4 * q + e] + bv[a][q][e];
-                        if constexpr (EPI == EPI_RES) o[e] += rv[e];
-                    }
-                    uint2 u;
-                    u.x = pack_bf16x2(o[0], o[1]);
-                    u.y = pack_bf16x2(o[2], o[3]);
-                    *reinterpret_cast<uint2*>(stage + (cb * 32 + px) * OS + (a * 32 + 8 * q + 4 * khalf) * 2) = u;
                 }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        constexpr int CPP = 4 * FA;   // 16-byte chunks per position slice
+        constexpr int CPP = 4 * FA;   // 16-byte output chunks per position slice
         constexpr int PPI = 64 / CPP;  // positions per store instruction
         const int c16 = lane % CPP;
         const int n = ab0 * 32 + c16 * 8;
 #pragma unroll
         for (int it = 0; it < 32 * FB / PPI; ++it) {
             const int col = it * PPI + lane / CPP;
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + col * OS + c16 * 16);
             long long pos;
             bool ok;
             if (KIND == SPATIAL3) {
@@ -842,8 +838,20 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 ok = hw < g.HW;
                 pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
             }
-            if (ok && n < g.Cout)  // Cout is a multiple of 8 on this path (checked by the launcher)
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(Y + pos * g.Cout) + nb + c16 * 16) = v;
+            ok = ok && n < g.Cout;  // Cout is a multiple of 8 on this path (checked by the launcher)
+            uint4 v;
+            if constexpr (EPI == EPI_RES) {
+                const float4 f0 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32);
+                const float4 f1 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32 + 16);
+                const uint4 r = ok ? *reinterpret_cast<const uint4*>(aux.res + pos * g.Cout + n) : make_uint4(0u, 0u, 0u, 0u);
+                v.x = pack_bf16x2(f0.x + bf16_lo(r.x), f0.y + bf16_hi(r.x));
+                v.y = pack_bf16x2(f0.z + bf16_lo(r.y), f0.w + bf16_hi(r.y));
+                v.z = pack_bf16x2(f1.x + bf16_lo(r.z), f1.y + bf16_hi(r.z));
+                v.w = pack_bf16x2(f1.z + bf16_lo(r.w), f1.w + bf16_hi(r.w));
+            } else {
+                v = *reinterpret_cast<const uint4*>(stage + col * OS + c16 * 16);
+            }
+            if (ok) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(Y + pos * g.Cout) + nb + c16 * 16) = v;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -874,7 +882,9 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint16_t* __restrict__ Hx, RowsGeom g, RowsAux aux) {
     constexpr int KIND = C::KIND;
     // the region buffers; the fused projection's partial sums reuse them after the K loop
-    __shared__ __attribute__((aligned(16))) uint8_t smem[(epi_proj<EPI>() || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES) : C::REGION_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[(epi_proj<EPI>() || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES)
+                                                                      : EPI == EPI_RES ? std::max(C::REGION_BYTES, C::RES_BYTES)
+                                                                                       : C::REGION_BYTES];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -1184,7 +1194,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
         }
     }
     if (Wpf || aux.ln_g) return hipErrorInvalidValue;
-    if constexpr (KIND == TEMPORAL3 && C::FA == 1) {  // residual epilogue on the plain temporal tiles
+    if constexpr (KIND == TEMPORAL3) {  // residual epilogue (4-wave tiles up to 256 channels, else 8-wave)
         if (aux.res) return launch_rows_tail<C, EPI_RES>(tail, X, Wf, bias, Y, nullptr, nullptr, Hx, g, aux, s);
     }
     if (aux.res) return hipErrorInvalidValue;
@@ -1199,7 +1209,10 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
         return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr, aux);
     if (cg.Cout <= TemporalNarrowCfg::TCH)
         return launch_rows_cfg<TemporalNarrowCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
-    if (Wpf || aux.ln_g) return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
+    // the epilogues with extra per-tile work (projection, norm, residual) run on 4-wave tiles, two
+    // workgroups per CU, so one's epilogue overlaps the other's MFMAs
+    if ((Wpf || aux.ln_g || aux.res) && cg.Cout <= TemporalProjCfg::TCH)
+        return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
     return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
 }
 

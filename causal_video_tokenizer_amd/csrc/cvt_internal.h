@@ -27,6 +27,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
 }
 
+// Swish y * sigmoid(y) with the hardware reciprocal (about 1 ulp) instead of a division.
+__device__ __forceinline__ float swish_f(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
+
 // Non-temporal (streaming) loads for data read exactly once: on gfx950 they raise
 // the achievable read bandwidth of a streaming kernel noticeably over plain loads.
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));

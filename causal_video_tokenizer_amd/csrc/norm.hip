@@ -8,7 +8,8 @@
 // smallest power of two >= C/8, at most 64) share a row, each holding NCH 16-byte chunks in
 // registers, so the row is read once: the mean and then the centred squares are reduced
 // across the G lanes with butterfly exchanges, and the normalized row is written back with
-// the same 16-byte accesses.  A wave covers 64/G rows per step; all statistics are float32.
+// the same 16-byte accesses.  A wave covers U * 64/G rows per step and issues the loads of
+// all of them first; all statistics are float32.
 // x and y may be the same buffer: every chunk is read before any store of its row.
 #include "cvt_internal.h"
 
@@ -36,16 +37,28 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* x, const
         }
     }
     const long long nw = (long long)gridDim.x * 4;
-    for (long long p0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * ppw; p0 < P; p0 += nw * ppw) {
-        const long long p = p0 + sub;
+    // U row groups per step: their loads are issued together, so more bytes are in flight
+    constexpr int U = NCH == 1 ? 4 : (NCH == 2 ? 2 : 1);
+    for (long long p00 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * ppw * U; p00 < P; p00 += nw * ppw * U) {
+        uint4 raw[U][NCH];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            const long long p = p00 + uu * ppw + sub;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int ch = gl + k * G;
+                raw[uu][k] = (p < P && ch < cpr) ? ld_stream16(x + p * C + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+        const long long p = p00 + uu * ppw + sub;
         const bool prow = p < P;
         float v[NCH][8];
         float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const int ch = gl + k * G;
-            uint4 u = make_uint4(0u, 0u, 0u, 0u);
-            if (prow && ch < cpr) u = ld_stream16(x + p * C + ch * 8);
+            const uint4 u = raw[uu][k];
             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -79,13 +92,14 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* x, const
                     float y0 = (v[k][2 * e] - mean) * rstd * gg[k][2 * e] + bb[k][2 * e];
                     float y1 = (v[k][2 * e + 1] - mean) * rstd * gg[k][2 * e + 1] + bb[k][2 * e + 1];
                     if (swish) {
-                        y0 = y0 / (1.0f + __expf(-y0));
-                        y1 = y1 / (1.0f + __expf(-y1));
+                        y0 = swish_f(y0);
+                        y1 = swish_f(y1);
                     }
                     o[e] = pack_bf16x2(y0, y1);
                 }
                 *reinterpret_cast<uint4*>(y + p * C + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
             }
+        }
         }
     }
 }
@@ -98,7 +112,8 @@ hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta
     int G = 1;
     while (G < cpr && G < 64) G <<= 1;
     const int nch = (cpr + 63) / 64;
-    const long long rows_per_block = 4LL * (64 / G);
+    const int U = nch == 1 ? 4 : (nch == 2 ? 2 : 1);  // as in the kernel
+    const long long rows_per_block = 4LL * (64 / G) * U;
     const long long nblk = std::min((P + rows_per_block - 1) / rows_per_block, 16384LL);
     const dim3 grid((unsigned)nblk), block(256);
     const uint16_t* xs = static_cast<const uint16_t*>(x);
