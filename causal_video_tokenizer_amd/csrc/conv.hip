@@ -324,15 +324,22 @@ constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows
 #ifndef CVT_ROWS_SP_PD
 #define CVT_ROWS_SP_PD 1
 #endif
-template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4>
+// S = 2: the stride-2 (downsampling) convolution.  Output row i reads input rows S i + j
+// (temporal: frames 2 (r0 + i) - 2 + j; spatial: rows 2 (r0 + i) - 1 + ky), so a tile of R
+// output rows stages S (R - 1) + 3 input rows.  Spatially the 2 NC + 1 input columns of a
+// tile are staged de-interleaved, the NC + 1 odd ones (input columns 2 c0 - 1 + 2 m) first
+// and the NC even ones (2 c0 + 2 m) after them, so the column shifts kx = 0, 1, 2 read the
+// contiguous runs starting at region columns 0, NC + 1 and 1.
+template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4, int S_ = 1>
 struct RowsCfg {
-    static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_, NW = NW_;
+    static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_, NW = NW_, S = S_;
     static constexpr int NTH = 64 * NW;                         // threads per workgroup
     static constexpr int WPOS = NW / WCH;                       // waves along columns
     static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;         // column shifts
     static constexpr int TCH = 32 * FA * WCH;                   // output channels per workgroup
     static constexpr int NC = 32 * FB * WPOS;                   // output columns per workgroup
-    static constexpr int RC = NC + (KIND == SPATIAL3 ? 2 : 0);  // region columns (with the x halo)
+    static constexpr int RC = KIND == SPATIAL3 ? S * NC + (S == 1 ? 2 : 1) : NC;  // region columns (with the x halo)
+    static constexpr int RROWS = S * (R - 1) + 3;                                  // region rows
     static constexpr int XS = rows_xs<BK>();
     // region rows per buffer, padded so that the 16-byte chunks (BK / 8 per row) split evenly
     // over the 256 threads: every thread issues the same unguarded loads (padding rows read
@@ -340,13 +347,13 @@ struct RowsCfg {
     // branch followed by a full memory wait
     static constexpr int PD = KIND == SPATIAL3 ? CVT_ROWS_SP_PD : 1;  // weight prefetch distance in steps
     static constexpr int PASS = NTH / (BK / 8);
-    static constexpr int XROWS = ((R + 2) * RC + PASS - 1) / PASS * PASS;
+    static constexpr int XROWS = (RROWS * RC + PASS - 1) / PASS * PASS;
     static constexpr int REGION_BYTES = 2 * XROWS * rows_xs<BK>();       // the two region buffers
     static constexpr int PRS = TCH * 2 + 16;                              // fused projection: bytes per staged column
     static constexpr int PROJ_BYTES = R * NC * PRS;                       // R frames of staged columns
     static constexpr int RES_BYTES = NW * 32 * FB * (128 * FA + 16);       // residual epilogue: float32 row stages
     static_assert((NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
-                      R <= 4,
+                      R <= 4 && (S == 1 || S == 2),
                   "tile shape");
 };
 
@@ -363,7 +370,9 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     constexpr int XQ = XROWS * CPR;
     constexpr int XL = (XQ + NTH - 1) / NTH;
     constexpr int OOB = 0x7fffffff;
-    constexpr int NRU = NV + 2;  // region rows that feed a valid output row
+    constexpr int SR = C::S;
+    constexpr int NRU = SR * (NV - 1) + 3;  // region rows that feed a valid output row
+    static_assert(SR == 1 || !HIST, "stream history frames only at stride 1");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in a scalar register
     const int wch = wave % WCH, wpos = wave / WCH;
@@ -386,10 +395,20 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         const int rr = row / RC, cc = row % RC;
         bool ok = q < XQ && rr < NRU;
         int pos = 0;
-        if (KIND == SPATIAL3) {
+        if (KIND == SPATIAL3 && SR == 2) {  // stride 2: rows 2 r0 - 1 + rr, de-interleaved columns
+            constexpr int NC = C::NC;
+            const int y = 2 * r0 - 1 + rr;
+            const int x = cc <= NC ? 2 * c0 - 1 + 2 * cc : 2 * c0 + 2 * (cc - NC - 1);
+            ok = ok && y >= 0 && y < g.Hi && x >= 0 && x < g.Wi;
+            pos = ((b * g.T + t) * g.Hi + y) * g.Wi + x;
+        } else if (KIND == SPATIAL3) {
             const int y = r0 - 1 + rr, x = c0 - 1 + cc;
             ok = ok && y >= 0 && y < g.H && x >= 0 && x < g.W;
             pos = g.ups ? ((b * g.T + t) * g.Hi + (y >> 1)) * g.Wi + (x >> 1) : ((b * g.T + t) * g.H + y) * g.W + x;
+        } else if (SR == 2) {  // stride 2: input frames 2 r0 - 2 + rr
+            const int fr = 2 * r0 - 2 + rr, hw = c0 + cc;
+            ok = ok && fr >= 0 && fr < g.Ti && hw < g.HW;
+            pos = (b * g.Ti + fr) * g.HW + hw;
         } else {
             const int fr = r0 - 2 + rr, hw = c0 + cc;
             if constexpr (HIST) {  // frames -2 and -1 are the history frames 0 and 1
@@ -495,16 +514,21 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // s % KX, channels of k-step s / KX.
     auto read_row = [&](bf16x8_t (&f)[NRU][FB], const uint8_t* xb, int s, int rr) {
         const int ch = (s / KX) * 2 + khalf, kx = s % KX;
+        // column shift kx starts at region column kx (stride 1) or, de-interleaved at stride 2,
+        // at 0 (odd columns), NC + 1 (even columns) or 1 (odd columns, one further)
+        const int kc0 = SR == 1 ? kx : (kx == 1 ? C::NC + 1 : kx / 2);
 #pragma unroll
         for (int cb = 0; cb < FB; ++cb)
-            f[rr][cb] = *reinterpret_cast<const bf16x8_t*>(xb + (rr * RC + cb * 32 + kx) * XS + ch * 16);
+            f[rr][cb] = *reinterpret_cast<const bf16x8_t*>(xb + (rr * RC + cb * 32 + kc0) * XS + ch * 16);
     };
-    // The MFMAs of region row rr: it meets tap row ky in output row rr - ky.
+    // The MFMAs of region row rr: it meets tap row ky in output row (rr - ky) / S.
     auto mfma_row = [&](const bf16x8_t (&f)[NRU][FB], int set, int rr) {
 #pragma unroll
         for (int ky = 0; ky < 3; ++ky) {
-            const int ry = rr - ky;
-            if (ry < 0 || ry >= NV) continue;
+            const int d = rr - ky;
+            if (d < 0 || d % SR != 0) continue;
+            const int ry = d / SR;
+            if (ry >= NV) continue;
 #pragma unroll
             for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -1121,7 +1145,7 @@ hipError_t launch_rows_k(const uint16_t* X, const uint16_t* Wf, const float* bia
                          const float* bias_p, const uint16_t* Hx, const RowsGeom& g, const RowsAux& aux,
                          hipStream_t s) {
     const dim3 grid((unsigned)(8LL * g.per_xcd)), block(C::NTH);
-    if constexpr (C::KIND == TEMPORAL3 && (EPI == EPI_PLAIN || EPI == EPI_PROJ)) {
+    if constexpr (C::KIND == TEMPORAL3 && C::S == 1 && (EPI == EPI_PLAIN || EPI == EPI_PROJ)) {
         if (Hx) {
             hipLaunchKernelGGL((conv_rows_kernel<C, TAIL, EPI, true>), grid, block, 0, s, X, Wf, bias, Y, Wpf, bias_p,
                                Hx, g, aux);
@@ -1153,9 +1177,11 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     RowsGeom g{};
     g.B = B; g.T = cg.T; g.H = cg.H; g.W = cg.W; g.HW = cg.H * cg.W; g.Cin = cg.Cin; g.Cout = cg.Cout;
     g.ups = cg.ups;
-    g.Ti = cg.ups ? cg.Ti : cg.T;
-    g.Hi = cg.ups ? cg.Hi : cg.H;
-    g.Wi = cg.ups ? cg.Wi : cg.W;
+    const bool in_grid = cg.ups || C::S == 2;  // the input grid differs from the output grid
+    g.Ti = in_grid ? cg.Ti : cg.T;
+    g.Hi = in_grid ? cg.Hi : cg.H;
+    g.Wi = in_grid ? cg.Wi : cg.W;
+    if (C::S == 2 && cg.ups) return hipErrorInvalidValue;
     g.x_bytes = (int)((long long)B * g.Ti * g.Hi * g.Wi * cg.Cin * 2);
     if (cg.ups && Hx) return hipErrorInvalidValue;
     g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
@@ -1214,6 +1240,34 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     if ((Wpf || aux.ln_g || aux.res) && cg.Cout <= TemporalProjCfg::TCH)
         return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
     return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
+}
+
+// The stride-2 (downsampling) convolutions on conv_rows_kernel: cg holds the output grid
+// and, in Ti, Hi, Wi, the input grid.  Spatial tiles of 2 output rows (5 input rows): 256
+// channels x 32 columns (65 de-interleaved input columns, each region staged once for 256
+// output channels: 1.46x faster than 128 x 64 tiles on 256 -> 256), or 128 x 64 up to 128
+// channels; temporal tiles as at stride 1 with 9 input frames per 4 output frames (5 per 2
+// on the 8-wave tiles above 256 channels).
+using SpatialS2NarrowCfg = RowsCfg<SPATIAL3, 2, 4, 1, 32, 4, 2>;
+using SpatialS2Cfg = RowsCfg<SPATIAL3, 2, 4, 2, 32, 4, 2>;
+using TemporalS2NarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, 32, 4, 2>;
+using TemporalS2Cfg = RowsCfg<TEMPORAL3, 4, 4, 2, 32, 4, 2>;
+using TemporalS2WideCfg = RowsCfg<TEMPORAL3, 2, 8, 1, 32, 8, 2>;  // 2 output frames: 5 staged rows fit the registers
+
+template <int KIND>
+hipError_t launch_rows_s2(const uint16_t* X, const uint16_t* Wf, const float* bias, uint16_t* Y, const ConvGeom& cg,
+                          int B, hipStream_t s) {
+    const RowsAux none{};
+    if constexpr (KIND == SPATIAL3) {
+        if (cg.Cout <= SpatialS2NarrowCfg::TCH)
+            return launch_rows_cfg<SpatialS2NarrowCfg>(X, Wf, bias, Y, cg, B, s, nullptr, nullptr, 0, nullptr, none);
+        return launch_rows_cfg<SpatialS2Cfg>(X, Wf, bias, Y, cg, B, s, nullptr, nullptr, 0, nullptr, none);
+    }
+    if (cg.Cout <= TemporalS2NarrowCfg::TCH)
+        return launch_rows_cfg<TemporalS2NarrowCfg>(X, Wf, bias, Y, cg, B, s, nullptr, nullptr, 0, nullptr, none);
+    if (cg.Cout <= TemporalS2Cfg::TCH)
+        return launch_rows_cfg<TemporalS2Cfg>(X, Wf, bias, Y, cg, B, s, nullptr, nullptr, 0, nullptr, none);
+    return launch_rows_cfg<TemporalS2WideCfg>(X, Wf, bias, Y, cg, B, s, nullptr, nullptr, 0, nullptr, none);
 }
 
 // Largest Cout whose temporal conv can take the NORM epilogue (all channels in one workgroup).
@@ -1497,8 +1551,9 @@ hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y
 }
 
 // Downsampling block: the spatial 1x3x3 conv at stride 2 in H and W (zero padding 1), then
-// the causal temporal 3x1x1 conv at stride 2 (T = 1 + 2k -> 1 + k), either part optional,
-// on conv_igemm_kernel with the strided input mapping.
+// the causal temporal 3x1x1 conv at stride 2 (T = 1 + 2k -> 1 + k), either part optional, on
+// conv_rows_kernel at stride 2 (conv_igemm_kernel with the strided input mapping for the
+// shapes the row kernel does not take).
 size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time) {
     size_t b = 0;
     if (space) b += pack_bytes(Cout, Cin, 9);
@@ -1519,25 +1574,34 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
         off += pack_bytes(Cout, Cin, 9);
         uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(ws + off + (w_t ? pack_bytes(Cout, Cout, 3) : 0))
                           : static_cast<uint16_t*>(y);
-        if ((e = pack(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
         H1 = H / 2;
         W1 = W / 2;
         ConvGeom g{};
         g.P = (long long)B * T * H1 * W1; g.T = T; g.H = H1; g.W = W1; g.Cin = Cin; g.Cout = Cout;
         g.kchunks = (Cin + BK - 1) / BK;
         g.Ti = T; g.Hi = H; g.Wi = W; g.st = 1; g.ss = 2;
-        if ((e = launch_igemm(SPATIAL3, tin, wps, b_s, S, g, s)) != hipSuccess) return e;
+        if (use_rows_kernel(3, Cout, (long long)B * T * H * W, Cin)) {
+            if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+            if ((e = launch_rows_s2<SPATIAL3>(tin, wps, b_s, S, g, B, s)) != hipSuccess) return e;
+        } else {
+            if ((e = pack(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+            if ((e = launch_igemm(SPATIAL3, tin, wps, b_s, S, g, s)) != hipSuccess) return e;
+        }
         tin = S;
         C1 = Cout;
     }
     if (!w_t) return hipSuccess;
     uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + off);
-    if ((e = pack(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
     const int T1 = 1 + (T - 1) / 2;
     ConvGeom g{};
     g.P = (long long)B * T1 * H1 * W1; g.T = T1; g.H = H1; g.W = W1; g.Cin = C1; g.Cout = Cout;
     g.kchunks = (C1 + BK - 1) / BK;
     g.Ti = T; g.Hi = H1; g.Wi = W1; g.st = 2; g.ss = 1;
+    if (C1 == Cout && use_rows_kernel(3, Cout, (long long)B * T * H1 * W1, C1)) {
+        if ((e = pack_frag(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
+        return launch_rows_s2<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
+    }
+    if ((e = pack(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
     return launch_igemm(TEMPORAL3, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
 }
 

@@ -115,6 +115,10 @@ DOWN_CASES = [
     (2, 192, 256, 2, 10, 6, True, False, False),
     (1, 64, 64, 7, 6, 10, False, True, True),
     (1, 256, 256, 9, 18, 32, True, True, False),     # 16 x 16 output positions per frame, ragged tiles
+    (2, 64, 64, 3, 10, 150, True, True, True),       # 75 output columns: two column tiles, ragged
+    (1, 72, 128, 5, 6, 8, True, False, False),       # input channels not a multiple of the K chunk
+    (1, 320, 320, 5, 4, 4, False, True, False),      # temporal above 256 channels (8-wave tiles)
+    (1, 64, 48, 5, 8, 8, True, True, True),          # Cout below 64: the implicit-GEMM fallback
 ]
 
 
