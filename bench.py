@@ -24,7 +24,8 @@ bandwidth-bound size (64 x 6 x 13 x 180 x 320 bf16) against the HBM peak; a four
 the factorized self-attention (spatial and causal temporal) on the 16 x 90 x 160 token
 grid of the CV8x8x8-720p model, 256 channels in 4 heads; a fifth, sliding windows of 17
 frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop); a sixth, the encoder's
-residual and downsampling blocks and the decoder's upsampling block on the CV8x8x8-720p grids.
+residual and downsampling blocks and the decoder's upsampling block on the CV8x8x8-720p grids; a
+seventh, the batched DV4x8x8-360p decode (8 clips: dequantize + 1x1, conv 192->192, inverse Haar).
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -70,6 +71,7 @@ def parse():
     ap.add_argument("--no-attention", action="store_true", help="skip the factorized-attention measurement")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window measurement")
     ap.add_argument("--no-blocks", action="store_true", help="skip the encoder/decoder block measurement")
+    ap.add_argument("--no-c5", action="store_true", help="skip the batched 360p decode measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -199,6 +201,7 @@ def main():
     attn = None if args.no_attention else attention_tokens(cvt, si, torch, dev, args)
     win = None if args.no_window else windowed_1080p(cvt, si, torch, dev, args)
     blk = None if args.no_blocks else blocks_cv8x8x8(cvt, si, torch, dev, args)
+    c5 = None if args.no_c5 else decode_c5(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -238,6 +241,7 @@ def main():
         "attention_cv8x8x8_720p_tokens": attn,
         "window_1080p_50f": win,
         "blocks_cv8x8x8_720p": blk,
+        "dv4x8x8_360p_decode_c5": c5,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -550,6 +554,76 @@ def blocks_cv8x8x8(cvt, si, torch, dev, args):
         out[name] = {"ms": round(ms, 4), "flops": flops, "TFLOPs": round(tf, 1),
                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
     del x, xl, y, yd, yu, ws_r, ws_d, ws_u, p
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_c5(cvt, si, torch, dev, args):
+    """The batched DV4x8x8-360p decode: 8 clips of int32 indices 8 x 13 x 90 x 160 -> FSQ
+    dequantize fused with the 1x1 6 -> 192 -> factorized causal conv 192 -> 192 (k = 3) ->
+    inverse Haar to 8 x 3 x 49 x 360 x 640 bf16.  Reports 392 output frames / the chain's
+    time, each stage's rate, and the unfused dequantize + 1x1 for comparison."""
+    cid = 5
+    wl = si.WORKLOADS["c5_dv4x8x8_360p_decode"]
+    B, Tq, Hq, Wq = wl["indices"]
+    P = B * Tq * Hq * Wq
+    log(f"c5 decode: generating indices {wl['indices']} ...")
+    idx = torch.from_numpy(si.uniform_indices(wl["indices"], wl["seed"])).to(dev)
+
+    def bf(shape, seed):
+        bits = si.to_bf16_bits(si.normal(shape, seed, 0.02))
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    lift, w_s, w_t = bf((192, 6, 1, 1, 1), si.weight_seed(cid, 0)), bf((192, 192, 1, 3, 3), si.weight_seed(cid, 1)), \
+        bf((192, 192, 3, 1, 1), si.weight_seed(cid, 2))
+    cl = torch.channels_last_3d
+    z = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    yc = torch.empty_like(z)
+    codes = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    xo = torch.empty(wl["out_x"], dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cvt.conv_workspace_bytes(z.shape, 192, 3, True, True), dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(cvt.conv_workspace_bytes(codes.shape, 192, 1, True, False), dtype=torch.uint8, device=dev)
+    stages = {
+        "dequantize_proj": lambda: cvt.fsq_dequantize_proj(idx, lift, out=z),
+        "conv_192_192": lambda: cvt.causal_conv3d_fact(z, w_s, w_t, workspace=ws, out=yc),
+        "haar_inv": lambda: cvt.haar3d_inv(yc, out=xo),
+    }
+    unfused = lambda: (cvt.fsq_dequantize(idx, out=codes), cvt.causal_conv3d_fact(codes, lift, None, workspace=ws1,
+                                                                                   out=z))
+    for _ in range(max(3, min(args.warmup, 10))):
+        for fn in stages.values():
+            fn()
+        unfused()
+    torch.cuda.synchronize()
+    reps = max(5, args.steps // 2)
+    out = {"indices": list(wl["indices"]), "out_frames": B * wl["out_x"][2]}
+    total = 0.0
+    for name, fn in list(stages.items()) + [("dequantize_then_proj_unfused", unfused)]:
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        d = {"ms": round(ms, 4)}
+        if name == "conv_192_192":
+            flops = (2.0 * 9 * 192 * 192 + 2.0 * 3 * 192 * 192) * P
+            d.update(TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1), mfma_frac=round(flops / (ms * 1e-3) / 1e12 /
+                                                                                   BF16_PEAK_TFLOPS, 4))
+        elif name == "haar_inv":
+            nbytes = 2.0 * P * 192 + 2.0 * int(np.prod(wl["out_x"]))
+            d.update(GBps=round(nbytes / (ms * 1e-3) / 1e9, 1), hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+        else:
+            nbytes = 4.0 * P + 2.0 * 192 * P
+            d.update(GBps=round(nbytes / (ms * 1e-3) / 1e9, 1), hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+        if name in stages:
+            total += ms
+        out[name] = d
+    out["chain_ms"] = round(total, 4)
+    out["frames_per_s"] = round(out["out_frames"] / (total * 1e-3), 1)
+    del idx, z, yc, codes, xo, ws, ws1
     torch.cuda.empty_cache()
     return out
 

@@ -979,19 +979,60 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
     }
 }
 
-// 1x1 projection for small Cin (<= 16): one thread per (position, 8 outputs), fp32 FMA.
-__global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ w,
-                                                              const float* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                              long long P, int Cin, int Cout) {
-    const int ng = (Cout + 7) / 8;
-    const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (item >= P * ng) return;
-    const long long pos = item / ng;
-    const int n0 = (int)(item - pos * ng) * 8;
-    float xv[16];
+// 1x1 projections with at most 16 input channels (the lift after FSQ dequantize): one item
+// per (position, 8 output channels), fp32 FMA in channel order, the bias first.  Items are
+// numbered position-major, so consecutive items are consecutive 16-byte chunks of one
+// position's output row (coalesced stores).  STAGED (the weights fit SMALL_PROJ_LDS_FLOATS):
+// the workgroup converts them once to float32 [c][CS] rows in LDS (CS = Cout rounded up to
+// 8, zeros past Cout; row Cin holds the bias), and the grid-stride is a multiple of the ng
+// channel groups of a position, so a thread's group never changes: it copies its 8 columns
+// of weights into registers once and the loop reads no weights at all.  Otherwise the
+// weights are read from global per item.
+constexpr int SMALL_PROJ_LDS_FLOATS = 12288;  // 48 KB
+
+__device__ __forceinline__ int small_proj_cs(int Cout) { return (Cout + 7) & ~7; }
+
+template <int CMAX>
+struct SmallProjW {
+    float w[CMAX][8];
+    float b[8];
+};
+
+template <int CMAX>
+__device__ __forceinline__ void small_proj_regs(const uint16_t* __restrict__ w, const float* __restrict__ bias,
+                                                float* sw, int Cin, int Cout, int n0, SmallProjW<CMAX>& r) {
+    const int CS = small_proj_cs(Cout);
+    for (int i = threadIdx.x; i < (Cin + 1) * CS; i += blockDim.x) {
+        const int c = i / CS, n = i - c * CS;
+        float v = 0.0f;
+        if (n < Cout) v = c < Cin ? bf16_to_f32(w[(size_t)n * Cin + c]) : (bias ? bias[n] : 0.0f);
+        sw[i] = v;
+    }
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 16; ++c) xv[c] = c < Cin ? bf16_to_f32(X[(size_t)pos * Cin + c]) : 0.0f;
-    float o[8];
+    for (int c = 0; c < CMAX; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.w[c][e] = c < Cin ? sw[c * CS + n0 + e] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.b[e] = sw[Cin * CS + n0 + e];
+}
+
+// o[e] = bias[n0 + e] + sum_c w[n0 + e][c] x[c]
+template <int CMAX>
+__device__ __forceinline__ void small_proj8_regs(const float* xv, int Cin, const SmallProjW<CMAX>& r, float* o) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = r.b[e];
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c)
+        if (c < Cin) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(r.w[c][e], xv[c], o[e]);
+        }
+}
+
+__device__ __forceinline__ void small_proj8_global(const float* xv, int Cin, int Cout, int n0,
+                                                   const uint16_t* __restrict__ w, const float* __restrict__ bias,
+                                                   float* o) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int n = n0 + e;
@@ -1004,6 +1045,10 @@ __global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __
         }
         o[e] = a;
     }
+}
+
+__device__ __forceinline__ void small_proj_store(uint16_t* __restrict__ Y, long long pos, int Cout, int n0,
+                                                 const float* o) {
     uint16_t* yrow = Y + (size_t)pos * Cout;
     if ((Cout & 7) == 0) {
         uint4 u;
@@ -1011,7 +1056,7 @@ __global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __
         u.y = pack_bf16x2(o[2], o[3]);
         u.z = pack_bf16x2(o[4], o[5]);
         u.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(yrow + n0) = u;
+        st_stream16(yrow + n0, u);  // written once, read back only by the next kernel
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -1019,69 +1064,117 @@ __global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __
     }
 }
 
-// FSQ dequantize fused with the 1x1 projection D -> Cout that follows it in the decoder:
-// thread = (position, 8 output channels).  The index is split into digits by exact
-// multiply-shift divisions, each code (d - L/2) / (L/2) is rounded to bf16 (what the
-// dequantize kernel stores) and the projection accumulates exactly as
-// pointwise_small_kernel does, so the result is bit-identical to the two kernels in a row
-// while the D-channel codes never reach HBM.  An index outside [0, codebook) gives NaN
-// outputs and is counted once per position in *invalid (one atomic per wave).
+// CMAX = 0: weights from global; else staged, CMAX >= Cin
+template <int CMAX>
+__global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ w,
+                                                              const float* __restrict__ bias, uint16_t* __restrict__ Y,
+                                                              long long P, int Cin, int Cout) {
+    extern __shared__ __attribute__((aligned(16))) float sw[];
+    const int ng = (Cout + 7) / 8;
+    const long long total = P * ng;
+    const long long first = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int n0 = (int)(first % ng) * 8;  // fixed: the stride is a multiple of ng
+    SmallProjW<(CMAX > 0 ? CMAX : 1)> r;
+    if constexpr (CMAX > 0) small_proj_regs<CMAX>(w, bias, sw, Cin, Cout, n0, r);
+    // the position advances by a constant (no 64-bit division per item)
+    const long long stride = (long long)gridDim.x * blockDim.x, dpos = stride / ng;
+    long long pos = first / ng;
+    for (long long item = first; item < total; item += stride, pos += dpos) {
+        float xv[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xv[c] = c < Cin ? bf16_to_f32(X[(size_t)pos * Cin + c]) : 0.0f;
+        float o[8];
+        if constexpr (CMAX > 0)
+            small_proj8_regs<CMAX>(xv, Cin, r, o);
+        else
+            small_proj8_global(xv, Cin, Cout, n0, w, bias, o);
+        small_proj_store(Y, pos, Cout, n0, o);
+    }
+}
+
+// FSQ dequantize fused with the 1x1 projection D -> Cout that follows it in the decoder.
+// The index is split into digits by exact multiply-shift divisions, each code
+// (d - L/2) / (L/2) is rounded to bf16 (what the dequantize kernel stores) and the
+// projection accumulates exactly as pointwise_small_kernel does, so the result is
+// bit-identical to the two kernels in a row while the D-channel codes never reach HBM.  An
+// index outside [0, codebook) gives NaN outputs and is counted once per position in
+// *invalid (one atomic per wave and step; the loop's trip count is uniform per wave).
+template <int CMAX>
 __global__ __launch_bounds__(256) void fsq_dequant_proj_kernel(const int32_t* __restrict__ idx, FsqParams p,
                                                                const uint16_t* __restrict__ w,
                                                                const float* __restrict__ bias,
                                                                uint16_t* __restrict__ Y, long long P, int Cout,
                                                                int32_t* __restrict__ invalid) {
+    extern __shared__ __attribute__((aligned(16))) float sw[];
     const int ng = (Cout + 7) / 8;
-    const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool live = item < P * ng;
-    const long long pos = live ? item / ng : 0;
-    const int n0 = (int)(item - pos * ng) * 8;
-    const int id = live ? idx[pos] : 0;
-    const bool bad = id < 0 || id >= p.codebook;
-    if (invalid) {
-        const unsigned long long m = __builtin_amdgcn_ballot_w64(live && bad && n0 == 0);
-        if (m && (threadIdx.x & 63) == (int)__builtin_ctzll(m)) atomicAdd(invalid, (int)__builtin_popcountll(m));
-    }
-    if (!live) return;
-    uint32_t rem = bad ? 0u : (uint32_t)id;
-    float xv[FSQ_MAX_D];
+    const long long total = P * ng;
+    const int lane = threadIdx.x & 63;
+    const long long first = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int n0 = (int)(first % ng) * 8;  // fixed: the stride is a multiple of ng
+    SmallProjW<(CMAX > 0 ? CMAX : 1)> r;
+    if constexpr (CMAX > 0) small_proj_regs<CMAX>(w, bias, sw, p.D, Cout, n0, r);
+    // the position advances by a constant (no 64-bit division per item); U items per step,
+    // their index loads issued together
+    constexpr int U = 4;
+    const long long stride = (long long)gridDim.x * blockDim.x, dpos = stride / ng;
+    long long pos = first / ng;
+    for (long long base = first - lane; base < total; base += U * stride, pos += U * dpos) {
+        int ids[U];
 #pragma unroll
-    for (int i = 0; i < FSQ_MAX_D; ++i) {
-        xv[i] = 0.0f;
-        if (i < p.D) {
-            const uint32_t q = div_magic(rem, p.magic[i], p.shift[i]);
-            const int d = (int)(rem - q * (uint32_t)p.levels[i]);
-            rem = q;
-            const float code = (float)(d - p.half[i]) / (float)p.half[i];
-            xv[i] = bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code));
+        for (int u = 0; u < U; ++u) ids[u] = base + u * stride + lane < total ? idx[pos + u * dpos] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+        const long long item = base + u * stride + lane;
+        const bool live = item < total;
+        const int id = ids[u];
+        const bool bad = id < 0 || id >= p.codebook;
+        if (invalid) {
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(live && bad && n0 == 0);
+            if (m && lane == (int)__builtin_ctzll(m)) atomicAdd(invalid, (int)__builtin_popcountll(m));
+        }
+        if (!live) continue;
+        uint32_t rem = bad ? 0u : (uint32_t)id;
+        float xv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            xv[i] = 0.0f;
+            if (i < FSQ_MAX_D && i < p.D) {
+                const uint32_t q = div_magic(rem, p.magic[i], p.shift[i]);
+                const int d = (int)(rem - q * (uint32_t)p.levels[i]);
+                rem = q;
+                // (d - h) / h; for a power-of-two h (every level of the default set) the product
+                // with the exact reciprocal is the same float, without a division
+                const int h = p.half[i];
+                const float code = (h & (h - 1)) == 0 ? (float)(d - h) * (1.0f / (float)h) : (float)(d - h) / (float)h;
+                xv[i] = bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code));
+            }
+        }
+        float o[8];
+        if constexpr (CMAX > 0)
+            small_proj8_regs<CMAX>(xv, p.D, r, o);
+        else
+            small_proj8_global(xv, p.D, Cout, n0, w, bias, o);
+        small_proj_store(Y, pos + u * dpos, Cout, n0, o);
         }
     }
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int n = n0 + e;
-        float a = 0.0f;
-        if (n < Cout) {
-            a = bias ? bias[n] : 0.0f;
-#pragma unroll
-            for (int c = 0; c < FSQ_MAX_D; ++c)
-                if (c < p.D) a = fmaf(bf16_to_f32(w[(size_t)n * p.D + c]), xv[c], a);
-        }
-        o[e] = a;
+}
+
+// Grid of the small projections: at most about 4096 workgroups, rounded up to a multiple of
+// ng / gcd(ng, 256) so that the grid-stride is a multiple of the ng channel groups.
+inline long long small_proj_blocks(long long items, int ng) {
+    long long a = ng, b = 256;
+    while (b) {
+        const long long t = a % b;
+        a = b;
+        b = t;
     }
-    uint16_t* yrow = Y + (size_t)pos * Cout;
-    if ((Cout & 7) == 0) {
-        uint4 u;
-        u.x = pack_bf16x2(o[0], o[1]);
-        u.y = pack_bf16x2(o[2], o[3]);
-        u.z = pack_bf16x2(o[4], o[5]);
-        u.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(yrow + n0) = u;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (n0 + e < Cout) yrow[n0 + e] = f32_to_bf16(o[e]);
-    }
+    const long long m = ng / a;
+    const long long nb = std::min((items + 255) / 256, 4096LL);
+    return (nb + m - 1) / m * m;
+}
+inline size_t small_proj_lds(int Cin, int Cout) { return (size_t)(Cin + 1) * ((Cout + 7) & ~7) * sizeof(float); }
+inline bool small_proj_staged(int Cin, int Cout) {
+    return (long long)(Cin + 1) * ((Cout + 7) & ~7) <= SMALL_PROJ_LDS_FLOATS;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1205,7 +1298,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
     const bool tail = cg.Cin % BK != 0;
-    if constexpr (KIND == TEMPORAL3 && C::NW == 4) {  // the 4-wave temporal tiles: fused projection, norm
+    if constexpr (KIND == TEMPORAL3 && C::NW == 4 && C::S == 1) {  // the 4-wave temporal tiles: projection, norm
         if (Wpf) {
             if (g.nct != 1 || Cp < 1 || Cp > 16 || aux.ln_g || aux.res) return hipErrorInvalidValue;
             if (aux.fsq_idx) {
@@ -1220,7 +1313,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
         }
     }
     if (Wpf || aux.ln_g) return hipErrorInvalidValue;
-    if constexpr (KIND == TEMPORAL3) {  // residual epilogue (4-wave tiles up to 256 channels, else 8-wave)
+    if constexpr (KIND == TEMPORAL3 && C::S == 1) {  // residual epilogue (4-wave tiles up to 256 channels, else 8-wave)
         if (aux.res) return launch_rows_tail<C, EPI_RES>(tail, X, Wf, bias, Y, nullptr, nullptr, Hx, g, aux, s);
     }
     if (aux.res) return hipErrorInvalidValue;
@@ -1243,14 +1336,14 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
 }
 
 // The stride-2 (downsampling) convolutions on conv_rows_kernel: cg holds the output grid
-// and, in Ti, Hi, Wi, the input grid.  Spatial tiles of 2 output rows (5 input rows): 256
-// channels x 32 columns (65 de-interleaved input columns, each region staged once for 256
-// output channels: 1.46x faster than 128 x 64 tiles on 256 -> 256), or 128 x 64 up to 128
-// channels; temporal tiles as at stride 1 with 9 input frames per 4 output frames (5 per 2
+// and, in Ti, Hi, Wi, the input grid.  Spatial tiles of 256 channels x 32 columns x 2 output
+// rows (5 input rows of 65 de-interleaved columns, each region staged once for 256 output
+// channels: 1.46x faster than 128 x 64 tiles on 256 -> 256), or 128 x 64 x 1 up to 128
+// channels (3 input rows of 129 columns, two workgroups per CU); temporal tiles as at stride 1 with 9 input frames per 4 output frames (5 per 2
 // on the 8-wave tiles above 256 channels).
-using SpatialS2NarrowCfg = RowsCfg<SPATIAL3, 2, 4, 1, 32, 4, 2>;
+using SpatialS2NarrowCfg = RowsCfg<SPATIAL3, 1, 4, 1, 32, 4, 2>;
 using SpatialS2Cfg = RowsCfg<SPATIAL3, 2, 4, 2, 32, 4, 2>;
-using TemporalS2NarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, 32, 4, 2>;
+using TemporalS2NarrowCfg = RowsCfg<TEMPORAL3, 3, 4, 1, 32, 4, 2>;  // 7 staged frames x 64 columns: 72 KB
 using TemporalS2Cfg = RowsCfg<TEMPORAL3, 4, 4, 2, 32, 4, 2>;
 using TemporalS2WideCfg = RowsCfg<TEMPORAL3, 2, 8, 1, 32, 8, 2>;  // 2 output frames: 5 staged rows fit the registers
 
@@ -1350,11 +1443,17 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
         uint16_t* sout = w_t ? S : static_cast<uint16_t*>(y);
         if (Cin % 8 != 0) {
             // small-Cin 1x1 path (k == 1 is enforced by the ABI): weights used as [Cout][Cin]
-            const long long items = P * ((Cout + 7) / 8);
-            const long long nblk = (items + 255) / 256;
-            if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL(pointwise_small_kernel, dim3((unsigned)nblk), dim3(256), 0, s, (const uint16_t*)x,
-                               (const uint16_t*)w_s, b_s, sout, P, Cin, Cout);
+            const int ng = (Cout + 7) / 8;
+            const dim3 grid((unsigned)small_proj_blocks(P * ng, ng));
+            if (small_proj_staged(Cin, Cout) && Cin <= 8)
+                hipLaunchKernelGGL(pointwise_small_kernel<8>, grid, dim3(256), small_proj_lds(Cin, Cout), s,
+                                   (const uint16_t*)x, (const uint16_t*)w_s, b_s, sout, P, Cin, Cout);
+            else if (small_proj_staged(Cin, Cout))
+                hipLaunchKernelGGL(pointwise_small_kernel<16>, grid, dim3(256), small_proj_lds(Cin, Cout), s,
+                                   (const uint16_t*)x, (const uint16_t*)w_s, b_s, sout, P, Cin, Cout);
+            else
+                hipLaunchKernelGGL(pointwise_small_kernel<0>, grid, dim3(256), 0, s, (const uint16_t*)x,
+                                   (const uint16_t*)w_s, b_s, sout, P, Cin, Cout);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else {
             ConvGeom g{};
@@ -1645,11 +1744,14 @@ hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, cons
 
 hipError_t launch_fsq_dequant_proj(const int32_t* idx, const FsqParams& p, const void* w_p, const float* b_p, void* y,
                                    long long P, int Cout, int32_t* invalid, hipStream_t s) {
-    const long long items = P * ((Cout + 7) / 8);
-    const long long nblk = (items + 255) / 256;
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fsq_dequant_proj_kernel, dim3((unsigned)nblk), dim3(256), 0, s, idx, p,
-                       static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
+    const int ng = (Cout + 7) / 8;
+    const dim3 grid((unsigned)small_proj_blocks(P * ng, ng));
+    if (small_proj_staged(p.D, Cout))  // D <= 8
+        hipLaunchKernelGGL(fsq_dequant_proj_kernel<8>, grid, dim3(256), small_proj_lds(p.D, Cout), s, idx, p,
+                           static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
+    else
+        hipLaunchKernelGGL(fsq_dequant_proj_kernel<0>, grid, dim3(256), 0, s, idx, p,
+                           static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
     return hipGetLastError();
 }
 

@@ -133,14 +133,14 @@ WORKLOADS = {
     # factorized attention on the CV8x8x8-720p token grid of a 121-frame clip (16 x 90 x 160),
     # 256 channels in 4 heads of 64; q, k, v ~ N(0, 1), seeds seed, seed + 1, seed + 2
     "attn_cv8x8x8_720p_tokens": dict(x=(1, 256, 16, 90, 160), heads=4, seed=1006, std=1.0),
-    # a 1080p clip whose length and height the tokenizer does not accept as they are: 50
-    # frames (not 1 + 4k) of 1080 rows (not a multiple of 16), worked through in windows of
-    # 17 frames padded to 1 + 4k frames and 1088 x 1920; pixels N(0, 0.5)
     # encoder / decoder blocks on the CV8x8x8-720p grids of a 121-frame clip: a residual block
     # and the stride-2 downsampling block at the post-Haar grid 31 x 180 x 320 (-> 16 x 90 x
     # 160), the mirrored upsampling block back; 256 channels, x ~ N(0, 1), conv weights
     # N(0, 0.02), LayerNorm scales 1 and shifts 0 (seeds seed .. seed + 9)
     "blocks_cv8x8x8_720p": dict(x=(1, 256, 31, 180, 320), low=(1, 256, 16, 90, 160), seed=1030, w_std=0.02),
+    # a 1080p clip whose length and height the tokenizer does not accept as they are: 50
+    # frames (not 1 + 4k) of 1080 rows (not a multiple of 16), worked through in windows of
+    # 17 frames padded to 1 + 4k frames and 1088 x 1920; pixels N(0, 0.5)
     "window_1080p_50f": dict(x=(1, 3, 50, 1080, 1920), seed=1020, std=0.5, window=17, t_align=4,
                              s_align=16),
 }
