@@ -28,6 +28,7 @@
 //   * attn_temporal_kernel - the other temporal cases (d = 32, or 32 < T, T * C <=
 //     16384): K and V of a few consecutive positions staged in LDS (one contiguous run
 //     per frame), one thread per (position, head, query frame) in fp32.
+#include <algorithm>
 #include <type_traits>
 
 #include "cvt_internal.h"
@@ -426,6 +427,10 @@ struct TAttnMGeom {
     float scale2;   // log2(e) / 8
 };
 
+// The waves loop over sequences (the grid-stride keeps the four waves of a workgroup on the
+// four heads of one position, i.e. one contiguous 512-byte run per frame and tensor) and
+// issue the next sequence's loads before computing the current one, so every wave keeps
+// loads in flight through its compute phase.
 __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t* __restrict__ Q,
                                                                  const uint16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V,
@@ -433,100 +438,141 @@ __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t*
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TM_WAVE_LDS];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sq = blockIdx.x * 4 + wave;
+    const int stride = (int)gridDim.x * 4;
+    int sq = (int)blockIdx.x * 4 + wave;
     if (sq >= g.nseq) return;  // wave-uniform; the kernel has no workgroup barrier
     const int px = lane & 31, hh = lane >> 5;
     const int per_b = g.HW * g.G;
-    const int b = sq / per_b, rem = sq - b * per_b;
-    const int pos = rem / g.G, head = rem - pos * g.G;
-    const long long base = ((long long)b * g.T * g.HW + pos) * g.C + head * 64;  // frame 0 token
-    const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
-    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
+    auto seq_base = [&](int s) {
+        const int b = s / per_b, rem = s - b * per_b;
+        const int pos = rem / g.G, head = rem - pos * g.G;
+        return ((long long)b * g.T * g.HW + pos) * g.C + head * 64;  // frame 0 token
+    };
     // lane (px, hh): frame px (a key for K and V, a query for Q), channels 16 ks + 8 hh ..
     // +7; frames past T read zeros (offset past the buffer)
     const int roff = px < g.T ? px * g.fsb + hh * 16 : 0x7fffff00;
-    bf16x8_t kf[4], qf[4];
-    uint4 vr[4];
+    // past the last sequence (the final prefetch) every offset is past the buffer: zeros, no
+    // memory access; the loads stay unconditional so that the wait before a sequence's
+    // MFMAs covers only its own loads, not the prefetch issued after them
+    auto load = [&](int s, bf16x8_t (&kf)[4], bf16x8_t (&qf)[4], uint4 (&vr)[4]) {
+        const bool live = s < g.nseq;
+        const long long base = seq_base(live ? s : 0);
+        const int ro = live ? roff : 0x7fffff00;
+        const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
+        const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        kf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, roff + ks * 32, 0, 0));
-        qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qres, roff + ks * 32, 0, 0));
-        const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, roff + ks * 32, 0, 0);
-        vr[ks] = *reinterpret_cast<const uint4*>(&vv);
-    }
-    // V^T into the wave's LDS tile: channel 16 ks + 8 hh + e, key px at its k-step column
+        for (int ks = 0; ks < 4; ++ks) {
+            kf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, ro + ks * 32, 0, 0));
+            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qres, ro + ks * 32, 0, 0));
+            const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, ro + ks * 32, 0, 0);
+            vr[ks] = *reinterpret_cast<const uint4*>(&vv);
+        }
+    };
     uint8_t* vt = smem + wave * TM_WAVE_LDS;
     const int col = vperm(px) * 2;
+    bf16x8_t kf[4], qf[4];
+    uint4 vr[4];
+    load(sq, kf, qf, vr);
+    for (;;) {
+        const int nx = sq + stride;
+        bf16x8_t kn[4], qn[4];
+        uint4 vn[4];
+        load(nx, kn, qn, vn);
+        // V^T into the wave's LDS tile: channel 16 ks + 8 hh + e, key px at its k-step column
+        // (the tile is wave-private and its accesses execute in order: the previous
+        // sequence's reads are done)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t w[4] = {vr[ks].x, vr[ks].y, vr[ks].z, vr[ks].w};
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t w[4] = {vr[ks].x, vr[ks].y, vr[ks].z, vr[ks].w};
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int row = ks * 16 + hh * 8 + 2 * e2;
-            *reinterpret_cast<uint16_t*>(vt + row * TM_VRS + col) = (uint16_t)(w[e2] & 0xffffu);
-            *reinterpret_cast<uint16_t*>(vt + (row + 1) * TM_VRS + col) = (uint16_t)(w[e2] >> 16);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int row = ks * 16 + hh * 8 + 2 * e2;
+                *reinterpret_cast<uint16_t*>(vt + row * TM_VRS + col) = (uint16_t)(w[e2] & 0xffffu);
+                *reinterpret_cast<uint16_t*>(vt + (row + 1) * TM_VRS + col) = (uint16_t)(w[e2] >> 16);
+            }
         }
-    }
-    // S^T = K Q^T (rows = keys, columns = queries)
-    f32x16_t st;
+        // S^T = K Q^T (rows = keys, columns = queries)
+        f32x16_t st;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] = 0.0f;
+        for (int e = 0; e < 16; ++e) st[e] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
-    // causal mask: key j after query px (this also masks keys past T for queries < T)
-    float mx = -INFINITY;
+        for (int ks = 0; ks < 4; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+        // causal mask: key j after query px (this also masks keys past T for queries < T)
+        float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int j = 8 * (r / 4) + 4 * hh + (r % 4);
-        if (j > px) st[r] = -INFINITY;
-        mx = fmaxf(mx, st[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m2 = mx * g.scale2;
-    float sum = 0.0f;
-    bf16x8_t pf[2];
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        uint32_t u[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = fast_exp2(fmaf(st[8 * h2 + 2 * e2], g.scale2, -m2));
-            const float p1 = fast_exp2(fmaf(st[8 * h2 + 2 * e2 + 1], g.scale2, -m2));
-            u[e2] = pack_bf16x2(p0, p1);
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e2]), ones, sum, false);
+        for (int r = 0; r < 16; ++r) {
+            const int j = 8 * (r / 4) + 4 * hh + (r % 4);
+            if (j > px) st[r] = -INFINITY;
+            mx = fmaxf(mx, st[r]);
         }
-        pf[h2] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
-    }
-    const float l = sum + __shfl_xor(sum, 32);
-    // the LDS tile is wave-private and its accesses execute in order
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    f32x16_t ot[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ot[cb][e] = 0.0f;
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m2 = mx * g.scale2;
+        float sum = 0.0f;
+        bf16x8_t pf[2];
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const bf16x8_t vf =
-                *reinterpret_cast<const bf16x8_t*>(vt + (cb * 32 + px) * TM_VRS + (h2 * 16 + hh * 8) * 2);
-            ot[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h2], ot[cb], 0, 0, 0);
-        }
-    }
-    if (px < g.T) {
-        const float inv = 1.0f / l;
-        uint16_t* orow = O + base + (long long)px * (g.fsb / 2);
+            uint32_t u[4];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                uint2 u;
-                u.x = pack_bf16x2(ot[cb][4 * q4] * inv, ot[cb][4 * q4 + 1] * inv);
-                u.y = pack_bf16x2(ot[cb][4 * q4 + 2] * inv, ot[cb][4 * q4 + 3] * inv);
-                *reinterpret_cast<uint2*>(orow + cb * 32 + q4 * 8 + hh * 4) = u;
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = fast_exp2(fmaf(st[8 * h2 + 2 * e2], g.scale2, -m2));
+                const float p1 = fast_exp2(fmaf(st[8 * h2 + 2 * e2 + 1], g.scale2, -m2));
+                u[e2] = pack_bf16x2(p0, p1);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e2]), ones, sum, false);
             }
+            pf[h2] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
+        }
+        const float l = sum + __shfl_xor(sum, 32);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x16_t ot[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ot[cb][e] = 0.0f;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const bf16x8_t vf =
+                    *reinterpret_cast<const bf16x8_t*>(vt + (cb * 32 + px) * TM_VRS + (h2 * 16 + hh * 8) * 2);
+                ot[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h2], ot[cb], 0, 0, 0);
+            }
+        }
+        {
+            // O rows staged in the wave's tile (frame px at byte px * 144), then written as
+            // 16-byte pieces, 8 lanes per 128-byte frame row
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const float inv = 1.0f / l;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    uint2 u;
+                    u.x = pack_bf16x2(ot[cb][4 * q4] * inv, ot[cb][4 * q4 + 1] * inv);
+                    u.y = pack_bf16x2(ot[cb][4 * q4 + 2] * inv, ot[cb][4 * q4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(vt + px * 144 + (cb * 32 + q4 * 8 + hh * 4) * 2) = u;
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint16_t* obase = O + seq_base(sq);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int fr = it * 8 + (lane >> 3), c8 = lane & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(vt + fr * 144 + c8 * 16);
+                if (fr < g.T) *reinterpret_cast<uint4*>(obase + (long long)fr * (g.fsb / 2) + c8 * 8) = v;
+            }
+        }
+        if (nx >= g.nseq) break;
+        sq = nx;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kf[ks] = kn[ks];
+            qf[ks] = qn[ks];
+            vr[ks] = vn[ks];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // this sequence's V^T reads before the next writes
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -581,7 +627,10 @@ hipError_t launch_attention3d(const void* q, const void* k, const void* v, void*
         g.fsb = (int)fsb;
         g.ext = (int)ext;
         g.scale2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-        hipLaunchKernelGGL(attn_temporal_mfma_kernel, dim3((unsigned)((nseq + 3) / 4)), dim3(256), 0, s, Q, K, V, O, g);
+        // persistent: three workgroups per CU (the occupancy its registers allow), each wave prefetching
+        // its next sequence
+        const long long nwg = std::min((nseq + 3) / 4, 256LL * 3);
+        hipLaunchKernelGGL(attn_temporal_mfma_kernel, dim3((unsigned)nwg), dim3(256), 0, s, Q, K, V, O, g);
         return hipGetLastError();
     }
     switch (d) {
