@@ -25,7 +25,8 @@ the factorized self-attention (spatial and causal temporal) on the 16 x 90 x 160
 grid of the CV8x8x8-720p model, 256 channels in 4 heads; a fifth, sliding windows of 17
 frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop); a sixth, the encoder's
 residual and downsampling blocks and the decoder's upsampling block on the CV8x8x8-720p grids; a
-seventh, the batched DV4x8x8-360p decode (8 clips: dequantize + 1x1, conv 192->192, inverse Haar).
+seventh, the batched DV4x8x8-360p decode (8 clips: dequantize + 1x1, conv 192->192, inverse Haar); an
+eighth, the 121-frame clip encoded as a stream of chunks against one whole-clip pass.
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -72,6 +73,7 @@ def parse():
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window measurement")
     ap.add_argument("--no-blocks", action="store_true", help="skip the encoder/decoder block measurement")
     ap.add_argument("--no-c5", action="store_true", help="skip the batched 360p decode measurement")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-encode measurement")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -202,6 +204,7 @@ def main():
     win = None if args.no_window else windowed_1080p(cvt, si, torch, dev, args)
     blk = None if args.no_blocks else blocks_cv8x8x8(cvt, si, torch, dev, args)
     c5 = None if args.no_c5 else decode_c5(cvt, si, torch, dev, args)
+    stream = None if args.no_stream else stream_encode(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -242,6 +245,7 @@ def main():
         "window_1080p_50f": win,
         "blocks_cv8x8x8_720p": blk,
         "dv4x8x8_360p_decode_c5": c5,
+        "stream_encode_121f_720p": stream,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -624,6 +628,90 @@ def decode_c5(cvt, si, torch, dev, args):
     out["chain_ms"] = round(total, 4)
     out["frames_per_s"] = round(out["out_frames"] / (total * 1e-3), 1)
     del idx, z, yc, codes, xo, ws, ws1
+    torch.cuda.empty_cache()
+    return out
+
+
+def stream_encode(cvt, si, torch, dev, args):
+    """Streaming causal encode of a 121-frame 720p clip (the CV8x8x8-720p shape, G_trans
+    pixels) to FSQ indices, chunk by chunk: a first chunk of 17 frames (Haar with the causal
+    first frame), then chunks of 16 frames (Haar continuation), each through the spatial conv
+    192 -> 256 and the causal temporal conv 256 -> 256 with the 1x1 -> 6 fused, reading the
+    previous chunk's last two frames in place of the zero padding, then FSQ.  The result
+    equals the whole-clip encode bit for bit; reported against the whole clip in one pass."""
+    wl = si.WORKLOADS["c3_cv8x8x8_720p_121f"]
+    B, C, T, H, W = wl["x"]
+    log(f"stream encode: generating {wl['x']} ...")
+    xb = si.to_bf16_bits(si.video_trans(wl["x"], wl["seed"]))
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
+    del xb
+
+    def bf(shape, seed):
+        bits = si.to_bf16_bits(si.normal(shape, seed, 0.02))
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w_s, w_t, w_p = bf((256, 192, 1, 3, 3), 3101), bf((256, 256, 3, 1, 1), 3102), bf((6, 256, 1, 1, 1), 3103)
+    cl = torch.channels_last_3d
+    Hq, Wq = H // 4, W // 4
+    cuts = [(0, 17, 2)] + [(t, t + 16, 3) for t in range(17, T, 16)]  # 17 + 7 x 16 = 129 > 121: clip the last
+    cuts = [(a, min(b, T), tl) for a, b, tl in cuts if a < T]
+    assert all((b - a) % 4 == 0 for a, b, tl in cuts if tl == 3), "continuation chunks of 4k frames"
+    bufs = []
+    for a, b, tl in cuts:
+        tq = 1 + (b - a - 1) // 4 if tl == 2 else (b - a) // 4
+        bufs.append(dict(
+            x=x[:, :, a:b],
+            hz=torch.empty((B, 192, tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl),
+            s=torch.empty((B, 256, tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl),
+            lat=torch.empty((B, 6, tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl),
+            idx=torch.empty((B, tq, Hq, Wq), dtype=torch.int32, device=dev), tl=tl))
+    xs = [bb["x"].contiguous() for bb in bufs]  # chunk inputs as the caller would hand them over
+    ws_s = torch.empty(cvt.conv_workspace_bytes(bufs[1]["hz"].shape, 256, 3, True, False), dtype=torch.uint8,
+                       device=dev)
+    ws_t = torch.empty(cvt.temporal_stream_workspace_bytes(256, 6), dtype=torch.uint8, device=dev)
+    Tq = 1 + (T - 1) // 4
+    hz_w = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    s_w = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    lat_w = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    idx_w = torch.empty((B, Tq, Hq, Wq), dtype=torch.int32, device=dev)
+    ws_sw = torch.empty(cvt.conv_workspace_bytes(hz_w.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)
+    ws_tw = torch.empty(cvt.conv_proj_workspace_bytes(s_w.shape, 256, 6, 3, False, True), dtype=torch.uint8,
+                        device=dev)
+
+    def streamed():
+        prev = None
+        for xc, bb in zip(xs, bufs):
+            cvt.haar3d_fwd(xc, bb["tl"], out=bb["hz"])
+            cvt.causal_conv3d_fact(bb["hz"], w_s, None, workspace=ws_s, out=bb["s"])
+            hist = None if prev is None else prev[:, :, -2:]
+            cvt.causal_conv3d_temporal_stream(bb["s"], w_t, hist=hist, w_p=w_p, workspace=ws_t, out=bb["lat"])
+            cvt.fsq_quantize(bb["lat"], indices=bb["idx"])
+            prev = bb["s"]
+
+    def whole():
+        cvt.haar3d_fwd(x, 2, out=hz_w)
+        cvt.causal_conv3d_fact(hz_w, w_s, None, workspace=ws_sw, out=s_w)
+        cvt.causal_conv3d_fact_proj(s_w, None, w_t, w_p, workspace=ws_tw, out=lat_w)
+        cvt.fsq_quantize(lat_w, indices=idx_w)
+
+    for _ in range(max(3, min(args.warmup, 10))):
+        streamed()
+        whole()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(torch.cat([bb["idx"] for bb in bufs], dim=1), idx_w))
+    reps = max(3, args.steps // 4)
+    out = {"clip": list(wl["x"]), "chunks_frames": [b - a for a, b, _ in cuts], "indices_equal_whole_clip": same}
+    for name, fn in (("streamed", streamed), ("whole_clip", whole)):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out[name] = {"ms": round(ms, 4), "frames_per_s": round(B * T / (ms * 1e-3), 1)}
+    del x, xs, bufs, hz_w, s_w, lat_w, idx_w
     torch.cuda.empty_cache()
     return out
 
