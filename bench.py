@@ -435,8 +435,10 @@ def windowed_1080p(cvt, si, torch, dev, args):
     """Sliding windows over a clip the tokenizer does not accept as it is (1 x 3 x 50 x
     1080 x 1920 bf16): per window of 17 frames, pad (mirror in time to 1 + 4k frames, zeros
     to 1088 rows), 2-level Haar, inverse Haar, crop back into the output clip.  Reports the
-    whole windowed round trip in frames/s and the pad and crop kernels against the HBM
-    peak (bytes read + written by each call, summed over the windows)."""
+    whole windowed round trip in frames/s, unfused (four calls per window) and fused (the
+    padding inside the Haar's loads, the crop inside the inverse's stores: two calls), and
+    the pad and crop kernels against the HBM peak (bytes read + written by each call,
+    summed over the windows)."""
     wl = si.WORKLOADS["window_1080p_50f"]
     shape = wl["x"]
     B, C, T, H, W = shape
@@ -466,14 +468,24 @@ def windowed_1080p(cvt, si, torch, dev, args):
             cvt.haar3d_inv(c, 2, out=r)
             cvt.video_unpad(r, out, t0, nt)
 
+    out_f = torch.empty_like(x)
+
+    def round_trip_fused():  # the padding inside the Haar's loads, the crop inside the inverse's stores
+        for (t0, nt, Tp, Hp, Wp), c in zip(wins, coef):
+            cvt.haar3d_fwd_window(x, t0, nt, Tp, Hp, Wp, 2, out=c)
+            cvt.haar3d_inv_window(c, out_f, t0, nt, 2)
+
     for _ in range(max(3, min(args.warmup, 10))):
+        round_trip_fused()
         round_trip()
     torch.cuda.synchronize()
     reps = max(5, args.steps // 2)
     res = {"shape": list(shape), "windows": [list(w) for w in wins]}
+    res["fused_equals_unfused"] = bool(torch.equal(out_f.view(torch.int16), out.view(torch.int16)))
     pad_bytes = sum(2.0 * B * C * (nt * H * W + Tp * Hp * Wp) for _, nt, Tp, Hp, Wp in wins)
     crop_bytes = sum(2.0 * B * C * 2 * nt * H * W for _, nt, _, _, _ in wins)
-    for name, fn, nbytes in (("pad", pads, pad_bytes), ("crop", crops, crop_bytes), ("round_trip", round_trip, None)):
+    for name, fn, nbytes in (("pad", pads, pad_bytes), ("crop", crops, crop_bytes), ("round_trip", round_trip, None),
+                             ("round_trip_fused", round_trip_fused, None)):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -492,7 +504,7 @@ def windowed_1080p(cvt, si, torch, dev, args):
     # coefficients and pixels rounds)
     err = (out.float() - x.float()).abs().max().item()
     res["round_trip_max_abs_err"] = err
-    del x, out, bufs, coef, rec
+    del x, out, out_f, bufs, coef, rec
     torch.cuda.empty_cache()
     return res
 

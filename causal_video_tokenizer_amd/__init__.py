@@ -56,6 +56,8 @@ SIGNATURES = {
     "cvt_video_window": (_ci, [_ci] * 7 + [_pi] * 6),
     "cvt_video_pad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
     "cvt_video_unpad": (_ci, [_vp, _vp] + [_ci] * 11 + [_vp]),
+    "cvt_haar3d_fwd_window": (_ci, [_vp, _ci, _vp, _ci, _ci] + [_ci] * 11 + [_vp]),
+    "cvt_haar3d_inv_window": (_ci, [_vp, _ci, _ci, _vp, _ci] + [_ci] * 11 + [_vp]),
     "cvt_causal_conv3d_fact_proj_fsq_workspace": (_sz, [_ci] * 9),
     "cvt_causal_conv3d_fact_proj_fsq": (_ci, [_vp] * 7 + [_vp, _ci, _vp, _vp] + [_ci] * 7 + [_vp, _sz, _vp]),
     "cvt_fsq_dequantize_proj": (_ci, [_vp, _vp, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
@@ -447,6 +449,48 @@ def video_unpad(y, clip, t0, nt):
         raise ValueError("y and clip must have the same batch and channels")
     _check(lib.cvt_video_unpad(_ptr(y), _ptr(clip), _dtype_code(clip.dtype), B, C, T, H, W, t0, nt, Tp, Hp, Wp,
                                _stream(clip.device)), "video_unpad")
+    return clip
+
+
+def haar3d_fwd_window(x, t0, nt, Tp, Hp, Wp, temporal_levels=2, out_dtype=None, layout="NTHWC", out=None):
+    """Forward Haar patcher of window (t0, nt) of the clip x [B, C, T, H, W] (NCTHW) padded to
+    Tp x Hp x Wp as video_pad pads it: the coefficients haar3d_fwd(video_pad(x, ...)) gives,
+    computed without writing the padded window."""
+    _require_gpu(x)
+    if not x.is_contiguous():
+        raise ValueError("x must be NCTHW-contiguous")
+    B, C, T, H, W = x.shape
+    lay = CVT_NTHWC if layout == "NTHWC" else CVT_NCTHW
+    odt = out_dtype or (out.dtype if out is not None else x.dtype)
+    if temporal_levels == 2:
+        shape = (B, 64 * C, 1 + max(Tp - 1, 0) // 4, Hp // 4, Wp // 4)
+    else:
+        shape = (B, 16 * C, Tp, Hp // 4, Wp // 4)
+    y = _check_out(out, shape, odt, x.device, lay) if out is not None else _empty5(shape, odt, x.device, lay)
+    _check(lib.cvt_haar3d_fwd_window(_ptr(x), _dtype_code(x.dtype), _ptr(y), _dtype_code(y.dtype), lay, B, C, T, H, W,
+                                     t0, nt, Tp, Hp, Wp, temporal_levels, _stream(x.device)), "haar3d_fwd_window")
+    return y
+
+
+def haar3d_inv_window(y, clip, t0, nt, temporal_levels=2):
+    """Inverse Haar patcher of a padded window's coefficients y (either layout) written
+    straight into frames t0 .. t0+nt-1 of ``clip`` [B, C, T, H, W] (NCTHW, in place), cropped
+    to the clip's H x W: what video_unpad(haar3d_inv(y), clip, t0, nt) gives.  Returns clip."""
+    _require_gpu(y, clip)
+    if not clip.is_contiguous():
+        raise ValueError("clip must be NCTHW-contiguous")
+    lay = _layout_of(y)
+    B, NCH, Tq, Hq, Wq = y.shape
+    G = 64 if temporal_levels == 2 else 16
+    if NCH % G:
+        raise ValueError(f"coefficient channels must be a multiple of {G}")
+    Bc, C, T, H, W = clip.shape
+    if (Bc, C) != (B, NCH // G):
+        raise ValueError("y and clip must have the same batch and pixel channels")
+    Tp = 4 * Tq - 3 if temporal_levels == 2 else Tq
+    _check(lib.cvt_haar3d_inv_window(_ptr(y), _dtype_code(y.dtype), lay, _ptr(clip), _dtype_code(clip.dtype), B, C, T,
+                                     H, W, t0, nt, Tp, 4 * Hq, 4 * Wq, temporal_levels, _stream(y.device)),
+           "haar3d_inv_window")
     return clip
 
 

@@ -70,6 +70,15 @@ int check_haar(const void* a, int a_dt, const void* b, int b_dt, int layout, int
     return CVT_OK;
 }
 
+// pix: the clip, coef: the padded window's coefficients.
+int check_haar_window(const void* pix, int pix_dt, const void* coef, int coef_dt, int layout, int B, int C, int T,
+                      int H, int W, int t0, int nt, int Tp, int Hp, int Wp, int tl) {
+    if (tl == 3) return fail(CVT_E_SHAPE, "a window starts with its own causal first frame: temporal_levels 0 or 2");
+    int st = check_haar(coef, coef_dt, pix, pix_dt, layout, B, C, Tp, Hp, Wp, tl);
+    if (st != CVT_OK) return st;
+    return check_window(pix, coef, pix_dt, B, C, T, H, W, t0, nt, Tp, Hp, Wp, Tp);
+}
+
 // FSQ breakpoints.  For L levels with h = (L-1)(1+eps)/2, o = 1/2 (L even) or
 // 0, s = atanh(o/h), the rounded bound q = rint(tanh(z+s) h - o) steps from j
 // to j+1 where tanh(z+s) h - o = j + 1/2, i.e. at z_j = atanh((j+1/2+o)/h) - s,
@@ -360,6 +369,28 @@ int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int 
     if (st != CVT_OK) return st;
     return hip_status(cvt::launch_video_unpad(y, x, dtype, B, C, T, H, W, t0, nt, Tp, Hp, Wp, (hipStream_t)stream),
                       "cvt_video_unpad launch");
+}
+
+int cvt_haar3d_fwd_window(const void* x, int x_dtype, void* y, int y_dtype, int y_layout, int B, int C, int T, int H,
+                          int W, int t0, int nt, int Tp, int Hp, int Wp, int temporal_levels, void* stream) {
+    const int st = check_haar_window(x, x_dtype, y, y_dtype, y_layout, B, C, T, H, W, t0, nt, Tp, Hp, Wp,
+                                     temporal_levels);
+    if (st != CVT_OK) return st;
+    const cvt::ClipWindow win{T, H, W, t0, nt};
+    return hip_status(cvt::launch_haar_fwd(x, x_dtype, y, y_dtype, y_layout, B, C, Tp, Hp, Wp, temporal_levels,
+                                           (hipStream_t)stream, &win),
+                      "cvt_haar3d_fwd_window launch");
+}
+
+int cvt_haar3d_inv_window(const void* y, int y_dtype, int y_layout, void* x, int x_dtype, int B, int C, int T, int H,
+                          int W, int t0, int nt, int Tp, int Hp, int Wp, int temporal_levels, void* stream) {
+    const int st = check_haar_window(x, x_dtype, y, y_dtype, y_layout, B, C, T, H, W, t0, nt, Tp, Hp, Wp,
+                                     temporal_levels);
+    if (st != CVT_OK) return st;
+    const cvt::ClipWindow win{T, H, W, t0, nt};
+    return hip_status(cvt::launch_haar_inv(y, y_dtype, y_layout, x, x_dtype, B, C, Tp, Hp, Wp, temporal_levels,
+                                           (hipStream_t)stream, &win),
+                      "cvt_haar3d_inv_window launch");
 }
 
 int cvt_layernorm3d(const void* x, const float* gamma, const float* beta, void* y, int B, int C, int T, int H, int W,

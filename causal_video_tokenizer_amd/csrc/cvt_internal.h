@@ -52,16 +52,35 @@ __device__ __forceinline__ void st_stream16(void* p, uint4 v) {
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
 }
 
+// One window of a clip (sliding windows over a video of any length): frames t0 .. t0+nt-1
+// of a T x H x W clip, seen as a padded window whose frame p is clip frame
+// t0 + mirror_frame(p, nt) and whose rows >= H and columns >= W are zero.
+struct ClipWindow {
+    int T, H, W;  // the clip
+    int t0, nt;   // the window's frames
+};
+
+// Padded frame t of an n-frame window: t itself inside the window, then the mirror about
+// the last frame without repeating it, bouncing between the two ends (period 2(n-1)).
+__device__ __forceinline__ int mirror_frame(int t, int n) {
+    if (n == 1) return 0;
+    const int p = 2 * (n - 1);
+    const int m = t % p;
+    return m < n ? m : p - m;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are already
 // validated by the C ABI layer.
 
+// win == nullptr: x is the whole [B, C, T, H, W] input.  Otherwise T, H, W are the padded
+// window's sizes and the pixels come from (go to) the clip win describes.
 hipError_t launch_haar_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout,
                            int B, int C, int T, int H, int W, int temporal_levels,
-                           hipStream_t stream);
+                           hipStream_t stream, const ClipWindow* win = nullptr);
 hipError_t launch_haar_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype,
                            int B, int C, int T, int H, int W, int temporal_levels,
-                           hipStream_t stream);
+                           hipStream_t stream, const ClipWindow* win = nullptr);
 
 // FSQ parameters precomputed on the host (double precision) and passed by value.
 constexpr int FSQ_MAX_D = 8;

@@ -21,6 +21,13 @@
 // A continuation chunk of a stream (pad = 0) has no leading copies: its latent
 // frame j is frames 4j .. 4j+3, exactly the latent frame the whole clip gives there.
 //
+// Sliding windows (WM != 0): the kernels can also read one window of a longer clip as the
+// padded window the tokenizer accepts (time mirrored about the window's last frame, zero
+// rows and columns past the frame) and write the inverse straight back into the clip,
+// cropped, so neither the padded window nor its reconstruction is materialised.  WM = 1
+// when the clip's width is a multiple of 4 (a 4-pixel group is wholly inside the clip's
+// row or wholly past it), WM = 2 for rows of any length, accessed element by element.
+//
 // Mapping: one wavefront per (b, t', h', run of 64 w' positions); lane = w'.
 // Each lane loads the 4 x 4 x 4 block of every input channel with 8-byte
 // (bf16) or 16-byte (fp32) streaming row loads, so each load instruction covers
@@ -70,6 +77,39 @@ __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16(
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
+
+// Window access: 4 pixels of row h from column w of a clip frame plane; rows >= H and
+// columns >= W of the padded window read as zero and are not written.
+template <int WM, typename T>
+__device__ __forceinline__ void load4_win(const T* plane, int h, int w, const ClipWindow& win, float* v) {
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+    if (h >= win.H || w >= win.W) return;
+    const T* p = plane + (size_t)h * win.W + w;
+    if (WM == 1) {
+        load4(p, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w + k < win.W) v[k] = load1(p + k);
+    }
+}
+template <int WM, typename T>
+__device__ __forceinline__ void store4_win(T* plane, int h, int w, const ClipWindow& win, const float* v) {
+    if (h >= win.H || w >= win.W) return;
+    T* p = plane + (size_t)h * win.W + w;
+    if (WM == 1) {
+        store4(p, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w + k < win.W) store1(p + k, v[k]);
+    }
+}
+// Clip frame plane of padded (forward) or cropped (inverse) window frame p, channel plane bc.
+template <typename T>
+__device__ __forceinline__ T* clip_plane(T* x, int bc, int frame, const ClipWindow& win) {
+    return x + ((size_t)bc * win.T + win.t0 + frame) * win.H * (size_t)win.W;
+}
 
 // Output channel of packet rows (rt, rh, rw) for input channel c.
 template <int NF>
@@ -140,6 +180,7 @@ template <>
 struct Row4<uint16_t> {
     uint2 u;
     __device__ void load(const uint16_t* p) { u = ld_stream8(p); }
+    __device__ void zero() { u = make_uint2(0u, 0u); }
     __device__ void get(float* v) const {
         v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
     }
@@ -151,6 +192,7 @@ struct Row4<float> {
         const uint4 w = ld_stream16(p);
         u = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
+    __device__ void zero() { u = make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
     __device__ void get(float* v) const { v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; }
 };
 
@@ -180,10 +222,11 @@ __device__ __forceinline__ void block_transform(float (&v)[NF][4][4]) {
 // the wave then copies its 64 contiguous rows out with 16-byte coalesced stores.
 // LDS row stride = row bytes + 16, so the 128-bit row accesses of 16 lanes fall
 // on distinct banks.
-template <typename Tin, typename Tout, int NF, int CT>
+template <typename Tin, typename Tout, int NF, int CT, int WM>
 __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
                                                              int T, int H, int W, int Tq, int Hq, int Wq,
-                                                             int nchunk, int pad) {
+                                                             int nchunk, int pad, ClipWindow win) {
+    static_assert(WM == 0 || WM == 1, "rows of any length take the generic kernel");
     constexpr int C = CT;
     constexpr int G = NF == 4 ? 64 : 16;
     constexpr int NCH = G * C;
@@ -205,9 +248,21 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             const int src = NF == 4 ? max(4 * tile.tq + f - pad, 0) : tile.tq;
-            const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * wq_ld;
+            if constexpr (WM == 0) {
+                const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * wq_ld;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) raw[c][f][r].load(base + (size_t)r * W);
+                for (int r = 0; r < 4; ++r) raw[c][f][r].load(base + (size_t)r * W);
+            } else {
+                const Tin* plane = clip_plane(x, tile.b * C + c, mirror_frame(src, win.nt), win);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int h = 4 * tile.hq + r;
+                    if (h < win.H && 4 * wq_ld < win.W)
+                        raw[c][f][r].load(plane + (size_t)h * win.W + 4 * wq_ld);
+                    else
+                        raw[c][f][r].zero();
+                }
+            }
         }
 
     // 2. transform, in output channel order
@@ -251,10 +306,11 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
 // Fast inverse kernel: compile-time CT, NTHWC input staged through LDS with
 // coalesced 16-byte streaming loads; each lane reads its row back with 128-bit
 // LDS reads.
-template <typename Tin, typename Tout, int NF, int CT>
+template <typename Tin, typename Tout, int NF, int CT, int WM>
 __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restrict__ y, Tout* __restrict__ x,
                                                              int T, int H, int W, int Tq, int Hq, int Wq,
-                                                             int nchunk, int pad) {
+                                                             int nchunk, int pad, ClipWindow win) {
+    static_assert(WM == 0 || WM == 1, "rows of any length take the generic kernel");
     constexpr int C = CT;
     constexpr int G = NF == 4 ? 64 : 16;
     constexpr int NCH = G * C;
@@ -308,13 +364,25 @@ __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restri
         for (int f = 0; f < NF; ++f) {
             const int t = NF == 4 ? 4 * tile.tq + f - pad : tile.tq;  // drop the leading padded frames
             if (t < 0) continue;
-            Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
+            if constexpr (WM == 0) {
+                Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float o[4];
+                for (int r = 0; r < 4; ++r) {
+                    float o[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
-                store4(base + (size_t)r * W, o);
+                    for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                    store4(base + (size_t)r * W, o);
+                }
+            } else {
+                if (t >= win.nt) continue;  // frames of the time padding are cropped
+                Tout* plane = clip_plane(x, tile.b * C + c, t, win);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                    store4_win<WM>(plane, 4 * tile.hq + r, 4 * tile.wq, win, o);
+                }
             }
         }
     }
@@ -323,10 +391,10 @@ __global__ __launch_bounds__(64) void haar_inv_staged_kernel(const Tin* __restri
 // ---------------------------------------------------------------------------------------------
 // Generic kernels (runtime channel count, either layout, no staging): correct for
 // every shape the ABI accepts; used when the fast kernels do not apply.
-template <typename Tin, typename Tout, int NF, int LAYOUT>
+template <typename Tin, typename Tout, int NF, int LAYOUT, int WM>
 __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restrict__ x, Tout* __restrict__ y, int C,
                                                               int T, int H, int W, int Tq, int Hq, int Wq,
-                                                              int nchunk, int pad) {
+                                                              int nchunk, int pad, ClipWindow win) {
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     if (!tile.valid) return;
     const int NCH = (NF == 4 ? 64 : 16) * C;
@@ -336,9 +404,15 @@ __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restr
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             const int src = NF == 4 ? max(4 * tile.tq + f - pad, 0) : tile.tq;
-            const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * tile.wq;
+            if constexpr (WM == 0) {
+                const Tin* base = x + (((size_t)(tile.b * C + c) * T + src) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) load4(base + (size_t)r * W, v[f][r]);
+                for (int r = 0; r < 4; ++r) load4(base + (size_t)r * W, v[f][r]);
+            } else {
+                const Tin* plane = clip_plane(x, tile.b * C + c, mirror_frame(src, win.nt), win);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) load4_win<WM>(plane, 4 * tile.hq + r, 4 * tile.wq, win, v[f][r]);
+            }
         }
         block_transform<NF>(v);
 #pragma unroll
@@ -356,10 +430,10 @@ __global__ __launch_bounds__(64) void haar_fwd_generic_kernel(const Tin* __restr
     }
 }
 
-template <typename Tin, typename Tout, int NF, int LAYOUT>
+template <typename Tin, typename Tout, int NF, int LAYOUT, int WM>
 __global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restrict__ y, Tout* __restrict__ x, int C,
                                                               int T, int H, int W, int Tq, int Hq, int Wq,
-                                                              int nchunk, int pad) {
+                                                              int nchunk, int pad, ClipWindow win) {
     const WaveTile tile = decode_tile(Tq, Hq, Wq, nchunk);
     if (!tile.valid) return;
     const int NCH = (NF == 4 ? 64 : 16) * C;
@@ -383,94 +457,132 @@ __global__ __launch_bounds__(64) void haar_inv_generic_kernel(const Tin* __restr
         for (int f = 0; f < NF; ++f) {
             const int t = NF == 4 ? 4 * tile.tq + f - pad : tile.tq;
             if (t < 0) continue;
-            Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
+            if constexpr (WM == 0) {
+                Tout* base = x + (((size_t)(tile.b * C + c) * T + t) * H + 4 * tile.hq) * W + 4 * tile.wq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float o[4];
+                for (int r = 0; r < 4; ++r) {
+                    float o[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
-                store4(base + (size_t)r * W, o);
+                    for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                    store4(base + (size_t)r * W, o);
+                }
+            } else {
+                if (t >= win.nt) continue;
+                Tout* plane = clip_plane(x, tile.b * C + c, t, win);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = v[f][r][k] * scale;
+                    store4_win<WM>(plane, 4 * tile.hq + r, 4 * tile.wq, win, o);
+                }
             }
         }
     }
 }
 
 // pad: leading copies of frame 0 (3 for a clip or a stream's first chunk, 0 for a
-// continuation chunk of 4k frames)
-template <typename Tin, typename Tout, int NF, int LAYOUT>
-hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int W, int pad, hipStream_t s) {
+// continuation chunk of 4k frames).  T, H, W: the (padded window's) pixel sizes.
+template <typename Tin, typename Tout, int NF, int LAYOUT, int WM>
+hipError_t launch_fwd_t(const void* x, void* y, int B, int C, int T, int H, int W, int pad, const ClipWindow& win,
+                        hipStream_t s) {
     const int Tq = NF == 4 ? (T + pad) / 4 : T, Hq = H / 4, Wq = W / 4;
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (LAYOUT == CVT_NTHWC && C == 3)
-        hipLaunchKernelGGL((haar_fwd_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)x, (Tout*)y, T, H, W, Tq, Hq, Wq, nchunk, pad);
-    else
-        hipLaunchKernelGGL((haar_fwd_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk, pad);
+    bool staged = false;
+    if constexpr (LAYOUT == CVT_NTHWC && WM != 2) {
+        if (C == 3) {
+            hipLaunchKernelGGL((haar_fwd_staged_kernel<Tin, Tout, NF, 3, WM>), dim3((unsigned)nblk), dim3(64), 0, s,
+                               (const Tin*)x, (Tout*)y, T, H, W, Tq, Hq, Wq, nchunk, pad, win);
+            staged = true;
+        }
+    }
+    if (!staged)
+        hipLaunchKernelGGL((haar_fwd_generic_kernel<Tin, Tout, NF, LAYOUT, WM>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)x, (Tout*)y, C, T, H, W, Tq, Hq, Wq, nchunk, pad, win);
     return hipGetLastError();
 }
 
-template <typename Tin, typename Tout, int NF, int LAYOUT>
-hipError_t launch_inv_t(const void* y, void* x, int B, int C, int T, int H, int W, int pad, hipStream_t s) {
+template <typename Tin, typename Tout, int NF, int LAYOUT, int WM>
+hipError_t launch_inv_t(const void* y, void* x, int B, int C, int T, int H, int W, int pad, const ClipWindow& win,
+                        hipStream_t s) {
     const int Tq = NF == 4 ? (T + pad) / 4 : T, Hq = H / 4, Wq = W / 4;
     const int nchunk = (Wq + 63) / 64;
     const long long nblk = (long long)B * Tq * Hq * nchunk;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (LAYOUT == CVT_NTHWC && C == 3)
-        hipLaunchKernelGGL((haar_inv_staged_kernel<Tin, Tout, NF, 3>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)y, (Tout*)x, T, H, W, Tq, Hq, Wq, nchunk, pad);
-    else
-        hipLaunchKernelGGL((haar_inv_generic_kernel<Tin, Tout, NF, LAYOUT>), dim3((unsigned)nblk), dim3(64), 0, s,
-                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk, pad);
+    bool staged = false;
+    if constexpr (LAYOUT == CVT_NTHWC && WM != 2) {
+        if (C == 3) {
+            hipLaunchKernelGGL((haar_inv_staged_kernel<Tin, Tout, NF, 3, WM>), dim3((unsigned)nblk), dim3(64), 0, s,
+                               (const Tin*)y, (Tout*)x, T, H, W, Tq, Hq, Wq, nchunk, pad, win);
+            staged = true;
+        }
+    }
+    if (!staged)
+        hipLaunchKernelGGL((haar_inv_generic_kernel<Tin, Tout, NF, LAYOUT, WM>), dim3((unsigned)nblk), dim3(64), 0, s,
+                           (const Tin*)y, (Tout*)x, C, T, H, W, Tq, Hq, Wq, nchunk, pad, win);
     return hipGetLastError();
 }
+
+// Window mode: 0 = the whole input, 1 = a window of a clip whose width is a multiple of 4,
+// 2 = a window of a clip with rows of any length.
+int window_mode(const ClipWindow* win) { return !win ? 0 : (win->W % 4 == 0 ? 1 : 2); }
 
 // tl: 0 = per-frame 2D patcher; 2 = 3D with the causal first frame; 3 = 3D continuation
 // chunk (frames 4j .. 4j+3 form latent frame j, no leading copies)
-template <typename Tin, typename Tout>
-hipError_t fwd_by_shape(const void* x, void* y, int layout, int B, int C, int T, int H, int W, int tl, hipStream_t s) {
-    if (tl == 2 || tl == 3) {
-        const int pad = tl == 2 ? 3 : 0;
-        return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 4, CVT_NTHWC>(x, y, B, C, T, H, W, pad, s)
-                                   : launch_fwd_t<Tin, Tout, 4, CVT_NCTHW>(x, y, B, C, T, H, W, pad, s);
-    }
-    return layout == CVT_NTHWC ? launch_fwd_t<Tin, Tout, 1, CVT_NTHWC>(x, y, B, C, T, H, W, 0, s)
-                               : launch_fwd_t<Tin, Tout, 1, CVT_NCTHW>(x, y, B, C, T, H, W, 0, s);
+template <bool FWD, typename Tin, typename Tout, int NF, int LAYOUT, int WM>
+hipError_t launch_dir(const void* a, void* b, int B, int C, int T, int H, int W, int pad, const ClipWindow& w,
+                      hipStream_t s) {
+    if constexpr (FWD) return launch_fwd_t<Tin, Tout, NF, LAYOUT, WM>(a, b, B, C, T, H, W, pad, w, s);
+    else return launch_inv_t<Tin, Tout, NF, LAYOUT, WM>(a, b, B, C, T, H, W, pad, w, s);
 }
 
-template <typename Tin, typename Tout>
-hipError_t inv_by_shape(const void* y, void* x, int layout, int B, int C, int T, int H, int W, int tl, hipStream_t s) {
+template <bool FWD, typename Tin, typename Tout, int NF, int LAYOUT>
+hipError_t dispatch_wm(const void* a, void* b, int B, int C, int T, int H, int W, int pad, const ClipWindow* win,
+                       hipStream_t s) {
+    const ClipWindow w = win ? *win : ClipWindow{T, H, W, 0, T};
+    switch (window_mode(win)) {
+        case 0: return launch_dir<FWD, Tin, Tout, NF, LAYOUT, 0>(a, b, B, C, T, H, W, pad, w, s);
+        case 1: return launch_dir<FWD, Tin, Tout, NF, LAYOUT, 1>(a, b, B, C, T, H, W, pad, w, s);
+        default: return launch_dir<FWD, Tin, Tout, NF, LAYOUT, 2>(a, b, B, C, T, H, W, pad, w, s);
+    }
+}
+
+template <bool FWD, typename Tin, typename Tout>
+hipError_t by_shape(const void* a, void* b, int layout, int B, int C, int T, int H, int W, int tl, const ClipWindow* win,
+                    hipStream_t s) {
     if (tl == 2 || tl == 3) {
         const int pad = tl == 2 ? 3 : 0;
-        return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 4, CVT_NTHWC>(y, x, B, C, T, H, W, pad, s)
-                                   : launch_inv_t<Tin, Tout, 4, CVT_NCTHW>(y, x, B, C, T, H, W, pad, s);
+        return layout == CVT_NTHWC ? dispatch_wm<FWD, Tin, Tout, 4, CVT_NTHWC>(a, b, B, C, T, H, W, pad, win, s)
+                                   : dispatch_wm<FWD, Tin, Tout, 4, CVT_NCTHW>(a, b, B, C, T, H, W, pad, win, s);
     }
-    return layout == CVT_NTHWC ? launch_inv_t<Tin, Tout, 1, CVT_NTHWC>(y, x, B, C, T, H, W, 0, s)
-                               : launch_inv_t<Tin, Tout, 1, CVT_NCTHW>(y, x, B, C, T, H, W, 0, s);
+    return layout == CVT_NTHWC ? dispatch_wm<FWD, Tin, Tout, 1, CVT_NTHWC>(a, b, B, C, T, H, W, 0, win, s)
+                               : dispatch_wm<FWD, Tin, Tout, 1, CVT_NCTHW>(a, b, B, C, T, H, W, 0, win, s);
 }
 
 }  // namespace
 
 hipError_t launch_haar_fwd(const void* x, int x_dtype, void* y, int y_dtype, int y_layout, int B, int C,
-                           int T, int H, int W, int temporal_levels, hipStream_t s) {
+                           int T, int H, int W, int temporal_levels, hipStream_t s, const ClipWindow* win) {
     if (x_dtype == CVT_BF16) {
-        return y_dtype == CVT_BF16 ? fwd_by_shape<uint16_t, uint16_t>(x, y, y_layout, B, C, T, H, W, temporal_levels, s)
-                                   : fwd_by_shape<uint16_t, float>(x, y, y_layout, B, C, T, H, W, temporal_levels, s);
+        return y_dtype == CVT_BF16
+                   ? by_shape<true, uint16_t, uint16_t>(x, y, y_layout, B, C, T, H, W, temporal_levels, win, s)
+                   : by_shape<true, uint16_t, float>(x, y, y_layout, B, C, T, H, W, temporal_levels, win, s);
     }
-    return y_dtype == CVT_BF16 ? fwd_by_shape<float, uint16_t>(x, y, y_layout, B, C, T, H, W, temporal_levels, s)
-                               : fwd_by_shape<float, float>(x, y, y_layout, B, C, T, H, W, temporal_levels, s);
+    return y_dtype == CVT_BF16 ? by_shape<true, float, uint16_t>(x, y, y_layout, B, C, T, H, W, temporal_levels, win, s)
+                               : by_shape<true, float, float>(x, y, y_layout, B, C, T, H, W, temporal_levels, win, s);
 }
 
 hipError_t launch_haar_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtype, int B, int C,
-                           int T, int H, int W, int temporal_levels, hipStream_t s) {
+                           int T, int H, int W, int temporal_levels, hipStream_t s, const ClipWindow* win) {
     if (y_dtype == CVT_BF16) {
-        return x_dtype == CVT_BF16 ? inv_by_shape<uint16_t, uint16_t>(y, x, y_layout, B, C, T, H, W, temporal_levels, s)
-                                   : inv_by_shape<uint16_t, float>(y, x, y_layout, B, C, T, H, W, temporal_levels, s);
+        return x_dtype == CVT_BF16
+                   ? by_shape<false, uint16_t, uint16_t>(y, x, y_layout, B, C, T, H, W, temporal_levels, win, s)
+                   : by_shape<false, uint16_t, float>(y, x, y_layout, B, C, T, H, W, temporal_levels, win, s);
     }
-    return x_dtype == CVT_BF16 ? inv_by_shape<float, uint16_t>(y, x, y_layout, B, C, T, H, W, temporal_levels, s)
-                               : inv_by_shape<float, float>(y, x, y_layout, B, C, T, H, W, temporal_levels, s);
+    return x_dtype == CVT_BF16 ? by_shape<false, float, uint16_t>(y, x, y_layout, B, C, T, H, W, temporal_levels, win, s)
+                               : by_shape<false, float, float>(y, x, y_layout, B, C, T, H, W, temporal_levels, win, s);
 }
 
 }  // namespace cvt

@@ -27,15 +27,6 @@ struct WinGeom {
     int planes;         // frame planes the launch covers (B*C*Tp for pad, B*C*nt for crop)
 };
 
-// Padded frame t of an n-frame window: t itself inside the window, then the mirror about
-// the last frame without repeating it, bouncing between the two ends (period 2(n-1)).
-__device__ __forceinline__ int mirror_frame(int t, int n) {
-    if (n == 1) return 0;
-    const int p = 2 * (n - 1);
-    const int m = t % p;
-    return m < n ? m : p - m;
-}
-
 // ALIGNED: W % V == 0, so a vector of the padded row is a vector of the source row (or
 // wholly past it).
 template <typename E, int V, bool ALIGNED>

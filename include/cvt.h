@@ -365,6 +365,35 @@ int cvt_video_unpad(const void* y, void* x, int dtype, int B, int C, int T, int 
                     int Hp, int Wp, void* stream);
 
 /*
+ * Haar patcher of one sliding window, with the window's padding and cropping
+ * done inside the transform's own loads and stores.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 6.3 (windows of a
+ * video of any length, padded, reconstructed and cropped back) and section 7.1
+ * (Haar wavelet patching), as for cvt_video_pad and cvt_haar3d_fwd.
+ *
+ * cvt_haar3d_fwd_window gives, bit for bit, what cvt_video_pad of window
+ * (t0, nt) to Tp x Hp x Wp followed by cvt_haar3d_fwd of that padded window
+ * gives, without writing the padded window: x is the clip [B, C, T, H, W]
+ * NCTHW (dtype x_dtype), y the coefficients of the padded window in y_layout /
+ * y_dtype, shaped as cvt_haar3d_fwd shapes them for a Tp x Hp x Wp input.
+ * cvt_haar3d_inv_window gives what cvt_haar3d_inv of y to a Tp x Hp x Wp
+ * window followed by cvt_video_unpad into frames t0 .. t0+nt-1 of the clip x
+ * gives: only the window's nt frames, H rows and W columns of x are written.
+ * temporal_levels: 2 (Tp = 1 + 4k, each window starts with its own causal
+ * first frame) or 0 (per-frame); a continuation chunk (3) is not a window.
+ * Hp and Wp are multiples of 4; the clip's H and W may be any size (a width
+ * that is not a multiple of 4 takes an element-by-element path).
+ * Errors: those of cvt_video_pad / cvt_video_unpad for the window and of
+ * cvt_haar3d_fwd / cvt_haar3d_inv for the padded sizes; CVT_E_SHAPE for
+ * temporal_levels 3.
+ */
+int cvt_haar3d_fwd_window(const void* x, int x_dtype, void* y, int y_dtype, int y_layout, int B, int C, int T,
+                          int H, int W, int t0, int nt, int Tp, int Hp, int Wp, int temporal_levels, void* stream);
+int cvt_haar3d_inv_window(const void* y, int y_dtype, int y_layout, void* x, int x_dtype, int B, int C, int T,
+                          int H, int W, int t0, int nt, int Tp, int Hp, int Wp, int temporal_levels, void* stream);
+
+/*
  * Encoder and decoder blocks.
  *
  * Defined by: "Cosmos World Foundation Model Platform for Physical AI

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 27
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -240,6 +240,34 @@ def test_video_pad_validation():
     assert pad(y=MIS) == E_ALIGN
     assert lib.cvt_video_unpad(A, B_, 1, 1, 3, 40, 30, 50, 34, 7, 9, 32, 56, None) == E_SHAPE
     assert lib.cvt_video_unpad(MIS, B_, 1, 1, 3, 40, 30, 50, 34, 6, 9, 32, 56, None) == E_ALIGN
+
+
+def test_haar_window_validation():
+    # every call below fails validation (no call may pass it: the pointers are not device memory)
+    def hw(fn, **kw):
+        a = dict(p=A, pdt=1, c=B_, cdt=1, lay=1, B=1, C=3, T=40, H=30, W=50, t0=34, nt=6, Tp=9, Hp=32, Wp=52, tl=2)
+        a.update(kw)
+        if fn == "fwd":
+            return lib.cvt_haar3d_fwd_window(a["p"], a["pdt"], a["c"], a["cdt"], a["lay"], a["B"], a["C"], a["T"],
+                                             a["H"], a["W"], a["t0"], a["nt"], a["Tp"], a["Hp"], a["Wp"], a["tl"], None)
+        return lib.cvt_haar3d_inv_window(a["c"], a["cdt"], a["lay"], a["p"], a["pdt"], a["B"], a["C"], a["T"],
+                                         a["H"], a["W"], a["t0"], a["nt"], a["Tp"], a["Hp"], a["Wp"], a["tl"], None)
+    for fn in ("fwd", "inv"):
+        assert hw(fn, p=None) == E_NULL
+        assert hw(fn, c=None) == E_NULL
+        assert hw(fn, pdt=7) == E_DTYPE
+        assert hw(fn, cdt=7) == E_DTYPE
+        assert hw(fn, lay=9) == E_LAYOUT
+        assert hw(fn, tl=3, Tp=8) == E_SHAPE      # a window is not a continuation chunk
+        assert hw(fn, Tp=8) == E_SHAPE            # not 1 + 4k
+        assert hw(fn, Hp=30) == E_SHAPE           # padded height not a multiple of 4
+        assert hw(fn, Wp=48) == E_SHAPE           # below the clip's width
+        assert hw(fn, nt=7) == E_SHAPE            # past the clip's end
+        assert hw(fn, t0=-1) == E_SHAPE
+        assert hw(fn, Tp=5, nt=6) == E_SHAPE      # shorter than the window
+        assert hw(fn, tl=0, Tp=5) == E_SHAPE
+        assert hw(fn, p=MIS) == E_ALIGN
+        assert hw(fn, c=MIS) == E_ALIGN
 
 
 def test_block_validation():
