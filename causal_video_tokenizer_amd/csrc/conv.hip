@@ -476,9 +476,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     static_assert(C::KX * KS % NSET == 0, "whole fragment-set cycles per chunk");
     bf16x8_t fa[NSET][3][FA];
     const int lane16 = lane * 16;
-    auto load_frags = [&](int kc16, int kx, int set) {
-#pragma unroll
-        for (int ky = 0; ky < 3; ++ky)
+    auto load_frags_ky = [&](int kc16, int kx, int set, int ky) {
 #pragma unroll
             for (int a = 0; a < FA; ++a) {
                 const int ab = ab0 + a, tap = ky * KX + kx;
@@ -497,6 +495,10 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 const int off = fbase + lane16;
                 fa[set][ky][a] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0));
             }
+    };
+    auto load_frags = [&](int kc16, int kx, int set) {
+#pragma unroll
+        for (int ky = 0; ky < 3; ++ky) load_frags_ky(kc16, kx, set, ky);
     };
 
     f32x16_t acc[NV][FA][FB];
@@ -541,12 +543,20 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // row rr of step s + 1 is read right after the MFMAs of row rr of step s, the last use
     // of that row's registers, so every read has the rest of the step to arrive (the
     // scheduling barriers keep that order; left alone the compiler would move the reads).
+    // Temporal tiles of two 32-channel blocks per wave (one weight fragment per 4 MFMAs) with two
+    // fragment sets (EARLY): tap row ky of a set is last used by region row ky + NRU - 3, so its
+    // fragments for the step after next are requested right there (refill(ky)) instead of at the
+    // start of the next step: a third more time for the L2 fetch, with no further registers.
+    constexpr bool EARLY = KIND == TEMPORAL3 && NSET == 2 && FA == 2;
     auto compute = [&](const bf16x8_t (&cur)[NRU][FB], bf16x8_t (&nxt)[NRU][FB], const uint8_t* xb, int s, int set,
-                       bool read_next) {
+                       bool read_next, auto refill) {
 #pragma unroll
         for (int rr = 0; rr < NRU; ++rr) {
             mfma_row(cur, set, rr);
             if (read_next) read_row(nxt, xb, s + 1, rr);
+            if constexpr (EARLY) {
+                if (rr >= NRU - 3) refill(rr - (NRU - 3));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -565,8 +575,12 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         const int kcs = s < NS ? kc : kc + 1, ss = s < NS ? s : s - NS;
         load_frags(KS * kcs + ss / KX, ss % KX, s % NSET);
     };
+    auto prefetch_ky = [&](int kc, int s, int ky) {
+        const int kcs = s < NS ? kc : kc + 1, ss = s < NS ? s : s - NS;
+        load_frags_ky(KS * kcs + ss / KX, ss % KX, s % NSET, ky);
+    };
 #pragma unroll
-    for (int s = 0; s < PD; ++s) prefetch(0, s);
+    for (int s = 0; s < (EARLY ? NSET : PD); ++s) prefetch(0, s);
     load_region(0, 0);
     store_region(0, 0);
     if (L1 > 0) {
@@ -584,7 +598,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         for (int rr = 0; rr < NRU; ++rr) read_row(fb[0], xb, 0, rr);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            prefetch(kc, st + PD);
+            if constexpr (!EARLY) prefetch(kc, st + PD);
             __builtin_amdgcn_sched_barrier(0);  // weight prefetch before any region load
             if (L1 > 0 && st == L1) store_region(nbuf, 0);
             if (st == 0) load_region(kc + 1, 0);
@@ -592,7 +606,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             // keep the prefetches issued here: left alone the scheduler sinks them towards
             // their use to save registers, which exposes the memory latency
             __builtin_amdgcn_sched_barrier(0);
-            compute(fb[st & 1], fb[(st + 1) & 1], xb, st, st % NSET, st + 1 < NS);
+            compute(fb[st & 1], fb[(st + 1) & 1], xb, st, st % NSET, st + 1 < NS,
+                    [&](int ky) { prefetch_ky(kc, st + 2, ky); });
         }
         if (L1 == 0)
             store_region(nbuf, 0);
