@@ -543,11 +543,12 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // row rr of step s + 1 is read right after the MFMAs of row rr of step s, the last use
     // of that row's registers, so every read has the rest of the step to arrive (the
     // scheduling barriers keep that order; left alone the compiler would move the reads).
-    // Temporal tiles of two 32-channel blocks per wave (one weight fragment per 4 MFMAs) with two
+    // Tiles of two 32-channel blocks per wave (one weight fragment per 4 MFMAs or fewer) with two
     // fragment sets (EARLY): tap row ky of a set is last used by region row ky + NRU - 3, so its
     // fragments for the step after next are requested right there (refill(ky)) instead of at the
     // start of the next step: a third more time for the L2 fetch, with no further registers.
-    constexpr bool EARLY = KIND == TEMPORAL3 && NSET == 2 && FA == 2;
+    // (On the one-block spatial tiles, whose fragments feed twice as many MFMAs, it is slower.)
+    constexpr bool EARLY = NSET == 2 && FA == 2;
     auto compute = [&](const bf16x8_t (&cur)[NRU][FB], bf16x8_t (&nxt)[NRU][FB], const uint8_t* xb, int s, int set,
                        bool read_next, auto refill) {
 #pragma unroll
