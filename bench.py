@@ -53,10 +53,10 @@ COPY_CAL_BYTES = 256 * 1024 * 1024
 # 1x3x3 192->256 on the 13 x 180 x 320 latent grid), from two rocprofv3 --pmc passes over
 # this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
 # what it reads for the 256 MiB device copy this script issues after timing: FETCH_SIZE
-# reads 131091.1 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
+# reads 131105.9 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
 # for the kernel version the counters were taken on: set to None when it changes.
-SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 233116.0, 374445.2
-COPY_FETCH_KIB, COPY_WRITE_KIB = 131091.1, 262144.0
+SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 226397.7, 374400.0
+COPY_FETCH_KIB, COPY_WRITE_KIB = 131105.9, 262144.0
 
 
 def parse():
@@ -195,7 +195,7 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": 2.0 * P * (192 + 256) + 2.0 * 256 * 192 * 9,
-                "kernel": "conv_rows_kernel<RowsCfg<SPATIAL3,R=4,WCH=4,FA=1,BK=32,NW=4>,false,false> (1x3x3 conv 192->256, bf16 MFMA)",
+                "kernel": "conv_rows_kernel<RowsCfg<SPATIAL3,R=4,WCH=4,FA=2,BK=32,NW=4>,false,false> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
