@@ -246,10 +246,10 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 //
 // Both convolutions are a 3-tap filter along one "row" axis, repeated over KX column
 // shifts:
-//   TEMPORAL3: rows are frames, columns are 64 flattened (h, w) positions; output frame t
+//   TEMPORAL3: rows are frames, columns are NC flattened (h, w) positions; output frame t
 //              reads input frames t-2, t-1, t through taps 0, 1, 2 (KX = 1);
-//   SPATIAL3:  rows are image rows of one frame, columns are 64 pixels of a row plus a
-//              1-pixel halo (66); output row y, pixel x reads input row y-1+ky, pixel
+//   SPATIAL3:  rows are image rows of one frame, columns are NC pixels of a row plus a
+//              1-pixel halo (NC + 2); output row y, pixel x reads input row y-1+ky, pixel
 //              x-1+kx through tap (ky, kx) (KX = 3).
 // One workgroup (4 or 8 waves) computes TCH output channels x NC columns x R consecutive
 // output rows r0 .. r0+R-1, which read the R+2 input rows r0-off .. r0+R-1 (off = 2
@@ -257,11 +257,13 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 // meets tap row ky in output row r0 + rr - ky.  Each wave owns FA 32-channel x FB 32-column
 // MFMA blocks (FA * FB = 2) over all R rows: per (16-channel k-step, column shift kx) it
 // takes its 3 FA weight fragments (3 tap rows) once and walks the region rows, each
-// activation fragment feeding up to three tap rows, i.e. three output rows.  Both
-// convolutions mostly use FA = 1, FB = 2 (32 channels x 64 columns per wave), which needs
-// half the weight bytes per MFMA of 64 x 32.  The temporal conv puts up to 256 channels in
-// one workgroup (8 waves, or 4 waves of 64 x 32 with the fused projection), so each region
-// is staged once for every output channel.  A step's activation reads are issued during the
+// activation fragment feeding up to three tap rows, i.e. three output rows.  Up to 256
+// output channels both convolutions use 4 waves of FA = 2, FB = 1 (64 channels x 32
+// columns per wave), so each region is staged once for every output channel and two
+// workgroups share a CU; their six weight fragments per step are requested right after
+// the previous use of their registers.  FA = 1, FB = 2 (32 x 64 per wave, half the weight
+// bytes per MFMA) serves up to 128 channels, and the temporal conv above 256 channels
+// (8 waves).  A step's activation reads are issued during the
 // previous step's MFMAs (see compute), so only a chunk's first step waits for LDS.
 //
 // Only the region is staged in LDS (two buffers of 30-36 KB; two 4-wave workgroups share a
@@ -1218,14 +1220,13 @@ hipError_t launch_igemm_k(const uint16_t* X, const uint16_t* Wp, const float* bi
 }
 
 // Tile configurations of conv_rows_kernel (see RowsCfg).  Spatial: 4 channel waves of 32
-// channels x 64 pixels each (128 x 64 per workgroup): three weight fragments per step per
-// wave instead of six, which relieves the per-CU vector-memory path that carries them
-// (measured 2-3% faster than 2 x 2 waves of 64 x 32).  Temporal: waves of 32 channels x 64
-// positions as well, 8 of them for up to 256 output channels (one workgroup per CU), 4 for
-// up to 128.  Temporal with the fused projection (all output channels in one workgroup):
-// 4 waves of 64 channels x 32 positions, so that two workgroups share a CU and their waves
-// are not all tied by one barrier; that measured 3-8% faster than the 8-wave tile there,
-// which in turn is 3% faster without the projection.
+// channels x 64 pixels (128 x 64 per workgroup, three weight fragments per step per wave)
+// up to 128 output channels, else 4 waves of 64 x 32 (256 x 32 per workgroup, six
+// fragments per step requested early), 2% faster on the 720p layers.  Temporal: 4 waves of
+// 32 x 64 up to 128 channels; 4 waves of 64 channels x 32 positions up to 256 (two
+// workgroups per CU, so their waves are not all tied by one barrier and one's epilogue
+// overlaps the other's MFMAs: 3-10% faster than 8 waves of 32 x 64 in one workgroup, which
+// remain above 256 channels).
 #ifndef CVT_ROWS_SP_WCH
 #define CVT_ROWS_SP_WCH 4
 #endif
