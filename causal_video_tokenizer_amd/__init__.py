@@ -252,6 +252,12 @@ def conv_proj_workspace_bytes(x_shape, Cout, Cp, k, spatial=True, temporal=True)
     return int(lib.cvt_causal_conv3d_fact_proj_workspace(B, Cin, Cout, Cp, T, H, W, k, parts))
 
 
+def conv_proj_fsq_workspace_bytes(x_shape, Cout, D, k, spatial=True, temporal=True):
+    B, Cin, T, H, W = x_shape
+    parts = (CVT_CONV_SPATIAL if spatial else 0) | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_causal_conv3d_fact_proj_fsq_workspace(B, Cin, Cout, D, T, H, W, k, parts))
+
+
 def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, workspace=None, out=None):
     """Factorized causal convolution followed by a 1x1x1 projection, without
     materialising the Cout-channel result.
