@@ -86,6 +86,8 @@ DQ_CASES = [
     (2, 3, 5, 7, 64, False, LEVELS),
     (1, 2, 4, 4, 20, True, LEVELS),        # Cout not a multiple of 8
     (1, 3, 4, 5, 48, False, (7, 6, 5)),    # codes not exact in bf16 (halves 3)
+    (1, 5, 7, 11, 72, True, LEVELS),       # 9 channel groups per position
+    (2, 3, 6, 9, 256, False, (7, 6, 5, 9)),  # four levels, halves 3 and 4
 ]
 
 
@@ -110,11 +112,12 @@ def test_dequantize_proj_equals_unfused_and_oracle(case):
     assert_rel(to_f64(y), ref, 1e-2, "dequant+proj")
 
 
-def test_dequantize_proj_invalid_indices():
+@pytest.mark.parametrize("Cout", [64, 192])
+def test_dequantize_proj_invalid_indices(Cout):
     idx_np = si.uniform_indices((1, 2, 4, 8), 930)
     idx_np[0, 0, 0, :3] = [-1, 64000, 2 ** 31 - 1]
     idx = torch.from_numpy(idx_np).cuda()
-    wp, _ = bf16_dev((64, 6, 1, 1, 1), 931, 0.2)
+    wp, _ = bf16_dev((Cout, 6, 1, 1, 1), 931, 0.2)
     cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
     y = cvt.fsq_dequantize_proj(idx, wp, invalid_count=cnt)
     torch.cuda.synchronize()
