@@ -180,7 +180,6 @@ template <>
 struct Row4<uint16_t> {
     uint2 u;
     __device__ void load(const uint16_t* p) { u = ld_stream8(p); }
-    __device__ void zero() { u = make_uint2(0u, 0u); }
     __device__ void get(float* v) const {
         v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
     }
@@ -192,7 +191,6 @@ struct Row4<float> {
         const uint4 w = ld_stream16(p);
         u = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
-    __device__ void zero() { u = make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
     __device__ void get(float* v) const { v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; }
 };
 
@@ -253,27 +251,35 @@ __global__ __launch_bounds__(64) void haar_fwd_staged_kernel(const Tin* __restri
 #pragma unroll
                 for (int r = 0; r < 4; ++r) raw[c][f][r].load(base + (size_t)r * W);
             } else {
+                // rows past the clip's frame and 4-pixel groups past its width load a clamped, valid
+                // group and are zeroed where the transform reads them: the loads stay unconditional,
+                // so all of them are in flight together
                 const Tin* plane = clip_plane(x, tile.b * C + c, mirror_frame(src, win.nt), win);
+                const int wl = min(4 * wq_ld, win.W - 4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int h = 4 * tile.hq + r;
-                    if (h < win.H && 4 * wq_ld < win.W)
-                        raw[c][f][r].load(plane + (size_t)h * win.W + 4 * wq_ld);
-                    else
-                        raw[c][f][r].zero();
-                }
+                for (int r = 0; r < 4; ++r)
+                    raw[c][f][r].load(plane + (size_t)min(4 * tile.hq + r, win.H - 1) * win.W + wl);
             }
         }
 
     // 2. transform, in output channel order
     float out[NCH];
+    bool okr[4];  // WM: row r of the block lies inside the clip's frame (and the lane's group inside its width)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) okr[r] = WM == 0 || (4 * tile.hq + r < win.H && 4 * wq_ld < win.W);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         float v[NF][4][4];
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) raw[c][f][r].get(v[f][r]);
+            for (int r = 0; r < 4; ++r) {
+                raw[c][f][r].get(v[f][r]);
+                if constexpr (WM != 0) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[f][r][k] = okr[r] ? v[f][r][k] : 0.0f;
+                }
+            }
         block_transform<NF>(v);
 #pragma unroll
         for (int rt = 0; rt < NF; ++rt)
