@@ -831,7 +831,9 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // accesses execute in order, so no barrier is needed.
     // RES stages the float32 sums instead (rows of 128 FA + 16 bytes) and adds the residual in
     // the store step, where each lane's 16 residual bytes sit at its store's offset (one
-    // coalesced load per store) before the single bf16 rounding.
+    // coalesced load per store, all of a frame's requested before its staging) before the
+    // single bf16 rounding.  A wave reads only the residual chunks it overwrites itself, each
+    // before its store, so the output may be the residual tensor.
     constexpr int ES = EPI == EPI_RES ? 4 : 2;  // staged element bytes
     constexpr int OS = 32 * FA * ES + 16;
     constexpr int STAGE = 32 * FB * OS;  // bytes per wave
@@ -839,8 +841,39 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                   "epilogue staging fits in the LDS buffer");
     uint8_t* stage = smem + wave * STAGE;
     const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
+    constexpr int CPP = 4 * FA;   // 16-byte output chunks per position slice
+    constexpr int PPI = 64 / CPP;  // positions per store instruction
+    constexpr int NIT = 32 * FB / PPI;
+    const int c16 = lane % CPP;
+    const int n = ab0 * 32 + c16 * 8;
+    // output position of store step it of frame ry, and whether it is stored
+    auto out_pos = [&](int ry, int it, long long& pos) {
+        const int col = it * PPI + lane / CPP;
+        bool ok;
+        if (KIND == SPATIAL3) {
+            const int y = r0 + ry, x = c0 + wpos * 32 * FB + col;
+            ok = x < g.W;
+            pos = (((long long)b * g.T + t) * g.H + y) * g.W + x;
+        } else {
+            const int hw = c0 + wpos * 32 * FB + col;
+            ok = hw < g.HW;
+            pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
+        }
+        return ok && n < g.Cout;  // Cout is a multiple of 8 on this path (checked by the launcher)
+    };
+    // RES: a frame's residual chunks are requested before its staging (unconditional loads, a
+    // stored position's chunk or the tensor's first one), so their latency overlaps the LDS work
+    uint4 rv[EPI == EPI_RES ? NIT : 1];
 #pragma unroll
     for (int ry = 0; ry < NV; ++ry) {
+        if constexpr (EPI == EPI_RES) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                long long pos;
+                const bool ok = out_pos(ry, it, pos);
+                rv[it] = *reinterpret_cast<const uint4*>(aux.res + (ok ? pos * g.Cout + n : 0));
+            }
+        }
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -862,30 +895,16 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        constexpr int CPP = 4 * FA;   // 16-byte output chunks per position slice
-        constexpr int PPI = 64 / CPP;  // positions per store instruction
-        const int c16 = lane % CPP;
-        const int n = ab0 * 32 + c16 * 8;
 #pragma unroll
-        for (int it = 0; it < 32 * FB / PPI; ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int col = it * PPI + lane / CPP;
             long long pos;
-            bool ok;
-            if (KIND == SPATIAL3) {
-                const int y = r0 + ry, x = c0 + wpos * 32 * FB + col;
-                ok = x < g.W;
-                pos = (((long long)b * g.T + t) * g.H + y) * g.W + x;
-            } else {
-                const int hw = c0 + wpos * 32 * FB + col;
-                ok = hw < g.HW;
-                pos = ((long long)b * g.T + r0 + ry) * g.HW + hw;
-            }
-            ok = ok && n < g.Cout;  // Cout is a multiple of 8 on this path (checked by the launcher)
+            const bool ok = out_pos(ry, it, pos);
             uint4 v;
             if constexpr (EPI == EPI_RES) {
                 const float4 f0 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32);
                 const float4 f1 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32 + 16);
-                const uint4 r = ok ? *reinterpret_cast<const uint4*>(aux.res + pos * g.Cout + n) : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 r = rv[it];
                 v.x = pack_bf16x2(f0.x + bf16_lo(r.x), f0.y + bf16_hi(r.x));
                 v.y = pack_bf16x2(f0.z + bf16_lo(r.y), f0.w + bf16_hi(r.y));
                 v.z = pack_bf16x2(f1.x + bf16_lo(r.z), f1.y + bf16_hi(r.z));

@@ -445,7 +445,8 @@ typedef struct cvt_resblock_weights {
  * factorized causal conv C -> C with k = 3 (1x3x3 zero padding 1, then 3x1x1
  * with two zero frames in front).  The second LayerNorm and Swish run in the
  * first conv's epilogue for C <= 256, the residual add in the second conv's
- * epilogue (one rounding).
+ * epilogue (one rounding).  y may be x (in place): the epilogue reads each
+ * residual element before the same wave overwrites it.
  * workspace: cvt_resblock3d_workspace(B, C, T, H, W) bytes, caller-owned.
  * Errors: CVT_E_NULL for a NULL tensor, weight or scale/shift; CVT_E_SHAPE for
  * a non-positive size, C < 64, C not a multiple of 8 or a tensor of 2 GiB or

@@ -109,6 +109,19 @@ def test_resblock_causality_and_determinism():
     assert np.array_equal(y2[:, :, :3], y0[:, :, :3]) and not np.array_equal(y2[:, :, 3:], y0[:, :, 3:])
 
 
+@pytest.mark.parametrize("C", [256, 320])
+def test_resblock_in_place_equals_out_of_place(C):
+    # the residual epilogue reads each residual chunk before the same wave overwrites it
+    B, T, H, W = 1, 5, 9, 70
+    x, _ = bf16_pair((B, C, T, H, W), 835, 1.0, cl=True)
+    p, _ = block_params_dev(C, 836, True)
+    y = to_bits(cvt.resblock3d(x, p))
+    x2 = x.clone(memory_format=torch.channels_last_3d)
+    cvt.resblock3d(x2, p, out=x2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(x2), y)
+
+
 DOWN_CASES = [
     # B, Cin, Cout, T, H, W, space, time, bias
     (1, 64, 128, 5, 8, 12, True, True, True),
