@@ -728,6 +728,18 @@ def stream_encode(cvt, si, torch, dev, args):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where the file has none)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):
     """The float64 oracle on a strip of the clip (all frames, all rows, `width`
     pixel columns), scaled to the whole clip by the width ratio."""
@@ -756,6 +768,7 @@ def cpu_baseline(xbits, zbits, ws_b, wt_b, pj_b, shape, width):
     scale = W / width
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(B * T / (dt * scale), 4), "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"all {T} frames x {H} rows x {width} of {W} pixel columns (1/{scale:g} of the clip), "
                       f"{dt:.1f} s, scaled by {scale:g}; float64 NumPy, BLAS threads={threads}",
             "seconds": round(dt, 2)}

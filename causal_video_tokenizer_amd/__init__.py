@@ -127,6 +127,23 @@ def _require_gpu(*ts):
             raise ValueError("tensors must be on a ROCm GPU device")
 
 
+def _same_device(x, *ts):
+    """Every tensor given (weights, biases, workspace) lives on x's device: the kernels
+    dereference their pointers on that device."""
+    for t in ts:
+        if t is not None and t.device != x.device:
+            raise ValueError(f"a tensor is on {t.device}, expected {x.device} (the device of x)")
+
+
+def _workspace_arg(workspace, need, x):
+    """The caller's workspace (uint8, contiguous, on x's device) or a new one of `need` bytes."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return workspace
+
+
 def _layout_of(t):
     """Physical layout code of a 5-D tensor (NCTHW contiguous or NTHWC)."""
     if t.is_contiguous():
@@ -214,9 +231,9 @@ def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out
     (spatial part only); b_s, b_t: float32 [Cout] or None.
     Returns y [B, Cout, T, H, W] bf16 channels_last_3d.
     """
-    _require_gpu(x, w_s, w_t, b_s, b_t)
-    if not x.is_contiguous(memory_format=torch.channels_last_3d):
-        raise ValueError("x must be channels_last_3d (NTHWC)")
+    _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, b_s, b_t, workspace)
+    _same_device(x, w_s, w_t, b_s, b_t, workspace)
     B, Cin, T, H, W = x.shape
     if w_s is not None:
         Cout, Cin_w, kt, k, k2 = w_s.shape
@@ -235,8 +252,7 @@ def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out
         if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or b.numel() != Cout):
             raise ValueError("biases must be contiguous float32 [Cout]")
     need = conv_workspace_bytes(x.shape, Cout, k, w_s is not None, w_t is not None)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     shape = (B, Cout, T, H, W)
     y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
          else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
@@ -265,9 +281,9 @@ def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, work
     x, w_s, w_t, b_s, b_t: as causal_conv3d_fact; w_p: [Cp, Cout, 1, 1, 1] bf16;
     b_p: float32 [Cp] or None.  Returns [B, Cp, T, H, W] bf16 channels_last_3d.
     """
-    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p)
-    if not x.is_contiguous(memory_format=torch.channels_last_3d):
-        raise ValueError("x must be channels_last_3d (NTHWC)")
+    _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p, workspace)
+    _same_device(x, w_s, w_t, w_p, b_s, b_t, b_p, workspace)
     B, Cin, T, H, W = x.shape
     if w_s is not None:
         Cout, k = w_s.shape[0], w_s.shape[3]
@@ -289,8 +305,7 @@ def causal_conv3d_fact_proj(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, work
         if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != n):
             raise ValueError("biases must be contiguous float32 of their output width")
     need = conv_proj_workspace_bytes(x.shape, Cout, Cp, k, w_s is not None, w_t is not None)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     shape = (B, Cp, T, H, W)
     y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
          else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
@@ -310,9 +325,9 @@ def causal_conv3d_temporal_stream(x, w_t, hist=None, w_p=None, b_t=None, b_p=Non
     hist: None (start of a stream: zero padding) or the two frames before x,
     [B, C, 2, H, W] bf16 channels_last_3d (for B = 1 a view of the previous chunk's last
     two frames).  Chunk by chunk this equals one call over the whole clip, bit for bit."""
-    _require_gpu(x, w_t, hist, w_p, b_t, b_p)
-    if x.dtype != torch.bfloat16 or not x.is_contiguous(memory_format=torch.channels_last_3d):
-        raise ValueError("x must be bfloat16 channels_last_3d (NTHWC)")
+    _nthwc_bf16(x, "x")
+    _require_gpu(x, w_t, hist, w_p, b_t, b_p, workspace)
+    _same_device(x, w_t, hist, w_p, b_t, b_p, workspace)
     B, C, T, H, W = x.shape
     if hist is not None:
         if (tuple(hist.shape) != (B, C, 2, H, W) or hist.dtype != torch.bfloat16
@@ -329,8 +344,7 @@ def causal_conv3d_temporal_stream(x, w_t, hist=None, w_p=None, b_t=None, b_p=Non
         if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != n):
             raise ValueError("biases must be contiguous float32 of their output width")
     need = temporal_stream_workspace_bytes(C, Cp)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     shape = (B, Cp if w_p is not None else C, T, H, W)
     y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
          else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
@@ -540,8 +554,9 @@ def resblock3d(x, p, eps=LN_EPS, workspace=None, out=None):
     """Residual block y = x + conv2(swish(LN2(conv1(swish(LN1(x)))))) on a bf16 NTHWC tensor.
     p: dict with ln1_g, ln1_b, ln2_g, ln2_b (float32 [C]), c1_s, c2_s (bf16 [C, C, 1, 3, 3]),
     c1_t, c2_t (bf16 [C, C, 3, 1, 1]) and optional biases c1_bs, c1_bt, c2_bs, c2_bt."""
-    _require_gpu(x, *[p.get(k) for k in RESBLOCK_KEYS])
     _nthwc_bf16(x, "x")
+    _require_gpu(x, workspace, *[p.get(k) for k in RESBLOCK_KEYS])
+    _same_device(x, workspace, *[p.get(k) for k in RESBLOCK_KEYS])
     B, C, T, H, W = x.shape
     for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
         if p.get(k) is None:
@@ -554,8 +569,7 @@ def resblock3d(x, p, eps=LN_EPS, workspace=None, out=None):
         _bf16_w(p.get(c + "_t"), (C, C, 3, 1, 1), c + "_t")
     w = ResblockWeights(*[p[k].data_ptr() if p.get(k) is not None else None for k in RESBLOCK_KEYS])
     need = int(lib.cvt_resblock3d_workspace(B, C, T, H, W))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     y = _check_out(out, x.shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None else torch.empty_like(x)
     _check(lib.cvt_resblock3d(_ptr(x), ctypes.byref(w), _ptr(y), B, C, T, H, W, eps, _ptr(workspace),
                               workspace.numel(), _stream(x.device)), "resblock3d")
@@ -566,8 +580,9 @@ def downsample3d(x, w_s=None, w_t=None, b_s=None, b_t=None, workspace=None, out=
     """Downsampling block on a bf16 NTHWC tensor: 1x3x3 conv at stride 2 in H and W (w_s
     [Cout, Cin, 1, 3, 3]) and/or causal 3x1x1 conv at stride 2 in time (w_t [Cout, C, 3, 1, 1],
     T = 1 + 2k -> 1 + k)."""
-    _require_gpu(x, w_s, w_t, b_s, b_t)
     _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, b_s, b_t, workspace)
+    _same_device(x, w_s, w_t, b_s, b_t, workspace)
     B, Cin, T, H, W = x.shape
     if w_s is None and w_t is None:
         raise ValueError("at least one of w_s and w_t is needed")
@@ -580,8 +595,7 @@ def downsample3d(x, w_s=None, w_t=None, b_s=None, b_t=None, workspace=None, out=
     _f32_vec(b_t, Cout, "b_t")
     parts = (CVT_CONV_SPATIAL if w_s is not None else 0) | (CVT_CONV_TEMPORAL if w_t is not None else 0)
     need = int(lib.cvt_downsample3d_workspace(B, Cin, Cout, T, H, W, parts))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     shape = (B, Cout, 1 + (T - 1) // 2 if w_t is not None else T, H // 2 if w_s is not None else H,
              W // 2 if w_s is not None else W)
     y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
@@ -595,8 +609,9 @@ def upsample3d(x, w_s, w_t, b_s=None, b_t=None, space=True, time=True, workspace
     """Upsampling block on a bf16 NTHWC tensor: nearest-neighbour repetition x2 in H and W
     (space) and/or causal x2 in time (time: T -> 2T - 1), then the factorized conv
     (w_s [Cout, Cin, 1, 3, 3], w_t [Cout, Cout, 3, 1, 1])."""
-    _require_gpu(x, w_s, w_t, b_s, b_t)
     _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, b_s, b_t, workspace)
+    _same_device(x, w_s, w_t, b_s, b_t, workspace)
     B, Cin, T, H, W = x.shape
     Cout = w_s.shape[0]
     _bf16_w(w_s, (Cout, Cin, 1, 3, 3), "w_s")
@@ -604,8 +619,7 @@ def upsample3d(x, w_s, w_t, b_s=None, b_t=None, space=True, time=True, workspace
     _f32_vec(b_s, Cout, "b_s")
     _f32_vec(b_t, Cout, "b_t")
     need = int(lib.cvt_upsample3d_workspace(B, Cin, Cout, T, H, W, int(space), int(time)))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     f = 2 if space else 1
     shape = (B, Cout, 2 * T - 1 if time else T, f * H, f * W)
     y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
@@ -621,16 +635,20 @@ def causal_conv3d_fact_proj_fsq(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, 
     """causal_conv3d_fact_proj to the D = len(levels) latent, then FSQ, in one pass where
     the projection is fused: returns int32 indices [B, T, H, W] (and the bf16 NTHWC latent
     when return_latent).  Bit-identical to fsq_quantize(causal_conv3d_fact_proj(...))."""
-    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p)
-    if not x.is_contiguous(memory_format=torch.channels_last_3d):
-        raise ValueError("x must be channels_last_3d (NTHWC)")
+    _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, w_p, b_s, b_t, b_p, workspace, indices, latent)
+    _same_device(x, w_s, w_t, w_p, b_s, b_t, b_p, workspace)
     B, Cin, T, H, W = x.shape
     if w_s is not None:
         Cout, k = w_s.shape[0], w_s.shape[3]
+        if tuple(w_s.shape) != (Cout, Cin, 1, k, k):
+            raise ValueError("w_s must be [Cout, Cin, 1, k, k]")
     elif w_t is not None:
         Cout, k = w_t.shape[0], w_t.shape[2]
     else:
         raise ValueError("at least one of w_s and w_t is needed")
+    if w_t is not None and tuple(w_t.shape) != (Cout, Cout, k, 1, 1):
+        raise ValueError("w_t must be [Cout, Cout, k, 1, 1]")
     D = len(levels)
     if tuple(w_p.shape) != (D, Cout, 1, 1, 1):
         raise ValueError("w_p must be [len(levels), Cout, 1, 1, 1]")
@@ -641,8 +659,7 @@ def causal_conv3d_fact_proj_fsq(x, w_s, w_t, w_p, b_s=None, b_t=None, b_p=None, 
         _f32_vec(bias, n, "bias")
     parts = (CVT_CONV_SPATIAL if w_s is not None else 0) | (CVT_CONV_TEMPORAL if w_t is not None else 0)
     need = int(lib.cvt_causal_conv3d_fact_proj_fsq_workspace(B, Cin, Cout, D, T, H, W, k, parts))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace_arg(workspace, need, x)
     idx = (_check_out(indices, (B, T, H, W), torch.int32, x.device, what="indices") if indices is not None
            else torch.empty((B, T, H, W), dtype=torch.int32, device=x.device))
     lat = None
