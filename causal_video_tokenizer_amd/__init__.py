@@ -15,7 +15,7 @@ Tensor conventions
 
 Entry points (same names as the C functions without the ``cvt_`` prefix):
 ``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``,
-``causal_conv3d_fact_proj``, ``causal_conv3d_temporal_stream``, ``attention3d``,
+``causal_conv3d_fact_noalloc``, ``causal_conv3d_fact_proj``, ``causal_conv3d_temporal_stream``, ``attention3d``,
 ``fsq_quantize``, ``fsq_dequantize``, ``video_window``, ``video_pad``,
 ``video_unpad``, ``layernorm3d``, ``resblock3d``, ``downsample3d``, ``upsample3d``.  ``lib`` is the loaded ctypes library with the raw C
 functions.
@@ -44,6 +44,7 @@ SIGNATURES = {
     "cvt_haar3d_inv": (_ci, [_vp, _ci, _ci, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_causal_conv3d_fact_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp]),
+    "cvt_causal_conv3d_fact_noalloc": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
     "cvt_causal_conv3d_fact_proj_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact_proj": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                           _ci, _vp, _sz, _vp]),
@@ -259,6 +260,39 @@ def causal_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out
     _check(lib.cvt_causal_conv3d_fact(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
                                       B, Cin, Cout, T, H, W, k, _ptr(workspace), workspace.numel(),
                                       _stream(x.device)), "causal_conv3d_fact")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CVT_NOALLOC_SCRATCH_BYTES
+
+
+def causal_conv3d_fact_noalloc(x, w_s, w_t=None, b_s=None, b_t=None, out=None):
+    """causal_conv3d_fact with the library's preallocated scratch in place of a workspace
+    (cvt_causal_conv3d_fact_noalloc): nothing is allocated but the output, and nothing at
+    all with ``out`` given.  Calls that overlap on one GPU share that scratch and race."""
+    _nthwc_bf16(x, "x")
+    _require_gpu(x, w_s, w_t, b_s, b_t)
+    _same_device(x, w_s, w_t, b_s, b_t)
+    B, Cin, T, H, W = x.shape
+    w0 = w_s if w_s is not None else w_t
+    if w0 is None:
+        raise ValueError("at least one of w_s and w_t is needed")
+    Cout, k = w0.shape[0], w0.shape[3] if w_s is not None else w0.shape[2]
+    if w_s is not None and tuple(w_s.shape) != (Cout, Cin, 1, k, k):
+        raise ValueError("w_s must be [Cout, Cin, 1, k, k]")
+    if w_t is not None and tuple(w_t.shape) != (Cout, Cout, k, 1, 1):
+        raise ValueError("w_t must be [Cout, Cout, k, 1, 1]")
+    for w in (w_s, w_t):
+        if w is not None and (w.dtype != torch.bfloat16 or not w.is_contiguous()):
+            raise ValueError("weights must be contiguous bfloat16")
+    for b in (b_s, b_t):
+        _f32_vec(b, Cout, "bias")
+    shape = (B, Cout, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_causal_conv3d_fact_noalloc(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
+                                              B, Cin, Cout, T, H, W, k, _stream(x.device)),
+           "causal_conv3d_fact_noalloc")
     return y
 
 

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcvt.so")
-SOURCES = ["abi.cpp", "haar.hip", "fsq.hip", "conv.hip", "attention.hip", "window.hip", "norm.hip"]
+SOURCES = ["abi.cpp", "haar.hip", "fsq.hip", "conv.hip", "attention.hip", "window.hip", "norm.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

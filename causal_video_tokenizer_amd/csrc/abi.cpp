@@ -173,9 +173,10 @@ size_t cvt_causal_conv3d_fact_workspace(int B, int Cin, int Cout, int T, int H, 
                                      (parts & CVT_CONV_TEMPORAL) != 0);
 }
 
-int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
-                           void* y, int B, int Cin, int Cout, int T, int H, int W, int k, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace {
+// The checks of cvt_causal_conv3d_fact that do not concern the workspace.
+int check_conv_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                    int B, int Cin, int Cout, int T, int H, int W, int k) {
     if (!x || !y) return fail(CVT_E_NULL, "x and y must not be NULL");
     if (!w_s && !w_t) return fail(CVT_E_NULL, "at least one of w_s and w_t must be given");
     if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0)
@@ -193,6 +194,15 @@ int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t, cons
         return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
     if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
         return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    return CVT_OK;
+}
+}  // namespace
+
+int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                           void* y, int B, int Cin, int Cout, int T, int H, int W, int k, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const int st = check_conv_fact(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, k);
+    if (st != CVT_OK) return st;
     const size_t need = cvt::conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
     if (!workspace || workspace_bytes < need)
         return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -201,6 +211,22 @@ int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t, cons
     return hip_status(cvt::launch_conv_fact(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, k, workspace,
                                             (hipStream_t)stream),
                       "cvt_causal_conv3d_fact launch");
+}
+
+int cvt_causal_conv3d_fact_noalloc(const void* x, const void* w_s, const void* w_t, const float* b_s,
+                                   const float* b_t, void* y, int B, int Cin, int Cout, int T, int H, int W, int k,
+                                   void* stream) {
+    const int st = check_conv_fact(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, k);
+    if (st != CVT_OK) return st;
+    const size_t need = cvt::conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
+    if (need > CVT_NOALLOC_SCRATCH_BYTES)
+        return fail(CVT_E_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the library's preallocated scratch holds %zu "
+                    "(use cvt_causal_conv3d_fact with a caller workspace)",
+                    need, (size_t)CVT_NOALLOC_SCRATCH_BYTES);
+    return hip_status(cvt::launch_conv_fact_noalloc(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, k,
+                                                    (hipStream_t)stream),
+                      "cvt_causal_conv3d_fact_noalloc launch");
 }
 
 size_t cvt_causal_conv3d_fact_proj_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, int parts) {

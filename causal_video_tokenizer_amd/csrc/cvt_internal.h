@@ -117,6 +117,11 @@ size_t conv_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, int k
 hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, const float* b_s,
                             const float* b_t, void* y, int B, int Cin, int Cout, int T, int H,
                             int W, int k, void* workspace, hipStream_t stream);
+// cvt_causal_conv3d_fact with the library's preallocated scratch as the workspace
+// (noalloc.hip); conv_workspace_bytes() must not exceed CVT_NOALLOC_SCRATCH_BYTES.
+hipError_t launch_conv_fact_noalloc(const void* x, const void* w_s, const void* w_t, const float* b_s,
+                                    const float* b_t, void* y, int B, int Cin, int Cout, int T, int H, int W, int k,
+                                    hipStream_t stream);
 // Factorized causal convolution followed by a 1x1x1 projection to Cp channels.
 size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
                                  bool temporal);

@@ -148,6 +148,33 @@ int cvt_causal_conv3d_fact(const void* x, const void* w_s, const void* w_t,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cvt_causal_conv3d_fact for callers that cannot allocate (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the same operation,
+ * kernels and result bit for bit, with the workspace replaced by scratch memory
+ * the library preallocates, a device array of CVT_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing and calls no allocating routine; the caller passes inputs
+ * and outputs only.
+ *
+ * Arguments and errors: as cvt_causal_conv3d_fact without the workspace;
+ * CVT_E_WORKSPACE (nothing launched) when the call would need more scratch than
+ * CVT_NOALLOC_SCRATCH_BYTES, i.e. when cvt_causal_conv3d_fact_workspace() for
+ * the same arguments exceeds it (the packed weights, plus the bf16 intermediate
+ * of B*T*H*W*Cout*2 bytes when both parts run: about 125,000 positions at
+ * 256 channels; a single part needs only its packed weights).
+ * Every call on one GPU uses that GPU's single copy of the scratch: calls that
+ * overlap on one GPU (two streams, two host threads) race and must be ordered
+ * by the caller.  The first call on a device looks up the scratch's address
+ * (hipGetSymbolAddress) on the calling thread's current device, which must be
+ * the device of the tensors and the stream.
+ */
+#define CVT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int cvt_causal_conv3d_fact_noalloc(const void* x, const void* w_s, const void* w_t,
+                                   const float* b_s, const float* b_t, void* y,
+                                   int B, int Cin, int Cout, int T, int H, int W, int k,
+                                   void* stream);
+
+/*
  * Factorized causal convolution (as cvt_causal_conv3d_fact) followed by a
  * 1x1x1 projection to Cp channels, without writing the Cout-channel result:
  *   y = bf16( w_p . bf16(conv(x)) + b_p ),

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 29
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -373,3 +373,22 @@ def test_conv_bindings_reject_non_bf16_inputs():
         cvt.causal_conv3d_fact(x, w_s, w_t)
     with pytest.raises(ValueError, match="channels_last_3d"):
         cvt.causal_conv3d_fact_proj(x, None, w_t, w_p)
+
+
+def test_conv_noalloc_validation():
+    """The no-alloc conv validates like cvt_causal_conv3d_fact and refuses, before touching
+    any device, a call whose packed weights and intermediate exceed the preallocated
+    scratch."""
+    def call(**kw):
+        return lib.cvt_causal_conv3d_fact_noalloc(kw.get("x", A), kw.get("ws", B_), kw.get("wt", C_), None, None,
+                                                  kw.get("y", ctypes.c_void_p(0x400000)), 1, kw.get("Cin", 256),
+                                                  kw.get("Cout", 256), kw.get("T", 10), kw.get("H", 100), 160, 3,
+                                                  None)
+    assert call(x=None) == E_NULL
+    assert call(ws=None, wt=None) == E_NULL
+    assert call(Cin=12) == E_SHAPE
+    assert call(x=MIS) == E_ALIGN
+    assert call() == E_WORKSPACE                      # 160,000 positions x 256 channels of intermediate
+    assert b"preallocated scratch" in lib.cvt_last_error()
+    assert lib.cvt_causal_conv3d_fact_workspace(1, 256, 256, 10, 100, 160, 3, 3) > cvt.NOALLOC_SCRATCH_BYTES
+    assert cvt.NOALLOC_SCRATCH_BYTES == 64 << 20
