@@ -62,6 +62,10 @@ SIGNATURES = {
     "cvt_causal_conv3d_fact_proj_fsq_workspace": (_sz, [_ci] * 9),
     "cvt_causal_conv3d_fact_proj_fsq": (_ci, [_vp] * 7 + [_vp, _ci, _vp, _vp] + [_ci] * 7 + [_vp, _sz, _vp]),
     "cvt_fsq_dequantize_proj": (_ci, [_vp, _vp, _ci, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "cvt_haar3d_conv3d_fact_workspace": (_sz, [_ci] * 6),
+    "cvt_haar3d_conv3d_fact": (_ci, [_vp] * 6 + [_ci] * 5 + [_vp, _sz, _vp]),
+    "cvt_fsq_dequantize_conv3d_fact_workspace": (_sz, [_ci] * 7),
+    "cvt_fsq_dequantize_conv3d_fact": (_ci, [_vp, _vp, _ci] + [_vp] * 7 + [_ci] * 6 + [_vp, _sz, _vp]),
     "cvt_layernorm3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _ci, _vp]),
     "cvt_resblock3d_workspace": (_sz, [_ci] * 5),
     "cvt_resblock3d": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _vp, _sz, _vp]),
@@ -725,4 +729,77 @@ def fsq_dequantize_proj(indices, w_p, b_p=None, levels=DEFAULT_LEVELS, invalid_c
     arr, n = _levels_arg(levels)
     _check(lib.cvt_fsq_dequantize_proj(_ptr(indices), arr, n, _ptr(w_p), _ptr(b_p), _ptr(y), B, Cout, T, H, W,
                                        _ptr(invalid_count), _stream(indices.device)), "fsq_dequantize_proj")
+    return y
+
+
+def haar3d_conv3d_fact_workspace_bytes(x_shape, Cout, temporal=True):
+    B, C, T, H, W = x_shape
+    parts = CVT_CONV_SPATIAL | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_haar3d_conv3d_fact_workspace(B, Cout, T, H, W, parts))
+
+
+def haar3d_conv3d_fact(x, w_s, w_t=None, b_s=None, b_t=None, workspace=None, out=None):
+    """causal_conv3d_fact(haar3d_fwd(x), w_s, w_t) for a 3-channel bf16 clip x [B, 3, T, H, W]
+    (NCTHW), the Haar coefficients computed inside the spatial conv's loads and never written.
+    w_s: bf16 [Cout, 192, 1, 3, 3]; w_t: bf16 [Cout, Cout, 3, 1, 1] or None.  Returns
+    [B, Cout, 1 + (T-1)/4, H/4, W/4] bf16 channels_last_3d."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (NCTHW) bfloat16 clip")
+    _require_gpu(x, w_s, w_t, b_s, b_t, workspace)
+    _same_device(x, w_s, w_t, b_s, b_t, workspace)
+    B, C, T, H, W = x.shape
+    if C != 3:
+        raise ValueError("the fused Haar conv takes 3-channel clips")
+    Cout = w_s.shape[0]
+    _bf16_w(w_s, (Cout, 192, 1, 3, 3), "w_s")
+    if w_t is not None:
+        _bf16_w(w_t, (Cout, Cout, 3, 1, 1), "w_t")
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    need = haar3d_conv3d_fact_workspace_bytes(x.shape, Cout, w_t is not None)
+    workspace = _workspace_arg(workspace, need, x)
+    shape = (B, Cout, 1 + max(T - 1, 0) // 4, H // 4, W // 4)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_haar3d_conv3d_fact(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cout, T, H, W,
+                                      _ptr(workspace), workspace.numel(), _stream(x.device)), "haar3d_conv3d_fact")
+    return y
+
+
+def fsq_dequantize_conv3d_fact_workspace_bytes(idx_shape, Cmid, Cout, temporal=True):
+    B, T, H, W = idx_shape
+    parts = CVT_CONV_SPATIAL | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_fsq_dequantize_conv3d_fact_workspace(B, Cmid, Cout, T, H, W, parts))
+
+
+def fsq_dequantize_conv3d_fact(indices, w_lift, w_s, w_t=None, b_lift=None, b_s=None, b_t=None,
+                               levels=DEFAULT_LEVELS, workspace=None, out=None):
+    """causal_conv3d_fact(fsq_dequantize_proj(indices, w_lift, b_lift), w_s, w_t) with the
+    projection computed inside the spatial conv's loads and never written; equal to the
+    unfused route bit for bit.  indices: int32 [B, T, H, W]; w_lift: bf16 [Cmid, D, 1, 1, 1];
+    w_s: bf16 [Cout, Cmid, 1, 3, 3]; w_t: bf16 [Cout, Cout, 3, 1, 1] or None."""
+    if indices.dtype != torch.int32 or not indices.is_contiguous():
+        raise ValueError("indices must be contiguous int32 [B, T, H, W]")
+    _require_gpu(indices, w_lift, w_s, w_t, b_lift, b_s, b_t, workspace)
+    _same_device(indices, w_lift, w_s, w_t, b_lift, b_s, b_t, workspace)
+    B, T, H, W = indices.shape
+    D = len(levels)
+    Cmid, Cout = w_lift.shape[0], w_s.shape[0]
+    _bf16_w(w_lift, (Cmid, D, 1, 1, 1), "w_lift")
+    _bf16_w(w_s, (Cout, Cmid, 1, 3, 3), "w_s")
+    if w_t is not None:
+        _bf16_w(w_t, (Cout, Cout, 3, 1, 1), "w_t")
+    _f32_vec(b_lift, Cmid, "b_lift")
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    need = fsq_dequantize_conv3d_fact_workspace_bytes(indices.shape, Cmid, Cout, w_t is not None)
+    workspace = _workspace_arg(workspace, need, indices)
+    shape = (B, Cout, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, indices.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, indices.device, CVT_NTHWC))
+    arr, n = _levels_arg(levels)
+    _check(lib.cvt_fsq_dequantize_conv3d_fact(_ptr(indices), arr, n, _ptr(w_lift), _ptr(b_lift), _ptr(w_s), _ptr(w_t),
+                                              _ptr(b_s), _ptr(b_t), _ptr(y), B, Cmid, Cout, T, H, W, _ptr(workspace),
+                                              workspace.numel(), _stream(indices.device)),
+           "fsq_dequantize_conv3d_fact")
     return y

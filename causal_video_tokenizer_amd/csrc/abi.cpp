@@ -587,4 +587,73 @@ int cvt_fsq_dequantize_proj(const int32_t* indices, const int32_t* levels, int D
                       "cvt_fsq_dequantize_proj launch");
 }
 
+size_t cvt_haar3d_conv3d_fact_workspace(int B, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    if (parts != CVT_CONV_SPATIAL && parts != (CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL)) return 0;
+    return cvt::haar_conv_workspace_bytes(B, Cout, T, H, W, (parts & CVT_CONV_TEMPORAL) != 0);
+}
+
+int cvt_haar3d_conv3d_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                           void* y, int B, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (!x || !w_s || !y) return fail(CVT_E_NULL, "x, w_s and y must not be NULL");
+    if (B <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (T % 4 != 1) return fail(CVT_E_SHAPE, "the clip needs T = 1 + 4k frames, got %d", T);
+    if (H % 4 != 0 || W % 4 != 0) return fail(CVT_E_SHAPE, "H and W must be multiples of 4, got %dx%d", H, W);
+    if (Cout < 64 || Cout > 4096 || Cout % 8 != 0)
+        return fail(CVT_E_SHAPE, "Cout must be a multiple of 8 in 64..4096, got %d", Cout);
+    // the fused loads address the clip with 31-bit byte offsets
+    if ((long long)B * 3 * T * H * W * 2 >= 0x7fff0000LL) return fail(CVT_E_SHAPE, "the clip must stay below 2 GiB");
+    if ((long long)(H / 4) * (W / 4) * (1 + (T - 1) / 4) * B >= (1LL << 31))
+        return fail(CVT_E_SHAPE, "too many latent positions");
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::haar_conv_workspace_bytes(B, Cout, T, H, W, w_t != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_haar_conv(x, w_s, w_t, b_s, b_t, y, B, Cout, T, H, W, workspace, (hipStream_t)stream),
+                      "cvt_haar3d_conv3d_fact launch");
+}
+
+size_t cvt_fsq_dequantize_conv3d_fact_workspace(int B, int Cmid, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cmid <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    if (parts != CVT_CONV_SPATIAL && parts != (CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL)) return 0;
+    return cvt::fsq_conv_workspace_bytes(B, Cmid, Cout, T, H, W, (parts & CVT_CONV_TEMPORAL) != 0);
+}
+
+int cvt_fsq_dequantize_conv3d_fact(const int32_t* indices, const int32_t* levels, int D, const void* w_lift,
+                                   const float* b_lift, const void* w_s, const void* w_t, const float* b_s,
+                                   const float* b_t, void* y, int B, int Cmid, int Cout, int T, int H, int W,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (!indices || !w_lift || !w_s || !y) return fail(CVT_E_NULL, "indices, w_lift, w_s and y must not be NULL");
+    cvt::FsqParams p;
+    const int st = fsq_params(levels, D, &p);
+    if (st != CVT_OK) return st;
+    if (B <= 0 || Cmid <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (Cmid % 32 != 0 || Cmid > 256) return fail(CVT_E_SHAPE, "Cmid must be a multiple of 32 up to 256, got %d", Cmid);
+    if (Cout < 64 || Cout > 4096 || Cout % 8 != 0)
+        return fail(CVT_E_SHAPE, "Cout must be a multiple of 8 in 64..4096, got %d", Cout);
+    if ((long long)B * T * H * W * 4 >= 0x7fff0000LL) return fail(CVT_E_SHAPE, "the indices must stay below 2 GiB");
+    if (!aligned16(indices) || !aligned16(y)) return fail(CVT_E_ALIGN, "indices and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w_lift) & 1u) || (reinterpret_cast<uintptr_t>(w_s) & 1u) ||
+        (reinterpret_cast<uintptr_t>(w_t) & 1u))
+        return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    if ((b_lift && (reinterpret_cast<uintptr_t>(b_lift) & 3u)) || (b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) ||
+        (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::fsq_conv_workspace_bytes(B, Cmid, Cout, T, H, W, w_t != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(cvt::launch_fsq_conv(indices, p, w_lift, b_lift, w_s, w_t, b_s, b_t, y, B, Cmid, Cout, T, H, W,
+                                           workspace, (hipStream_t)stream),
+                      "cvt_fsq_dequantize_conv3d_fact launch");
+}
+
 }  // extern "C"

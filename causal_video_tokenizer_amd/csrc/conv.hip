@@ -310,7 +310,10 @@ struct RowsAux {
     float eps;             // NORM: added to the variance
     int swish;             // NORM: apply Swish after the affine step
     int32_t* fsq_idx;      // PROJ: FSQ indices of the projected latent (nullptr = none)
-    FsqParams fsq;         // PROJ with fsq_idx: the level set (D = Cp <= 8)
+    FsqParams fsq;         // PROJ with fsq_idx, and SRC_FSQ: the level set (D = Cp <= 8)
+    int px_T;              // SRC_HAAR: frames of the pixel clip (4 T' - 3)
+    const uint16_t* lift_w;  // SRC_FSQ: the projection D -> Cin, bf16 [Cin][D]
+    const float* lift_b;     // SRC_FSQ: its bias, float32 [Cin] or nullptr
 };
 
 // LDS bytes per region row: BK channels + 16 bytes of padding
@@ -332,9 +335,21 @@ constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows
 // tile are staged de-interleaved, the NC + 1 odd ones (input columns 2 c0 - 1 + 2 m) first
 // and the NC even ones (2 c0 + 2 m) after them, so the column shifts kx = 0, 1, 2 read the
 // contiguous runs starting at region columns 0, NC + 1 and 1.
-template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4, int S_ = 1>
+// SRC: where the region's input channels come from.  SRC_TENSOR: the NTHWC input tensor.
+// The other two compute them while staging (cross-stage fusion, spatial conv at stride 1 on
+// 256-thread workgroups with one region row per thread):
+//   SRC_HAAR: X holds the pixel clip [B, 3, 4T'-3, 4H, 4W] (bf16 NCTHW) and the 192 input
+//     channels are its 2-level Haar coefficients in pixel-channel order (see haar_region);
+//   SRC_FSQ: X holds int32 FSQ indices [B, T, H, W] and the input channels are the 1x1
+//     projection of their dequantized codes (see fsq_region).
+constexpr int SRC_TENSOR = 0, SRC_HAAR = 1, SRC_FSQ = 2;
+constexpr int LIFT_MAX_C = 256;                          // SRC_FSQ: widest projection staged in LDS
+constexpr int LIFT_BYTES = (FSQ_MAX_D + 1) * LIFT_MAX_C * 4;  // its weights [c][n] and bias, float32
+
+template <int KIND_, int R_, int WCH_, int FA_, int BK_, int NW_ = 4, int S_ = 1, int SRC_ = SRC_TENSOR>
 struct RowsCfg {
     static constexpr int KIND = KIND_, R = R_, WCH = WCH_, FA = FA_, FB = 2 / FA_, BK = BK_, NW = NW_, S = S_;
+    static constexpr int SRC = SRC_;
     static constexpr int NTH = 64 * NW;                         // threads per workgroup
     static constexpr int WPOS = NW / WCH;                       // waves along columns
     static constexpr int KX = KIND == SPATIAL3 ? 3 : 1;         // column shifts
@@ -357,6 +372,8 @@ struct RowsCfg {
     static_assert((NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
                       R <= 4 && (S == 1 || S == 2),
                   "tile shape");
+    static_assert(SRC == SRC_TENSOR || (KIND == SPATIAL3 && S == 1 && BK == 32 && RROWS * RC <= NTH && XROWS == NTH),
+                  "computed regions: spatial, stride 1, 32-channel chunks, one region row per thread");
 };
 
 template <typename C, int NV, bool TAIL, int EPI, bool HIST>
@@ -437,7 +454,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     constexpr int NS = KS * KX;                       // steps per chunk: (k-step, column shift)
     constexpr int XH = NS >= 4 ? (XL + 1) / 2 : XL;  // loads of batch 0 (short chunks: one batch)
     uint4 xr[XH];
-    auto load_region = [&](int kc, int half) {  // kc past the last chunk reads zeros
+    auto load_region_t = [&](int kc, int half) {  // kc past the last chunk reads zeros
 #pragma unroll
         for (int i = half * XH; i < (half ? XL : XH); ++i) {
             int off = xbase[i] + kc * BK * 2;
@@ -459,7 +476,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             xr[i - half * XH] = u;
         }
     };
-    auto store_region = [&](int buf, int half) {
+    auto store_region_t = [&](int buf, int half) {
 #pragma unroll
         for (int i = half * XH; i < (half ? XL : XH); ++i) {
             const int q = tid + NTH * i;
@@ -467,6 +484,173 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             xmap(q, row, c16);
             if (XQ % NTH == 0 || q < XQ) *reinterpret_cast<uint4*>(sX(buf) + row * XS + c16 * 16) = xr[i - half * XH];
         }
+    };
+
+    // ---- computed regions: thread tid stages region row tid (region row prr, column pcc, i.e.
+    // latent row py and column pxx of frame t), zeros outside the grid
+    constexpr int SRC = C::SRC;
+    const int prr = tid / RC, pcc = tid % RC;
+    const int py = r0 - 1 + prr, pxx = c0 - 1 + pcc;
+    const bool pok = tid < C::RROWS * RC && prr < NRU && py >= 0 && py < g.H && pxx >= 0 && pxx < g.W;
+    // SRC_HAAR.  Chunk kc holds 32 coefficients of pixel channel kc / 2: those of level-1
+    // temporal band q = kc % 2 (packet rows rt = 2 q, 2 q + 1), channel m = 16 (rt % 2) + 4 rh +
+    // rw (pack_frag_kernel orders the weights to match).  By linearity the two temporal rows
+    // of the 4-frame block are 2D transforms of A = P + Q and B = P - Q with P = f0 + s f1,
+    // Q = f2 + s f3, s = (-1)^q; the two frame pairs are loaded in the two region batches,
+    // and P waits in the thread's own (still free) region row between them.
+    const int hrow = 8 * g.W;                 // bytes per pixel row
+    const int hplane = 32 * g.H * g.W;        // bytes per pixel frame
+    int hoff = 0;                             // the block's first row in frame 0 of pixel channel 0
+    int hfr[4] = {0, 0, 0, 0};                // frame offsets: padded frame 4 t + f is frame max(4 t + f - 3, 0)
+    if constexpr (SRC == SRC_HAAR) {
+        hoff = b * 3 * aux.px_T * hplane + 4 * py * hrow + 8 * pxx;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) hfr[f] = max(4 * t + f - 3, 0) * hplane;
+    }
+    uint2 hr[SRC == SRC_HAAR ? 8 : 1];        // 4 rows of 4 pixels of two frames
+    auto haar_load = [&](int kc, int half) {  // kc past the last chunk reads zeros
+        const bool ok = pok && kc * BK < g.Cin;
+        const int cbase = hoff + (kc >> 1) * aux.px_T * hplane;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int off = ok ? cbase + hfr[2 * half + f] + r * hrow : OOB;
+                hr[4 * f + r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xres, off, 0, 0));
+            }
+    };
+    auto pix = [](const uint2 u, int k) {
+        return k == 0 ? bf16_lo(u.x) : k == 1 ? bf16_hi(u.x) : k == 2 ? bf16_lo(u.y) : bf16_hi(u.y);
+    };
+    auto haar_store = [&](int buf, int half, int kc) {
+        float* rowf = reinterpret_cast<float*>(sX(buf) + tid * XS);
+        const float sg = (kc & 1) ? -1.0f : 1.0f;
+        if (half == 0) {  // P, parked in the row
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<float4*>(rowf + 4 * r) =
+                    make_float4(pix(hr[r], 0) + sg * pix(hr[4 + r], 0), pix(hr[r], 1) + sg * pix(hr[4 + r], 1),
+                                pix(hr[r], 2) + sg * pix(hr[4 + r], 2), pix(hr[r], 3) + sg * pix(hr[4 + r], 3));
+            return;
+        }
+        float A[4][4], Bq[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 pv = *reinterpret_cast<const float4*>(rowf + 4 * r);
+            const float P[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float Q = pix(hr[r], k) + sg * pix(hr[4 + r], k);
+                A[r][k] = P[k] + Q;
+                Bq[r][k] = P[k] - Q;
+            }
+        }
+        auto packet = [](float& a, float& b, float& c, float& d) {  // rows 1/2 (1,1,1,1), (1,1,-1,-1), (1,-1,1,-1), (1,-1,-1,1), unscaled
+            const float s0 = a + b, d0 = a - b, s1 = c + d, d1 = c - d;
+            a = s0 + s1;
+            b = s0 - s1;
+            c = d0 + d1;
+            d = d0 - d1;
+        };
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            packet(A[r][0], A[r][1], A[r][2], A[r][3]);
+            packet(Bq[r][0], Bq[r][1], Bq[r][2], Bq[r][3]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            packet(A[0][k], A[1][k], A[2][k], A[3][k]);
+            packet(Bq[0][k], Bq[1][k], Bq[2][k], Bq[3][k]);
+        }
+        uint4* rowv = reinterpret_cast<uint4*>(rowf);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {  // channels 8 j .. 8 j + 7: rh = 2 j, 2 j + 1 of A; then of B
+            rowv[j] = make_uint4(pack_bf16x2(A[2 * j][0] * 0.125f, A[2 * j][1] * 0.125f),
+                                 pack_bf16x2(A[2 * j][2] * 0.125f, A[2 * j][3] * 0.125f),
+                                 pack_bf16x2(A[2 * j + 1][0] * 0.125f, A[2 * j + 1][1] * 0.125f),
+                                 pack_bf16x2(A[2 * j + 1][2] * 0.125f, A[2 * j + 1][3] * 0.125f));
+            rowv[2 + j] = make_uint4(pack_bf16x2(Bq[2 * j][0] * 0.125f, Bq[2 * j][1] * 0.125f),
+                                     pack_bf16x2(Bq[2 * j][2] * 0.125f, Bq[2 * j][3] * 0.125f),
+                                     pack_bf16x2(Bq[2 * j + 1][0] * 0.125f, Bq[2 * j + 1][1] * 0.125f),
+                                     pack_bf16x2(Bq[2 * j + 1][2] * 0.125f, Bq[2 * j + 1][3] * 0.125f));
+        }
+    };
+    // SRC_FSQ.  The position's index, the same for every chunk, is loaded once; chunk kc holds
+    // output channels 32 kc .. 32 kc + 31 of the projection, each accumulated as the
+    // dequantize + 1x1 kernel does (bias, then fmaf over the bf16-rounded codes in channel
+    // order), so the staged values equal that kernel's bf16 output.  The projection weights
+    // and bias sit in LDS after the region buffers as float32 [c][LIFT_MAX_C] rows (row
+    // FSQ_MAX_D: the bias), read as broadcasts.
+    int fidx = 0;
+    if constexpr (SRC == SRC_FSQ) {
+        const int pos = ((b * g.T + t) * g.H + py) * g.W + pxx;
+        fidx = (int)__builtin_amdgcn_raw_buffer_load_b32(xres, pok ? pos * 4 : OOB, 0, 0);
+    }
+    auto fsq_store = [&](int buf, int kc) {
+        const float* wl = reinterpret_cast<const float*>(smem + C::REGION_BYTES);
+        const FsqParams& fp = aux.fsq;
+        const bool bad = fidx < 0 || fidx >= fp.codebook;
+        uint32_t rem = bad ? 0u : (uint32_t)fidx;
+        float xv[FSQ_MAX_D];
+#pragma unroll
+        for (int i = 0; i < FSQ_MAX_D; ++i) {
+            xv[i] = 0.0f;
+            if (i < fp.D) {
+                const uint32_t q = div_magic(rem, fp.magic[i], fp.shift[i]);
+                const int d = (int)(rem - q * (uint32_t)fp.levels[i]);
+                rem = q;
+                const int h = fp.half[i];
+                const float code = (h & (h - 1)) == 0 ? (float)(d - h) * (1.0f / (float)h) : (float)(d - h) / (float)h;
+                xv[i] = bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code));
+            }
+        }
+        uint4* rowv = reinterpret_cast<uint4*>(sX(buf) + tid * XS);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // 8 channels at a time
+            const int n0 = kc * BK + 8 * j;
+            float o[8];
+            const float4 b0 = *reinterpret_cast<const float4*>(wl + FSQ_MAX_D * LIFT_MAX_C + n0);
+            const float4 b1 = *reinterpret_cast<const float4*>(wl + FSQ_MAX_D * LIFT_MAX_C + n0 + 4);
+            o[0] = b0.x; o[1] = b0.y; o[2] = b0.z; o[3] = b0.w; o[4] = b1.x; o[5] = b1.y; o[6] = b1.z; o[7] = b1.w;
+#pragma unroll
+            for (int c = 0; c < FSQ_MAX_D; ++c) {
+                if (c < fp.D) {
+                    const float4 w0 = *reinterpret_cast<const float4*>(wl + c * LIFT_MAX_C + n0);
+                    const float4 w1 = *reinterpret_cast<const float4*>(wl + c * LIFT_MAX_C + n0 + 4);
+                    o[0] = fmaf(w0.x, xv[c], o[0]); o[1] = fmaf(w0.y, xv[c], o[1]);
+                    o[2] = fmaf(w0.z, xv[c], o[2]); o[3] = fmaf(w0.w, xv[c], o[3]);
+                    o[4] = fmaf(w1.x, xv[c], o[4]); o[5] = fmaf(w1.y, xv[c], o[5]);
+                    o[6] = fmaf(w1.z, xv[c], o[6]); o[7] = fmaf(w1.w, xv[c], o[7]);
+                }
+            }
+            rowv[j] = pok ? make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                       pack_bf16x2(o[6], o[7]))
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    if constexpr (SRC == SRC_FSQ) {  // the projection table, once per tile
+        float* wl = reinterpret_cast<float*>(smem + C::REGION_BYTES);
+        const int D = aux.fsq.D;
+        for (int i = tid; i < (FSQ_MAX_D + 1) * LIFT_MAX_C; i += NTH) {
+            const int c = i / LIFT_MAX_C, n = i - c * LIFT_MAX_C;
+            float v = 0.0f;
+            if (n < g.Cin) {
+                if (c < D) v = bf16_to_f32(aux.lift_w[n * D + c]);
+                else if (c == FSQ_MAX_D && aux.lift_b) v = aux.lift_b[n];
+            }
+            wl[i] = v;
+        }
+        __syncthreads();
+    }
+    // region batch `half` of chunk kc: loads, then (a few steps later) the LDS stores
+    auto load_region = [&](int kc, int half) {
+        if constexpr (SRC == SRC_TENSOR) load_region_t(kc, half);
+        else if constexpr (SRC == SRC_HAAR) haar_load(kc, half);
+    };
+    auto store_region = [&](int buf, int half, int kc) {
+        if constexpr (SRC == SRC_TENSOR) store_region_t(buf, half);
+        else if constexpr (SRC == SRC_HAAR) haar_store(buf, half, kc);
+        else if (half == 1) fsq_store(buf, kc);
     };
 
     // weight fragments of (k-step kc16, column shift kx): tap rows 0..2 of blocks ab0 ..
@@ -585,10 +769,10 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
 #pragma unroll
     for (int s = 0; s < (EARLY ? NSET : PD); ++s) prefetch(0, s);
     load_region(0, 0);
-    store_region(0, 0);
+    store_region(0, 0, 0);
     if (L1 > 0) {
         load_region(0, 1);
-        store_region(0, 1);
+        store_region(0, 1, 0);
     }
     __syncthreads();
     bf16x8_t fb[2][NRU][FB];  // activation fragments of the current and the next step
@@ -603,7 +787,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         for (int st = 0; st < NS; ++st) {
             if constexpr (!EARLY) prefetch(kc, st + PD);
             __builtin_amdgcn_sched_barrier(0);  // weight prefetch before any region load
-            if (L1 > 0 && st == L1) store_region(nbuf, 0);
+            if (L1 > 0 && st == L1) store_region(nbuf, 0, kc + 1);
             if (st == 0) load_region(kc + 1, 0);
             if (L1 > 0 && st == L1) load_region(kc + 1, 1);
             // keep the prefetches issued here: left alone the scheduler sinks them towards
@@ -613,9 +797,9 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                     [&](int ky) { prefetch_ky(kc, st + 2, ky); });
         }
         if (L1 == 0)
-            store_region(nbuf, 0);
+            store_region(nbuf, 0, kc + 1);
         else
-            store_region(nbuf, 1);
+            store_region(nbuf, 1, kc + 1);
         __syncthreads();
     }
 
@@ -945,7 +1129,7 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     // the region buffers; the fused projection's partial sums reuse them after the K loop
     __shared__ __attribute__((aligned(16))) uint8_t smem[(epi_proj<EPI>() || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES)
                                                                       : EPI == EPI_RES ? std::max(C::REGION_BYTES, C::RES_BYTES)
-                                                                                       : C::REGION_BYTES];
+                                                                                       : C::REGION_BYTES + (C::SRC == SRC_FSQ ? LIFT_BYTES : 0)];
 
     int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
@@ -978,12 +1162,26 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
         rows_nv<C, TAIL, EPI, false>(nv, Wf, X, bias, Y, Wpf, bias_p, Hx, g, aux, smem, b, t, ct, r0, c0);
 }
 
+// Input channel k of the K dimension in the Haar-fused spatial conv (SRC_HAAR): pixel
+// channel k / 64, level-1 temporal band q = (k / 32) % 2, m = k % 32 the packet rows rt =
+// 2 q + m / 16, rh = (m / 4) % 4, rw = m % 4, which the Haar coefficient channel
+// s2 * 24 + s1 * 3 + c holds (s1 the level-1 bands (rt, rh, rw) / 2, s2 the level-2 bands
+// (rt, rh, rw) % 2, each as 4 b_t + 2 b_h + b_w).
+__host__ __device__ inline int haar_k_channel(int k) {
+    const int c = k / 64, q = (k / 32) & 1, m = k & 31;
+    const int rt = 2 * q + m / 16, rh = (m / 4) & 3, rw = m & 3;
+    const int s1 = ((rt >> 1) << 2) | ((rh >> 1) << 1) | (rw >> 1);
+    const int s2 = ((rt & 1) << 2) | ((rh & 1) << 1) | (rw & 1);
+    return s2 * 24 + s1 * 3 + c;
+}
+
 // Weights in MFMA fragment order for conv_rows_kernel: fragment f = (kc16 * taps + j) * NA
 // + ab holds, for lane l, the 8 values w[ab * 32 + l % 32][kc16 * 16 + (l / 32) * 8 + e][j],
 // e = 0..7, at element offset (f * 64 + l) * 8 + e; rows past Cout and channels past Cin
-// are zero.  Input layout is torch's [Cout][Cin][taps].
+// are zero.  Input layout is torch's [Cout][Cin][taps].  haar_k: input channel k is
+// haar_k_channel(k) of w (Cin = 192).
 __global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wf,
-                                                        int Cout, int Cin, int ntaps, int NA, int KC16) {
+                                                        int Cout, int Cin, int ntaps, int NA, int KC16, int haar_k) {
     const long long total = (long long)KC16 * ntaps * NA * 512;
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (long long)gridDim.x * blockDim.x) {
@@ -994,7 +1192,8 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restri
         const int j = (int)(f2 % ntaps), kc16 = (int)(f2 / ntaps);
         const int row = ab * 32 + (l & 31);
         const int k = kc16 * 16 + (l >> 5) * 8 + e;
-        wf[i] = (row < Cout && k < Cin) ? w[((size_t)row * Cin + k) * ntaps + j] : (uint16_t)0;
+        const int ks = haar_k ? haar_k_channel(k) : k;
+        wf[i] = (row < Cout && k < Cin) ? w[((size_t)row * Cin + ks) * ntaps + j] : (uint16_t)0;
     }
 }
 
@@ -1263,6 +1462,9 @@ using SpatialCfg = RowsCfg<SPATIAL3, 4, CVT_ROWS_SP_WCH, CVT_ROWS_SP_FA, CVT_ROW
 // the default; 2% faster than 128 x 64 on the 720p layers, and it pads less on some shapes (192
 // channels on 160-column rows: 1.33x the work instead of 1.6x)
 using SpatialWideCfg = RowsCfg<SPATIAL3, 4, 4, 2, 32, 4>;
+// the same tiles staging computed regions (cross-stage fusion): Haar of pixels, dequantized FSQ
+using SpatialHaarCfg = RowsCfg<SPATIAL3, 4, 4, 2, 32, 4, 1, SRC_HAAR>;
+using SpatialFsqCfg = RowsCfg<SPATIAL3, 4, 4, 2, 32, 4, 1, SRC_FSQ>;
 #ifndef CVT_ROWS_TM_BK
 #define CVT_ROWS_TM_BK 32
 #endif
@@ -1316,6 +1518,8 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.Wi = in_grid ? cg.Wi : cg.W;
     if (C::S == 2 && cg.ups) return hipErrorInvalidValue;
     g.x_bytes = (int)((long long)B * g.Ti * g.Hi * g.Wi * cg.Cin * 2);
+    if constexpr (C::SRC == SRC_HAAR) g.x_bytes = (int)((long long)B * 3 * aux.px_T * 16 * cg.H * cg.W * 2);
+    if constexpr (C::SRC == SRC_FSQ) g.x_bytes = (int)((long long)B * cg.T * cg.H * cg.W * 4);
     if (cg.ups && Hx) return hipErrorInvalidValue;
     g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
     g.NA = (cg.Cout + 31) / 32;
@@ -1449,12 +1653,12 @@ bool use_rows_kernel(int k, int Cout, long long P, int Cin) {
     return k == 3 && Cout >= 64 && Cout % 8 == 0 && P * Cin * 2 < ROWS_OOB_BASE;
 }
 
-hipError_t pack_frag(const void* w, uint16_t* wf, int Cout, int Cin, int ntaps, hipStream_t s) {
+hipError_t pack_frag(const void* w, uint16_t* wf, int Cout, int Cin, int ntaps, hipStream_t s, int haar_k = 0) {
     const int NA = (Cout + 31) / 32, KC16 = (Cin + 15) / 16;
     const long long total = (long long)KC16 * ntaps * NA * 512;
     const long long nblk = std::min((total + 255) / 256, 65535LL);
     hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)nblk), dim3(256), 0, s, (const uint16_t*)w, wf, Cout, Cin,
-                       ntaps, NA, KC16);
+                       ntaps, NA, KC16, haar_k);
     return hipGetLastError();
 }
 
@@ -1533,6 +1737,74 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     }
     if ((e = pack(w_t, wpt, Cout, Cout, k, s)) != hipSuccess) return e;
     return launch_igemm(k == 3 ? TEMPORAL3 : POINT, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
+}
+
+// The factorized conv of the Haar coefficients of a 3-channel bf16 clip [B, 3, T, H, W]
+// (T = 1 + 4k, causal first frame), the coefficients computed while the spatial conv stages
+// its input (SpatialHaarCfg) and never written.  Workspace: the packed spatial weights (in
+// the staged channel order) and, with the temporal part, its packed weights and the bf16
+// spatial output.
+size_t haar_conv_workspace_bytes(int B, int Cout, int T, int H, int W, bool temporal) {
+    const size_t P = (size_t)B * (1 + (T - 1) / 4) * (H / 4) * (W / 4);
+    size_t b = pack_bytes(Cout, 192, 9);
+    if (temporal) b += pack_bytes(Cout, Cout, 3) + align256(P * Cout * 2);
+    return b;
+}
+
+hipError_t launch_haar_conv(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                            void* y, int B, int Cout, int T, int H, int W, void* workspace, hipStream_t s) {
+    const int Tq = 1 + (T - 1) / 4, Hq = H / 4, Wq = W / 4;
+    const long long P = (long long)B * Tq * Hq * Wq;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint16_t* wps = reinterpret_cast<uint16_t*>(ws);
+    size_t off = pack_bytes(Cout, 192, 9);
+    uint8_t* tws = ws + off;
+    uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(tws + pack_bytes(Cout, Cout, 3)) : static_cast<uint16_t*>(y);
+    hipError_t e;
+    if ((e = pack_frag(w_s, wps, Cout, 192, 9, s, 1)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = P; g.T = Tq; g.H = Hq; g.W = Wq; g.Cin = 192; g.Cout = Cout;
+    g.kchunks = 192 / BK;
+    RowsAux aux{};
+    aux.px_T = T;
+    if ((e = launch_rows_cfg<SpatialHaarCfg>(static_cast<const uint16_t*>(x), wps, b_s, S, g, B, s, nullptr, nullptr,
+                                             0, nullptr, aux)) != hipSuccess)
+        return e;
+    if (!w_t) return hipSuccess;
+    return launch_conv_fact(S, nullptr, w_t, nullptr, b_t, y, B, Cout, Cout, Tq, Hq, Wq, 3, tws, s);
+}
+
+// The factorized conv of the D -> Cmid projection of dequantized FSQ indices [B, T, H, W],
+// the projection computed while the spatial conv stages its input (SpatialFsqCfg).
+size_t fsq_conv_workspace_bytes(int B, int Cmid, int Cout, int T, int H, int W, bool temporal) {
+    const size_t P = (size_t)B * T * H * W;
+    size_t b = pack_bytes(Cout, Cmid, 9);
+    if (temporal) b += pack_bytes(Cout, Cout, 3) + align256(P * Cout * 2);
+    return b;
+}
+
+hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w_lift, const float* b_lift,
+                           const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
+                           int Cmid, int Cout, int T, int H, int W, void* workspace, hipStream_t s) {
+    const long long P = (long long)B * T * H * W;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint16_t* wps = reinterpret_cast<uint16_t*>(ws);
+    uint8_t* tws = ws + pack_bytes(Cout, Cmid, 9);
+    uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(tws + pack_bytes(Cout, Cout, 3)) : static_cast<uint16_t*>(y);
+    hipError_t e;
+    if ((e = pack_frag(w_s, wps, Cout, Cmid, 9, s)) != hipSuccess) return e;
+    ConvGeom g{};
+    g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cmid; g.Cout = Cout;
+    g.kchunks = Cmid / BK;
+    RowsAux aux{};
+    aux.fsq = p;
+    aux.lift_w = static_cast<const uint16_t*>(w_lift);
+    aux.lift_b = b_lift;
+    if ((e = launch_rows_cfg<SpatialFsqCfg>(reinterpret_cast<const uint16_t*>(idx), wps, b_s, S, g, B, s, nullptr,
+                                            nullptr, 0, nullptr, aux)) != hipSuccess)
+        return e;
+    if (!w_t) return hipSuccess;
+    return launch_conv_fact(S, nullptr, w_t, nullptr, b_t, y, B, Cout, Cout, T, H, W, 3, tws, s);
 }
 
 namespace {

@@ -122,6 +122,13 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
 hipError_t launch_conv_fact_noalloc(const void* x, const void* w_s, const void* w_t, const float* b_s,
                                     const float* b_t, void* y, int B, int Cin, int Cout, int T, int H, int W, int k,
                                     hipStream_t stream);
+// Cross-stage fusion (conv.hip): the factorized conv of the Haar coefficients of a 3-channel
+// bf16 clip [B, 3, T, H, W] (pixel sizes; coefficients computed in the spatial conv's loads),
+// and of the D -> Cmid projection of dequantized FSQ indices [B, T, H, W].
+size_t haar_conv_workspace_bytes(int B, int Cout, int T, int H, int W, bool temporal);
+hipError_t launch_haar_conv(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                            void* y, int B, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
+size_t fsq_conv_workspace_bytes(int B, int Cmid, int Cout, int T, int H, int W, bool temporal);
 // Factorized causal convolution followed by a 1x1x1 projection to Cp channels.
 size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
                                  bool temporal);
@@ -138,6 +145,9 @@ size_t conv_proj_fsq_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, in
 // kernel: y [positions][Cout] bf16 = w_p . bf16(codes) + b_p.
 hipError_t launch_fsq_dequant_proj(const int32_t* idx, const FsqParams& p, const void* w_p, const float* b_p, void* y,
                                    long long P, int Cout, int32_t* invalid, hipStream_t s);
+hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w_lift, const float* b_lift,
+                           const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
+                           int Cmid, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
 
 // Causal temporal convolution of one chunk of a stream (conv.hip): history frames in place
 // of the zero padding, optional fused 1x1 projection (C <= 256, Cp <= 16).

@@ -537,6 +537,68 @@ int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float*
 int cvt_fsq_dequantize_proj(const int32_t* indices, const int32_t* levels, int D, const void* w_p, const float* b_p,
                             void* y, int B, int Cout, int T, int H, int W, int32_t* d_invalid_count, void* stream);
 
+/*
+ * Cross-stage fusion: the Haar patcher inside the first convolution.  Computes
+ *   y = cvt_causal_conv3d_fact(cvt_haar3d_fwd(x, temporal_levels = 2), w_s, w_t)
+ * for a 3-channel clip without writing the 192 Haar coefficient channels: the
+ * spatial convolution computes them from the pixels while it stages its input
+ * (each 4 x 4 x 4 block per pixel channel; by linearity of the transform in an
+ * order of additions that differs from cvt_haar3d_fwd's, so values may differ
+ * from the unfused route by a bf16 rounding step).
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.1 (the Haar
+ * patcher is a fixed, parameter-free first stage of the encoder) and the
+ * Cosmos-Predict1 summary, section "1) Cosmos Tokenizer" (the factorized causal
+ * convolution that follows it).
+ *
+ * x:   bf16 NCTHW [B, 3, T, H, W], T = 1 + 4k, H and W multiples of 4, below
+ *      2 GiB.
+ * w_s: bf16 [Cout, 192, 1, 3, 3] over the coefficient channels in the order
+ *      cvt_haar3d_fwd writes them; w_t: bf16 [Cout, Cout, 3, 1, 1] or NULL
+ *      (spatial part only); b_s, b_t: float32 [Cout] or NULL.
+ * y:   bf16 NTHWC [B, Cout, 1 + (T-1)/4, H/4, W/4].  64 <= Cout <= 4096,
+ *      Cout % 8 == 0.
+ * workspace: cvt_haar3d_conv3d_fact_workspace() bytes (parts: CVT_CONV_SPATIAL,
+ *      or CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL when w_t is given).
+ * Errors: CVT_E_NULL (x, w_s, y), CVT_E_SHAPE (sizes above), CVT_E_ALIGN,
+ *      CVT_E_WORKSPACE.
+ */
+size_t cvt_haar3d_conv3d_fact_workspace(int B, int Cout, int T, int H, int W, int parts);
+int cvt_haar3d_conv3d_fact(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
+                           void* y, int B, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Cross-stage fusion: FSQ dequantize and the decoder's 1x1 projection inside the
+ * decoder's first convolution.  Computes
+ *   y = cvt_causal_conv3d_fact(cvt_fsq_dequantize_proj(indices, w_lift), w_s, w_t)
+ * without writing the Cmid-channel projection: the spatial convolution computes
+ * it from the int32 index of each position while it stages its input, rounded
+ * exactly as cvt_fsq_dequantize_proj rounds it, so y equals the unfused route
+ * bit for bit.
+ *
+ * Defined by: "NVIDIA Cosmos Tokenizer 完全指南", section 7.2 (FSQ: codes come
+ * from the index by mixed-radix digits, no codebook lookup) and the model card
+ * "Model Architecture" (the decoder mirrors the encoder, so its first layers are
+ * the projection out of the latent and the factorized causal convolution).
+ *
+ * indices: int32 [B, T, H, W] below 2 GiB; levels, D: as cvt_fsq_dequantize
+ *      (an out-of-range index gives NaN codes; it is not counted here).
+ * w_lift: bf16 [Cmid, D, 1, 1, 1], Cmid a multiple of 32 up to 256; b_lift:
+ *      float32 [Cmid] or NULL.
+ * w_s: bf16 [Cout, Cmid, 1, 3, 3]; w_t: bf16 [Cout, Cout, 3, 1, 1] or NULL;
+ *      b_s, b_t: float32 [Cout] or NULL.  64 <= Cout <= 4096, Cout % 8 == 0.
+ * y:   bf16 NTHWC [B, Cout, T, H, W].
+ * workspace: cvt_fsq_dequantize_conv3d_fact_workspace() bytes (parts as for
+ *      cvt_haar3d_conv3d_fact).
+ * Errors: CVT_E_NULL, CVT_E_LEVELS, CVT_E_SHAPE, CVT_E_ALIGN, CVT_E_WORKSPACE.
+ */
+size_t cvt_fsq_dequantize_conv3d_fact_workspace(int B, int Cmid, int Cout, int T, int H, int W, int parts);
+int cvt_fsq_dequantize_conv3d_fact(const int32_t* indices, const int32_t* levels, int D, const void* w_lift,
+                                   const float* b_lift, const void* w_s, const void* w_t, const float* b_s,
+                                   const float* b_t, void* y, int B, int Cmid, int Cout, int T, int H, int W,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
