@@ -26,7 +26,10 @@ grid of the CV8x8x8-720p model, 256 channels in 4 heads; a fifth, sliding window
 frames over a 50-frame 1080p clip (pad, Haar, inverse Haar, crop); a sixth, the encoder's
 residual and downsampling blocks and the decoder's upsampling block on the CV8x8x8-720p grids; a
 seventh, the batched DV4x8x8-360p decode (8 clips: dequantize + 1x1, conv 192->192, inverse Haar); an
-eighth, the 121-frame clip encoded as a stream of chunks against one whole-clip pass.
+eighth, the 121-frame clip encoded as a stream of chunks against one whole-clip pass.  The 49- and
+121-frame clips and the decode also time the cross-stage fusions inside the conv's operand loads
+(Haar of the pixels in the first spatial conv; dequantize + 1x1 in the decoder's conv) against
+the unfused calls, interleaved in one process.
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -74,6 +77,7 @@ def parse():
     ap.add_argument("--no-blocks", action="store_true", help="skip the encoder/decoder block measurement")
     ap.add_argument("--no-c5", action="store_true", help="skip the batched 360p decode measurement")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-encode measurement")
+    ap.add_argument("--no-fusion", action="store_true", help="skip the fused-versus-unfused measurements")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -81,6 +85,32 @@ def parse():
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def interleaved(torch, fns, reps, rounds=6, warm_s=0.5):
+    """Median milliseconds per call of each function: after warm_s seconds of calling them all
+    (the clocks settle only after some tens of milliseconds of work), `rounds` rounds each
+    time every function `reps` times back to back with HIP events on the current stream,
+    alternating the order from round to round (the first-measured one otherwise reads
+    slower)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+    res = [[] for _ in fns]
+    for r in range(rounds):
+        order = list(range(len(fns))) if r % 2 == 0 else list(reversed(range(len(fns))))
+        for i in order:
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fns[i]()
+            e.record()
+            torch.cuda.synchronize()
+            res[i].append(s.elapsed_time(e) / reps)
+    return [float(np.median(v)) for v in res]
 
 
 def main():
@@ -198,6 +228,18 @@ def main():
                 "kernel": "conv_rows_kernel<RowsCfg<SPATIAL3,R=4,WCH=4,FA=2,BK=32,NW=4>,false,false> (1x3x3 conv 192->256, bf16 MFMA)",
                 "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
 
+    fusion = None
+    if not args.no_fusion:
+        # the Haar patcher inside the spatial conv's loads, against the two calls of the step
+        hz_conv = torch.empty_like(s1)
+        ws_fz = torch.empty(cvt.haar3d_conv3d_fact_workspace_bytes(x.shape, 256, False), dtype=torch.uint8, device=dev)
+        unf, fus = interleaved(torch, [lambda: (calls["haar_fwd"](), calls["conv_spatial"]()),
+                                       lambda: cvt.haar3d_conv3d_fact(x, w_s, workspace=ws_fz, out=hz_conv)],
+                               max(5, args.steps // 2))
+        fusion = {"haar_then_spatial_conv_ms": round(unf, 4), "haar_inside_spatial_conv_ms": round(fus, 4),
+                  "fused_over_unfused": round(fus / unf, 4),
+                  "note": "the step keeps the two calls: its inverse-Haar stage reads the coefficients"}
+        del hz_conv, ws_fz
     c3 = None if args.no_c3 else cv8x8x8_chain(cvt, si, torch, dev, args)
     fsq_bw = None if args.no_fsq_bw else fsq_bandwidth(cvt, si, torch, dev, args)
     attn = None if args.no_attention else attention_tokens(cvt, si, torch, dev, args)
@@ -239,6 +281,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": per_stage,
+        "fusion_haar_conv_49f": fusion,
         "cv8x8x8_720p_121f": c3,
         "fsq_bandwidth_size": fsq_bw,
         "attention_cv8x8x8_720p_tokens": attn,
@@ -327,6 +370,17 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
     out["frames_per_s"] = round(B * T / (total * 1e-3), 1)
     out["conv_TFLOPs"] = round(conv_flops / (conv_ms * 1e-3) / 1e12, 1)
     out["conv_mfma_frac"] = round(conv_flops / (conv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    if not args.no_fusion:  # the Haar patcher inside layer 1's spatial conv
+        ws_fz = torch.empty(cvt.haar3d_conv3d_fact_workspace_bytes(x.shape, 256, False), dtype=torch.uint8, device=dev)
+        a2 = torch.empty_like(a)
+        unf, fus = interleaved(torch, [lambda: (stages[0][1](), stages[1][1]()),
+                                       lambda: cvt.haar3d_conv3d_fact(x, w[0], workspace=ws_fz, out=a2)],
+                               max(3, args.steps // 4))
+        rest = total - out["stages"]["haar_fwd"]["ms"] - out["stages"]["l1_spatial"]["ms"]
+        out["fusion"] = {"haar_then_l1_spatial_ms": round(unf, 4), "haar_inside_l1_spatial_ms": round(fus, 4),
+                         "fused_over_unfused": round(fus / unf, 4),
+                         "frames_per_s_fused_route": round(B * T / ((rest + fus) * 1e-3), 1)}
+        del ws_fz, a2
     del x, hz, a, b, lat, ws
     torch.cuda.empty_cache()
     return out
@@ -356,23 +410,13 @@ def fsq_bandwidth(cvt, si, torch, dev, args):
         ("quantize_nthwc", lambda: cvt.fsq_quantize(zc, indices=idx)),
         ("dequantize_nthwc", lambda: cvt.fsq_dequantize(idx, out=codes_c)),
     ]
-    reps = max(10, args.steps)
+    reps = max(10, args.steps // 2)
     nbytes = P * (D * 2 + 4.0)
-    out = {"shape": list(shape), "bytes_per_call": nbytes, "reps": reps}
-    # the GPU idled while the host generated the latents: bring its clocks back up first
-    for _ in range(max(10, args.warmup)):
-        for _, fn in cases:
-            fn()
-    torch.cuda.synchronize()
-    for name, fn in cases:
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
+    out = {"shape": list(shape), "bytes_per_call": nbytes, "reps": reps,
+           "timing": "median of 6 rounds alternating the case order, after 1 s of warm-up calls"}
+    # the GPU idled while the host generated the latents: interleaved() warms it up first
+    times = interleaved(torch, [fn for _, fn in cases], reps, warm_s=1.0)
+    for (name, fn), ms in zip(cases, times):
         gbps = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     del z, zc, idx, codes, codes_c
@@ -639,6 +683,19 @@ def decode_c5(cvt, si, torch, dev, args):
         out[name] = d
     out["chain_ms"] = round(total, 4)
     out["frames_per_s"] = round(out["out_frames"] / (total * 1e-3), 1)
+    if not args.no_fusion:  # dequantize + 1x1 inside the conv's loads
+        ws_fz = torch.empty(cvt.fsq_dequantize_conv3d_fact_workspace_bytes(idx.shape, 192, 192, True),
+                            dtype=torch.uint8, device=dev)
+        yf = torch.empty_like(yc)
+        unf, fus = interleaved(torch, [lambda: (stages["dequantize_proj"](), stages["conv_192_192"]()),
+                                       lambda: cvt.fsq_dequantize_conv3d_fact(idx, lift, w_s, w_t, workspace=ws_fz,
+                                                                              out=yf)],
+                               max(3, args.steps // 4))
+        out["fusion"] = {"dequantize_proj_then_conv_ms": round(unf, 4), "dequantize_proj_inside_conv_ms": round(fus, 4),
+                         "fused_over_unfused": round(fus / unf, 4),
+                         "frames_per_s_fused_route": round(out["out_frames"] /
+                                                           ((fus + out["haar_inv"]["ms"]) * 1e-3), 1)}
+        del ws_fz, yf
     del idx, z, yc, codes, xo, ws, ws1
     torch.cuda.empty_cache()
     return out

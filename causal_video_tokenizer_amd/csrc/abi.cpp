@@ -280,11 +280,10 @@ int cvt_causal_conv3d_temporal_stream(const void* x, const void* hist, const voi
     const int cp = w_p ? Cp : 0;
     if (w_p && (Cp < 1 || Cp > 16 || C > 256))
         return fail(CVT_E_SHAPE, "the fused projection needs C <= 256 and 1 <= Cp <= 16 (got C=%d, Cp=%d)", C, Cp);
-    // the kernel addresses x and the two history frames with 31-bit byte offsets
-    const long long P = std::max((long long)B * T * H * W, hist ? 2LL * B * H * W : 0LL);
-    if (C < 64 || C % 8 != 0 || !cvt::conv_temporal_stream_supported(C, cp, P))
-        return fail(CVT_E_SHAPE, "the stream convolution needs C >= 64, C %% 8 == 0 and an input below 2 GiB (C=%d)",
-                    C);
+    // a tile's frames (and the two history frames) are addressed with 31-bit byte offsets
+    if (C < 64 || C % 8 != 0 || !cvt::conv_temporal_stream_supported(C, cp, (long long)H * W))
+        return fail(CVT_E_SHAPE, "the stream convolution needs C >= 64, C %% 8 == 0 and 9 frames of the input below "
+                                 "2 GiB (C=%d)", C);
     if (!aligned16(x) || !aligned16(y) || (hist && !aligned16(hist)))
         return fail(CVT_E_ALIGN, "x, hist and y must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(w_t) & 1u) || (reinterpret_cast<uintptr_t>(w_p) & 1u))
@@ -443,9 +442,9 @@ int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B,
     if (!w->ln1_g || !w->ln1_b || !w->ln2_g || !w->ln2_b || !w->c1_s || !w->c1_t || !w->c2_s || !w->c2_t)
         return fail(CVT_E_NULL, "scales, shifts and conv weights must not be NULL");
     if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
-    const long long P = (long long)B * T * H * W;
-    if (C < 64 || C % 8 != 0 || !cvt::resblock_supported(C, P))
-        return fail(CVT_E_SHAPE, "the residual block needs C >= 64, C %% 8 == 0 and tensors below 2 GiB (C=%d)", C);
+    if (C < 64 || C % 8 != 0 || !cvt::resblock_supported(C, H, W))
+        return fail(CVT_E_SHAPE, "the residual block needs C >= 64, C %% 8 == 0 and 9 frames of a tensor below 2 GiB "
+                                 "(C=%d)", C);
     if (!(eps >= 0.0f)) return fail(CVT_E_SHAPE, "eps must be >= 0");
     if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
     for (const float* v : {w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b})
@@ -504,12 +503,12 @@ int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float*
     if (!x || !y || !w_s || !w_t) return fail(CVT_E_NULL, "x, y, w_s and w_t must not be NULL");
     if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
     const int f = up_space ? 2 : 1;
-    const long long Pin = (long long)B * T * H * W, Pmid = Pin * f * f;
     const long long Pout = (long long)B * (up_time ? 2 * T - 1 : T) * f * H * f * W;
-    if (Cin % 8 != 0 || Cout % 8 != 0 || Cout < 64 || !cvt::upsample_supported(Cin, Cout, Pin, Pmid) ||
+    if (Cin % 8 != 0 || Cout % 8 != 0 || Cout < 64 ||
+        !cvt::upsample_supported(Cin, Cout, W, (long long)f * H * f * W) ||
         (long long)f * H * f * W * Cout >= (1LL << 30) || Pout * Cout * 2 >= (1LL << 40))
-        return fail(CVT_E_SHAPE, "upsampling needs Cin, Cout multiples of 8, Cout >= 64 and tensors below 2 GiB "
-                                 "(Cin=%d, Cout=%d)", Cin, Cout);
+        return fail(CVT_E_SHAPE, "upsampling needs Cin, Cout multiples of 8, Cout >= 64 and 9 frames of the "
+                                 "upsampled tensor below 2 GiB (Cin=%d, Cout=%d)", Cin, Cout);
     if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
         return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");

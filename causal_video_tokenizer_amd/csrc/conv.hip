@@ -283,12 +283,13 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const uint16_t* __restr
 // below it, which re-read two of its rows - share an L2.
 struct RowsGeom {
     int B, T, H, W, HW, Cin, Cout;
-    int x_bytes, wf_bytes;  // buffer-resource extents (the launcher keeps both below 2^31)
+    long long x_total;      // bytes of the input tensor (any size: a tile's region is addressed from its own base)
+    int wf_bytes;           // packed weights' buffer-resource extent
     int NA, KC16;           // 32-row weight blocks, 16-channel k-steps
     int nct, ncol, nrow;    // channel tiles, column tiles, row tiles
     int ntiles, per_xcd;
     int Cp, wp_bytes;       // fused 1x1 projection: output channels, packed weight bytes (0 = none)
-    int h_bytes;            // temporal stream: extent of the two history frames [B][2][HW][Cin] (0 = none)
+    long long h_total;      // temporal stream: bytes of the two history frames [B][2][HW][Cin] (0 = none)
     int ups;                // input nearest-neighbour upsampled (spatial: x2 in H, W; temporal: causal x2)
     int Ti, Hi, Wi;         // with ups: the input grid
 };
@@ -321,7 +322,7 @@ template <int BK>
 constexpr int rows_xs() {
     return BK * 2 + 16;
 }
-constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (tensors stay below it)
+constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (a tile's span stays below it)
 
 // Tile configuration.  A workgroup has NW waves (4 or 8): WCH along output channels and
 // NW / WCH along columns.  Each wave owns FA 32-channel MFMA blocks x FB 32-column blocks
@@ -404,6 +405,24 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         row = (q / (8 * CPR)) * 8 + (q & 7);
         c16 = (q >> 3) % CPR;
     };
+    // The region is addressed from the tile's first input row (spatial: first image row of the
+    // frame; temporal: first frame at the tile's first column), p0 positions into the tensor:
+    // the buffer resource is based there, so the offsets below are tile-relative and the
+    // tensor may have any size (the launcher keeps a tile's span below ROWS_OOB_BASE bytes).
+    // Computed regions (SRC_HAAR, SRC_FSQ) address their smaller inputs from the start.
+    const int ymin = KIND == SPATIAL3 ? max(SR * r0 - 1, 0) : 0;
+    const int frmin = KIND == TEMPORAL3 ? max(SR * r0 - 2, 0) : 0;
+    long long p0 = 0;
+    if constexpr (C::SRC == SRC_TENSOR) {
+        if (KIND == SPATIAL3 && SR == 2)
+            p0 = ((long long)(b * g.T + t) * g.Hi + ymin) * g.Wi;
+        else if (KIND == SPATIAL3)
+            p0 = g.ups ? ((long long)(b * g.T + t) * g.Hi + (ymin >> 1)) * g.Wi : ((long long)(b * g.T + t) * g.H + ymin) * g.W;
+        else if (SR == 2)
+            p0 = ((long long)b * g.Ti + frmin) * g.HW + c0;
+        else
+            p0 = g.ups ? ((long long)b * g.Ti + ((frmin + 1) >> 1)) * g.HW + c0 : ((long long)b * g.T + frmin) * g.HW + c0;
+    }
     int xbase[XL];
     int hbase[HIST ? XL : 1];  // HIST (temporal stream, first row tile): offsets into the history frames
 #pragma unroll
@@ -413,38 +432,42 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         xmap(q, row, c16);
         const int rr = row / RC, cc = row % RC;
         bool ok = q < XQ && rr < NRU;
-        int pos = 0;
+        int rel = 0;  // input position relative to p0
         if (KIND == SPATIAL3 && SR == 2) {  // stride 2: rows 2 r0 - 1 + rr, de-interleaved columns
             constexpr int NC = C::NC;
             const int y = 2 * r0 - 1 + rr;
             const int x = cc <= NC ? 2 * c0 - 1 + 2 * cc : 2 * c0 + 2 * (cc - NC - 1);
             ok = ok && y >= 0 && y < g.Hi && x >= 0 && x < g.Wi;
-            pos = ((b * g.T + t) * g.Hi + y) * g.Wi + x;
+            rel = (y - ymin) * g.Wi + x;
         } else if (KIND == SPATIAL3) {
             const int y = r0 - 1 + rr, x = c0 - 1 + cc;
             ok = ok && y >= 0 && y < g.H && x >= 0 && x < g.W;
-            pos = g.ups ? ((b * g.T + t) * g.Hi + (y >> 1)) * g.Wi + (x >> 1) : ((b * g.T + t) * g.H + y) * g.W + x;
+            rel = g.ups ? ((y >> 1) - (ymin >> 1)) * g.Wi + (x >> 1) : (y - ymin) * g.W + x;
         } else if (SR == 2) {  // stride 2: input frames 2 r0 - 2 + rr
             const int fr = 2 * r0 - 2 + rr, hw = c0 + cc;
             ok = ok && fr >= 0 && fr < g.Ti && hw < g.HW;
-            pos = (b * g.Ti + fr) * g.HW + hw;
+            rel = (fr - frmin) * g.HW + cc;
         } else {
             const int fr = r0 - 2 + rr, hw = c0 + cc;
-            if constexpr (HIST) {  // frames -2 and -1 are the history frames 0 and 1
+            if constexpr (HIST) {  // frames -2 and -1 are the history frames 0 and 1 (based at the tile's column)
                 const bool hok = ok && fr < 0 && hw < g.HW;
-                hbase[i] = hok ? (((b * 2 + fr + 2) * g.HW + hw) * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
+                hbase[i] = hok ? (((fr + 2) * g.HW + cc) * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
             }
             ok = ok && fr >= 0 && fr < g.T && hw < g.HW;
             // upsampled in time: output frame fr of the causal repetition is input frame (fr + 1) / 2
-            pos = g.ups ? (b * g.Ti + ((fr + 1) >> 1)) * g.HW + hw : (b * g.T + fr) * g.HW + hw;
+            rel = g.ups ? (((fr + 1) >> 1) - ((frmin + 1) >> 1)) * g.HW + cc : (fr - frmin) * g.HW + cc;
         }
-        // rows outside the tensor get a base past its end for every chunk (the launcher keeps
-        // the tensor below ROWS_OOB_BASE bytes and chunk offsets below 64 KiB)
-        xbase[i] = ok ? (pos * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
+        // rows outside the tensor get a base past its end for every chunk (chunk offsets stay
+        // below 64 KiB)
+        xbase[i] = ok ? (rel * g.Cin + c16 * 8) * 2 : ROWS_OOB_BASE;
     }
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, g.x_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t hres =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(HIST ? Hx : X), (short)0, HIST ? g.h_bytes : 0, 0x00020000);
+    const long long xoff = p0 * g.Cin;  // elements
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(X + xoff), (short)0, (int)min(g.x_total - 2 * xoff, (long long)ROWS_OOB_BASE), 0x00020000);
+    const long long hoff64 = HIST ? ((long long)b * 2 * g.HW + c0) * g.Cin : 0;
+    const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(HIST ? Hx + hoff64 : X), (short)0, HIST ? (int)min(g.h_total - 2 * hoff64, (long long)ROWS_OOB_BASE) : 0,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)Wf, (short)0, g.wf_bytes, 0x00020000);
 
     // The region of chunk c + 1 goes to the buffer last read in chunk c - 1, free since that
@@ -1472,7 +1495,8 @@ using TemporalCfg = RowsCfg<TEMPORAL3, 4, 8, 1, CVT_ROWS_TM_BK, 8>;
 using TemporalNarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, CVT_ROWS_TM_BK, 4>;
 using TemporalProjCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK, 4>;
 
-// conv_rows_kernel over an NTHWC input: Cout % 8 == 0, input below ROWS_OOB_BASE bytes.
+// conv_rows_kernel over an NTHWC input: Cout % 8 == 0, a tile's input span below ROWS_OOB_BASE
+// bytes (use_rows_kernel).
 // With Wpf (temporal only, Cout <= 256, Cp <= 16) the epilogue applies the 1x1 projection
 // to Cp channels and Y is the [positions][Cp] projected output.
 template <typename C, bool TAIL, int EPI>
@@ -1517,9 +1541,9 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.Hi = in_grid ? cg.Hi : cg.H;
     g.Wi = in_grid ? cg.Wi : cg.W;
     if (C::S == 2 && cg.ups) return hipErrorInvalidValue;
-    g.x_bytes = (int)((long long)B * g.Ti * g.Hi * g.Wi * cg.Cin * 2);
-    if constexpr (C::SRC == SRC_HAAR) g.x_bytes = (int)((long long)B * 3 * aux.px_T * 16 * cg.H * cg.W * 2);
-    if constexpr (C::SRC == SRC_FSQ) g.x_bytes = (int)((long long)B * cg.T * cg.H * cg.W * 4);
+    g.x_total = (long long)B * g.Ti * g.Hi * g.Wi * cg.Cin * 2;
+    if constexpr (C::SRC == SRC_HAAR) g.x_total = (long long)B * 3 * aux.px_T * 16 * cg.H * cg.W * 2;
+    if constexpr (C::SRC == SRC_FSQ) g.x_total = (long long)B * cg.T * cg.H * cg.W * 4;
     if (cg.ups && Hx) return hipErrorInvalidValue;
     g.wf_bytes = (int)frag_bytes(cg.Cout, cg.Cin, KIND == SPATIAL3 ? 9 : 3);
     g.NA = (cg.Cout + 31) / 32;
@@ -1527,7 +1551,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.nct = (cg.Cout + C::TCH - 1) / C::TCH;
     g.Cp = Cp;
     g.wp_bytes = Wpf ? (int)frag_bytes(Cp, cg.Cout, 1) : 0;
-    g.h_bytes = Hx ? (int)((long long)B * 2 * g.HW * cg.Cin * 2) : 0;
+    g.h_total = Hx ? (long long)B * 2 * g.HW * cg.Cin * 2 : 0;
     long long ntiles;
     if (KIND == SPATIAL3) {
         g.ncol = (cg.W + C::NC - 1) / C::NC;
@@ -1649,8 +1673,14 @@ size_t pack_bytes(int Cout, int Cin, int ntaps) {
     return align256(std::max((size_t)Cout * Cin * ntaps * 2, frag_bytes(Cout, Cin, ntaps)));
 }
 
-bool use_rows_kernel(int k, int Cout, long long P, int Cin) {
-    return k == 3 && Cout >= 64 && Cout % 8 == 0 && P * Cin * 2 < ROWS_OOB_BASE;
+// conv_rows_kernel takes a k = 3 conv with Cout >= 64, Cout % 8 == 0 when a tile's region fits
+// its 31-bit buffer offsets: span = input positions between a tile's first and last staged
+// row (spatial: 10 image rows of the input; temporal: 9 frames of the input, the stride-2 tiles'
+// reach), whatever the tensor's total size.
+long long rows_span_spatial(int W_in) { return 10LL * W_in; }
+long long rows_span_temporal(long long HW_in) { return 9LL * HW_in; }
+bool use_rows_kernel(int k, int Cout, long long span, int Cin) {
+    return k == 3 && Cout >= 64 && Cout % 8 == 0 && span * Cin * 2 + 65536 < ROWS_OOB_BASE;
 }
 
 hipError_t pack_frag(const void* w, uint16_t* wf, int Cout, int Cin, int ntaps, hipStream_t s, int haar_k = 0) {
@@ -1713,7 +1743,7 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
             ConvGeom g{};
             g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cin; g.Cout = Cout;
             g.kchunks = (Cin + BK - 1) / BK;
-            if (use_rows_kernel(k, Cout, P, Cin)) {
+            if (use_rows_kernel(k, Cout, rows_span_spatial(W), Cin)) {
                 if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
                 if ((e = launch_rows<SPATIAL3>((const uint16_t*)x, wps, b_s, sout, g, B, s)) != hipSuccess) return e;
             } else {
@@ -1731,7 +1761,7 @@ hipError_t launch_conv_fact(const void* x, const void* w_s, const void* w_t, con
     ConvGeom g{};
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
     g.kchunks = (Cout + BK - 1) / BK;
-    if (use_rows_kernel(k, Cout, P, Cout)) {
+    if (use_rows_kernel(k, Cout, rows_span_temporal((long long)H * W), Cout)) {
         if ((e = pack_frag(w_t, wpt, Cout, Cout, 3, s)) != hipSuccess) return e;
         return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
     }
@@ -1810,15 +1840,15 @@ hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w
 namespace {
 // the fused projection applies when the temporal part runs on conv_rows_kernel with every
 // output channel in one workgroup
-bool proj_fused(int k, int Cout, int Cp, long long P, bool temporal) {
-    return temporal && use_rows_kernel(k, Cout, P, Cout) && Cout <= 256 && Cp <= 16;
+bool proj_fused(int k, int Cout, int Cp, long long HW, bool temporal) {
+    return temporal && use_rows_kernel(k, Cout, rows_span_temporal(HW), Cout) && Cout <= 256 && Cp <= 16;
 }
 }  // namespace
 
 size_t conv_proj_workspace_bytes(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, bool spatial,
                                  bool temporal) {
     const long long P = (long long)B * T * H * W;
-    if (proj_fused(k, Cout, Cp, P, temporal)) {
+    if (proj_fused(k, Cout, Cp, (long long)H * W, temporal)) {
         size_t b = pack_bytes(Cout, Cout, k) + align256(frag_bytes(Cp, Cout, 1));
         if (spatial) b += pack_bytes(Cout, Cin, k * k) + align256((size_t)P * Cout * 2);
         return b;
@@ -1840,7 +1870,7 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
     const long long P = (long long)B * T * H * W;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     hipError_t e;
-    if (idx && (!proj_fused(k, Cout, Cp, P, w_t != nullptr) || Cp > 8)) {
+    if (idx && (!proj_fused(k, Cout, Cp, (long long)H * W, w_t != nullptr) || Cp > 8)) {
         // the unfused route: the latent (into y, or the workspace's last buffer), then FSQ
         const size_t base = conv_proj_workspace_bytes(B, Cin, Cout, Cp, T, H, W, k, w_s != nullptr, w_t != nullptr);
         void* lat = y ? y : static_cast<void*>(ws + base);
@@ -1849,7 +1879,7 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
             return e;
         return launch_fsq_quantize(lat, CVT_BF16, CVT_NTHWC, idx, nullptr, *fsq, B, (long long)T * H * W, s);
     }
-    if (!proj_fused(k, Cout, Cp, P, w_t != nullptr)) {
+    if (!proj_fused(k, Cout, Cp, (long long)H * W, w_t != nullptr)) {
         // conv into the workspace, then the 1x1 projection
         size_t off = conv_workspace_bytes(B, Cin, Cout, T, H, W, k, w_s != nullptr, w_t != nullptr);
         uint16_t* ymid = reinterpret_cast<uint16_t*>(ws + off);
@@ -1891,8 +1921,8 @@ size_t conv_temporal_stream_workspace_bytes(int C, int Cp) {
     return pack_bytes(C, C, 3) + (Cp > 0 ? align256(frag_bytes(Cp, C, 1)) : 0);
 }
 
-bool conv_temporal_stream_supported(int C, int Cp, long long P) {
-    return use_rows_kernel(3, C, P, C) && (Cp == 0 || (C <= 256 && Cp <= 16));
+bool conv_temporal_stream_supported(int C, int Cp, long long HW) {
+    return use_rows_kernel(3, C, rows_span_temporal(HW), C) && (Cp == 0 || (C <= 256 && Cp <= 16));
 }
 
 hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
@@ -1922,7 +1952,9 @@ hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const vo
 //   A = swish(LN2(temporal1(S)))           (NORM epilogue; C > 256: plain conv + layernorm in place)
 //   S = spatial2(A)
 //   y = temporal2(S) + x                   (RES epilogue, one rounding)
-bool resblock_supported(int C, long long P) { return use_rows_kernel(3, C, P, C); }
+bool resblock_supported(int C, int H, int W) {
+    return use_rows_kernel(3, C, rows_span_spatial(W), C) && use_rows_kernel(3, C, rows_span_temporal((long long)H * W), C);
+}
 
 size_t resblock_workspace_bytes(int B, int C, int T, int H, int W) {
     const size_t P = (size_t)B * T * H * W;
@@ -2001,7 +2033,7 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
         g.P = (long long)B * T * H1 * W1; g.T = T; g.H = H1; g.W = W1; g.Cin = Cin; g.Cout = Cout;
         g.kchunks = (Cin + BK - 1) / BK;
         g.Ti = T; g.Hi = H; g.Wi = W; g.st = 1; g.ss = 2;
-        if (use_rows_kernel(3, Cout, (long long)B * T * H * W, Cin)) {
+        if (use_rows_kernel(3, Cout, rows_span_spatial(W), Cin)) {
             if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
             if ((e = launch_rows_s2<SPATIAL3>(tin, wps, b_s, S, g, B, s)) != hipSuccess) return e;
         } else {
@@ -2018,7 +2050,7 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
     g.P = (long long)B * T1 * H1 * W1; g.T = T1; g.H = H1; g.W = W1; g.Cin = C1; g.Cout = Cout;
     g.kchunks = (C1 + BK - 1) / BK;
     g.Ti = T; g.Hi = H1; g.Wi = W1; g.st = 2; g.ss = 1;
-    if (C1 == Cout && use_rows_kernel(3, Cout, (long long)B * T * H1 * W1, C1)) {
+    if (C1 == Cout && use_rows_kernel(3, Cout, rows_span_temporal((long long)H1 * W1), C1)) {
         if ((e = pack_frag(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
         return launch_rows_s2<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
     }
@@ -2032,8 +2064,9 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
 // index), so the repeated tensor is never written.  The spatial conv runs on the T input
 // frames (it is frame-local, so repeating frames before or after it is the same), the
 // temporal conv reads those frames through the causal repetition.
-bool upsample_supported(int Cin, int Cout, long long P_in, long long P_mid) {
-    return use_rows_kernel(3, Cout, P_in, Cin) && use_rows_kernel(3, Cout, P_mid, Cout);
+bool upsample_supported(int Cin, int Cout, int W_in, long long HW_mid) {
+    return use_rows_kernel(3, Cout, rows_span_spatial(W_in), Cin) &&
+           use_rows_kernel(3, Cout, rows_span_temporal(HW_mid), Cout);
 }
 
 size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space) {

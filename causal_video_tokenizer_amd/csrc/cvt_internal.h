@@ -152,7 +152,7 @@ hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w
 // Causal temporal convolution of one chunk of a stream (conv.hip): history frames in place
 // of the zero padding, optional fused 1x1 projection (C <= 256, Cp <= 16).
 size_t conv_temporal_stream_workspace_bytes(int C, int Cp);
-bool conv_temporal_stream_supported(int C, int Cp, long long P);
+bool conv_temporal_stream_supported(int C, int Cp, long long HW);
 hipError_t launch_conv_temporal_stream(const void* x, const void* hist, const void* w_t, const float* b_t,
                                        const void* w_p, const float* b_p, void* y, int B, int C, int Cp, int T,
                                        int H, int W, void* workspace, hipStream_t s);
@@ -175,14 +175,14 @@ hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta
                             float eps, int swish, hipStream_t s);
 
 // Encoder / decoder blocks (conv.hip).
-bool resblock_supported(int C, long long P);
+bool resblock_supported(int C, int H, int W);
 size_t resblock_workspace_bytes(int B, int C, int T, int H, int W);
 hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
                            float eps, void* workspace, hipStream_t s);
 size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time);
 hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
                              void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
-bool upsample_supported(int Cin, int Cout, long long P_in, long long P_mid);
+bool upsample_supported(int Cin, int Cout, int W_in, long long HW_mid);
 size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space);
 hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                            int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool up_time, void* workspace,

@@ -260,7 +260,8 @@ int cvt_causal_conv3d_fact_proj_fsq(const void* x, const void* w_s, const void* 
  *    (Cp = 0 without projection); owned by the caller.
  * Errors: CVT_E_NULL for a NULL x, w_t or y; CVT_E_SHAPE for a non-positive
  * size, C < 64, C not a multiple of 8, a projection outside the limits above or
- * an input of 2 GiB or more; CVT_E_ALIGN unless x, hist and y are 16-byte
+ * 9 frames of the input (9*H*W*C*2 bytes) of 2 GiB or more (the input itself
+ * may have any size); CVT_E_ALIGN unless x, hist and y are 16-byte
  * aligned; CVT_E_WORKSPACE when the workspace is too small.
  */
 size_t cvt_causal_conv3d_temporal_stream_workspace(int C, int Cp);
@@ -476,8 +477,9 @@ typedef struct cvt_resblock_weights {
  * residual element before the same wave overwrites it.
  * workspace: cvt_resblock3d_workspace(B, C, T, H, W) bytes, caller-owned.
  * Errors: CVT_E_NULL for a NULL tensor, weight or scale/shift; CVT_E_SHAPE for
- * a non-positive size, C < 64, C not a multiple of 8 or a tensor of 2 GiB or
- * more; CVT_E_ALIGN; CVT_E_WORKSPACE.
+ * a non-positive size, C < 64, C not a multiple of 8 or 9 frames of the
+ * tensor (9*H*W*C*2 bytes) of 2 GiB or more (the tensor itself may have any
+ * size); CVT_E_ALIGN; CVT_E_WORKSPACE.
  */
 size_t cvt_resblock3d_workspace(int B, int C, int T, int H, int W);
 int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W,
@@ -508,7 +510,8 @@ int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const floa
  * 1, 1], both required).  The repetition happens inside the conv's loads.
  * x: [B, Cin, T, H, W]; y: [B, Cout, T', 2H or H, 2W or W].
  * Errors: CVT_E_NULL; CVT_E_SHAPE for a non-positive size, Cin or Cout not a
- * multiple of 8, Cout < 64 or a tensor of 2 GiB or more; CVT_E_ALIGN;
+ * multiple of 8, Cout < 64 or 9 frames of the upsampled tensor of 2 GiB or
+ * more (the tensors themselves may have any size); CVT_E_ALIGN;
  * CVT_E_WORKSPACE.
  */
 size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time);

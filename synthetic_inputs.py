@@ -143,4 +143,11 @@ WORKLOADS = {
     # 17 frames padded to 1 + 4k frames and 1088 x 1920; pixels N(0, 0.5)
     "window_1080p_50f": dict(x=(1, 3, 50, 1080, 1920), seed=1020, std=0.5, window=17, t_align=4,
                              s_align=16),
+    # activations of 2 GiB or more: a 256-channel tensor on 40 frames of a 1080p clip's post-Haar
+    # grid (270 x 480), 2.65 GB in bf16; x ~ N(0, 1), conv weights N(0, 0.02)
+    "large_256x40x270x480": dict(x=(1, 256, 40, 270, 480), seed=1040, w_std=0.02),
+    # a 129-frame 1080p clip (the model card's longest one-pass 1080p input is 8 s): Haar ->
+    # conv 192 -> 256 (its output, 2.19 GB, is the temporal conv's input) -> temporal conv with
+    # the 1x1 -> 16 fused; G_trans pixels
+    "clip_1080p_129f": dict(x=(1, 3, 129, 1080, 1920), seed=1041),
 }
