@@ -29,7 +29,8 @@ seventh, the batched DV4x8x8-360p decode (8 clips: dequantize + 1x1, conv 192->1
 eighth, the 121-frame clip encoded as a stream of chunks against one whole-clip pass.  The 49- and
 121-frame clips and the decode also time the cross-stage fusions inside the conv's operand loads
 (Haar of the pixels in the first spatial conv; dequantize + 1x1 in the decoder's conv) against
-the unfused calls, interleaved in one process.
+the unfused calls, interleaved in one process; a ninth object runs a 129-frame 1080p clip through
+Haar and the conv chain, whose 2.19 GB activation exceeds 2 GiB.
 
 The default 25 warmup steps matter: with 3 the GPU clocks have not settled and every
 stage measures about 10% slower.
@@ -78,6 +79,7 @@ def parse():
     ap.add_argument("--no-c5", action="store_true", help="skip the batched 360p decode measurement")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-encode measurement")
     ap.add_argument("--no-fusion", action="store_true", help="skip the fused-versus-unfused measurements")
+    ap.add_argument("--no-1080p", action="store_true", help="skip the 129-frame 1080p chain (activations above 2 GiB)")
     ap.add_argument("--cpu-width", type=int, default=1280,
                     help="pixel width of the strip the CPU oracle is timed on")
     return ap.parse_args()
@@ -247,6 +249,7 @@ def main():
     blk = None if args.no_blocks else blocks_cv8x8x8(cvt, si, torch, dev, args)
     c5 = None if args.no_c5 else decode_c5(cvt, si, torch, dev, args)
     stream = None if args.no_stream else stream_encode(cvt, si, torch, dev, args)
+    long1080 = None if args.no_1080p else clip_1080p_chain(cvt, si, torch, dev, args)
 
     # Copy calibration for the HBM-traffic counters: one device copy of a known
     # number of bytes, outside the timed region (its FETCH_SIZE / WRITE_SIZE readings
@@ -289,6 +292,7 @@ def main():
         "blocks_cv8x8x8_720p": blk,
         "dv4x8x8_360p_decode_c5": c5,
         "stream_encode_121f_720p": stream,
+        "clip_1080p_129f": long1080,
         "copy_calibration_bytes": COPY_CAL_BYTES,
     }
     print(json.dumps(out), flush=True)
@@ -781,6 +785,53 @@ def stream_encode(cvt, si, torch, dev, args):
         ms = s.elapsed_time(e) / reps
         out[name] = {"ms": round(ms, 4), "frames_per_s": round(B * T / (ms * 1e-3), 1)}
     del x, xs, bufs, hz_w, s_w, lat_w, idx_w
+    torch.cuda.empty_cache()
+    return out
+
+
+def clip_1080p_chain(cvt, si, torch, dev, args):
+    """A 129-frame 1080p clip (1 x 3 x 129 x 1080 x 1920 bf16, G_trans pixels) through Haar ->
+    spatial conv 192 -> 256 -> causal temporal conv 256 -> 256 with the 1x1 -> 16 fused: the
+    spatial conv's 2.19 GB output is the temporal conv's input, so the row-tiled kernels run
+    beyond 2 GiB.  Per-stage times with HIP events, MFMA fraction of each conv, frames/s."""
+    wl = si.WORKLOADS["clip_1080p_129f"]
+    B, C, T, H, W = wl["x"]
+    Tq, Hq, Wq = 1 + (T - 1) // 4, H // 4, W // 4
+    P = B * Tq * Hq * Wq
+    log(f"1080p chain: generating {wl['x']} ...")
+    xb = si.to_bf16_bits(si.video_trans(wl["x"], wl["seed"]))
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
+    del xb
+
+    def bf(shape, seed):
+        bits = si.to_bf16_bits(si.normal(shape, seed, 0.02))
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ws, wt, wp = bf((256, 192, 1, 3, 3), wl["seed"] + 1), bf((256, 256, 3, 1, 1), wl["seed"] + 2), \
+        bf((16, 256, 1, 1, 1), wl["seed"] + 3)
+    cl = torch.channels_last_3d
+    hz = torch.empty((B, 192, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    s1 = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    lat = torch.empty((B, 16, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
+    w1 = torch.empty(cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)
+    w2 = torch.empty(cvt.conv_proj_workspace_bytes(s1.shape, 256, 16, 3, False, True), dtype=torch.uint8, device=dev)
+    stages = [("haar_fwd", lambda: cvt.haar3d_fwd(x, out=hz), None),
+              ("spatial_192_256", lambda: cvt.causal_conv3d_fact(hz, ws, None, workspace=w1, out=s1),
+               2.0 * 9 * 192 * 256 * P),
+              ("temporal_256_256_proj16", lambda: cvt.causal_conv3d_fact_proj(s1, None, wt, wp, workspace=w2, out=lat),
+               2.0 * 3 * 256 * 256 * P + 2.0 * 256 * 16 * P)]
+    times = interleaved(torch, [fn for _, fn, _ in stages], max(2, args.steps // 4), rounds=4)
+    out = {"clip": list(wl["x"]), "latent_grid": [Tq, Hq, Wq], "spatial_output_bytes": s1.numel() * 2, "stages": {}}
+    for (name, _, flops), ms in zip(stages, times):
+        d = {"ms": round(ms, 4)}
+        if flops:
+            d["TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            d["mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        else:
+            d["GBps"] = round((2.0 * B * C * T * H * W + 2.0 * P * 192) / (ms * 1e-3) / 1e9, 1)
+        out["stages"][name] = d
+    out["frames_per_s"] = round(B * T / (sum(times) * 1e-3), 1)
+    del x, hz, s1, lat, w1, w2
     torch.cuda.empty_cache()
     return out
 

@@ -615,8 +615,23 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         const bool bad = fidx < 0 || fidx >= fp.codebook;
         uint32_t rem = bad ? 0u : (uint32_t)fidx;
         float xv[FSQ_MAX_D];
+        // the default level set (8, 8, 8, 5, 5, 5): bit fields and exact multiply-shift divisions
+        // (q / 5 = (q * 205) >> 10 for q < 1024), the digits the general split gives
+        const bool def = fp.D == 6 && fp.levels[0] == 8 && fp.levels[1] == 8 && fp.levels[2] == 8 &&
+                         fp.levels[3] == 5 && fp.levels[4] == 5 && fp.levels[5] == 5;
+        if (def) {
+            const uint32_t q = rem >> 9, q5 = (q * 205u) >> 10, q25 = (q5 * 205u) >> 10;
+            const int d[6] = {(int)(rem & 7u), (int)((rem >> 3) & 7u), (int)((rem >> 6) & 7u), (int)(q - 5u * q5),
+                              (int)(q5 - 5u * q25), (int)q25};
+#pragma unroll
+            for (int i = 0; i < FSQ_MAX_D; ++i) {
+                const float code = i < 3 ? (float)(d[i] - 4) * 0.25f : (float)(d[i < 6 ? i : 5] - 2) * 0.5f;
+                xv[i] = i < 6 ? (bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code))) : 0.0f;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < FSQ_MAX_D; ++i) {
+            if (def) break;
             xv[i] = 0.0f;
             if (i < fp.D) {
                 const uint32_t q = div_magic(rem, fp.magic[i], fp.shift[i]);
@@ -1358,7 +1373,11 @@ __global__ __launch_bounds__(256) void pointwise_small_kernel(const uint16_t* __
 // bit-identical to the two kernels in a row while the D-channel codes never reach HBM.  An
 // index outside [0, codebook) gives NaN outputs and is counted once per position in
 // *invalid (one atomic per wave and step; the loop's trip count is uniform per wave).
-template <int CMAX>
+// DEF: the default level set (8, 8, 8, 5, 5, 5), whose digits are the three 3-bit fields of
+// idx mod 512 and the base-5 digits of q = idx / 512 < 125, split by q / 5 = (q * 205) >> 10
+// (exact for q < 1024): about 10 operations per index instead of six general divisions, the
+// same digits and codes.
+template <int CMAX, bool DEF = false>
 __global__ __launch_bounds__(256) void fsq_dequant_proj_kernel(const int32_t* __restrict__ idx, FsqParams p,
                                                                const uint16_t* __restrict__ w,
                                                                const float* __restrict__ bias,
@@ -1394,8 +1413,19 @@ __global__ __launch_bounds__(256) void fsq_dequant_proj_kernel(const int32_t* __
         if (!live) continue;
         uint32_t rem = bad ? 0u : (uint32_t)id;
         float xv[16];
+        if constexpr (DEF) {
+            const uint32_t q = rem >> 9, q5 = (q * 205u) >> 10, q25 = (q5 * 205u) >> 10;
+            const int d[6] = {(int)(rem & 7u), (int)((rem >> 3) & 7u), (int)((rem >> 6) & 7u), (int)(q - 5u * q5),
+                              (int)(q5 - 5u * q25), (int)q25};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float code = i < 3 ? (float)(d[i] - 4) * 0.25f : (float)(d[i < 6 ? i : 5] - 2) * 0.5f;
+                xv[i] = i < 6 ? (bad ? __builtin_nanf("") : bf16_to_f32(f32_to_bf16(code))) : 0.0f;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+            if (DEF) break;
             xv[i] = 0.0f;
             if (i < FSQ_MAX_D && i < p.D) {
                 const uint32_t q = div_magic(rem, p.magic[i], p.shift[i]);
@@ -2101,7 +2131,12 @@ hipError_t launch_fsq_dequant_proj(const int32_t* idx, const FsqParams& p, const
                                    long long P, int Cout, int32_t* invalid, hipStream_t s) {
     const int ng = (Cout + 7) / 8;
     const dim3 grid((unsigned)small_proj_blocks(P * ng, ng));
-    if (small_proj_staged(p.D, Cout))  // D <= 8
+    const bool def = p.D == 6 && p.levels[0] == 8 && p.levels[1] == 8 && p.levels[2] == 8 && p.levels[3] == 5 &&
+                     p.levels[4] == 5 && p.levels[5] == 5;
+    if (def && small_proj_staged(p.D, Cout))
+        hipLaunchKernelGGL((fsq_dequant_proj_kernel<8, true>), grid, dim3(256), small_proj_lds(p.D, Cout), s, idx, p,
+                           static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
+    else if (small_proj_staged(p.D, Cout))  // D <= 8
         hipLaunchKernelGGL(fsq_dequant_proj_kernel<8>, grid, dim3(256), small_proj_lds(p.D, Cout), s, idx, p,
                            static_cast<const uint16_t*>(w_p), b_p, static_cast<uint16_t*>(y), P, Cout, invalid);
     else
