@@ -324,7 +324,7 @@ constexpr int rows_xs() {
 }
 constexpr int ROWS_OOB_BASE = 0x7fff0000;  // buffer offset base of padding rows (a tile's span stays below it)
 
-// Tile configuration.  A workgroup has NW waves (4 or 8): WCH along output channels and
+// Tile configuration.  A workgroup has NW waves (3, 4 or 8): WCH along output channels and
 // NW / WCH along columns.  Each wave owns FA 32-channel MFMA blocks x FB 32-column blocks
 // (FA * FB = 2, so 128 fp32 accumulators for R = 4 rows) over all R output rows.
 #ifndef CVT_ROWS_SP_PD
@@ -370,7 +370,7 @@ struct RowsCfg {
     static constexpr int PRS = TCH * 2 + 16;                              // fused projection: bytes per staged column
     static constexpr int PROJ_BYTES = R * NC * PRS;                       // R frames of staged columns
     static constexpr int RES_BYTES = NW * 32 * FB * (128 * FA + 16);       // residual epilogue: float32 row stages
-    static_assert((NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
+    static_assert((NW == 3 || NW == 4 || NW == 8) && WCH * WPOS == NW && FA * FB == 2 && (BK == 32 || BK == 64) && R >= 1 &&
                       R <= 4 && (S == 1 || S == 2),
                   "tile shape");
     static_assert(SRC == SRC_TENSOR || (KIND == SPATIAL3 && S == 1 && BK == 32 && RROWS * RC <= NTH && XROWS == NTH),
@@ -1524,6 +1524,13 @@ using SpatialFsqCfg = RowsCfg<SPATIAL3, 4, 4, 2, 32, 4, 1, SRC_FSQ>;
 using TemporalCfg = RowsCfg<TEMPORAL3, 4, 8, 1, CVT_ROWS_TM_BK, 8>;
 using TemporalNarrowCfg = RowsCfg<TEMPORAL3, 4, 4, 1, CVT_ROWS_TM_BK, 4>;
 using TemporalProjCfg = RowsCfg<TEMPORAL3, 4, 4, 2, CVT_ROWS_TM_BK, 4>;
+// 129..192 output channels without padding them to 256: 3 waves of 64 channels x 32 columns
+// (two 3-wave workgroups per CU, 6 of the 8 wave slots; on 192 -> 192 at 8 x 13 x 90 x 160
+// the spatial conv runs 12% and the temporal conv 8% faster than on the padded 4-wave
+// tiles).  The computed-region variant holds 3 rows (5 x 34 region rows for 192 threads).
+using SpatialTriCfg = RowsCfg<SPATIAL3, 4, 3, 2, 32, 3>;
+using SpatialFsqTriCfg = RowsCfg<SPATIAL3, 3, 3, 2, 32, 3, 1, SRC_FSQ>;
+using TemporalTriCfg = RowsCfg<TEMPORAL3, 4, 3, 2, CVT_ROWS_TM_BK, 3>;
 
 // conv_rows_kernel over an NTHWC input: Cout % 8 == 0, a tile's input span below ROWS_OOB_BASE
 // bytes (use_rows_kernel).
@@ -1596,7 +1603,7 @@ hipError_t launch_rows_cfg(const uint16_t* X, const uint16_t* Wf, const float* b
     g.ntiles = (int)ntiles;
     g.per_xcd = (int)((ntiles + 7) / 8);
     const bool tail = cg.Cin % BK != 0;
-    if constexpr (KIND == TEMPORAL3 && C::NW == 4 && C::S == 1) {  // the 4-wave temporal tiles: projection, norm
+    if constexpr (KIND == TEMPORAL3 && (C::NW == 4 || C::NW == 3) && C::S == 1) {  // 3- and 4-wave temporal tiles: projection, norm
         if (Wpf) {
             if (g.nct != 1 || Cp < 1 || Cp > 16 || aux.ln_g || aux.res) return hipErrorInvalidValue;
             if (aux.fsq_idx) {
@@ -1628,6 +1635,8 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
         auto padded = [&](int tch, int nc) {
             return (long long)((cg.Cout + tch - 1) / tch) * tch * (long long)(((cg.W + nc - 1) / nc) * nc);
         };
+        if (cg.Cout > 128 && cg.Cout <= SpatialTriCfg::TCH)
+            return launch_rows_cfg<SpatialTriCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr, aux);
         if (padded(SpatialCfg::TCH, SpatialCfg::NC) < padded(SpatialWideCfg::TCH, SpatialWideCfg::NC))
             return launch_rows_cfg<SpatialCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr, aux);
         return launch_rows_cfg<SpatialWideCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, nullptr, aux);
@@ -1638,19 +1647,23 @@ hipError_t launch_rows(const uint16_t* X, const uint16_t* Wf, const float* bias,
     // one's epilogue (projection, norm, residual or plain stores) overlaps the other's MFMAs, with
     // the weight fragments requested right after their last use (also 2.5-10% faster than the
     // 8-wave tiles for the plain conv)
+    if (cg.Cout <= TemporalTriCfg::TCH)
+        return launch_rows_cfg<TemporalTriCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
     if (cg.Cout <= TemporalProjCfg::TCH)
         return launch_rows_cfg<TemporalProjCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
     return launch_rows_cfg<TemporalCfg>(X, Wf, bias, Y, cg, B, s, Wpf, bias_p, Cp, Hx, aux);
 }
 
 // The stride-2 (downsampling) convolutions on conv_rows_kernel: cg holds the output grid
-// and, in Ti, Hi, Wi, the input grid.  Spatial tiles of 256 channels x 32 columns x 2 output
-// rows (5 input rows of 65 de-interleaved columns, each region staged once for 256 output
-// channels: 1.46x faster than 128 x 64 tiles on 256 -> 256), or 128 x 64 x 1 up to 128
-// channels (3 input rows of 129 columns, two workgroups per CU); temporal tiles as at stride 1 with 9 input frames per 4 output frames (5 per 2
-// on the 8-wave tiles above 256 channels).
+// and, in Ti, Hi, Wi, the input grid.  Spatial tiles of 256 channels x 32 columns x 3 output
+// rows (7 input rows of 65 de-interleaved columns, each region staged once for 256 output
+// channels; the two 80 KB region buffers still let two workgroups share a CU, and a weight
+// fragment feeds 3 MFMAs: 14% faster than 2 output rows, 1.46x faster than 128 x 64 tiles on
+// 256 -> 256), or 128 x 64 x 1 up to 128 channels (3 input rows of 129 columns, two
+// workgroups per CU); temporal tiles as at stride 1 with 9 input frames per 4 output frames
+// (5 per 2 on the 8-wave tiles above 256 channels).
 using SpatialS2NarrowCfg = RowsCfg<SPATIAL3, 1, 4, 1, 32, 4, 2>;
-using SpatialS2Cfg = RowsCfg<SPATIAL3, 2, 4, 2, 32, 4, 2>;
+using SpatialS2Cfg = RowsCfg<SPATIAL3, 3, 4, 2, 32, 4, 2>;
 using TemporalS2NarrowCfg = RowsCfg<TEMPORAL3, 3, 4, 1, 32, 4, 2>;  // 7 staged frames x 64 columns: 72 KB
 using TemporalS2Cfg = RowsCfg<TEMPORAL3, 4, 4, 2, 32, 4, 2>;
 using TemporalS2WideCfg = RowsCfg<TEMPORAL3, 2, 8, 1, 32, 8, 2>;  // 2 output frames: 5 staged rows fit the registers
@@ -1860,9 +1873,12 @@ hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w
     aux.fsq = p;
     aux.lift_w = static_cast<const uint16_t*>(w_lift);
     aux.lift_b = b_lift;
-    if ((e = launch_rows_cfg<SpatialFsqCfg>(reinterpret_cast<const uint16_t*>(idx), wps, b_s, S, g, B, s, nullptr,
-                                            nullptr, 0, nullptr, aux)) != hipSuccess)
-        return e;
+    e = Cout > 128 && Cout <= SpatialFsqTriCfg::TCH
+            ? launch_rows_cfg<SpatialFsqTriCfg>(reinterpret_cast<const uint16_t*>(idx), wps, b_s, S, g, B, s, nullptr,
+                                                nullptr, 0, nullptr, aux)
+            : launch_rows_cfg<SpatialFsqCfg>(reinterpret_cast<const uint16_t*>(idx), wps, b_s, S, g, B, s, nullptr,
+                                             nullptr, 0, nullptr, aux);
+    if (e != hipSuccess) return e;
     if (!w_t) return hipSuccess;
     return launch_conv_fact(S, nullptr, w_t, nullptr, b_t, y, B, Cout, Cout, T, H, W, 3, tws, s);
 }

@@ -67,10 +67,12 @@ def block_params_dev(C, seed, bias):
 
 
 RES_CASES = [
-    # B, C, T, H, W, bias: 64 and 128 channels on the 4-wave 128-channel tiles, 192 and 256 on
-    # the 256-channel tiles (192: staged zeros past Cout), 320 on the plain conv + layernorm path
+    # B, C, T, H, W, bias: 64 and 128 channels on the 4-wave 128-channel tiles, 136 and 192 on
+    # the 3-wave 192-channel tiles (136: staged zeros past Cout), 256 on the 256-channel tiles,
+    # 320 on the plain conv + layernorm path
     (1, 64, 5, 7, 9, False),
     (2, 128, 3, 6, 10, True),
+    (1, 136, 3, 6, 7, True),
     (1, 192, 4, 5, 8, False),
     (1, 256, 6, 9, 13, True),
     (1, 320, 2, 4, 6, False),
@@ -127,7 +129,8 @@ DOWN_CASES = [
     (1, 64, 128, 5, 8, 12, True, True, True),
     (2, 192, 256, 2, 10, 6, True, False, False),
     (1, 64, 64, 7, 6, 10, False, True, True),
-    (1, 256, 256, 9, 18, 32, True, True, False),     # 16 x 16 output positions per frame, ragged tiles
+    (1, 256, 256, 9, 18, 32, True, True, False),     # 9 x 16 output positions per frame: 3 row tiles of 3
+    (1, 200, 256, 3, 14, 20, True, True, True),      # K chunk tail on the 3-row tiles, 7 output rows (3 + 3 + 1)
     (2, 64, 64, 3, 10, 150, True, True, True),       # 75 output columns: two column tiles, ragged
     (1, 72, 128, 5, 6, 8, True, False, False),       # input channels not a multiple of the K chunk
     (1, 320, 320, 5, 4, 4, False, True, False),      # temporal above 256 channels (8-wave tiles)

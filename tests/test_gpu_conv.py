@@ -41,7 +41,9 @@ CASES = [
     (1, 48, 64, 1, 16, 16, 3, True, False),      # single image grid (T = 1: last temporal tap only)
     (2, 64, 256, 5, 12, 20, 3, True, False),     # 2400 positions: 19 position tiles, ragged tail
     (1, 256, 256, 3, 9, 13, 3, True, True),      # 256 -> 256 with biases
-    (1, 192, 192, 4, 10, 10, 3, True, False),    # 192 output channels
+    (1, 192, 192, 4, 10, 10, 3, True, False),    # 192 output channels (3-wave 192-channel tiles)
+    (1, 40, 160, 3, 7, 9, 3, True, True),        # Cin tail on the 3-wave tiles, Cout 160 of 192
+    (2, 192, 176, 5, 6, 37, 3, True, False),     # Cout 176 of 192, ragged column and frame tiles, 2 clips
     (1, 136, 40, 3, 7, 9, 3, True, False),       # Cin tail inside a 64-channel step, Cout tail
     (1, 8, 8, 3, 5, 5, 3, True, False),
     (1, 256, 16, 3, 8, 8, 1, False, False),      # 1x1 projection to the 16-dim latent
@@ -210,7 +212,8 @@ PROJ_CASES = [
     # B, Cin, Cout, Cp, T, H, W, spatial, bias
     (1, 192, 256, 6, 5, 12, 20, True, True),    # the 49-frame chain's shape family: conv -> 1x1 to the FSQ latent
     (1, 256, 256, 16, 7, 9, 13, False, True),   # temporal-only, 16-dim continuous latent, frame tiles of 4 and 3
-    (2, 96, 192, 6, 6, 5, 70, True, False),     # Cout 192 in a 256-channel workgroup, ragged columns, 2 clips
+    (2, 96, 192, 6, 6, 5, 70, True, False),     # Cout 192 on the 3-wave 192-channel tiles, ragged columns, 2 clips
+    (1, 64, 144, 16, 5, 7, 9, True, True),      # Cout 144 of 192 (staged zeros past Cout), Cp 16
     (1, 64, 64, 3, 2, 8, 8, True, True),        # narrow channels, 2 frames
     (1, 64, 128, 24, 3, 6, 6, True, True),      # Cp > 16: conv then a separate 1x1 pass
 ]

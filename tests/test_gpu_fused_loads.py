@@ -103,7 +103,8 @@ def test_haar_conv_fused_dv8x16x16_720p_frames():
 FSQ_CASES = [
     # B, T, H, W, Cmid, Cout, temporal, bias, levels
     (1, 3, 9, 13, 64, 64, False, False, LEVELS),
-    (2, 5, 12, 40, 192, 192, True, True, LEVELS),
+    (2, 5, 12, 40, 192, 192, True, True, LEVELS),   # 3-wave tiles of 3 rows (4 row tiles)
+    (1, 3, 10, 35, 160, 136, True, False, LEVELS),  # Cout 136 of 192, ragged row and column tiles
     (1, 4, 7, 70, 256, 256, True, False, LEVELS),
     (1, 2, 8, 8, 96, 128, True, True, (8, 5, 5, 5)),
     (1, 1, 10, 33, 192, 64, False, True, (7, 5, 5, 5, 3)),
