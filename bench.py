@@ -57,10 +57,10 @@ COPY_CAL_BYTES = 256 * 1024 * 1024
 # 1x3x3 192->256 on the 13 x 180 x 320 latent grid), from two rocprofv3 --pmc passes over
 # this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
 # what it reads for the 256 MiB device copy this script issues after timing: FETCH_SIZE
-# reads 131105.9 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
+# reads 131092.4 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
 # for the kernel version the counters were taken on: set to None when it changes.
-SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 226397.7, 374400.0
-COPY_FETCH_KIB, COPY_WRITE_KIB = 131105.9, 262144.0
+SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 229616.4, 374400.0
+COPY_FETCH_KIB, COPY_WRITE_KIB = 131092.4, 262144.0
 
 
 def parse():
@@ -660,17 +660,12 @@ def decode_c5(cvt, si, torch, dev, args):
         unfused()
     torch.cuda.synchronize()
     reps = max(5, args.steps // 2)
-    out = {"indices": list(wl["indices"]), "out_frames": B * wl["out_x"][2]}
+    out = {"indices": list(wl["indices"]), "out_frames": B * wl["out_x"][2],
+           "timing": "median of 6 rounds alternating the stage order, after 0.5 s of warm-up calls"}
     total = 0.0
-    for name, fn in list(stages.items()) + [("dequantize_then_proj_unfused", unfused)]:
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
+    named = list(stages.items()) + [("dequantize_then_proj_unfused", unfused)]
+    times = interleaved(torch, [fn for _, fn in named], reps)
+    for (name, fn), ms in zip(named, times):
         d = {"ms": round(ms, 4)}
         if name == "conv_192_192":
             flops = (2.0 * 9 * 192 * 192 + 2.0 * 3 * 192 * 192) * P
