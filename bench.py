@@ -12,10 +12,12 @@ behind the C ABI:
   dequantize;  inverse Haar of the coefficients back to pixels.
 
 Inputs are resident in HBM before timing.  `value` is frames per second of the
-whole step (49 frames per step).  The roofline object reports the dominant
-kernel, the spatial convolution's MFMA implicit GEMM: algorithmic FLOPs
+whole step (49 frames per step), timed over K steps that carry only one pair of
+HIP events, around the dominant kernel; K further steps with an event between
+every stage give the per-stage breakdown.  The roofline object reports the
+dominant kernel, the spatial convolution's MFMA implicit GEMM: algorithmic FLOPs
 2*9*Cin*Cout per output position, divided by its average duration measured
-with HIP events on the launch stream over the timed steps.  The CPU baseline is
+with those HIP events on the launch stream over the timed steps.  The CPU baseline is
 the float64 oracle timed on a bounded sample of the same workload (a strip of
 the frame), scaled to the full clip.  A second object reports the 121-frame
 CV8x8x8-720p-shaped chain (two factorized conv layers and the 1x1), where the
@@ -159,17 +161,18 @@ def main():
     codes = torch.empty((B, 6, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
     xr = torch.empty_like(x)
     ws_sp = torch.empty(cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)
-    ws_tp = torch.empty(cvt.conv_proj_workspace_bytes(s1.shape, 256, 6, 3, False, True), dtype=torch.uint8,
-                        device=dev)
 
     # (FSQ can also run inside the projection epilogue, causal_conv3d_fact_proj_fsq; on this
     # workload that is 4% slower than the FSQ kernel after the conv, so the step keeps two calls)
     stages = ["haar_fwd", "conv_spatial", "conv_temporal_proj", "fsq_quantize", "fsq_quantize_sep",
               "fsq_dequantize", "haar_inv"]
+    # the weights are fixed across steps: packed once here, outside the timed region, in the
+    # order the conv kernels read them (the per-call repack costs about 4.5 us per weight tensor)
+    pw_s, pw_t, pw_p = cvt.conv_weights_pack(w_s), cvt.conv_weights_pack(w_t), cvt.conv_weights_pack(w_p)
     calls = {
         "haar_fwd": lambda: cvt.haar3d_fwd(x, out=hz),
-        "conv_spatial": lambda: cvt.causal_conv3d_fact(hz, w_s, None, workspace=ws_sp, out=s1),
-        "conv_temporal_proj": lambda: cvt.causal_conv3d_fact_proj(s1, None, w_t, w_p, workspace=ws_tp, out=lat),
+        "conv_spatial": lambda: cvt.causal_conv3d_fact_packed(hz, pw_s, None, out=s1),
+        "conv_temporal_proj": lambda: cvt.causal_conv3d_fact_proj_packed(s1, None, pw_t, pw_p, out=lat),
         "fsq_quantize": lambda: cvt.fsq_quantize(lat, indices=idx),
         "fsq_quantize_sep": lambda: cvt.fsq_quantize(z_sep, indices=idx2),
         "fsq_dequantize": lambda: cvt.fsq_dequantize(idx2, out=codes),
@@ -177,11 +180,17 @@ def main():
     }
     stream = torch.cuda.current_stream(dev)
 
-    def step(evs=None):
+    def step(evs=None, dom_evs=None):
+        # evs: an event before every stage and after the last (the per-stage breakdown);
+        # dom_evs: a pair of events around the dominant kernel's call only (the roofline)
         for i, name in enumerate(stages):
             if evs is not None:
                 evs[i].record(stream)
+            if dom_evs is not None and name == "conv_spatial":
+                dom_evs[0].record(stream)
             calls[name]()
+            if dom_evs is not None and name == "conv_spatial":
+                dom_evs[1].record(stream)
         if evs is not None:
             evs[len(stages)].record(stream)
 
@@ -190,13 +199,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    # the timed region: K steps with one pair of events around the dominant kernel (an event
+    # between every stage costs about 4 us each, 3% of the step)
+    dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(ev[k])
+        step(dom_evs=dev_ev[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = float(np.mean([dev_ev[k][0].elapsed_time(dev_ev[k][1]) for k in range(args.steps)]))
+    # then K more steps with an event between every stage, for the per-stage breakdown
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
                 for i, name in enumerate(stages)}
 
@@ -222,20 +239,23 @@ def main():
         per_stage[name] = d
 
     dom = "conv_spatial"
-    achieved = conv_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    achieved = conv_flops[dom] / (dom_ms * 1e-3) / 1e12  # HIP events inside the timed region
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(),
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": 2.0 * P * (192 + 256) + 2.0 * 256 * 192 * 9,
                 "kernel": "conv_rows_kernel<RowsCfg<SPATIAL3,R=4,WCH=4,FA=2,BK=32,NW=4>,false,false> (1x3x3 conv 192->256, bf16 MFMA)",
-                "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+                "flops_per_launch": conv_flops[dom], "avg_launch_ms": round(dom_ms, 4),
+                "timing": "HIP events on the launch stream around each timed step's call (weights packed once, before timing)"}
 
     fusion = None
     if not args.no_fusion:
         # the Haar patcher inside the spatial conv's loads, against the two calls of the step
         hz_conv = torch.empty_like(s1)
         ws_fz = torch.empty(cvt.haar3d_conv3d_fact_workspace_bytes(x.shape, 256, False), dtype=torch.uint8, device=dev)
-        unf, fus = interleaved(torch, [lambda: (calls["haar_fwd"](), calls["conv_spatial"]()),
+        # both routes repack their weights per call (there is no packed form of the fused call)
+        unf, fus = interleaved(torch, [lambda: (calls["haar_fwd"](),
+                                                cvt.causal_conv3d_fact(hz, w_s, None, workspace=ws_sp, out=s1)),
                                        lambda: cvt.haar3d_conv3d_fact(x, w_s, workspace=ws_fz, out=hz_conv)],
                                max(5, args.steps // 2))
         fusion = {"haar_then_spatial_conv_ms": round(unf, 4), "haar_inside_spatial_conv_ms": round(fus, 4),
@@ -284,6 +304,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": per_stage,
+        "stages_timing": "K further steps with an event between every stage (not part of value)",
         "fusion_haar_conv_49f": fusion,
         "cv8x8x8_720p_121f": c3,
         "fsq_bandwidth_size": fsq_bw,
@@ -330,17 +351,14 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
     a = torch.empty((B, 256, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
     b = torch.empty_like(a)
     lat = torch.empty((B, 16, Tq, Hq, Wq), dtype=torch.bfloat16, device=dev, memory_format=cl)
-    ws = {k: torch.empty(n, dtype=torch.uint8, device=dev) for k, n in [
-        ("s1", cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False)),
-        ("t", cvt.conv_workspace_bytes(a.shape, 256, 3, False, True)),
-        ("s2", cvt.conv_workspace_bytes(a.shape, 256, 3, True, False)),
-        ("tp", cvt.conv_proj_workspace_bytes(a.shape, 256, 16, 3, False, True))]}
+    ws = {"s1": torch.empty(cvt.conv_workspace_bytes(hz.shape, 256, 3, True, False), dtype=torch.uint8, device=dev)}
+    pw = [cvt.conv_weights_pack(wi) for wi in w]  # fixed weights: packed once, outside the timed region
     stages = [
         ("haar_fwd", lambda: cvt.haar3d_fwd(x, out=hz), None),
-        ("l1_spatial", lambda: cvt.causal_conv3d_fact(hz, w[0], None, workspace=ws["s1"], out=a), 2.0 * 9 * 192 * 256 * P),
-        ("l1_temporal", lambda: cvt.causal_conv3d_fact(a, None, w[1], workspace=ws["t"], out=b), 2.0 * 3 * 256 * 256 * P),
-        ("l2_spatial", lambda: cvt.causal_conv3d_fact(b, w[2], None, workspace=ws["s2"], out=a), 2.0 * 9 * 256 * 256 * P),
-        ("l2_temporal_proj", lambda: cvt.causal_conv3d_fact_proj(a, None, w[3], w[4], workspace=ws["tp"], out=lat),
+        ("l1_spatial", lambda: cvt.causal_conv3d_fact_packed(hz, pw[0], None, out=a), 2.0 * 9 * 192 * 256 * P),
+        ("l1_temporal", lambda: cvt.causal_conv3d_fact_packed(a, None, pw[1], out=b), 2.0 * 3 * 256 * 256 * P),
+        ("l2_spatial", lambda: cvt.causal_conv3d_fact_packed(b, pw[2], None, out=a), 2.0 * 9 * 256 * 256 * P),
+        ("l2_temporal_proj", lambda: cvt.causal_conv3d_fact_proj_packed(a, None, pw[3], pw[4], out=lat),
          2.0 * 3 * 256 * 256 * P + 2.0 * 256 * 16 * P),
     ]
     stream = torch.cuda.current_stream(dev)
@@ -377,7 +395,9 @@ def cv8x8x8_chain(cvt, si, torch, dev, args):
     if not args.no_fusion:  # the Haar patcher inside layer 1's spatial conv
         ws_fz = torch.empty(cvt.haar3d_conv3d_fact_workspace_bytes(x.shape, 256, False), dtype=torch.uint8, device=dev)
         a2 = torch.empty_like(a)
-        unf, fus = interleaved(torch, [lambda: (stages[0][1](), stages[1][1]()),
+        # both routes repack their weights per call (there is no packed form of the fused call)
+        unf, fus = interleaved(torch, [lambda: (stages[0][1](),
+                                                cvt.causal_conv3d_fact(hz, w[0], None, workspace=ws["s1"], out=a)),
                                        lambda: cvt.haar3d_conv3d_fact(x, w[0], workspace=ws_fz, out=a2)],
                                max(3, args.steps // 4))
         rest = total - out["stages"]["haar_fwd"]["ms"] - out["stages"]["l1_spatial"]["ms"]

@@ -15,7 +15,8 @@ Tensor conventions
 
 Entry points (same names as the C functions without the ``cvt_`` prefix):
 ``haar3d_fwd``, ``haar3d_inv``, ``causal_conv3d_fact``,
-``causal_conv3d_fact_noalloc``, ``causal_conv3d_fact_proj``, ``causal_conv3d_temporal_stream``, ``attention3d``,
+``causal_conv3d_fact_noalloc``, ``causal_conv3d_fact_proj``, ``conv_weights_pack``,
+``causal_conv3d_fact_packed``, ``causal_conv3d_fact_proj_packed``, ``causal_conv3d_temporal_stream``, ``attention3d``,
 ``fsq_quantize``, ``fsq_dequantize``, ``video_window``, ``video_pad``,
 ``video_unpad``, ``layernorm3d``, ``resblock3d``, ``downsample3d``, ``upsample3d``.  ``lib`` is the loaded ctypes library with the raw C
 functions.
@@ -45,6 +46,12 @@ SIGNATURES = {
     "cvt_causal_conv3d_fact_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp]),
     "cvt_causal_conv3d_fact_noalloc": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp]),
+    "cvt_conv_weights_packed_bytes": (_sz, [_ci, _ci, _ci]),
+    "cvt_conv_weights_pack": (_ci, [_vp, _vp, _ci, _ci, _ci, _vp]),
+    "cvt_causal_conv3d_fact_packed_workspace": (_sz, [_ci] * 6),
+    "cvt_causal_conv3d_fact_packed": (_ci, [_vp] * 6 + [_ci] * 6 + [_vp, _sz, _vp]),
+    "cvt_causal_conv3d_fact_proj_packed_workspace": (_sz, [_ci] * 6),
+    "cvt_causal_conv3d_fact_proj_packed": (_ci, [_vp] * 8 + [_ci] * 7 + [_vp, _sz, _vp]),
     "cvt_causal_conv3d_fact_proj_workspace": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]),
     "cvt_causal_conv3d_fact_proj": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                           _ci, _vp, _sz, _vp]),
@@ -297,6 +304,114 @@ def causal_conv3d_fact_noalloc(x, w_s, w_t=None, b_s=None, b_t=None, out=None):
     _check(lib.cvt_causal_conv3d_fact_noalloc(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y),
                                               B, Cin, Cout, T, H, W, k, _stream(x.device)),
            "causal_conv3d_fact_noalloc")
+    return y
+
+
+class PackedWeights:
+    """Conv weights in the order the row-tiled kernels read them (conv_weights_pack):
+    ``data`` is a uint8 device tensor; Cout, Cin and taps (9 spatial 1x3x3, 3 temporal
+    3x1x1, 1 projection) record the tensor it was packed from."""
+
+    def __init__(self, data, Cout, Cin, taps):
+        self.data, self.Cout, self.Cin, self.taps = data, Cout, Cin, taps
+
+
+def conv_weights_pack(w):
+    """Pack bf16 conv weights [Cout, Cin, kt, kh, kw] (torch order; 1x3x3, 3x1x1 or 1x1x1)
+    once, for repeated packed calls (causal_conv3d_fact_packed and
+    causal_conv3d_fact_proj_packed) on fixed weights."""
+    _require_gpu(w)
+    if w.dim() != 5 or w.dtype != torch.bfloat16 or not w.is_contiguous():
+        raise ValueError("w must be contiguous bfloat16 [Cout, Cin, kt, kh, kw]")
+    Cout, Cin, kt, kh, kw = w.shape
+    taps = {(1, 3, 3): 9, (3, 1, 1): 3, (1, 1, 1): 1}.get((kt, kh, kw))
+    if taps is None:
+        raise ValueError("w must be a 1x3x3, 3x1x1 or 1x1x1 kernel")
+    n = int(lib.cvt_conv_weights_packed_bytes(Cout, Cin, taps))
+    if n == 0:
+        raise ValueError(f"unsupported weight shape {tuple(w.shape)}")
+    data = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check(lib.cvt_conv_weights_pack(_ptr(w), _ptr(data), Cout, Cin, taps, _stream(w.device)), "conv_weights_pack")
+    return PackedWeights(data, Cout, Cin, taps)
+
+
+def _packed(pw, taps, what):
+    if pw is None:
+        return None
+    if not isinstance(pw, PackedWeights) or pw.taps != taps:
+        raise ValueError(f"{what} must be PackedWeights of a {'1x3x3' if taps == 9 else '3x1x1' if taps == 3 else '1x1x1'}"
+                         " kernel (conv_weights_pack)")
+    return pw
+
+
+def conv_packed_workspace_bytes(x_shape, Cout, spatial=True, temporal=True):
+    B, _, T, H, W = x_shape
+    parts = (CVT_CONV_SPATIAL if spatial else 0) | (CVT_CONV_TEMPORAL if temporal else 0)
+    return int(lib.cvt_causal_conv3d_fact_packed_workspace(B, Cout, T, H, W, parts))
+
+
+def causal_conv3d_fact_packed(x, pw_s, pw_t=None, b_s=None, b_t=None, workspace=None, out=None):
+    """causal_conv3d_fact (k = 3) on weights packed once by conv_weights_pack: the same
+    kernels and result bit for bit, without the per-call weight repack.  The workspace holds
+    only the spatial->temporal intermediate (none for one part)."""
+    _nthwc_bf16(x, "x")
+    pw_s, pw_t = _packed(pw_s, 9, "pw_s"), _packed(pw_t, 3, "pw_t")
+    if pw_s is None and pw_t is None:
+        raise ValueError("at least one of pw_s and pw_t is needed")
+    B, Cin, T, H, W = x.shape
+    Cout = (pw_s or pw_t).Cout
+    if pw_s is not None and pw_s.Cin != Cin:
+        raise ValueError(f"pw_s was packed for Cin={pw_s.Cin}, x has {Cin} channels")
+    if pw_t is not None and (pw_t.Cout != Cout or pw_t.Cin != Cout):
+        raise ValueError("pw_t must be packed from [Cout, Cout, 3, 1, 1] weights")
+    ds = [t.data if t is not None else None for t in (pw_s, pw_t)]
+    _require_gpu(x, *ds, b_s, b_t, workspace)
+    _same_device(x, *ds, b_s, b_t, workspace)
+    for b in (b_s, b_t):
+        _f32_vec(b, Cout, "bias")
+    need = conv_packed_workspace_bytes(x.shape, Cout, pw_s is not None, pw_t is not None)
+    workspace = _workspace_arg(workspace, need, x) if need else workspace
+    shape = (B, Cout, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_causal_conv3d_fact_packed(_ptr(x), _ptr(ds[0]), _ptr(ds[1]), _ptr(b_s), _ptr(b_t), _ptr(y),
+                                             B, Cin, Cout, T, H, W, _ptr(workspace),
+                                             workspace.numel() if workspace is not None else 0, _stream(x.device)),
+           "causal_conv3d_fact_packed")
+    return y
+
+
+def conv_proj_packed_workspace_bytes(x_shape, Cout, spatial=True):
+    B, _, T, H, W = x_shape
+    parts = CVT_CONV_TEMPORAL | (CVT_CONV_SPATIAL if spatial else 0)
+    return int(lib.cvt_causal_conv3d_fact_proj_packed_workspace(B, Cout, T, H, W, parts))
+
+
+def causal_conv3d_fact_proj_packed(x, pw_s, pw_t, pw_p, b_s=None, b_t=None, b_p=None, workspace=None, out=None):
+    """causal_conv3d_fact_proj (k = 3, the projection in the temporal conv's epilogue) on
+    weights packed once by conv_weights_pack; bit for bit the unpacked call's result."""
+    _nthwc_bf16(x, "x")
+    pw_s, pw_t, pw_p = _packed(pw_s, 9, "pw_s"), _packed(pw_t, 3, "pw_t"), _packed(pw_p, 1, "pw_p")
+    if pw_t is None or pw_p is None:
+        raise ValueError("pw_t and pw_p are needed")
+    B, Cin, T, H, W = x.shape
+    Cout, Cp = pw_t.Cout, pw_p.Cout
+    if pw_t.Cin != Cout or pw_p.Cin != Cout or (pw_s is not None and (pw_s.Cout != Cout or pw_s.Cin != Cin)):
+        raise ValueError("packed weights do not chain: pw_s [Cout, Cin], pw_t [Cout, Cout], pw_p [Cp, Cout]")
+    ds = [t.data if t is not None else None for t in (pw_s, pw_t, pw_p)]
+    _require_gpu(x, *ds, b_s, b_t, b_p, workspace)
+    _same_device(x, *ds, b_s, b_t, b_p, workspace)
+    for bias, n in ((b_s, Cout), (b_t, Cout), (b_p, Cp)):
+        _f32_vec(bias, n, "bias")
+    need = conv_proj_packed_workspace_bytes(x.shape, Cout, pw_s is not None)
+    workspace = _workspace_arg(workspace, need, x) if need else workspace
+    shape = (B, Cp, T, H, W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_causal_conv3d_fact_proj_packed(_ptr(x), _ptr(ds[0]), _ptr(ds[1]), _ptr(b_s), _ptr(b_t), _ptr(ds[2]),
+                                                  _ptr(b_p), _ptr(y), B, Cin, Cout, Cp, T, H, W, _ptr(workspace),
+                                                  workspace.numel() if workspace is not None else 0,
+                                                  _stream(x.device)), "causal_conv3d_fact_proj_packed")
     return y
 
 

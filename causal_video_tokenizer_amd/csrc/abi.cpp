@@ -229,6 +229,101 @@ int cvt_causal_conv3d_fact_noalloc(const void* x, const void* w_s, const void* w
                       "cvt_causal_conv3d_fact_noalloc launch");
 }
 
+size_t cvt_conv_weights_packed_bytes(int Cout, int Cin, int taps) {
+    if (Cout <= 0 || Cin <= 0 || Cout > 4096 || Cin > 4096 || (taps != 1 && taps != 3 && taps != 9)) return 0;
+    return cvt::conv_weights_packed_bytes(Cout, Cin, taps);
+}
+
+int cvt_conv_weights_pack(const void* w, void* packed, int Cout, int Cin, int taps, void* stream) {
+    if (!w || !packed) return fail(CVT_E_NULL, "w and packed must not be NULL");
+    if (Cout <= 0 || Cin <= 0 || Cout > 4096 || Cin > 4096)
+        return fail(CVT_E_SHAPE, "Cout and Cin must be in 1..4096, got %d and %d", Cout, Cin);
+    if (taps != 1 && taps != 3 && taps != 9) return fail(CVT_E_SHAPE, "taps must be 1, 3 or 9, got %d", taps);
+    if (reinterpret_cast<uintptr_t>(w) & 1u) return fail(CVT_E_ALIGN, "w must be 2-byte aligned");
+    if (!aligned16(packed)) return fail(CVT_E_ALIGN, "packed must be 16-byte aligned");
+    return hip_status(cvt::launch_conv_weights_pack(w, packed, Cout, Cin, taps, (hipStream_t)stream),
+                      "cvt_conv_weights_pack launch");
+}
+
+size_t cvt_causal_conv3d_fact_packed_workspace(int B, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0 || parts < 1 || parts > 3) return 0;
+    return cvt::conv_packed_workspace_bytes(B, Cout, T, H, W, (parts & CVT_CONV_SPATIAL) != 0,
+                                            (parts & CVT_CONV_TEMPORAL) != 0);
+}
+
+namespace {
+// The checks shared by the two packed-weight calls (the projection's own ones aside).
+int check_conv_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t, void* y,
+                      int B, int Cin, int Cout, int T, int H, int W) {
+    if (!x || !y) return fail(CVT_E_NULL, "x and y must not be NULL");
+    if (!pw_s && !pw_t) return fail(CVT_E_NULL, "at least one of pw_s and pw_t must be given");
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
+    if (Cout > 4096) return fail(CVT_E_SHAPE, "Cout must be at most 4096, got %d", Cout);
+    if (!pw_s && Cin != Cout)
+        return fail(CVT_E_SHAPE, "a temporal-only call needs Cin == Cout (got %d and %d)", Cin, Cout);
+    if (Cin % 8 != 0 || Cout % 8 != 0)
+        return fail(CVT_E_SHAPE, "packed weights need Cin and Cout to be multiples of 8, got %d and %d", Cin, Cout);
+    if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if ((pw_s && !aligned16(pw_s)) || (pw_t && !aligned16(pw_t)))
+        return fail(CVT_E_ALIGN, "packed weights must be 16-byte aligned");
+    if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
+        return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    return CVT_OK;
+}
+
+int check_packed_workspace(void* workspace, size_t workspace_bytes, size_t need) {
+    if (need == 0) return CVT_OK;
+    if (!workspace || workspace_bytes < need)
+        return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return CVT_OK;
+}
+}  // namespace
+
+int cvt_causal_conv3d_fact_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t,
+                                  void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    int st = check_conv_packed(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W);
+    if (st != CVT_OK) return st;
+    if (Cout < 64 || !cvt::conv_packed_supported(Cin, Cout, H, W, pw_s != nullptr, pw_t != nullptr))
+        return fail(CVT_E_SHAPE, "packed weights run the row-tiled kernels: Cout >= 64 and a tile's rows of the "
+                                 "input (10 image rows, 9 frames) below 2 GiB (Cin=%d, Cout=%d)", Cin, Cout);
+    const size_t need = cvt::conv_packed_workspace_bytes(B, Cout, T, H, W, pw_s != nullptr, pw_t != nullptr);
+    if ((st = check_packed_workspace(workspace, workspace_bytes, need)) != CVT_OK) return st;
+    return hip_status(cvt::launch_conv_fact_packed(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace,
+                                                   (hipStream_t)stream),
+                      "cvt_causal_conv3d_fact_packed launch");
+}
+
+size_t cvt_causal_conv3d_fact_proj_packed_workspace(int B, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0 || parts < 2 || parts > 3) return 0;
+    return cvt::conv_proj_packed_workspace_bytes(B, Cout, T, H, W, (parts & CVT_CONV_SPATIAL) != 0);
+}
+
+int cvt_causal_conv3d_fact_proj_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s,
+                                       const float* b_t, const void* pw_p, const float* b_p, void* y, int B, int Cin,
+                                       int Cout, int Cp, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+    if (!pw_t || !pw_p) return fail(CVT_E_NULL, "pw_t and pw_p must not be NULL (the projection runs in the "
+                                                "temporal convolution's epilogue)");
+    int st = check_conv_packed(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W);
+    if (st != CVT_OK) return st;
+    if (Cp < 1 || Cp > 16 || Cout > 256)
+        return fail(CVT_E_SHAPE, "the fused projection needs Cout <= 256 and 1 <= Cp <= 16 (got Cout=%d, Cp=%d)", Cout,
+                    Cp);
+    if (Cout < 64 || !cvt::conv_proj_packed_supported(Cin, Cout, Cp, H, W, pw_s != nullptr))
+        return fail(CVT_E_SHAPE, "packed weights run the row-tiled kernels: Cout >= 64 and a tile's rows of the "
+                                 "input (10 image rows, 9 frames) below 2 GiB (Cin=%d, Cout=%d)", Cin, Cout);
+    if (!aligned16(pw_p)) return fail(CVT_E_ALIGN, "packed weights must be 16-byte aligned");
+    if (b_p && (reinterpret_cast<uintptr_t>(b_p) & 3u)) return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
+    const size_t need = cvt::conv_proj_packed_workspace_bytes(B, Cout, T, H, W, pw_s != nullptr);
+    if ((st = check_packed_workspace(workspace, workspace_bytes, need)) != CVT_OK) return st;
+    return hip_status(cvt::launch_conv_fact_proj_packed(x, pw_s, pw_t, b_s, b_t, pw_p, b_p, y, B, Cin, Cout, Cp, T, H,
+                                                        W, workspace, (hipStream_t)stream),
+                      "cvt_causal_conv3d_fact_proj_packed launch");
+}
+
 size_t cvt_causal_conv3d_fact_proj_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k, int parts) {
     if (B <= 0 || Cin <= 0 || Cout <= 0 || Cp <= 0 || T <= 0 || H <= 0 || W <= 0 || (k != 1 && k != 3)) return 0;
     if (parts < 1 || parts > 3) return 0;

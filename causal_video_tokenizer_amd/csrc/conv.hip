@@ -1961,6 +1961,73 @@ hipError_t launch_conv_fact_proj(const void* x, const void* w_s, const void* w_t
     return launch_rows<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s, wpp, b_p, Cp, nullptr, aux);
 }
 
+// Weights packed once by the caller (cvt_conv_weights_pack) for repeated calls: the order in
+// which conv_rows_kernel reads them (pack_frag_kernel).  The packed calls run the row-tiled
+// kernels only, with the caller's packed weights in place of the per-call repack; the
+// results are those of the unpacked calls bit for bit (same kernels, same weights).
+size_t conv_weights_packed_bytes(int Cout, int Cin, int taps) { return align256(frag_bytes(Cout, Cin, taps)); }
+
+hipError_t launch_conv_weights_pack(const void* w, void* packed, int Cout, int Cin, int taps, hipStream_t s) {
+    return pack_frag(w, static_cast<uint16_t*>(packed), Cout, Cin, taps, s);
+}
+
+bool conv_packed_supported(int Cin, int Cout, int H, int W, bool spatial, bool temporal) {
+    return (!spatial || use_rows_kernel(3, Cout, rows_span_spatial(W), Cin)) &&
+           (!temporal || use_rows_kernel(3, Cout, rows_span_temporal((long long)H * W), Cout));
+}
+
+size_t conv_packed_workspace_bytes(int B, int Cout, int T, int H, int W, bool spatial, bool temporal) {
+    return spatial && temporal ? align256((size_t)B * T * H * W * Cout * 2) : 0;
+}
+
+hipError_t launch_conv_fact_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s,
+                                   const float* b_t, void* y, int B, int Cin, int Cout, int T, int H, int W,
+                                   void* workspace, hipStream_t s) {
+    ConvGeom g{};
+    g.P = (long long)B * T * H * W; g.T = T; g.H = H; g.W = W; g.Cin = Cin; g.Cout = Cout;
+    g.kchunks = (Cin + BK - 1) / BK;
+    const uint16_t* tin = static_cast<const uint16_t*>(x);
+    hipError_t e;
+    if (pw_s) {  // spatial part into the workspace (or y when there is no temporal part)
+        uint16_t* sout = static_cast<uint16_t*>(pw_t ? workspace : y);
+        if ((e = launch_rows<SPATIAL3>(tin, static_cast<const uint16_t*>(pw_s), b_s, sout, g, B, s)) != hipSuccess)
+            return e;
+        tin = sout;
+    }
+    if (!pw_t) return hipSuccess;
+    g.Cin = Cout;
+    g.kchunks = (Cout + BK - 1) / BK;
+    return launch_rows<TEMPORAL3>(tin, static_cast<const uint16_t*>(pw_t), b_t, static_cast<uint16_t*>(y), g, B, s);
+}
+
+bool conv_proj_packed_supported(int Cin, int Cout, int Cp, int H, int W, bool spatial) {
+    return proj_fused(3, Cout, Cp, (long long)H * W, true) &&
+           (!spatial || use_rows_kernel(3, Cout, rows_span_spatial(W), Cin));
+}
+
+size_t conv_proj_packed_workspace_bytes(int B, int Cout, int T, int H, int W, bool spatial) {
+    return spatial ? align256((size_t)B * T * H * W * Cout * 2) : 0;
+}
+
+hipError_t launch_conv_fact_proj_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s,
+                                        const float* b_t, const void* pw_p, const float* b_p, void* y, int B, int Cin,
+                                        int Cout, int Cp, int T, int H, int W, void* workspace, hipStream_t s) {
+    const uint16_t* tin = static_cast<const uint16_t*>(x);
+    hipError_t e;
+    if (pw_s) {  // spatial part on its own into the workspace
+        uint16_t* S = static_cast<uint16_t*>(workspace);
+        if ((e = launch_conv_fact_packed(x, pw_s, nullptr, b_s, nullptr, S, B, Cin, Cout, T, H, W, nullptr, s)) !=
+            hipSuccess)
+            return e;
+        tin = S;
+    }
+    ConvGeom g{};
+    g.P = (long long)B * T * H * W; g.T = T; g.H = H; g.W = W; g.Cin = Cout; g.Cout = Cout;
+    g.kchunks = (Cout + BK - 1) / BK;
+    return launch_rows<TEMPORAL3>(tin, static_cast<const uint16_t*>(pw_t), b_t, static_cast<uint16_t*>(y), g, B, s,
+                                  static_cast<const uint16_t*>(pw_p), b_p, Cp);
+}
+
 // Causal temporal convolution of one chunk of a stream (optionally with the fused 1x1
 // projection): the frames before the chunk come from hist instead of the zero padding.
 size_t conv_temporal_stream_workspace_bytes(int C, int Cp) {

@@ -149,6 +149,21 @@ hipError_t launch_fsq_conv(const int32_t* idx, const FsqParams& p, const void* w
                            const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
                            int Cmid, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
 
+// Weights packed once by the caller (conv.hip): the row-tiled kernels' fragment order
+// (taps 9, 3 or 1), and the factorized conv (with the fused 1x1) on packed weights.
+size_t conv_weights_packed_bytes(int Cout, int Cin, int taps);
+hipError_t launch_conv_weights_pack(const void* w, void* packed, int Cout, int Cin, int taps, hipStream_t s);
+bool conv_packed_supported(int Cin, int Cout, int H, int W, bool spatial, bool temporal);
+size_t conv_packed_workspace_bytes(int B, int Cout, int T, int H, int W, bool spatial, bool temporal);
+hipError_t launch_conv_fact_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s,
+                                   const float* b_t, void* y, int B, int Cin, int Cout, int T, int H, int W,
+                                   void* workspace, hipStream_t s);
+bool conv_proj_packed_supported(int Cin, int Cout, int Cp, int H, int W, bool spatial);
+size_t conv_proj_packed_workspace_bytes(int B, int Cout, int T, int H, int W, bool spatial);
+hipError_t launch_conv_fact_proj_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s,
+                                        const float* b_t, const void* pw_p, const float* b_p, void* y, int B, int Cin,
+                                        int Cout, int Cp, int T, int H, int W, void* workspace, hipStream_t s);
+
 // Causal temporal convolution of one chunk of a stream (conv.hip): history frames in place
 // of the zero padding, optional fused 1x1 projection (C <= 256, Cp <= 16).
 size_t conv_temporal_stream_workspace_bytes(int C, int Cp);

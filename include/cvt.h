@@ -175,6 +175,60 @@ int cvt_causal_conv3d_fact_noalloc(const void* x, const void* w_s, const void* w
                                    void* stream);
 
 /*
+ * Conv weights packed once, for callers whose weights stay fixed across calls
+ * (inference): the same operations as cvt_causal_conv3d_fact (k = 3) and
+ * cvt_causal_conv3d_fact_proj, without the per-call weight repack.  Source:
+ * as cvt_causal_conv3d_fact ("Cosmos World Foundation Model Platform for
+ * Physical AI (Cosmos-Predict1)", section "1) Cosmos Tokenizer").
+ *
+ * cvt_conv_weights_packed_bytes(Cout, Cin, taps): bytes of the packed form of a
+ *      bf16 weight tensor [Cout, Cin, taps] in torch order: taps = 9 (1x3x3
+ *      spatial), 3 (3x1x1 temporal) or 1 (1x1 projection); 0 for invalid
+ *      arguments.
+ * cvt_conv_weights_pack: writes that packed form of w into `packed` (device,
+ *      16-byte aligned, owned by the caller, at least that many bytes) on the
+ *      stream: the order in which the row-tiled convolution kernels read their
+ *      weights (1 KB fragments of 32 output x 16 input channels, zeros past
+ *      Cout and Cin).  The projection of the _proj call is packed with
+ *      Cout = Cp, Cin = the conv's Cout, taps = 1.
+ *      Errors: CVT_E_NULL, CVT_E_SHAPE (Cout or Cin outside 1..4096, taps not
+ *      1, 3 or 9), CVT_E_ALIGN (w not 2-byte, packed not 16-byte aligned).
+ * cvt_causal_conv3d_fact_packed: x, b_s, b_t, y, sizes as
+ *      cvt_causal_conv3d_fact with k = 3; pw_s, pw_t: the packed spatial
+ *      (taps 9) and temporal (taps 3) weights, either NULL as there.
+ *      workspace: cvt_causal_conv3d_fact_packed_workspace() bytes (the bf16
+ *      intermediate when both parts run; 0, and workspace may be NULL, for one
+ *      part).
+ * cvt_causal_conv3d_fact_proj_packed: as cvt_causal_conv3d_fact_proj with
+ *      k = 3 and packed weights; the temporal part (pw_t) and the projection
+ *      (pw_p, Cp channels) are required, the projection runs in the temporal
+ *      convolution's epilogue.  workspace: the spatial part's bf16 output when
+ *      pw_s is given (cvt_causal_conv3d_fact_proj_packed_workspace, parts =
+ *      CVT_CONV_TEMPORAL or CVT_CONV_SPATIAL | CVT_CONV_TEMPORAL), else none.
+ * The outputs equal those of the unpacked calls bit for bit.
+ * Errors: CVT_E_NULL (x, y; both pw_s and pw_t NULL; for _proj pw_t or pw_p);
+ *      CVT_E_SHAPE for Cin or Cout not a multiple of 8, Cout < 64 or above
+ *      4096, a temporal-only call with Cin != Cout, shapes the row-tiled
+ *      kernels do not take (10 image rows or 9 frames of the input of 2 GiB
+ *      or more), and for _proj Cout > 256 or Cp outside 1..16; CVT_E_ALIGN
+ *      unless x, y, the packed weights and the workspace are 16-byte and the
+ *      biases 4-byte aligned; CVT_E_WORKSPACE when the workspace is too small.
+ */
+size_t cvt_conv_weights_packed_bytes(int Cout, int Cin, int taps);
+int cvt_conv_weights_pack(const void* w, void* packed, int Cout, int Cin, int taps, void* stream);
+size_t cvt_causal_conv3d_fact_packed_workspace(int B, int Cout, int T, int H, int W, int parts);
+int cvt_causal_conv3d_fact_packed(const void* x, const void* pw_s, const void* pw_t,
+                                  const float* b_s, const float* b_t, void* y,
+                                  int B, int Cin, int Cout, int T, int H, int W,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+size_t cvt_causal_conv3d_fact_proj_packed_workspace(int B, int Cout, int T, int H, int W, int parts);
+int cvt_causal_conv3d_fact_proj_packed(const void* x, const void* pw_s, const void* pw_t,
+                                       const float* b_s, const float* b_t, const void* pw_p,
+                                       const float* b_p, void* y, int B, int Cin, int Cout, int Cp,
+                                       int T, int H, int W, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * Factorized causal convolution (as cvt_causal_conv3d_fact) followed by a
  * 1x1x1 projection to Cp channels, without writing the Cout-channel result:
  *   y = bf16( w_p . bf16(conv(x)) + b_p ),

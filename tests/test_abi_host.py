@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 34
+    assert len(names) == 40
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -392,3 +392,65 @@ def test_conv_noalloc_validation():
     assert b"preallocated scratch" in lib.cvt_last_error()
     assert lib.cvt_causal_conv3d_fact_workspace(1, 256, 256, 10, 100, 160, 3, 3) > cvt.NOALLOC_SCRATCH_BYTES
     assert cvt.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_conv_packed_validation_and_workspace():
+    """Packing and the packed-weight convs: sizes of the packed form, workspace queries (only
+    the bf16 intermediate), and every argument check before any launch."""
+    assert lib.cvt_conv_weights_packed_bytes(256, 192, 9) == 12 * 9 * 8 * 1024  # Cin/16 x taps x Cout/32 fragments
+    assert lib.cvt_conv_weights_packed_bytes(256, 256, 3) == 48 * 8 * 1024
+    assert lib.cvt_conv_weights_packed_bytes(6, 256, 1) == 16 * 1024             # rows past Cp padded to 32
+    assert lib.cvt_conv_weights_packed_bytes(256, 256, 2) == 0
+    assert lib.cvt_conv_weights_packed_bytes(0, 256, 3) == 0
+    assert lib.cvt_conv_weights_pack(None, B_, 256, 256, 3, None) == E_NULL
+    assert lib.cvt_conv_weights_pack(A, None, 256, 256, 3, None) == E_NULL
+    assert lib.cvt_conv_weights_pack(A, B_, 256, 256, 5, None) == E_SHAPE
+    assert lib.cvt_conv_weights_pack(A, B_, 5000, 256, 3, None) == E_SHAPE
+    assert lib.cvt_conv_weights_pack(ctypes.c_void_p(0x100001), B_, 256, 256, 3, None) == E_ALIGN
+    assert lib.cvt_conv_weights_pack(A, MIS, 256, 256, 3, None) == E_ALIGN
+
+    P = 5 * 8 * 8
+    assert lib.cvt_causal_conv3d_fact_packed_workspace(1, 256, 5, 8, 8, 3) == P * 256 * 2
+    assert lib.cvt_causal_conv3d_fact_packed_workspace(1, 256, 5, 8, 8, 1) == 0
+    assert lib.cvt_causal_conv3d_fact_packed_workspace(1, 256, 5, 8, 8, 2) == 0
+    assert lib.cvt_causal_conv3d_fact_packed_workspace(1, 256, 5, 8, 8, 0) == 0
+    assert lib.cvt_causal_conv3d_fact_proj_packed_workspace(1, 256, 5, 8, 8, 3) == P * 256 * 2
+    assert lib.cvt_causal_conv3d_fact_proj_packed_workspace(1, 256, 5, 8, 8, 2) == 0
+    assert lib.cvt_causal_conv3d_fact_proj_packed_workspace(1, 256, 5, 8, 8, 1) == 0  # the temporal part is required
+
+    W8 = ctypes.c_void_p(0x500000)
+
+    def call(**kw):
+        return lib.cvt_causal_conv3d_fact_packed(kw.get("x", A), kw.get("ws", B_), kw.get("wt", C_), None, None,
+                                                 kw.get("y", ctypes.c_void_p(0x400000)), 1, kw.get("Cin", 192),
+                                                 kw.get("Cout", 256), 5, 8, kw.get("W", 8), kw.get("work", W8),
+                                                 kw.get("wsb", P * 256 * 2), None)
+    assert call(x=None) == E_NULL
+    assert call(ws=None, wt=None) == E_NULL
+    assert call(ws=None) == E_SHAPE           # temporal-only needs Cin == Cout
+    assert call(Cin=12) == E_SHAPE
+    assert call(Cout=12) == E_SHAPE
+    assert call(Cout=32) == E_SHAPE           # the row-tiled kernels need Cout >= 64
+    assert b"row-tiled" in lib.cvt_last_error()
+    assert call(Cout=5000) == E_SHAPE
+    assert call(x=MIS) == E_ALIGN
+    assert call(ws=MIS) == E_ALIGN
+    assert call(wsb=P * 256 * 2 - 1) == E_WORKSPACE
+    assert call(work=None) == E_WORKSPACE
+    assert call(wt=None, work=None, wsb=0, W=1 << 23) == E_SHAPE   # 10 image rows of 2^23 x 192 x 2 bytes > 2 GiB
+
+    def pcall(**kw):
+        return lib.cvt_causal_conv3d_fact_proj_packed(kw.get("x", A), kw.get("ws", B_), kw.get("wt", C_), None, None,
+                                                      kw.get("wp", ctypes.c_void_p(0x600000)), None,
+                                                      kw.get("y", ctypes.c_void_p(0x400000)), 1, kw.get("Cin", 192),
+                                                      kw.get("Cout", 256), kw.get("Cp", 6), 5, 8, 8,
+                                                      kw.get("work", W8), kw.get("wsb", P * 256 * 2), None)
+    assert pcall(wt=None) == E_NULL
+    assert pcall(wp=None) == E_NULL
+    assert pcall(y=None) == E_NULL
+    assert pcall(Cp=0) == E_SHAPE
+    assert pcall(Cp=17) == E_SHAPE
+    assert pcall(Cout=320, Cin=320) == E_SHAPE   # the fused projection needs Cout <= 256
+    assert pcall(ws=None) == E_SHAPE             # temporal-only needs Cin == Cout
+    assert pcall(wp=ctypes.c_void_p(0x600008)) == E_ALIGN
+    assert pcall(wsb=P * 256 * 2 - 1) == E_WORKSPACE
