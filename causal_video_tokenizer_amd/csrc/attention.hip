@@ -13,7 +13,7 @@
 // as bf16, the output is rounded to bf16 once.
 //
 // Kernels:
-//   * attn_spatial_kernel - flash attention (d = 64) on bf16 MFMA 32x32x16, in
+//   * attn_spatial_kernel<D> - flash attention (d = 32, 64, 128) on bf16 MFMA 32x32x16, in
 //     transposed form: S^T = K Q^T and O^T = V^T P^T, so a lane owns one query
 //     column of every accumulator and the running max / sum of the online
 //     softmax stay in its registers (the two lane halves of a column exchange
@@ -27,7 +27,10 @@
 //     per byte, so it is bound by HBM, not by the matrix cores;
 //   * attn_temporal_kernel - the other temporal cases (d = 32, or 32 < T, T * C <=
 //     16384): K and V of a few consecutive positions staged in LDS (one contiguous run
-//     per frame), one thread per (position, head, query frame) in fp32.
+//     per frame), one thread per (position, head, query frame) in fp32;
+//   * attn_generic_kernel - every other shape of either axis (any head dim d % 8 == 0 up
+//     to 256, any sequence length): one thread per query, keys and values from global
+//     memory, fp32.
 #include <algorithm>
 #include <type_traits>
 
@@ -40,20 +43,30 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------------------
-// Spatial attention.  Workgroup = 4 waves x 64 queries (two 32-query MFMA column blocks
-// per wave) of one (clip, frame, head) sequence; the keys go by in blocks of 64, staged
-// in LDS (K rows [key][64 channels], V^T rows [channel][64 keys], 16-byte padded rows,
-// two buffers), loaded during the previous block.  Per block and wave: 16 MFMAs for
-// S^T (2 key blocks x 2 query blocks x 4 channel k-steps) and 16 for O^T (2 channel
-// blocks x 2 query blocks x 4 key k-steps).
-constexpr int AD = 64;               // head dim of the spatial kernel
-constexpr int AQW = 64;              // queries per wave
-constexpr int AQT = 4 * AQW;         // queries per workgroup
+// Spatial attention, head dim D in {32, 64, 128}.  Workgroup = 4 waves x 32 QB queries
+// (QB 32-query MFMA column blocks per wave: 2 up to D = 64, 1 at D = 128, whose
+// accumulators are twice as many) of one (clip, frame, head) sequence; the keys go by in
+// blocks of 64, staged in LDS (K rows [key][D channels], V^T rows [channel][64 keys],
+// 16-byte padded rows, two buffers), loaded during the previous block.  Per block and wave:
+// 2 key blocks x QB query blocks x D/16 channel k-steps MFMAs for S^T and D/32 channel
+// blocks x QB query blocks x 4 key k-steps for O^T.
 constexpr int AKB = 64;              // keys per block
-constexpr int AKRS = AD * 2 + 16;    // bytes per K row in LDS
 constexpr int AVRS = AKB * 2 + 16;   // bytes per V^T row in LDS
-constexpr int AKBUF = AKB * AKRS;
-constexpr int AVBUF = AD * AVRS;
+
+template <int D>
+struct SpatialAttnCfg {
+    static_assert(D == 32 || D == 64 || D == 128, "spatial head dims 32, 64, 128");
+    static constexpr int QB = D <= 64 ? 2 : 1;   // 32-query blocks per wave
+    static constexpr int QW = 32 * QB;           // queries per wave
+    static constexpr int QT = 4 * QW;            // queries per workgroup
+    static constexpr int KRS = D * 2 + 16;       // bytes per K row in LDS
+    static constexpr int KBUF = AKB * KRS;
+    static constexpr int VBUF = D * AVRS;
+    static constexpr int CPK = D / 8;            // 16-byte chunks per key row
+    static constexpr int KL = AKB * CPK / 256;   // K chunks per thread and block
+    static constexpr int VI = 32 * CPK;          // V items: (key pair, chunk)
+    static constexpr int VL = (VI + 255) / 256;  // V items per thread
+};
 
 struct AttnGeom {
     int N;          // tokens per sequence (H * W)
@@ -77,17 +90,21 @@ __device__ __forceinline__ int vperm(int k) {
     return (k & ~15) | (k & 3) | (((k >> 3) & 1) << 2) | (((k >> 2) & 1) << 3);
 }
 
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_spatial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, AttnGeom g) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (AKBUF + AVBUF)];
+    using Cf = SpatialAttnCfg<D>;
+    constexpr int QB = Cf::QB, QW = Cf::QW, QT = Cf::QT, KRS = Cf::KRS, KBUF = Cf::KBUF, VBUF = Cf::VBUF;
+    constexpr int CPK = Cf::CPK, KL = Cf::KL, VI = Cf::VI, VL = Cf::VL, CB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (KBUF + VBUF)];
     // XCD-aware order: consecutive tiles (the query tiles of one sequence, which read the
     // same keys) run on one XCD's L2
     const int tile = (int)(blockIdx.x & 7) * g.per_xcd + (int)(blockIdx.x >> 3);
     if (tile >= g.ntiles) return;
     const int qt = tile % g.nqt, seq = tile / g.nqt;
     const int head = seq % g.G;
-    const long long base = (long long)(seq / g.G) * g.N * g.C + head * AD;  // element offset of token 0
+    const long long base = (long long)(seq / g.G) * g.N * g.C + head * D;  // element offset of token 0
     const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
     const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
@@ -98,84 +115,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
     // Q^T B operand: lane (query px of block qb, half hh) holds channels 16 ks + 8 hh .. +7.
     // Queries past N read zeros (past the buffer) and are never stored.
-    bf16x8_t qf[2][AD / 16];
+    bf16x8_t qf[QB][D / 16];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qt * AQT + wave * AQW + qb * 32 + px;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qt * QT + wave * QW + qb * 32 + px;
         const int off = qi < g.N ? qi * rowb : 0x7fffff00;
 #pragma unroll
-        for (int ks = 0; ks < AD / 16; ++ks)
+        for (int ks = 0; ks < D / 16; ++ks)
             qf[qb][ks] = __builtin_bit_cast(bf16x8_t,
                                             __builtin_amdgcn_raw_buffer_load_b128(qres, off + (ks * 16 + hh * 8) * 2, 0, 0));
     }
 
-    // Staging of a key block: thread -> key j = tid / 8 (+ 32), 16-byte chunk c8 = tid % 8
-    // for K; pair of keys 2 p, 2 p + 1 (p = tid / 8) at chunk c8 for V.  Keys past N are
+    // Staging of a key block: K chunk i = tid + 256 r is key i / CPK at 16-byte chunk i % CPK;
+    // V item i is the key pair 2 p, 2 p + 1 (p = i / CPK) at chunk i % CPK.  Keys past N are
     // staged as zeros (and masked from the scores).
-    const int c8 = tid & 7, jr = tid >> 3;
-    uint4 kst[2], vst[2];
+    uint4 kst[KL], vst[VL][2];
     auto load_block = [&](int blk) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int j = blk * AKB + jr + 32 * r;
-            const auto kv = __builtin_amdgcn_raw_buffer_load_b128(kres, j < g.N ? j * rowb + c8 * 16 : 0x7fffff00, 0, 0);
+        for (int r = 0; r < KL; ++r) {
+            const int i = tid + 256 * r, j = blk * AKB + i / CPK, c = i % CPK;
+            const auto kv = __builtin_amdgcn_raw_buffer_load_b128(kres, j < g.N ? j * rowb + c * 16 : 0x7fffff00, 0, 0);
             kst[r] = *reinterpret_cast<const uint4*>(&kv);
-            const int jv = blk * AKB + 2 * jr + r;
-            const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, jv < g.N ? jv * rowb + c8 * 16 : 0x7fffff00, 0, 0);
-            vst[r] = *reinterpret_cast<const uint4*>(&vv);
+        }
+#pragma unroll
+        for (int r = 0; r < VL; ++r) {
+            const int i = tid + 256 * r, p = i / CPK, c = i % CPK;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int jv = blk * AKB + 2 * p + e;
+                const auto vv = __builtin_amdgcn_raw_buffer_load_b128(
+                    vres, i < VI && jv < g.N ? jv * rowb + c * 16 : 0x7fffff00, 0, 0);
+                vst[r][e] = *reinterpret_cast<const uint4*>(&vv);
+            }
         }
     };
     auto store_block = [&](int buf) {
-        uint8_t* sk = smem + buf * (AKBUF + AVBUF);
-        uint8_t* sv = sk + AKBUF;
+        uint8_t* sk = smem + buf * (KBUF + VBUF);
+        uint8_t* sv = sk + KBUF;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(sk + (jr + 32 * r) * AKRS + c8 * 16) = kst[r];
-        // V^T: channel c8 * 8 + e gets the pair (key 2 jr, key 2 jr + 1) at its permuted column
-        const uint32_t a[4] = {vst[0].x, vst[0].y, vst[0].z, vst[0].w};
-        const uint32_t b[4] = {vst[1].x, vst[1].y, vst[1].z, vst[1].w};
-        const int col = vperm(2 * jr) * 2;
+        for (int r = 0; r < KL; ++r) {
+            const int i = tid + 256 * r;
+            *reinterpret_cast<uint4*>(sk + (i / CPK) * KRS + (i % CPK) * 16) = kst[r];
+        }
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            // channels 2 e2 and 2 e2 + 1 of the chunk: low halves, then high halves
-            *reinterpret_cast<uint32_t*>(sv + (c8 * 8 + 2 * e2) * AVRS + col) = (a[e2] & 0xffffu) | (b[e2] << 16);
-            *reinterpret_cast<uint32_t*>(sv + (c8 * 8 + 2 * e2 + 1) * AVRS + col) = (a[e2] >> 16) | (b[e2] & 0xffff0000u);
+        for (int r = 0; r < VL; ++r) {
+            const int i = tid + 256 * r, p = i / CPK, c = i % CPK;
+            if (VI % 256 == 0 || i < VI) {
+                // V^T: channel c * 8 + e gets the pair (key 2 p, key 2 p + 1) at its permuted column
+                const uint32_t a[4] = {vst[r][0].x, vst[r][0].y, vst[r][0].z, vst[r][0].w};
+                const uint32_t b[4] = {vst[r][1].x, vst[r][1].y, vst[r][1].z, vst[r][1].w};
+                const int col = vperm(2 * p) * 2;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    // channels 2 e2 and 2 e2 + 1 of the chunk: low halves, then high halves
+                    *reinterpret_cast<uint32_t*>(sv + (c * 8 + 2 * e2) * AVRS + col) = (a[e2] & 0xffffu) | (b[e2] << 16);
+                    *reinterpret_cast<uint32_t*>(sv + (c * 8 + 2 * e2 + 1) * AVRS + col) =
+                        (a[e2] >> 16) | (b[e2] & 0xffff0000u);
+                }
+            }
         }
     };
 
-    f32x16_t o[2][2];  // O^T: [channel block][query block]
+    f32x16_t o[CB][QB];  // O^T: [channel block][query block]
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[cb][qb][e] = 0.0f;
-    float m[2] = {-INFINITY, -INFINITY};  // running max (log2 domain) of the lane's query
-    float lp[2] = {0.0f, 0.0f};           // running sum over the lane's own keys
+    float m[QB], lp[QB];  // running max (log2 domain) and the sum over the lane's own keys
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        lp[qb] = 0.0f;
+    }
 
     const int nblk = (g.N + AKB - 1) / AKB;
     // per-lane byte offsets of the K and V^T fragments within a buffer; every fragment is
     // this plus a compile-time offset
-    const int klane = px * AKRS + hh * 16, vlane = AKBUF + px * AVRS + hh * 16;
+    const int klane = px * KRS + hh * 16, vlane = KBUF + px * AVRS + hh * 16;
 
     // One key block.  MASKED (the last block when N is not a multiple of 64): keys past N
     // get a score of -inf.  A compile-time flag, so that the full blocks carry no mask code.
     auto block = [&](int blk, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
-        const uint8_t* kbase = smem + (blk & 1) * (AKBUF + AVBUF) + klane;
-        const uint8_t* vbase = smem + (blk & 1) * (AKBUF + AVBUF) + vlane;
+        const uint8_t* kbase = smem + (blk & 1) * (KBUF + VBUF) + klane;
+        const uint8_t* vbase = smem + (blk & 1) * (KBUF + VBUF) + vlane;
         if (blk + 1 < nblk) load_block(blk + 1);
 
-        // S^T = K Q^T: rows = 64 keys (2 blocks), columns = the wave's 64 queries; the first
+        // S^T = K Q^T: rows = 64 keys (2 blocks), columns = the wave's queries; the first
         // k-step accumulates onto the inline constant 0 (no register clearing per block)
-        f32x16_t s[2][2];
+        f32x16_t s[2][QB];
         const f32x16_t zero16 = {};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int ks = 0; ks < AD / 16; ++ks) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kbase + kb * 32 * AKRS + ks * 32);
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kbase + kb * 32 * KRS + ks * 32);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < QB; ++qb)
                     s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], ks == 0 ? zero16 : s[kb][qb],
                                                                          0, 0, 0);
             }
@@ -187,15 +225,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int r = 0; r < 16; ++r) {
                     const int j = blk * AKB + kb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
                     if (j >= g.N) {
-                        s[kb][0][r] = -INFINITY;
-                        s[kb][1][r] = -INFINITY;
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
                     }
                 }
         }
 
         // online softmax per query column; P (bf16) straight into the P V MFMAs
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             float mx = s[0][qb][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -230,22 +268,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             // once the maximum has settled, most blocks skip it
             if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[cb][qb][e] *= alpha;
             }
             // O^T += V^T P^T: A = V^T rows (32 channels) x the k-step's 16 keys in lane order
-    #pragma unroll
+#pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
+                    for (int cb = 0; cb < CB; ++cb) {
                         const bf16x8_t vf =
                             *reinterpret_cast<const bf16x8_t*>(vbase + cb * 32 * AVRS + (kb * 32 + h2 * 16) * 2);
                         o[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][h2], o[cb][qb], 0, 0, 0);
                     }
-            }
+        }
         if (blk + 1 < nblk) store_block((blk + 1) & 1);
         __syncthreads();
     };
@@ -260,14 +298,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     // normalise and store: element r of O^T block (cb, qb) is channel 32 cb + 8 (r / 4) +
     // 4 hh + r % 4 of the lane's query; four consecutive channels per 8-byte store
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const float l = lp[qb] + __shfl_xor(lp[qb], 32);
         const float inv = 1.0f / l;
-        const int qi = qt * AQT + wave * AQW + qb * 32 + px;
+        const int qi = qt * QT + wave * QW + qb * 32 + px;
         if (qi < g.N) {
             uint16_t* orow = O + base + (long long)qi * g.C;
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     uint2 u;
@@ -595,6 +633,132 @@ hipError_t launch_temporal(const uint16_t* q, const uint16_t* k, const uint16_t*
 
 int attention_max_tc() { return 16384; }
 
+// ---------------------------------------------------------------------------------------
+// Any head dim (d % 8 == 0, d <= 256) and any sequence length, either axis: one thread per
+// (sequence, query token), keys and values read straight from global memory (the
+// sequence's rows are shared by the wave's threads through the caches), two passes: the
+// maximum score, then, for each 64-channel slice of the output, the weights (fp32) and the
+// weighted sum of the values, the scores recomputed per slice.  The path for the shapes the
+// tiled kernels do not take (spatial head dims other than 32, 64, 128; temporal head dims
+// other than 32, 64 or sequences whose K and V do not fit the LDS tile); its rate is not a
+// target.
+struct GAttnGeom {
+    long long nitems;    // sequences x tokens
+    int N;               // tokens per sequence
+    int G, d, C, HW, T;  // heads, head dim, channels, positions per frame, frames
+    int causal;          // temporal: token i sees tokens j <= i
+    long long tstride;   // elements between consecutive tokens of a sequence
+    float scale2;        // log2(e) / sqrt(d)
+};
+
+__global__ __launch_bounds__(256) void attn_generic_kernel(const uint16_t* __restrict__ Q,
+                                                           const uint16_t* __restrict__ K,
+                                                           const uint16_t* __restrict__ V,
+                                                           uint16_t* __restrict__ O, GAttnGeom g) {
+    const long long item = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (item >= g.nitems) return;
+    const long long sq = item / g.N;
+    const int i = (int)(item - sq * g.N);
+    const int head = (int)(sq % g.G);
+    const long long outer = sq / g.G;  // spatial: clip * T + frame; temporal: clip * HW + position
+    long long base;                    // element offset of the sequence's token 0
+    if (g.causal) {
+        const long long b = outer / g.HW, pos = outer - b * g.HW;
+        base = (b * g.T * g.HW + pos) * g.C + (long long)head * g.d;
+    } else {
+        base = outer * g.N * g.C + (long long)head * g.d;
+    }
+    const uint16_t* qrow = Q + base + i * g.tstride;
+    const int nk = g.causal ? i + 1 : g.N;
+    auto score = [&](int j) {  // q . k_j in fp32, two products per instruction
+        const uint16_t* krow = K + base + j * g.tstride;
+        float a = 0.0f;
+        for (int c = 0; c < g.d; c += 8) {
+            const uint4 q = *reinterpret_cast<const uint4*>(qrow + c);
+            const uint4 k = *reinterpret_cast<const uint4*>(krow + c);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, k.x), a,
+                                                false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, k.y), a,
+                                                false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, k.z), a,
+                                                false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, k.w), a,
+                                                false);
+        }
+        return a;
+    };
+    float mx = -INFINITY;
+    for (int j = 0; j < nk; ++j) mx = fmaxf(mx, score(j));
+    const float m2 = mx * g.scale2;
+    for (int c0 = 0; c0 < g.d; c0 += 64) {
+        const int nc = min(64, g.d - c0);  // a multiple of 8
+        float o[64];
+#pragma unroll
+        for (int c = 0; c < 64; ++c) o[c] = 0.0f;
+        float l = 0.0f;
+        for (int j = 0; j < nk; ++j) {
+            const float p = fast_exp2(fmaf(score(j), g.scale2, -m2));
+            l += p;
+            const uint16_t* vrow = V + base + j * g.tstride + c0;
+#pragma unroll
+            for (int c = 0; c < 64; c += 8) {
+                if (c < nc) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(vrow + c);
+                    o[c] = fmaf(p, bf16_lo(u.x), o[c]); o[c + 1] = fmaf(p, bf16_hi(u.x), o[c + 1]);
+                    o[c + 2] = fmaf(p, bf16_lo(u.y), o[c + 2]); o[c + 3] = fmaf(p, bf16_hi(u.y), o[c + 3]);
+                    o[c + 4] = fmaf(p, bf16_lo(u.z), o[c + 4]); o[c + 5] = fmaf(p, bf16_hi(u.z), o[c + 5]);
+                    o[c + 6] = fmaf(p, bf16_lo(u.w), o[c + 6]); o[c + 7] = fmaf(p, bf16_hi(u.w), o[c + 7]);
+                }
+            }
+        }
+        const float inv = 1.0f / l;
+        uint16_t* orow = O + base + i * g.tstride + c0;
+#pragma unroll
+        for (int c = 0; c < 64; c += 8) {
+            if (c < nc) {
+                uint4 u;
+                u.x = pack_bf16x2(o[c] * inv, o[c + 1] * inv);
+                u.y = pack_bf16x2(o[c + 2] * inv, o[c + 3] * inv);
+                u.z = pack_bf16x2(o[c + 4] * inv, o[c + 5] * inv);
+                u.w = pack_bf16x2(o[c + 6] * inv, o[c + 7] * inv);
+                *reinterpret_cast<uint4*>(orow + c) = u;
+            }
+        }
+    }
+}
+
+hipError_t launch_attention_generic(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O, int B, int C,
+                                    int T, int HW, int heads, bool causal, hipStream_t s) {
+    GAttnGeom g{};
+    g.G = heads; g.d = C / heads; g.C = C; g.HW = HW; g.T = T;
+    g.causal = causal ? 1 : 0;
+    g.N = causal ? T : HW;
+    g.tstride = causal ? (long long)HW * C : C;
+    g.nitems = (long long)B * T * HW * heads;  // every (token, head) of the tensor is one query
+    g.scale2 = 1.4426950408889634f / sqrtf((float)g.d);
+    const long long nblk = (g.nitems + 255) / 256;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(attn_generic_kernel, dim3((unsigned)nblk), dim3(256), 0, s, Q, K, V, O, g);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_spatial(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O, int B, int C, int T,
+                          int HW, int heads, hipStream_t s) {
+    using Cf = SpatialAttnCfg<D>;
+    AttnGeom g{};
+    g.N = HW; g.C = C; g.G = heads;
+    g.nqt = (HW + Cf::QT - 1) / Cf::QT;
+    const long long ntiles = (long long)B * T * heads * g.nqt;
+    if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
+    g.ntiles = (int)ntiles;
+    g.per_xcd = (int)((ntiles + 7) / 8);
+    g.ext = ((HW - 1) * C + D) * 2;
+    g.scale2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+    hipLaunchKernelGGL(attn_spatial_kernel<D>, dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, Q, K, V, O, g);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H,
                               int W, int heads, int axis, hipStream_t s) {
     const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -603,20 +767,15 @@ hipError_t launch_attention3d(const void* q, const void* k, const void* v, void*
     uint16_t* O = static_cast<uint16_t*>(out);
     const int d = C / heads, HW = H * W;
     if (axis == CVT_ATTN_SPATIAL) {
-        if (d != AD) return hipErrorInvalidValue;
-        AttnGeom g{};
-        g.N = HW; g.C = C; g.G = heads;
-        g.nqt = (HW + AQT - 1) / AQT;
-        const long long ntiles = (long long)B * T * heads * g.nqt;
-        if (ntiles > 0x7ffffff0LL) return hipErrorInvalidConfiguration;
-        g.ntiles = (int)ntiles;
-        g.per_xcd = (int)((ntiles + 7) / 8);
-        g.ext = ((HW - 1) * C + AD) * 2;
-        g.scale2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-        hipLaunchKernelGGL(attn_spatial_kernel, dim3((unsigned)(8LL * g.per_xcd)), dim3(256), 0, s, Q, K, V, O, g);
-        return hipGetLastError();
+        switch (d) {
+            case 32: return launch_spatial<32>(Q, K, V, O, B, C, T, HW, heads, s);
+            case 64: return launch_spatial<64>(Q, K, V, O, B, C, T, HW, heads, s);
+            case 128: return launch_spatial<128>(Q, K, V, O, B, C, T, HW, heads, s);
+            default: return launch_attention_generic(Q, K, V, O, B, C, T, HW, heads, false, s);
+        }
     }
-    if (T * C > attention_max_tc()) return hipErrorInvalidValue;
+    if ((d != 32 && d != 64) || (long long)T * C > attention_max_tc())
+        return launch_attention_generic(Q, K, V, O, B, C, T, HW, heads, true, s);
     const long long fsb = (long long)HW * C * 2;         // bytes between frames
     const long long ext = (long long)(T - 1) * fsb + 64 * 2;  // a sequence's buffer extent
     const long long nseq = (long long)B * HW * heads;

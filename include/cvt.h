@@ -348,8 +348,14 @@ int cvt_causal_conv3d_temporal_stream(const void* x, const void* hist, const voi
  * Errors: CVT_E_NULL for a NULL tensor; CVT_E_ALIGN unless all four are
  * 16-byte aligned; CVT_E_LAYOUT for an unknown axis; CVT_E_SHAPE for a
  * non-positive size, heads not dividing C, C not a multiple of 8 or above
- * 4096, a head dim other than 64 (spatial) or 32 / 64 (temporal), or, for the
- * temporal axis, T * C above 16384 (K and V of one position must fit in LDS).
+ * 4096, a head dim d = C / heads that is not a multiple of 8 or above 256, or
+ * a frame of H * W * C elements of 2^30 or more.
+ * Kernels: spatial head dims 32, 64 and 128 run tiled flash attention on the
+ * matrix cores; temporal head dim 64 with T <= 32 one MFMA block per
+ * sequence, head dims 32 and 64 with T * C <= 16384 an LDS-staged kernel;
+ * every other shape (any head dim up to 256, any T) a one-thread-per-query
+ * kernel reading global memory, with the same numerics except that its
+ * probabilities stay float32.
  */
 enum { CVT_ATTN_SPATIAL = 0, CVT_ATTN_TEMPORAL_CAUSAL = 1 };
 int cvt_attention3d(const void* q, const void* k, const void* v, void* out, int B, int C, int T, int H, int W,

@@ -176,14 +176,14 @@ def test_attention_validation():
     assert call(o=None) == E_NULL
     assert call(axis=2) == E_LAYOUT
     assert call(heads=3) == E_SHAPE           # does not divide 256
-    assert call(heads=2) == E_SHAPE           # spatial head dim 128
-    assert call(heads=2, axis=1) == E_SHAPE   # temporal head dim 128
+    assert call(heads=64) == E_SHAPE          # head dim 4: not a multiple of 8
+    assert call(C=512, heads=1) == E_SHAPE    # head dim 512 above 256
     assert call(C=260, heads=4) == E_SHAPE    # C not a multiple of 8
-    assert call(T=65, axis=1) == E_SHAPE      # T * C above 16384
     assert call(H=0) == E_SHAPE
+    assert call(H=4096, W=1024) == E_SHAPE    # a frame of 2^30 elements
     assert call(q=MIS) == E_ALIGN
     assert call(o=ctypes.c_void_p(0x400008)) == E_ALIGN
-    assert b"head dim" in (call(heads=2) and lib.cvt_last_error())
+    assert b"head dim" in (call(heads=64) and lib.cvt_last_error())
 
 
 def test_temporal_stream_validation():

@@ -33,6 +33,12 @@ SPATIAL = [
     (1, 256, 2, 24, 20, 4, 1.0),    # 480 tokens: 8 key blocks, 2 query tiles
     (1, 64, 1, 40, 40, 1, 3.0),     # 1600 tokens, sharp softmax (scores ~ N(0, 9))
     (1, 192, 1, 7, 9, 3, 2.0),      # 63 tokens, 3 heads
+    (1, 64, 2, 9, 15, 2, 1.0),      # head dim 32: 135 tokens, ragged key block and query tile
+    (1, 128, 1, 40, 40, 4, 3.0),    # head dim 32, sharp softmax
+    (2, 128, 2, 10, 13, 1, 1.0),    # head dim 128: 130 tokens, 32 queries per wave
+    (1, 256, 1, 24, 25, 2, 2.0),    # head dim 128: 600 tokens, 10 key blocks
+    (1, 48, 2, 6, 11, 3, 1.0),      # head dim 16: the one-thread-per-query kernel
+    (1, 192, 1, 9, 9, 1, 1.0),      # head dim 192: three 64-channel output slices
 ]
 
 
@@ -53,6 +59,9 @@ TEMPORAL = [
     (1, 256, 16, 8, 12, 4, 2.0),
     (1, 64, 31, 5, 5, 2, 1.0),       # head dim 32, 31 frames
     (1, 256, 64, 3, 3, 4, 1.0),      # T * C at the 16384 limit: one position per workgroup
+    (1, 512, 40, 3, 4, 8, 1.0),      # T * C = 20480 beyond the LDS tile: one-thread-per-query kernel
+    (2, 256, 17, 4, 5, 2, 2.0),      # head dim 128: one-thread-per-query kernel
+    (1, 120, 9, 5, 6, 5, 1.0),       # head dim 24
 ]
 
 
@@ -131,10 +140,28 @@ def test_token_grid_full_size_sampled():
     assert_rel(sub(g_tm), ref_t, TOL, "temporal sampled")
 
 
+def test_generic_temporal_causality_and_single_frame_bit_exact():
+    """The one-thread-per-query kernel (here head dim 128): a later frame's change leaves
+    every earlier frame's output unchanged, and a one-frame clip returns v."""
+    shape = (1, 256, 10, 4, 6)
+    (q, _), (k, _), (v, _) = qkv(shape, 520)
+    base = to_bits(cvt.attention3d(q, k, v, 2, "temporal"))
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 6:] = -k2[:, :, 6:]
+    v2[:, :, 6:] = 2 * v2[:, :, 6:]
+    pert = to_bits(cvt.attention3d(q, k2, v2, 2, "temporal"))
+    assert np.array_equal(base[:, :, :6], pert[:, :, :6])
+    assert not np.array_equal(base[:, :, 6:], pert[:, :, 6:])
+    (q1, _), (k1, _), (v1, _) = qkv((1, 256, 1, 4, 6), 525)
+    o1 = cvt.attention3d(q1, k1, v1, 2, "temporal")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(o1), to_bits(v1))
+
+
 def test_invalid_arguments_raise():
     (q, _), (k, _), (v, _) = qkv((1, 128, 2, 4, 4), 530)
     with pytest.raises(cvt.CvtError):
-        cvt.attention3d(q, k, v, 1, "spatial")       # head dim 128
+        cvt.attention3d(q, k, v, 32, "spatial")      # head dim 4: not a multiple of 8
     with pytest.raises(cvt.CvtError):
         cvt.attention3d(q, k, v, 3, "temporal")      # 3 does not divide 128
     with pytest.raises(ValueError):
