@@ -1,10 +1,12 @@
 """The route bench.py times, at the full sizes it times it on, against the float64 oracle.
 
 The 49-frame DV8x16x16-720p-shaped step runs Haar, the spatial conv on its own
-(causal_conv3d_fact with w_t = None) and then the causal temporal conv with the
-1x1 -> 6 projection in its epilogue (causal_conv3d_fact_proj with w_s = None) and FSQ;
-the 121-frame CV8x8x8-720p-shaped chain runs Haar, spatial, temporal, spatial, and the
-temporal conv with the 1x1 -> 16 fused.  Each call is checked stage by stage on whole
+(causal_conv3d_fact_packed with pw_t = None, on weights packed once as the benchmark
+packs them) and then the causal temporal conv with the 1x1 -> 6 projection in its
+epilogue (causal_conv3d_fact_proj_packed with pw_s = None) and FSQ; the 121-frame
+CV8x8x8-720p-shaped chain runs Haar, spatial, temporal, spatial, and the temporal conv
+with the 1x1 -> 16 fused, all on packed weights.  The calls that repack per call use the
+same kernels and are bit-identical (tests/test_gpu_packed.py).  Each call is checked stage by stage on whole
 latent frames (every column and channel tile of the frame), each stage's oracle taking
 the GPU's actual input to that stage (its bf16 bits): the spatial conv on the frame,
 the temporal conv on the frame and its two predecessors, its output rounded to bf16 (the
@@ -73,9 +75,10 @@ def test_dv8x16x16_720p_timed_route_full_frames():
     w_s, ws64 = _w((256, 192, 1, 3, 3), si.weight_seed(cid, 0))
     w_t, wt64 = _w((256, 256, 3, 1, 1), si.weight_seed(cid, 1))
     w_p, wp64 = _w((6, 256, 1, 1, 1), si.weight_seed(cid, 2))
+    pw_s, pw_t, pw_p = cvt.conv_weights_pack(w_s), cvt.conv_weights_pack(w_t), cvt.conv_weights_pack(w_p)
     hz = cvt.haar3d_fwd(x)
-    s1 = cvt.causal_conv3d_fact(hz, w_s, None)
-    lat = cvt.causal_conv3d_fact_proj(s1, None, w_t, w_p)
+    s1 = cvt.causal_conv3d_fact_packed(hz, pw_s, None)
+    lat = cvt.causal_conv3d_fact_proj_packed(s1, None, pw_t, pw_p)
     idx = cvt.fsq_quantize(lat)
     torch.cuda.synchronize()
     assert tuple(lat.shape) == (1, 6, 13, 180, 320)
@@ -120,12 +123,13 @@ def test_cv8x8x8_720p_timed_route_full_frames():
         _w(shape, si.weight_seed(cid, i)) for i, shape in enumerate([(256, 192, 1, 3, 3), (256, 256, 3, 1, 1),
                                                                      (256, 256, 1, 3, 3), (256, 256, 3, 1, 1)])]
     w_p, wp64 = _w((16, 256, 1, 1, 1), si.weight_seed(cid, 4))
+    p1s, p1t, p2s, p2t, pp = (cvt.conv_weights_pack(w) for w in (w1s, w1t, w2s, w2t, w_p))
     hz = cvt.haar3d_fwd(x)
     del x
-    a1 = cvt.causal_conv3d_fact(hz, w1s, None)
-    b1 = cvt.causal_conv3d_fact(a1, None, w1t)
-    a2 = cvt.causal_conv3d_fact(b1, w2s, None)
-    lat = cvt.causal_conv3d_fact_proj(a2, None, w2t, w_p)
+    a1 = cvt.causal_conv3d_fact_packed(hz, p1s, None)
+    b1 = cvt.causal_conv3d_fact_packed(a1, None, p1t)
+    a2 = cvt.causal_conv3d_fact_packed(b1, p2s, None)
+    lat = cvt.causal_conv3d_fact_proj_packed(a2, None, p2t, pp)
     torch.cuda.synchronize()
     assert tuple(lat.shape) == (1, 16, 31, 180, 320)
     frames = (0, 1, 27, 28, 30)
