@@ -667,9 +667,11 @@ def decode_c5(cvt, si, torch, dev, args):
     xo = torch.empty(wl["out_x"], dtype=torch.bfloat16, device=dev)
     ws = torch.empty(cvt.conv_workspace_bytes(z.shape, 192, 3, True, True), dtype=torch.uint8, device=dev)
     ws1 = torch.empty(cvt.conv_workspace_bytes(codes.shape, 192, 1, True, False), dtype=torch.uint8, device=dev)
+    pw_s, pw_t = cvt.conv_weights_pack(w_s), cvt.conv_weights_pack(w_t)  # fixed weights: packed once
+    ws_pk = torch.empty(cvt.conv_packed_workspace_bytes(z.shape, 192), dtype=torch.uint8, device=dev)
     stages = {
         "dequantize_proj": lambda: cvt.fsq_dequantize_proj(idx, lift, out=z),
-        "conv_192_192": lambda: cvt.causal_conv3d_fact(z, w_s, w_t, workspace=ws, out=yc),
+        "conv_192_192": lambda: cvt.causal_conv3d_fact_packed(z, pw_s, pw_t, workspace=ws_pk, out=yc),
         "haar_inv": lambda: cvt.haar3d_inv(yc, out=xo),
     }
     unfused = lambda: (cvt.fsq_dequantize(idx, out=codes), cvt.causal_conv3d_fact(codes, lift, None, workspace=ws1,
@@ -706,7 +708,9 @@ def decode_c5(cvt, si, torch, dev, args):
         ws_fz = torch.empty(cvt.fsq_dequantize_conv3d_fact_workspace_bytes(idx.shape, 192, 192, True),
                             dtype=torch.uint8, device=dev)
         yf = torch.empty_like(yc)
-        unf, fus = interleaved(torch, [lambda: (stages["dequantize_proj"](), stages["conv_192_192"]()),
+        # both routes repack their weights per call (there is no packed form of the fused call)
+        unf, fus = interleaved(torch, [lambda: (stages["dequantize_proj"](),
+                                                cvt.causal_conv3d_fact(z, w_s, w_t, workspace=ws, out=yc)),
                                        lambda: cvt.fsq_dequantize_conv3d_fact(idx, lift, w_s, w_t, workspace=ws_fz,
                                                                               out=yf)],
                                max(3, args.steps // 4))
@@ -715,7 +719,7 @@ def decode_c5(cvt, si, torch, dev, args):
                          "frames_per_s_fused_route": round(out["out_frames"] /
                                                            ((fus + out["haar_inv"]["ms"]) * 1e-3), 1)}
         del ws_fz, yf
-    del idx, z, yc, codes, xo, ws, ws1
+    del idx, z, yc, codes, xo, ws, ws1, ws_pk
     torch.cuda.empty_cache()
     return out
 
