@@ -854,7 +854,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                 bv[a][q][e] = bias ? bias[min(n, g.Cout - 1)] : 0.0f;
             }
 
-    if constexpr (epi_proj<EPI>() || EPI == EPI_NORM) {
+    if constexpr (epi_proj<EPI>()) {
         // Epilogues over whole position rows (temporal kernel with every output channel in the
         // workgroup).  The tile's conv outputs, bias added and rounded to bf16 once (what a
         // separate pass would read), are staged in LDS as [frame][column][channel] rows, and
@@ -892,87 +892,6 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                         *reinterpret_cast<uint2*>(smem + (ry * NC + wpos * 32 * FB + cb * 32 + px) * PRS + n * 2) = u;
                     }
         __syncthreads();
-        if constexpr (EPI == EPI_NORM) {
-            // LayerNorm over the Cout channels of each staged column, then the per-channel scale
-            // and shift and (optionally) Swish.  Lane (px, khalf) sums half of the channels of
-            // column px and the halves meet through one cross-lane exchange: the mean first,
-            // then the centred squares (a second pass over LDS).  The results are written as
-            // whole position rows, 16-byte chunks of consecutive lanes.
-            constexpr int HALF = TCH / 2;
-            constexpr int NBLK = NC / 32;
-            const int Cout = g.Cout, cpr = Cout >> 3;  // 16-byte chunks per position row
-            const float inv_n = 1.0f / (float)Cout;
-            const int nit = (32 * cpr + 63) >> 6;
-            // a lane's channel chunk is lane % cpr in every store step when cpr divides 64 (C =
-            // 64, 128, 256): its scale and shift are then loaded once
-            const bool fixed_ch = (64 % cpr) == 0;
-            float gg[8], bb[8];
-            auto load_affine = [&](int ch) {
-                const float4 g0 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8);
-                const float4 g1 = *reinterpret_cast<const float4*>(aux.ln_g + ch * 8 + 4);
-                const float4 b0 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8);
-                const float4 b1 = *reinterpret_cast<const float4*>(aux.ln_b + ch * 8 + 4);
-                gg[0] = g0.x; gg[1] = g0.y; gg[2] = g0.z; gg[3] = g0.w;
-                gg[4] = g1.x; gg[5] = g1.y; gg[6] = g1.z; gg[7] = g1.w;
-                bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
-                bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-            };
-            if (fixed_ch) load_affine(lane % cpr);
-            for (int pr = wave; pr < NV * NBLK; pr += C::NW) {  // wave-uniform
-                const int fr = pr / NBLK, cblk = pr % NBLK;
-                const uint8_t* col = smem + (fr * NC + cblk * 32) * PRS;
-                const uint8_t* mine = col + px * PRS + khalf * HALF * 2;
-                float sum = 0.0f;
-#pragma unroll
-                for (int c8 = 0; c8 < HALF / 8; ++c8) {  // channels past Cout are staged zeros
-                    const uint4 v = *reinterpret_cast<const uint4*>(mine + c8 * 16);
-                    sum += (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
-                           (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
-                }
-                sum += __shfl_xor(sum, 32);
-                const float mean = sum * inv_n;
-                float sq = 0.0f;
-#pragma unroll
-                for (int c8 = 0; c8 < HALF / 8; ++c8) {
-                    if (khalf * HALF + c8 * 8 < Cout) {
-                        const uint4 v = *reinterpret_cast<const uint4*>(mine + c8 * 16);
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const float d0 = bf16_lo(w[k]) - mean, d1 = bf16_hi(w[k]) - mean;
-                            sq += d0 * d0 + d1 * d1;
-                        }
-                    }
-                }
-                sq += __shfl_xor(sq, 32);
-                const float rstd = rsqrtf(sq * inv_n + aux.eps);
-                const int hw0 = c0 + cblk * 32;
-                const long long pbase = ((long long)b * g.T + r0 + fr) * g.HW + hw0;
-                for (int it = 0; it < nit; ++it) {  // wave-uniform trip count
-                    const int f = it * 64 + lane;
-                    const int pc = f / cpr, ch = f - pc * cpr;
-                    const float m = __shfl(mean, pc & 31), r = __shfl(rstd, pc & 31);
-                    if (pc < 32 && hw0 + pc < g.HW) {
-                        const uint4 v = *reinterpret_cast<const uint4*>(col + pc * PRS + ch * 16);
-                        if (!fixed_ch) load_affine(ch);
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                        uint32_t o[4];
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            float y0 = (bf16_lo(w[k]) - m) * r * gg[2 * k] + bb[2 * k];
-                            float y1 = (bf16_hi(w[k]) - m) * r * gg[2 * k + 1] + bb[2 * k + 1];
-                            if (aux.swish) {
-                                y0 = swish_f(y0);
-                                y1 = swish_f(y1);
-                            }
-                            o[k] = pack_bf16x2(y0, y1);
-                        }
-                        *reinterpret_cast<uint4*>(Y + (pbase + pc) * Cout + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-                    }
-                }
-            }
-            return;
-        }
         const int Cp = g.Cp;
         float bp[8];
 #pragma unroll
@@ -1062,6 +981,106 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     static_assert(C::NW * STAGE <= (EPI == EPI_RES ? C::RES_BYTES : C::REGION_BYTES),
                   "epilogue staging fits in the LDS buffer");
     uint8_t* stage = smem + wave * STAGE;
+
+    // NORM: LayerNorm over the Cout channels of every output position, then the per-channel
+    // scale and shift and (optionally) Swish, applied to the float32 sums (bias added) before
+    // the single bf16 rounding of the staging below.  A position's channels are spread over
+    // the WCH waves of its column block and, within a wave, over the two lane halves; two
+    // reductions through LDS (past the staging area) give the mean and then the sum of
+    // squared deviations from it.  Every lane sums the WCH partials in the same order, so all
+    // channels of a position use the same statistics.
+    // per position (frame, column block): nr = 1 / sqrt(variance + eps), nm = -mean * nr
+    float nm[EPI == EPI_NORM ? NV : 1][FB], nr[EPI == EPI_NORM ? NV : 1][FB];
+    float4 lg[EPI == EPI_NORM ? FA : 1][4], lb[EPI == EPI_NORM ? FA : 1][4];
+    if constexpr (EPI == EPI_NORM) {
+        constexpr int NC = C::NC, RED = WCH * C::R * NC;  // floats per reduction array
+        static_assert(C::NW * STAGE + 2 * RED * 4 <= C::REGION_BYTES, "norm reductions fit in the LDS buffer");
+        float* red1 = reinterpret_cast<float*>(smem + C::NW * STAGE);
+        float* red2 = red1 + RED;
+        const float inv_n = 1.0f / (float)g.Cout;
+        bool vq[FA][4];  // Cout % 8 == 0: the 4 channels of a group are all valid or all not
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = (ab0 + a) * 32 + 8 * q + 4 * khalf;
+                vq[a][q] = n < g.Cout;
+                lg[a][q] = vq[a][q] ? *reinterpret_cast<const float4*>(aux.ln_g + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+                lb[a][q] = vq[a][q] ? *reinterpret_cast<const float4*>(aux.ln_b + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        // the bias joins the sums once, here
+#pragma unroll
+        for (int ry = 0; ry < NV; ++ry)
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int cb = 0; cb < FB; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[ry][a][cb][4 * q + e] += bv[a][q][e];
+        auto slot = [&](int w, int ry, int cb) { return (w * C::R + ry) * NC + wpos * 32 * FB + cb * 32 + px; };
+        // the sum over the lane's valid channels and its partner lane's: of the values for
+        // the mean, of their squared deviations from m for the variance
+        auto partial = [&](int ry, int cb, float m, bool squares) {
+            float acc_s = 0.0f;
+#pragma unroll
+            for (int a = 0; a < FA; ++a)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (vq[a][q]) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = acc[ry][a][cb][4 * q + e];
+                            acc_s = squares ? fmaf(v - m, v - m, acc_s) : acc_s + v;
+                        }
+                    }
+            return acc_s + __shfl_xor(acc_s, 32);
+        };
+#pragma unroll
+        for (int ry = 0; ry < NV; ++ry)
+#pragma unroll
+            for (int cb = 0; cb < FB; ++cb) {
+                const float ps = partial(ry, cb, 0.0f, false);
+                if (khalf == 0) red1[slot(wch, ry, cb)] = ps;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int ry = 0; ry < NV; ++ry)
+#pragma unroll
+            for (int cb = 0; cb < FB; ++cb) {
+                float t = 0.0f;
+                for (int w = 0; w < WCH; ++w) t += red1[slot(w, ry, cb)];
+                nm[ry][cb] = t * inv_n;
+                const float ps = partial(ry, cb, nm[ry][cb], true);
+                if (khalf == 0) red2[slot(wch, ry, cb)] = ps;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int ry = 0; ry < NV; ++ry)
+#pragma unroll
+            for (int cb = 0; cb < FB; ++cb) {
+                float t = 0.0f;
+                for (int w = 0; w < WCH; ++w) t += red2[slot(w, ry, cb)];
+                nr[ry][cb] = rsqrtf(t * inv_n + aux.eps);
+                nm[ry][cb] *= -nr[ry][cb];  // (v - mean) * rstd = fma(v, rstd, -mean * rstd)
+            }
+    }
+    // the staged value of accumulator element e of group (a, q): the sum with its bias, and for
+    // NORM normalised, scaled, shifted and passed through Swish
+    auto outv = [&](const f32x16_t& c, int ry, int a, int cb, int q, int e) {
+        float v;
+        if constexpr (EPI == EPI_NORM) {  // the bias is already in c
+            const float4 gq = lg[a][q], bq = lb[a][q];
+            const float gv = e == 0 ? gq.x : e == 1 ? gq.y : e == 2 ? gq.z : gq.w;
+            const float bw = e == 0 ? bq.x : e == 1 ? bq.y : e == 2 ? bq.z : bq.w;
+            v = fmaf(fmaf(c[4 * q + e], nr[ry][cb], nm[ry][cb]), gv, bw);
+            if (aux.swish) v = swish_f(v);
+        } else {
+            v = c[4 * q + e] + bv[a][q][e];
+        }
+        return v;
+    };
     const int nb = (ab0 * 32) * 2;  // byte offset of this wave's first channel in a position row
     constexpr int CPP = 4 * FA;   // 16-byte output chunks per position slice
     constexpr int PPI = 64 / CPP;  // positions per store instruction
@@ -1110,8 +1129,8 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
                                                                       c[4 * q + 3] + bv[a][q][3]);
                     } else {
                         uint2 u;
-                        u.x = pack_bf16x2(c[4 * q] + bv[a][q][0], c[4 * q + 1] + bv[a][q][1]);
-                        u.y = pack_bf16x2(c[4 * q + 2] + bv[a][q][2], c[4 * q + 3] + bv[a][q][3]);
+                        u.x = pack_bf16x2(outv(c, ry, a, cb, q, 0), outv(c, ry, a, cb, q, 1));
+                        u.y = pack_bf16x2(outv(c, ry, a, cb, q, 2), outv(c, ry, a, cb, q, 3));
                         *reinterpret_cast<uint2*>(dst) = u;
                     }
                 }
@@ -1165,7 +1184,7 @@ __global__ __launch_bounds__(C::NTH) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint16_t* __restrict__ Hx, RowsGeom g, RowsAux aux) {
     constexpr int KIND = C::KIND;
     // the region buffers; the fused projection's partial sums reuse them after the K loop
-    __shared__ __attribute__((aligned(16))) uint8_t smem[(epi_proj<EPI>() || EPI == EPI_NORM) ? std::max(C::REGION_BYTES, C::PROJ_BYTES)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[epi_proj<EPI>() ? std::max(C::REGION_BYTES, C::PROJ_BYTES)
                                                                       : EPI == EPI_RES ? std::max(C::REGION_BYTES, C::RES_BYTES)
                                                                                        : C::REGION_BYTES + (C::SRC == SRC_FSQ ? LIFT_BYTES : 0)];
 
