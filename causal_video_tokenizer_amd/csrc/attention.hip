@@ -453,7 +453,8 @@ __global__ __launch_bounds__(256) void attn_temporal_kernel(const uint16_t* __re
 // keys after the query's frame are masked, the softmax runs over the lane's query column
 // as in the spatial kernel, and O^T = V^T P^T takes 2 channel blocks x 2 key k-steps.  V^T
 // goes through a wave-private LDS tile (64 channel rows of 32 keys in the k-step key order,
-// 16-byte padded rows) - the only LDS use, so many waves fit on a CU to hide HBM latency.
+// 16-byte padded rows), Q, K and O through a wave-private tile of frame rows; 9.5 KB of LDS
+// and at most 128 VGPRs per wave up to 24 frames, so 16 waves fit on a CU to hide HBM latency.
 constexpr int TM_VRS = 32 * 2 + 16;  // bytes per V^T row (32 keys)
 constexpr int TM_WAVE_LDS = 64 * TM_VRS;
 
@@ -468,64 +469,93 @@ struct TAttnMGeom {
 // The waves loop over sequences (the grid-stride keeps the four waves of a workgroup on the
 // four heads of one position, i.e. one contiguous 512-byte run per frame and tensor) and
 // issue the next sequence's loads before computing the current one, so every wave keeps
-// loads in flight through its compute phase.
+// loads in flight through its compute phase.  A load instruction covers 8 whole frame rows
+// (8 lanes x 16 bytes = the head's 128 bytes of a frame), NF = ceil(T / 8) per tensor; Q and
+// K reach the MFMA operand layout through the wave's row tile in LDS (frame f at f * 144
+// bytes), V through its V^T tile.
+constexpr int TM_RRS = 64 * 2 + 16;            // bytes per staged frame row (64 channels)
+constexpr int TM_ROWS_LDS = 32 * TM_RRS;       // the wave's Q / K row tile (32 frames)
+template <int NF>
 __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t* __restrict__ Q,
                                                                  const uint16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V,
                                                                  uint16_t* __restrict__ O, TAttnMGeom g) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TM_WAVE_LDS];
+    static_assert(NF >= 1 && NF <= 4, "T <= 32");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * (TM_WAVE_LDS + TM_ROWS_LDS)];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int stride = (int)gridDim.x * 4;
     int sq = (int)blockIdx.x * 4 + wave;
     if (sq >= g.nseq) return;  // wave-uniform; the kernel has no workgroup barrier
     const int px = lane & 31, hh = lane >> 5;
+    const int fr8 = lane >> 3, c8 = lane & 7;  // loads: frame 8 it + fr8, channels 8 c8 .. 8 c8 + 7
     const int per_b = g.HW * g.G;
     auto seq_base = [&](int s) {
         const int b = s / per_b, rem = s - b * per_b;
         const int pos = rem / g.G, head = rem - pos * g.G;
         return ((long long)b * g.T * g.HW + pos) * g.C + head * 64;  // frame 0 token
     };
-    // lane (px, hh): frame px (a key for K and V, a query for Q), channels 16 ks + 8 hh ..
-    // +7; frames past T read zeros (offset past the buffer)
-    const int roff = px < g.T ? px * g.fsb + hh * 16 : 0x7fffff00;
-    // past the last sequence (the final prefetch) every offset is past the buffer: zeros, no
-    // memory access; the loads stay unconditional so that the wait before a sequence's
-    // MFMAs covers only its own loads, not the prefetch issued after them
-    auto load = [&](int s, bf16x8_t (&kf)[4], bf16x8_t (&qf)[4], uint4 (&vr)[4]) {
+    // frames past T, and every offset past the last sequence (the final prefetch), read
+    // zeros from past the buffer with no memory access; the loads stay unconditional so that
+    // the wait before a sequence's MFMAs covers only its own loads, not the prefetch after them
+    auto load = [&](int s, uint4 (&qr)[NF], uint4 (&kr)[NF], uint4 (&vr)[NF]) {
         const bool live = s < g.nseq;
         const long long base = seq_base(live ? s : 0);
-        const int ro = live ? roff : 0x7fffff00;
         const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + base), (short)0, g.ext, 0x00020000);
         const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, g.ext, 0x00020000);
         const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, g.ext, 0x00020000);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            kf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, ro + ks * 32, 0, 0));
-            qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qres, ro + ks * 32, 0, 0));
-            const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, ro + ks * 32, 0, 0);
-            vr[ks] = *reinterpret_cast<const uint4*>(&vv);
+        for (int it = 0; it < NF; ++it) {
+            const int fr = it * 8 + fr8;
+            const int off = live && fr < g.T ? fr * g.fsb + c8 * 16 : 0x7fffff00;
+            const auto qv = __builtin_amdgcn_raw_buffer_load_b128(qres, off, 0, 0);
+            const auto kv = __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0);
+            const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
+            qr[it] = *reinterpret_cast<const uint4*>(&qv);
+            kr[it] = *reinterpret_cast<const uint4*>(&kv);
+            vr[it] = *reinterpret_cast<const uint4*>(&vv);
         }
     };
-    uint8_t* vt = smem + wave * TM_WAVE_LDS;
-    const int col = vperm(px) * 2;
-    bf16x8_t kf[4], qf[4];
-    uint4 vr[4];
-    load(sq, kf, qf, vr);
+    uint8_t* vt = smem + wave * (TM_WAVE_LDS + TM_ROWS_LDS);
+    uint8_t* rt = vt + TM_WAVE_LDS;
+    // frames NF * 8 .. 31 of the row tile and keys past NF * 8 in V^T are never written:
+    // zeros once (keys past T must be finite, their weights are 0)
+    for (int i = lane; i < (TM_WAVE_LDS + TM_ROWS_LDS) / 16; i += 64)
+        reinterpret_cast<uint4*>(vt)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the MFMA operand of a row tile: lane (px, hh) holds frame px, channels 16 ks + 8 hh .. +7
+    auto stage_rows = [&](const uint4 (&r)[NF], bf16x8_t (&f)[4]) {
+#pragma unroll
+        for (int it = 0; it < NF; ++it)
+            *reinterpret_cast<uint4*>(rt + (it * 8 + fr8) * TM_RRS + c8 * 16) = r[it];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            f[ks] = *reinterpret_cast<const bf16x8_t*>(rt + px * TM_RRS + (ks * 16 + hh * 8) * 2);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the reads before the tile's next writes
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    uint4 qr[NF], kr[NF], vr[NF];
+    load(sq, qr, kr, vr);
     for (;;) {
         const int nx = sq + stride;
-        bf16x8_t kn[4], qn[4];
-        uint4 vn[4];
-        load(nx, kn, qn, vn);
-        // V^T into the wave's LDS tile: channel 16 ks + 8 hh + e, key px at its k-step column
-        // (the tile is wave-private and its accesses execute in order: the previous
-        // sequence's reads are done)
+        uint4 qn[NF], kn[NF], vn[NF];
+        load(nx, qn, kn, vn);
+        bf16x8_t qf[4], kf[4];
+        stage_rows(qr, qf);
+        stage_rows(kr, kf);
+        // V^T into the wave's LDS tile: channel 8 c8 + e, key fr at its k-step column (the
+        // tile is wave-private and its accesses execute in order: the previous sequence's
+        // reads are done)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t w[4] = {vr[ks].x, vr[ks].y, vr[ks].z, vr[ks].w};
+        for (int it = 0; it < NF; ++it) {
+            const int col = vperm(it * 8 + fr8) * 2;
+            const uint32_t w[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                const int row = ks * 16 + hh * 8 + 2 * e2;
+                const int row = c8 * 8 + 2 * e2;
                 *reinterpret_cast<uint16_t*>(vt + row * TM_VRS + col) = (uint16_t)(w[e2] & 0xffffu);
                 *reinterpret_cast<uint16_t*>(vt + (row + 1) * TM_VRS + col) = (uint16_t)(w[e2] >> 16);
             }
@@ -577,10 +607,9 @@ __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t*
             }
         }
         {
-            // O rows staged in the wave's tile (frame px at byte px * 144), then written as
-            // 16-byte pieces, 8 lanes per 128-byte frame row
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // O rows staged in the row tile (frame px at byte px * 144), then written as
+            // 16-byte pieces, 8 lanes per 128-byte frame row, with streaming stores (written
+            // once, read by the next layer)
             const float inv = 1.0f / l;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
@@ -589,27 +618,27 @@ __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t*
                     uint2 u;
                     u.x = pack_bf16x2(ot[cb][4 * q4] * inv, ot[cb][4 * q4 + 1] * inv);
                     u.y = pack_bf16x2(ot[cb][4 * q4 + 2] * inv, ot[cb][4 * q4 + 3] * inv);
-                    *reinterpret_cast<uint2*>(vt + px * 144 + (cb * 32 + q4 * 8 + hh * 4) * 2) = u;
+                    *reinterpret_cast<uint2*>(rt + px * TM_RRS + (cb * 32 + q4 * 8 + hh * 4) * 2) = u;
                 }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             uint16_t* obase = O + seq_base(sq);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int fr = it * 8 + (lane >> 3), c8 = lane & 7;
-                const uint4 v = *reinterpret_cast<const uint4*>(vt + fr * 144 + c8 * 16);
-                if (fr < g.T) *reinterpret_cast<uint4*>(obase + (long long)fr * (g.fsb / 2) + c8 * 8) = v;
+            for (int it = 0; it < NF; ++it) {
+                const int fr = it * 8 + fr8;
+                const uint4 v = *reinterpret_cast<const uint4*>(rt + fr * TM_RRS + c8 * 16);
+                if (fr < g.T) st_stream16(obase + (long long)fr * (g.fsb / 2) + c8 * 8, v);
             }
         }
         if (nx >= g.nseq) break;
         sq = nx;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            kf[ks] = kn[ks];
-            qf[ks] = qn[ks];
-            vr[ks] = vn[ks];
+        for (int it = 0; it < NF; ++it) {
+            qr[it] = qn[it];
+            kr[it] = kn[it];
+            vr[it] = vn[it];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // this sequence's V^T reads before the next writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // this sequence's tile reads before the next writes
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
@@ -786,10 +815,16 @@ hipError_t launch_attention3d(const void* q, const void* k, const void* v, void*
         g.fsb = (int)fsb;
         g.ext = (int)ext;
         g.scale2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-        // persistent: three workgroups per CU (the occupancy its registers allow), each wave prefetching
-        // its next sequence
-        const long long nwg = std::min((nseq + 3) / 4, 256LL * 3);
-        hipLaunchKernelGGL(attn_temporal_mfma_kernel, dim3((unsigned)nwg), dim3(256), 0, s, Q, K, V, O, g);
+        // persistent, each wave prefetching its next sequence: as many workgroups per CU as the
+        // registers allow (up to 24 frames 128 VGPRs or fewer: four; 32 frames: three)
+        const long long nwg = std::min((nseq + 3) / 4, 256LL * (T <= 24 ? 4 : 3));
+        const dim3 grid((unsigned)nwg), block(256);
+        switch ((T + 7) / 8) {
+            case 1: hipLaunchKernelGGL(attn_temporal_mfma_kernel<1>, grid, block, 0, s, Q, K, V, O, g); break;
+            case 2: hipLaunchKernelGGL(attn_temporal_mfma_kernel<2>, grid, block, 0, s, Q, K, V, O, g); break;
+            case 3: hipLaunchKernelGGL(attn_temporal_mfma_kernel<3>, grid, block, 0, s, Q, K, V, O, g); break;
+            default: hipLaunchKernelGGL(attn_temporal_mfma_kernel<4>, grid, block, 0, s, Q, K, V, O, g); break;
+        }
         return hipGetLastError();
     }
     switch (d) {
