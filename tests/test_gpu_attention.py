@@ -56,6 +56,8 @@ TEMPORAL = [
     # B, C, T, H, W, heads, q_std
     (1, 64, 5, 6, 7, 1, 1.0),
     (2, 128, 16, 9, 11, 2, 1.0),     # 99 positions: ragged last position tile
+    (1, 128, 23, 5, 7, 2, 1.0),      # 23 frames: three 8-frame row loads per tensor
+    (1, 256, 32, 4, 6, 4, 1.5),      # 32 frames: the matrix-core kernel's largest T
     (1, 256, 16, 8, 12, 4, 2.0),
     (1, 64, 31, 5, 5, 2, 1.0),       # head dim 32, 31 frames
     (1, 256, 64, 3, 3, 4, 1.0),      # T * C at the 16384 limit: one position per workgroup
