@@ -46,8 +46,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // Spatial attention, head dim D in {32, 64, 128}.  Workgroup = 4 waves x 32 QB queries
 // (QB 32-query MFMA column blocks per wave: 2 up to D = 64, 1 at D = 128, whose
 // accumulators are twice as many) of one (clip, frame, head) sequence; the keys go by in
-// blocks of 64, staged in LDS (K rows [key][D channels], V^T rows [channel][64 keys],
-// 16-byte padded rows, two buffers), loaded during the previous block.  Per block and wave:
+// blocks of 64, staged in LDS (K rows [key][D channels], V^T rows [channel][64 keys] with
+// their 16-byte chunks swizzled, 16-byte padded rows, two buffers), loaded during the
+// previous block.  Per block and wave:
 // 2 key blocks x QB query blocks x D/16 channel k-steps MFMAs for S^T and D/32 channel
 // blocks x QB query blocks x 4 key k-steps for O^T.
 constexpr int AKB = 64;              // keys per block
@@ -66,6 +67,11 @@ struct SpatialAttnCfg {
     static constexpr int KL = AKB * CPK / 256;   // K chunks per thread and block
     static constexpr int VI = 32 * CPK;          // V items: (key pair, chunk)
     static constexpr int VL = (VI + 255) / 256;  // V items per thread
+    // V^T rows are swizzled in 16-byte chunks: row r keeps chunk k at k ^ (((r / 16) * SW) % 8),
+    // which makes both the staging writes (4-byte key pairs of 8 channels per lane) and the
+    // fragment reads (16 rows per 16 lanes) free of bank conflicts (d = 32, 64; d = 128: the
+    // writes 2-way instead of 8-way)
+    static constexpr int SW = D == 32 ? 4 : 2;
 };
 
 struct AttnGeom {
@@ -164,7 +170,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 // V^T: channel c * 8 + e gets the pair (key 2 p, key 2 p + 1) at its permuted column
                 const uint32_t a[4] = {vst[r][0].x, vst[r][0].y, vst[r][0].z, vst[r][0].w};
                 const uint32_t b[4] = {vst[r][1].x, vst[r][1].y, vst[r][1].z, vst[r][1].w};
-                const int col = vperm(2 * p) * 2;
+                // byte column of the key pair, its 16-byte chunk swizzled by the rows' group (all
+                // 8 rows c * 8 .. c * 8 + 7 of the chunk lie in one 16-row group)
+                const int col = (vperm(2 * p) * 2) ^ ((((c >> 1) * Cf::SW) & 7) << 4);
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     // channels 2 e2 and 2 e2 + 1 of the chunk: low halves, then high halves
@@ -194,6 +202,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     // per-lane byte offsets of the K and V^T fragments within a buffer; every fragment is
     // this plus a compile-time offset
     const int klane = px * KRS + hh * 16, vlane = KBUF + px * AVRS + hh * 16;
+    // V^T fragment (channel block cb, keys 32 kb + 16 h2 + 8 hh ..): row cb * 32 + px, chunk
+    // 4 kb + 2 h2 + hh swizzled by ((row / 16) * SW) % 8 = (cb * 2 SW) % 8 ^ (px / 16) SW
+    // (even: the lane's hh bit stays); vsw[j] = byte offset of chunk pair 2 j after the lane's part
+    int vsw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vsw[j] = ((2 * j) ^ (((px >> 4) * Cf::SW) & 7)) * 16;
+    auto vfrag = [&](const uint8_t* vb, int cb, int kb, int h2) {  // vb: the buffer's base + vlane
+        const int k2 = (4 * kb + 2 * h2) ^ ((cb * 2 * Cf::SW) & 7);  // compile-time
+        return *reinterpret_cast<const bf16x8_t*>(vb + cb * 32 * AVRS + vsw[k2 >> 1]);
+    };
 
     // One key block.  MASKED (the last block when N is not a multiple of 64): keys past N
     // get a score of -inf.  A compile-time flag, so that the full blocks carry no mask code.
@@ -279,8 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        const bf16x8_t vf =
-                            *reinterpret_cast<const bf16x8_t*>(vbase + cb * 32 * AVRS + (kb * 32 + h2 * 16) * 2);
+                        const bf16x8_t vf = vfrag(vbase, cb, kb, h2);
                         o[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][h2], o[cb][qb], 0, 0, 0);
                     }
         }
