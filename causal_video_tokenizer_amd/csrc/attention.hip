@@ -568,7 +568,9 @@ __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t*
         // reads are done)
 #pragma unroll
         for (int it = 0; it < NF; ++it) {
-            const int col = vperm(it * 8 + fr8) * 2;
+            // rows 16 .. 31 and 48 .. 63 (channel groups c8 = 2, 3, 6, 7) keep their two 32-byte
+            // halves swapped: the 2-byte writes of a store then spread over twice the banks
+            const int col = (vperm(it * 8 + fr8) * 2) ^ (((c8 >> 1) & 1) << 5);
             const uint32_t w[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(256) void attn_temporal_mfma_kernel(const uint16_t*
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const bf16x8_t vf =
-                    *reinterpret_cast<const bf16x8_t*>(vt + (cb * 32 + px) * TM_VRS + (h2 * 16 + hh * 8) * 2);
+                    *reinterpret_cast<const bf16x8_t*>(vt + (cb * 32 + px) * TM_VRS + ((h2 ^ (px >> 4)) * 16 + hh * 8) * 2);
                 ot[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h2], ot[cb], 0, 0, 0);
             }
         }
