@@ -967,13 +967,15 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
     // Bias, bf16 RNE, staged per output row through a wave-private LDS tile of 32 FB columns
     // x 32 FA channels (rows of 64 FA bytes + 16 bytes of padding, so the 8-byte writes of 8
     // consecutive columns hit distinct banks), then written back with each 4 FA consecutive
-    // lanes storing one position's 64 FA contiguous bytes.  The region buffers are free after
+    // lanes storing one position's 64 FA contiguous bytes, as streaming (non-temporal) stores:
+    // the output is not read again by this kernel (identical output; 1.8-2.3% faster than plain
+    // stores per 720p layer, 0.3-0.8% over a chain of layers, whose next layer reads it).  The region buffers are free after
     // the last barrier of the K loop; a wave reads back only what it wrote and its LDS
     // accesses execute in order, so no barrier is needed.
     // RES stages the float32 sums instead (rows of 128 FA + 16 bytes) and adds the residual in
     // the store step, where each lane's 16 residual bytes sit at its store's offset (one
-    // coalesced load per store, all of a frame's requested before its staging) before the
-    // single bf16 rounding.  A wave reads only the residual chunks it overwrites itself, each
+    // coalesced load per store, all of the tile's requested before the first staging) before
+    // the single bf16 rounding.  A wave reads only the residual chunks it overwrites itself, each
     // before its store, so the output may be the residual tensor.
     constexpr int ES = EPI == EPI_RES ? 4 : 2;  // staged element bytes
     constexpr int OS = 32 * FA * ES + 16;
@@ -1102,19 +1104,23 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
         }
         return ok && n < g.Cout;  // Cout is a multiple of 8 on this path (checked by the launcher)
     };
-    // RES: a frame's residual chunks are requested before its staging (unconditional loads, a
-    // stored position's chunk or the tensor's first one), so their latency overlaps the LDS work
-    uint4 rv[EPI == EPI_RES ? NIT : 1];
+    // RES: the residual chunks of every frame of the tile are requested at once, before any
+    // staging (unconditional loads, a stored position's chunk or the tensor's first one), so the
+    // tile waits for one HBM round trip instead of one per frame; the operand registers of the K
+    // loop are free by now.
+    uint4 rv[EPI == EPI_RES ? NV : 1][EPI == EPI_RES ? NIT : 1];
+    if constexpr (EPI == EPI_RES) {
 #pragma unroll
-    for (int ry = 0; ry < NV; ++ry) {
-        if constexpr (EPI == EPI_RES) {
+        for (int ry = 0; ry < NV; ++ry)
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 long long pos;
                 const bool ok = out_pos(ry, it, pos);
-                rv[it] = *reinterpret_cast<const uint4*>(aux.res + (ok ? pos * g.Cout + n : 0));
+                rv[ry][it] = *reinterpret_cast<const uint4*>(aux.res + (ok ? pos * g.Cout + n : 0));
             }
-        }
+    }
+#pragma unroll
+    for (int ry = 0; ry < NV; ++ry) {
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
@@ -1145,7 +1151,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             if constexpr (EPI == EPI_RES) {
                 const float4 f0 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32);
                 const float4 f1 = *reinterpret_cast<const float4*>(stage + col * OS + c16 * 32 + 16);
-                const uint4 r = rv[it];
+                const uint4 r = rv[ry][it];
                 v.x = pack_bf16x2(f0.x + bf16_lo(r.x), f0.y + bf16_hi(r.x));
                 v.y = pack_bf16x2(f0.z + bf16_lo(r.y), f0.w + bf16_hi(r.y));
                 v.z = pack_bf16x2(f1.x + bf16_lo(r.z), f1.y + bf16_hi(r.z));
@@ -1153,7 +1159,7 @@ __device__ __forceinline__ void rows_tile(const uint16_t* __restrict__ Wf, const
             } else {
                 v = *reinterpret_cast<const uint4*>(stage + col * OS + c16 * 16);
             }
-            if (ok) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(Y + pos * g.Cout) + nb + c16 * 16) = v;
+            if (ok) st_stream16(reinterpret_cast<uint8_t*>(Y + pos * g.Cout) + nb + c16 * 16, v);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
