@@ -59,10 +59,10 @@ COPY_CAL_BYTES = 256 * 1024 * 1024
 # 1x3x3 192->256 on the 13 x 180 x 320 latent grid), from two rocprofv3 --pmc passes over
 # this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
 # what it reads for the 256 MiB device copy this script issues after timing: FETCH_SIZE
-# reads 131092.4 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
+# reads 131106.7 KiB there (factor 2.0), WRITE_SIZE 262144 KiB (factor 1.0).  Only valid
 # for the kernel version the counters were taken on: set to None when it changes.
-SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 229616.4, 374400.0
-COPY_FETCH_KIB, COPY_WRITE_KIB = 131092.4, 262144.0
+SPATIAL_FETCH_KIB, SPATIAL_WRITE_KIB = 162925.8, 374400.0
+COPY_FETCH_KIB, COPY_WRITE_KIB = 131106.7, 262144.0
 
 
 def parse():
