@@ -8,8 +8,9 @@
 // smallest power of two >= C/8, at most 64) share a row, each holding NCH 16-byte chunks in
 // registers, so the row is read once: the mean and then the centred squares are reduced
 // across the G lanes with butterfly exchanges, and the normalized row is written back with
-// the same 16-byte accesses.  A wave covers U * 64/G rows per step and issues the loads of
-// all of them first; all statistics are float32.
+// the same 16-byte accesses, as streaming (non-temporal) stores (4.5% faster than plain
+// stores at 31 x 180 x 320 x 256, identical output).  A wave covers U * 64/G rows per step and
+// issues the loads of all of them first; all statistics are float32.
 // x and y may be the same buffer: every chunk is read before any store of its row.
 #include "cvt_internal.h"
 
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* x, const
                     }
                     o[e] = pack_bf16x2(y0, y1);
                 }
-                *reinterpret_cast<uint4*>(y + p * C + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+                st_stream16(y + p * C + ch * 8, make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
         }
