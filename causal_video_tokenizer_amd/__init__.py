@@ -76,6 +76,8 @@ SIGNATURES = {
     "cvt_layernorm3d": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _ci, _vp]),
     "cvt_resblock3d_workspace": (_sz, [_ci] * 5),
     "cvt_resblock3d": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _vp, _sz, _vp]),
+    "cvt_resblock3d_packed_workspace": (_sz, [_ci] * 5),
+    "cvt_resblock3d_packed": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, ctypes.c_float, _vp, _sz, _vp]),
     "cvt_downsample3d_workspace": (_sz, [_ci] * 7),
     "cvt_downsample3d": (_ci, [_vp] * 6 + [_ci] * 6 + [_vp, _sz, _vp]),
     "cvt_upsample3d_workspace": (_sz, [_ci] * 8),
@@ -726,6 +728,37 @@ def resblock3d(x, p, eps=LN_EPS, workspace=None, out=None):
     y = _check_out(out, x.shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None else torch.empty_like(x)
     _check(lib.cvt_resblock3d(_ptr(x), ctypes.byref(w), _ptr(y), B, C, T, H, W, eps, _ptr(workspace),
                               workspace.numel(), _stream(x.device)), "resblock3d")
+    return y
+
+
+def resblock3d_packed(x, p, eps=LN_EPS, workspace=None, out=None):
+    """resblock3d on conv weights packed once by conv_weights_pack: p as for resblock3d, with
+    c1_s, c2_s the PackedWeights of the [C, C, 1, 3, 3] and c1_t, c2_t those of the
+    [C, C, 3, 1, 1] weights; bit for bit resblock3d's result, without its four repacks."""
+    _nthwc_bf16(x, "x")
+    B, C, T, H, W = x.shape
+    q = dict(p)
+    for k, taps in (("c1_s", 9), ("c1_t", 3), ("c2_s", 9), ("c2_t", 3)):
+        pw = _packed(p.get(k), taps, k)
+        if pw is None:
+            raise ValueError(f"{k} is required")
+        if pw.Cout != C or pw.Cin != C:
+            raise ValueError(f"{k} was packed for [{pw.Cout}, {pw.Cin}], x has {C} channels")
+        q[k] = pw.data
+    _require_gpu(x, workspace, *[q.get(k) for k in RESBLOCK_KEYS])
+    _same_device(x, workspace, *[q.get(k) for k in RESBLOCK_KEYS])
+    for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
+        if q.get(k) is None:
+            raise ValueError(f"{k} is required")
+        _f32_vec(q[k], C, k)
+    for k in ("c1_bs", "c1_bt", "c2_bs", "c2_bt"):
+        _f32_vec(q.get(k), C, k)
+    w = ResblockWeights(*[q[k].data_ptr() if q.get(k) is not None else None for k in RESBLOCK_KEYS])
+    need = int(lib.cvt_resblock3d_packed_workspace(B, C, T, H, W))
+    workspace = _workspace_arg(workspace, need, x)
+    y = _check_out(out, x.shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None else torch.empty_like(x)
+    _check(lib.cvt_resblock3d_packed(_ptr(x), ctypes.byref(w), _ptr(y), B, C, T, H, W, eps, _ptr(workspace),
+                                     workspace.numel(), _stream(x.device)), "resblock3d_packed")
     return y
 
 

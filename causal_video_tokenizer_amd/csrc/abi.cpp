@@ -525,8 +525,11 @@ size_t cvt_resblock3d_workspace(int B, int C, int T, int H, int W) {
     return cvt::resblock_workspace_bytes(B, C, T, H, W);
 }
 
-int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W, float eps,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Arguments of cvt_resblock3d and cvt_resblock3d_packed (packed: the conv weights are the
+// 16-byte aligned packed forms).
+int check_resblock(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W, float eps,
+                   void* workspace, size_t workspace_bytes, bool packed) {
     if (!x || !w || !y) return fail(CVT_E_NULL, "x, w and y must not be NULL");
     if (!w->ln1_g || !w->ln1_b || !w->ln2_g || !w->ln2_b || !w->c1_s || !w->c1_t || !w->c2_s || !w->c2_t)
         return fail(CVT_E_NULL, "scales, shifts and conv weights must not be NULL");
@@ -538,17 +541,40 @@ int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B,
     if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
     for (const float* v : {w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b})
         if (!aligned16(v)) return fail(CVT_E_ALIGN, "LayerNorm scales and shifts must be 16-byte aligned");
-    for (const void* v : {w->c1_s, w->c1_t, w->c2_s, w->c2_t})
+    for (const void* v : {w->c1_s, w->c1_t, w->c2_s, w->c2_t}) {
+        if (packed && !aligned16(v)) return fail(CVT_E_ALIGN, "packed weights must be 16-byte aligned");
         if (reinterpret_cast<uintptr_t>(v) & 1u) return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
+    }
     for (const float* v : {w->c1_bs, w->c1_bt, w->c2_bs, w->c2_bt})
         if (v && (reinterpret_cast<uintptr_t>(v) & 3u)) return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
-    const size_t need = cvt::resblock_workspace_bytes(B, C, T, H, W);
+    const size_t need = cvt::resblock_workspace_bytes(B, C, T, H, W, packed);
     if (!workspace || workspace_bytes < need)
         return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return CVT_OK;
+}
+}  // namespace
+
+int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W, float eps,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_resblock(x, w, y, B, C, T, H, W, eps, workspace, workspace_bytes, false);
+    if (st != CVT_OK) return st;
     return hip_status(cvt::launch_resblock(x, *w, y, B, C, T, H, W, eps, workspace, (hipStream_t)stream),
                       "cvt_resblock3d launch");
+}
+
+size_t cvt_resblock3d_packed_workspace(int B, int C, int T, int H, int W) {
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    return cvt::resblock_workspace_bytes(B, C, T, H, W, true);
+}
+
+int cvt_resblock3d_packed(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W,
+                          float eps, void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_resblock(x, w, y, B, C, T, H, W, eps, workspace, workspace_bytes, true);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_resblock(x, *w, y, B, C, T, H, W, eps, workspace, (hipStream_t)stream, true),
+                      "cvt_resblock3d_packed launch");
 }
 
 size_t cvt_downsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int parts) {

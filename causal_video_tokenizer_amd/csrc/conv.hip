@@ -2094,13 +2094,15 @@ bool resblock_supported(int C, int H, int W) {
     return use_rows_kernel(3, C, rows_span_spatial(W), C) && use_rows_kernel(3, C, rows_span_temporal((long long)H * W), C);
 }
 
-size_t resblock_workspace_bytes(int B, int C, int T, int H, int W) {
+// packed: the four conv weights of w are already in the row kernels' fragment order
+// (cvt_conv_weights_pack), so neither their workspace nor their repack is needed.
+size_t resblock_workspace_bytes(int B, int C, int T, int H, int W, bool packed) {
     const size_t P = (size_t)B * T * H * W;
-    return 2 * pack_bytes(C, C, 9) + 2 * pack_bytes(C, C, 3) + 2 * align256(P * C * 2);
+    return (packed ? 0 : 2 * pack_bytes(C, C, 9) + 2 * pack_bytes(C, C, 3)) + 2 * align256(P * C * 2);
 }
 
 hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
-                           float eps, void* workspace, hipStream_t s) {
+                           float eps, void* workspace, hipStream_t s, bool packed) {
     const long long P = (long long)B * T * H * W;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     size_t off = 0;
@@ -2109,17 +2111,26 @@ hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y
         off += n;
         return reinterpret_cast<uint16_t*>(q);
     };
-    uint16_t* w1s = take(pack_bytes(C, C, 9));
-    uint16_t* w1t = take(pack_bytes(C, C, 3));
-    uint16_t* w2s = take(pack_bytes(C, C, 9));
-    uint16_t* w2t = take(pack_bytes(C, C, 3));
+    hipError_t e;
+    const uint16_t *w1s, *w1t, *w2s, *w2t;
+    if (packed) {
+        w1s = static_cast<const uint16_t*>(w.c1_s);
+        w1t = static_cast<const uint16_t*>(w.c1_t);
+        w2s = static_cast<const uint16_t*>(w.c2_s);
+        w2t = static_cast<const uint16_t*>(w.c2_t);
+    } else {
+        uint16_t* p1s = take(pack_bytes(C, C, 9));
+        uint16_t* p1t = take(pack_bytes(C, C, 3));
+        uint16_t* p2s = take(pack_bytes(C, C, 9));
+        uint16_t* p2t = take(pack_bytes(C, C, 3));
+        if ((e = pack_frag(w.c1_s, p1s, C, C, 9, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w.c1_t, p1t, C, C, 3, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w.c2_s, p2s, C, C, 9, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w.c2_t, p2t, C, C, 3, s)) != hipSuccess) return e;
+        w1s = p1s; w1t = p1t; w2s = p2s; w2t = p2t;
+    }
     uint16_t* A = take(align256((size_t)P * C * 2));
     uint16_t* S = take(align256((size_t)P * C * 2));
-    hipError_t e;
-    if ((e = pack_frag(w.c1_s, w1s, C, C, 9, s)) != hipSuccess) return e;
-    if ((e = pack_frag(w.c1_t, w1t, C, C, 3, s)) != hipSuccess) return e;
-    if ((e = pack_frag(w.c2_s, w2s, C, C, 9, s)) != hipSuccess) return e;
-    if ((e = pack_frag(w.c2_t, w2t, C, C, 3, s)) != hipSuccess) return e;
     ConvGeom g{};
     g.P = P; g.T = T; g.H = H; g.W = W; g.Cin = C; g.Cout = C;
     g.kchunks = (C + BK - 1) / BK;

@@ -191,9 +191,9 @@ hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta
 
 // Encoder / decoder blocks (conv.hip).
 bool resblock_supported(int C, int H, int W);
-size_t resblock_workspace_bytes(int B, int C, int T, int H, int W);
+size_t resblock_workspace_bytes(int B, int C, int T, int H, int W, bool packed = false);
 hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
-                           float eps, void* workspace, hipStream_t s);
+                           float eps, void* workspace, hipStream_t s, bool packed = false);
 size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time);
 hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
                              void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s);

@@ -546,6 +546,25 @@ int cvt_resblock3d(const void* x, const cvt_resblock_weights* w, void* y, int B,
                    float eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The residual block on weights packed once, for callers whose weights stay
+ * fixed (inference): the same operation and kernels as cvt_resblock3d, bit for
+ * bit the same y, without its four per-call weight repacks.  Source: as
+ * cvt_resblock3d ("Cosmos World Foundation Model Platform for Physical AI
+ * (Cosmos-Predict1)", section "1) Cosmos Tokenizer").  In w, c1_s and c2_s hold
+ * the packed forms of the [C, C, 1, 3, 3] weights (cvt_conv_weights_pack with
+ * Cout = Cin = C, taps = 9) and c1_t and c2_t those of the [C, C, 3, 1, 1]
+ * weights (taps = 3), each 16-byte aligned, device, caller-owned; the other
+ * fields are as for cvt_resblock3d.
+ * workspace: cvt_resblock3d_packed_workspace(B, C, T, H, W) bytes (the two
+ * intermediate tensors only), caller-owned.
+ * Errors: as cvt_resblock3d; CVT_E_ALIGN also for packed weights that are not
+ * 16-byte aligned.
+ */
+size_t cvt_resblock3d_packed_workspace(int B, int C, int T, int H, int W);
+int cvt_resblock3d_packed(const void* x, const cvt_resblock_weights* w, void* y, int B, int C, int T, int H, int W,
+                          float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Downsampling block: the 1x3x3 conv Cin -> Cout at stride 2 in H and W (zero
  * padding 1: H, W -> H/2, W/2), then the causal 3x1x1 conv at stride 2 in time
  * (two zero frames in front: T = 1 + 2k -> 1 + k, output frame 0 from frame 0

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 40
+    assert len(names) == 42
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -294,6 +294,22 @@ def test_block_validation():
     odd = cvt.ResblockWeights(*([0x700000] * 12))
     odd.ln2_b = 0x700004
     assert rb(w=odd) == E_ALIGN
+
+    # the packed-weight block: only the two intermediates in its workspace, 16-byte aligned packed weights
+    need_p = lib.cvt_resblock3d_packed_workspace(1, 256, 5, 8, 8)
+    assert need_p == 2 * 5 * 8 * 8 * 256 * 2 and need - need_p >= 2 * 256 * 256 * 12 * 2
+    assert lib.cvt_resblock3d_packed_workspace(1, 256, 0, 8, 8) == 0
+
+    def rbp(**kw):
+        return lib.cvt_resblock3d_packed(kw.get("x", A), ctypes.byref(kw.get("w", w)), B_, 1, kw.get("C", 256), 5, 8,
+                                         8, 1e-6, kw.get("work", wk), kw.get("wsb", need_p), None)
+    assert rbp(w=bad) == E_NULL
+    assert rbp(C=48) == E_SHAPE
+    assert rbp(wsb=need_p - 1) == E_WORKSPACE
+    assert rbp(x=MIS) == E_ALIGN
+    odd_w = cvt.ResblockWeights(*([0x700000] * 12))
+    odd_w.c1_t = 0x700008                      # 2-byte aligned (enough unpacked), not 16-byte
+    assert rbp(w=odd_w) == E_ALIGN
 
     def ds(**kw):
         return lib.cvt_downsample3d(A, kw.get("ws", C_), kw.get("wt", C_), None, None, B_, 1, kw.get("Cin", 64), 64,

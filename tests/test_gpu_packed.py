@@ -119,3 +119,55 @@ def test_packed_binding_rejects_mismatched_weights():
                      memory_format=torch.channels_last_3d)
     with pytest.raises(ValueError):
         cvt.causal_conv3d_fact_packed(x2, pw_s, pw_t)            # packed for 192 input channels
+
+
+RESBLOCK_CASES = [
+    # B, C, T, H, W, bias, in place: 256 (4-wave tiles), 192 (192-channel tiles), 320 (plain conv +
+    # LayerNorm kernel), 64 (128-channel tiles)
+    (1, 256, 5, 9, 35, True, False),
+    (2, 192, 4, 6, 20, False, True),
+    (1, 320, 3, 5, 9, True, False),
+    (1, 64, 6, 7, 12, False, False),
+]
+
+
+@pytest.mark.parametrize("case", RESBLOCK_CASES)
+def test_packed_resblock_equals_unpacked(case):
+    """cvt_resblock3d_packed on weights packed once equals cvt_resblock3d bit for bit (and in
+    place, y = x)."""
+    B, C, T, H, W, bias, inplace = case
+    log(f"packed residual block {case}")
+    seed = 2900 + C + T
+    x = bits_to_torch(si.to_bf16_bits(si.normal((B, C, T, H, W), seed, 1.0)), channels_last=True)
+    p = {"ln1_g": f32_to_torch(1.0 + si.normal((C,), seed + 1, 0.1)), "ln1_b": f32_to_torch(si.normal((C,), seed + 2, 0.1)),
+         "ln2_g": f32_to_torch(1.0 + si.normal((C,), seed + 3, 0.1)), "ln2_b": f32_to_torch(si.normal((C,), seed + 4, 0.1)),
+         "c1_s": _w((C, C, 1, 3, 3), seed + 5, 0.03)[0], "c1_t": _w((C, C, 3, 1, 1), seed + 6, 0.03)[0],
+         "c2_s": _w((C, C, 1, 3, 3), seed + 7, 0.03)[0], "c2_t": _w((C, C, 3, 1, 1), seed + 8, 0.03)[0]}
+    if bias:
+        for j, k in enumerate(("c1_bs", "c1_bt", "c2_bs", "c2_bt")):
+            p[k] = f32_to_torch(si.normal((C,), seed + 9 + j, 0.1))
+    q = dict(p)
+    for k in ("c1_s", "c1_t", "c2_s", "c2_t"):
+        q[k] = cvt.conv_weights_pack(p[k])
+    r = cvt.resblock3d(x, p)
+    if inplace:
+        y = x.clone()
+        cvt.resblock3d_packed(y, q, out=y)
+    else:
+        y = cvt.resblock3d_packed(x, q)
+    torch.cuda.synchronize()
+    _same(y, r, f"residual block {case}")
+
+
+def test_packed_resblock_binding_rejects_unpacked_weights():
+    C = 64
+    x = torch.empty((1, C, 3, 4, 4), dtype=torch.bfloat16, device="cuda", memory_format=torch.channels_last_3d)
+    ones, zeros = torch.ones(C, device="cuda"), torch.zeros(C, device="cuda")
+    ws, wt = _w((C, C, 1, 3, 3), 2990)[0], _w((C, C, 3, 1, 1), 2991)[0]
+    p = {"ln1_g": ones, "ln1_b": zeros, "ln2_g": ones, "ln2_b": zeros, "c1_s": ws, "c1_t": wt, "c2_s": ws, "c2_t": wt}
+    with pytest.raises(ValueError):
+        cvt.resblock3d_packed(x, p)                                           # unpacked weights
+    q = dict(p, c1_s=cvt.conv_weights_pack(wt), c1_t=cvt.conv_weights_pack(wt),
+             c2_s=cvt.conv_weights_pack(ws), c2_t=cvt.conv_weights_pack(wt))
+    with pytest.raises(ValueError):
+        cvt.resblock3d_packed(x, q)                                           # temporal packing as spatial weights
