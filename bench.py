@@ -582,8 +582,9 @@ def blocks_cv8x8x8(cvt, si, torch, dev, args):
     the residual block at the post-Haar grid 31 x 180 x 320 (LayerNorm + Swish, two
     factorized convs, LayerNorm + Swish and the residual add fused into the temporal convs),
     the stride-2 downsampling block to 16 x 90 x 160, and the decoder's upsampling block back
-    (repetition inside the conv loads).  The residual block's weights are packed once
-    (cvt_resblock3d_packed); the call that repacks them every time is timed beside it.  FLOP =
+    (repetition inside the conv loads).  The blocks' weights are fixed, so they are packed once
+    (the _packed entry points); the residual block that repacks them every call is timed beside
+    it.  FLOP =
     2 * taps * Cin * Cout per output position of each conv; timed over back-to-back calls with
     HIP events."""
     wl = si.WORKLOADS["blocks_cv8x8x8_720p"]
@@ -614,17 +615,19 @@ def blocks_cv8x8x8(cvt, si, torch, dev, args):
     for k in ("c1_s", "c1_t", "c2_s", "c2_t"):
         pp[k] = cvt.conv_weights_pack(p[k])
     ws_rp = torch.empty(int(cvt.lib.cvt_resblock3d_packed_workspace(B, C, T, H, W)), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(int(cvt.lib.cvt_downsample3d_workspace(B, C, C, T, H, W, 3)), dtype=torch.uint8, device=dev)
-    ws_u = torch.empty(int(cvt.lib.cvt_upsample3d_workspace(B, C, C, Tl, Hl, Wl, 1, 1)), dtype=torch.uint8,
+    pds_s, pds_t, pus_s, pus_t = (cvt.conv_weights_pack(w) for w in (ds_s, ds_t, us_s, us_t))
+    ws_d = torch.empty(int(cvt.lib.cvt_downsample3d_packed_workspace(B, C, C, T, H, W, 3)), dtype=torch.uint8,
+                       device=dev)
+    ws_u = torch.empty(int(cvt.lib.cvt_upsample3d_packed_workspace(B, C, C, Tl, Hl, Wl, 1, 1)), dtype=torch.uint8,
                        device=dev)
     P = B * T * H * W
     conv = 2.0 * C * C * (9 + 3)
     calls = {
         "resblock_31x180x320": (lambda: cvt.resblock3d_packed(x, pp, workspace=ws_rp, out=y), 2 * conv * P),
         "resblock_31x180x320_repack_per_call": (lambda: cvt.resblock3d(x, p, workspace=ws_r, out=y), 2 * conv * P),
-        "downsample_to_16x90x160": (lambda: cvt.downsample3d(x, ds_s, ds_t, workspace=ws_d, out=yd),
+        "downsample_to_16x90x160": (lambda: cvt.downsample3d_packed(x, pds_s, pds_t, workspace=ws_d, out=yd),
                                     2.0 * C * C * 9 * B * T * Hl * Wl + 2.0 * C * C * 3 * B * Tl * Hl * Wl),
-        "upsample_to_31x180x320": (lambda: cvt.upsample3d(xl, us_s, us_t, workspace=ws_u, out=yu),
+        "upsample_to_31x180x320": (lambda: cvt.upsample3d_packed(xl, pus_s, pus_t, workspace=ws_u, out=yu),
                                    2.0 * C * C * 9 * B * Tl * H * W + 2.0 * C * C * 3 * P),
     }
     for _ in range(max(3, min(args.warmup, 10))):
@@ -645,7 +648,7 @@ def blocks_cv8x8x8(cvt, si, torch, dev, args):
         tf = flops / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "flops": flops, "TFLOPs": round(tf, 1),
                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
-    del x, xl, y, yd, yu, ws_r, ws_rp, ws_d, ws_u, p, pp
+    del x, xl, y, yd, yu, ws_r, ws_rp, ws_d, ws_u, p, pp, pds_s, pds_t, pus_s, pus_t
     torch.cuda.empty_cache()
     return out
 

@@ -82,6 +82,10 @@ SIGNATURES = {
     "cvt_downsample3d": (_ci, [_vp] * 6 + [_ci] * 6 + [_vp, _sz, _vp]),
     "cvt_upsample3d_workspace": (_sz, [_ci] * 8),
     "cvt_upsample3d": (_ci, [_vp] * 6 + [_ci] * 8 + [_vp, _sz, _vp]),
+    "cvt_downsample3d_packed_workspace": (_sz, [_ci] * 7),
+    "cvt_downsample3d_packed": (_ci, [_vp] * 6 + [_ci] * 6 + [_vp, _sz, _vp]),
+    "cvt_upsample3d_packed_workspace": (_sz, [_ci] * 8),
+    "cvt_upsample3d_packed": (_ci, [_vp] * 6 + [_ci] * 8 + [_vp, _sz, _vp]),
 }
 
 
@@ -813,6 +817,65 @@ def upsample3d(x, w_s, w_t, b_s=None, b_t=None, space=True, time=True, workspace
     _check(lib.cvt_upsample3d(_ptr(x), _ptr(w_s), _ptr(w_t), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout, T, H, W,
                               int(space), int(time), _ptr(workspace), workspace.numel(), _stream(x.device)),
            "upsample3d")
+    return y
+
+
+def downsample3d_packed(x, pw_s=None, pw_t=None, b_s=None, b_t=None, workspace=None, out=None):
+    """downsample3d on weights packed once by conv_weights_pack (pw_s of the [Cout, Cin, 1, 3, 3],
+    pw_t of the [Cout, C, 3, 1, 1] weights, either None); bit for bit downsample3d's result."""
+    _nthwc_bf16(x, "x")
+    pw_s, pw_t = _packed(pw_s, 9, "pw_s"), _packed(pw_t, 3, "pw_t")
+    if pw_s is None and pw_t is None:
+        raise ValueError("at least one of pw_s and pw_t is needed")
+    B, Cin, T, H, W = x.shape
+    Cout = (pw_s or pw_t).Cout
+    if pw_s is not None and pw_s.Cin != Cin:
+        raise ValueError(f"pw_s was packed for Cin={pw_s.Cin}, x has {Cin} channels")
+    if pw_t is not None and (pw_t.Cout != Cout or pw_t.Cin != (Cout if pw_s is not None else Cin)):
+        raise ValueError("pw_t must be packed from [Cout, Cout (or Cin without pw_s), 3, 1, 1] weights")
+    ds = [t.data if t is not None else None for t in (pw_s, pw_t)]
+    _require_gpu(x, *ds, b_s, b_t, workspace)
+    _same_device(x, *ds, b_s, b_t, workspace)
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    parts = (CVT_CONV_SPATIAL if pw_s is not None else 0) | (CVT_CONV_TEMPORAL if pw_t is not None else 0)
+    need = int(lib.cvt_downsample3d_packed_workspace(B, Cin, Cout, T, H, W, parts))
+    workspace = _workspace_arg(workspace, need, x) if need else workspace
+    shape = (B, Cout, 1 + (T - 1) // 2 if pw_t is not None else T, H // 2 if pw_s is not None else H,
+             W // 2 if pw_s is not None else W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_downsample3d_packed(_ptr(x), _ptr(ds[0]), _ptr(ds[1]), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout,
+                                       T, H, W, _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                       _stream(x.device)), "downsample3d_packed")
+    return y
+
+
+def upsample3d_packed(x, pw_s, pw_t, b_s=None, b_t=None, space=True, time=True, workspace=None, out=None):
+    """upsample3d on weights packed once by conv_weights_pack (pw_s of the [Cout, Cin, 1, 3, 3],
+    pw_t of the [Cout, Cout, 3, 1, 1] weights); bit for bit upsample3d's result."""
+    _nthwc_bf16(x, "x")
+    pw_s, pw_t = _packed(pw_s, 9, "pw_s"), _packed(pw_t, 3, "pw_t")
+    if pw_s is None or pw_t is None:
+        raise ValueError("pw_s and pw_t are needed")
+    B, Cin, T, H, W = x.shape
+    Cout = pw_s.Cout
+    if pw_s.Cin != Cin or pw_t.Cout != Cout or pw_t.Cin != Cout:
+        raise ValueError("packed weights do not chain: pw_s [Cout, Cin], pw_t [Cout, Cout]")
+    ds = [pw_s.data, pw_t.data]
+    _require_gpu(x, *ds, b_s, b_t, workspace)
+    _same_device(x, *ds, b_s, b_t, workspace)
+    _f32_vec(b_s, Cout, "b_s")
+    _f32_vec(b_t, Cout, "b_t")
+    need = int(lib.cvt_upsample3d_packed_workspace(B, Cin, Cout, T, H, W, int(space), int(time)))
+    workspace = _workspace_arg(workspace, need, x)
+    f = 2 if space else 1
+    shape = (B, Cout, 2 * T - 1 if time else T, f * H, f * W)
+    y = (_check_out(out, shape, torch.bfloat16, x.device, CVT_NTHWC) if out is not None
+         else _empty5(shape, torch.bfloat16, x.device, CVT_NTHWC))
+    _check(lib.cvt_upsample3d_packed(_ptr(x), _ptr(ds[0]), _ptr(ds[1]), _ptr(b_s), _ptr(b_t), _ptr(y), B, Cin, Cout, T,
+                                     H, W, int(space), int(time), _ptr(workspace), workspace.numel(),
+                                     _stream(x.device)), "upsample3d_packed")
     return y
 
 

@@ -582,28 +582,62 @@ size_t cvt_downsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W,
     return cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, parts & CVT_CONV_SPATIAL, parts & CVT_CONV_TEMPORAL);
 }
 
-int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+namespace {
+// Arguments of cvt_downsample3d and cvt_downsample3d_packed (packed: 16-byte aligned packed
+// weights, both parts on the row-tiled kernels).
+int check_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                      int B, int Cin, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     bool packed) {
     if (!x || !y || (!w_s && !w_t)) return fail(CVT_E_NULL, "x, y and at least one weight must not be NULL");
     if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
     if (Cin % 8 != 0 || Cout % 8 != 0)
         return fail(CVT_E_SHAPE, "Cin and Cout must be multiples of 8 (got %d, %d)", Cin, Cout);
     if (w_s && (H % 2 || W % 2)) return fail(CVT_E_SHAPE, "spatial downsampling needs even H and W (got %dx%d)", H, W);
     if (w_t && (T - 1) % 2) return fail(CVT_E_SHAPE, "temporal downsampling needs T = 1 + 2k frames (got %d)", T);
+    if (packed && (Cout < 64 || !cvt::downsample_packed_supported(Cin, Cout, H, W, w_s != nullptr, w_t != nullptr)))
+        return fail(CVT_E_SHAPE, "packed weights run the row-tiled kernels: Cout >= 64, Cin == Cout for the temporal "
+                                 "part alone and a tile's rows of the input below 2 GiB (Cin=%d, Cout=%d)", Cin, Cout);
     if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if (packed && ((w_s && !aligned16(w_s)) || (w_t && !aligned16(w_t))))
+        return fail(CVT_E_ALIGN, "packed weights must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
         return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
     if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
         return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
-    const size_t need = cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, w_s != nullptr, w_t != nullptr);
+    const size_t need = cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, w_s != nullptr, w_t != nullptr, packed);
+    if (need == 0) return CVT_OK;  // packed, one part: no workspace
     if (!workspace || workspace_bytes < need)
         return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return CVT_OK;
+}
+}  // namespace
+
+int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
+                     int B, int Cin, int Cout, int T, int H, int W, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int st = check_downsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace, workspace_bytes, false);
+    if (st != CVT_OK) return st;
     return hip_status(cvt::launch_downsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace,
                                              (hipStream_t)stream),
                       "cvt_downsample3d launch");
+}
+
+size_t cvt_downsample3d_packed_workspace(int B, int Cin, int Cout, int T, int H, int W, int parts) {
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0 || parts < 1 || parts > 3) return 0;
+    return cvt::downsample_workspace_bytes(B, Cin, Cout, T, H, W, parts & CVT_CONV_SPATIAL, parts & CVT_CONV_TEMPORAL,
+                                           true);
+}
+
+int cvt_downsample3d_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t,
+                            void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    const int st = check_downsample(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace, workspace_bytes, true);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_downsample(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W, workspace,
+                                             (hipStream_t)stream, true),
+                      "cvt_downsample3d_packed launch");
 }
 
 size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time) {
@@ -612,9 +646,11 @@ size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, i
     return cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0);
 }
 
-int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
+namespace {
+// Arguments of cvt_upsample3d and cvt_upsample3d_packed (packed: 16-byte aligned packed weights).
+int check_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
                    int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, bool packed) {
     if (!x || !y || !w_s || !w_t) return fail(CVT_E_NULL, "x, y, w_s and w_t must not be NULL");
     if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return fail(CVT_E_SHAPE, "non-positive size");
     const int f = up_space ? 2 : 1;
@@ -625,18 +661,46 @@ int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float*
         return fail(CVT_E_SHAPE, "upsampling needs Cin, Cout multiples of 8, Cout >= 64 and 9 frames of the "
                                  "upsampled tensor below 2 GiB (Cin=%d, Cout=%d)", Cin, Cout);
     if (!aligned16(x) || !aligned16(y)) return fail(CVT_E_ALIGN, "x and y must be 16-byte aligned");
+    if (packed && (!aligned16(w_s) || !aligned16(w_t))) return fail(CVT_E_ALIGN, "packed weights must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(w_s) & 1u) || (reinterpret_cast<uintptr_t>(w_t) & 1u))
         return fail(CVT_E_ALIGN, "weights must be 2-byte aligned");
     if ((b_s && (reinterpret_cast<uintptr_t>(b_s) & 3u)) || (b_t && (reinterpret_cast<uintptr_t>(b_t) & 3u)))
         return fail(CVT_E_ALIGN, "biases must be 4-byte aligned");
-    const size_t need = cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0);
+    const size_t need = cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0, packed);
     if (!workspace || workspace_bytes < need)
         return fail(CVT_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(CVT_E_ALIGN, "workspace must be 16-byte aligned");
+    return CVT_OK;
+}
+}  // namespace
+
+int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y, int B,
+                   int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    const int st = check_upsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, up_space, up_time, workspace,
+                                  workspace_bytes, false);
+    if (st != CVT_OK) return st;
     return hip_status(cvt::launch_upsample(x, w_s, w_t, b_s, b_t, y, B, Cin, Cout, T, H, W, up_space != 0,
                                            up_time != 0, workspace, (hipStream_t)stream),
                       "cvt_upsample3d launch");
+}
+
+size_t cvt_upsample3d_packed_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time) {
+    (void)up_time;
+    if (B <= 0 || Cin <= 0 || Cout <= 0 || T <= 0 || H <= 0 || W <= 0) return 0;
+    return cvt::upsample_workspace_bytes(B, Cin, Cout, T, H, W, up_space != 0, true);
+}
+
+int cvt_upsample3d_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t,
+                          void* y, int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = check_upsample(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W, up_space, up_time, workspace,
+                                  workspace_bytes, true);
+    if (st != CVT_OK) return st;
+    return hip_status(cvt::launch_upsample(x, pw_s, pw_t, b_s, b_t, y, B, Cin, Cout, T, H, W, up_space != 0,
+                                           up_time != 0, workspace, (hipStream_t)stream, true),
+                      "cvt_upsample3d_packed launch");
 }
 
 size_t cvt_causal_conv3d_fact_proj_fsq_workspace(int B, int Cin, int Cout, int Cp, int T, int H, int W, int k,

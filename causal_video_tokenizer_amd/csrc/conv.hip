@@ -2156,26 +2156,36 @@ hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y
 // the causal temporal 3x1x1 conv at stride 2 (T = 1 + 2k -> 1 + k), either part optional, on
 // conv_rows_kernel at stride 2 (conv_igemm_kernel with the strided input mapping for the
 // shapes the row kernel does not take).
-size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time) {
+// packed: w_s and w_t hold the packed forms (cvt_conv_weights_pack), which only the row-tiled
+// kernels read: both parts must take them (downsample_packed_supported), and the workspace
+// holds only the intermediate.
+bool downsample_packed_supported(int Cin, int Cout, int H, int W, bool space, bool time) {
+    const int C1 = space ? Cout : Cin, H1 = space ? H / 2 : H, W1 = space ? W / 2 : W;
+    return (!space || use_rows_kernel(3, Cout, rows_span_spatial(W), Cin)) &&
+           (!time || (C1 == Cout && use_rows_kernel(3, Cout, rows_span_temporal((long long)H1 * W1), C1)));
+}
+
+size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time, bool packed) {
     size_t b = 0;
-    if (space) b += pack_bytes(Cout, Cin, 9);
-    if (time) b += pack_bytes(Cout, space ? Cout : Cin, 3);
+    if (space && !packed) b += pack_bytes(Cout, Cin, 9);
+    if (time && !packed) b += pack_bytes(Cout, space ? Cout : Cin, 3);
     if (space && time) b += align256((size_t)B * T * (H / 2) * (W / 2) * Cout * 2);
     return b;
 }
 
 hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
-                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s) {
+                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s,
+                             bool packed) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    size_t off = 0;
+    // workspace: [spatial weights][temporal weights] (repacked per call only) [intermediate]
+    const size_t ps = w_s && !packed ? pack_bytes(Cout, Cin, 9) : 0;
+    const size_t pt = w_t && !packed ? pack_bytes(Cout, w_s ? Cout : Cin, 3) : 0;
     hipError_t e;
     const uint16_t* tin = static_cast<const uint16_t*>(x);
     int C1 = Cin, H1 = H, W1 = W;
     if (w_s) {
-        uint16_t* wps = reinterpret_cast<uint16_t*>(ws + off);
-        off += pack_bytes(Cout, Cin, 9);
-        uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(ws + off + (w_t ? pack_bytes(Cout, Cout, 3) : 0))
-                          : static_cast<uint16_t*>(y);
+        uint16_t* wps = packed ? const_cast<uint16_t*>(static_cast<const uint16_t*>(w_s)) : reinterpret_cast<uint16_t*>(ws);
+        uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(ws + ps + pt) : static_cast<uint16_t*>(y);
         H1 = H / 2;
         W1 = W / 2;
         ConvGeom g{};
@@ -2183,9 +2193,10 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
         g.kchunks = (Cin + BK - 1) / BK;
         g.Ti = T; g.Hi = H; g.Wi = W; g.st = 1; g.ss = 2;
         if (use_rows_kernel(3, Cout, rows_span_spatial(W), Cin)) {
-            if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+            if (!packed && (e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
             if ((e = launch_rows_s2<SPATIAL3>(tin, wps, b_s, S, g, B, s)) != hipSuccess) return e;
         } else {
+            if (packed) return hipErrorInvalidValue;
             if ((e = pack(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
             if ((e = launch_igemm(SPATIAL3, tin, wps, b_s, S, g, s)) != hipSuccess) return e;
         }
@@ -2193,16 +2204,17 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
         C1 = Cout;
     }
     if (!w_t) return hipSuccess;
-    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + off);
+    uint16_t* wpt = packed ? const_cast<uint16_t*>(static_cast<const uint16_t*>(w_t)) : reinterpret_cast<uint16_t*>(ws + ps);
     const int T1 = 1 + (T - 1) / 2;
     ConvGeom g{};
     g.P = (long long)B * T1 * H1 * W1; g.T = T1; g.H = H1; g.W = W1; g.Cin = C1; g.Cout = Cout;
     g.kchunks = (C1 + BK - 1) / BK;
     g.Ti = T; g.Hi = H1; g.Wi = W1; g.st = 2; g.ss = 1;
     if (C1 == Cout && use_rows_kernel(3, Cout, rows_span_temporal((long long)H1 * W1), C1)) {
-        if ((e = pack_frag(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
+        if (!packed && (e = pack_frag(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
         return launch_rows_s2<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
     }
+    if (packed) return hipErrorInvalidValue;
     if ((e = pack(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
     return launch_igemm(TEMPORAL3, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
 }
@@ -2218,22 +2230,29 @@ bool upsample_supported(int Cin, int Cout, int W_in, long long HW_mid) {
            use_rows_kernel(3, Cout, rows_span_temporal(HW_mid), Cout);
 }
 
-size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space) {
+// packed: w_s and w_t hold the packed forms (cvt_conv_weights_pack); the workspace holds only
+// the intermediate.
+size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool packed) {
     const int f = up_space ? 2 : 1;
-    return pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3) + align256((size_t)B * T * (f * H) * (f * W) * Cout * 2);
+    return (packed ? 0 : pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3)) +
+           align256((size_t)B * T * (f * H) * (f * W) * Cout * 2);
 }
 
 hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                            int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool up_time, void* workspace,
-                           hipStream_t s) {
+                           hipStream_t s, bool packed) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    uint16_t* wps = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* wpt = reinterpret_cast<uint16_t*>(ws + pack_bytes(Cout, Cin, 9));
-    uint16_t* S = reinterpret_cast<uint16_t*>(ws + pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3));
+    const size_t pw = packed ? 0 : pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3);
+    const uint16_t* wps = packed ? static_cast<const uint16_t*>(w_s) : reinterpret_cast<const uint16_t*>(ws);
+    const uint16_t* wpt =
+        packed ? static_cast<const uint16_t*>(w_t) : reinterpret_cast<const uint16_t*>(ws + pack_bytes(Cout, Cin, 9));
+    uint16_t* S = reinterpret_cast<uint16_t*>(ws + pw);
     const int Ho = up_space ? 2 * H : H, Wo = up_space ? 2 * W : W, To = up_time ? 2 * T - 1 : T;
     hipError_t e;
-    if ((e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
-    if ((e = pack_frag(w_t, wpt, Cout, Cout, 3, s)) != hipSuccess) return e;
+    if (!packed) {
+        if ((e = pack_frag(w_s, const_cast<uint16_t*>(wps), Cout, Cin, 9, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w_t, const_cast<uint16_t*>(wpt), Cout, Cout, 3, s)) != hipSuccess) return e;
+    }
     ConvGeom g{};
     g.P = (long long)B * T * Ho * Wo; g.T = T; g.H = Ho; g.W = Wo; g.Cin = Cin; g.Cout = Cout;
     g.kchunks = (Cin + BK - 1) / BK;

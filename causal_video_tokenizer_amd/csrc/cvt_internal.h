@@ -194,13 +194,16 @@ bool resblock_supported(int C, int H, int W);
 size_t resblock_workspace_bytes(int B, int C, int T, int H, int W, bool packed = false);
 hipError_t launch_resblock(const void* x, const cvt_resblock_weights& w, void* y, int B, int C, int T, int H, int W,
                            float eps, void* workspace, hipStream_t s, bool packed = false);
-size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time);
+bool downsample_packed_supported(int Cin, int Cout, int H, int W, bool space, bool time);
+size_t downsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool space, bool time,
+                                  bool packed = false);
 hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t,
-                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s);
+                             void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace, hipStream_t s,
+                             bool packed = false);
 bool upsample_supported(int Cin, int Cout, int W_in, long long HW_mid);
-size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space);
+size_t upsample_workspace_bytes(int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool packed = false);
 hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                            int B, int Cin, int Cout, int T, int H, int W, bool up_space, bool up_time, void* workspace,
-                           hipStream_t s);
+                           hipStream_t s, bool packed = false);
 
 }  // namespace cvt

@@ -582,6 +582,23 @@ int cvt_downsample3d(const void* x, const void* w_s, const void* w_t, const floa
                      void* stream);
 
 /*
+ * The downsampling block on weights packed once (fixed weights): pw_s and pw_t
+ * are the packed forms (cvt_conv_weights_pack, taps 9 and 3) of w_s and w_t,
+ * 16-byte aligned, either NULL to skip that part; the same kernels and y bit
+ * for bit as cvt_downsample3d, without its per-call repacks.  Source: as
+ * cvt_downsample3d.  workspace: cvt_downsample3d_packed_workspace bytes (the
+ * intermediate of a two-part call; 0 for one part, workspace may then be NULL).
+ * Errors: as cvt_downsample3d; CVT_E_SHAPE also where a part would not run on
+ * the row-tiled kernels (Cout < 64, a temporal part alone with Cin != Cout,
+ * or 10 image rows / 9 frames of the input of 2 GiB or more); CVT_E_ALIGN also
+ * for packed weights that are not 16-byte aligned.
+ */
+size_t cvt_downsample3d_packed_workspace(int B, int Cin, int Cout, int T, int H, int W, int parts);
+int cvt_downsample3d_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t,
+                            void* y, int B, int Cin, int Cout, int T, int H, int W, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Upsampling block (the decoder's mirror of downsampling): nearest-neighbour
  * repetition x2 in H and W (up_space) and/or causal repetition in time
  * (up_time: frame 0 once, every later frame twice, T -> 2T - 1), then the
@@ -597,6 +614,20 @@ size_t cvt_upsample3d_workspace(int B, int Cin, int Cout, int T, int H, int W, i
 int cvt_upsample3d(const void* x, const void* w_s, const void* w_t, const float* b_s, const float* b_t, void* y,
                    int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * The upsampling block on weights packed once (fixed weights): pw_s and pw_t
+ * are the packed forms (cvt_conv_weights_pack, taps 9 and 3) of w_s and w_t,
+ * 16-byte aligned; the same kernels and y bit for bit as cvt_upsample3d,
+ * without its two per-call repacks.  Source: as cvt_upsample3d.
+ * workspace: cvt_upsample3d_packed_workspace bytes (the intermediate only).
+ * Errors: as cvt_upsample3d; CVT_E_ALIGN also for packed weights that are not
+ * 16-byte aligned.
+ */
+size_t cvt_upsample3d_packed_workspace(int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time);
+int cvt_upsample3d_packed(const void* x, const void* pw_s, const void* pw_t, const float* b_s, const float* b_t,
+                          void* y, int B, int Cin, int Cout, int T, int H, int W, int up_space, int up_time,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * FSQ dequantize fused with the decoder's first layer, the 1x1 projection

@@ -28,7 +28,7 @@ def header_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_symbols()
-    assert len(names) == 42
+    assert len(names) == 46
     for n in names:
         assert hasattr(lib, n), n
         assert n in cvt.SIGNATURES, n
@@ -329,6 +329,35 @@ def test_block_validation():
     assert us(wsb=10) == E_WORKSPACE
     assert lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4, 4, 1, 1) > lib.cvt_upsample3d_workspace(1, 64, 128, 3, 4,
                                                                                                    4, 0, 1)
+
+    # the packed-weight blocks: only the intermediates in their workspaces, 16-byte aligned packed weights, and
+    # (downsampling) every part on the row-tiled kernels
+    P16, P8 = ctypes.c_void_p(0x300000), ctypes.c_void_p(0x300008)
+    assert lib.cvt_downsample3d_packed_workspace(1, 64, 64, 5, 8, 8, 3) == 5 * 4 * 4 * 64 * 2   # the 5 x 4 x 4 intermediate
+    assert lib.cvt_downsample3d_packed_workspace(1, 64, 64, 5, 8, 8, 1) == 0
+    assert lib.cvt_downsample3d_packed_workspace(1, 64, 64, 5, 8, 8, 2) == 0
+
+    def dsp(**kw):
+        return lib.cvt_downsample3d_packed(A, kw.get("ws", P16), kw.get("wt", P16), None, None, B_, 1,
+                                           kw.get("Cin", 64), kw.get("Cout", 64), kw.get("T", 5), 8, 8, wk,
+                                           kw.get("wsb", 10), None)
+    assert dsp(ws=None, wt=None) == E_NULL
+    assert dsp(T=4) == E_SHAPE
+    assert dsp(Cout=32) == E_SHAPE                    # below the row kernels' 64 output channels
+    assert dsp(ws=None, Cin=128) == E_SHAPE           # temporal part alone with Cin != Cout
+    assert dsp(wt=P8) == E_ALIGN
+    assert dsp() == E_WORKSPACE                       # two parts: the intermediate
+
+    need_up = lib.cvt_upsample3d_packed_workspace(1, 64, 64, 3, 4, 4, 1, 1)
+    assert need_up == 3 * 8 * 8 * 64 * 2 and lib.cvt_upsample3d_workspace(1, 64, 64, 3, 4, 4, 1, 1) > need_up
+
+    def usp(**kw):
+        return lib.cvt_upsample3d_packed(A, kw.get("ws", P16), P16, None, None, B_, 1, 64, kw.get("Cout", 64), 3, 4,
+                                         4, 1, 1, wk, kw.get("wsb", need_up - 1), None)
+    assert usp(ws=None) == E_NULL
+    assert usp(Cout=32) == E_SHAPE
+    assert usp(ws=P8) == E_ALIGN
+    assert usp() == E_WORKSPACE
 
 
 def test_fused_fsq_validation():

@@ -4,7 +4,8 @@ repack the weights on every call: bit-identical outputs (same kernels, same weig
 spatial only, temporal only and both parts, with and without biases, on the 4-wave
 256-channel, 3-wave 192-channel and 128 x 64 tiles, ragged grids and two clips; the same
 packed weights reused on a second input; one case also against the float64 oracle,
-|g - o| <= 2e-2 (|o| + rms(o))."""
+|g - o| <= 2e-2 (|o| + rms(o)).  The blocks on packed weights (cvt_resblock3d_packed,
+cvt_downsample3d_packed, cvt_upsample3d_packed) against the blocks that repack: bit-identical."""
 
 import numpy as np
 import pytest
@@ -171,3 +172,54 @@ def test_packed_resblock_binding_rejects_unpacked_weights():
              c2_s=cvt.conv_weights_pack(ws), c2_t=cvt.conv_weights_pack(wt))
     with pytest.raises(ValueError):
         cvt.resblock3d_packed(x, q)                                           # temporal packing as spatial weights
+
+
+DOWN_CASES = [
+    # B, Cin, Cout, T, H, W, space, time, bias
+    (1, 256, 256, 9, 12, 40, True, True, True),
+    (2, 128, 128, 5, 8, 18, True, True, False),    # 128-channel tiles
+    (1, 192, 192, 7, 10, 14, True, False, True),   # spatial part only
+    (1, 256, 256, 9, 6, 10, False, True, True),    # temporal part only (Cin == Cout)
+]
+
+
+@pytest.mark.parametrize("case", DOWN_CASES)
+def test_packed_downsample_equals_unpacked(case):
+    B, Cin, Cout, T, H, W, space, time, bias = case
+    log(f"packed downsampling block {case}")
+    seed = 3000 + Cin + T + H
+    x = bits_to_torch(si.to_bf16_bits(si.normal((B, Cin, T, H, W), seed, 1.0)), channels_last=True)
+    w_s = _w((Cout, Cin, 1, 3, 3), seed + 1)[0] if space else None
+    w_t = _w((Cout, Cout if space else Cin, 3, 1, 1), seed + 2)[0] if time else None
+    b_s = f32_to_torch(si.normal((Cout,), seed + 3, 0.1)) if bias and space else None
+    b_t = f32_to_torch(si.normal((Cout,), seed + 4, 0.1)) if bias and time else None
+    pw_s = cvt.conv_weights_pack(w_s) if space else None
+    pw_t = cvt.conv_weights_pack(w_t) if time else None
+    y = cvt.downsample3d_packed(x, pw_s, pw_t, b_s, b_t)
+    r = cvt.downsample3d(x, w_s, w_t, b_s, b_t)
+    torch.cuda.synchronize()
+    _same(y, r, f"downsampling {case}")
+
+
+UP_CASES = [
+    # B, Cin, Cout, T, H, W, space, time, bias
+    (1, 256, 256, 4, 6, 20, True, True, True),
+    (1, 128, 192, 3, 5, 9, True, False, False),    # 192-channel tiles, spatial repetition only
+    (2, 64, 64, 3, 4, 6, False, True, True),       # temporal repetition only
+]
+
+
+@pytest.mark.parametrize("case", UP_CASES)
+def test_packed_upsample_equals_unpacked(case):
+    B, Cin, Cout, T, H, W, space, time, bias = case
+    log(f"packed upsampling block {case}")
+    seed = 3100 + Cin + Cout + T
+    x = bits_to_torch(si.to_bf16_bits(si.normal((B, Cin, T, H, W), seed, 1.0)), channels_last=True)
+    w_s, w_t = _w((Cout, Cin, 1, 3, 3), seed + 1)[0], _w((Cout, Cout, 3, 1, 1), seed + 2)[0]
+    b_s = f32_to_torch(si.normal((Cout,), seed + 3, 0.1)) if bias else None
+    b_t = f32_to_torch(si.normal((Cout,), seed + 4, 0.1)) if bias else None
+    pw_s, pw_t = cvt.conv_weights_pack(w_s), cvt.conv_weights_pack(w_t)
+    y = cvt.upsample3d_packed(x, pw_s, pw_t, b_s, b_t, space=space, time=time)
+    r = cvt.upsample3d(x, w_s, w_t, b_s, b_t, space=space, time=time)
+    torch.cuda.synchronize()
+    _same(y, r, f"upsampling {case}")
