@@ -2184,7 +2184,8 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
     const uint16_t* tin = static_cast<const uint16_t*>(x);
     int C1 = Cin, H1 = H, W1 = W;
     if (w_s) {
-        uint16_t* wps = packed ? const_cast<uint16_t*>(static_cast<const uint16_t*>(w_s)) : reinterpret_cast<uint16_t*>(ws);
+        uint16_t* pbuf = reinterpret_cast<uint16_t*>(ws);  // per-call repack target
+        const uint16_t* wps = packed ? static_cast<const uint16_t*>(w_s) : pbuf;
         uint16_t* S = w_t ? reinterpret_cast<uint16_t*>(ws + ps + pt) : static_cast<uint16_t*>(y);
         H1 = H / 2;
         W1 = W / 2;
@@ -2193,29 +2194,30 @@ hipError_t launch_downsample(const void* x, const void* w_s, const void* w_t, co
         g.kchunks = (Cin + BK - 1) / BK;
         g.Ti = T; g.Hi = H; g.Wi = W; g.st = 1; g.ss = 2;
         if (use_rows_kernel(3, Cout, rows_span_spatial(W), Cin)) {
-            if (!packed && (e = pack_frag(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+            if (!packed && (e = pack_frag(w_s, pbuf, Cout, Cin, 9, s)) != hipSuccess) return e;
             if ((e = launch_rows_s2<SPATIAL3>(tin, wps, b_s, S, g, B, s)) != hipSuccess) return e;
         } else {
             if (packed) return hipErrorInvalidValue;
-            if ((e = pack(w_s, wps, Cout, Cin, 9, s)) != hipSuccess) return e;
+            if ((e = pack(w_s, pbuf, Cout, Cin, 9, s)) != hipSuccess) return e;
             if ((e = launch_igemm(SPATIAL3, tin, wps, b_s, S, g, s)) != hipSuccess) return e;
         }
         tin = S;
         C1 = Cout;
     }
     if (!w_t) return hipSuccess;
-    uint16_t* wpt = packed ? const_cast<uint16_t*>(static_cast<const uint16_t*>(w_t)) : reinterpret_cast<uint16_t*>(ws + ps);
+    uint16_t* pbuf = reinterpret_cast<uint16_t*>(ws + ps);  // per-call repack target
+    const uint16_t* wpt = packed ? static_cast<const uint16_t*>(w_t) : pbuf;
     const int T1 = 1 + (T - 1) / 2;
     ConvGeom g{};
     g.P = (long long)B * T1 * H1 * W1; g.T = T1; g.H = H1; g.W = W1; g.Cin = C1; g.Cout = Cout;
     g.kchunks = (C1 + BK - 1) / BK;
     g.Ti = T; g.Hi = H1; g.Wi = W1; g.st = 2; g.ss = 1;
     if (C1 == Cout && use_rows_kernel(3, Cout, rows_span_temporal((long long)H1 * W1), C1)) {
-        if (!packed && (e = pack_frag(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
+        if (!packed && (e = pack_frag(w_t, pbuf, Cout, C1, 3, s)) != hipSuccess) return e;
         return launch_rows_s2<TEMPORAL3>(tin, wpt, b_t, static_cast<uint16_t*>(y), g, B, s);
     }
     if (packed) return hipErrorInvalidValue;
-    if ((e = pack(w_t, wpt, Cout, C1, 3, s)) != hipSuccess) return e;
+    if ((e = pack(w_t, pbuf, Cout, C1, 3, s)) != hipSuccess) return e;
     return launch_igemm(TEMPORAL3, tin, wpt, b_t, static_cast<uint16_t*>(y), g, s);
 }
 
@@ -2243,15 +2245,16 @@ hipError_t launch_upsample(const void* x, const void* w_s, const void* w_t, cons
                            hipStream_t s, bool packed) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const size_t pw = packed ? 0 : pack_bytes(Cout, Cin, 9) + pack_bytes(Cout, Cout, 3);
-    const uint16_t* wps = packed ? static_cast<const uint16_t*>(w_s) : reinterpret_cast<const uint16_t*>(ws);
-    const uint16_t* wpt =
-        packed ? static_cast<const uint16_t*>(w_t) : reinterpret_cast<const uint16_t*>(ws + pack_bytes(Cout, Cin, 9));
+    uint16_t* ps_buf = reinterpret_cast<uint16_t*>(ws);  // per-call repack targets
+    uint16_t* pt_buf = reinterpret_cast<uint16_t*>(ws + pack_bytes(Cout, Cin, 9));
+    const uint16_t* wps = packed ? static_cast<const uint16_t*>(w_s) : ps_buf;
+    const uint16_t* wpt = packed ? static_cast<const uint16_t*>(w_t) : pt_buf;
     uint16_t* S = reinterpret_cast<uint16_t*>(ws + pw);
     const int Ho = up_space ? 2 * H : H, Wo = up_space ? 2 * W : W, To = up_time ? 2 * T - 1 : T;
     hipError_t e;
     if (!packed) {
-        if ((e = pack_frag(w_s, const_cast<uint16_t*>(wps), Cout, Cin, 9, s)) != hipSuccess) return e;
-        if ((e = pack_frag(w_t, const_cast<uint16_t*>(wpt), Cout, Cout, 3, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w_s, ps_buf, Cout, Cin, 9, s)) != hipSuccess) return e;
+        if ((e = pack_frag(w_t, pt_buf, Cout, Cout, 3, s)) != hipSuccess) return e;
     }
     ConvGeom g{};
     g.P = (long long)B * T * Ho * Wo; g.T = T; g.H = Ho; g.W = Wo; g.Cin = Cin; g.Cout = Cout;
