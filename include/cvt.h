@@ -128,7 +128,9 @@ int cvt_haar3d_inv(const void* y, int y_dtype, int y_layout, void* x, int x_dtyp
  *      (with k = 1 and w_t = NULL the call is a 1x1x1 projection).
  *      At least one of w_s and w_t must be given.
  * b_s, b_t: float32 [Cout] biases or NULL.
- * y:   bf16 NTHWC [B, Cout, T, H, W].
+ * y:   bf16 NTHWC [B, Cout, T, H, W]; must not overlap x, the weights or the
+ *      workspace (a tile reads input rows and frames that the outputs of other
+ *      tiles would overwrite).
  * k:   1 or 3.
  * Accumulation is float32; the spatial result is stored as bf16 in the
  * workspace before the temporal convolution reads it.
