@@ -27,6 +27,7 @@ CASES = [
     (1, 160, 192, 6, 9, 20, True),     # 3-wave 192-channel tiles
     (1, 64, 128, 4, 10, 70, False),    # 128-channel tiles of 64 columns
     (1, 96, 64, 1, 5, 9, True),
+    (1, 40, 64, 3, 6, 10, True),       # input-channel tail (40 = 32 + 8): the chunk past Cin reads zeros
 ]
 
 
@@ -129,6 +130,7 @@ RESBLOCK_CASES = [
     (2, 192, 4, 6, 20, False, True),
     (1, 320, 3, 5, 9, True, False),
     (1, 64, 6, 7, 12, False, False),
+    (1, 136, 3, 6, 7, True, False),     # channels past Cout left out of the LayerNorm statistics
 ]
 
 
@@ -180,6 +182,7 @@ DOWN_CASES = [
     (2, 128, 128, 5, 8, 18, True, True, False),    # 128-channel tiles
     (1, 192, 192, 7, 10, 14, True, False, True),   # spatial part only
     (1, 256, 256, 9, 6, 10, False, True, True),    # temporal part only (Cin == Cout)
+    (1, 128, 256, 5, 8, 12, True, True, True),     # channels widened by the spatial part
 ]
 
 
