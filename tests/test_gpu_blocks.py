@@ -184,3 +184,31 @@ def test_upsample_parity_and_equals_materialized_repeat(case):
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(y), to_bits(y2))
     assert_rel(to_f64(y), ob.upsample(x64, ws64, wt64, bs64, bt64, space, time), TOL, "upsample")
+
+
+def test_packed_resblock_full_grid_sampled():
+    """The route the benchmark times at its size: the residual block on packed weights over the
+    31 x 180 x 320 x 256 grid of a 121-frame 720p clip, against the float64 oracle on sampled
+    windows (corners and the middle).  The oracle runs on a crop holding each window's
+    receptive field (4 frames back, 2 positions each way in space: two factorized convs); where
+    the crop meets the tensor's edge it is the tensor's own zero padding."""
+    wl = si.WORKLOADS["blocks_cv8x8x8_720p"]
+    B, C, T, H, W = wl["x"]
+    log(f"packed resblock full grid {wl['x']}")
+    xb = si.to_bf16_bits(si.normal((B, C, T, H, W), 840, 1.0))
+    x = bits_to_torch(xb, channels_last=True)
+    p, ref = block_params_dev(C, 841, True)
+    q = dict(p)
+    for k in ("c1_s", "c1_t", "c2_s", "c2_t"):
+        q[k] = cvt.conv_weights_pack(p[k])
+    y = cvt.resblock3d_packed(x, q)
+    torch.cuda.synchronize()
+    for (t0, t1), (y0, y1), (x0, x1) in [((0, 2), (0, 3), (0, 3)), ((14, 16), (88, 91), (150, 153)),
+                                         ((28, 30), (176, 179), (316, 319))]:
+        ct, cy, cx = max(t0 - 4, 0), max(y0 - 2, 0), max(x0 - 2, 0)
+        crop = obf16.decode(xb[:, :, ct:t1 + 1, cy:min(y1 + 2, H - 1) + 1, cx:min(x1 + 2, W - 1) + 1])
+        o = ob.resblock(crop, ref)[:, :, t0 - ct:, y0 - cy:y0 - cy + y1 - y0 + 1, x0 - cx:x0 - cx + x1 - x0 + 1]
+        g = to_f64(y[:, :, t0:t1 + 1, y0:y1 + 1, x0:x1 + 1])
+        assert_rel(g, o, TOL, f"resblock window t {t0}-{t1} y {y0}-{y1} x {x0}-{x1}")
+    del x, y
+    torch.cuda.empty_cache()
