@@ -209,6 +209,73 @@ def test_packed_resblock_full_grid_sampled():
         crop = obf16.decode(xb[:, :, ct:t1 + 1, cy:min(y1 + 2, H - 1) + 1, cx:min(x1 + 2, W - 1) + 1])
         o = ob.resblock(crop, ref)[:, :, t0 - ct:, y0 - cy:y0 - cy + y1 - y0 + 1, x0 - cx:x0 - cx + x1 - x0 + 1]
         g = to_f64(y[:, :, t0:t1 + 1, y0:y1 + 1, x0:x1 + 1])
+        assert g.shape == o.shape == (B, C, t1 - t0 + 1, y1 - y0 + 1, x1 - x0 + 1), (g.shape, o.shape)
         assert_rel(g, o, TOL, f"resblock window t {t0}-{t1} y {y0}-{y1} x {x0}-{x1}")
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def _packed_pair(shape, seed, std):
+    w, w64 = bf16_pair(shape, seed, std)
+    return cvt.conv_weights_pack(w), w64
+
+
+def test_packed_downsample_full_grid_sampled():
+    """The benchmark's downsampling route at its size: packed weights, 31 x 180 x 320 x 256 ->
+    16 x 90 x 160, against the oracle on sampled output windows.  Each crop starts on an even
+    input row, column and frame, so the stride-2 grid of the crop is the tensor's, and holds
+    the window's receptive field (input rows 2 y' - 1 .. 2 y' + 1, frames 2 t' - 2 .. 2 t')."""
+    wl = si.WORKLOADS["blocks_cv8x8x8_720p"]
+    B, C, T, H, W = wl["x"]
+    log(f"packed downsample full grid {wl['x']}")
+    xb = si.to_bf16_bits(si.normal((B, C, T, H, W), 850, 1.0))
+    x = bits_to_torch(xb, channels_last=True)
+    (pws, ws64), (pwt, wt64) = _packed_pair((C, C, 1, 3, 3), 851, 0.02), _packed_pair((C, C, 3, 1, 1), 852, 0.03)
+    bs, bs64 = f32_pair((C,), 853, 0.1)
+    bt, bt64 = f32_pair((C,), 854, 0.1)
+    y = cvt.downsample3d_packed(x, pws, pwt, bs, bt)
+    torch.cuda.synchronize()
+
+    def crop(o0, o1, n, temporal):  # input range [c0, c1] and the first wanted crop output
+        c0 = max(0, 2 * o0 - 2)
+        c1 = 2 * o1 if temporal else min(n - 1, 2 * o1 + 1)
+        return c0, c1, o0 - c0 // 2
+    for wt_, wy, wx in [((0, 1), (0, 3), (0, 3)), ((8, 9), (44, 47), (80, 83)), ((14, 15), (86, 89), (156, 159))]:
+        (t0, t1, jt), (y0, y1, jy), (x0, x1, jx) = crop(*wt_, T, True), crop(*wy, H, False), crop(*wx, W, False)
+        o = ob.downsample(obf16.decode(xb[:, :, t0:t1 + 1, y0:y1 + 1, x0:x1 + 1]), ws64, wt64, bs64, bt64)
+        o = o[:, :, jt:jt + wt_[1] - wt_[0] + 1, jy:jy + wy[1] - wy[0] + 1, jx:jx + wx[1] - wx[0] + 1]
+        g = to_f64(y[:, :, wt_[0]:wt_[1] + 1, wy[0]:wy[1] + 1, wx[0]:wx[1] + 1])
+        assert g.shape == o.shape == (B, C, wt_[1] - wt_[0] + 1, wy[1] - wy[0] + 1, wx[1] - wx[0] + 1), (g.shape, o.shape)
+        assert_rel(g, o, TOL, f"downsample window t' {wt_} y' {wy} x' {wx}")
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def test_packed_upsample_full_grid_sampled():
+    """The benchmark's upsampling route at its size: packed weights, 16 x 90 x 160 x 256 ->
+    31 x 180 x 320, against the oracle on sampled output windows.  The crops keep every input
+    frame (the causal repetition doubles every frame but the first) and the input rows and
+    columns whose repetitions the window's 3 x 3 taps reach."""
+    wl = si.WORKLOADS["blocks_cv8x8x8_720p"]
+    B, C, Ti, Hi, Wi = wl["low"]
+    log(f"packed upsample full grid {wl['low']}")
+    xb = si.to_bf16_bits(si.normal((B, C, Ti, Hi, Wi), 860, 1.0))
+    x = bits_to_torch(xb, channels_last=True)
+    (pws, ws64), (pwt, wt64) = _packed_pair((C, C, 1, 3, 3), 861, 0.02), _packed_pair((C, C, 3, 1, 1), 862, 0.03)
+    bs, bs64 = f32_pair((C,), 863, 0.1)
+    bt, bt64 = f32_pair((C,), 864, 0.1)
+    y = cvt.upsample3d_packed(x, pws, pwt, bs, bt)
+    torch.cuda.synchronize()
+
+    def crop(o0, o1, n):  # low-resolution input range and the crop output row of o0
+        c0, c1 = max(0, (o0 - 1) // 2), min(n - 1, (o1 + 1) // 2)
+        return c0, c1, o0 - 2 * c0
+    for wt_, wy, wx in [((0, 2), (0, 3), (0, 3)), ((14, 16), (89, 92), (157, 160)), ((28, 30), (176, 179), (316, 319))]:
+        (y0, y1, jy), (x0, x1, jx) = crop(*wy, Hi), crop(*wx, Wi)
+        o = ob.upsample(obf16.decode(xb[:, :, :, y0:y1 + 1, x0:x1 + 1]), ws64, wt64, bs64, bt64)
+        o = o[:, :, wt_[0]:wt_[1] + 1, jy:jy + wy[1] - wy[0] + 1, jx:jx + wx[1] - wx[0] + 1]
+        g = to_f64(y[:, :, wt_[0]:wt_[1] + 1, wy[0]:wy[1] + 1, wx[0]:wx[1] + 1])
+        assert g.shape == o.shape == (B, C, wt_[1] - wt_[0] + 1, wy[1] - wy[0] + 1, wx[1] - wx[0] + 1), (g.shape, o.shape)
+        assert_rel(g, o, TOL, f"upsample window t {wt_} y {wy} x {wx}")
     del x, y
     torch.cuda.empty_cache()
